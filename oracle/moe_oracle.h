@@ -1,0 +1,79 @@
+/*
+ * moe_oracle.h -- plain, slow, fp64 CPU reference of one routed
+ * Mixture-of-Experts FFN layer whose experts are stored as MXFP4.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no
+ * code, header, table or constant with the GPU library, and the GPU library
+ * never calls it.
+ *
+ * Every array is row-major, host memory, owned by the caller.  "bf16" means
+ * the upper 16 bits of an IEEE binary32, carried in a uint16_t.
+ *
+ * Expert weight layout (per expert e, K contiguous within a row):
+ *   gu_codes  [E][2f][d/2]  E2M1 codes, element 2i in the low nibble of byte i
+ *   gu_scales [E][2f][d/32] E8M0 codes, one per 32 consecutive K elements
+ *   dn_codes  [E][d][f/2]
+ *   dn_scales [E][d][f/32]
+ *   gate = rows [0, f) of gu, up = rows [f, 2f).
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- scalar formats ---------------------------------------------------- */
+double   orc_bf16_value(uint16_t bits);
+double   orc_e2m1_value(unsigned code);            /* 4-bit code          */
+double   orc_e8m0_value(unsigned code);            /* 8-bit code, 255=NaN */
+uint16_t orc_round_to_bf16(double v);              /* RNE, fp64 -> bf16   */
+double   orc_mxfp4_weight(const uint8_t *codes, const uint8_t *scales,
+                          int K, int row, int col);
+
+/* ---- router ------------------------------------------------------------ */
+void orc_router_logits(int T, int d, int E, const uint16_t *x,
+                       const uint16_t *router_w, const float *bias,
+                       float *logits);
+void orc_topk_softmax(int T, int E, int k, const float *logits,
+                      int32_t *topk_ids, double *topk_w);
+
+/* ---- grouping rows by expert ------------------------------------------- */
+void orc_permute(int T, int E, int k, const int32_t *topk_ids,
+                 int32_t *counts, int32_t *offsets, int32_t *sorted_rows,
+                 int32_t *row_pos);
+
+/* ---- one routed expert applied to one token row ------------------------ */
+void orc_expert_row(int d, int f, const uint16_t *x_row,
+                    const uint8_t *gu_codes, const uint8_t *gu_scales,
+                    const uint8_t *dn_codes, const uint8_t *dn_scales,
+                    double *h, double *o);
+
+/* ---- weighted combine of one token's k expert outputs ------------------ */
+void orc_combine_token(int d, int k, const double *w, const double *o,
+                       double *y64, uint16_t *y_bf16);
+
+/* ---- whole layer, for configurations small enough to run in full ------- */
+int orc_layer_forward(int T, int d, int E, int k, int f, const uint16_t *x,
+                      const uint16_t *router_w, const float *bias,
+                      const uint8_t *gu_codes, const uint8_t *gu_scales,
+                      const uint8_t *dn_codes, const uint8_t *dn_scales,
+                      float *logits, int32_t *topk_ids, double *topk_w,
+                      double *y64, uint16_t *y_bf16, int n_threads);
+
+/* ---- OCP MX conversion model (element formats below) ------------------- */
+enum { ORC_FMT_E4M3 = 0, ORC_FMT_E2M3 = 1, ORC_FMT_E2M1 = 2 };
+double orc_elem_value(int fmt, unsigned code);
+void   orc_mx_quantize_block(int fmt, const double *v, uint8_t *scale_code,
+                             uint8_t *codes);
+void   orc_mx_split_block(int fmt, const float *v, uint8_t *hi_scale,
+                          uint8_t *hi_codes, uint8_t *lo_scale,
+                          uint8_t *lo_codes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
