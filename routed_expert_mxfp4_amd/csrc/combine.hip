@@ -1,0 +1,54 @@
+// combine.hip -- weighted combine of each token's k expert outputs (gfx950).
+//
+// y[t][m] = sum_j w[t][j] * rows_out[row_pos[t*k+j]][m], accumulated in fp32
+// in slot order and rounded once to bf16 (the MoE tail's weighted reduction:
+// Moonshine README, "Run layer-major prefill").  Each thread owns 8
+// consecutive outputs of one token, so every y element has exactly one
+// writer (no atomics) and all loads and stores are 16 bytes wide.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ rows_out,
+                                                      const int32_t *__restrict__ row_pos,
+                                                      const float *__restrict__ topk_w,
+                                                      uint16_t *__restrict__ y, int T, int d,
+                                                      int k) {
+    const int t = blockIdx.y;
+    const int v = blockIdx.x * 256 + threadIdx.x;       // 8-element vector index
+    if (v >= (d >> 3)) return;
+    const int nrows = T * k;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+        const int p = row_pos[(size_t)t * k + j];
+        if ((unsigned)p >= (unsigned)nrows) continue;
+        const float wj = topk_w[(size_t)t * k + j];
+        const uint4 q = reinterpret_cast<const uint4 *>(rows_out + (size_t)p * d)[v];
+        const uint32_t wds[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wj * bf16_bits_to_f32(wds[i] & 0xFFFFu);
+            acc[2 * i + 1] += wj * bf16_bits_to_f32(wds[i] >> 16);
+        }
+    }
+    uint4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | ((uint32_t)f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | ((uint32_t)f32_to_bf16_rne(acc[7]) << 16);
+    reinterpret_cast<uint4 *>(y + (size_t)t * d)[v] = o;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
+                          const float *topk_w, uint16_t *y, int T, int d, int k,
+                          hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    dim3 grid(((d >> 3) + 255) / 256, T);
+    combine_kernel<<<grid, 256, 0, s>>>(rows_out, row_pos, topk_w, y, T, d, k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,278 @@
+// moe_abi.cpp -- the C ABI of include/moe.h: host-side validation, workspace
+// planning and dispatch of the gfx950 kernels onto the caller's stream.
+//
+// Every entry point validates all arguments before launching anything
+// (a refused request leaves the outputs untouched), never allocates, never
+// synchronises the host with the device, and never lets a C++ exception out.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "moe_internal.hpp"
+
+namespace {
+
+using moe::ExpertArgs;
+
+constexpr int64_t kRowsLimit = (int64_t)1 << 31;
+constexpr int kFuseMaxT = 4;          // small T: fused down + combine
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+moe_status check_dims(const moe_dims *dm) {
+    if (!dm) return MOE_ERR_NULL;
+    const moe_dims &D = *dm;
+    if (D.T < 0 || D.d <= 0 || D.E <= 0 || D.k <= 0 || D.f <= 0) return MOE_ERR_SHAPE;
+    if (D.d % 64 != 0 || D.d > 32768) return MOE_ERR_SHAPE;
+    if (D.f % 32 != 0 || D.f > 16384) return MOE_ERR_SHAPE;
+    if (D.E > moe::kMaxExperts) return MOE_ERR_SHAPE;
+    if (D.k > D.E || D.k > moe::kMaxTopK) return MOE_ERR_SHAPE;
+    if ((int64_t)D.T * D.k >= kRowsLimit) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+moe_status check_experts(const moe_mxfp4_experts *w) {
+    if (!w) return MOE_ERR_NULL;
+    if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales) return MOE_ERR_NULL;
+    if (!aligned16(w->gu_codes) || !aligned16(w->gu_scales) || !aligned16(w->dn_codes) ||
+        !aligned16(w->dn_scales))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+moe_status device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+// ---- workspace layouts ------------------------------------------------------
+struct RouteWs {
+    size_t logits, total;
+};
+RouteWs route_ws(const moe_dims &D) {
+    RouteWs w;
+    w.logits = 0;
+    w.total = al256((size_t)D.T * D.E * 4);
+    return w;
+}
+
+struct FfnWs {
+    size_t plan, h, total;
+};
+FfnWs ffn_ws(const moe_dims &D) {
+    FfnWs w;
+    w.plan = 0;
+    w.h = al256((size_t)(D.E + 1) * 4);
+    w.total = w.h + al256((size_t)D.T * D.k * D.f * 4);
+    return w;
+}
+
+struct LayerWs {
+    size_t logits, ids, tw, counts, offsets, sorted_rows, row_pos, perm, ffn, rows_out, total;
+};
+LayerWs layer_ws(const moe_dims &D) {
+    const size_t rows = (size_t)D.T * D.k;
+    LayerWs w;
+    size_t p = 0;
+    w.logits = p; p += al256((size_t)D.T * D.E * 4);
+    w.ids = p; p += al256(rows * 4);
+    w.tw = p; p += al256(rows * 4);
+    w.counts = p; p += al256((size_t)D.E * 4);
+    w.offsets = p; p += al256((size_t)(D.E + 1) * 4);
+    w.sorted_rows = p; p += al256(rows * 4);
+    w.row_pos = p; p += al256(rows * 4);
+    w.perm = p; p += al256(moe::permute_ws_bytes(D.T, D.E));
+    w.ffn = p; p += al256(ffn_ws(D).total);
+    w.rows_out = p;
+    if (D.T > kFuseMaxT) p += al256(rows * D.d * 2);
+    w.total = p;
+    return w;
+}
+
+template <typename Fn>
+moe_status guarded(Fn fn) {
+    try {
+        return fn();
+    } catch (...) {
+        return MOE_ERR_DEVICE;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_str(int status) {
+    switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: dims outside the supported limits";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request not served by this build";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: HIP reported an error while launching";
+    default: return "unknown moe_status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_dims *dims, int entry) {
+    if (check_dims(dims) != MOE_OK) return (size_t)-1;
+    const moe_dims &D = *dims;
+    switch (entry) {
+    case MOE_ENTRY_ROUTE: return route_ws(D).total;
+    case MOE_ENTRY_PERMUTE: return moe::permute_ws_bytes(D.T, D.E);
+    case MOE_ENTRY_EXPERT_FFN: return ffn_ws(D).total;
+    case MOE_ENTRY_COMBINE: return 0;
+    case MOE_ENTRY_LAYER_FORWARD: return layer_ws(D).total;
+    default: return (size_t)-1;
+    }
+}
+
+moe_status moe_route(const moe_dims *dims, const uint16_t *x, const uint16_t *router_w,
+                     const float *router_bias, float *logits_out, int32_t *topk_ids,
+                     float *topk_w, void *ws, size_t ws_bytes, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (D.T == 0) return MOE_OK;
+        if (!x || !router_w || !topk_ids || !topk_w) return MOE_ERR_NULL;
+        if (!aligned16(x) || !aligned16(router_w)) return MOE_ERR_ALIGN;
+        float *logits = logits_out;
+        if (!logits) {
+            if (!ws) return MOE_ERR_NULL;
+            if (!aligned16(ws)) return MOE_ERR_ALIGN;
+            if (ws_bytes < route_ws(D).total) return MOE_ERR_WORKSPACE;
+            logits = reinterpret_cast<float *>(static_cast<char *>(ws) + route_ws(D).logits);
+        }
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        hipError_t e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
+        if (e == hipSuccess) e = moe::launch_topk_softmax(logits, topk_ids, topk_w, D.T, D.E, D.k, s);
+        return device_status(e);
+    });
+}
+
+moe_status moe_permute(const moe_dims *dims, const int32_t *topk_ids, int32_t *counts,
+                       int32_t *offsets, int32_t *sorted_rows, int32_t *row_pos, void *ws,
+                       size_t ws_bytes, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (D.T == 0) return MOE_OK;
+        if (!topk_ids || !counts || !offsets || !sorted_rows || !row_pos) return MOE_ERR_NULL;
+        const size_t need = moe::permute_ws_bytes(D.T, D.E);
+        if (need) {
+            if (!ws) return MOE_ERR_NULL;
+            if (!aligned16(ws)) return MOE_ERR_ALIGN;
+            if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+        }
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        return device_status(moe::launch_permute(topk_ids, counts, offsets, sorted_rows, row_pos,
+                                                 nullptr, D.T, D.E, D.k, ws, s));
+    });
+}
+
+moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x,
+                          const moe_mxfp4_experts *experts, const int32_t *offsets,
+                          const int32_t *sorted_rows, uint16_t *rows_out, void *ws,
+                          size_t ws_bytes, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (D.T == 0) return MOE_OK;
+        if (!x || !offsets || !sorted_rows || !rows_out) return MOE_ERR_NULL;
+        if ((st = check_experts(experts)) != MOE_OK) return st;
+        if (!aligned16(x) || !aligned16(rows_out)) return MOE_ERR_ALIGN;
+        const FfnWs L = ffn_ws(D);
+        if (!ws) return MOE_ERR_NULL;
+        if (!aligned16(ws)) return MOE_ERR_ALIGN;
+        if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+        char *base = static_cast<char *>(ws);
+        int32_t *plan = reinterpret_cast<int32_t *>(base + L.plan);
+        float *h = reinterpret_cast<float *>(base + L.h);
+        const ExpertArgs W{experts->gu_codes, experts->gu_scales, experts->dn_codes,
+                           experts->dn_scales};
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        hipError_t e = moe::launch_plan(offsets, plan, D.E, s);
+        if (e == hipSuccess)
+            e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
+                                         D.f, s);
+        if (e == hipSuccess)
+            e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f, s);
+        return device_status(e);
+    });
+}
+
+moe_status moe_combine(const moe_dims *dims, const uint16_t *rows_out, const int32_t *row_pos,
+                       const float *topk_w, uint16_t *y, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (D.T == 0) return MOE_OK;
+        if (!rows_out || !row_pos || !topk_w || !y) return MOE_ERR_NULL;
+        if (!aligned16(rows_out) || !aligned16(y)) return MOE_ERR_ALIGN;
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        return device_status(moe::launch_combine(rows_out, row_pos, topk_w, y, D.T, D.d, D.k, s));
+    });
+}
+
+moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint16_t *router_w,
+                             const float *router_bias, const moe_mxfp4_experts *experts,
+                             uint16_t *y, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                             size_t ws_bytes, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (D.T == 0) return MOE_OK;
+        if (!x || !router_w || !y) return MOE_ERR_NULL;
+        if ((st = check_experts(experts)) != MOE_OK) return st;
+        if (!aligned16(x) || !aligned16(router_w) || !aligned16(y)) return MOE_ERR_ALIGN;
+        const LayerWs L = layer_ws(D);
+        if (!ws) return MOE_ERR_NULL;
+        if (!aligned16(ws)) return MOE_ERR_ALIGN;
+        if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+        char *base = static_cast<char *>(ws);
+        float *logits = reinterpret_cast<float *>(base + L.logits);
+        int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(base + L.ids);
+        float *tw = topk_w_out ? topk_w_out : reinterpret_cast<float *>(base + L.tw);
+        int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
+        int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+        int32_t *sorted_rows = reinterpret_cast<int32_t *>(base + L.sorted_rows);
+        int32_t *row_pos = reinterpret_cast<int32_t *>(base + L.row_pos);
+        void *perm_ws = base + L.perm;
+        const FfnWs F = ffn_ws(D);
+        int32_t *plan = reinterpret_cast<int32_t *>(base + L.ffn + F.plan);
+        float *h = reinterpret_cast<float *>(base + L.ffn + F.h);
+        uint16_t *rows_out = reinterpret_cast<uint16_t *>(base + L.rows_out);
+        const ExpertArgs W{experts->gu_codes, experts->gu_scales, experts->dn_codes,
+                           experts->dn_scales};
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+
+        hipError_t e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
+        if (e == hipSuccess) e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
+        if (e == hipSuccess)
+            e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T, D.E,
+                                    D.k, perm_ws, s);
+        if (e == hipSuccess)
+            e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
+                                         D.f, s);
+        if (D.T <= kFuseMaxT) {
+            if (e == hipSuccess)
+                e = moe::launch_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E, D.k, D.f, s);
+        } else {
+            if (e == hipSuccess)
+                e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f,
+                                          s);
+            if (e == hipSuccess) e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
+        }
+        return device_status(e);
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// moe_internal.hpp -- device helpers and kernel-launch declarations shared
+// by the gfx950 kernels of the routed MXFP4 MoE layer and its C ABI.
+//
+// Nothing here is visible through include/moe.h; the ABI file validates
+// arguments and then calls the launch_* functions below, all of which queue
+// work on the given stream and return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Fixed limits of this build (checked on the host before any launch).
+// ---------------------------------------------------------------------------
+constexpr int kMaxExperts = 1024;   // top-k keeps <= 16 logits per lane
+constexpr int kMaxTopK = 32;
+constexpr int kPermTokensPerBlock = 1024;   // 16 sub-blocks of 64 tokens
+constexpr int kPermSub = kPermTokensPerBlock / 64;
+
+// ---------------------------------------------------------------------------
+// Small device helpers.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// x * 2^(code - 127) for an E8M0 scale code; code 255 is NaN.  ldexp keeps
+// the result exact down to fp32 subnormals (code 0 is 2^-127).
+__device__ __forceinline__ float apply_e8m0(float x, uint32_t code) {
+    return code == 255u ? __uint_as_float(0x7FC00000u) : ldexpf(x, (int)code - 127);
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) v += __shfl_xor(v, w, 64);
+    return v;
+}
+
+// Sum over the 16 lanes of a lane group (lanes 16g .. 16g+15).
+__device__ __forceinline__ float group16_sum_f32(float v) {
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1) v += __shfl_xor(v, w, 64);
+    return v;
+}
+
+// Dot product of 8 E2M1 codes (one 32-bit word, element 2i in the low
+// nibble of byte i) with 8 bf16 values (four bf16x2 words), fp32 accumulate.
+__device__ __forceinline__ float dot8_fp4_bf16(uint32_t codes, uint4 xv, float acc) {
+    bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 0);
+    bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 1);
+    bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 2);
+    bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, 3);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(w0, __builtin_bit_cast(bf16x2_t, xv.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(w1, __builtin_bit_cast(bf16x2_t, xv.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(w2, __builtin_bit_cast(bf16x2_t, xv.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(w3, __builtin_bit_cast(bf16x2_t, xv.w), acc, false);
+    return acc;
+}
+
+// Dot product of 8 E2M1 codes with 8 fp32 values.
+__device__ __forceinline__ float dot8_fp4_f32(uint32_t codes, float4 a, float4 b, float acc) {
+    f32x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    f32x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    f32x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    f32x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    acc = fmaf(w0.x, a.x, acc); acc = fmaf(w0.y, a.y, acc);
+    acc = fmaf(w1.x, a.z, acc); acc = fmaf(w1.y, a.w, acc);
+    acc = fmaf(w2.x, b.x, acc); acc = fmaf(w2.y, b.y, acc);
+    acc = fmaf(w3.x, b.z, acc); acc = fmaf(w3.y, b.w, acc);
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (defined in the .hip files).  All pointers are device pointers.
+// ---------------------------------------------------------------------------
+hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const float *bias,
+                                float *logits, int T, int d, int E, hipStream_t s);
+hipError_t launch_topk_softmax(const float *logits, int32_t *ids, float *w, int T, int E,
+                               int k, hipStream_t s);
+
+size_t permute_ws_bytes(int T, int E);
+// plan (nullable): int32 [1 + E] = number of active experts, then their ids.
+hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
+                          int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, int T,
+                          int E, int k, void *ws, hipStream_t s);
+hipError_t launch_plan(const int32_t *offsets, int32_t *plan, int E, hipStream_t s);
+
+struct ExpertArgs {
+    const uint8_t *gu_codes, *gu_scales, *dn_codes, *dn_scales;
+};
+
+// h: fp32 [T*k][f], expert-major rows (the row order of sorted_rows).
+hipError_t launch_gemv_gate_up(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
+                               const int32_t *sorted_rows, const int32_t *plan, float *h,
+                               int T, int d, int E, int k, int f, hipStream_t s);
+hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets,
+                            const int32_t *plan, uint16_t *rows_out, int T, int d, int E,
+                            int k, int f, hipStream_t s);
+hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
+                               const float *topk_w, const int32_t *row_pos, uint16_t *y,
+                               int T, int d, int E, int k, int f, hipStream_t s);
+hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
+                          const float *topk_w, uint16_t *y, int T, int d, int k,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,238 @@
+"""Thin Python binding of the C ABI in ``include/moe.h``.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+of ``libmoe_mxfp4.so``.  Torch supplies device memory (outputs and
+workspace) and the current stream.  There is no fallback: if the compiled
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, 1, 2, 3
+MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = 4, 5, 6
+ENTRY_ROUTE, ENTRY_PERMUTE, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER_FORWARD = range(5)
+SIZE_MAX = (1 << 64) - 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_str(status)))
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("f", ctypes.c_int32)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("gu_codes", ctypes.c_void_p), ("gu_scales", ctypes.c_void_p),
+                ("dn_codes", ctypes.c_void_p), ("dn_scales", ctypes.c_void_p)]
+
+
+EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
+           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward")
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libmoe_mxfp4.so is not built (run `python -m routed_expert_mxfp4_amd.build`); "
+                "there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        DP = ctypes.POINTER(Dims)
+        EP = ctypes.POINTER(Experts)
+        L.moe_abi_version.restype = I
+        L.moe_abi_version.argtypes = []
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [I]
+        L.moe_workspace_bytes.restype = S
+        L.moe_workspace_bytes.argtypes = [DP, I]
+        L.moe_route.restype = I
+        L.moe_route.argtypes = [DP, P, P, P, P, P, P, P, S, P]
+        L.moe_permute.restype = I
+        L.moe_permute.argtypes = [DP, P, P, P, P, P, P, S, P]
+        L.moe_expert_ffn.restype = I
+        L.moe_expert_ffn.argtypes = [DP, P, EP, P, P, P, P, S, P]
+        L.moe_combine.restype = I
+        L.moe_combine.argtypes = [DP, P, P, P, P, P]
+        L.moe_layer_forward.restype = I
+        L.moe_layer_forward.argtypes = [DP, P, P, P, EP, P, P, P, P, S, P]
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def dims_of(T, d, E, k, f) -> Dims:
+    return Dims(int(T), int(d), int(E), int(k), int(f))
+
+
+def experts_of(w: dict) -> Experts:
+    return Experts(w["gu_codes"].data_ptr(), w["gu_scales"].data_ptr(),
+                   w["dn_codes"].data_ptr(), w["dn_scales"].data_ptr())
+
+
+def moe_workspace_bytes(dims: Dims, entry: int) -> int:
+    n = lib().moe_workspace_bytes(ctypes.byref(dims), int(entry))
+    if n == SIZE_MAX:
+        raise MoeError(MOE_ERR_SHAPE, "moe_workspace_bytes")
+    return n
+
+
+def workspace(dims: Dims, entry: int, device) -> torch.Tensor:
+    n = moe_workspace_bytes(dims, entry)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    assert t.dtype in (torch.bfloat16, torch.int16, torch.uint16), t.dtype
+    return t.contiguous()
+
+
+def moe_route(x, router_w, k, router_bias=None, want_logits=False, ws=None, stream=None):
+    """Router + top-k + softmax.  Returns (topk_ids int32 [T][k],
+    topk_w fp32 [T][k]) and, if ``want_logits``, the fp32 [T][E] logits."""
+    x, router_w = _bits16(x), _bits16(router_w)
+    T, d = x.shape
+    E = router_w.shape[0]
+    dims = dims_of(T, d, E, k, 32)
+    dev = x.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    if ws is None and not want_logits:
+        ws = workspace(dims, ENTRY_ROUTE, dev)
+    bias = None if router_bias is None else router_bias.contiguous().float()
+    st = lib().moe_route(ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(logits),
+                         _ptr(ids), _ptr(w), _ptr(ws), 0 if ws is None else ws.numel(),
+                         _stream(stream))
+    _check(st, "moe_route")
+    return (ids, w, logits) if want_logits else (ids, w)
+
+
+def moe_permute(topk_ids, E, ws=None, stream=None):
+    """Group rows by expert.  Returns (counts [E], offsets [E+1],
+    sorted_rows [T*k], row_pos [T*k]), all int32."""
+    topk_ids = topk_ids.contiguous()
+    T, k = topk_ids.shape
+    dims = dims_of(T, 64, E, k, 32)
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_rows = torch.empty(T * k, dtype=torch.int32, device=dev)
+    row_pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(dims, ENTRY_PERMUTE, dev)
+    st = lib().moe_permute(ctypes.byref(dims), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                           _ptr(sorted_rows), _ptr(row_pos), _ptr(ws), ws.numel(),
+                           _stream(stream))
+    _check(st, "moe_permute")
+    return counts, offsets, sorted_rows, row_pos
+
+
+def moe_expert_ffn(x, experts: dict, offsets, sorted_rows, k, ws=None, stream=None):
+    """Expert FFN over grouped rows.  Returns rows_out bf16 [T*k][d]."""
+    x = _bits16(x)
+    T, d = x.shape
+    E, two_f = experts["gu_codes"].shape[:2]
+    dims = dims_of(T, d, E, k, two_f // 2)
+    rows_out = torch.empty((T * k, d), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = workspace(dims, ENTRY_EXPERT_FFN, x.device)
+    ex = experts_of(experts)
+    st = lib().moe_expert_ffn(ctypes.byref(dims), _ptr(x), ctypes.byref(ex), _ptr(offsets),
+                              _ptr(sorted_rows), _ptr(rows_out), _ptr(ws), ws.numel(),
+                              _stream(stream))
+    _check(st, "moe_expert_ffn")
+    return rows_out
+
+
+def moe_combine(rows_out, row_pos, topk_w, stream=None):
+    """Weighted combine.  Returns y bf16 [T][d]."""
+    rows_out = _bits16(rows_out)
+    T, k = topk_w.shape
+    d = rows_out.shape[1]
+    dims = dims_of(T, d, max(k, 1), k, 32)
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=rows_out.device)
+    st = lib().moe_combine(ctypes.byref(dims), _ptr(rows_out), _ptr(row_pos.contiguous()),
+                           _ptr(topk_w.contiguous()), _ptr(y), _stream(stream))
+    _check(st, "moe_combine")
+    return y
+
+
+class Layer:
+    """Holds device pointers, dims and a reusable workspace for repeated
+    ``moe_layer_forward`` calls (the benchmark's hot loop)."""
+
+    def __init__(self, experts: dict, router_w, k, router_bias=None, T=1):
+        self.experts = experts
+        self.router_w = _bits16(router_w)
+        self.bias = None if router_bias is None else router_bias.contiguous().float()
+        self.E, self.d = self.router_w.shape
+        self.f = experts["gu_codes"].shape[1] // 2
+        self.k = k
+        self._ex = experts_of(experts)
+        self._ws = None
+        self._ws_T = -1
+        self.reserve(T)
+
+    def reserve(self, T):
+        if T > self._ws_T:
+            dims = dims_of(T, self.d, self.E, self.k, self.f)
+            self._ws = workspace(dims, ENTRY_LAYER_FORWARD, self.router_w.device)
+            self._ws_T = T
+
+    def forward(self, x, y=None, topk_ids=None, topk_w=None, stream=None):
+        T = x.shape[0]
+        self.reserve(T)
+        if y is None:
+            y = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
+        dims = dims_of(T, self.d, self.E, self.k, self.f)
+        st = lib().moe_layer_forward(ctypes.byref(dims), _ptr(x), _ptr(self.router_w),
+                                     _ptr(self.bias), ctypes.byref(self._ex), _ptr(y),
+                                     _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
+                                     self._ws.numel(), _stream(stream))
+        _check(st, "moe_layer_forward")
+        return y
+
+
+def moe_layer_forward(x, router_w, experts: dict, k, router_bias=None, return_routing=False,
+                      stream=None):
+    """The whole layer.  Returns y bf16 [T][d] (and topk_ids, topk_w)."""
+    x = _bits16(x)
+    T = x.shape[0]
+    layer = Layer(experts, router_w, k, router_bias, T=T)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
+    y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)
+    return (y, ids, w) if return_routing else y

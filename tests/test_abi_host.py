@@ -1,0 +1,128 @@
+"""CPU-side checks of the C ABI library: it loads, exports every symbol that
+include/moe.h declares, sizes workspaces, and refuses bad arguments on the
+host before any launch (no GPU is touched: every call here fails validation
+or has T = 0)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from routed_expert_mxfp4_amd import build as hipbuild
+from routed_expert_mxfp4_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hipbuild.LIB_PATH):
+        hipbuild.build()
+    return moe.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _declared_functions()
+    assert set(declared) == set(moe.EXPORTS), declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.moe_abi_version() == 1
+
+
+def test_status_strings(L):
+    for s in range(7):
+        txt = moe.status_str(s)
+        assert txt and "unknown" not in txt
+    assert "unknown" in moe.status_str(99)
+
+
+def _dims(T=8, d=256, E=16, k=2, f=128):
+    return moe.dims_of(T, d, E, k, f)
+
+
+def test_workspace_sizes(L):
+    for entry in range(5):
+        n = moe.moe_workspace_bytes(_dims(), entry)
+        assert 0 <= n < 1 << 40
+    # the big prefill shape fits comfortably in one GPU's HBM
+    big = moe.moe_workspace_bytes(_dims(32768, 7168, 896, 16, 1536), moe.ENTRY_LAYER_FORWARD)
+    assert big < 16 * 2 ** 30
+    assert L.moe_workspace_bytes(ctypes.byref(_dims()), 17) == moe.SIZE_MAX
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_bytes(_dims(d=100), 0)
+
+
+@pytest.mark.parametrize("bad", [dict(d=100), dict(d=0), dict(f=48), dict(E=0), dict(E=2000),
+                                 dict(k=0), dict(k=17, E=16), dict(k=33, E=64), dict(T=-1),
+                                 dict(T=1 << 27, k=16), dict(d=65536)])
+def test_bad_shapes_refused(L, bad):
+    dims = _dims(**bad)
+    P = ctypes.c_void_p(0x1000)
+    ex = moe.Experts(0x1000, 0x1000, 0x1000, 0x1000)
+    st = L.moe_layer_forward(ctypes.byref(dims), P, P, None, ctypes.byref(ex), P, None, None,
+                             P, 1 << 40, None)
+    assert st == moe.MOE_ERR_SHAPE
+    st = L.moe_route(ctypes.byref(dims), P, P, None, P, P, P, None, 0, None)
+    assert st == moe.MOE_ERR_SHAPE
+
+
+def test_null_and_alignment_refused(L):
+    dims = _dims()
+    A = ctypes.c_void_p(0x10000)
+    M = ctypes.c_void_p(0x10008)          # 8-byte aligned only
+    ex = moe.Experts(0x10000, 0x10000, 0x10000, 0x10000)
+    exm = moe.Experts(0x10000, 0x10008, 0x10000, 0x10000)
+    exn = moe.Experts(0x10000, None, 0x10000, 0x10000)
+    big = 1 << 40
+    f = L.moe_layer_forward
+    assert f(None, A, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), None, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), A, A, None, None, A, None, None, A, big, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(exn), A, None, None, A, big, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), M, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_ALIGN
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(exm), A, None, None, A, big, None) == moe.MOE_ERR_ALIGN
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(ex), A, None, None, None, big, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(ex), A, None, None, M, big, None) == moe.MOE_ERR_ALIGN
+    need = moe.moe_workspace_bytes(dims, moe.ENTRY_LAYER_FORWARD)
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(ex), A, None, None, A, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    # route: logits buffer or workspace required
+    r = L.moe_route
+    assert r(ctypes.byref(dims), A, A, None, None, A, A, None, 0, None) == moe.MOE_ERR_NULL
+    assert r(ctypes.byref(dims), A, A, None, None, A, A, A, 1, None) == moe.MOE_ERR_WORKSPACE
+    assert r(ctypes.byref(dims), A, A, None, A, None, A, None, 0, None) == moe.MOE_ERR_NULL
+    # permute / ffn / combine
+    p = L.moe_permute
+    assert p(ctypes.byref(dims), None, A, A, A, A, None, 0, None) == moe.MOE_ERR_NULL
+    big_dims = _dims(T=4096, d=7168, E=896, k=16, f=1536)
+    assert p(ctypes.byref(big_dims), A, A, A, A, A, None, 0, None) == moe.MOE_ERR_NULL
+    assert p(ctypes.byref(big_dims), A, A, A, A, A, A, 16, None) == moe.MOE_ERR_WORKSPACE
+    e = L.moe_expert_ffn
+    assert e(ctypes.byref(dims), A, ctypes.byref(ex), A, A, A, None, 0, None) == moe.MOE_ERR_NULL
+    assert e(ctypes.byref(dims), A, ctypes.byref(ex), A, A, M, A, big, None) == moe.MOE_ERR_ALIGN
+    assert e(ctypes.byref(dims), A, ctypes.byref(ex), A, A, A, A, 16, None) == moe.MOE_ERR_WORKSPACE
+    c = L.moe_combine
+    assert c(ctypes.byref(dims), A, A, A, None, None) == moe.MOE_ERR_NULL
+    assert c(ctypes.byref(dims), M, A, A, A, None) == moe.MOE_ERR_ALIGN
+
+
+def test_zero_tokens_is_a_no_op(L):
+    dims = _dims(T=0)
+    ex = moe.Experts(0x10000, 0x10000, 0x10000, 0x10000)
+    # nothing is validated beyond the dims and nothing is launched
+    assert L.moe_layer_forward(ctypes.byref(dims), None, None, None, ctypes.byref(ex), None,
+                               None, None, None, 0, None) == moe.MOE_OK
+    assert L.moe_permute(ctypes.byref(dims), None, None, None, None, None, None, 0, None) == moe.MOE_OK
+    assert L.moe_combine(ctypes.byref(dims), None, None, None, None, None) == moe.MOE_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        moe.lib()

@@ -1,0 +1,302 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle.
+
+Bar: routing ids, logits, counts, offsets, sorted_rows and row_pos bit-exact;
+routing weights within 1e-5 (and summing to 1 within 1e-6); expert rows and
+layer outputs within max|gpu - oracle| <= 1e-2 * max|oracle| (fp32
+accumulation, bf16 in and out).  Inputs come from the seeded generator;
+expected values come from the oracle only.
+"""
+import concurrent.futures as cf
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from routed_expert_mxfp4_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+W_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from routed_expert_mxfp4_amd import moe
+    moe.lib()              # raises if the HIP library is missing: no fallback
+    return torch.device("cuda:0")
+
+
+def _moe():
+    from routed_expert_mxfp4_amd import moe
+    return moe
+
+
+def _np_experts(L):
+    return {n: L[n].cpu().numpy() for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")}
+
+
+def _dev_experts(L, dev):
+    return {n: L[n].to(dev).contiguous() for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")}
+
+
+def _bf16_to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _close(gpu, ref, what):
+    err = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    assert err <= TOL * scale, "%s: max err %.4g > %.0e * %.4g" % (what, err, TOL, scale)
+    return err, scale
+
+
+def _small_cfg(T, d, E, k, f, seed):
+    return synth.Config(100 + seed, "case", T, d, E, k, f, seed=seed)
+
+
+def _oracle_o_rows(x_u16, ids, W, d, f):
+    """Oracle expert outputs o[t][j][:] for every (token, slot)."""
+    T, k = ids.shape
+    o = np.zeros((T, k, d))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            _, o[t, j] = oracle.expert_row(x_u16[t], W["gu_codes"][e], W["gu_scales"][e],
+                                           W["dn_codes"][e], W["dn_scales"][e], d, f)
+    return o
+
+
+SMALL_CASES = [
+    # (T, d, E, k, f, seed)
+    (8, 256, 16, 2, 128, 0),        # the tiny workload
+    (1, 256, 16, 2, 128, 11),
+    (3, 192, 40, 5, 64, 12),        # odd chunk length (d/64 = 3), E not a multiple of 64
+    (5, 128, 7, 7, 32, 13),         # k = E, a single MX block along f
+    (17, 512, 70, 1, 96, 14),       # k = 1, ragged T
+    (300, 128, 24, 3, 64, 15),      # T > 256: multi-block grouping
+    (70, 64, 130, 4, 32, 16),       # E > 128
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[str(c) for c in SMALL_CASES])
+def test_entry_points_small(dev, case):
+    moe = _moe()
+    T, d, E, k, f, seed = case
+    cfg = synth.CONFIGS[0] if seed == 0 else _small_cfg(T, d, E, k, f, seed)
+    print("case", case, flush=True)
+    L = synth.gen_layer(cfg)
+    x16, wr16 = synth.as_u16(L["x"]), synth.as_u16(L["router_w"])
+    W = _np_experts(L)
+    # --- oracle
+    lg = oracle.router_logits(x16, wr16)
+    ids_o, w_o = oracle.topk_softmax(lg, k)
+    counts_o, offsets_o, sr_o, rp_o = oracle.permute(ids_o, E)
+    o_rows = _oracle_o_rows(x16, ids_o, W, d, f)
+    y_o = np.einsum("tj,tjd->td", w_o, o_rows)
+    # --- GPU, entry by entry
+    x, wr = L["x"].to(dev), L["router_w"].to(dev)
+    ex = _dev_experts(L, dev)
+    ids, w, logits = moe.moe_route(x, wr, k, want_logits=True)
+    counts, offsets, sr, rp = moe.moe_permute(ids, E)
+    rows_out = moe.moe_expert_ffn(x, ex, offsets, sr, k)
+    y = moe.moe_combine(rows_out, rp, w)
+    torch.cuda.synchronize()
+    assert (logits.cpu().numpy().view(np.uint32) == lg.view(np.uint32)).all(), "logits not bit-exact"
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    wg = w.cpu().numpy()
+    assert np.abs(wg - w_o).max() <= W_TOL
+    assert np.abs(wg.astype(np.float64).sum(1) - 1).max() <= 1e-6
+    np.testing.assert_array_equal(counts.cpu().numpy(), counts_o)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), offsets_o)
+    np.testing.assert_array_equal(sr.cpu().numpy(), sr_o)
+    np.testing.assert_array_equal(rp.cpu().numpy(), rp_o)
+    # rows_out is expert-major: position p holds row sr_o[p]
+    o_sorted = o_rows.reshape(T * k, d)[sr_o]
+    _close(_bf16_to_f64(rows_out), o_sorted, "rows_out")
+    _close(_bf16_to_f64(y), y_o, "combine y")
+    # --- fused entry
+    y2, ids2, w2 = moe.moe_layer_forward(x, wr, ex, k, return_routing=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids2.cpu().numpy(), ids_o)
+    assert np.abs(w2.cpu().numpy() - w_o).max() <= W_TOL
+    _close(_bf16_to_f64(y2), y_o, "layer_forward y")
+
+
+def test_router_bias_and_ties(dev):
+    moe = _moe()
+    cfg = _small_cfg(12, 256, 48, 6, 64, 21)
+    x = synth.gen_x(cfg)
+    wr = synth.gen_router_w(cfg).clone()
+    wr[20] = wr[3]                       # equal logits: lower index first
+    wr[33] = wr[3]
+    bias = torch.linspace(-0.5, 0.5, cfg.E, dtype=torch.float32)
+    bias[20] = bias[3]
+    bias[33] = bias[3]
+    lg = oracle.router_logits(synth.as_u16(x), synth.as_u16(wr), bias.numpy())
+    ids_o, w_o = oracle.topk_softmax(lg, cfg.k)
+    ids, w, logits = moe.moe_route(x.to(dev), wr.to(dev), cfg.k, router_bias=bias.to(dev),
+                                   want_logits=True)
+    torch.cuda.synchronize()
+    assert (logits.cpu().numpy().view(np.uint32) == lg.view(np.uint32)).all()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    assert np.abs(w.cpu().numpy() - w_o).max() <= W_TOL
+    # full ranking with ties
+    ids_f, _ = oracle.topk_softmax(lg, 32)
+    ids_g, _ = moe.moe_route(x.to(dev), wr.to(dev), 32, router_bias=bias.to(dev))
+    np.testing.assert_array_equal(ids_g.cpu().numpy(), ids_f)
+
+
+def test_permute_synthetic_ids_full_size(dev):
+    # grouping of the long-prefill shape, from seeded ids with a skewed
+    # expert distribution (independent of the router)
+    moe = _moe()
+    T, E, k = 32768, 896, 16
+    rng = np.random.default_rng(5)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    ids_np = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    counts_o, offsets_o, sr_o, rp_o = oracle.permute(ids_np, E)
+    counts, offsets, sr, rp = moe.moe_permute(torch.from_numpy(ids_np).to(dev), E)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(counts.cpu().numpy(), counts_o)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), offsets_o)
+    np.testing.assert_array_equal(sr.cpu().numpy(), sr_o)
+    np.testing.assert_array_equal(rp.cpu().numpy(), rp_o)
+
+
+def test_all_zero_experts_exact_zero(dev):
+    moe = _moe()
+    cfg = _small_cfg(6, 256, 8, 2, 64, 31)
+    L = synth.gen_layer(cfg)
+    g = torch.Generator().manual_seed(0)
+    for n in ("gu_codes", "dn_codes"):
+        lo = torch.randint(0, 2, L[n].shape, generator=g, dtype=torch.uint8) * 8
+        hi = torch.randint(0, 2, L[n].shape, generator=g, dtype=torch.uint8) * 8
+        L[n] = lo | (hi << 4)
+    y = moe.moe_layer_forward(L["x"].to(dev), L["router_w"].to(dev), _dev_experts(L, dev), cfg.k)
+    torch.cuda.synchronize()
+    assert (y.float() == 0).all()
+
+
+def test_scale_plus_one_doubles_expert_output_exactly(dev):
+    moe = _moe()
+    cfg = _small_cfg(9, 256, 12, 3, 64, 41)
+    L = synth.gen_layer(cfg)
+    x, wr = L["x"].to(dev), L["router_w"].to(dev)
+    ids, w = moe.moe_route(x, wr, cfg.k)
+    counts, offsets, sr, rp = moe.moe_permute(ids, cfg.E)
+    base = moe.moe_expert_ffn(x, _dev_experts(L, dev), offsets, sr, cfg.k).clone()
+    e = int(ids[0, 0])
+    lo, hi = int(offsets[e]), int(offsets[e + 1])
+    for variant in ("down", "up"):
+        L2 = dict(L)
+        if variant == "down":
+            L2["dn_scales"] = L["dn_scales"].clone()
+            L2["dn_scales"][e] += 1
+        else:
+            L2["gu_scales"] = L["gu_scales"].clone()
+            L2["gu_scales"][e, cfg.f:] += 1
+        out = moe.moe_expert_ffn(x, _dev_experts(L2, dev), offsets, sr, cfg.k)
+        torch.cuda.synchronize()
+        assert torch.equal(out[lo:hi].float(), 2 * base[lo:hi].float()), variant
+        mask = torch.ones(out.shape[0], dtype=torch.bool, device=dev)
+        mask[lo:hi] = False
+        assert torch.equal(out[mask], base[mask])
+
+
+def test_deterministic_run_twice(dev):
+    moe = _moe()
+    cfg = _small_cfg(40, 512, 64, 8, 128, 51)
+    L = synth.gen_layer(cfg)
+    x, wr, ex = L["x"].to(dev), L["router_w"].to(dev), _dev_experts(L, dev)
+    a = moe.moe_layer_forward(x, wr, ex, cfg.k, return_routing=True)
+    b = moe.moe_layer_forward(x, wr, ex, cfg.k, return_routing=True)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_token_permutation_permutes_outputs(dev):
+    moe = _moe()
+    cfg = _small_cfg(16, 256, 32, 4, 64, 61)
+    L = synth.gen_layer(cfg)
+    x, wr, ex = L["x"].to(dev), L["router_w"].to(dev), _dev_experts(L, dev)
+    perm = torch.randperm(cfg.T, generator=torch.Generator().manual_seed(1)).to(dev)
+    y = moe.moe_layer_forward(x, wr, ex, cfg.k)
+    yp = moe.moe_layer_forward(x[perm].contiguous(), wr, ex, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, y[perm])
+
+
+def _decode_parity(dev, cfg, batch, tokens):
+    """Full-size layer: routing of ``tokens`` bit-exact and y within
+    tolerance, against the oracle on just the experts those tokens use."""
+    moe = _moe()
+    x_cpu = synth.gen_x(cfg, batch)
+    wr_cpu = synth.gen_router_w(cfg)
+    bias = synth.gen_bias(cfg)
+    x16, wr16 = synth.as_u16(x_cpu), synth.as_u16(wr_cpu)
+    ex = _FULL[cfg.index]
+    y, ids, w = moe.moe_layer_forward(x_cpu.to(dev), wr_cpu.to(dev), ex, cfg.k,
+                                      router_bias=None if bias is None else bias.to(dev),
+                                      return_routing=True)
+    torch.cuda.synchronize()
+    sel = x16[tokens]
+    lg = oracle.router_logits(sel, wr16, None if bias is None else bias.numpy())
+    ids_o, w_o = oracle.topk_softmax(lg, cfg.k)
+    np.testing.assert_array_equal(ids.cpu().numpy()[tokens], ids_o)
+    assert np.abs(w.cpu().numpy()[tokens] - w_o).max() <= W_TOL
+    need = sorted(set(ids_o.ravel().tolist()))
+    Wn = {n: v.numpy() for n, v in synth.gen_experts(cfg, experts=need).items()}
+    remap = {e: i for i, e in enumerate(need)}
+    yg = _bf16_to_f64(y)
+
+    def row(ij):
+        i, j = ij
+        r = remap[int(ids_o[i, j])]
+        return oracle.expert_row(sel[i], Wn["gu_codes"][r], Wn["gu_scales"][r],
+                                 Wn["dn_codes"][r], Wn["dn_scales"][r], cfg.d, cfg.f)[1]
+
+    # the oracle's C code releases the GIL: rows run in parallel threads
+    jobs = [(i, j) for i in range(len(tokens)) for j in range(cfg.k)]
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as pool:
+        outs = list(pool.map(row, jobs))
+    for i, t in enumerate(tokens):
+        o = np.stack(outs[i * cfg.k:(i + 1) * cfg.k])
+        y_o, _ = oracle.combine_token(w_o[i], o)
+        _close(yg[t], y_o, "token %d" % t)
+    return ids
+
+
+_FULL = {}
+
+
+@pytest.fixture(scope="module")
+def full_experts(dev):
+    def get(index):
+        if index not in _FULL:
+            _FULL.clear()
+            torch.cuda.empty_cache()
+            _FULL[index] = synth.gen_experts(synth.CONFIGS[index], device=dev)
+        return _FULL[index]
+    yield get
+    _FULL.clear()
+
+
+def test_decode_full_size(dev, full_experts):
+    cfg = synth.CONFIGS[1]
+    full_experts(1)
+    for batch in (0, 1, 999):
+        print("decode token", batch, flush=True)
+        _decode_parity(dev, cfg, batch, [0])
+
+
+def test_batched_decode_full_size(dev, full_experts):
+    cfg = synth.CONFIGS[2]
+    full_experts(2)
+    _decode_parity(dev, cfg, 0, [0, 37, 63])
