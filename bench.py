@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of one routed MoE FFN layer with MXFP4 experts on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+Default workload: one-token decode (T=1, d=7168, E=896 experts, top-16,
+f=1536) over 1000 distinct seeded tokens; one step = one moe_layer_forward
+call on one token (router, top-k, grouping, gate/up + SwiGLU, down,
+combine), cycling through the tokens so that no token is timed twice in a
+row.  Inputs are synthetic and resident in HBM before timing starts.
+
+Prints one JSON line: throughput (tokens/s), the roofline of the dominant
+kernel (HIP events on the library's own stream inside the timed region),
+and the CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+WORKLOADS = {"tiny": 0, "decode": 1, "batched-decode": 2, "zipf-prefill": 3, "long-prefill": 4}
+DOMINANT = "gemv_gate_up"
+KERNELS = ("router_logits", "topk_softmax", "permute", "gemv_gate_up", "down_combine",
+           "gemv_down", "combine")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--cpu-sample", type=int, default=2,
+                    help="tokens of the workload the CPU oracle runs (0: skip)")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel timing passes after the timed region")
+    return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def usable_cores():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def traffic_from_profiles(kernel: str, workload: str, src_sha: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the kernel source as it is now; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != src_sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, n_tokens):
+    """The oracle, as it stands, on the first n_tokens tokens of the workload:
+    router + top-k over all experts, the k expert rows (in parallel threads,
+    the C code releases the GIL), combine.  Weight generation is excluded."""
+    import numpy as np
+    import oracle
+    from routed_expert_mxfp4_amd import synth
+    wr16 = synth.as_u16(synth.gen_router_w(cfg))
+    bias = synth.gen_bias(cfg)
+    bias_np = None if bias is None else bias.numpy()
+    threads = usable_cores()
+    spent = 0.0
+    tokens = 0
+    with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        for n in range(n_tokens):
+            batch, t = (n, 0) if cfg.T == 1 else (0, n)
+            x16 = synth.as_u16(synth.gen_x(cfg, batch, tokens=[t]))
+            t0 = time.perf_counter()
+            lg = oracle.router_logits(x16, wr16, bias_np)
+            ids, w = oracle.topk_softmax(lg, cfg.k)
+            spent += time.perf_counter() - t0
+            need = [int(e) for e in ids[0]]
+            W = {k: v.numpy() for k, v in synth.gen_experts(cfg, experts=need).items()}
+
+            def row(j):
+                return oracle.expert_row(x16[0], W["gu_codes"][j], W["gu_scales"][j],
+                                         W["dn_codes"][j], W["dn_scales"][j], cfg.d, cfg.f)[1]
+            t0 = time.perf_counter()
+            o = np.stack(list(pool.map(row, range(cfg.k))))
+            oracle.combine_token(w[0], o)
+            spent += time.perf_counter() - t0
+            tokens += 1
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": min(threads, cfg.k),
+            "kind": "oracle",
+            "sample": "%d token(s) of the %s workload, all %d expert rows each, oracle "
+                      "(plain C, fp64) on %s" % (tokens, cfg.name, cfg.k, cpu_model()),
+            "seconds": spent}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py runs on one GPU only: the multi-GPU (expert-parallel) path is "
+                  "not built; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from routed_expert_mxfp4_amd import moe, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[WORKLOADS[args.workload]]
+    L = moe.lib()
+
+    # ---- inputs, resident in HBM before timing --------------------------------
+    experts = synth.gen_experts(cfg, device=dev)
+    wr = synth.gen_router_w(cfg).to(dev)
+    bias = synth.gen_bias(cfg)
+    bias = None if bias is None else bias.to(dev)
+    n_batches = min(cfg.batches, max(1, args.steps + args.warmup))
+    xs = [synth.gen_x(cfg, b).to(dev) for b in range(n_batches)]
+    layer = moe.Layer(experts, wr, cfg.k, bias, T=cfg.T)
+    y = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    dims = moe.dims_of(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f)
+    ex = moe.experts_of(experts)
+    ws = layer._ws
+    argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(wr.data_ptr()),
+                None if bias is None else ctypes.c_void_p(bias.data_ptr()), ctypes.byref(ex),
+                ctypes.c_void_p(y.data_ptr()), None, None, ctypes.c_void_p(ws.data_ptr()),
+                ws.numel(), sptr) for x in xs]
+    fwd = L.moe_layer_forward
+
+    def run(n0, count):
+        for i in range(count):
+            st = fwd(*argsets[(n0 + i) % n_batches])
+            if st != 0:
+                raise moe.MoeError(st, "moe_layer_forward")
+
+    run(0, args.warmup)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, dominant kernel timed with HIP events ------------
+    moe.diag_time_kernel(DOMINANT, capacity=max(1, args.steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom_ms, dom_n = moe.diag_kernel_time()
+    moe.diag_time_kernel(None, 0)
+    elapsed = t1 - t0
+
+    # ---- per-kernel breakdown (separate passes, outside the timed region) -------
+    breakdown = {}
+    if not args.no_breakdown:
+        for kname in KERNELS:
+            moe.diag_time_kernel(kname, capacity=max(1, args.steps))
+            run(args.warmup, args.steps)
+            torch.cuda.synchronize()
+            ms, n = moe.diag_kernel_time()
+            if n:
+                breakdown[kname] = {"avg_us": 1e3 * ms / n, "launches": n}
+        moe.diag_time_kernel(None, 0)
+        t2 = time.perf_counter()
+        run(args.warmup, args.steps)
+        torch.cuda.synchronize()
+        breakdown["steps_without_events_ms_per_step"] = 1e3 * (time.perf_counter() - t2) / args.steps
+
+    # ---- algorithmic work ------------------------------------------------------------
+    ids_probe = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    per_expert_gu = 2 * cfg.f * (cfg.d // 2) + 2 * cfg.f * (cfg.d // 32)
+    touched = []
+    for b in range(min(n_batches, 64)):
+        layer.forward(xs[b], y=y, topk_ids=ids_probe)
+        touched.append(torch.unique(ids_probe).numel())
+    torch.cuda.synchronize()
+    mean_touched = sum(touched) / len(touched)
+    bytes_per_launch = mean_touched * per_expert_gu
+    avg_launch_s = (dom_ms / dom_n) * 1e-3 if dom_n else float("nan")
+    achieved = bytes_per_launch / avg_launch_s / 1e9
+    src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_gemv.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    traffic = traffic_from_profiles(DOMINANT, args.workload, sha)
+
+    tokens = args.steps * cfg.T
+    value = tokens / elapsed
+    layer_bytes = mean_touched * cfg.expert_bytes
+    out = {
+        "metric": "MoE-layer tokens/s + expert-weight GB/s (decode) / MXFP4 TFLOP/s (prefill), 1 GPU",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "f": cfg.f, "distinct_batches": n_batches,
+                   "weights": "MXFP4 (E2M1 codes + E8M0 scale per 32), resident in HBM",
+                   "activations": "bf16", "accumulate": "fp32"},
+        "expert_weight_GBps": layer_bytes * args.steps / elapsed / 1e9,
+        "expert_weight_hbm_frac": layer_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBPS,
+        "tflops": 2.0 * tokens * cfg.k * 3 * cfg.d * cfg.f / elapsed / 1e12,
+        "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n},
+        "cpu_baseline": None,
+        "breakdown": breakdown,
+    }
+    if args.cpu_sample > 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

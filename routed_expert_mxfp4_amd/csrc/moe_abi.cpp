@@ -5,10 +5,16 @@
 // (a refused request leaves the outputs untouched), never allocates, never
 // synchronises the host with the device, and never lets a C++ exception out.
 #include "../../include/moe.h"
+#include "../../include/moe_diag.h"
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
 
 #include "moe_internal.hpp"
 
@@ -89,6 +95,40 @@ LayerWs layer_ws(const moe_dims &D) {
     return w;
 }
 
+// ---- diagnostics: HIP events around the launches of one named kernel ------
+struct Diag {
+    std::mutex mu;
+    std::atomic<bool> active{false};
+    std::string name;
+    std::vector<hipEvent_t> ev;       // [2 * capacity]: start, stop pairs
+    int used = 0;
+};
+Diag g_diag;
+
+// Records a start event before and a stop event after one launch when that
+// kernel is being timed.  When timing is off the cost is one atomic load.
+class DiagScope {
+  public:
+    DiagScope(const char *kernel, hipStream_t s) : s_(s) {
+        if (!g_diag.active.load(std::memory_order_acquire)) return;
+        std::lock_guard<std::mutex> lk(g_diag.mu);
+        if (g_diag.name != kernel || 2 * (g_diag.used + 1) > (int)g_diag.ev.size()) return;
+        hipEvent_t start = g_diag.ev[2 * g_diag.used];
+        stop_ = g_diag.ev[2 * g_diag.used + 1];
+        ++g_diag.used;
+        (void)hipEventRecord(start, s_);
+    }
+    ~DiagScope() {
+        if (stop_) (void)hipEventRecord(stop_, s_);
+    }
+    DiagScope(const DiagScope &) = delete;
+    DiagScope &operator=(const DiagScope &) = delete;
+
+  private:
+    hipStream_t s_;
+    hipEvent_t stop_ = nullptr;
+};
+
 template <typename Fn>
 moe_status guarded(Fn fn) {
     try {
@@ -148,8 +188,15 @@ moe_status moe_route(const moe_dims *dims, const uint16_t *x, const uint16_t *ro
             logits = reinterpret_cast<float *>(static_cast<char *>(ws) + route_ws(D).logits);
         }
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        hipError_t e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
-        if (e == hipSuccess) e = moe::launch_topk_softmax(logits, topk_ids, topk_w, D.T, D.E, D.k, s);
+        hipError_t e;
+        {
+            DiagScope t("router_logits", s);
+            e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
+        }
+        if (e == hipSuccess) {
+            DiagScope t("topk_softmax", s);
+            e = moe::launch_topk_softmax(logits, topk_ids, topk_w, D.T, D.E, D.k, s);
+        }
         return device_status(e);
     });
 }
@@ -170,6 +217,7 @@ moe_status moe_permute(const moe_dims *dims, const int32_t *topk_ids, int32_t *c
             if (ws_bytes < need) return MOE_ERR_WORKSPACE;
         }
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        DiagScope t("permute", s);
         return device_status(moe::launch_permute(topk_ids, counts, offsets, sorted_rows, row_pos,
                                                  nullptr, D.T, D.E, D.k, ws, s));
     });
@@ -197,12 +245,20 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x,
         const ExpertArgs W{experts->gu_codes, experts->gu_scales, experts->dn_codes,
                            experts->dn_scales};
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        hipError_t e = moe::launch_plan(offsets, plan, D.E, s);
-        if (e == hipSuccess)
+        hipError_t e;
+        {
+            DiagScope t("plan", s);
+            e = moe::launch_plan(offsets, plan, D.E, s);
+        }
+        if (e == hipSuccess) {
+            DiagScope t("gemv_gate_up", s);
             e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
                                          D.f, s);
-        if (e == hipSuccess)
+        }
+        if (e == hipSuccess) {
+            DiagScope t("gemv_down", s);
             e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f, s);
+        }
         return device_status(e);
     });
 }
@@ -217,6 +273,7 @@ moe_status moe_combine(const moe_dims *dims, const uint16_t *rows_out, const int
         if (!rows_out || !row_pos || !topk_w || !y) return MOE_ERR_NULL;
         if (!aligned16(rows_out) || !aligned16(y)) return MOE_ERR_ALIGN;
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        DiagScope t("combine", s);
         return device_status(moe::launch_combine(rows_out, row_pos, topk_w, y, D.T, D.d, D.k, s));
     });
 }
@@ -254,25 +311,82 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
                            experts->dn_scales};
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
-        hipError_t e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
-        if (e == hipSuccess) e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
-        if (e == hipSuccess)
+        hipError_t e;
+        {
+            DiagScope t("router_logits", s);
+            e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
+        }
+        if (e == hipSuccess) {
+            DiagScope t("topk_softmax", s);
+            e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
+        }
+        if (e == hipSuccess) {
+            DiagScope t("permute", s);
             e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T, D.E,
                                     D.k, perm_ws, s);
-        if (e == hipSuccess)
+        }
+        if (e == hipSuccess) {
+            DiagScope t("gemv_gate_up", s);
             e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
                                          D.f, s);
+        }
         if (D.T <= kFuseMaxT) {
-            if (e == hipSuccess)
+            if (e == hipSuccess) {
+                DiagScope t("down_combine", s);
                 e = moe::launch_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E, D.k, D.f, s);
+            }
         } else {
-            if (e == hipSuccess)
+            if (e == hipSuccess) {
+                DiagScope t("gemv_down", s);
                 e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f,
                                           s);
-            if (e == hipSuccess) e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
+            }
+            if (e == hipSuccess) {
+                DiagScope t("combine", s);
+                e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
+            }
         }
         return device_status(e);
     });
+}
+
+int moe_diag_time_kernel(const char *kernel, int capacity) {
+    try {
+        if (capacity < 0) return -1;
+        std::lock_guard<std::mutex> lk(g_diag.mu);
+        g_diag.active.store(false, std::memory_order_release);
+        g_diag.used = 0;
+        g_diag.name = kernel ? kernel : "";
+        while ((int)g_diag.ev.size() < 2 * capacity) {
+            hipEvent_t ev;
+            if (hipEventCreate(&ev) != hipSuccess) return -1;
+            g_diag.ev.push_back(ev);
+        }
+        g_diag.active.store(!g_diag.name.empty() && capacity > 0, std::memory_order_release);
+        return 0;
+    } catch (...) {
+        return -1;
+    }
+}
+
+int moe_diag_kernel_time(double *total_ms, long long *launches) {
+    try {
+        std::lock_guard<std::mutex> lk(g_diag.mu);
+        double sum = 0.0;
+        int rc = 0;
+        for (int i = 0; i < g_diag.used; ++i) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, g_diag.ev[2 * i], g_diag.ev[2 * i + 1]) != hipSuccess)
+                rc = -1;
+            sum += ms;
+        }
+        if (total_ms) *total_ms = sum;
+        if (launches) *launches = g_diag.used;
+        g_diag.used = 0;
+        return rc;
+    } catch (...) {
+        return -1;
+    }
 }
 
 }  // extern "C"

@@ -37,7 +37,8 @@ class Experts(ctypes.Structure):
 
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
-           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward")
+           "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+           "moe_diag_time_kernel", "moe_diag_kernel_time")
 
 _lib = None
 
@@ -70,8 +71,29 @@ def lib():
         L.moe_combine.argtypes = [DP, P, P, P, P, P]
         L.moe_layer_forward.restype = I
         L.moe_layer_forward.argtypes = [DP, P, P, P, EP, P, P, P, P, S, P]
+        L.moe_diag_time_kernel.restype = I
+        L.moe_diag_time_kernel.argtypes = [ctypes.c_char_p, I]
+        L.moe_diag_kernel_time.restype = I
+        L.moe_diag_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_longlong)]
         _lib = L
     return _lib
+
+
+def diag_time_kernel(kernel, capacity: int = 4096):
+    """Time every launch of one named kernel with HIP events (None stops)."""
+    name = None if kernel is None else kernel.encode()
+    if lib().moe_diag_time_kernel(name, int(capacity)) != 0:
+        raise RuntimeError("moe_diag_time_kernel failed")
+
+
+def diag_kernel_time():
+    """(total ms, launches) recorded since the last call; synchronise first."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_longlong(0)
+    if lib().moe_diag_kernel_time(ctypes.byref(ms), ctypes.byref(n)) != 0:
+        raise RuntimeError("moe_diag_kernel_time failed")
+    return ms.value, n.value
 
 
 def status_str(status: int) -> str:

@@ -3,6 +3,7 @@ include/moe.h declares, sizes workspaces, and refuses bad arguments on the
 host before any launch (no GPU is touched: every call here fails validation
 or has T = 0)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -22,9 +23,11 @@ def L():
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(L):
