@@ -31,8 +31,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 WORKLOADS = {"tiny": 0, "decode": 1, "batched-decode": 2, "zipf-prefill": 3, "long-prefill": 4}
 DOMINANT = "gemv_gate_up"
-KERNELS = ("router_logits", "topk_softmax", "permute", "gemv_gate_up", "down_combine",
-           "gemv_down", "combine")
+KERNELS = ("router_logits", "topk_softmax", "permute", "topk_permute", "gemv_gate_up",
+           "down_combine", "gemv_down", "combine")
 
 
 def parse():

@@ -4,8 +4,9 @@
  * the kernel's launches.  Not part of the layer's computation; a benchmark
  * uses it to time its dominant kernel inside the timed region.
  *
- * Kernel names: "router_logits", "topk_softmax", "permute", "plan",
- * "gemv_gate_up", "gemv_down", "down_combine", "combine".
+ * Kernel names: "router_logits", "topk_softmax", "permute", "topk_permute"
+ * (the two fused, small T), "plan", "gemv_gate_up", "gemv_down",
+ * "down_combine", "combine".
  */
 #ifndef ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 #define ROUTED_EXPERT_MXFP4_MOE_DIAG_H

@@ -20,16 +20,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     if (v >= (d >> 3)) return;
     const int nrows = T * k;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const int p = row_pos[(size_t)t * k + j];
-        if ((unsigned)p >= (unsigned)nrows) continue;
-        const float wj = topk_w[(size_t)t * k + j];
-        const uint4 q = reinterpret_cast<const uint4 *>(rows_out + (size_t)p * d)[v];
-        const uint32_t wds[4] = {q.x, q.y, q.z, q.w};
+    // slots in groups of 8: all loads of a group are issued before use
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        uint4 q[8];
+        float wj[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += wj * bf16_bits_to_f32(wds[i] & 0xFFFFu);
-            acc[2 * i + 1] += wj * bf16_bits_to_f32(wds[i] >> 16);
+        for (int jj = 0; jj < 8; ++jj) {
+            const int j = min(j0 + jj, k - 1);
+            int p = row_pos[(size_t)t * k + j];
+            const bool ok = j0 + jj < k && (unsigned)p < (unsigned)nrows;
+            p = ok ? p : 0;
+            wj[jj] = ok ? topk_w[(size_t)t * k + j] : 0.f;
+            q[jj] = reinterpret_cast<const uint4 *>(rows_out + (size_t)p * d)[v];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            if (j0 + jj < k) {
+                const uint32_t wds[4] = {q[jj].x, q[jj].y, q[jj].z, q[jj].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += wj[jj] * bf16_bits_to_f32(wds[i] & 0xFFFFu);
+                    acc[2 * i + 1] += wj[jj] * bf16_bits_to_f32(wds[i] >> 16);
+                }
+            }
         }
     }
     uint4 o;

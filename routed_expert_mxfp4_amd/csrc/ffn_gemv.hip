@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(
     const int nrows = T * k;
     int e, row0, ne;
     if (!expert_group(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nblk = d >> 5;
     const size_t code_row = (size_t)d >> 1;
     const uint8_t *codes = W.gu_codes + (size_t)e * 2 * f * code_row;
@@ -115,7 +116,8 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(
     const int nrows = T * k;
     int e, row0, ne;
     if (!expert_group(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int grp = lane >> 4, gl = lane & 15;
     const int nblk = f >> 5;
     const size_t code_row = (size_t)f >> 1;
@@ -231,17 +233,343 @@ __global__ __launch_bounds__(64) void down_combine_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Decode-shaped kernels: activations and h in registers, every weight load of
+// a row issued before any of it is used, DPP lane reductions.
+// ---------------------------------------------------------------------------
+constexpr int kRxPairs = 32;         // gate/up pairs per block (8 per wave)
+constexpr int kStageX = 4;           // x staging: d <= 4 * 256 * 8 = 8192
+
+// Gate/up for decode-sized groups, software-pipelined: lane l owns the MX
+// blocks b = l + 64 i (i < NBL) of d; the token row is staged once in LDS
+// (shared by the block's four waves) and each wave streams its output pairs
+// with the next pair's code loads issued before the current pair's math, so
+// HBM reads and VALU work overlap instead of alternating.
+template <int NBL>
+struct PairBuf {
+    uint4 c[2][NBL];       // gate, up
+    uint32_t s[2][NBL];
+};
+
+template <int NBL>
+__device__ __forceinline__ void load_pair(rsrc_t codes, rsrc_t scales, int n, int f, int lane,
+                                          int nblk, uint32_t code_row, PairBuf<NBL> &pb) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        const uint32_t row = (uint32_t)(n + v * f);                 // wave-uniform
+#pragma unroll
+        for (int i = 0; i < NBL; ++i) {
+            const uint32_t b = (uint32_t)min(lane + 64 * i, nblk - 1);
+            pb.c[v][i] = buf_load16(codes, 16u * b, row * code_row);
+            pb.s[v][i] = buf_load8(scales, b, row * (uint32_t)nblk);
+        }
+    }
+}
+
+template <int NBL>
+__device__ __forceinline__ float pair_h(const PairBuf<NBL> &pb, const uint4 *__restrict__ xs,
+                                        int lane, int nblk) {
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+        const int b = min(lane + 64 * i, nblk - 1);
+        const bool ok = lane + 64 * i < nblk;
+        const uint4 x0 = xs[4 * b], x1 = xs[4 * b + 1], x2 = xs[4 * b + 2], x3 = xs[4 * b + 3];
+        float pg = 0.f, pu = 0.f;
+        pg = dot8_fp4_bf16(pb.c[0][i].x, x0, pg);
+        pu = dot8_fp4_bf16(pb.c[1][i].x, x0, pu);
+        pg = dot8_fp4_bf16(pb.c[0][i].y, x1, pg);
+        pu = dot8_fp4_bf16(pb.c[1][i].y, x1, pu);
+        pg = dot8_fp4_bf16(pb.c[0][i].z, x2, pg);
+        pu = dot8_fp4_bf16(pb.c[1][i].z, x2, pu);
+        pg = dot8_fp4_bf16(pb.c[0][i].w, x3, pg);
+        pu = dot8_fp4_bf16(pb.c[1][i].w, x3, pu);
+        g += ok ? apply_e8m0(pg, pb.s[0][i]) : 0.f;
+        u += ok ? apply_e8m0(pu, pb.s[1][i]) : 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    g = wave_sum_f32(g);
+    u = wave_sum_f32(u);
+    return silu_mul(g, u);
+}
+
+template <int NBL>
+__global__ __launch_bounds__(256) void gate_up_regx_kernel(
+    const uint16_t *__restrict__ x, ExpertArgs W, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
+    float *__restrict__ h, int T, int d, int E, int k, int f) {
+    const int nrows = T * k;
+    int e, row0, ne;
+    if (!expert_group(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
+    extern __shared__ uint4 xs[];                 // one token row, d/8 x 16 B, + 1 spare
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int nblk = d >> 5;
+    const int nvec = d >> 3;
+    const uint32_t code_row = (uint32_t)d >> 1;
+    const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
+    const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
+    constexpr int kPerWave = kRxPairs / 4;        // pairs n_base + wid + 4 q
+    const int n_base = blockIdx.x * kRxPairs + wid;
+    for (int r = 0; r < ne; ++r) {
+        const int row = sorted_rows[row0 + r];
+        const int tok = (unsigned)row < (unsigned)nrows ? row / k : 0;
+        PairBuf<NBL> A, B;
+        load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);   // before the x sync
+        __syncthreads();
+        {
+            const uint4 *xrow = reinterpret_cast<const uint4 *>(x + (size_t)tok * d);
+            uint4 tmp[kStageX];
+#pragma unroll
+            for (int j = 0; j < kStageX; ++j)
+                tmp[j] = xrow[min((int)threadIdx.x + 256 * j, nvec - 1)];
+            loads_done(tmp);                        // all loads before any store      // all loads before any store
+#pragma unroll
+            for (int j = 0; j < kStageX; ++j) {     // spare slot: no branch per store
+                const int i = (int)threadIdx.x + 256 * j;
+                xs[i < nvec ? i : nvec] = tmp[j];
+            }
+        }
+        __syncthreads();
+        float* hrow = h + (size_t)(row0 + r) * f;
+        // sched_barrier keeps each stage in place: a later pair's loads may
+        // not be hoisted above an earlier pair's math (that would only grow
+        // the register footprint, not the bytes in flight)
+#pragma unroll 1
+        for (int q = 0; q < kPerWave; q += 2) {
+            load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
+            __builtin_amdgcn_sched_barrier(0);
+            const float va = pair_h<NBL>(A, xs, lane, nblk);
+            if (lane == 0) hrow[n_base + 4 * q] = va;
+            __builtin_amdgcn_sched_barrier(0);
+            if (q + 2 < kPerWave)
+                load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
+            __builtin_amdgcn_sched_barrier(0);
+            const float vb = pair_h<NBL>(B, xs, lane, nblk);
+            if (lane == 0) hrow[n_base + 4 * (q + 1)] = vb;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Down rows for one h row: lane l owns the MX blocks b = l + 64 i (i < NBLD)
+// of f, so its slice of h (32 floats per block) is loaded once into
+// registers and reused for every output row; rows go in batches of 8 whose
+// code loads are all in flight together, and each row's partial sums are
+// reduced across the wave.  Lanes past the end of f hold zero h.
+constexpr int kDnBatch = 4;
+
+template <int NBLD>
+__device__ __forceinline__ void load_h_slice(rsrc_t hbuf, uint32_t hrow_off, int lane, int nblk,
+                                             float4 (&hv)[NBLD][8]) {
+#pragma unroll
+    for (int i = 0; i < NBLD; ++i) {
+        const uint32_t b = (uint32_t)min(lane + 64 * i, nblk - 1);
+        const bool ok = lane + 64 * i < nblk;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const float4 v = __builtin_bit_cast(float4, buf_load16(hbuf, 128u * b + 16u * q, hrow_off));
+            hv[i][q] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
+// Down rows in batches of kDnBatch: load_batch issues every code and scale
+// load of a batch, dot_batch does its math (out[rr] = h . Wd[m + rr], every
+// lane gets the sums).  Callers issue the next batch's loads before the
+// current batch's math.
+__device__ __forceinline__ void store_bf16x4(uint16_t *dst, const float (&v)[kDnBatch]) {
+    uint2 o;
+    o.x = f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+    o.y = f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+    *reinterpret_cast<uint2 *>(dst) = o;
+}
+
+template <int NBLD>
+struct RowBuf {
+    uint4 c[kDnBatch][NBLD];
+    uint32_t s[kDnBatch][NBLD];
+};
+
+template <int NBLD>
+__device__ __forceinline__ void load_batch(rsrc_t codes, rsrc_t scales, int m, int lane,
+                                           int nblk, uint32_t code_row, RowBuf<NBLD> &rb) {
+#pragma unroll
+    for (int rr = 0; rr < kDnBatch; ++rr)
+#pragma unroll
+        for (int i = 0; i < NBLD; ++i) {
+            const uint32_t b = (uint32_t)min(lane + 64 * i, nblk - 1);
+            const uint32_t row = (uint32_t)(m + rr);                  // wave-uniform
+            rb.c[rr][i] = buf_load16(codes, 16u * b, row * code_row);
+            rb.s[rr][i] = buf_load8(scales, b, row * (uint32_t)nblk);
+        }
+}
+
+template <int NBLD>
+__device__ __forceinline__ void dot_batch(const RowBuf<NBLD> &rb, const float4 (&hv)[NBLD][8],
+                                          int lane, int nblk, float (&out)[kDnBatch]) {
+#pragma unroll
+    for (int rr = 0; rr < kDnBatch; ++rr) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < NBLD; ++i) {
+            float s = 0.f;
+            s = dot8_fp4_f32(rb.c[rr][i].x, hv[i][0], hv[i][1], s);
+            s = dot8_fp4_f32(rb.c[rr][i].y, hv[i][2], hv[i][3], s);
+            s = dot8_fp4_f32(rb.c[rr][i].z, hv[i][4], hv[i][5], s);
+            s = dot8_fp4_f32(rb.c[rr][i].w, hv[i][6], hv[i][7], s);
+            acc += lane + 64 * i < nblk ? apply_e8m0(s, rb.s[rr][i]) : 0.f;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        out[rr] = wave_sum_f32(acc);
+    }
+}
+
+// Fused down + combine for small T: block (kDcRows output rows, token t);
+// wave j computes slot j's expert output for the block's rows (j = wid,
+// wid + 16, ...) and parks it in LDS; then y = sum_j w_j o_j in fp32, slot
+// order, one writer per output.
+constexpr int kDcRows = 16;
+
+template <int NBLD>
+__global__ __launch_bounds__(1024) void down_combine_split_kernel(
+    const float *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ ids,
+    const float *__restrict__ topk_w, const int32_t *__restrict__ row_pos,
+    uint16_t *__restrict__ y, int T, int d, int E, int k, int f) {
+    __shared__ float part[kMaxTopK][kDcRows];
+    const int t = blockIdx.y;
+    const int m0 = blockIdx.x * kDcRows;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int nblk = f >> 5;
+    const uint32_t code_row = (uint32_t)f >> 1;
+    const int nrows = T * k;
+    const rsrc_t hbuf = make_rsrc(h, (uint32_t)min((size_t)nrows * f * 4, (size_t)0xFFFFFFF0u));
+    for (int j = wid; j < k; j += 16) {
+        const int e = __builtin_amdgcn_readfirstlane(ids[(size_t)t * k + j]);
+        const int p = __builtin_amdgcn_readfirstlane(row_pos[(size_t)t * k + j]);
+        const bool ok = (unsigned)e < (unsigned)E && (unsigned)p < (unsigned)nrows;
+        if (ok) {
+            const rsrc_t codes = make_rsrc(W.dn_codes + (size_t)e * d * code_row, (uint32_t)d * code_row);
+            const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
+            float4 hv[NBLD][8];
+            load_h_slice<NBLD>(hbuf, (uint32_t)p * f * 4u, lane, nblk, hv);
+            RowBuf<NBLD> A, B;
+            load_batch<NBLD>(codes, scales, m0, lane, nblk, code_row, A);
+            // batches of kDnBatch rows, the next batch's loads in flight
+            // during the current batch's math
+#pragma unroll 1
+            for (int b0 = 0; b0 < kDcRows; b0 += 2 * kDnBatch) {
+                load_batch<NBLD>(codes, scales, m0 + b0 + kDnBatch, lane, nblk, code_row, B);
+                __builtin_amdgcn_sched_barrier(0);
+                float out[kDnBatch];
+                dot_batch<NBLD>(A, hv, lane, nblk, out);
+                if (lane == 0) {
+#pragma unroll
+                    for (int rr = 0; rr < kDnBatch; ++rr) part[j][b0 + rr] = out[rr];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (b0 + 2 * kDnBatch < kDcRows)
+                    load_batch<NBLD>(codes, scales, m0 + b0 + 2 * kDnBatch, lane, nblk, code_row, A);
+                __builtin_amdgcn_sched_barrier(0);
+                dot_batch<NBLD>(B, hv, lane, nblk, out);
+                if (lane == 0) {
+#pragma unroll
+                    for (int rr = 0; rr < kDnBatch; ++rr) part[j][b0 + kDnBatch + rr] = out[rr];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if (lane < kDcRows) {
+            part[j][lane] = 0.f;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < kDcRows) {
+        float yv = 0.f;
+        for (int j = 0; j < k; ++j) yv += topk_w[(size_t)t * k + j] * part[j][threadIdx.x];
+        y[(size_t)t * d + m0 + threadIdx.x] = f32_to_bf16_rne(yv);
+    }
+}
+
+// Expert-major down for decode-sized groups: block (64 output rows, expert
+// a), 16 rows per wave; the expert's token rows are walked one by one
+// (weights re-read from L2 after the first).
+template <int NBLD>
+__global__ __launch_bounds__(256) void down_rows_kernel(
+    const float *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ plan, uint16_t *__restrict__ rows_out, int T, int d, int E,
+    int k, int f) {
+    const int nrows = T * k;
+    int e, row0, ne;
+    if (!expert_group(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int nblk = f >> 5;
+    const uint32_t code_row = (uint32_t)f >> 1;
+    const int m = blockIdx.x * 64 + wid * 16;
+    const rsrc_t codes = make_rsrc(W.dn_codes + (size_t)e * d * code_row, (uint32_t)d * code_row);
+    const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
+    const rsrc_t hbuf = make_rsrc(h + (size_t)row0 * f, (uint32_t)ne * f * 4u);
+    for (int r = 0; r < ne; ++r) {
+        float4 hv[NBLD][8];
+        load_h_slice<NBLD>(hbuf, (uint32_t)r * f * 4u, lane, nblk, hv);
+        uint16_t *orow = rows_out + (size_t)(row0 + r) * d + m;
+        RowBuf<NBLD> A, B;
+        load_batch<NBLD>(codes, scales, m, lane, nblk, code_row, A);
+#pragma unroll 1
+        for (int b0 = 0; b0 < 16; b0 += 2 * kDnBatch) {
+            load_batch<NBLD>(codes, scales, m + b0 + kDnBatch, lane, nblk, code_row, B);
+            __builtin_amdgcn_sched_barrier(0);
+            float out[kDnBatch];
+            dot_batch<NBLD>(A, hv, lane, nblk, out);
+            if (lane == 0) store_bf16x4(orow + b0, out);
+            __builtin_amdgcn_sched_barrier(0);
+            if (b0 + 2 * kDnBatch < 16)
+                load_batch<NBLD>(codes, scales, m + b0 + 2 * kDnBatch, lane, nblk, code_row, A);
+            __builtin_amdgcn_sched_barrier(0);
+            dot_batch<NBLD>(B, hv, lane, nblk, out);
+            if (lane == 0) store_bf16x4(orow + b0 + kDnBatch, out);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 }  // namespace
+
+template <int NBL>
+hipError_t launch_regx(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
+                       const int32_t *sorted_rows, const int32_t *plan, float *h, int T, int d,
+                       int E, int k, int f, int amax, hipStream_t s) {
+    dim3 grid(f / kRxPairs, amax);
+    gate_up_regx_kernel<NBL><<<grid, 256, (size_t)d * 2 + 16, s>>>(x, w, offsets, sorted_rows, plan, h,
+                                                              T, d, E, k, f);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemv_gate_up(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                                const int32_t *sorted_rows, const int32_t *plan, float *h,
                                int T, int d, int E, int k, int f, hipStream_t s) {
     const int amax = min(E, T * k);
     if (amax <= 0) return hipSuccess;
+    const int nbl = (d / 32 + 63) / 64;               // MX blocks per lane along d
+    if (f % kRxPairs == 0 && T <= 64 && nbl <= 4 && d <= 8192) {
+        if (nbl == 1) return launch_regx<1>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        if (nbl == 2) return launch_regx<2>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        return launch_regx<4>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+    }
     const int rpp = max(1, min(kRowsMax, 32768 / d));   // <= 64 KB of LDS
     dim3 grid(f / kGuPairs, amax);
     gemv_gate_up_kernel<<<grid, 256, (size_t)rpp * d * 2, s>>>(x, w, offsets, sorted_rows, plan,
                                                                h, T, d, E, k, f, rpp);
+    return hipGetLastError();
+}
+
+template <int NBLD>
+hipError_t launch_down_rows(const float *h, ExpertArgs w, const int32_t *offsets,
+                            const int32_t *plan, uint16_t *rows_out, int T, int d, int E,
+                            int k, int f, int amax, hipStream_t s) {
+    dim3 grid(d / 64, amax);
+    down_rows_kernel<NBLD><<<grid, 256, 0, s>>>(h, w, offsets, plan, rows_out, T, d, E, k, f);
     return hipGetLastError();
 }
 
@@ -250,6 +578,11 @@ hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets
                             int k, int f, hipStream_t s) {
     const int amax = min(E, T * k);
     if (amax <= 0) return hipSuccess;
+    const int nbld = (f / 32 + 63) / 64;              // MX blocks per lane along f
+    if (T <= 64 && nbld <= 2) {
+        if (nbld == 1) return launch_down_rows<1>(h, w, offsets, plan, rows_out, T, d, E, k, f, amax, s);
+        return launch_down_rows<2>(h, w, offsets, plan, rows_out, T, d, E, k, f, amax, s);
+    }
     const int rpp = max(1, min(kRowsMax, 16384 / f));   // <= 64 KB of LDS
     dim3 grid(d / kDnRows, amax);
     gemv_down_kernel<<<grid, 256, (size_t)rpp * f * 4, s>>>(h, w, offsets, plan, rows_out, T, d,
@@ -257,10 +590,25 @@ hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets
     return hipGetLastError();
 }
 
+template <int NBLD>
+hipError_t launch_dc_split(const float *h, ExpertArgs w, const int32_t *ids,
+                           const float *topk_w, const int32_t *row_pos, uint16_t *y, int T,
+                           int d, int E, int k, int f, hipStream_t s) {
+    dim3 grid(d / kDcRows, T);
+    down_combine_split_kernel<NBLD><<<grid, 1024, 0, s>>>(h, w, ids, topk_w, row_pos, y, T, d,
+                                                           E, k, f);
+    return hipGetLastError();
+}
+
 hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
                                const float *topk_w, const int32_t *row_pos, uint16_t *y,
                                int T, int d, int E, int k, int f, hipStream_t s) {
     if (T <= 0) return hipSuccess;
+    const int nbld = (f / 32 + 63) / 64;
+    if (nbld <= 2) {
+        if (nbld == 1) return launch_dc_split<1>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+        return launch_dc_split<2>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+    }
     dim3 grid(d / 16, T);
     down_combine_kernel<<<grid, 64, 0, s>>>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f);
     return hipGetLastError();

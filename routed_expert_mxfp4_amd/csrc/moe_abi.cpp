@@ -316,14 +316,22 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
             DiagScope t("router_logits", s);
             e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
         }
-        if (e == hipSuccess) {
-            DiagScope t("topk_softmax", s);
-            e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
-        }
-        if (e == hipSuccess) {
-            DiagScope t("permute", s);
-            e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T, D.E,
-                                    D.k, perm_ws, s);
+        if (moe::topk_permute_fusable(D.T, D.E, D.k)) {
+            if (e == hipSuccess) {
+                DiagScope t("topk_permute", s);
+                e = moe::launch_topk_permute_small(logits, ids, tw, counts, offsets, sorted_rows,
+                                                   row_pos, plan, D.T, D.E, D.k, s);
+            }
+        } else {
+            if (e == hipSuccess) {
+                DiagScope t("topk_softmax", s);
+                e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
+            }
+            if (e == hipSuccess) {
+                DiagScope t("permute", s);
+                e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
+                                        D.E, D.k, perm_ws, s);
+            }
         }
         if (e == hipSuccess) {
             DiagScope t("gemv_gate_up", s);

@@ -17,8 +17,6 @@ namespace moe {
 // ---------------------------------------------------------------------------
 constexpr int kMaxExperts = 1024;   // top-k keeps <= 16 logits per lane
 constexpr int kMaxTopK = 32;
-constexpr int kPermTokensPerBlock = 1024;   // 16 sub-blocks of 64 tokens
-constexpr int kPermSub = kPermTokensPerBlock / 64;
 
 // ---------------------------------------------------------------------------
 // Small device helpers.
@@ -45,17 +43,64 @@ __device__ __forceinline__ float apply_e8m0(float x, uint32_t code) {
     return code == 255u ? __uint_as_float(0x7FC00000u) : ldexpf(x, (int)code - 127);
 }
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-    for (int w = 32; w >= 1; w >>= 1) v += __shfl_xor(v, w, 64);
+// Raw buffer loads: a wave-uniform resource (base, byte size) plus a 32-bit
+// per-lane offset and a uniform offset.  Loads past the size return 0, so
+// a malformed index can never fault; addresses need one VGPR, not two.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
+// Issue-order helpers: an empty asm statement that takes loaded values as
+// operands makes every one of them complete at that point, so a batch of
+// loads is issued back to back and waited for once (instead of each load
+// being scheduled next to its single use, one memory round trip apiece).
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t as_v4(uint4 v) { return __builtin_bit_cast(u32x4_t, v); }
+__device__ __forceinline__ void loads_done(const uint4 (&b)[4]) {
+    __asm__ volatile("" ::"v"(as_v4(b[0])), "v"(as_v4(b[1])), "v"(as_v4(b[2])), "v"(as_v4(b[3])));
+}
+__device__ __forceinline__ void loads_done(const uint4 (&b)[16]) {
+    __asm__ volatile("" ::"v"(as_v4(b[0])), "v"(as_v4(b[1])), "v"(as_v4(b[2])), "v"(as_v4(b[3])),
+                     "v"(as_v4(b[4])), "v"(as_v4(b[5])), "v"(as_v4(b[6])), "v"(as_v4(b[7])),
+                     "v"(as_v4(b[8])), "v"(as_v4(b[9])), "v"(as_v4(b[10])), "v"(as_v4(b[11])),
+                     "v"(as_v4(b[12])), "v"(as_v4(b[13])), "v"(as_v4(b[14])), "v"(as_v4(b[15])));
+}
+
+// DPP row_ror:n on a float (rotate right by n within each row of 16 lanes).
+template <int N>
+__device__ __forceinline__ float dpp_ror_f32(float v) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a lane group (lanes 16g .. 16g+15); every lane of
+// the group gets the sum (DPP rotations, no LDS traffic).
+__device__ __forceinline__ float group16_sum_f32(float v) {
+    v += dpp_ror_f32<8>(v);
+    v += dpp_ror_f32<4>(v);
+    v += dpp_ror_f32<2>(v);
+    v += dpp_ror_f32<1>(v);
     return v;
 }
 
-// Sum over the 16 lanes of a lane group (lanes 16g .. 16g+15).
-__device__ __forceinline__ float group16_sum_f32(float v) {
-#pragma unroll
-    for (int w = 8; w >= 1; w >>= 1) v += __shfl_xor(v, w, 64);
-    return v;
+// Sum over the wave (fixed order: rows 0+1, rows 2+3, then the two); the
+// result is wave-uniform.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v = group16_sum_f32(v);
+    const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (a + b) + (c + d);
 }
 
 // Dot product of 8 E2M1 codes (one 32-bit word, element 2i in the low
@@ -99,6 +144,12 @@ hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
                           int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, int T,
                           int E, int k, void *ws, hipStream_t s);
 hipError_t launch_plan(const int32_t *offsets, int32_t *plan, int E, hipStream_t s);
+// T <= 16: top-k + softmax and the grouping (with the plan) in one launch.
+bool topk_permute_fusable(int T, int E, int k);
+hipError_t launch_topk_permute_small(const float *logits, int32_t *ids, float *tw,
+                                     int32_t *counts, int32_t *offsets, int32_t *sorted_rows,
+                                     int32_t *row_pos, int32_t *plan, int T, int E, int k,
+                                     hipStream_t s);
 
 struct ExpertArgs {
     const uint8_t *gu_codes, *gu_scales, *dn_codes, *dn_scales;

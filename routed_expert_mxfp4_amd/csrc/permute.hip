@@ -12,6 +12,7 @@
 // are grouped into blocks of kSub tiles; block-level counts are scanned over
 // blocks (per expert) and over experts (offsets).
 #include "moe_internal.hpp"
+#include "select_dev.hpp"
 
 namespace moe {
 namespace {
@@ -53,20 +54,18 @@ __device__ __forceinline__ int valid_id(int e, int E) { return (unsigned)e < (un
 // ---------------------------------------------------------------------------
 // T <= kTokBlk: one block of 1024 threads does everything.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void permute_single_kernel(
-    const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
-    int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, int T, int E, int k) {
-    extern __shared__ unsigned long long smem_u64[];
-    unsigned long long *mask = smem_u64;                         // [kSub][E]
-    int *off_s = reinterpret_cast<int *>(mask + kSub * E);       // [E]
-    __shared__ int tmp[48];
+// mask: LDS u64 [kSub][E]; off_s: LDS int [E]; tmp: LDS int [48].
+__device__ void permute_block(const int32_t *ids, unsigned long long *mask, int *off_s,
+                              int *tmp, int32_t *__restrict__ counts,
+                              int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
+                              int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, int T,
+                              int E, int k) {
     const int tid = threadIdx.x;
     const int nrows = T * k;
     for (int i = tid; i < kSub * E; i += 1024) mask[i] = 0ull;
     __syncthreads();
     for (int r = tid; r < nrows; r += 1024) {
-        int t = r / k, e = ids[r];
+        const int t = r / k, e = ids[r];
         if (valid_id(e, E)) atomicOr(&mask[(t >> 6) * E + e], 1ull << (t & 63));
     }
     __syncthreads();
@@ -74,7 +73,7 @@ __global__ __launch_bounds__(1024) void permute_single_kernel(
     if (tid < E)
         for (int sb = 0; sb < kSub; ++sb) c += __popcll(mask[sb * E + tid]);
     int total;
-    int off = block_exclusive_scan(tid < E ? c : 0, tmp, &total);
+    const int off = block_exclusive_scan(tid < E ? c : 0, tmp, &total);
     if (tid < E) {
         off_s[tid] = off;
         counts[tid] = c;
@@ -83,21 +82,59 @@ __global__ __launch_bounds__(1024) void permute_single_kernel(
     if (tid == 0) offsets[E] = total;
     if (plan) {
         int act_total;
-        int a = block_exclusive_scan(tid < E && c > 0 ? 1 : 0, tmp, &act_total);
+        const int a = block_exclusive_scan(tid < E && c > 0 ? 1 : 0, tmp, &act_total);
         if (tid < E && c > 0) plan[1 + a] = tid;
         if (tid == 0) plan[0] = act_total;
     }
     __syncthreads();
     for (int r = tid; r < nrows; r += 1024) {
-        int t = r / k, e = ids[r];
+        const int t = r / k, e = ids[r];
         if (!valid_id(e, E)) continue;
-        int sb = t >> 6, tl = t & 63;
+        const int sb = t >> 6, tl = t & 63;
         int pos = off_s[e];
         for (int s2 = 0; s2 < sb; ++s2) pos += __popcll(mask[s2 * E + e]);
         pos += __popcll(mask[sb * E + e] & ((1ull << tl) - 1ull));
         sorted_rows[pos] = r;
         row_pos[r] = pos;
     }
+}
+
+__global__ __launch_bounds__(1024) void permute_single_kernel(
+    const int32_t *__restrict__ ids, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
+    int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, int T, int E, int k) {
+    extern __shared__ unsigned long long smem_u64[];
+    unsigned long long *mask = smem_u64;                         // [kSub][E]
+    int *off_s = reinterpret_cast<int *>(mask + kSub * E);       // [E]
+    __shared__ int tmp[48];
+    permute_block(ids, mask, off_s, tmp, counts, offsets, sorted_rows, row_pos, plan, T, E, k);
+}
+
+// T <= 16: top-k + softmax (one wave per token) and the grouping in one block.
+template <int PL>
+__global__ __launch_bounds__(1024) void topk_permute_small_kernel(
+    const float *__restrict__ logits, int32_t *__restrict__ ids, float *__restrict__ tw,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_rows, int32_t *__restrict__ row_pos,
+    int32_t *__restrict__ plan, int T, int E, int k) {
+    extern __shared__ unsigned long long smem_u64[];
+    unsigned long long *mask = smem_u64;                         // [kSub][E]
+    int *off_s = reinterpret_cast<int *>(mask + kSub * E);       // [E]
+    int *ids_s = off_s + E;                                      // [16 * k]
+    __shared__ int tmp[48];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (wid < T) {
+        int e;
+        float wt;
+        wave_topk_softmax<PL>(logits + (size_t)wid * E, E, k, &e, &wt);
+        if (lane < k) {
+            ids[(size_t)wid * k + lane] = e;
+            tw[(size_t)wid * k + lane] = wt;
+            ids_s[wid * k + lane] = e;
+        }
+    }
+    __syncthreads();
+    permute_block(ids_s, mask, off_s, tmp, counts, offsets, sorted_rows, row_pos, plan, T, E, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -240,6 +277,26 @@ hipError_t launch_permute(const int32_t *ids, int32_t *counts, int32_t *offsets,
     const long long rows = (long long)T * k;
     permute_scatter_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, s>>>(
         ids, masks, blkpre, offsets, sorted_rows, row_pos, T, E, k, nb);
+    return hipGetLastError();
+}
+
+bool topk_permute_fusable(int T, int E, int k) { return T <= 16 && E <= 1024 && k <= 32; }
+
+hipError_t launch_topk_permute_small(const float *logits, int32_t *ids, float *tw,
+                                     int32_t *counts, int32_t *offsets, int32_t *sorted_rows,
+                                     int32_t *row_pos, int32_t *plan, int T, int E, int k,
+                                     hipStream_t s) {
+    const size_t lds = (size_t)kSub * E * 8 + (size_t)E * 4 + (size_t)16 * k * 4;
+    const int pl = (E + 63) / 64;
+    if (pl <= 4)
+        topk_permute_small_kernel<4><<<1, 1024, lds, s>>>(logits, ids, tw, counts, offsets,
+                                                          sorted_rows, row_pos, plan, T, E, k);
+    else if (pl <= 8)
+        topk_permute_small_kernel<8><<<1, 1024, lds, s>>>(logits, ids, tw, counts, offsets,
+                                                          sorted_rows, row_pos, plan, T, E, k);
+    else
+        topk_permute_small_kernel<16><<<1, 1024, lds, s>>>(logits, ids, tw, counts, offsets,
+                                                           sorted_rows, row_pos, plan, T, E, k);
     return hipGetLastError();
 }
 

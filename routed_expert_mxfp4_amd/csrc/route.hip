@@ -12,6 +12,7 @@
 // Top-k: descending logit, lower expert index first on equal logits; the
 // routing weights are a softmax over the k selected logits, no extra scale.
 #include "moe_internal.hpp"
+#include "select_dev.hpp"
 
 namespace moe {
 namespace {
@@ -130,17 +131,77 @@ hipError_t launch_logits_tile(const uint16_t *x, const uint16_t *wr, const float
 }
 
 // ---------------------------------------------------------------------------
-// top-k + softmax: one wave per token; lane l holds experts l, l+64, ...
+// One token with d % 512 == 0: router rows staged through LDS.
 // ---------------------------------------------------------------------------
-struct Cand {
-    float v;
-    int e;
-};
+// Lane c of a wave sums chunk c (P consecutive inputs) of one router row.  A
+// direct load would have the 64 lanes of a wave read 64 rows 2P bytes apart,
+// so every 16-byte load touches 64 cache lines; instead the block copies its
+// four router rows into LDS with coalesced 16-byte loads, laid out chunk by
+// chunk with 16 bytes of padding (a chunk stride of 2P+16 bytes keeps the
+// 16 lanes of a b128 read on distinct banks), and each lane then reads its
+// own chunk from LDS.  The lane's chunk of x goes straight to registers.
+constexpr int kStagePieces = 16;                    // d <= 8192
 
-__device__ __forceinline__ bool better(float va, int ea, float vb, int eb) {
-    return va > vb || (va == vb && ea < eb);
+__global__ __launch_bounds__(256) void router_small_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const float *__restrict__ bias, float *__restrict__ logits, int T, int d, int E) {
+    extern __shared__ uint4 wrs[];                  // [4][64][(2P+16)/16] + 1 spare
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int P = d >> 6;
+    const int q_per_chunk = P >> 3;                 // 16-byte pieces per chunk
+    const int cstride = q_per_chunk + 1;            // in uint4, with padding
+    const int e0 = blockIdx.x * 4;
+    const int pieces = 64 * q_per_chunk;            // 16-byte pieces per row
+    const int total = 4 * pieces;                   // <= 256 * kStagePieces
+    // every load first, then every LDS store: one memory round trip
+    uint4 buf[kStagePieces];
+#pragma unroll
+    for (int j = 0; j < kStagePieces; ++j) {
+        const int i = min((int)threadIdx.x + 256 * j, total - 1);
+        const int r = i / pieces, q = i - r * pieces;
+        buf[j] = reinterpret_cast<const uint4 *>(wr + (size_t)min(e0 + r, E - 1) * d)[q];
+    }
+    // every load completes here, then unconditional stores (pieces past the
+    // end go to a spare slot)
+    loads_done(buf);
+    const int spare = 4 * 64 * cstride;
+#pragma unroll
+    for (int j = 0; j < kStagePieces; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        const int r = i / pieces, q = i - r * pieces;
+        const int c = q / q_per_chunk, w = q - c * q_per_chunk;
+        wrs[i < total ? (r * 64 + c) * cstride + w : spare] = buf[j];
+    }
+    __syncthreads();
+    const int e = e0 + wid;
+    const uint4 *wc = wrs + (wid * 64 + lane) * cstride;
+    double acc = 0.0;
+    // the lane's chunk of x (one token) is loaded into registers up front
+    const uint4 *xr = reinterpret_cast<const uint4 *>(x + (size_t)lane * P);
+    uint4 xv[kStagePieces];
+#pragma unroll
+    for (int w = 0; w < kStagePieces; ++w) xv[w] = xr[min(w, q_per_chunk - 1)];
+#pragma unroll
+    for (int w = 0; w < kStagePieces; ++w) {
+        if (w < q_per_chunk) {
+            const uint4 wv = wc[w];
+            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+            const uint32_t xx[4] = {xv[w].x, xv[w].y, xv[w].z, xv[w].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {                  // ascending element order
+                acc = fma(bf16_lo(xx[q]), bf16_lo(ww[q]), acc);
+                acc = fma(bf16_hi(xx[q]), bf16_hi(ww[q]), acc);
+            }
+        }
+    }
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) acc += __shfl_xor(acc, w, 64);
+    if (e < E && lane == 0) logits[e] = (float)(acc + (bias ? (double)bias[e] : 0.0));
 }
 
+// ---------------------------------------------------------------------------
+// top-k + softmax: one wave per token.
+// ---------------------------------------------------------------------------
 template <int PL>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restrict__ logits,
                                                            int32_t *__restrict__ ids,
@@ -149,52 +210,12 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    float v[PL];
-    const float *row = logits + (size_t)t * E;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-        int e = lane + 64 * i;
-        float a = e < E ? row[e] : -INFINITY;
-        v[i] = (a != a) ? -INFINITY : a;             // NaN ranks lowest
-    }
-    uint32_t taken = 0;
-    float my_v = 0.f;
-    int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int be = 0x7FFFFFFF;
-#pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            int e = lane + 64 * i;
-            if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, be)) {
-                bv = v[i];
-                be = e;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            float ov = __shfl_xor(bv, off, 64);
-            int oe = __shfl_xor(be, off, 64);
-            if (better(ov, oe, bv, be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == j) {
-            my_v = bv;
-            my_e = be;
-        }
-    }
-    // softmax over the selected logits (fp64), max = the first selected
-    double vmax = (double)__shfl(my_v, 0, 64);
-    double ex = lane < k ? exp((double)my_v - vmax) : 0.0;
-    double sum = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    int e;
+    float wt;
+    wave_topk_softmax<PL>(logits + (size_t)t * E, E, k, &e, &wt);
     if (lane < k) {
-        ids[(size_t)t * k + lane] = my_e;
-        w[(size_t)t * k + lane] = (float)(ex / sum);
+        ids[(size_t)t * k + lane] = e;
+        w[(size_t)t * k + lane] = wt;
     }
 }
 
@@ -203,6 +224,12 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
 hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const float *bias,
                                 float *logits, int T, int d, int E, hipStream_t s) {
     if (T <= 0) return hipSuccess;
+    const int P = d / 64;
+    const size_t lds = (size_t)4 * 64 * ((P / 8) + 1) * 16 + 16;   // + spare slot
+    if (T == 1 && P % 8 == 0 && d <= 8192 && lds <= 65536) {
+        router_small_kernel<<<(E + 3) / 4, 256, lds, s>>>(x, wr, bias, logits, T, d, E);
+        return hipGetLastError();
+    }
     if (T < 4) return launch_logits_tile<1, 4>(x, wr, bias, logits, T, d, E, s);
     return launch_logits_tile<4, 8>(x, wr, bias, logits, T, d, E, s);
 }
