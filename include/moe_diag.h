@@ -6,14 +6,32 @@
  *
  * Kernel names: "router_logits", "topk_softmax", "permute", "topk_permute"
  * (the two fused, small T), "plan", "gemv_gate_up", "gemv_down",
- * "down_combine", "combine".
+ * "down_combine", "combine", "mfma_ffn" (the whole scaled-MFMA expert
+ * FFN of large T: activation split, gate/up, h split, down).
  */
 #ifndef ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 #define ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* The activation split the scaled-MFMA expert path feeds to the matrix
+ * cores, exposed for bit-exact checks: each row of `in` (rows x K, K a
+ * multiple of 128; bf16 bits if in_is_bf16, else fp32; 16-byte aligned) is
+ * cut into 32-element blocks and each block a into two OCP MX E2M3 terms,
+ * hi = MX(a), lo = MX(a - hi): shared exponent X = floor(log2 max|.|) - 2
+ * clamped to [-127, 127] (E8M0 code X + 127; all-zero block -> code 0),
+ * elements rounded to nearest even and saturated at 7.5.  Output per row:
+ *   q [K/128][2 terms][4 blocks][24 B]  6-bit codes, element i of a block at
+ *                                       bits 6i..6i+5, little-endian
+ *   s [K/128][2 terms][4 blocks]        E8M0 codes
+ * Device pointers; asynchronous on hip_stream.  Returns 0, or -1 on bad
+ * arguments or a launch error. */
+int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint8_t *q,
+                           uint8_t *s, void *hip_stream);
 
 /* Start timing every launch of `kernel` (NULL or "" stops timing).  Creates
  * `capacity` event pairs up front (the only allocation); launches beyond

@@ -63,13 +63,15 @@ RouteWs route_ws(const moe_dims &D) {
 }
 
 struct FfnWs {
-    size_t plan, h, total;
+    size_t plan, h, mfma, total;
 };
 FfnWs ffn_ws(const moe_dims &D) {
     FfnWs w;
     w.plan = 0;
     w.h = al256((size_t)(D.E + 1) * 4);
-    w.total = w.h + al256((size_t)D.T * D.k * D.f * 4);
+    w.mfma = w.h + al256((size_t)D.T * D.k * D.f * 4);
+    w.total = w.mfma;
+    if (moe::mfma_path_ok(D.T, D.d, D.f)) w.total += al256(moe::mfma_ws_bytes(D.T, D.d, D.E, D.k, D.f));
     return w;
 }
 
@@ -250,6 +252,14 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x,
             DiagScope t("plan", s);
             e = moe::launch_plan(offsets, plan, D.E, s);
         }
+        if (moe::mfma_path_ok(D.T, D.d, D.f)) {
+            if (e == hipSuccess) {
+                DiagScope t("mfma_ffn", s);
+                e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, h, rows_out,
+                                         base + L.mfma, D.T, D.d, D.E, D.k, D.f, s);
+            }
+            return device_status(e);
+        }
         if (e == hipSuccess) {
             DiagScope t("gemv_gate_up", s);
             e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
@@ -333,6 +343,18 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
                                         D.E, D.k, perm_ws, s);
             }
         }
+        if (moe::mfma_path_ok(D.T, D.d, D.f)) {
+            if (e == hipSuccess) {
+                DiagScope t("mfma_ffn", s);
+                e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, h, rows_out,
+                                         base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f, s);
+            }
+            if (e == hipSuccess) {
+                DiagScope t("combine", s);
+                e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
+            }
+            return device_status(e);
+        }
         if (e == hipSuccess) {
             DiagScope t("gemv_gate_up", s);
             e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
@@ -356,6 +378,21 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
         }
         return device_status(e);
     });
+}
+
+int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint8_t *q,
+                           uint8_t *s, void *hip_stream) {
+    try {
+        if (!in || !q || !s || rows < 0 || K <= 0 || K % 128 != 0) return -1;
+        if (((uintptr_t)in & 15u) != 0) return -1;
+        hipStream_t st = static_cast<hipStream_t>(hip_stream);
+        hipError_t e = in_is_bf16
+                           ? moe::launch_mx_split_bf16(static_cast<const uint16_t *>(in), rows, K, q, s, st)
+                           : moe::launch_mx_split_f32(static_cast<const float *>(in), rows, K, q, s, st);
+        return e == hipSuccess ? 0 : -1;
+    } catch (...) {
+        return -1;
+    }
 }
 
 int moe_diag_time_kernel(const char *kernel, int capacity) {

@@ -17,6 +17,7 @@ namespace moe {
 // ---------------------------------------------------------------------------
 constexpr int kMaxExperts = 1024;   // top-k keeps <= 16 logits per lane
 constexpr int kMaxTopK = 32;
+constexpr int kMfmaMinT = 128;      // tokens from which the scaled-MFMA expert path runs
 
 // ---------------------------------------------------------------------------
 // Small device helpers.
@@ -165,6 +166,20 @@ hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets
 hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
                                const float *topk_w, const int32_t *row_pos, uint16_t *y,
                                int T, int d, int E, int k, int f, hipStream_t s);
+// Prefill expert FFN on scaled MFMA (x and h as two-term MX E2M3, weights
+// as stored).  Needs d % 128 == 0, f % 128 == 0; ws of mfma_ws_bytes.
+bool mfma_path_ok(int T, int d, int f);
+size_t mfma_ws_bytes(int T, int d, int E, int k, int f);
+hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
+                           const int32_t *sorted_rows, const int32_t *plan, float *h,
+                           uint16_t *rows_out, void *ws, int T, int d, int E, int k, int f,
+                           hipStream_t s);
+// rows x K (K % 128 == 0) -> two-term MX E2M3 codes and scales
+hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, uint8_t *s,
+                                hipStream_t st);
+hipError_t launch_mx_split_f32(const float *in, int rows, int K, uint8_t *q, uint8_t *s,
+                               hipStream_t st);
+
 hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
                           const float *topk_w, uint16_t *y, int T, int d, int k,
                           hipStream_t s);

@@ -38,7 +38,7 @@ class Experts(ctypes.Structure):
 
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_diag_time_kernel", "moe_diag_kernel_time")
+           "moe_diag_time_kernel", "moe_diag_kernel_time", "moe_diag_mx_split_e2m3")
 
 _lib = None
 
@@ -73,6 +73,8 @@ def lib():
         L.moe_layer_forward.argtypes = [DP, P, P, P, EP, P, P, P, P, S, P]
         L.moe_diag_time_kernel.restype = I
         L.moe_diag_time_kernel.argtypes = [ctypes.c_char_p, I]
+        L.moe_diag_mx_split_e2m3.restype = I
+        L.moe_diag_mx_split_e2m3.argtypes = [P, I, I, I, P, P, P]
         L.moe_diag_kernel_time.restype = I
         L.moe_diag_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_longlong)]
@@ -94,6 +96,23 @@ def diag_kernel_time():
     if lib().moe_diag_kernel_time(ctypes.byref(ms), ctypes.byref(n)) != 0:
         raise RuntimeError("moe_diag_kernel_time failed")
     return ms.value, n.value
+
+
+def diag_mx_split_e2m3(rows_tensor, stream=None):
+    """Two-term MX E2M3 split of a [rows][K] bf16 or fp32 device tensor (the
+    scaled-MFMA path's activation staging).  Returns (q uint8 [rows][K/128*192],
+    s uint8 [rows][K/128*8])."""
+    t = rows_tensor.contiguous()
+    R, K = t.shape
+    q = torch.empty((R, K // 128 * 192), dtype=torch.uint8, device=t.device)
+    s = torch.empty((R, K // 128 * 8), dtype=torch.uint8, device=t.device)
+    is_bf16 = 1 if t.dtype == torch.bfloat16 else 0
+    if not is_bf16:
+        assert t.dtype == torch.float32
+    rc = lib().moe_diag_mx_split_e2m3(_ptr(t), is_bf16, R, K, _ptr(q), _ptr(s), _stream(stream))
+    if rc != 0:
+        raise RuntimeError("moe_diag_mx_split_e2m3 failed")
+    return q, s
 
 
 def status_str(status: int) -> str:

@@ -26,7 +26,7 @@ def _declared_functions():
     names = set()
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src))
+        names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src))
     return sorted(names)
 
 

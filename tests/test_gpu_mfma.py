@@ -1,0 +1,153 @@
+"""GPU parity of the scaled-MFMA (prefill) expert path.
+
+* The activation split (two-term MX E2M3 codes and E8M0 scales) must equal
+  the oracle's OCP MX conversion model bit for bit.
+* The layer on shapes that take the MFMA path (T >= 128, d and f multiples
+  of 128) must match the oracle within max|gpu - oracle| <= 1e-2 max|oracle|,
+  with routing and grouping bit-exact; ragged tiles and experts spanning
+  several 128-row tiles are covered.
+* The skewed 4096-token and the 32768-token workloads at full size: routing
+  of sampled tokens bit-exact, their outputs within tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from routed_expert_mxfp4_amd import synth
+
+from test_gpu_parity import (_FULL, _bf16_to_f64, _close, _decode_parity, _dev_experts,
+                             _np_experts, _oracle_o_rows, _small_cfg, dev, full_experts)  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    from routed_expert_mxfp4_amd import moe
+    return moe
+
+
+def _unpack(q, s, K):
+    """GPU split layout -> per-element codes [R][K] and scales [R][K/32]
+    (hi, lo)."""
+    R = q.shape[0]
+    nst = K // 128
+    qb = q.reshape(R, nst, 2, 4, 24)
+    bits = np.unpackbits(qb, axis=-1, bitorder="little").reshape(R, nst, 2, 4, 32, 6)
+    codes = (bits * (1 << np.arange(6))).sum(-1).astype(np.uint8)     # [R][st][term][g][32]
+    sc = s.reshape(R, nst, 2, 4)
+    hc = codes[:, :, 0].reshape(R, K)
+    lc = codes[:, :, 1].reshape(R, K)
+    hs = sc[:, :, 0].reshape(R, K // 32)
+    ls = sc[:, :, 1].reshape(R, K // 32)
+    return hs, hc, ls, lc
+
+
+def _split_inputs():
+    rng = np.random.default_rng(77)
+    R, K = 24, 512
+    v = rng.standard_normal((R, K)) * np.exp(rng.standard_normal((R, K)) * 3)
+    v[0, :32] = 0.0                                   # all-zero block
+    v[1, :32] = -0.0                                  # negative zeros
+    v[2, :64] = rng.standard_normal(64) * 1e-40       # fp32 subnormals
+    v[3, :32] = 1e30 * rng.standard_normal(32)        # large
+    # exact E2M3 midpoints relative to the block scale (ties to even)
+    grid = np.array([0, 1, 2, 3, 4, 5, 6, 7]) / 8.0
+    mids = (grid[:-1] + grid[1:]) / 2
+    v[4, :32] = np.concatenate([[7.5], mids, -mids, mids * 2 + 0, np.full(32 - 1 - 21, 0.3)])[:32]
+    v[5, :32] = np.linspace(-7.9, 7.9, 32)            # saturation above 7.5
+    return v.astype(np.float32)
+
+
+def test_activation_split_bit_exact_fp32(dev):
+    moe = _moe()
+    v = _split_inputs()
+    q, s = moe.diag_mx_split_e2m3(torch.from_numpy(v).to(dev))
+    torch.cuda.synchronize()
+    hs, hc, ls, lc = _unpack(q.cpu().numpy(), s.cpu().numpy(), v.shape[1])
+    ohs, ohc, ols, olc = oracle.mx_split_rows(oracle.FMT_E2M3, v)
+    np.testing.assert_array_equal(hs, ohs)
+    np.testing.assert_array_equal(ls, ols)
+    np.testing.assert_array_equal(hc, ohc)
+    np.testing.assert_array_equal(lc, olc)
+
+
+def test_activation_split_bit_exact_bf16_workload_rows(dev):
+    moe = _moe()
+    cfg = synth.CONFIGS[4]
+    x = synth.gen_x(cfg, tokens=range(16))
+    q, s = moe.diag_mx_split_e2m3(x.to(dev))
+    torch.cuda.synchronize()
+    hs, hc, ls, lc = _unpack(q.cpu().numpy(), s.cpu().numpy(), cfg.d)
+    ohs, ohc, ols, olc = oracle.mx_split_rows(oracle.FMT_E2M3, x.float().numpy())
+    np.testing.assert_array_equal(hs, ohs)
+    np.testing.assert_array_equal(hc, ohc)
+    np.testing.assert_array_equal(ls, ols)
+    np.testing.assert_array_equal(lc, olc)
+
+
+MFMA_CASES = [
+    # (T, d, E, k, f, seed)
+    (200, 256, 16, 4, 128, 71),      # ragged tiles
+    (400, 256, 8, 4, 256, 72),       # ~200 rows per expert: two 128-row tiles each
+    (300, 512, 40, 6, 128, 73),
+    (128, 384, 64, 2, 384, 74),      # K steps 3, several experts with one row
+]
+
+
+@pytest.mark.parametrize("case", MFMA_CASES, ids=[str(c) for c in MFMA_CASES])
+def test_mfma_path_small(dev, case):
+    moe = _moe()
+    T, d, E, k, f, seed = case
+    cfg = _small_cfg(T, d, E, k, f, seed)
+    print("case", case, flush=True)
+    L = synth.gen_layer(cfg)
+    x16, wr16 = synth.as_u16(L["x"]), synth.as_u16(L["router_w"])
+    W = _np_experts(L)
+    lg = oracle.router_logits(x16, wr16)
+    ids_o, w_o = oracle.topk_softmax(lg, k)
+    counts_o, offsets_o, sr_o, rp_o = oracle.permute(ids_o, E)
+    o_rows = _oracle_o_rows(x16, ids_o, W, d, f)
+    y_o = np.einsum("tj,tjd->td", w_o, o_rows)
+    x, wr = L["x"].to(dev), L["router_w"].to(dev)
+    ex = _dev_experts(L, dev)
+    ids, w = moe.moe_route(x, wr, k)
+    counts, offsets, sr, rp = moe.moe_permute(ids, E)
+    rows_out = moe.moe_expert_ffn(x, ex, offsets, sr, k)
+    y2, ids2, w2 = moe.moe_layer_forward(x, wr, ex, k, return_routing=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    np.testing.assert_array_equal(sr.cpu().numpy(), sr_o)
+    np.testing.assert_array_equal(ids2.cpu().numpy(), ids_o)
+    o_sorted = o_rows.reshape(T * k, d)[sr_o]
+    _close(_bf16_to_f64(rows_out), o_sorted, "rows_out")
+    _close(_bf16_to_f64(y2), y_o, "layer_forward y")
+
+
+def test_mfma_path_deterministic(dev):
+    moe = _moe()
+    cfg = _small_cfg(256, 256, 12, 3, 128, 75)
+    L = synth.gen_layer(cfg)
+    x, wr, ex = L["x"].to(dev), L["router_w"].to(dev), _dev_experts(L, dev)
+    a = moe.moe_layer_forward(x, wr, ex, cfg.k)
+    b = moe.moe_layer_forward(x, wr, ex, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_skewed_prefill_full_size(dev, full_experts):
+    cfg = synth.CONFIGS[3]
+    full_experts(3)
+    ids = _decode_parity(dev, cfg, 0, [0, 1777, 4095])
+    # the Zipf bias concentrates load: hottest expert well above the mean
+    counts = torch.bincount(ids.flatten().long(), minlength=cfg.E).cpu().numpy()
+    ratio = counts.max() / (cfg.T * cfg.k / cfg.E)
+    print("max/mean expert load", ratio)
+    assert 5.0 <= ratio <= 20.0
+    assert (counts > 0).all()
+
+
+def test_long_prefill_full_size(dev, full_experts):
+    cfg = synth.CONFIGS[4]
+    full_experts(4)
+    _decode_parity(dev, cfg, 0, [0, 12345, 32767])
