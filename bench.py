@@ -5,13 +5,17 @@
 
 Default workload: one-token decode (T=1, d=7168, E=896 experts, top-16,
 f=1536) over 1000 distinct seeded tokens; one step = one moe_layer_forward
-call on one token (router, top-k, grouping, gate/up + SwiGLU, down,
-combine), cycling through the tokens so that no token is timed twice in a
-row.  Inputs are synthetic and resident in HBM before timing starts.
+call on one batch (router, top-k, grouping, gate/up + SwiGLU, down,
+combine), cycling through the batches so that no token is timed twice in a
+row.  Inputs are synthetic and resident in HBM before timing starts.  The
+other workloads (batched-decode T=64, zipf-prefill T=4096, long-prefill
+T=32768) time the same call on their own shapes.
 
 Prints one JSON line: throughput (tokens/s), the roofline of the dominant
-kernel (HIP events on the library's own stream inside the timed region),
-and the CPU oracle timed on a bounded sample on this host.
+kernel (HIP events on the library's own stream inside the timed region):
+the gate/up GEMV against HBM bandwidth for decode-sized T, the scaled-MFMA
+gate/up GEMM against the MXFP4 matrix peak for prefill-sized T; and the
+CPU oracle timed on a bounded sample on this host.
 """
 from __future__ import annotations
 
@@ -30,16 +34,23 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 WORKLOADS = {"tiny": 0, "decode": 1, "batched-decode": 2, "zipf-prefill": 3, "long-prefill": 4}
-DOMINANT = "gemv_gate_up"
+DEFAULT_STEPS = {"tiny": 1000, "decode": 1000, "batched-decode": 200, "zipf-prefill": 20,
+                 "long-prefill": 5}
 KERNELS = ("router_logits", "topk_softmax", "permute", "topk_permute", "gemv_gate_up",
-           "down_combine", "gemv_down", "combine")
+           "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "mx_split_h", "down_mfma",
+           "combine")
+MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 / MXFP6, published
+MFMA_MIN_T = 128                # the library's scaled-MFMA path starts here
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: decode 1000, batched-decode 200, "
+                         "zipf-prefill 20, long-prefill 5, tiny 1000)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 20 decode-sized, 2 prefill)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
     ap.add_argument("--cpu-sample", type=int, default=2,
                     help="tokens of the workload the CPU oracle runs (0: skip)")
@@ -141,6 +152,15 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[WORKLOADS[args.workload]]
+    if args.steps is None:
+        args.steps = DEFAULT_STEPS[args.workload]
+    if args.warmup is None:
+        args.warmup = 2 if cfg.T >= MFMA_MIN_T else 20
+    # the kernel that dominates the step: the expert-weight stream of the
+    # gate/up GEMV (HBM-bound) for decode-sized T, the scaled-MFMA gate/up
+    # GEMM (matrix-core-bound) for prefill-sized T
+    mfma = cfg.T >= MFMA_MIN_T and cfg.d % 128 == 0 and cfg.f % 128 == 0
+    dominant = "gate_up_mfma" if mfma else "gemv_gate_up"
     L = moe.lib()
 
     # ---- inputs, resident in HBM before timing --------------------------------
@@ -175,7 +195,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, dominant kernel timed with HIP events ------------
-    moe.diag_time_kernel(DOMINANT, capacity=max(1, args.steps))
+    moe.diag_time_kernel(dominant, capacity=max(1, args.steps))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(args.warmup, args.steps)
@@ -210,16 +230,32 @@ def main():
         touched.append(torch.unique(ids_probe).numel())
     torch.cuda.synchronize()
     mean_touched = sum(touched) / len(touched)
-    bytes_per_launch = mean_touched * per_expert_gu
     avg_launch_s = (dom_ms / dom_n) * 1e-3 if dom_n else float("nan")
-    achieved = bytes_per_launch / avg_launch_s / 1e9
-    src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_gemv.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    traffic = traffic_from_profiles(DOMINANT, args.workload, sha)
-
     tokens = args.steps * cfg.T
     value = tokens / elapsed
     layer_bytes = mean_touched * cfg.expert_bytes
+    layer_flops = 2.0 * cfg.T * cfg.k * 3 * cfg.d * cfg.f
+    if mfma:
+        # gate/up: every routed row times the [2f x d] gate/up matrix
+        flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
+        achieved = flops_per_launch / avg_launch_s / 1e12
+        roofline = {"bound": "mfma", "kernel": dominant, "achieved": achieved,
+                    "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / MXFP4_PEAK_TFLOPS, "traffic": None,
+                    "algorithmic_flops_per_launch": flops_per_launch,
+                    "mfma_passes_per_product": 2,
+                    "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
+    else:
+        bytes_per_launch = mean_touched * per_expert_gu
+        achieved = bytes_per_launch / avg_launch_s / 1e9
+        src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_gemv.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                    "traffic": traffic_from_profiles(dominant, args.workload, sha),
+                    "algorithmic_bytes_per_launch": bytes_per_launch,
+                    "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
+
     out = {
         "metric": "MoE-layer tokens/s + expert-weight GB/s (decode) / MXFP4 TFLOP/s (prefill), 1 GPU",
         "value": value,
@@ -236,15 +272,13 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "f": cfg.f, "distinct_batches": n_batches,
                    "weights": "MXFP4 (E2M1 codes + E8M0 scale per 32), resident in HBM",
-                   "activations": "bf16", "accumulate": "fp32"},
+                   "activations": "bf16", "accumulate": "fp32",
+                   "expert_path": "scaled MFMA" if mfma else "GEMV"},
         "expert_weight_GBps": layer_bytes * args.steps / elapsed / 1e9,
         "expert_weight_hbm_frac": layer_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBPS,
-        "tflops": 2.0 * tokens * cfg.k * 3 * cfg.d * cfg.f / elapsed / 1e12,
-        "roofline": {"bound": "hbm", "kernel": DOMINANT, "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n},
+        "tflops": layer_flops * args.steps / elapsed / 1e12,
+        "mxfp4_frac": layer_flops * args.steps / elapsed / 1e12 / MXFP4_PEAK_TFLOPS,
+        "roofline": roofline,
         "cpu_baseline": None,
         "breakdown": breakdown,
     }

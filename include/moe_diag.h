@@ -7,7 +7,8 @@
  * Kernel names: "router_logits", "topk_softmax", "permute", "topk_permute"
  * (the two fused, small T), "plan", "gemv_gate_up", "gemv_down",
  * "down_combine", "combine", "mfma_ffn" (the whole scaled-MFMA expert
- * FFN of large T: activation split, gate/up, h split, down).
+ * FFN of large T), and its parts "mx_split_x", "gate_up_mfma",
+ * "mx_split_h", "down_mfma".
  */
 #ifndef ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 #define ROUTED_EXPERT_MXFP4_MOE_DIAG_H
@@ -24,14 +25,17 @@ extern "C" {
  * cut into 32-element blocks and each block a into two OCP MX E2M3 terms,
  * hi = MX(a), lo = MX(a - hi): shared exponent X = floor(log2 max|.|) - 2
  * clamped to [-127, 127] (E8M0 code X + 127; all-zero block -> code 0),
- * elements rounded to nearest even and saturated at 7.5.  Output per row:
- *   q [K/128][2 terms][4 blocks][24 B]  6-bit codes, element i of a block at
- *                                       bits 6i..6i+5, little-endian
- *   s [K/128][2 terms][4 blocks]        E8M0 codes
- * Device pointers; asynchronous on hip_stream.  Returns 0, or -1 on bad
- * arguments or a launch error. */
-int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint8_t *q,
-                           uint8_t *s, void *hip_stream);
+ * elements rounded to nearest even and saturated at 7.5.  Output `out`,
+ * rows x (K/128) x 208 bytes; per row and 128-element step:
+ *   block g (0..3) at byte 48 g: [hi codes 0..15][lo codes 0..15]
+ *                                [hi codes 16..23][lo codes 16..23]
+ *   byte 192 + 2 g: E8M0 code of hi, 193 + 2 g: of lo; bytes 200..207 zero
+ * where a term's "codes" are its 24-byte stream of 6-bit fields, element i
+ * of the block at bits 6i..6i+5, little-endian.  Device pointers;
+ * asynchronous on hip_stream.  Returns 0, or -1 on bad arguments or a
+ * launch error. */
+int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint8_t *out,
+                           void *hip_stream);
 
 /* Start timing every launch of `kernel` (NULL or "" stops timing).  Creates
  * `capacity` event pairs up front (the only allocation); launches beyond

@@ -11,10 +11,14 @@
 // and accumulate into one fp32 tile.  A single 6-bit term keeps only ~3
 // significant bits and misses the output tolerance; two terms keep ~7.
 //
-// Layouts (per row; a "step" is 128 K elements = 4 MX blocks):
-//   q [rows][K/128][2 terms][4 blocks][24 B]   E2M3 codes, 6-bit fields
-//                                             packed little-endian
-//   s [rows][K/128][2 terms][4 blocks]        E8M0 scale codes
+// Split layout: per row, per K step of 128 elements (4 MX blocks), 208 bytes
+//   block g (0..3) at 48 g:  [hi codes 0..15][lo codes 0..15]
+//                            [hi codes 16..23][lo codes 16..23]
+//   192 + 2 g: E8M0 scale of hi, 193 + 2 g: of lo;  200..207: zero
+// where "codes" is the block's 24-byte stream of 6-bit E2M3 fields packed
+// little-endian (the MFMA operand format).  A lane's fp6 operand (6 dwords)
+// is then one 16-byte read plus one 8-byte read per term.
+//
 // MFMA operand layout (16x16x128): lane l holds row (l % 16) of a 16-row
 // tile and K block (l / 16) of the step; the output tile holds
 // C[4 * (l / 16) + i][l % 16] in lane l, register i.
@@ -24,10 +28,11 @@ namespace moe {
 namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kStepQ = 192;      // bytes of codes per row per step (2 terms x 96)
-constexpr int kStepS = 8;        // scale bytes per row per step
+constexpr int kStepBytes = 208;  // split bytes per row per K step
+constexpr int kSlotsRow = 13;    // 16-byte pieces per row per K step
 
 // ---------------------------------------------------------------------------
 // MX E2M3 conversion (OCP MX v1.0): shared exponent X = floor(log2(amax)) - 2
@@ -80,10 +85,16 @@ __device__ __forceinline__ float2 load_pair_f32<float>(const float *p) {
     return *reinterpret_cast<const float2 *>(p);
 }
 
+// Byte offset, inside a block's 48 bytes, of byte o (0..23) of term t's
+// code stream.
+__device__ __forceinline__ int code_byte(int t, int o) {
+    return o < 16 ? 16 * t + o : 32 + 8 * t + (o - 16);
+}
+
 // Packs the 12-bit code pairs of the 16 lanes of a group (lane j: elements
-// 2j, 2j+1 of the block) into the block's 24 bytes: lanes j % 4 == 0 write
-// 6 bytes (three 16-bit words) covering lanes j .. j+3.
-__device__ __forceinline__ void store_block_codes(uint8_t *dst24, uint32_t pair12, int j) {
+// 2j, 2j+1 of the block) into term t's 24-byte stream: lanes j % 4 == 0
+// write stream bytes 6 (j / 4) .. +5 as three 16-bit words.
+__device__ __forceinline__ void store_block_codes(uint8_t *blk48, int t, uint32_t pair12, int j) {
     const uint32_t p1 = (uint32_t)__shfl_down((int)pair12, 1, 16);
     const uint32_t p2 = (uint32_t)__shfl_down((int)pair12, 2, 16);
     const uint32_t p3 = (uint32_t)__shfl_down((int)pair12, 3, 16);
@@ -92,19 +103,19 @@ __device__ __forceinline__ void store_block_codes(uint8_t *dst24, uint32_t pair1
                                         ((unsigned long long)p1 << 12) |
                                         ((unsigned long long)p2 << 24) |
                                         ((unsigned long long)p3 << 36);
-        uint16_t *w = reinterpret_cast<uint16_t *>(dst24 + 6 * (j >> 2));
-        w[0] = (uint16_t)(bits & 0xFFFFu);
-        w[1] = (uint16_t)((bits >> 16) & 0xFFFFu);
-        w[2] = (uint16_t)((bits >> 32) & 0xFFFFu);
+        const int o = 6 * (j >> 2);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            *reinterpret_cast<uint16_t *>(blk48 + code_byte(t, o + 2 * q)) =
+                (uint16_t)((bits >> (16 * q)) & 0xFFFFu);
     }
 }
 
 // One wave per (row, step): lane l handles elements 2j, 2j+1 (j = l % 16) of
-// MX block g = l / 16 of the step.  Rows are `src_row(r)` of the input.
+// MX block g = l / 16 of the step.
 template <typename In>
 __global__ __launch_bounds__(256) void mx_split_e2m3_kernel(const In *__restrict__ in, int rows,
-                                                            int K, uint8_t *__restrict__ q,
-                                                            uint8_t *__restrict__ s) {
+                                                            int K, uint8_t *__restrict__ q) {
     const int lane = threadIdx.x & 63;
     const int nsteps = K >> 7;
     const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -112,8 +123,7 @@ __global__ __launch_bounds__(256) void mx_split_e2m3_kernel(const In *__restrict
     const int r = (int)(item / nsteps), st = (int)(item % nsteps);
     const int g = lane >> 4, j = lane & 15;
     const float2 v = load_pair_f32<In>(in + (size_t)r * K + (size_t)st * 128 + g * 32 + 2 * j);
-    uint8_t *qrow = q + ((size_t)r * nsteps + st) * kStepQ;
-    uint8_t *srow = s + ((size_t)r * nsteps + st) * kStepS;
+    uint8_t *out = q + ((size_t)r * nsteps + st) * kStepBytes;
     // hi term
     const float amax_h = group16_max_f32(fmaxf(fabsf(v.x), fabsf(v.y)));
     const int xh = mx_exponent(amax_h);
@@ -124,12 +134,13 @@ __global__ __launch_bounds__(256) void mx_split_e2m3_kernel(const In *__restrict
     const float amax_l = group16_max_f32(fmaxf(fabsf(r0), fabsf(r1)));
     const int xl = mx_exponent(amax_l);
     const uint32_t l0 = e2m3_encode(ldexpf(r0, -xl)), l1 = e2m3_encode(ldexpf(r1, -xl));
-    store_block_codes(qrow + g * 24, h0 | (h1 << 6), j);
-    store_block_codes(qrow + 96 + g * 24, l0 | (l1 << 6), j);
+    store_block_codes(out + 48 * g, 0, h0 | (h1 << 6), j);
+    store_block_codes(out + 48 * g, 1, l0 | (l1 << 6), j);
     if (j == 0) {
-        srow[g] = (uint8_t)(xh + 127);
-        srow[4 + g] = (uint8_t)(xl + 127);
+        out[192 + 2 * g] = (uint8_t)(xh + 127);
+        out[193 + 2 * g] = (uint8_t)(xl + 127);
     }
+    if (lane == 0) *reinterpret_cast<uint2 *>(out + 200) = make_uint2(0u, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -164,8 +175,8 @@ __global__ __launch_bounds__(1024) void mfma_plan_kernel(const int32_t *__restri
     if (tid == 1023) tiles[0] = base + inc;
 }
 
-// Which (active expert, m-tile) a global m-tile index belongs to: binary
-// search over the tile prefix of the plan's active experts.
+// Which active expert a global m-tile index belongs to: binary search over
+// the tile prefix of the plan's active experts.
 __device__ __forceinline__ int find_expert(const int32_t *tiles, int nact, int mt) {
     int lo = 0, hi = nact - 1;
     while (lo < hi) {
@@ -177,263 +188,349 @@ __device__ __forceinline__ int find_expert(const int32_t *tiles, int nact, int m
 }
 
 // ---------------------------------------------------------------------------
-// Grouped scaled-MFMA GEMM tile: 128 rows x 128 columns, K in steps of 128,
-// 4 waves in a 2 x 2 arrangement (64 x 64 per wave = 4 x 4 MFMA tiles, two A
-// terms each).  LDS holds two stages (double buffer); the next step's global
-// loads sit in registers while the current step computes.
+// Grouped GEMM block: 128 rows of one expert x 512 weight rows (gate/up:
+// 256 gate + the matching 256 up rows; down: 512 output columns), K in steps
+// of 128.  Four waves, one per SIMD, each owning all 128 rows x 128 weight
+// rows: 8 x 8 MFMA tiles, 256 fp32 accumulators, two MFMAs (hi, lo) per
+// tile and step.
+//
+// Data movement per step:
+//   A (split activations, shared by the four waves): global -> LDS direct
+//     loads into a ring of kNst stages, issued kNst - 1 steps ahead; each
+//     wave waits for its own loads (vmcnt) and a barrier publishes them.
+//     Fragment reads are explicit ds_read instructions so that the next
+//     stages' loads stay in flight while a stage is read.
+//   B (weights, private to a wave): global -> registers, 16 bytes of codes
+//     and one scale byte per lane and tile, issued two steps ahead into a
+//     three-deep register ring.
+// Every step issues the same number of loads (steps past the end re-load
+// the last step), so the wait counts are constants.
 // ---------------------------------------------------------------------------
-constexpr int kAStride = 208;    // LDS bytes per A row (192 + pad: 16-B aligned, conflict-free b64 reads)
-constexpr int kBStride = 80;     // LDS bytes per B row (64 + pad: conflict-free b128 reads)
+constexpr int kNst = 4;                              // LDS stages
+constexpr int kDmaPerWave = 7;                       // 128 x 13 pieces = 26 wave loads, 28 issued
+constexpr int kStageBytes = 4 * kDmaPerWave * 1024;  // 28672 (26624 used + overflow of the pad loads)
+constexpr int kLdsBytes = kNst * kStageBytes;        // 114688
+constexpr int kBLoads = 16;                          // per wave per step: 8 code + 8 scale loads
+constexpr int kPerStep = kBLoads + kDmaPerWave;      // vector memory instructions per step
+static_assert(kBM * kSlotsRow <= 4 * kDmaPerWave * 64, "direct loads must cover the stage");
+static_assert(kBLoads + 2 * kPerStep <= 63, "vmcnt range");
 
-struct alignas(16) Stage {
-    uint8_t a[kBM][kAStride];
-    uint8_t as[kBM][kStepS];
-    uint8_t b[128][kBStride];
-    uint8_t bs[128][4];
-};
+// Global -> LDS direct load of 16 bytes per lane (lane l fills LDS bytes
+// m0 + 16 l).  Written as inline asm so that the compiler's wait-count
+// bookkeeping sees only the weight loads (all of one kind, hence exact
+// waits); the direct loads are waited for explicitly with vmcnt.  m0 holds
+// nothing else in these kernels (no other direct loads, GWS or messages).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void direct16(uint32_t voff, const uint8_t *sbase, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds_addr)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
-__device__ __forceinline__ i32x8_t load_a_frag(const uint8_t *p) {
-    const uint2 w0 = *reinterpret_cast<const uint2 *>(p);
-    const uint2 w1 = *reinterpret_cast<const uint2 *>(p + 8);
-    const uint2 w2 = *reinterpret_cast<const uint2 *>(p + 16);
-    i32x8_t v = {(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y, (int)w2.x, (int)w2.y, 0, 0};
+// s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left free.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int OFF>
+__device__ __forceinline__ u32x4_t ds_read128(uint32_t a) {
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read64(uint32_t a) {
+    u32x2_t v;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF));
+    return v;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t ds_read_u16(uint32_t a) {
+    uint32_t v;
+    asm volatile("ds_read_u16 %0, %1 offset:%2" : "=v"(v) : "v"(a), "i"(OFF));
     return v;
 }
 
-__device__ __forceinline__ i32x8_t load_b_frag(const uint8_t *p) {
-    const uint4 w = *reinterpret_cast<const uint4 *>(p);
-    i32x8_t v = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-    return v;
-}
-
-// The tile step: 32 MFMAs per wave.  acc[mt][nt] += A(mt) . B(nt) for both
-// A terms, scales per lane.
-// B rows of the wave's four 16-column tiles: gate/up (kGateUp) takes
-// gate rows wn*32 + {0,16} and the matching up rows 64 + wn*32 + {0,16};
-// down takes rows wn*64 + {0,16,32,48}.
-template <bool kGateUp>
-__device__ __forceinline__ int b_tile_row(int wn, int nt) {
-    return kGateUp ? (nt >> 1) * 64 + wn * 32 + (nt & 1) * 16 : wn * 64 + nt * 16;
-}
-
-template <bool kGateUp>
-__device__ __forceinline__ void mfma_step(const Stage &S, int wm, int wn, int lane,
-                                          f32x4_t (&acc)[4][4]) {
-    const int r16 = lane & 15, g = lane >> 4;
-    i32x8_t b[4];
-    int bsc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int br = b_tile_row<kGateUp>(wn, nt) + r16;
-        b[nt] = load_b_frag(&S.b[br][g * 16]);
-        bsc[nt] = S.bs[br][g];
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int ar = wm * 64 + mt * 16 + r16;
-        const i32x8_t ahi = load_a_frag(&S.a[ar][g * 24]);
-        const i32x8_t alo = load_a_frag(&S.a[ar][96 + g * 24]);
-        const int shi = S.as[ar][g], slo = S.as[ar][4 + g];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                ahi, b[nt], acc[mt][nt], 2, 4, 0, shi, 0, bsc[nt]);
-            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                alo, b[nt], acc[mt][nt], 2, 4, 0, slo, 0, bsc[nt]);
-        }
-    }
-}
-
-// Global -> LDS loads of one step go straight into LDS (gfx950 direct
-// loads: lane l of a wave instruction fills LDS bytes base + size * l), so
-// no registers hold the next step.  Each LDS region is a run of equal slots
-// (A: 13 slots of 16 B per row, the 13th a pad slot that repeats a valid
-// piece; B: 5 slots per row; scales in 4-byte slots), and wave w issues the
-// instructions covering slots 64 * (4 i + w) .. + 63.
-struct StepSrc {
-    const uint8_t *aq, *as;
-    const int *a_rowidx;
-    size_t a_rowq, a_rows;
-    const uint8_t *bq, *bsb;
-    int b_r0, b_r1;
-    size_t b_code_row;
-    int b_nblk;
+struct AFrag {
+    i32x8_t hi, lo;
+    uint32_t sc;   // byte 0: hi scale, byte 1: lo scale
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void direct16(const void *g, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void direct4(const void *g, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds_base, 4, 0, 0);
-}
-
-constexpr int kASlots = kBM * (kAStride / 16);     // 1664 = 26 x 64
-constexpr int kBSlots = 128 * (kBStride / 16);     // 640  = 10 x 64
-static_assert(kASlots % 64 == 0 && kBSlots % 64 == 0, "slot runs must fill waves");
-
-__device__ __forceinline__ void issue_step(Stage &S, const StepSrc &src, int kk, int wid,
-                                           int lane) {
-    uint8_t *abase = &S.a[0][0];
-    for (int i = 0; 64 * (4 * i + wid) < kASlots; ++i) {
-        const int s0 = 64 * (4 * i + wid), sl = s0 + lane;
-        const int r = sl / (kAStride / 16), pc = min(sl - r * (kAStride / 16), kStepQ / 16 - 1);
-        direct16(src.aq + (size_t)src.a_rowidx[r] * src.a_rowq + (size_t)kk * kStepQ + pc * 16,
-                 abase + 16 * s0);
-    }
-    {   // A scales: 256 four-byte slots (2 per row), one instruction per wave
-        const int sl = 64 * wid + lane, r = sl >> 1;
-        direct4(src.as + (size_t)src.a_rowidx[r] * src.a_rows + (size_t)kk * kStepS + (sl & 1) * 4,
-                &S.as[0][0] + 4 * 64 * wid);
-    }
-    uint8_t *bbase = &S.b[0][0];
-    for (int i = 0; 64 * (4 * i + wid) < kBSlots; ++i) {
-        const int s0 = 64 * (4 * i + wid), sl = s0 + lane;
-        const int n = sl / (kBStride / 16), pc = min(sl - n * (kBStride / 16), 3);
-        const int row = n < 64 ? src.b_r0 + n : src.b_r1 + (n - 64);
-        direct16(src.bq + (size_t)row * src.b_code_row + (size_t)kk * 64 + pc * 16, bbase + 16 * s0);
-    }
-    if (wid < 2) {   // B scales: 128 four-byte slots
-        const int n = 64 * wid + lane;
-        const int row = n < 64 ? src.b_r0 + n : src.b_r1 + (n - 64);
-        direct4(src.bsb + (size_t)row * src.b_nblk + (size_t)kk * 4, &S.bs[0][0] + 4 * 64 * wid);
-    }
+// Issues the five LDS reads of m-tile MT's A fragment (a: this lane's row /
+// block address in the stage, s: its scale address).
+template <int MT>
+__device__ __forceinline__ void read_afrag(AFrag &f, uint32_t a, uint32_t s) {
+    constexpr int o = MT * 16 * kStepBytes;
+    const u32x4_t h0 = ds_read128<o>(a);
+    const u32x4_t l0 = ds_read128<o + 16>(a);
+    const u32x2_t h1 = ds_read64<o + 32>(a);
+    const u32x2_t l1 = ds_read64<o + 40>(a);
+    f.sc = ds_read_u16<o>(s);
+    const u32x4_t h1w = __builtin_shufflevector(h1, h1, 0, 1, -1, -1);
+    const u32x4_t l1w = __builtin_shufflevector(l1, l1, 0, 1, -1, -1);
+    f.hi = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(h0, h1w, 0, 1, 2, 3, 4, 5, -1, -1));
+    f.lo = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(l0, l1w, 0, 1, 2, 3, 4, 5, -1, -1));
 }
 
-// Common GEMM core: computes the 128 x 128 tile into acc (per wave 64 x 64).
-template <bool kGateUp>
-__device__ __forceinline__ void gemm_tile(Stage *stages, const StepSrc &src, int nsteps, int wm,
-                                          int wn, f32x4_t (&acc)[4][4]) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    issue_step(stages[0], src, 0, wid, lane);
-    __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0): this wave's loads landed
-    __syncthreads();                                   // ... and every other wave's
-    for (int kk = 0; kk < nsteps; ++kk) {
-        const int cur = kk & 1;
-        if (kk + 1 < nsteps) issue_step(stages[cur ^ 1], src, kk + 1, wid, lane);
-        mfma_step<kGateUp>(stages[cur], wm, wn, lane, acc);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
+// Waits until at most N LDS reads are outstanding; the fragment's values
+// are tied to the wait so that no use is scheduled before it.
+template <int N>
+__device__ __forceinline__ void afrag_ready(AFrag &f) {
+    asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(f.hi), "+v"(f.lo), "+v"(f.sc) : "n"(N));
+}
+
+struct BRing {
+    uint4 q[3][8];
+    uint32_t s[3][8];
+};
+
+struct GemmArgs {
+    rsrc_t bq, bs;              // this expert's weight codes / scales
+    uint32_t boff, soff;        // this lane's offsets in its first B tile (codes, scales)
+    uint32_t tq[8], ts[8];      // wave-uniform offsets of the 8 B tiles (codes, scales)
+    uint32_t sshift;            // bit position of this lane's scale byte in a step's dword
+    int nsteps;
+};
+
+template <int R>
+__device__ __forceinline__ void issue_b(BRing &br, const GemmArgs &ga, int j) {
+    const uint32_t jj = (uint32_t)min(j, ga.nsteps - 1);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) br.q[R][nt] = buf_load16(ga.bq, ga.boff, ga.tq[nt] + jj * 64u);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) br.s[R][nt] = buf_load4(ga.bs, ga.soff, ga.ts[nt] + jj * 4u);
+}
+
+__device__ __forceinline__ void issue_a(uint32_t lds_addr, const uint8_t *aq,
+                                        const uint32_t (&src)[kDmaPerWave], int nsteps, int j,
+                                        int wid) {
+    const uint32_t jj = (uint32_t)min(j, nsteps - 1);
+    const uint32_t stage = lds_addr + (uint32_t)((j & (kNst - 1)) * kStageBytes);
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i)
+        direct16(src[i] + jj * (uint32_t)kStepBytes, aq,
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(stage + 1024u * (4 * i + wid))));
+}
+
+// The scale operand reads byte 0 of the register (bits above are ignored).
+template <int R>
+__device__ __forceinline__ void mfma_mt(f32x4_t (&acc)[8], const AFrag &a, const BRing &br,
+                                        const uint32_t (&bsc)[8]) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const uint4 q = br.q[R][nt];
+        const i32x8_t b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.hi, b, acc[nt], 2, 4, 0,
+                                                                   (int)a.sc, 0, (int)bsc[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const uint4 q = br.q[R][nt];
+        const i32x8_t b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+        acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.lo, b, acc[nt], 2, 4, 1,
+                                                                   (int)a.sc, 0, (int)bsc[nt]);
     }
 }
 
-// ---------------------------------------------------------------------------
-// gate/up: tile = 128 rows x (64 gate + 64 up) columns of one expert.
-// Epilogue: h = silu(gate) * up in fp32.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gate_up_mfma_kernel(
-    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xs, ExpertArgs W,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ sorted_rows,
-    const int32_t *__restrict__ plan, const int32_t *__restrict__ tiles, float *__restrict__ h,
-    int T, int d, int E, int k, int f, int mt_max) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    Stage *stages = reinterpret_cast<Stage *>(smem);
-    __shared__ int a_rowidx[kBM];
-    const int nt_blk = blockIdx.x / mt_max;           // 64-column block of f
-    const int mt = blockIdx.x - nt_blk * mt_max;      // global m-tile
-    const int total = tiles[0];
-    if (mt >= total) return;
+// One K step: wait for stage kk, queue step kk + 2's weights and step
+// kk + 3's activations, then 128 MFMAs (A fragments read one m-tile ahead).
+template <int R>
+__device__ __forceinline__ void gemm_step(f32x4_t (&acc)[8][8], BRing &br, const GemmArgs &ga,
+                                          const uint8_t *aq, const uint32_t (&src)[kDmaPerWave],
+                                          uint32_t lds_addr, uint32_t a_lane, uint32_t s_lane,
+                                          int kk, int wid, bool live) {
+    // loads after this wave's part of stage kk: B(kk - 1), then two whole
+    // steps (issue order per step: activations j + 3, then weights j + 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBLoads + 2 * kPerStep));
+    __builtin_amdgcn_s_barrier();                        // everyone's part; stage kk-1 free
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(lds_addr, aq, src, ga.nsteps, kk + 3, wid);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b<(R + 2) % 3>(br, ga, kk + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!live) return;
+    const uint32_t st = lds_addr + (uint32_t)((kk & (kNst - 1)) * kStageBytes);
+    const uint32_t a = st + a_lane, s = st + s_lane;
+    uint32_t bsc[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) bsc[nt] = br.s[R][nt] >> ga.sshift;
+    AFrag f0, f1;
+    read_afrag<0>(f0, a, s);
+    read_afrag<1>(f1, a, s);
+    afrag_ready<5>(f0);
+    mfma_mt<R>(acc[0], f0, br, bsc);
+    read_afrag<2>(f0, a, s);
+    afrag_ready<5>(f1);
+    mfma_mt<R>(acc[1], f1, br, bsc);
+    read_afrag<3>(f1, a, s);
+    afrag_ready<5>(f0);
+    mfma_mt<R>(acc[2], f0, br, bsc);
+    read_afrag<4>(f0, a, s);
+    afrag_ready<5>(f1);
+    mfma_mt<R>(acc[3], f1, br, bsc);
+    read_afrag<5>(f1, a, s);
+    afrag_ready<5>(f0);
+    mfma_mt<R>(acc[4], f0, br, bsc);
+    read_afrag<6>(f0, a, s);
+    afrag_ready<5>(f1);
+    mfma_mt<R>(acc[5], f1, br, bsc);
+    read_afrag<7>(f1, a, s);
+    afrag_ready<5>(f0);
+    mfma_mt<R>(acc[6], f0, br, bsc);
+    afrag_ready<0>(f1);
+    mfma_mt<R>(acc[7], f1, br, bsc);
+}
+
+// The block's tile: which expert, which 128 rows of it, which 512 weight
+// rows.  Blocks are spread over the 8 XCDs (consecutive block ids go to
+// consecutive XCDs) so that each XCD walks a contiguous range of the
+// (m-tile, n-block) order: the n-blocks of one m-tile, and the m-tiles of
+// one expert, meet in the same L2.
+struct TileSel {
+    int e, row0, ne, m0, nb;
+};
+
+__device__ __forceinline__ bool select_tile(const int32_t *tiles, const int32_t *plan,
+                                            const int32_t *offsets, int E, int nrows, int NB,
+                                            TileSel &ts) {
+    const int total_u = tiles[0] * NB;
+    const int per = (total_u + 7) >> 3;
+    const int loc = (int)(blockIdx.x >> 3);
+    if (loc >= per) return false;
+    const int u = (int)(blockIdx.x & 7) * per + loc;
+    if (u >= total_u) return false;
+    const int mt = u / NB;
+    ts.nb = u - mt * NB;
     const int nact = plan[0];
     const int a = find_expert(tiles, nact, mt);
-    const int e = plan[1 + a];
-    if ((unsigned)e >= (unsigned)E) return;
+    ts.e = plan[1 + a];
+    if ((unsigned)ts.e >= (unsigned)E) return false;
+    ts.row0 = offsets[ts.e];
+    ts.ne = offsets[ts.e + 1] - ts.row0;
+    if (ts.row0 < 0 || ts.ne <= 0 || ts.row0 + ts.ne > nrows) return false;
+    ts.m0 = (mt - tiles[1 + a]) * kBM;
+    return true;
+}
+
+// kGateUp: A = split x (token rows), out = h fp32 [rows][f] (silu(gate) * up);
+// else:    A = split h (expert-major rows), out = rows_out bf16 [rows][d].
+template <bool kGateUp>
+__global__ __launch_bounds__(256) void ffn_mfma_kernel(
+    const uint8_t *__restrict__ aq, ExpertArgs W, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
+    const int32_t *__restrict__ tiles, float *__restrict__ h, uint16_t *__restrict__ rows_out,
+    int T, int d, int E, int k, int f) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ int a_rowidx[kBM];
     const int nrows = T * k;
-    const int row0 = offsets[e], ne = offsets[e + 1] - row0;
-    if (row0 < 0 || ne <= 0 || row0 + ne > nrows) return;
-    const int m0 = (mt - tiles[1 + a]) * kBM;          // first row of the tile in the expert
+    const int NB = kGateUp ? f / 256 : d / 512;
+    TileSel ts;
+    if (!select_tile(tiles, plan, offsets, E, nrows, NB, ts)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wid >> 1, wn = wid & 1;
     if (tid < kBM) {
-        const int r = min(m0 + tid, ne - 1);
-        const int row = sorted_rows[row0 + r];
-        a_rowidx[tid] = (unsigned)row < (unsigned)nrows ? row / k : 0;
+        const int r = ts.row0 + min(ts.m0 + tid, ts.ne - 1);
+        if (kGateUp) {
+            const int row = sorted_rows[r];
+            a_rowidx[tid] = (unsigned)row < (unsigned)nrows ? row / k : 0;
+        } else {
+            a_rowidx[tid] = r;                      // h rows are expert-major
+        }
     }
     __syncthreads();
-    const int nsteps = d >> 7, nblk = d >> 5;
-    const size_t code_row = (size_t)d >> 1;
-    const uint8_t *bq = W.gu_codes + (size_t)e * 2 * f * code_row;
-    const uint8_t *bsb = W.gu_scales + (size_t)e * 2 * f * nblk;
-    const int n0 = nt_blk * 64;
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const StepSrc src{xq, xs, a_rowidx, (size_t)nsteps * kStepQ, (size_t)nsteps * kStepS,
-                      bq, bsb, n0, f + n0, code_row, nblk};
-    gemm_tile<true>(stages, src, nsteps, wm, wn, acc);
-    // epilogue: lane holds rows 4 (l/16) + i, column l % 16 of each tile
-    const int g = lane >> 4, c16 = lane & 15;
-#pragma unroll
-    for (int mtl = 0; mtl < 4; ++mtl)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = m0 + wm * 64 + mtl * 16 + 4 * g + i;
-            if (r < ne) {
-                float *hrow = h + (size_t)(row0 + r) * f + n0 + wn * 32;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const float gv = acc[mtl][j][i], uv = acc[mtl][2 + j][i];
-                    hrow[j * 16 + c16] = gv / (1.0f + expf(-gv)) * uv;
-                }
-            }
-        }
-}
 
-// ---------------------------------------------------------------------------
-// down: tile = 128 rows x 128 output columns of one expert -> bf16 rows_out.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void down_mfma_kernel(
-    const uint8_t *__restrict__ hq, const uint8_t *__restrict__ hs, ExpertArgs W,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ plan,
-    const int32_t *__restrict__ tiles, uint16_t *__restrict__ rows_out, int T, int d, int E,
-    int k, int f, int mt_max) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    Stage *stages = reinterpret_cast<Stage *>(smem);
-    __shared__ int a_rowidx[kBM];
-    const int nt_blk = blockIdx.x / mt_max;           // 128-column block of d
-    const int mt = blockIdx.x - nt_blk * mt_max;
-    const int total = tiles[0];
-    if (mt >= total) return;
-    const int nact = plan[0];
-    const int a = find_expert(tiles, nact, mt);
-    const int e = plan[1 + a];
-    if ((unsigned)e >= (unsigned)E) return;
-    const int nrows = T * k;
-    const int row0 = offsets[e], ne = offsets[e + 1] - row0;
-    if (row0 < 0 || ne <= 0 || row0 + ne > nrows) return;
-    const int m0 = (mt - tiles[1 + a]) * kBM;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wid >> 1, wn = wid & 1;
-    if (tid < kBM) a_rowidx[tid] = row0 + min(m0 + tid, ne - 1);   // h rows are expert-major
-    __syncthreads();
-    const int nsteps = f >> 7, nblk = f >> 5;
-    const size_t code_row = (size_t)f >> 1;
-    const uint8_t *bq = W.dn_codes + (size_t)e * d * code_row;
-    const uint8_t *bsb = W.dn_scales + (size_t)e * d * nblk;
-    const int n0 = nt_blk * 128;
-    f32x4_t acc[4][4];
+    const int K = kGateUp ? d : f;
+    GemmArgs ga;
+    ga.nsteps = K >> 7;
+    const uint32_t a_row_bytes = (uint32_t)ga.nsteps * kStepBytes;
+    const uint32_t code_row = (uint32_t)K >> 1, nblk = (uint32_t)K >> 5;
+    const uint32_t wrows = kGateUp ? 2u * (uint32_t)f : (uint32_t)d;
+    const uint8_t *bq = (kGateUp ? W.gu_codes : W.dn_codes) + (size_t)ts.e * wrows * code_row;
+    const uint8_t *bsb = (kGateUp ? W.gu_scales : W.dn_scales) + (size_t)ts.e * wrows * nblk;
+    ga.bq = make_rsrc(bq, wrows * code_row);
+    ga.bs = make_rsrc(bsb, wrows * nblk);
+    const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int nt = 0; nt < 8; ++nt) {
+        const int wr = kGateUp ? (nt < 4 ? ts.nb * 256 + 64 * wid + 16 * nt
+                                         : f + ts.nb * 256 + 64 * wid + 16 * (nt - 4))
+                               : ts.nb * 512 + 128 * wid + 16 * nt;
+        ga.tq[nt] = (uint32_t)wr * code_row;
+        ga.ts[nt] = (uint32_t)wr * nblk;
+    }
+    ga.boff = (uint32_t)r16 * code_row + 16u * g;
+    ga.soff = (uint32_t)r16 * nblk;                 // nblk % 4 == 0: dword aligned
+    ga.sshift = 8u * (uint32_t)g;
+    uint32_t src[kDmaPerWave];                      // byte offsets into aq (< 4 GiB)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const StepSrc src{hq, hs, a_rowidx, (size_t)nsteps * kStepQ, (size_t)nsteps * kStepS,
-                      bq, bsb, n0, n0 + 64, code_row, nblk};
-    gemm_tile<false>(stages, src, nsteps, wm, wn, acc);
-    const int g = lane >> 4, c16 = lane & 15;
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int sl = 64 * (4 * i + wid) + lane;
+        const int r = sl < kBM * kSlotsRow ? sl / kSlotsRow : kBM - 1;
+        const int pc = sl < kBM * kSlotsRow ? sl - r * kSlotsRow : kSlotsRow - 1;
+        src[i] = (uint32_t)a_rowidx[r] * a_row_bytes + 16u * pc;
+    }
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+    const uint32_t a_lane = (uint32_t)(r16 * kStepBytes + 48 * g);
+    const uint32_t s_lane = (uint32_t)(r16 * kStepBytes + 192 + 2 * g);
+
+    f32x4_t acc[8][8];
 #pragma unroll
-    for (int mtl = 0; mtl < 4; ++mtl)
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // prologue, in the steady state's issue order: A(0), then (A(j+3), B(j+2))
+    // for j = -2, -1
+    BRing br;
+    issue_a(lds_addr, aq, src, ga.nsteps, 0, wid);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(lds_addr, aq, src, ga.nsteps, 1, wid);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b<0>(br, ga, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(lds_addr, aq, src, ga.nsteps, 2, wid);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b<1>(br, ga, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 0 has fewer loads behind A(0) than the steady state assumes
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerStep + kPerStep));
+    // three steps per turn of the register ring and no branch around any
+    // load, wait or barrier (a step past the end only skips its MFMAs), so
+    // the wait counts the compiler derives at the loop header are exact
+    for (int kk = 0; kk < ga.nsteps; kk += 3) {
+        gemm_step<0>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk, wid, true);
+        gemm_step<1>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 1, wid,
+                     kk + 1 < ga.nsteps);
+        gemm_step<2>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 2, wid,
+                     kk + 2 < ga.nsteps);
+    }
+    // drain the trailing (re-)loads before the block can exit
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // epilogue: lane holds rows 4 (l / 16) + i, column l % 16 of each tile
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = m0 + wm * 64 + mtl * 16 + 4 * g + i;
-            if (r < ne) {
-                uint16_t *orow = rows_out + (size_t)(row0 + r) * d + n0 + wn * 64;
+            const int r = ts.m0 + mt * 16 + 4 * g + i;
+            if (r < ts.ne) {
+                if (kGateUp) {
+                    float *hrow = h + (size_t)(ts.row0 + r) * f + ts.nb * 256 + 64 * wid;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) orow[j * 16 + c16] = f32_to_bf16_rne(acc[mtl][j][i]);
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const float gv = acc[mt][nt][i], uv = acc[mt][nt + 4][i];
+                        hrow[16 * nt + r16] = gv / (1.0f + expf(-gv)) * uv;
+                    }
+                } else {
+                    uint16_t *orow = rows_out + (size_t)(ts.row0 + r) * d + ts.nb * 512 + 128 * wid;
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) orow[16 * nt + r16] = f32_to_bf16_rne(acc[mt][nt][i]);
+                }
             }
         }
 }
@@ -444,40 +541,43 @@ bool g_attr_done = false;
 
 hipError_t set_lds_attrs() {
     if (g_attr_done) return hipSuccess;
-    const int bytes = (int)(2 * sizeof(Stage));
-    hipError_t e = hipFuncSetAttribute((const void *)gate_up_mfma_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    hipError_t e = hipFuncSetAttribute((const void *)ffn_mfma_kernel<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)down_mfma_kernel,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        e = hipFuncSetAttribute((const void *)ffn_mfma_kernel<false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e == hipSuccess) g_attr_done = true;
     return e;
 }
 
 }  // namespace
 
-bool mfma_path_ok(int T, int d, int f) { return d % 128 == 0 && f % 128 == 0 && T >= kMfmaMinT; }
+// The split rows are addressed with 32-bit byte offsets.
+bool mfma_path_ok(int T, int d, int k, int f) {
+    return d % 512 == 0 && f % 256 == 0 && T >= kMfmaMinT &&
+           (double)T * (d / 128) * kStepBytes < 4294967296.0 &&
+           (double)T * k * (f / 128) * kStepBytes < 4294967296.0;
+}
+
+size_t mx_split_bytes(int rows, int K) { return (size_t)rows * (K / 128) * kStepBytes; }
 
 size_t mfma_ws_bytes(int T, int d, int E, int k, int f) {
     const size_t rows = (size_t)T * k;
-    return al256((size_t)T * (d / 128) * kStepQ) + al256((size_t)T * (d / 128) * kStepS) +
-           al256(rows * (f / 128) * kStepQ) + al256(rows * (f / 128) * kStepS) +
+    return al256(mx_split_bytes(T, d)) + al256(mx_split_bytes((int)rows, f)) +
            al256((size_t)(E + 1) * 4);
 }
 
-hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, uint8_t *s,
-                                hipStream_t st) {
+hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, hipStream_t st) {
     const long long items = (long long)rows * (K / 128);
     if (items <= 0) return hipSuccess;
-    mx_split_e2m3_kernel<uint16_t><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(in, rows, K, q, s);
+    mx_split_e2m3_kernel<uint16_t><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(in, rows, K, q);
     return hipGetLastError();
 }
 
-hipError_t launch_mx_split_f32(const float *in, int rows, int K, uint8_t *q, uint8_t *s,
-                               hipStream_t st) {
+hipError_t launch_mx_split_f32(const float *in, int rows, int K, uint8_t *q, hipStream_t st) {
     const long long items = (long long)rows * (K / 128);
     if (items <= 0) return hipSuccess;
-    mx_split_e2m3_kernel<float><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(in, rows, K, q, s);
+    mx_split_e2m3_kernel<float><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(in, rows, K, q);
     return hipGetLastError();
 }
 
@@ -490,28 +590,38 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
     const size_t rows = (size_t)T * k;
     char *p = static_cast<char *>(ws);
     uint8_t *xq = reinterpret_cast<uint8_t *>(p);
-    p += al256((size_t)T * (d / 128) * kStepQ);
-    uint8_t *xs = reinterpret_cast<uint8_t *>(p);
-    p += al256((size_t)T * (d / 128) * kStepS);
+    p += al256(mx_split_bytes(T, d));
     uint8_t *hq = reinterpret_cast<uint8_t *>(p);
-    p += al256(rows * (f / 128) * kStepQ);
-    uint8_t *hs = reinterpret_cast<uint8_t *>(p);
-    p += al256(rows * (f / 128) * kStepS);
+    p += al256(mx_split_bytes((int)rows, f));
     int32_t *tiles = reinterpret_cast<int32_t *>(p);
 
-    e = launch_mx_split_bf16(x, T, d, xq, xs, s);
+    {
+        DiagScope t("mx_split_x", s);
+        e = launch_mx_split_bf16(x, T, d, xq, s);
+    }
     if (e != hipSuccess) return e;
     mfma_plan_kernel<<<1, 1024, 0, s>>>(offsets, plan, tiles, E);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int mt_max = min(E, (int)rows) + (int)((rows + kBM - 1) / kBM);
-    const size_t lds = 2 * sizeof(Stage);
-    gate_up_mfma_kernel<<<(unsigned)(mt_max * (f / 64)), 256, lds, s>>>(
-        xq, xs, w, offsets, sorted_rows, plan, tiles, h, T, d, E, k, f, mt_max);
+    // upper bound on the m-tiles: one partial tile per expert plus full tiles
+    const long long mt_max = min(E, (int)rows) + (long long)((rows + kBM - 1) / kBM);
+    {
+        DiagScope t("gate_up_mfma", s);
+        const long long blocks = 8 * ((mt_max * (f / 256) + 7) / 8);
+        ffn_mfma_kernel<true><<<(unsigned)blocks, 256, kLdsBytes, s>>>(
+            xq, w, offsets, sorted_rows, plan, tiles, h, nullptr, T, d, E, k, f);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = launch_mx_split_f32(h, (int)rows, f, hq, hs, s);
+    {
+        DiagScope t("mx_split_h", s);
+        e = launch_mx_split_f32(h, (int)rows, f, hq, s);
+    }
     if (e != hipSuccess) return e;
-    down_mfma_kernel<<<(unsigned)(mt_max * (d / 128)), 256, lds, s>>>(
-        hq, hs, w, offsets, plan, tiles, rows_out, T, d, E, k, f, mt_max);
+    {
+        DiagScope t("down_mfma", s);
+        const long long blocks = 8 * ((mt_max * (d / 512) + 7) / 8);
+        ffn_mfma_kernel<false><<<(unsigned)blocks, 256, kLdsBytes, s>>>(
+            hq, w, offsets, sorted_rows, plan, tiles, nullptr, rows_out, T, d, E, k, f);
+    }
     return hipGetLastError();
 }
 

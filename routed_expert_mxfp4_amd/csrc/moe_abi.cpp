@@ -71,7 +71,7 @@ FfnWs ffn_ws(const moe_dims &D) {
     w.h = al256((size_t)(D.E + 1) * 4);
     w.mfma = w.h + al256((size_t)D.T * D.k * D.f * 4);
     w.total = w.mfma;
-    if (moe::mfma_path_ok(D.T, D.d, D.f)) w.total += al256(moe::mfma_ws_bytes(D.T, D.d, D.E, D.k, D.f));
+    if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) w.total += al256(moe::mfma_ws_bytes(D.T, D.d, D.E, D.k, D.f));
     return w;
 }
 
@@ -107,30 +107,6 @@ struct Diag {
 };
 Diag g_diag;
 
-// Records a start event before and a stop event after one launch when that
-// kernel is being timed.  When timing is off the cost is one atomic load.
-class DiagScope {
-  public:
-    DiagScope(const char *kernel, hipStream_t s) : s_(s) {
-        if (!g_diag.active.load(std::memory_order_acquire)) return;
-        std::lock_guard<std::mutex> lk(g_diag.mu);
-        if (g_diag.name != kernel || 2 * (g_diag.used + 1) > (int)g_diag.ev.size()) return;
-        hipEvent_t start = g_diag.ev[2 * g_diag.used];
-        stop_ = g_diag.ev[2 * g_diag.used + 1];
-        ++g_diag.used;
-        (void)hipEventRecord(start, s_);
-    }
-    ~DiagScope() {
-        if (stop_) (void)hipEventRecord(stop_, s_);
-    }
-    DiagScope(const DiagScope &) = delete;
-    DiagScope &operator=(const DiagScope &) = delete;
-
-  private:
-    hipStream_t s_;
-    hipEvent_t stop_ = nullptr;
-};
-
 template <typename Fn>
 moe_status guarded(Fn fn) {
     try {
@@ -141,6 +117,25 @@ moe_status guarded(Fn fn) {
 }
 
 }  // namespace
+
+namespace moe {
+// Records a start event before and a stop event after the launches in the
+// scope's lifetime when that kernel name is being timed.
+DiagScope::DiagScope(const char *kernel, hipStream_t s) : s_(s) {
+    if (!g_diag.active.load(std::memory_order_acquire)) return;
+    std::lock_guard<std::mutex> lk(g_diag.mu);
+    if (g_diag.name != kernel || 2 * (g_diag.used + 1) > (int)g_diag.ev.size()) return;
+    hipEvent_t start = g_diag.ev[2 * g_diag.used];
+    stop_ = g_diag.ev[2 * g_diag.used + 1];
+    ++g_diag.used;
+    (void)hipEventRecord(start, s_);
+}
+DiagScope::~DiagScope() {
+    if (stop_) (void)hipEventRecord(stop_, s_);
+}
+}  // namespace moe
+
+using moe::DiagScope;
 
 extern "C" {
 
@@ -252,7 +247,7 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x,
             DiagScope t("plan", s);
             e = moe::launch_plan(offsets, plan, D.E, s);
         }
-        if (moe::mfma_path_ok(D.T, D.d, D.f)) {
+        if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
             if (e == hipSuccess) {
                 DiagScope t("mfma_ffn", s);
                 e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, h, rows_out,
@@ -343,7 +338,7 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
                                         D.E, D.k, perm_ws, s);
             }
         }
-        if (moe::mfma_path_ok(D.T, D.d, D.f)) {
+        if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
             if (e == hipSuccess) {
                 DiagScope t("mfma_ffn", s);
                 e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, h, rows_out,
@@ -380,15 +375,15 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
     });
 }
 
-int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint8_t *q,
-                           uint8_t *s, void *hip_stream) {
+int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint8_t *out,
+                           void *hip_stream) {
     try {
-        if (!in || !q || !s || rows < 0 || K <= 0 || K % 128 != 0) return -1;
+        if (!in || !out || rows < 0 || K <= 0 || K % 128 != 0) return -1;
         if (((uintptr_t)in & 15u) != 0) return -1;
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
         hipError_t e = in_is_bf16
-                           ? moe::launch_mx_split_bf16(static_cast<const uint16_t *>(in), rows, K, q, s, st)
-                           : moe::launch_mx_split_f32(static_cast<const float *>(in), rows, K, q, s, st);
+                           ? moe::launch_mx_split_bf16(static_cast<const uint16_t *>(in), rows, K, out, st)
+                           : moe::launch_mx_split_f32(static_cast<const float *>(in), rows, K, out, st);
         return e == hipSuccess ? 0 : -1;
     } catch (...) {
         return -1;

@@ -56,6 +56,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
 __device__ __forceinline__ uint32_t buf_load8(rsrc_t r, uint32_t voff, uint32_t soff) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
@@ -132,6 +135,23 @@ __device__ __forceinline__ float dot8_fp4_f32(uint32_t codes, float4 a, float4 b
 }
 
 // ---------------------------------------------------------------------------
+// Diagnostics: while moe_diag_time_kernel(name) is active, a DiagScope named
+// `name` records HIP events before and after the launches in its lifetime
+// (defined in moe_abi.cpp; costs one atomic load when timing is off).
+// ---------------------------------------------------------------------------
+class DiagScope {
+  public:
+    DiagScope(const char *kernel, hipStream_t s);
+    ~DiagScope();
+    DiagScope(const DiagScope &) = delete;
+    DiagScope &operator=(const DiagScope &) = delete;
+
+  private:
+    hipStream_t s_;
+    hipEvent_t stop_ = nullptr;
+};
+
+// ---------------------------------------------------------------------------
 // Launchers (defined in the .hip files).  All pointers are device pointers.
 // ---------------------------------------------------------------------------
 hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const float *bias,
@@ -167,18 +187,18 @@ hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
                                const float *topk_w, const int32_t *row_pos, uint16_t *y,
                                int T, int d, int E, int k, int f, hipStream_t s);
 // Prefill expert FFN on scaled MFMA (x and h as two-term MX E2M3, weights
-// as stored).  Needs d % 128 == 0, f % 128 == 0; ws of mfma_ws_bytes.
-bool mfma_path_ok(int T, int d, int f);
+// as stored).  Needs d % 512 == 0, f % 256 == 0; ws of mfma_ws_bytes.
+bool mfma_path_ok(int T, int d, int k, int f);
 size_t mfma_ws_bytes(int T, int d, int E, int k, int f);
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                            const int32_t *sorted_rows, const int32_t *plan, float *h,
                            uint16_t *rows_out, void *ws, int T, int d, int E, int k, int f,
                            hipStream_t s);
-// rows x K (K % 128 == 0) -> two-term MX E2M3 codes and scales
-hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, uint8_t *s,
-                                hipStream_t st);
-hipError_t launch_mx_split_f32(const float *in, int rows, int K, uint8_t *q, uint8_t *s,
-                               hipStream_t st);
+// rows x K (K % 128 == 0) -> two-term MX E2M3 split rows, 208 bytes per row
+// and 128-element step (codes of both terms, then their E8M0 scales).
+size_t mx_split_bytes(int rows, int K);
+hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, hipStream_t st);
+hipError_t launch_mx_split_f32(const float *in, int rows, int K, uint8_t *q, hipStream_t st);
 
 hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
                           const float *topk_w, uint16_t *y, int T, int d, int k,

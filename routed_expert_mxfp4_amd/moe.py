@@ -74,7 +74,7 @@ def lib():
         L.moe_diag_time_kernel.restype = I
         L.moe_diag_time_kernel.argtypes = [ctypes.c_char_p, I]
         L.moe_diag_mx_split_e2m3.restype = I
-        L.moe_diag_mx_split_e2m3.argtypes = [P, I, I, I, P, P, P]
+        L.moe_diag_mx_split_e2m3.argtypes = [P, I, I, I, P, P]
         L.moe_diag_kernel_time.restype = I
         L.moe_diag_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_longlong)]
@@ -100,19 +100,19 @@ def diag_kernel_time():
 
 def diag_mx_split_e2m3(rows_tensor, stream=None):
     """Two-term MX E2M3 split of a [rows][K] bf16 or fp32 device tensor (the
-    scaled-MFMA path's activation staging).  Returns (q uint8 [rows][K/128*192],
-    s uint8 [rows][K/128*8])."""
+    scaled-MFMA path's activation staging).  Returns uint8 [rows][K/128*208]
+    in the library's split layout (codes of both terms, then their scales,
+    per 128-element step)."""
     t = rows_tensor.contiguous()
     R, K = t.shape
-    q = torch.empty((R, K // 128 * 192), dtype=torch.uint8, device=t.device)
-    s = torch.empty((R, K // 128 * 8), dtype=torch.uint8, device=t.device)
+    out = torch.empty((R, K // 128 * 208), dtype=torch.uint8, device=t.device)
     is_bf16 = 1 if t.dtype == torch.bfloat16 else 0
     if not is_bf16:
         assert t.dtype == torch.float32
-    rc = lib().moe_diag_mx_split_e2m3(_ptr(t), is_bf16, R, K, _ptr(q), _ptr(s), _stream(stream))
+    rc = lib().moe_diag_mx_split_e2m3(_ptr(t), is_bf16, R, K, _ptr(out), _stream(stream))
     if rc != 0:
         raise RuntimeError("moe_diag_mx_split_e2m3 failed")
-    return q, s
+    return out
 
 
 def status_str(status: int) -> str:
