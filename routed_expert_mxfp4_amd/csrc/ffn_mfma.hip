@@ -28,6 +28,7 @@ namespace moe {
 namespace {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -200,9 +201,7 @@ __device__ __forceinline__ int find_expert(const int32_t *tiles, int nact, int m
 //     wave waits for its own loads (vmcnt) and a barrier publishes them.
 //     Fragment reads are explicit ds_read instructions so that the next
 //     stages' loads stay in flight while a stage is read.
-//   B (weights, private to a wave): global -> registers, 16 bytes of codes
-//     and one scale byte per lane and tile, issued two steps ahead into a
-//     three-deep register ring.
+//   B (weights, private to a wave): global -> registers (see BRing).
 // Every step issues the same number of loads (steps past the end re-load
 // the last step), so the wait counts are constants.
 // ---------------------------------------------------------------------------
@@ -210,10 +209,7 @@ constexpr int kNst = 4;                              // LDS stages
 constexpr int kDmaPerWave = 7;                       // 128 x 13 pieces = 26 wave loads, 28 issued
 constexpr int kStageBytes = 4 * kDmaPerWave * 1024;  // 28672 (26624 used + overflow of the pad loads)
 constexpr int kLdsBytes = kNst * kStageBytes;        // 114688
-constexpr int kBLoads = 16;                          // per wave per step: 8 code + 8 scale loads
-constexpr int kPerStep = kBLoads + kDmaPerWave;      // vector memory instructions per step
 static_assert(kBM * kSlotsRow <= 4 * kDmaPerWave * 64, "direct loads must cover the stage");
-static_assert(kBLoads + 2 * kPerStep <= 63, "vmcnt range");
 
 // Global -> LDS direct load of 16 bytes per lane (lane l fills LDS bytes
 // m0 + 16 l).  Written as inline asm so that the compiler's wait-count
@@ -283,26 +279,118 @@ __device__ __forceinline__ void afrag_ready(AFrag &f) {
     asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(f.hi), "+v"(f.lo), "+v"(f.sc) : "n"(N));
 }
 
+// Weight loads.  Codes: the 64 bytes a step needs from a row are half of a
+// 128-byte line, so steps are loaded in pairs (2p, 2p+1), first all tiles'
+// step 2p then all tiles' step 2p+1 (the second touch of each line hits the
+// L1), into a ring of two pair slots; pair p is issued at step 2p - 2.
+// Scales: one 16-byte load per row covers four steps (4 blocks each); group
+// G (steps 4G..4G+3) is issued at step 4G - 3 and each lane keeps its four
+// bytes (block g of each step) packed in one register.
+//
+// Like the direct loads, these are inline asm, waited for by the one
+// explicit vmcnt at the top of each step.  The destinations are tied
+// ("+v"): a ring slot keeps one register for its whole life, so no copy of
+// a register whose load is still in flight can exist (a codegen test checks
+// that the main loop holds no vector register copies).
 struct BRing {
-    uint4 q[3][8];
-    uint32_t s[3][8];
+    u32x4_t q[2][2][8];         // [pair slot][step in pair][tile]
+    u32x4_t sraw[8];            // scale group in flight
+    uint32_t spk[8];            // current group, this lane's byte per step
 };
 
 struct GemmArgs {
-    rsrc_t bq, bs;              // this expert's weight codes / scales
+    i32x4_t bq, bs;             // buffer resources: this expert's codes / scales
     uint32_t boff, soff;        // this lane's offsets in its first B tile (codes, scales)
     uint32_t tq[8], ts[8];      // wave-uniform offsets of the 8 B tiles (codes, scales)
-    uint32_t sshift;            // bit position of this lane's scale byte in a step's dword
+    uint32_t psel01;            // v_perm selector: byte g of two dwords
     int nsteps;
 };
 
-template <int R>
-__device__ __forceinline__ void issue_b(BRing &br, const GemmArgs &ga, int j) {
-    const uint32_t jj = (uint32_t)min(j, ga.nsteps - 1);
+// A raw buffer resource (base, byte size) in scalar registers.
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+__device__ __forceinline__ void buf_load16_async(u32x4_t &dst, const i32x4_t &rsrc, uint32_t voff,
+                                                 uint32_t soff) {
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
+                 : "+v"(dst)
+                 : "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+
+// Vector memory instructions issued at a step with ring position R (= the
+// step index mod 4), in this order: 7 direct loads; at even R 16 code loads
+// (8 of the pair's first step, then 8 of its second); at R == 1 8 scale
+// loads.
+constexpr int kCodeLoads = 16, kScaleLoads = 8;
+// The one wait at the top of step kk (ring position R): what must have
+// landed is this wave's part of stage kk (issued at step kk - 3), the codes
+// of step kk (issued at step kk - 2 for even R, kk - 3 for odd R) and, at
+// R == 0, the scale group (issued at step kk - 3).  The count is the number
+// of loads issued after the last of those.
+//   R = 0: last needed = codes s0 of step kk-2; after it: s1 (8), A(kk+2)
+//   R = 1: last needed = codes s1 of step kk-3; after: A(kk+1), A(kk+2), 16 codes
+//   R = 2: last needed = codes s0 of step kk-2; after: s1 (8), A(kk+2), 8 scales
+//   R = 3: last needed = codes s1 of step kk-3; after: A(kk+1), 8 scales,
+//          A(kk+2), 16 codes
+constexpr int step_top_vmcnt(int R) {
+    return R == 0 ? 8 + kDmaPerWave
+         : R == 1 ? kDmaPerWave + kDmaPerWave + kCodeLoads
+         : R == 2 ? 8 + kDmaPerWave + kScaleLoads
+         : kDmaPerWave + kScaleLoads + kDmaPerWave + kCodeLoads;
+}
+static_assert(step_top_vmcnt(0) == 15 && step_top_vmcnt(1) == 30 && step_top_vmcnt(2) == 23 &&
+                  step_top_vmcnt(3) == 38,
+              "wait counts");
+
+template <int PS>
+__device__ __forceinline__ void issue_codes(BRing &br, const GemmArgs &ga, int j) {
+    const uint32_t j0 = (uint32_t)min(j, ga.nsteps - 1), j1 = (uint32_t)min(j + 1, ga.nsteps - 1);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) br.q[R][nt] = buf_load16(ga.bq, ga.boff, ga.tq[nt] + jj * 64u);
+    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.q[PS][0][nt], ga.bq, ga.boff, ga.tq[nt] + j0 * 64u);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) br.s[R][nt] = buf_load4(ga.bs, ga.soff, ga.ts[nt] + jj * 4u);
+    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.q[PS][1][nt], ga.bq, ga.boff, ga.tq[nt] + j1 * 64u);
+}
+
+__device__ __forceinline__ void issue_scales(BRing &br, const GemmArgs &ga, int G) {
+    const uint32_t gg = (uint32_t)min(G, (ga.nsteps - 1) >> 2);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.sraw[nt], ga.bs, ga.soff, ga.ts[nt] + gg * 16u);
+}
+
+// After the last step some weight loads (the clamped re-loads past the end)
+// may still be in flight into ring registers the compiler no longer needs.
+// Waiting for them, then naming every ring register in an asm statement,
+// keeps those registers from being reused before the data has landed.
+__device__ __forceinline__ void drain_weight_loads(BRing &br) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+            asm volatile("" ::"v"(br.q[ps][sub][0]), "v"(br.q[ps][sub][1]), "v"(br.q[ps][sub][2]),
+                         "v"(br.q[ps][sub][3]), "v"(br.q[ps][sub][4]), "v"(br.q[ps][sub][5]),
+                         "v"(br.q[ps][sub][6]), "v"(br.q[ps][sub][7]));
+    asm volatile("" ::"v"(br.sraw[0]), "v"(br.sraw[1]), "v"(br.sraw[2]), "v"(br.sraw[3]),
+                 "v"(br.sraw[4]), "v"(br.sraw[5]), "v"(br.sraw[6]), "v"(br.sraw[7]));
+}
+
+// spk byte i = byte g of dword i of the group's 16 bytes.
+__device__ __forceinline__ void pack_scales(BRing &br, const GemmArgs &ga) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const u32x4_t r = br.sraw[nt];
+        const uint32_t t01 = __builtin_amdgcn_perm(r.y, r.x, ga.psel01);
+        const uint32_t t23 = __builtin_amdgcn_perm(r.w, r.z, ga.psel01);
+        br.spk[nt] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    }
 }
 
 __device__ __forceinline__ void issue_a(uint32_t lds_addr, const uint8_t *aq,
@@ -317,72 +405,70 @@ __device__ __forceinline__ void issue_a(uint32_t lds_addr, const uint8_t *aq,
 }
 
 // The scale operand reads byte 0 of the register (bits above are ignored).
-template <int R>
+template <int PS, int SUB>
 __device__ __forceinline__ void mfma_mt(f32x4_t (&acc)[8], const AFrag &a, const BRing &br,
                                         const uint32_t (&bsc)[8]) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-        const uint4 q = br.q[R][nt];
+        const u32x4_t q = br.q[PS][SUB][nt];
         const i32x8_t b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
         acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.hi, b, acc[nt], 2, 4, 0,
                                                                    (int)a.sc, 0, (int)bsc[nt]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        const uint4 q = br.q[R][nt];
-        const i32x8_t b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
         acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.lo, b, acc[nt], 2, 4, 1,
                                                                    (int)a.sc, 0, (int)bsc[nt]);
     }
 }
 
-// One K step: wait for stage kk, queue step kk + 2's weights and step
-// kk + 3's activations, then 128 MFMAs (A fragments read one m-tile ahead).
+// One K step at ring position R = kk % 4: wait for stage kk, queue step
+// kk + 3's activations (and, by R, a code pair or a scale group), then 128
+// MFMAs (A fragments read one m-tile ahead).
 template <int R>
 __device__ __forceinline__ void gemm_step(f32x4_t (&acc)[8][8], BRing &br, const GemmArgs &ga,
                                           const uint8_t *aq, const uint32_t (&src)[kDmaPerWave],
                                           uint32_t lds_addr, uint32_t a_lane, uint32_t s_lane,
                                           int kk, int wid, bool live) {
-    // loads after this wave's part of stage kk: B(kk - 1), then two whole
-    // steps (issue order per step: activations j + 3, then weights j + 2)
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBLoads + 2 * kPerStep));
+    constexpr int PS = (R >> 1) & 1;        // pair slot of steps kk (and kk ^ 1)
+    constexpr int SUB = R & 1;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(step_top_vmcnt(R)));   // see step_top_vmcnt
     __builtin_amdgcn_s_barrier();                        // everyone's part; stage kk-1 free
     __builtin_amdgcn_sched_barrier(0);
     issue_a(lds_addr, aq, src, ga.nsteps, kk + 3, wid);
     __builtin_amdgcn_sched_barrier(0);
-    issue_b<(R + 2) % 3>(br, ga, kk + 2);
+    if constexpr ((R & 1) == 0) issue_codes<PS ^ 1>(br, ga, kk + 2);
+    if constexpr (R == 1) issue_scales(br, ga, (kk + 3) >> 2);
+    if constexpr (R == 0) pack_scales(br, ga);
     __builtin_amdgcn_sched_barrier(0);
     if (!live) return;
     const uint32_t st = lds_addr + (uint32_t)((kk & (kNst - 1)) * kStageBytes);
     const uint32_t a = st + a_lane, s = st + s_lane;
     uint32_t bsc[8];
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) bsc[nt] = br.s[R][nt] >> ga.sshift;
+    for (int nt = 0; nt < 8; ++nt) bsc[nt] = br.spk[nt] >> (8 * R);
     AFrag f0, f1;
     read_afrag<0>(f0, a, s);
     read_afrag<1>(f1, a, s);
     afrag_ready<5>(f0);
-    mfma_mt<R>(acc[0], f0, br, bsc);
+    mfma_mt<PS, SUB>(acc[0], f0, br, bsc);
     read_afrag<2>(f0, a, s);
     afrag_ready<5>(f1);
-    mfma_mt<R>(acc[1], f1, br, bsc);
+    mfma_mt<PS, SUB>(acc[1], f1, br, bsc);
     read_afrag<3>(f1, a, s);
     afrag_ready<5>(f0);
-    mfma_mt<R>(acc[2], f0, br, bsc);
+    mfma_mt<PS, SUB>(acc[2], f0, br, bsc);
     read_afrag<4>(f0, a, s);
     afrag_ready<5>(f1);
-    mfma_mt<R>(acc[3], f1, br, bsc);
+    mfma_mt<PS, SUB>(acc[3], f1, br, bsc);
     read_afrag<5>(f1, a, s);
     afrag_ready<5>(f0);
-    mfma_mt<R>(acc[4], f0, br, bsc);
+    mfma_mt<PS, SUB>(acc[4], f0, br, bsc);
     read_afrag<6>(f0, a, s);
     afrag_ready<5>(f1);
-    mfma_mt<R>(acc[5], f1, br, bsc);
+    mfma_mt<PS, SUB>(acc[5], f1, br, bsc);
     read_afrag<7>(f1, a, s);
     afrag_ready<5>(f0);
-    mfma_mt<R>(acc[6], f0, br, bsc);
+    mfma_mt<PS, SUB>(acc[6], f0, br, bsc);
     afrag_ready<0>(f1);
-    mfma_mt<R>(acc[7], f1, br, bsc);
+    mfma_mt<PS, SUB>(acc[7], f1, br, bsc);
 }
 
 // The block's tile: which expert, which 128 rows of it, which 512 weight
@@ -451,8 +537,8 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     const uint32_t wrows = kGateUp ? 2u * (uint32_t)f : (uint32_t)d;
     const uint8_t *bq = (kGateUp ? W.gu_codes : W.dn_codes) + (size_t)ts.e * wrows * code_row;
     const uint8_t *bsb = (kGateUp ? W.gu_scales : W.dn_scales) + (size_t)ts.e * wrows * nblk;
-    ga.bq = make_rsrc(bq, wrows * code_row);
-    ga.bs = make_rsrc(bsb, wrows * nblk);
+    ga.bq = buffer_rsrc(bq, wrows * code_row);
+    ga.bs = buffer_rsrc(bsb, wrows * nblk);
     const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
@@ -464,7 +550,7 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     }
     ga.boff = (uint32_t)r16 * code_row + 16u * g;
     ga.soff = (uint32_t)r16 * nblk;                 // nblk % 4 == 0: dword aligned
-    ga.sshift = 8u * (uint32_t)g;
+    ga.psel01 = (uint32_t)g | ((4u + (uint32_t)g) << 8);
     uint32_t src[kDmaPerWave];                      // byte offsets into aq (< 4 GiB)
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
@@ -483,33 +569,35 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // prologue, in the steady state's issue order: A(0), then (A(j+3), B(j+2))
-    // for j = -2, -1
-    BRing br;
+    // prologue: the loads of steps -3, -2, -1 in the steady state's roles
+    // (ring positions 1, 2, 3): A(0) + scale group 0, A(1) + codes of steps
+    // 0 and 1, A(2)
+    BRing br = {};
     issue_a(lds_addr, aq, src, ga.nsteps, 0, wid);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_scales(br, ga, 0);
     __builtin_amdgcn_sched_barrier(0);
     issue_a(lds_addr, aq, src, ga.nsteps, 1, wid);
     __builtin_amdgcn_sched_barrier(0);
-    issue_b<0>(br, ga, 0);
+    issue_codes<0>(br, ga, 0);
     __builtin_amdgcn_sched_barrier(0);
     issue_a(lds_addr, aq, src, ga.nsteps, 2, wid);
     __builtin_amdgcn_sched_barrier(0);
-    issue_b<1>(br, ga, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    // step 0 has fewer loads behind A(0) than the steady state assumes
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerStep + kPerStep));
-    // three steps per turn of the register ring and no branch around any
+    // four steps per turn of the register ring and no branch around any
     // load, wait or barrier (a step past the end only skips its MFMAs), so
     // the wait counts the compiler derives at the loop header are exact
-    for (int kk = 0; kk < ga.nsteps; kk += 3) {
+    for (int kk = 0; kk < ga.nsteps; kk += 4) {
         gemm_step<0>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk, wid, true);
         gemm_step<1>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 1, wid,
                      kk + 1 < ga.nsteps);
         gemm_step<2>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 2, wid,
                      kk + 2 < ga.nsteps);
+        gemm_step<3>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 3, wid,
+                     kk + 3 < ga.nsteps);
     }
-    // drain the trailing (re-)loads before the block can exit
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // drain the trailing (re-)loads before their registers or the block's
+    // LDS can be reused
+    drain_weight_loads(br);
     __builtin_amdgcn_sched_barrier(0);
 
     // epilogue: lane holds rows 4 (l / 16) + i, column l % 16 of each tile
