@@ -36,7 +36,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 WORKLOADS = {"tiny": 0, "decode": 1, "batched-decode": 2, "zipf-prefill": 3, "long-prefill": 4}
 DEFAULT_STEPS = {"tiny": 1000, "decode": 1000, "batched-decode": 200, "zipf-prefill": 20,
                  "long-prefill": 5}
-KERNELS = ("router_logits", "topk_softmax", "permute", "topk_permute", "gemv_gate_up",
+KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm",
+           "router_refine", "permute", "topk_permute", "gemv_gate_up",
            "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "mx_split_h", "down_mfma",
            "combine")
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 / MXFP6, published

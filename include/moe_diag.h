@@ -5,7 +5,8 @@
  * uses it to time its dominant kernel inside the timed region.
  *
  * Kernel names: "router_logits", "topk_softmax", "permute", "topk_permute"
- * (the two fused, small T), "plan", "gemv_gate_up", "gemv_down",
+ * (the two fused, small T), "router_norms", "router_filter_gemm",
+ * "router_refine" (routing of many tokens), "plan", "gemv_gate_up", "gemv_down",
  * "down_combine", "combine", "mfma_ffn" (the whole scaled-MFMA expert
  * FFN of large T), and its parts "mx_split_x", "gate_up_mfma",
  * "mx_split_h", "down_mfma".

@@ -52,13 +52,18 @@ moe_status check_experts(const moe_mxfp4_experts *w) {
 moe_status device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 // ---- workspace layouts ------------------------------------------------------
+// Route: logits (the canonical ones, or the filter's approximations) and
+// the row norms of the filtered path.
 struct RouteWs {
-    size_t logits, total;
+    size_t logits, nx, nw, total;
 };
 RouteWs route_ws(const moe_dims &D) {
     RouteWs w;
-    w.logits = 0;
-    w.total = al256((size_t)D.T * D.E * 4);
+    size_t p = 0;
+    w.logits = p; p += al256((size_t)D.T * D.E * 4);
+    w.nx = p; p += al256((size_t)D.T * 4);
+    w.nw = p; p += al256((size_t)D.E * 4);
+    w.total = p;
     return w;
 }
 
@@ -76,13 +81,13 @@ FfnWs ffn_ws(const moe_dims &D) {
 }
 
 struct LayerWs {
-    size_t logits, ids, tw, counts, offsets, sorted_rows, row_pos, perm, ffn, rows_out, total;
+    size_t route, ids, tw, counts, offsets, sorted_rows, row_pos, perm, ffn, rows_out, total;
 };
 LayerWs layer_ws(const moe_dims &D) {
     const size_t rows = (size_t)D.T * D.k;
     LayerWs w;
     size_t p = 0;
-    w.logits = p; p += al256((size_t)D.T * D.E * 4);
+    w.route = p; p += route_ws(D).total;
     w.ids = p; p += al256(rows * 4);
     w.tw = p; p += al256(rows * 4);
     w.counts = p; p += al256((size_t)D.E * 4);
@@ -177,6 +182,21 @@ moe_status moe_route(const moe_dims *dims, const uint16_t *x, const uint16_t *ro
         if (D.T == 0) return MOE_OK;
         if (!x || !router_w || !topk_ids || !topk_w) return MOE_ERR_NULL;
         if (!aligned16(x) || !aligned16(router_w)) return MOE_ERR_ALIGN;
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        hipError_t e;
+        if (!logits_out && moe::route_filter_ok(D.T, D.d, D.E)) {
+            if (!ws) return MOE_ERR_NULL;
+            if (!aligned16(ws)) return MOE_ERR_ALIGN;
+            const RouteWs R = route_ws(D);
+            if (ws_bytes < R.total) return MOE_ERR_WORKSPACE;
+            char *base = static_cast<char *>(ws);
+            e = moe::launch_route_filtered(x, router_w, router_bias,
+                                           reinterpret_cast<float *>(base + R.logits),
+                                           reinterpret_cast<float *>(base + R.nx),
+                                           reinterpret_cast<float *>(base + R.nw), topk_ids,
+                                           topk_w, D.T, D.d, D.E, D.k, s);
+            return device_status(e);
+        }
         float *logits = logits_out;
         if (!logits) {
             if (!ws) return MOE_ERR_NULL;
@@ -184,8 +204,6 @@ moe_status moe_route(const moe_dims *dims, const uint16_t *x, const uint16_t *ro
             if (ws_bytes < route_ws(D).total) return MOE_ERR_WORKSPACE;
             logits = reinterpret_cast<float *>(static_cast<char *>(ws) + route_ws(D).logits);
         }
-        hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        hipError_t e;
         {
             DiagScope t("router_logits", s);
             e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
@@ -300,7 +318,8 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
         if (!aligned16(ws)) return MOE_ERR_ALIGN;
         if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
         char *base = static_cast<char *>(ws);
-        float *logits = reinterpret_cast<float *>(base + L.logits);
+        const RouteWs RW = route_ws(D);
+        float *logits = reinterpret_cast<float *>(base + L.route + RW.logits);
         int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(base + L.ids);
         float *tw = topk_w_out ? topk_w_out : reinterpret_cast<float *>(base + L.tw);
         int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
@@ -317,11 +336,23 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
 
         hipError_t e;
-        {
+        const bool filtered = moe::route_filter_ok(D.T, D.d, D.E);
+        if (filtered) {
+            e = moe::launch_route_filtered(x, router_w, router_bias, logits,
+                                           reinterpret_cast<float *>(base + L.route + RW.nx),
+                                           reinterpret_cast<float *>(base + L.route + RW.nw), ids,
+                                           tw, D.T, D.d, D.E, D.k, s);
+        } else {
             DiagScope t("router_logits", s);
             e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
         }
-        if (moe::topk_permute_fusable(D.T, D.E, D.k)) {
+        if (filtered) {
+            if (e == hipSuccess) {
+                DiagScope t("permute", s);
+                e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
+                                        D.E, D.k, perm_ws, s);
+            }
+        } else if (moe::topk_permute_fusable(D.T, D.E, D.k)) {
             if (e == hipSuccess) {
                 DiagScope t("topk_permute", s);
                 e = moe::launch_topk_permute_small(logits, ids, tw, counts, offsets, sorted_rows,

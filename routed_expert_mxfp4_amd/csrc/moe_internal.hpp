@@ -18,6 +18,7 @@ namespace moe {
 constexpr int kMaxExperts = 1024;   // top-k keeps <= 16 logits per lane
 constexpr int kMaxTopK = 32;
 constexpr int kMfmaMinT = 128;      // tokens from which the scaled-MFMA expert path runs
+constexpr int kRouteFilterMinT = 256; // tokens from which routing filters on bf16 MFMA logits
 
 // ---------------------------------------------------------------------------
 // Small device helpers.
@@ -158,6 +159,13 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const flo
                                 float *logits, int T, int d, int E, hipStream_t s);
 hipError_t launch_topk_softmax(const float *logits, int32_t *ids, float *w, int T, int E,
                                int k, hipStream_t s);
+// Many tokens: top-k + softmax of the canonical logits without computing all
+// of them (bf16 MFMA filter, certified bounds, canonical refinement).
+// zt: fp32 [T][E] scratch, nx: fp32 [T], nw: fp32 [E] scratch.
+bool route_filter_ok(int T, int d, int E);
+hipError_t launch_route_filtered(const uint16_t *x, const uint16_t *wr, const float *bias,
+                                 float *zt, float *nx, float *nw, int32_t *ids, float *tw,
+                                 int T, int d, int E, int k, hipStream_t s);
 
 size_t permute_ws_bytes(int T, int E);
 // plan (nullable): int32 [1 + E] = number of active experts, then their ids.

@@ -1,0 +1,429 @@
+// route_filter.hip -- routing for many tokens: approximate logits on the
+// bf16 matrix cores, then the canonical logit only where it can matter.
+//
+// The canonical logit of (t, e) is the router dot product summed in the
+// fixed fp64 order of route.hip, plus the bias, rounded once to fp32.  For
+// prefill-sized T computing all T x E of them in fp64 dominates the layer,
+// yet only the k largest per token are ever used.  So:
+//   1. zt[t][e] = x[t] . wr[e] on v_mfma_f32_16x16x32_bf16 (bf16 products
+//      are exact in fp32; the fp32 additions are the only error), and the
+//      row norms |x_t|, |w_e| (computed in fp64, rounded up).
+//   2. Per token, a certified interval for every canonical logit:
+//        |z_te - (zt_te + b_e)| <= B_te
+//        B_te = gamma |x_t| |w_e| (1 + 2^-20) + 2^-23 (|zt_te + b_e| + gamma |x_t| |w_e|)
+//               + 1e-30
+//      with gamma = 2 (d + 64) 2^-23 / (1 - 2 (d + 64) 2^-23): twice the
+//      classic bound (d u / (1 - d u)) sum |x_i w_i| of any fp32 summation
+//      order (u = 2^-23 also covers truncating adders), Cauchy-Schwarz for
+//      sum |x_i w_i| <= |x_t| |w_e|, and 2^-23 |z| for the final rounding of
+//      the canonical value.  Rows holding a subnormal, infinite or NaN bf16
+//      get an infinite norm (no finite interval), which forces the exact
+//      path below.
+//   3. tau = the k-th largest lower end.  An expert whose upper end is
+//      below tau is below k others for certain, so it is not selected; the
+//      canonical logits of the others (the candidates, usually ~20) are
+//      computed exactly, and top-k + softmax run over them with the
+//      non-candidates at -inf.  A token with any non-finite interval, or
+//      more than kCandMax candidates (e.g. massively tied logits), takes
+//      the canonical logits of all E experts instead.
+// The selected experts and weights are therefore exactly those of the
+// canonical logits; only the amount of fp64 work depends on the data.
+#include "moe_internal.hpp"
+#include "select_dev.hpp"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kCandMax = 64;
+
+// ---------------------------------------------------------------------------
+// Row norms in fp64, rounded up to fp32; +inf if the row holds a subnormal,
+// infinite or NaN bf16.  One wave per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void row_norm_kernel(const uint16_t *__restrict__ m, int R,
+                                                       int d, float *__restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= R) return;
+    const uint16_t *row = m + (size_t)r * d;
+    double ss = 0.0;
+    bool odd = false;
+    for (int i = lane * 8; i < d; i += 64 * 8) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(row + i);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t b = (w[j] >> (16 * h)) & 0xFFFFu;
+                const uint32_t ex = (b >> 7) & 0xFFu, mant = b & 0x7Fu;
+                odd |= ex == 0xFFu || (ex == 0u && mant != 0u);
+                const double v = (double)__uint_as_float(b << 16);
+                ss = fma(v, v, ss);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const bool any_odd = __ballot(odd) != 0ull;
+    if (lane == 0) {
+        // sqrt in fp64 (relative error ~1e-16) then a margin far above it
+        const float n = (float)(sqrt(ss) * (1.0 + 1.0 / 1048576.0));
+        out[r] = any_odd || !(n < INFINITY) ? INFINITY : n;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// zt = x . wr^T on bf16 MFMA.  Block: 128 tokens x 128 experts, four waves
+// in 2 x 2 (64 x 64 each, 4 x 4 tiles of 16 x 16), K in stages of 64
+// staged through LDS (double buffer, next stage held in registers while the
+// current one computes).  Rows past T or E are clamped loads, discarded.
+// ---------------------------------------------------------------------------
+constexpr int kFT = 128, kFE = 128, kFK = 64;
+constexpr int kFStride = 2 * kFK + 16;                 // bytes per LDS row (conflict-free b128)
+constexpr int kFOperand = kFT * kFStride;              // 18432
+constexpr int kFLds = 2 * 2 * kFOperand;               // 73728
+
+__global__ __launch_bounds__(256) void filter_gemm_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ wr,
+                                                          float *__restrict__ zt, int T, int d,
+                                                          int E) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid >> 1, wn = wid & 1;
+    const int t0 = blockIdx.y * kFT, e0 = blockIdx.x * kFE;
+    const int r16 = lane & 15, g = lane >> 4;
+    // this thread's 4 + 4 sixteen-byte pieces of each stage
+    const uint16_t *pa[4], *pb[4];
+    int so[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i, row = idx >> 3, pc = idx & 7;
+        pa[i] = x + (size_t)min(t0 + row, T - 1) * d + pc * 8;
+        pb[i] = wr + (size_t)min(e0 + row, E - 1) * d + pc * 8;
+        so[i] = row * kFStride + pc * 16;
+    }
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nst = d / kFK;
+    uint4 ra[4], rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ra[i] = *reinterpret_cast<const uint4 *>(pa[i]);
+        rb[i] = *reinterpret_cast<const uint4 *>(pb[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<uint4 *>(lds + so[i]) = ra[i];
+        *reinterpret_cast<uint4 *>(lds + kFOperand + so[i]) = rb[i];
+    }
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+        uint8_t *cur = lds + (s & 1) * 2 * kFOperand;
+        uint8_t *nxt = lds + ((s + 1) & 1) * 2 * kFOperand;
+        // the next stage (the last one again on the final pass: a harmless
+        // rewrite of the idle buffer keeps the loop free of branches)
+        const size_t koff = (size_t)min(s + 1, nst - 1) * kFK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ra[i] = *reinterpret_cast<const uint4 *>(pa[i] + koff);
+            rb[i] = *reinterpret_cast<const uint4 *>(pb[i] + koff);
+        }
+#pragma unroll
+        for (int ks = 0; ks < kFK / 32; ++ks) {
+            bf16x8_t af[4], bfr[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                af[mt] = *reinterpret_cast<const bf16x8_t *>(
+                    cur + (wm * 64 + mt * 16 + r16) * kFStride + ks * 64 + 16 * g);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                bfr[nt] = *reinterpret_cast<const bf16x8_t *>(
+                    cur + kFOperand + (wn * 64 + nt * 16 + r16) * kFStride + ks * 64 + 16 * g);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt],
+                                                                          acc[mt][nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<uint4 *>(nxt + so[i]) = ra[i];
+            *reinterpret_cast<uint4 *>(nxt + kFOperand + so[i]) = rb[i];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + wm * 64 + mt * 16 + 4 * g + i;
+            if (t < T) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int e = e0 + wn * 64 + nt * 16 + r16;
+                    if (e < E) zt[(size_t)t * E + e] = acc[mt][nt][i];
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Certified selection + canonical refinement + top-k/softmax: one wave per
+// token.
+// ---------------------------------------------------------------------------
+// fp32 bounds that contain a finite double: round toward -inf / +inf (one
+// step of the fp32 grid when the nearest rounding went the wrong way).
+__device__ __forceinline__ float f32_step_down(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if (f == 0.f) return -__uint_as_float(1u);             // largest negative subnormal
+    return __uint_as_float(f > 0.f ? u - 1u : u + 1u);
+}
+__device__ __forceinline__ float f32_down(double v) {
+    const float f = (float)v;
+    return (double)f > v ? f32_step_down(f) : f;
+}
+__device__ __forceinline__ float f32_up(double v) {
+    const float f = (float)v;
+    return (double)f < v ? -f32_step_down(-f) : f;
+}
+
+// The canonical logit of (token row xr, expert row wrow): lane c sums its
+// P = d / 64 inputs in ascending order in fp64, the 64 sums meet in the
+// fixed xor-butterfly tree, the bias is added in fp64, one rounding.  Same
+// arithmetic, in the same order, as the router kernels of route.hip.
+__device__ __forceinline__ float canonical_logit(const uint16_t *xr, const uint16_t *wrow, int P,
+                                                 int lane, double bias) {
+    const uint16_t *xc = xr + (size_t)lane * P, *wc = wrow + (size_t)lane * P;
+    double acc = 0.0;
+    int p = 0;
+    if ((P & 7) == 0) {
+        for (; p < P; p += 8) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(xc + p);
+            const uint4 wv = *reinterpret_cast<const uint4 *>(wc + p);
+            const uint32_t xx[4] = {xv.x, xv.y, xv.z, xv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = fma((double)__uint_as_float(xx[q] << 16), (double)__uint_as_float(ww[q] << 16), acc);
+                acc = fma((double)__uint_as_float(xx[q] & 0xFFFF0000u),
+                          (double)__uint_as_float(ww[q] & 0xFFFF0000u), acc);
+            }
+        }
+    } else {
+        for (; p < P; ++p)
+            acc = fma((double)__uint_as_float((uint32_t)xc[p] << 16),
+                      (double)__uint_as_float((uint32_t)wc[p] << 16), acc);
+    }
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) acc += __shfl_xor(acc, w, 64);
+    return (float)(acc + bias);
+}
+
+// canonical_logit with the lane's chunks (8 NQ inputs) already in registers.
+template <int NQ>
+__device__ __forceinline__ float canonical_from_regs(const uint4 (&xq)[NQ], const uint4 (&wq)[NQ],
+                                                     int lane, double bias) {
+    double acc = 0.0;
+#pragma unroll
+    for (int p = 0; p < NQ; ++p) {
+        const uint32_t xx[4] = {xq[p].x, xq[p].y, xq[p].z, xq[p].w};
+        const uint32_t ww[4] = {wq[p].x, wq[p].y, wq[p].z, wq[p].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc = fma((double)__uint_as_float(xx[q] << 16), (double)__uint_as_float(ww[q] << 16), acc);
+            acc = fma((double)__uint_as_float(xx[q] & 0xFFFF0000u),
+                      (double)__uint_as_float(ww[q] & 0xFFFF0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) acc += __shfl_xor(acc, w, 64);
+    return (float)(acc + bias);
+}
+
+template <int PL, int NQ>
+__global__ __launch_bounds__(256) void select_refine_kernel(
+    const float *__restrict__ zt, const float *__restrict__ nx, const float *__restrict__ nw,
+    const float *__restrict__ bias, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ wr, int32_t *__restrict__ ids, float *__restrict__ tw, int T,
+    int d, int E, int k, double gamma) {
+    extern __shared__ float srow[];                        // [4][E] masked canonical logits
+    __shared__ int cand[4][kCandMax];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wid;
+    if (t >= T) return;                                    // no block-level sync below
+    float *row = srow + (size_t)wid * E;
+    const double gx = gamma * (double)nx[t];
+    uint32_t lok[PL], upk[PL];
+    bool bad = !(gx < INFINITY);
+    float zl[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) zl[i] = zt[(size_t)t * E + min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int e = lane + 64 * i;
+        lok[i] = 0u;
+        upk[i] = 0u;
+        if (e < E) {
+            const double zf = (double)zl[i] + (bias ? (double)bias[e] : 0.0);
+            const double sb = gx * (double)nw[e];
+            const double B = sb * (1.0 + 1.0 / 1048576.0) + (fabs(zf) + sb) * (1.0 / 8388608.0) + 1e-30;
+            const double lo = zf - B, up = zf + B;
+            if (!(fabs(lo) < INFINITY) || !(fabs(up) < INFINITY)) bad = true;
+            lok[i] = logit_key(f32_down(lo));
+            upk[i] = logit_key(f32_up(up));
+        }
+    }
+    bad = __ballot(bad) != 0ull;
+    int ncand = 0;
+    if (!bad) {
+        // tau: the k-th largest lower end (with multiplicity)
+        uint32_t kk[PL];
+#pragma unroll
+        for (int i = 0; i < PL; ++i) kk[i] = lok[i];
+        uint32_t tau = 0u;
+        for (int j = 0; j < k; ++j) {
+            uint32_t bk = 0u;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) bk = max(bk, kk[i]);
+            const uint32_t gk = wave_max_u32(bk);
+            const unsigned long long m = __ballot(bk == gk);
+            if (lane == (int)__builtin_ctzll(m)) {
+                bool done = false;
+#pragma unroll
+                for (int i = 0; i < PL; ++i)
+                    if (!done && kk[i] == gk) {
+                        kk[i] = 0u;
+                        done = true;
+                    }
+            }
+            tau = gk;
+        }
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const bool c = lane + 64 * i < E && upk[i] >= tau;
+            const unsigned long long m = __ballot(c);
+            const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
+            if (c && pos < kCandMax) cand[wid][pos] = lane + 64 * i;
+            base += (int)__popcll(m);
+        }
+        ncand = base;
+        bad = ncand > kCandMax;
+    }
+    if (bad) ncand = E;
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+        if (lane + 64 * i < E) row[lane + 64 * i] = -INFINITY;
+    const int P = d >> 6;
+    const uint16_t *xr = x + (size_t)t * d;
+    if constexpr (NQ > 0) {
+        // P = 8 NQ: the lane's chunk of x stays in registers; the next
+        // candidate's chunk of its router row is loaded while the current
+        // one is summed (every load of a chunk issued before any use)
+        uint4 xq[NQ], wq[2][NQ];
+        const uint4 *xc = reinterpret_cast<const uint4 *>(xr + (size_t)lane * P);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) xq[q] = xc[q];
+        auto wchunk = [&](int c) {
+            const int e = bad ? c : cand[wid][min(c, kCandMax - 1)];
+            return reinterpret_cast<const uint4 *>(wr + (size_t)min(e, E - 1) * d + (size_t)lane * P);
+        };
+        {
+            const uint4 *wc = wchunk(0);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) wq[0][q] = wc[q];
+        }
+        for (int c = 0; c < ncand; c += 2) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int cc = c + h;
+                if (cc < ncand) {
+                    const uint4 *wn = wchunk(min(cc + 1, ncand - 1));
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) wq[h ^ 1][q] = wn[q];
+                    const int e = bad ? cc : cand[wid][cc];
+                    const float z = canonical_from_regs<NQ>(xq, wq[h], lane,
+                                                            bias ? (double)bias[e] : 0.0);
+                    if (lane == 0) row[e] = z;
+                }
+            }
+        }
+    } else {
+        for (int c = 0; c < ncand; ++c) {
+            const int e = bad ? c : cand[wid][c];
+            const float z = canonical_logit(xr, wr + (size_t)e * d, P, lane,
+                                            bias ? (double)bias[e] : 0.0);
+            if (lane == 0) row[e] = z;
+        }
+    }
+    int se;
+    float sw;
+    wave_topk_softmax<PL>(row, E, k, &se, &sw);
+    if (lane < k) {
+        ids[(size_t)t * k + lane] = se;
+        tw[(size_t)t * k + lane] = sw;
+    }
+}
+
+bool g_filter_attr = false;
+
+}  // namespace
+
+bool route_filter_ok(int T, int d, int E) {
+    return T >= kRouteFilterMinT && d % 64 == 0 && E <= kMaxExperts;
+}
+
+hipError_t launch_route_filtered(const uint16_t *x, const uint16_t *wr, const float *bias,
+                                 float *zt, float *nx, float *nw, int32_t *ids, float *tw,
+                                 int T, int d, int E, int k, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    hipError_t e;
+    if (!g_filter_attr) {
+        e = hipFuncSetAttribute((const void *)filter_gemm_kernel,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kFLds);
+        if (e != hipSuccess) return e;
+        g_filter_attr = true;
+    }
+    {
+        DiagScope ds("router_norms", s);
+        row_norm_kernel<<<(T + 3) / 4, 256, 0, s>>>(x, T, d, nx);
+        row_norm_kernel<<<(E + 3) / 4, 256, 0, s>>>(wr, E, d, nw);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        DiagScope ds("router_filter_gemm", s);
+        dim3 grid((E + kFE - 1) / kFE, (T + kFT - 1) / kFT);
+        filter_gemm_kernel<<<grid, 256, kFLds, s>>>(x, wr, zt, T, d, E);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const double c = 2.0 * (double)(d + 64) / 8388608.0;
+    const double gamma = c / (1.0 - c);
+    const size_t lds = (size_t)4 * E * sizeof(float);
+    const int pl = (E + 63) / 64;
+    {
+        DiagScope ds("router_refine", s);
+        const unsigned grid = (unsigned)((T + 3) / 4);
+        const int P = d / 64;
+        // the register-resident chunk covers d = 512 * NQ; other d take the
+        // loop that reads both chunks from memory
+        if (pl <= 16 && P == 112)
+            select_refine_kernel<16, 14><<<grid, 256, lds, s>>>(zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+        else if (pl <= 4)
+            select_refine_kernel<4, 0><<<grid, 256, lds, s>>>(zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+        else if (pl <= 8)
+            select_refine_kernel<8, 0><<<grid, 256, lds, s>>>(zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+        else
+            select_refine_kernel<16, 0><<<grid, 256, lds, s>>>(zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe
