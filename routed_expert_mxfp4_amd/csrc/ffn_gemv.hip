@@ -429,7 +429,7 @@ __device__ __forceinline__ void dot_batch(const RowBuf<NBLD> &rb, const float4 (
 // wave j computes slot j's expert output for the block's rows (j = wid,
 // wid + 16, ...) and parks it in LDS; then y = sum_j w_j o_j in fp32, slot
 // order, one writer per output.
-constexpr int kDcRows = 16;
+constexpr int kDcRows = 32;
 
 template <int NBLD>
 __global__ __launch_bounds__(1024) void down_combine_split_kernel(

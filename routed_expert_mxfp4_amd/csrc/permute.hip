@@ -122,11 +122,12 @@ __global__ __launch_bounds__(1024) void topk_permute_small_kernel(
     int *off_s = reinterpret_cast<int *>(mask + kSub * E);       // [E]
     int *ids_s = off_s + E;                                      // [16 * k]
     __shared__ int tmp[48];
+    __shared__ uint32_t tsc[16][kTopkScratch];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     if (wid < T) {
         int e;
         float wt;
-        wave_topk_softmax<PL>(logits + (size_t)wid * E, E, k, &e, &wt);
+        wave_topk_softmax<PL>(logits + (size_t)wid * E, E, k, tsc[wid], &e, &wt);
         if (lane < k) {
             ids[(size_t)wid * k + lane] = e;
             tw[(size_t)wid * k + lane] = wt;
@@ -135,6 +136,82 @@ __global__ __launch_bounds__(1024) void topk_permute_small_kernel(
     }
     __syncthreads();
     permute_block(ids_s, mask, off_s, tmp, counts, offsets, sorted_rows, row_pos, plan, T, E, k);
+}
+
+// T * k <= 256: top-k + softmax (wave t for token t), then the grouping with
+// three barriers.  Each row's key (expert << 8 | row) is distinct, so its
+// position in (expert, token, slot) order is the number of smaller keys;
+// offsets[e] is the lower bound of e << 8 in the sorted keys; the plan lists
+// the experts that start a run of the sorted keys.
+constexpr int kTinyRows = 256;
+
+template <int PL>
+__global__ __launch_bounds__(1024) void topk_permute_tiny_kernel(
+    const float *__restrict__ logits, int32_t *__restrict__ ids, float *__restrict__ tw,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_rows, int32_t *__restrict__ row_pos,
+    int32_t *__restrict__ plan, int T, int E, int k) {
+    __shared__ uint32_t key[kTinyRows];
+    __shared__ uint32_t skey[kTinyRows];
+    __shared__ int wcnt[16];
+    __shared__ uint32_t tsc[16][kTopkScratch];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int R = T * k;
+    if (wid < T) {
+        int e;
+        float wt;
+        wave_topk_softmax<PL>(logits + (size_t)wid * E, E, k, tsc[wid], &e, &wt);
+        if (lane < k) {
+            const int r = wid * k + lane;
+            ids[r] = e;
+            tw[r] = wt;
+            key[r] = ((uint32_t)min(max(e, 0), E - 1) << 8) | (uint32_t)r;
+        }
+    }
+    __syncthreads();
+    if (tid < R) {
+        const uint32_t kv = key[tid];
+        int pos = 0;
+        for (int i = 0; i < R; ++i) pos += key[i] < kv ? 1 : 0;
+        skey[pos] = kv;
+        sorted_rows[pos] = tid;
+        row_pos[tid] = pos;
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += 1024) {
+        int lo = 0, hi = R;
+        const uint32_t t0 = (uint32_t)e << 8;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (skey[mid] < t0) lo = mid + 1;
+            else hi = mid;
+        }
+        offsets[e] = lo;
+        if (e < E) {
+            int lo2 = lo, hi2 = R;
+            const uint32_t t1 = (uint32_t)(e + 1) << 8;
+            while (lo2 < hi2) {
+                const int mid = (lo2 + hi2) >> 1;
+                if (skey[mid] < t1) lo2 = mid + 1;
+                else hi2 = mid;
+            }
+            counts[e] = lo2 - lo;
+        }
+    }
+    if (plan) {
+        const bool start = tid < R && (tid == 0 || (skey[tid] >> 8) != (skey[tid - 1] >> 8));
+        const unsigned long long m = __ballot(start);
+        if (lane == 0) wcnt[wid] = (int)__popcll(m);
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wid; ++w) base += wcnt[w];
+        if (start) plan[1 + base + (int)__popcll(m & ((1ull << lane) - 1ull))] = (int)(skey[tid] >> 8);
+        if (tid == 0) {
+            int tot = 0;
+            for (int w = 0; w < 16; ++w) tot += wcnt[w];
+            plan[0] = tot;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -288,6 +365,18 @@ hipError_t launch_topk_permute_small(const float *logits, int32_t *ids, float *t
                                      hipStream_t s) {
     const size_t lds = (size_t)kSub * E * 8 + (size_t)E * 4 + (size_t)16 * k * 4;
     const int pl = (E + 63) / 64;
+    if (T * k <= kTinyRows) {
+        if (pl <= 4)
+            topk_permute_tiny_kernel<4><<<1, 1024, 0, s>>>(logits, ids, tw, counts, offsets,
+                                                          sorted_rows, row_pos, plan, T, E, k);
+        else if (pl <= 8)
+            topk_permute_tiny_kernel<8><<<1, 1024, 0, s>>>(logits, ids, tw, counts, offsets,
+                                                          sorted_rows, row_pos, plan, T, E, k);
+        else
+            topk_permute_tiny_kernel<16><<<1, 1024, 0, s>>>(logits, ids, tw, counts, offsets,
+                                                           sorted_rows, row_pos, plan, T, E, k);
+        return hipGetLastError();
+    }
     if (pl <= 4)
         topk_permute_small_kernel<4><<<1, 1024, lds, s>>>(logits, ids, tw, counts, offsets,
                                                           sorted_rows, row_pos, plan, T, E, k);

@@ -207,12 +207,13 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
                                                            int32_t *__restrict__ ids,
                                                            float *__restrict__ w, int T,
                                                            int E, int k) {
+    __shared__ uint32_t tsc[4][kTopkScratch];
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     int e;
     float wt;
-    wave_topk_softmax<PL>(logits + (size_t)t * E, E, k, &e, &wt);
+    wave_topk_softmax<PL>(logits + (size_t)t * E, E, k, tsc[threadIdx.x >> 6], &e, &wt);
     if (lane < k) {
         ids[(size_t)t * k + lane] = e;
         w[(size_t)t * k + lane] = wt;

@@ -256,6 +256,7 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     int d, int E, int k, double gamma) {
     extern __shared__ float srow[];                        // [4][E] masked canonical logits
     __shared__ int cand[4][kCandMax];
+    __shared__ uint32_t tsc[4][kTopkScratch];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wid;
     if (t >= T) return;                                    // no block-level sync below
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     }
     int se;
     float sw;
-    wave_topk_softmax<PL>(row, E, k, &se, &sw);
+    wave_topk_softmax<PL>(row, E, k, tsc[wid], &se, &sw);
     if (lane < k) {
         ids[(size_t)t * k + lane] = se;
         tw[(size_t)t * k + lane] = sw;

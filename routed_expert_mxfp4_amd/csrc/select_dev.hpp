@@ -62,11 +62,22 @@ __device__ __forceinline__ float key_logit(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// Selects the top-k of one token's logits row.  On return lane j < k holds
-// the j-th selected expert in *sel_e and its weight in *sel_w.
+// LDS scratch of one wave for wave_topk_softmax (uint32 words).
+constexpr int kTopkScratch = 192;
+
+// Selects the top-k (k <= 32) of one token's logits row.  On return lane
+// j < k holds the j-th selected expert in *sel_e and its weight in *sel_w.
+// sc: this wave's kTopkScratch words of LDS.
+//
+// tau, the k-th largest of the 64 lane maxima, is at most the k-th largest
+// key (those k lane maxima are k distinct keys >= tau), so every selected
+// expert has key >= tau.  The keys >= tau (about k + a few on real logits)
+// are gathered and each one's rank in (key descending, expert ascending)
+// order is counted against the others.  If more than 64 keys tie at or
+// above tau, k rounds of wave-wide max/min select instead.
 template <int PL>
 __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row, int E, int k,
-                                                  int *sel_e, float *sel_w) {
+                                                  uint32_t *sc, int *sel_e, float *sel_w) {
     const int lane = threadIdx.x & 63;
     uint32_t key[PL];
     float v[PL];
@@ -76,27 +87,73 @@ __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row,
     for (int i = 0; i < PL; ++i) key[i] = lane + 64 * i < E ? logit_key(v[i]) : 0u;
     float my_v = 0.f;
     int my_e = 0;
-    for (int j = 0; j < k; ++j) {
-        uint32_t bk = 0u;
-        int bi = 0;
+    uint32_t lmax = 0u;
 #pragma unroll
-        for (int i = 0; i < PL; ++i)              // ascending e: ties keep the lower e
-            if (key[i] > bk) {
-                bk = key[i];
-                bi = i;
-            }
-        const uint32_t gk = wave_max_u32(bk);
-        const uint32_t cand = (bk == gk) ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu;
-        const uint32_t ge = wave_min_u32(cand);
-        if ((int)(ge & 63u) == lane) {
-            const int gi = (int)(ge >> 6);
+    for (int i = 0; i < PL; ++i) lmax = max(lmax, key[i]);
+    sc[lane] = lmax;
+    int r = 0;
+    for (int j = 0; j < 64; ++j) {
+        const uint32_t u = sc[j];
+        r += (u > lmax || (u == lmax && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long mt = __ballot(r == k - 1);
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lmax, (int)__builtin_ctzll(mt));
+    int C = 0;
+    const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
-            for (int i = 0; i < PL; ++i)
-                if (i == gi) key[i] = 0u;
+    for (int i = 0; i < PL; ++i) {
+        const bool c = key[i] != 0u && key[i] >= tau;
+        const unsigned long long m = __ballot(c);
+        const int pos = C + (int)__popcll(m & below);
+        if (c && pos < 64) {
+            sc[64 + pos] = key[i];
+            sc[128 + pos] = (uint32_t)(lane + 64 * i);
         }
-        if (lane == j) {
-            my_e = (int)ge;
-            my_v = key_logit(gk);
+        C += (int)__popcll(m);
+    }
+    if (C <= 64) {
+        int rank = 64;
+        uint32_t ka = 0u, ea = 0u;
+        if (lane < C) {
+            ka = sc[64 + lane];
+            ea = sc[128 + lane];
+            rank = 0;
+            for (int j = 0; j < C; ++j) {
+                const uint32_t kb = sc[64 + j], eb = sc[128 + j];
+                rank += (kb > ka || (kb == ka && eb < ea)) ? 1 : 0;
+            }
+        }
+        if (rank < k) {
+            sc[rank] = ea;
+            sc[32 + rank] = ka;
+        }
+        if (lane < k) {
+            my_e = (int)sc[lane];
+            my_v = key_logit(sc[32 + lane]);
+        }
+    } else {
+        for (int j = 0; j < k; ++j) {
+            uint32_t bk = 0u;
+            int bi = 0;
+#pragma unroll
+            for (int i = 0; i < PL; ++i)          // ascending e: ties keep the lower e
+                if (key[i] > bk) {
+                    bk = key[i];
+                    bi = i;
+                }
+            const uint32_t gk = wave_max_u32(bk);
+            const uint32_t cand = (bk == gk) ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu;
+            const uint32_t ge = wave_min_u32(cand);
+            if ((int)(ge & 63u) == lane) {
+                const int gi = (int)(ge >> 6);
+#pragma unroll
+                for (int i = 0; i < PL; ++i)
+                    if (i == gi) key[i] = 0u;
+            }
+            if (lane == j) {
+                my_e = (int)ge;
+                my_v = key_logit(gk);
+            }
         }
     }
     const double vmax = (double)__shfl(my_v, 0, 64);
