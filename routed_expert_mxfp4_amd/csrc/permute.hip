@@ -122,7 +122,7 @@ __global__ __launch_bounds__(1024) void topk_permute_small_kernel(
     int *off_s = reinterpret_cast<int *>(mask + kSub * E);       // [E]
     int *ids_s = off_s + E;                                      // [16 * k]
     __shared__ int tmp[48];
-    __shared__ uint32_t tsc[16][kTopkScratch];
+    __shared__ __align__(16) uint32_t tsc[16][kTopkScratch];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     if (wid < T) {
         int e;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(1024) void topk_permute_tiny_kernel(
     __shared__ uint32_t key[kTinyRows];
     __shared__ uint32_t skey[kTinyRows];
     __shared__ int wcnt[16];
-    __shared__ uint32_t tsc[16][kTopkScratch];
+    __shared__ __align__(16) uint32_t tsc[16][kTopkScratch];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int R = T * k;
     if (wid < T) {

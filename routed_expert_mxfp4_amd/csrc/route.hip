@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float *__restri
                                                            int32_t *__restrict__ ids,
                                                            float *__restrict__ w, int T,
                                                            int E, int k) {
-    __shared__ uint32_t tsc[4][kTopkScratch];
+    __shared__ __align__(16) uint32_t tsc[4][kTopkScratch];
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
     int d, int E, int k, double gamma) {
     extern __shared__ float srow[];                        // [4][E] masked canonical logits
     __shared__ int cand[4][kCandMax];
-    __shared__ uint32_t tsc[4][kTopkScratch];
+    __shared__ __align__(16) uint32_t tsc[4][kTopkScratch];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wid;
     if (t >= T) return;                                    // no block-level sync below

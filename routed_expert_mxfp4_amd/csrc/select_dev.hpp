@@ -62,19 +62,21 @@ __device__ __forceinline__ float key_logit(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// LDS scratch of one wave for wave_topk_softmax (uint32 words).
+// LDS scratch of one wave for wave_topk_softmax (uint32 words, 16-byte
+// aligned).
 constexpr int kTopkScratch = 192;
 
 // Selects the top-k (k <= 32) of one token's logits row.  On return lane
 // j < k holds the j-th selected expert in *sel_e and its weight in *sel_w.
 // sc: this wave's kTopkScratch words of LDS.
 //
-// tau, the k-th largest of the 64 lane maxima, is at most the k-th largest
-// key (those k lane maxima are k distinct keys >= tau), so every selected
-// expert has key >= tau.  The keys >= tau (about k + a few on real logits)
-// are gathered and each one's rank in (key descending, expert ascending)
-// order is counted against the others.  If more than 64 keys tie at or
-// above tau, k rounds of wave-wide max/min select instead.
+// tau, the k-th largest of the 64 lane maxima (found by bisection on the
+// key), is at most the k-th largest key: those k lane maxima are k distinct
+// keys >= tau.  So every selected expert has key >= tau.  The keys >= tau
+// (about k + a few on real logits) are gathered and each one's rank in (key
+// descending, expert ascending) order is counted against the others.  If
+// more than 64 keys lie at or above tau (massive ties), k rounds of
+// wave-wide max/min select instead.
 template <int PL>
 __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row, int E, int k,
                                                   uint32_t *sc, int *sel_e, float *sel_w) {
@@ -90,14 +92,14 @@ __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row,
     uint32_t lmax = 0u;
 #pragma unroll
     for (int i = 0; i < PL; ++i) lmax = max(lmax, key[i]);
-    sc[lane] = lmax;
-    int r = 0;
-    for (int j = 0; j < 64; ++j) {
-        const uint32_t u = sc[j];
-        r += (u > lmax || (u == lmax && j < lane)) ? 1 : 0;
+    // tau = the largest t with #{lanes : lmax >= t} >= k, by bisection on
+    // the key (each step one compare whose result is the ballot)
+    uint32_t tau = 0u;
+#pragma unroll 1
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = tau | (1u << bit);
+        if ((int)__popcll(__ballot(lmax >= t)) >= k) tau = t;
     }
-    const unsigned long long mt = __ballot(r == k - 1);
-    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lmax, (int)__builtin_ctzll(mt));
     int C = 0;
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll
@@ -114,15 +116,25 @@ __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row,
     if (C <= 64) {
         int rank = 64;
         uint32_t ka = 0u, ea = 0u;
+        const uint4 *sc4 = reinterpret_cast<const uint4 *>(sc);
         if (lane < C) {
             ka = sc[64 + lane];
             ea = sc[128 + lane];
             rank = 0;
-            for (int j = 0; j < C; ++j) {
-                const uint32_t kb = sc[64 + j], eb = sc[128 + j];
-                rank += (kb > ka || (kb == ka && eb < ea)) ? 1 : 0;
+        }
+        // candidates past C are ignored (keys there may be stale)
+#pragma unroll
+        for (int j4 = 0; j4 < 16; ++j4) {
+            if (4 * j4 < C) {
+                const uint4 kb4 = sc4[16 + j4], eb4 = sc4[32 + j4];
+                const uint32_t kb[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
+                const uint32_t eb[4] = {eb4.x, eb4.y, eb4.z, eb4.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    rank += (4 * j4 + q < C && (kb[q] > ka || (kb[q] == ka && eb[q] < ea))) ? 1 : 0;
             }
         }
+        if (lane >= C) rank = 64;
         if (rank < k) {
             sc[rank] = ea;
             sc[32 + rank] = ka;
