@@ -385,17 +385,17 @@ __device__ __forceinline__ void store_bf16x4(uint16_t *dst, const float (&v)[kDn
     *reinterpret_cast<uint2 *>(dst) = o;
 }
 
-template <int NBLD>
+template <int NBLD, int B = kDnBatch>
 struct RowBuf {
-    uint4 c[kDnBatch][NBLD];
-    uint32_t s[kDnBatch][NBLD];
+    uint4 c[B][NBLD];
+    uint32_t s[B][NBLD];
 };
 
-template <int NBLD>
+template <int NBLD, int B = kDnBatch>
 __device__ __forceinline__ void load_batch(rsrc_t codes, rsrc_t scales, int m, int lane,
-                                           int nblk, uint32_t code_row, RowBuf<NBLD> &rb) {
+                                           int nblk, uint32_t code_row, RowBuf<NBLD, B> &rb) {
 #pragma unroll
-    for (int rr = 0; rr < kDnBatch; ++rr)
+    for (int rr = 0; rr < B; ++rr)
 #pragma unroll
         for (int i = 0; i < NBLD; ++i) {
             const uint32_t b = (uint32_t)min(lane + 64 * i, nblk - 1);
@@ -405,11 +405,11 @@ __device__ __forceinline__ void load_batch(rsrc_t codes, rsrc_t scales, int m, i
         }
 }
 
-template <int NBLD>
-__device__ __forceinline__ void dot_batch(const RowBuf<NBLD> &rb, const float4 (&hv)[NBLD][8],
-                                          int lane, int nblk, float (&out)[kDnBatch]) {
+template <int NBLD, int B = kDnBatch>
+__device__ __forceinline__ void dot_batch(const RowBuf<NBLD, B> &rb, const float4 (&hv)[NBLD][8],
+                                          int lane, int nblk, float (&out)[B]) {
 #pragma unroll
-    for (int rr = 0; rr < kDnBatch; ++rr) {
+    for (int rr = 0; rr < B; ++rr) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < NBLD; ++i) {
@@ -425,20 +425,20 @@ __device__ __forceinline__ void dot_batch(const RowBuf<NBLD> &rb, const float4 (
     }
 }
 
-// Fused down + combine for small T: block (kDcRows output rows, token t);
-// wave j computes slot j's expert output for the block's rows (j = wid,
-// wid + 16, ...) and parks it in LDS; then y = sum_j w_j o_j in fp32, slot
-// order, one writer per output.
-constexpr int kDcRows = 32;
-
-template <int NBLD>
+// Fused down + combine for small T: block (ROWS output rows, token t); wave
+// j computes slot j's expert output for the block's rows (j = wid, wid + 16,
+// ...) in batches of B rows (the next batch's loads in flight during the
+// current batch's math) and parks it in LDS; then y = sum_j w_j o_j in fp32,
+// slot order, one writer per output.  ROWS is a multiple of B.
+template <int NBLD, int ROWS, int B>
 __global__ __launch_bounds__(1024) void down_combine_split_kernel(
     const float *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ ids,
     const float *__restrict__ topk_w, const int32_t *__restrict__ row_pos,
     uint16_t *__restrict__ y, int T, int d, int E, int k, int f) {
-    __shared__ float part[kMaxTopK][kDcRows];
+    static_assert(ROWS % B == 0, "whole batches");
+    __shared__ float part[kMaxTopK][ROWS];
     const int t = blockIdx.y;
-    const int m0 = blockIdx.x * kDcRows;
+    const int m0 = blockIdx.x * ROWS;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nblk = f >> 5;
@@ -454,37 +454,37 @@ __global__ __launch_bounds__(1024) void down_combine_split_kernel(
             const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
             float4 hv[NBLD][8];
             load_h_slice<NBLD>(hbuf, (uint32_t)p * f * 4u, lane, nblk, hv);
-            RowBuf<NBLD> A, B;
-            load_batch<NBLD>(codes, scales, m0, lane, nblk, code_row, A);
-            // batches of kDnBatch rows, the next batch's loads in flight
-            // during the current batch's math
-#pragma unroll 1
-            for (int b0 = 0; b0 < kDcRows; b0 += 2 * kDnBatch) {
-                load_batch<NBLD>(codes, scales, m0 + b0 + kDnBatch, lane, nblk, code_row, B);
+            RowBuf<NBLD, B> A, Bb;
+            constexpr int NB = ROWS / B;
+            load_batch<NBLD, B>(codes, scales, m0, lane, nblk, code_row, A);
+#pragma unroll
+            for (int bi = 0; bi < NB; bi += 2) {
+                if (bi + 1 < NB) load_batch<NBLD, B>(codes, scales, m0 + (bi + 1) * B, lane, nblk, code_row, Bb);
                 __builtin_amdgcn_sched_barrier(0);
-                float out[kDnBatch];
-                dot_batch<NBLD>(A, hv, lane, nblk, out);
+                float out[B];
+                dot_batch<NBLD, B>(A, hv, lane, nblk, out);
                 if (lane == 0) {
 #pragma unroll
-                    for (int rr = 0; rr < kDnBatch; ++rr) part[j][b0 + rr] = out[rr];
+                    for (int rr = 0; rr < B; ++rr) part[j][bi * B + rr] = out[rr];
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                if (b0 + 2 * kDnBatch < kDcRows)
-                    load_batch<NBLD>(codes, scales, m0 + b0 + 2 * kDnBatch, lane, nblk, code_row, A);
+                if (bi + 2 < NB) load_batch<NBLD, B>(codes, scales, m0 + (bi + 2) * B, lane, nblk, code_row, A);
                 __builtin_amdgcn_sched_barrier(0);
-                dot_batch<NBLD>(B, hv, lane, nblk, out);
-                if (lane == 0) {
+                if (bi + 1 < NB) {
+                    dot_batch<NBLD, B>(Bb, hv, lane, nblk, out);
+                    if (lane == 0) {
 #pragma unroll
-                    for (int rr = 0; rr < kDnBatch; ++rr) part[j][b0 + kDnBatch + rr] = out[rr];
+                        for (int rr = 0; rr < B; ++rr) part[j][(bi + 1) * B + rr] = out[rr];
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-        } else if (lane < kDcRows) {
+        } else if (lane < ROWS) {
             part[j][lane] = 0.f;
         }
     }
     __syncthreads();
-    if (threadIdx.x < kDcRows) {
+    if (threadIdx.x < ROWS) {
         float yv = 0.f;
         for (int j = 0; j < k; ++j) yv += topk_w[(size_t)t * k + j] * part[j][threadIdx.x];
         y[(size_t)t * d + m0 + threadIdx.x] = f32_to_bf16_rne(yv);
@@ -594,9 +594,16 @@ template <int NBLD>
 hipError_t launch_dc_split(const float *h, ExpertArgs w, const int32_t *ids,
                            const float *topk_w, const int32_t *row_pos, uint16_t *y, int T,
                            int d, int E, int k, int f, hipStream_t s) {
-    dim3 grid(d / kDcRows, T);
-    down_combine_split_kernel<NBLD><<<grid, 1024, 0, s>>>(h, w, ids, topk_w, row_pos, y, T, d,
-                                                           E, k, f);
+    // 28 output rows per block: 7168 / 28 = 256 blocks, one per CU
+    if (d % 28 == 0) {
+        dim3 grid(d / 28, T);
+        down_combine_split_kernel<NBLD, 28, 4><<<grid, 1024, 0, s>>>(h, w, ids, topk_w, row_pos, y,
+                                                                      T, d, E, k, f);
+    } else {
+        dim3 grid(d / 32, T);
+        down_combine_split_kernel<NBLD, 32, 4><<<grid, 1024, 0, s>>>(h, w, ids, topk_w, row_pos, y,
+                                                                      T, d, E, k, f);
+    }
     return hipGetLastError();
 }
 

@@ -136,38 +136,44 @@ hipError_t launch_logits_tile(const uint16_t *x, const uint16_t *wr, const float
 // Lane c of a wave sums chunk c (P consecutive inputs) of one router row.  A
 // direct load would have the 64 lanes of a wave read 64 rows 2P bytes apart,
 // so every 16-byte load touches 64 cache lines; instead the block copies its
-// four router rows into LDS with coalesced 16-byte loads, laid out chunk by
+// router rows into LDS with coalesced 16-byte loads, laid out chunk by
 // chunk with 16 bytes of padding (a chunk stride of 2P+16 bytes keeps the
 // 16 lanes of a b128 read on distinct banks), and each lane then reads its
 // own chunk from LDS.  The lane's chunk of x goes straight to registers.
 constexpr int kStagePieces = 16;                    // d <= 8192
+constexpr int kRouterRowsPerBlock = 4;              // one token: router rows (waves) per block
 
-__global__ __launch_bounds__(256) void router_small_kernel(
+// RPB router rows per block (one wave each); a block stages its rows with
+// RPB * 64 threads, each loading d / 512 sixteen-byte pieces.
+template <int RPB>
+__global__ __launch_bounds__(64 * RPB) void router_small_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     const float *__restrict__ bias, float *__restrict__ logits, int T, int d, int E) {
-    extern __shared__ uint4 wrs[];                  // [4][64][(2P+16)/16] + 1 spare
+    constexpr int kThreads = 64 * RPB;
+    constexpr int kPer = kStagePieces;              // pieces per thread: d / 512 <= 16
+    extern __shared__ uint4 wrs[];                  // [RPB][64][(2P+16)/16] + 1 spare
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int P = d >> 6;
     const int q_per_chunk = P >> 3;                 // 16-byte pieces per chunk
     const int cstride = q_per_chunk + 1;            // in uint4, with padding
-    const int e0 = blockIdx.x * 4;
+    const int e0 = blockIdx.x * RPB;
     const int pieces = 64 * q_per_chunk;            // 16-byte pieces per row
-    const int total = 4 * pieces;                   // <= 256 * kStagePieces
+    const int total = RPB * pieces;                 // <= kThreads * kPer
     // every load first, then every LDS store: one memory round trip
-    uint4 buf[kStagePieces];
+    uint4 buf[kPer];
 #pragma unroll
-    for (int j = 0; j < kStagePieces; ++j) {
-        const int i = min((int)threadIdx.x + 256 * j, total - 1);
+    for (int j = 0; j < kPer; ++j) {
+        const int i = min((int)threadIdx.x + kThreads * j, total - 1);
         const int r = i / pieces, q = i - r * pieces;
         buf[j] = reinterpret_cast<const uint4 *>(wr + (size_t)min(e0 + r, E - 1) * d)[q];
     }
     // every load completes here, then unconditional stores (pieces past the
     // end go to a spare slot)
     loads_done(buf);
-    const int spare = 4 * 64 * cstride;
+    const int spare = RPB * 64 * cstride;
 #pragma unroll
-    for (int j = 0; j < kStagePieces; ++j) {
-        const int i = (int)threadIdx.x + 256 * j;
+    for (int j = 0; j < kPer; ++j) {
+        const int i = (int)threadIdx.x + kThreads * j;
         const int r = i / pieces, q = i - r * pieces;
         const int c = q / q_per_chunk, w = q - c * q_per_chunk;
         wrs[i < total ? (r * 64 + c) * cstride + w : spare] = buf[j];
@@ -226,9 +232,11 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const flo
                                 float *logits, int T, int d, int E, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     const int P = d / 64;
-    const size_t lds = (size_t)4 * 64 * ((P / 8) + 1) * 16 + 16;   // + spare slot
+    constexpr int kRpb = kRouterRowsPerBlock;
+    const size_t lds = (size_t)kRpb * 64 * ((P / 8) + 1) * 16 + 16;   // + spare slot
     if (T == 1 && P % 8 == 0 && d <= 8192 && lds <= 65536) {
-        router_small_kernel<<<(E + 3) / 4, 256, lds, s>>>(x, wr, bias, logits, T, d, E);
+        router_small_kernel<kRpb><<<(E + kRpb - 1) / kRpb, 64 * kRpb, lds, s>>>(x, wr, bias, logits,
+                                                                               T, d, E);
         return hipGetLastError();
     }
     if (T < 4) return launch_logits_tile<1, 4>(x, wr, bias, logits, T, d, E, s);
