@@ -22,7 +22,8 @@ extern "C" {
 
 /* The activation split the scaled-MFMA expert path feeds to the matrix
  * cores, exposed for bit-exact checks: each row of `in` (rows x K, K a
- * multiple of 128; bf16 bits if in_is_bf16, else fp32; 16-byte aligned) is
+ * multiple of 128; bf16 bits if in_is_bf16, else fp32; in and out 16-byte
+ * aligned; the output under 4 GiB) is
  * cut into 32-element blocks and each block a into two OCP MX E2M3 terms,
  * hi = MX(a), lo = MX(a - hi): shared exponent X = floor(log2 max|.|) - 2
  * clamped to [-127, 127] (E8M0 code X + 127; all-zero block -> code 0),

@@ -39,9 +39,14 @@ constexpr int kSlotsRow = 13;    // 16-byte pieces per row per K step
 // MX E2M3 conversion (OCP MX v1.0): shared exponent X = floor(log2(amax)) - 2
 // clamped to [-127, 127] (E8M0 code X + 127; an all-zero block gets code 0);
 // elements v / 2^X rounded to nearest even onto the E2M3 grid (subnormals
-// 0, 1/8, .., 7/8; then 1..1.875, 2..3.75, 4..7.5), saturating at 7.5.  The
-// code is monotone in the rounded magnitude, so it is computed directly.
+// 0, 1/8, .., 7/8; then 1..1.875, 2..3.75, 4..7.5), saturating at 7.5, the
+// sign kept (also on zero).  gfx950 converts and packs 32 such elements in
+// one instruction, and decodes them back exactly.
 // ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x32_t __attribute__((ext_vector_type(32)));
+typedef unsigned u32x6_t __attribute__((ext_vector_type(6)));
+
 __device__ __forceinline__ int mx_exponent(float amax) {
     if (!(amax > 0.f)) return -127;
     int e;
@@ -49,99 +54,121 @@ __device__ __forceinline__ int mx_exponent(float amax) {
     return min(max(e - 1 - 2, -127), 127);
 }
 
-__device__ __forceinline__ uint32_t e2m3_encode(float r) {
-    const uint32_t sign = (__float_as_uint(r) >> 31) << 5;
-    const float a = fabsf(r);
-    uint32_t c;
-    if (a >= 7.5f) c = 31u;
-    else if (a < 2.0f) c = (uint32_t)__builtin_rintf(a * 8.0f);
-    else if (a < 4.0f) c = 8u + (uint32_t)__builtin_rintf(a * 4.0f);
-    else c = 16u + (uint32_t)__builtin_rintf(a * 2.0f);
-    return sign | c;
+// The scale 2^X as the conversions' fp32 operand: they read only its
+// exponent field, which holds the E8M0 code (X = -127 gives +0.0f).
+__device__ __forceinline__ float e8m0_operand(int X) {
+    return __uint_as_float((uint32_t)(X + 127) << 23);
 }
 
-__device__ __forceinline__ float e2m3_decode(uint32_t c) {
-    const uint32_t f = (c >> 3) & 3u, m = c & 7u;
-    const float mag = f == 0u ? (float)m * 0.125f : ldexpf(1.0f + (float)m * 0.125f, (int)f - 1);
-    return (c & 32u) ? -mag : mag;
+// Codes of 32 values, 6 bits each, element i at bits 6i of the 192 bits.
+// The conversion puts its first operand's 16 values in the even slots and
+// the second's in the odd ones.  It writes its first result registers
+// before it has read all of its sources, so its destination must not
+// overlap them: the empty asm keeps the sources live past the instruction
+// (and, taking the result, cannot be hoisted above it), which keeps the
+// register allocator from overlapping them.
+__device__ __forceinline__ u32x6_t e2m3_pack32(const float (&v)[32], float scale) {
+    f32x16_t ev, od;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        ev[m] = v[2 * m];
+        od[m] = v[2 * m + 1];
+    }
+    u32x6_t c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, scale);
+    asm volatile("" : "+v"(c) : "v"(ev), "v"(od), "v"(scale));
+    return c;
 }
 
-__device__ __forceinline__ float group16_max_f32(float v) {
-    v = fmaxf(v, dpp_ror_f32<8>(v));
-    v = fmaxf(v, dpp_ror_f32<4>(v));
-    v = fmaxf(v, dpp_ror_f32<2>(v));
-    v = fmaxf(v, dpp_ror_f32<1>(v));
+// The exact values of 32 packed codes under scale 2^X (same constraint).
+__device__ __forceinline__ f32x32_t e2m3_unpack32(u32x6_t c, float scale) {
+    f32x32_t v = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, scale);
+    asm volatile("" : "+v"(v) : "v"(c), "v"(scale));
     return v;
 }
 
-template <typename In>
-__device__ __forceinline__ float2 load_pair_f32(const In *p);
-template <>
-__device__ __forceinline__ float2 load_pair_f32<uint16_t>(const uint16_t *p) {
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
-    return make_float2(bf16_bits_to_f32(w & 0xFFFFu), bf16_bits_to_f32(w >> 16));
-}
-template <>
-__device__ __forceinline__ float2 load_pair_f32<float>(const float *p) {
-    return *reinterpret_cast<const float2 *>(p);
-}
-
-// Byte offset, inside a block's 48 bytes, of byte o (0..23) of term t's
-// code stream.
-__device__ __forceinline__ int code_byte(int t, int o) {
-    return o < 16 ? 16 * t + o : 32 + 8 * t + (o - 16);
-}
-
-// Packs the 12-bit code pairs of the 16 lanes of a group (lane j: elements
-// 2j, 2j+1 of the block) into term t's 24-byte stream: lanes j % 4 == 0
-// write stream bytes 6 (j / 4) .. +5 as three 16-bit words.
-__device__ __forceinline__ void store_block_codes(uint8_t *blk48, int t, uint32_t pair12, int j) {
-    const uint32_t p1 = (uint32_t)__shfl_down((int)pair12, 1, 16);
-    const uint32_t p2 = (uint32_t)__shfl_down((int)pair12, 2, 16);
-    const uint32_t p3 = (uint32_t)__shfl_down((int)pair12, 3, 16);
-    if ((j & 3) == 0) {
-        const unsigned long long bits = (unsigned long long)pair12 |
-                                        ((unsigned long long)p1 << 12) |
-                                        ((unsigned long long)p2 << 24) |
-                                        ((unsigned long long)p3 << 36);
-        const int o = 6 * (j >> 2);
+__device__ __forceinline__ float amax32(const float (&v)[32]) {
+    float a = 0.f;
 #pragma unroll
-        for (int q = 0; q < 3; ++q)
-            *reinterpret_cast<uint16_t *>(blk48 + code_byte(t, o + 2 * q)) =
-                (uint16_t)((bits >> (16 * q)) & 0xFFFFu);
+    for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+    return a;
+}
+
+// Two-term split of one 32-element block held by one lane: hi = the block
+// quantised, lo = the residual (exact in fp32) quantised with its own scale.
+struct SplitBlock {
+    u32x6_t hi, lo;
+    uint32_t scales;                              // hi E8M0 | lo E8M0 << 8
+};
+
+__device__ __forceinline__ SplitBlock split_block32(const float (&v)[32]) {
+    SplitBlock b;
+    const int xh = mx_exponent(amax32(v));
+    b.hi = e2m3_pack32(v, e8m0_operand(xh));
+    const f32x32_t hd = e2m3_unpack32(b.hi, e8m0_operand(xh));
+    float r[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) r[i] = v[i] - hd[i];
+    const int xl = mx_exponent(amax32(r));
+    b.lo = e2m3_pack32(r, e8m0_operand(xl));
+    b.scales = (uint32_t)(xh + 127) | ((uint32_t)(xl + 127) << 8);
+    return b;
+}
+
+// The block's 48 code bytes [hi 0..15][lo 0..15][hi 16..23][lo 16..23] as
+// three 16-byte words.
+__device__ __forceinline__ void split_words(const SplitBlock &b, u32x4_t (&w)[3]) {
+    w[0] = u32x4_t{b.hi[0], b.hi[1], b.hi[2], b.hi[3]};
+    w[1] = u32x4_t{b.lo[0], b.lo[1], b.lo[2], b.lo[3]};
+    w[2] = u32x4_t{b.hi[4], b.hi[5], b.lo[4], b.lo[5]};
+}
+
+template <typename In>
+__device__ __forceinline__ void load_block32(const In *p, float (&v)[32]);
+template <>
+__device__ __forceinline__ void load_block32<uint16_t>(const uint16_t *p, float (&v)[32]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t *>(p + 8 * c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[8 * c + 2 * q] = __uint_as_float(w[q] << 16);
+            v[8 * c + 2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+    }
+}
+template <>
+__device__ __forceinline__ void load_block32<float>(const float *p, float (&v)[32]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const f32x4_t w = *reinterpret_cast<const f32x4_t *>(p + 4 * c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[4 * c + q] = w[q];
     }
 }
 
-// One wave per (row, step): lane l handles elements 2j, 2j+1 (j = l % 16) of
-// MX block g = l / 16 of the step.
+// One lane per 32-element block: item = row * (K / 32) + block.  Block g of
+// step st of row r lands at bytes 48 g of the row's step, its scales at
+// 192 + 2 g; the lane of block 0 zeroes the step's pad bytes 200..207.
 template <typename In>
-__global__ __launch_bounds__(256) void mx_split_e2m3_kernel(const In *__restrict__ in, int rows,
-                                                            int K, uint8_t *__restrict__ q) {
-    const int lane = threadIdx.x & 63;
-    const int nsteps = K >> 7;
-    const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= (long long)rows * nsteps) return;
-    const int r = (int)(item / nsteps), st = (int)(item % nsteps);
-    const int g = lane >> 4, j = lane & 15;
-    const float2 v = load_pair_f32<In>(in + (size_t)r * K + (size_t)st * 128 + g * 32 + 2 * j);
-    uint8_t *out = q + ((size_t)r * nsteps + st) * kStepBytes;
-    // hi term
-    const float amax_h = group16_max_f32(fmaxf(fabsf(v.x), fabsf(v.y)));
-    const int xh = mx_exponent(amax_h);
-    const uint32_t h0 = e2m3_encode(ldexpf(v.x, -xh)), h1 = e2m3_encode(ldexpf(v.y, -xh));
-    // lo term: the residual a - hi is exact in fp32
-    const float r0 = v.x - ldexpf(e2m3_decode(h0), xh);
-    const float r1 = v.y - ldexpf(e2m3_decode(h1), xh);
-    const float amax_l = group16_max_f32(fmaxf(fabsf(r0), fabsf(r1)));
-    const int xl = mx_exponent(amax_l);
-    const uint32_t l0 = e2m3_encode(ldexpf(r0, -xl)), l1 = e2m3_encode(ldexpf(r1, -xl));
-    store_block_codes(out + 48 * g, 0, h0 | (h1 << 6), j);
-    store_block_codes(out + 48 * g, 1, l0 | (l1 << 6), j);
-    if (j == 0) {
-        out[192 + 2 * g] = (uint8_t)(xh + 127);
-        out[193 + 2 * g] = (uint8_t)(xl + 127);
-    }
-    if (lane == 0) *reinterpret_cast<uint2 *>(out + 200) = make_uint2(0u, 0u);
+__global__ __launch_bounds__(256) void mx_split_e2m3_kernel(const In *__restrict__ in,
+                                                            uint32_t items, int K,
+                                                            uint8_t *__restrict__ q) {
+    const uint32_t item = blockIdx.x * 256u + threadIdx.x;
+    if (item >= items) return;
+    const uint32_t nblk = (uint32_t)K >> 5;
+    const uint32_t r = item / nblk, b = item - r * nblk;
+    float v[32];
+    load_block32<In>(in + (size_t)r * K + 32 * b, v);
+    const SplitBlock sb = split_block32(v);
+    uint8_t *step = q + ((size_t)r * (nblk >> 2) + (b >> 2)) * kStepBytes;
+    u32x4_t w[3];
+    split_words(sb, w);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(step + 48 * (b & 3));
+    dst[0] = w[0];
+    dst[1] = w[1];
+    dst[2] = w[2];
+    *reinterpret_cast<uint16_t *>(step + 192 + 2 * (b & 3)) = (uint16_t)sb.scales;
+    if ((b & 3) == 0) *reinterpret_cast<u32x2_t *>(step + 200) = u32x2_t{0u, 0u};
 }
 
 // ---------------------------------------------------------------------------
@@ -502,13 +529,14 @@ __device__ __forceinline__ bool select_tile(const int32_t *tiles, const int32_t 
     return true;
 }
 
-// kGateUp: A = split x (token rows), out = h fp32 [rows][f] (silu(gate) * up);
-// else:    A = split h (expert-major rows), out = rows_out bf16 [rows][d].
+// kGateUp: A = split x (token rows), out = hq, the split of h = silu(gate) *
+//          up [rows][f] (expert-major rows), the down pass's A;
+// else:    A = hq, out = rows_out bf16 [rows][d].
 template <bool kGateUp>
 __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     const uint8_t *__restrict__ aq, ExpertArgs W, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
-    const int32_t *__restrict__ tiles, float *__restrict__ h, uint16_t *__restrict__ rows_out,
+    const int32_t *__restrict__ tiles, uint8_t *__restrict__ hq, uint16_t *__restrict__ rows_out,
     int T, int d, int E, int k, int f) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ int a_rowidx[kBM];
@@ -601,26 +629,74 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // epilogue: lane holds rows 4 (l / 16) + i, column l % 16 of each tile
+    if (kGateUp) {
+        // h = silu(gate) * up goes through LDS (the A ring is idle now) in
+        // two halves of 64 rows, then is split one 32-element block per
+        // lane: the wave's 64 h columns hc0 .. hc0 + 63 are MX blocks gb0,
+        // gb0 + 1 of down step hc0 / 128
+        constexpr int kHs = 68;                          // floats per staged row
+        float *hs = reinterpret_cast<float *>(lds) + wid * 64 * kHs;
+        const int hc0 = ts.nb * 256 + 64 * wid;
+        const uint32_t hq_row = (uint32_t)(f >> 7) * kStepBytes;
+        uint8_t *hq_step = hq + (size_t)(hc0 >> 7) * kStepBytes;
+        const int gb0 = (hc0 & 127) >> 5;
+        __syncthreads();                                 // every wave is done with the ring
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+        for (int pass = 0; pass < 2; ++pass) {
+            const int left = ts.ne - ts.m0 - 64 * pass;   // rows of the tile from this pass on
+            if (left <= 0) break;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = ts.m0 + mt * 16 + 4 * g + i;
-            if (r < ts.ne) {
-                if (kGateUp) {
-                    float *hrow = h + (size_t)(ts.row0 + r) * f + ts.nb * 256 + 64 * wid;
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) {
-                        const float gv = acc[mt][nt][i], uv = acc[mt][nt + 4][i];
-                        hrow[16 * nt + r16] = gv / (1.0f + expf(-gv)) * uv;
+                        const float gv = acc[4 * pass + m][nt][i], uv = acc[4 * pass + m][nt + 4][i];
+                        hs[(16 * m + 4 * g + i) * kHs + 16 * nt + r16] = gv / (1.0f + expf(-gv)) * uv;
                     }
-                } else {
+            __syncthreads();
+            // buffer stores drop offsets past the pass's live rows
+            const uint32_t live_bytes = (uint32_t)min(left, 64) * hq_row;
+            const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
+                hq_step + (size_t)(ts.row0 + ts.m0 + 64 * pass) * hq_row, 0, (int)live_bytes,
+                0x00020000);
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+                if (it == 1 && left <= 32) break;
+                const int item = 64 * it + lane, rl = item >> 1, blk = gb0 + (item & 1);
+                float v[32];
+                const float *src = hs + rl * kHs + 32 * (item & 1);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const f32x4_t w = *reinterpret_cast<const f32x4_t *>(src + 4 * c);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[4 * c + q] = w[q];
+                }
+                const SplitBlock sb = split_block32(v);
+                u32x4_t w[3];
+                split_words(sb, w);
+                const uint32_t o = (uint32_t)rl * hq_row;
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    __builtin_amdgcn_raw_buffer_store_b128(w[c], out, o + 48u * blk + 16u * c, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sb.scales, out, o + 192u + 2u * blk,
+                                                      0, 0);
+            }
+            __syncthreads();
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ts.m0 + mt * 16 + 4 * g + i;
+                if (r < ts.ne) {
                     uint16_t *orow = rows_out + (size_t)(ts.row0 + r) * d + ts.nb * 512 + 128 * wid;
 #pragma unroll
                     for (int nt = 0; nt < 8; ++nt) orow[16 * nt + r16] = f32_to_bf16_rne(acc[mt][nt][i]);
                 }
             }
-        }
+    }
 }
 
 size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -656,23 +732,22 @@ size_t mfma_ws_bytes(int T, int d, int E, int k, int f) {
 }
 
 hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, hipStream_t st) {
-    const long long items = (long long)rows * (K / 128);
-    if (items <= 0) return hipSuccess;
-    mx_split_e2m3_kernel<uint16_t><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(in, rows, K, q);
+    const uint32_t items = (uint32_t)rows * (uint32_t)(K / 32);
+    if (items == 0) return hipSuccess;
+    mx_split_e2m3_kernel<uint16_t><<<(items + 255) / 256, 256, 0, st>>>(in, items, K, q);
     return hipGetLastError();
 }
 
 hipError_t launch_mx_split_f32(const float *in, int rows, int K, uint8_t *q, hipStream_t st) {
-    const long long items = (long long)rows * (K / 128);
-    if (items <= 0) return hipSuccess;
-    mx_split_e2m3_kernel<float><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(in, rows, K, q);
+    const uint32_t items = (uint32_t)rows * (uint32_t)(K / 32);
+    if (items == 0) return hipSuccess;
+    mx_split_e2m3_kernel<float><<<(items + 255) / 256, 256, 0, st>>>(in, items, K, q);
     return hipGetLastError();
 }
 
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
-                           const int32_t *sorted_rows, const int32_t *plan, float *h,
-                           uint16_t *rows_out, void *ws, int T, int d, int E, int k, int f,
-                           hipStream_t s) {
+                           const int32_t *sorted_rows, const int32_t *plan, uint16_t *rows_out,
+                           void *ws, int T, int d, int E, int k, int f, hipStream_t s) {
     hipError_t e = set_lds_attrs();
     if (e != hipSuccess) return e;
     const size_t rows = (size_t)T * k;
@@ -696,14 +771,9 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
         DiagScope t("gate_up_mfma", s);
         const long long blocks = 8 * ((mt_max * (f / 256) + 7) / 8);
         ffn_mfma_kernel<true><<<(unsigned)blocks, 256, kLdsBytes, s>>>(
-            xq, w, offsets, sorted_rows, plan, tiles, h, nullptr, T, d, E, k, f);
+            xq, w, offsets, sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    {
-        DiagScope t("mx_split_h", s);
-        e = launch_mx_split_f32(h, (int)rows, f, hq, s);
-    }
-    if (e != hipSuccess) return e;
     {
         DiagScope t("down_mfma", s);
         const long long blocks = 8 * ((mt_max * (d / 512) + 7) / 8);

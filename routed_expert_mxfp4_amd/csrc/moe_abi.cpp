@@ -74,9 +74,12 @@ FfnWs ffn_ws(const moe_dims &D) {
     FfnWs w;
     w.plan = 0;
     w.h = al256((size_t)(D.E + 1) * 4);
-    w.mfma = w.h + al256((size_t)D.T * D.k * D.f * 4);
-    w.total = w.mfma;
-    if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) w.total += al256(moe::mfma_ws_bytes(D.T, D.d, D.E, D.k, D.f));
+    w.mfma = w.h;
+    // the fp32 h of the GEMV path; the MFMA path keeps h split in its own ws
+    if (moe::mfma_path_ok(D.T, D.d, D.k, D.f))
+        w.total = w.mfma + al256(moe::mfma_ws_bytes(D.T, D.d, D.E, D.k, D.f));
+    else
+        w.total = w.h + al256((size_t)D.T * D.k * D.f * 4);
     return w;
 }
 
@@ -268,7 +271,7 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x,
         if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
             if (e == hipSuccess) {
                 DiagScope t("mfma_ffn", s);
-                e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, h, rows_out,
+                e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
                                          base + L.mfma, D.T, D.d, D.E, D.k, D.f, s);
             }
             return device_status(e);
@@ -372,7 +375,7 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
         if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
             if (e == hipSuccess) {
                 DiagScope t("mfma_ffn", s);
-                e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, h, rows_out,
+                e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
                                          base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f, s);
             }
             if (e == hipSuccess) {
@@ -410,7 +413,8 @@ int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint
                            void *hip_stream) {
     try {
         if (!in || !out || rows < 0 || K <= 0 || K % 128 != 0) return -1;
-        if (((uintptr_t)in & 15u) != 0) return -1;
+        if ((((uintptr_t)in | (uintptr_t)out) & 15u) != 0) return -1;
+        if ((double)rows * (K / 128) * 208.0 >= 4294967296.0) return -1;
         hipStream_t st = static_cast<hipStream_t>(hip_stream);
         hipError_t e = in_is_bf16
                            ? moe::launch_mx_split_bf16(static_cast<const uint16_t *>(in), rows, K, out, st)

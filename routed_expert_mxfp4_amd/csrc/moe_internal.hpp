@@ -195,13 +195,13 @@ hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
                                const float *topk_w, const int32_t *row_pos, uint16_t *y,
                                int T, int d, int E, int k, int f, hipStream_t s);
 // Prefill expert FFN on scaled MFMA (x and h as two-term MX E2M3, weights
-// as stored).  Needs d % 512 == 0, f % 256 == 0; ws of mfma_ws_bytes.
+// as stored; the gate/up pass writes h already split).  Needs d % 512 == 0,
+// f % 256 == 0; ws of mfma_ws_bytes.
 bool mfma_path_ok(int T, int d, int k, int f);
 size_t mfma_ws_bytes(int T, int d, int E, int k, int f);
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
-                           const int32_t *sorted_rows, const int32_t *plan, float *h,
-                           uint16_t *rows_out, void *ws, int T, int d, int E, int k, int f,
-                           hipStream_t s);
+                           const int32_t *sorted_rows, const int32_t *plan, uint16_t *rows_out,
+                           void *ws, int T, int d, int E, int k, int f, hipStream_t s);
 // rows x K (K % 128 == 0) -> two-term MX E2M3 split rows, 208 bytes per row
 // and 128-element step (codes of both terms, then their E8M0 scales).
 size_t mx_split_bytes(int rows, int K);
