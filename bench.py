@@ -38,7 +38,7 @@ DEFAULT_STEPS = {"tiny": 1000, "decode": 1000, "batched-decode": 200, "zipf-pref
                  "long-prefill": 5}
 KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm",
            "router_refine", "permute", "topk_permute", "gemv_gate_up",
-           "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "mx_split_h", "down_mfma",
+           "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "down_mfma",
            "combine")
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 / MXFP6, published
 MFMA_MIN_T = 128                # the library's scaled-MFMA path starts here
@@ -57,7 +57,25 @@ def parse():
                     help="tokens of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel timing passes after the timed region")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain fp32 device copy (torch.neg) of MIB MiB five "
+                         "times, the reference for scaling HBM traffic counters, and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """Reads and writes exactly mib MiB per launch: what a traffic counter
+    reads for it gives the counter's scale."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
+                      "launches": 5}))
 
 
 def cpu_model():
@@ -151,6 +169,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy > 0:
+        calibrate_copy(args.calibrate_copy)
+        return
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[WORKLOADS[args.workload]]
     if args.steps is None:
@@ -160,7 +181,7 @@ def main():
     # the kernel that dominates the step: the expert-weight stream of the
     # gate/up GEMV (HBM-bound) for decode-sized T, the scaled-MFMA gate/up
     # GEMM (matrix-core-bound) for prefill-sized T
-    mfma = cfg.T >= MFMA_MIN_T and cfg.d % 128 == 0 and cfg.f % 128 == 0
+    mfma = cfg.T >= MFMA_MIN_T and cfg.d % 512 == 0 and cfg.f % 256 == 0
     dominant = "gate_up_mfma" if mfma else "gemv_gate_up"
     L = moe.lib()
 
@@ -206,6 +227,7 @@ def main():
     moe.diag_time_kernel(None, 0)
     elapsed = t1 - t0
 
+
     # ---- per-kernel breakdown (separate passes, outside the timed region) -------
     breakdown = {}
     if not args.no_breakdown:
@@ -240,9 +262,12 @@ def main():
         # gate/up: every routed row times the [2f x d] gate/up matrix
         flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
         achieved = flops_per_launch / avg_launch_s / 1e12
+        src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_mfma.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         roofline = {"bound": "mfma", "kernel": dominant, "achieved": achieved,
                     "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / MXFP4_PEAK_TFLOPS, "traffic": None,
+                    "frac": achieved / MXFP4_PEAK_TFLOPS,
+                    "traffic": traffic_from_profiles(dominant, args.workload, sha),
                     "algorithmic_flops_per_launch": flops_per_launch,
                     "mfma_passes_per_product": 2,
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}

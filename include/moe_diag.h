@@ -41,12 +41,16 @@ int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint
 
 /* Start timing every launch of `kernel` (NULL or "" stops timing).  Creates
  * `capacity` event pairs up front (the only allocation); launches beyond
- * that many are not timed.  Drops any earlier records.  Returns 0, or -1 if
- * event creation failed or capacity < 0. */
+ * that many are not timed.  A single-kernel name is timed by events that
+ * its launch itself records (hipExtLaunchKernel) and that skip the
+ * system-scope fence; names covering several launches (permute, plan,
+ * mfma_ffn, router_norms) by events recorded around them.  Drops any
+ * earlier records.  Returns 0, or -1 if event creation failed or
+ * capacity < 0. */
 int moe_diag_time_kernel(const char *kernel, int capacity);
 
 /* Sum of the elapsed times (ms) of the recorded launches and their count.
- * Call only after the streams they ran on have been synchronised.  Clears
+ * Call only after the device has been synchronised.  Clears
  * the records (timing stays on).  Returns 0, or -1 on a HIP error. */
 int moe_diag_kernel_time(double *total_ms, long long *launches);
 

@@ -60,7 +60,7 @@ hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
                           hipStream_t s) {
     if (T <= 0) return hipSuccess;
     dim3 grid(((d >> 3) + 255) / 256, T);
-    combine_kernel<<<grid, 256, 0, s>>>(rows_out, row_pos, topk_w, y, T, d, k);
+    (void)timed_launch("combine", combine_kernel, dim3(grid), dim3(256), 0, s, rows_out, row_pos, topk_w, y, T, d, k);
     return hipGetLastError();
 }
 

@@ -541,7 +541,7 @@ hipError_t launch_regx(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                        const int32_t *sorted_rows, const int32_t *plan, float *h, int T, int d,
                        int E, int k, int f, int amax, hipStream_t s) {
     dim3 grid(f / kRxPairs, amax);
-    gate_up_regx_kernel<NBL><<<grid, 256, (size_t)d * 2 + 16, s>>>(x, w, offsets, sorted_rows, plan, h,
+    (void)timed_launch("gemv_gate_up", gate_up_regx_kernel<NBL>, dim3(grid), dim3(256), (size_t)d * 2 + 16, s, x, w, offsets, sorted_rows, plan, h,
                                                               T, d, E, k, f);
     return hipGetLastError();
 }
@@ -559,7 +559,7 @@ hipError_t launch_gemv_gate_up(const uint16_t *x, ExpertArgs w, const int32_t *o
     }
     const int rpp = max(1, min(kRowsMax, 32768 / d));   // <= 64 KB of LDS
     dim3 grid(f / kGuPairs, amax);
-    gemv_gate_up_kernel<<<grid, 256, (size_t)rpp * d * 2, s>>>(x, w, offsets, sorted_rows, plan,
+    (void)timed_launch("gemv_gate_up", gemv_gate_up_kernel, dim3(grid), dim3(256), (size_t)rpp * d * 2, s, x, w, offsets, sorted_rows, plan,
                                                                h, T, d, E, k, f, rpp);
     return hipGetLastError();
 }
@@ -569,7 +569,7 @@ hipError_t launch_down_rows(const float *h, ExpertArgs w, const int32_t *offsets
                             const int32_t *plan, uint16_t *rows_out, int T, int d, int E,
                             int k, int f, int amax, hipStream_t s) {
     dim3 grid(d / 64, amax);
-    down_rows_kernel<NBLD><<<grid, 256, 0, s>>>(h, w, offsets, plan, rows_out, T, d, E, k, f);
+    (void)timed_launch("gemv_down", down_rows_kernel<NBLD>, dim3(grid), dim3(256), 0, s, h, w, offsets, plan, rows_out, T, d, E, k, f);
     return hipGetLastError();
 }
 
@@ -585,7 +585,7 @@ hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets
     }
     const int rpp = max(1, min(kRowsMax, 16384 / f));   // <= 64 KB of LDS
     dim3 grid(d / kDnRows, amax);
-    gemv_down_kernel<<<grid, 256, (size_t)rpp * f * 4, s>>>(h, w, offsets, plan, rows_out, T, d,
+    (void)timed_launch("gemv_down", gemv_down_kernel, dim3(grid), dim3(256), (size_t)rpp * f * 4, s, h, w, offsets, plan, rows_out, T, d,
                                                             E, k, f, rpp);
     return hipGetLastError();
 }
@@ -597,11 +597,11 @@ hipError_t launch_dc_split(const float *h, ExpertArgs w, const int32_t *ids,
     // 28 output rows per block: 7168 / 28 = 256 blocks, one per CU
     if (d % 28 == 0) {
         dim3 grid(d / 28, T);
-        down_combine_split_kernel<NBLD, 28, 4><<<grid, 1024, 0, s>>>(h, w, ids, topk_w, row_pos, y,
+        (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, 28, 4>, dim3(grid), dim3(1024), 0, s, h, w, ids, topk_w, row_pos, y,
                                                                       T, d, E, k, f);
     } else {
         dim3 grid(d / 32, T);
-        down_combine_split_kernel<NBLD, 32, 4><<<grid, 1024, 0, s>>>(h, w, ids, topk_w, row_pos, y,
+        (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, 32, 4>, dim3(grid), dim3(1024), 0, s, h, w, ids, topk_w, row_pos, y,
                                                                       T, d, E, k, f);
     }
     return hipGetLastError();
@@ -617,7 +617,7 @@ hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
         return launch_dc_split<2>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
     }
     dim3 grid(d / 16, T);
-    down_combine_kernel<<<grid, 64, 0, s>>>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f);
+    (void)timed_launch("down_combine", down_combine_kernel, dim3(grid), dim3(64), 0, s, h, w, ids, topk_w, row_pos, y, T, d, E, k, f);
     return hipGetLastError();
 }
 

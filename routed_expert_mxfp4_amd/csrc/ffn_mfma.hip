@@ -734,7 +734,7 @@ size_t mfma_ws_bytes(int T, int d, int E, int k, int f) {
 hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, hipStream_t st) {
     const uint32_t items = (uint32_t)rows * (uint32_t)(K / 32);
     if (items == 0) return hipSuccess;
-    mx_split_e2m3_kernel<uint16_t><<<(items + 255) / 256, 256, 0, st>>>(in, items, K, q);
+    (void)timed_launch("mx_split_x", mx_split_e2m3_kernel<uint16_t>, dim3((items + 255) / 256), dim3(256), 0, st, in, items, K, q);
     return hipGetLastError();
 }
 
@@ -759,7 +759,6 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
     int32_t *tiles = reinterpret_cast<int32_t *>(p);
 
     {
-        DiagScope t("mx_split_x", s);
         e = launch_mx_split_bf16(x, T, d, xq, s);
     }
     if (e != hipSuccess) return e;
@@ -768,17 +767,13 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
     // upper bound on the m-tiles: one partial tile per expert plus full tiles
     const long long mt_max = min(E, (int)rows) + (long long)((rows + kBM - 1) / kBM);
     {
-        DiagScope t("gate_up_mfma", s);
         const long long blocks = 8 * ((mt_max * (f / 256) + 7) / 8);
-        ffn_mfma_kernel<true><<<(unsigned)blocks, 256, kLdsBytes, s>>>(
-            xq, w, offsets, sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f);
+        (void)timed_launch("gate_up_mfma", ffn_mfma_kernel<true>, dim3((unsigned)blocks), dim3(256), kLdsBytes, s, xq, w, offsets, sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
-        DiagScope t("down_mfma", s);
         const long long blocks = 8 * ((mt_max * (d / 512) + 7) / 8);
-        ffn_mfma_kernel<false><<<(unsigned)blocks, 256, kLdsBytes, s>>>(
-            hq, w, offsets, sorted_rows, plan, tiles, nullptr, rows_out, T, d, E, k, f);
+        (void)timed_launch("down_mfma", ffn_mfma_kernel<false>, dim3((unsigned)blocks), dim3(256), kLdsBytes, s, hq, w, offsets, sorted_rows, plan, tiles, nullptr, rows_out, T, d, E, k, f);
     }
     return hipGetLastError();
 }

@@ -141,6 +141,15 @@ DiagScope::DiagScope(const char *kernel, hipStream_t s) : s_(s) {
 DiagScope::~DiagScope() {
     if (stop_) (void)hipEventRecord(stop_, s_);
 }
+void diag_launch_events(const char *kernel, hipEvent_t *start, hipEvent_t *stop) {
+    *start = *stop = nullptr;
+    if (!g_diag.active.load(std::memory_order_acquire)) return;
+    std::lock_guard<std::mutex> lk(g_diag.mu);
+    if (g_diag.name != kernel || 2 * (g_diag.used + 1) > (int)g_diag.ev.size()) return;
+    *start = g_diag.ev[2 * g_diag.used];
+    *stop = g_diag.ev[2 * g_diag.used + 1];
+    ++g_diag.used;
+}
 }  // namespace moe
 
 using moe::DiagScope;
@@ -208,11 +217,9 @@ moe_status moe_route(const moe_dims *dims, const uint16_t *x, const uint16_t *ro
             logits = reinterpret_cast<float *>(static_cast<char *>(ws) + route_ws(D).logits);
         }
         {
-            DiagScope t("router_logits", s);
             e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
         }
         if (e == hipSuccess) {
-            DiagScope t("topk_softmax", s);
             e = moe::launch_topk_softmax(logits, topk_ids, topk_w, D.T, D.E, D.k, s);
         }
         return device_status(e);
@@ -277,12 +284,10 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x,
             return device_status(e);
         }
         if (e == hipSuccess) {
-            DiagScope t("gemv_gate_up", s);
             e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
                                          D.f, s);
         }
         if (e == hipSuccess) {
-            DiagScope t("gemv_down", s);
             e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f, s);
         }
         return device_status(e);
@@ -299,7 +304,6 @@ moe_status moe_combine(const moe_dims *dims, const uint16_t *rows_out, const int
         if (!rows_out || !row_pos || !topk_w || !y) return MOE_ERR_NULL;
         if (!aligned16(rows_out) || !aligned16(y)) return MOE_ERR_ALIGN;
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
-        DiagScope t("combine", s);
         return device_status(moe::launch_combine(rows_out, row_pos, topk_w, y, D.T, D.d, D.k, s));
     });
 }
@@ -346,7 +350,6 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
                                            reinterpret_cast<float *>(base + L.route + RW.nw), ids,
                                            tw, D.T, D.d, D.E, D.k, s);
         } else {
-            DiagScope t("router_logits", s);
             e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
         }
         if (filtered) {
@@ -357,13 +360,11 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
             }
         } else if (moe::topk_permute_fusable(D.T, D.E, D.k)) {
             if (e == hipSuccess) {
-                DiagScope t("topk_permute", s);
                 e = moe::launch_topk_permute_small(logits, ids, tw, counts, offsets, sorted_rows,
                                                    row_pos, plan, D.T, D.E, D.k, s);
             }
         } else {
             if (e == hipSuccess) {
-                DiagScope t("topk_softmax", s);
                 e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
             }
             if (e == hipSuccess) {
@@ -379,29 +380,24 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
                                          base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f, s);
             }
             if (e == hipSuccess) {
-                DiagScope t("combine", s);
                 e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
             }
             return device_status(e);
         }
         if (e == hipSuccess) {
-            DiagScope t("gemv_gate_up", s);
             e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
                                          D.f, s);
         }
         if (D.T <= kFuseMaxT) {
             if (e == hipSuccess) {
-                DiagScope t("down_combine", s);
                 e = moe::launch_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E, D.k, D.f, s);
             }
         } else {
             if (e == hipSuccess) {
-                DiagScope t("gemv_down", s);
                 e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f,
                                           s);
             }
             if (e == hipSuccess) {
-                DiagScope t("combine", s);
                 e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
             }
         }
@@ -434,7 +430,10 @@ int moe_diag_time_kernel(const char *kernel, int capacity) {
         g_diag.name = kernel ? kernel : "";
         while ((int)g_diag.ev.size() < 2 * capacity) {
             hipEvent_t ev;
-            if (hipEventCreate(&ev) != hipSuccess) return -1;
+            // timing only (read after the caller synchronises the device):
+            // no system-scope fence, whose cache writeback and invalidate
+            // would add to every timed launch
+            if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return -1;
             g_diag.ev.push_back(ev);
         }
         g_diag.active.store(!g_diag.name.empty() && capacity > 0, std::memory_order_release);

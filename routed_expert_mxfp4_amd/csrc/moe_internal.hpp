@@ -6,6 +6,7 @@
 // work on the given stream and return the hipError_t of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -151,6 +152,22 @@ class DiagScope {
     hipStream_t s_;
     hipEvent_t stop_ = nullptr;
 };
+
+// The same timing for one launch, taken at the kernel itself: when `kernel`
+// is being timed, the next start/stop event pair, which the launch records
+// at the kernel's start and end; both null otherwise.
+void diag_launch_events(const char *kernel, hipEvent_t *start, hipEvent_t *stop);
+
+// Launches `fn` on stream s, timed as `kernel` when that name is being timed
+// (the launch records the events itself, so no dispatch gap is counted).
+template <typename F, typename... Args>
+inline hipError_t timed_launch(const char *kernel, F fn, dim3 grid, dim3 block, size_t shmem,
+                               hipStream_t s, Args... args) {
+    hipEvent_t a = nullptr, b = nullptr;
+    diag_launch_events(kernel, &a, &b);
+    hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)shmem, s, a, b, 0u, args...);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // Launchers (defined in the .hip files).  All pointers are device pointers.

@@ -367,24 +367,24 @@ hipError_t launch_topk_permute_small(const float *logits, int32_t *ids, float *t
     const int pl = (E + 63) / 64;
     if (T * k <= kTinyRows) {
         if (pl <= 4)
-            topk_permute_tiny_kernel<4><<<1, 1024, 0, s>>>(logits, ids, tw, counts, offsets,
+            (void)timed_launch("topk_permute", topk_permute_tiny_kernel<4>, dim3(1), dim3(1024), 0, s, logits, ids, tw, counts, offsets,
                                                           sorted_rows, row_pos, plan, T, E, k);
         else if (pl <= 8)
-            topk_permute_tiny_kernel<8><<<1, 1024, 0, s>>>(logits, ids, tw, counts, offsets,
+            (void)timed_launch("topk_permute", topk_permute_tiny_kernel<8>, dim3(1), dim3(1024), 0, s, logits, ids, tw, counts, offsets,
                                                           sorted_rows, row_pos, plan, T, E, k);
         else
-            topk_permute_tiny_kernel<16><<<1, 1024, 0, s>>>(logits, ids, tw, counts, offsets,
+            (void)timed_launch("topk_permute", topk_permute_tiny_kernel<16>, dim3(1), dim3(1024), 0, s, logits, ids, tw, counts, offsets,
                                                            sorted_rows, row_pos, plan, T, E, k);
         return hipGetLastError();
     }
     if (pl <= 4)
-        topk_permute_small_kernel<4><<<1, 1024, lds, s>>>(logits, ids, tw, counts, offsets,
+        (void)timed_launch("topk_permute", topk_permute_small_kernel<4>, dim3(1), dim3(1024), lds, s, logits, ids, tw, counts, offsets,
                                                           sorted_rows, row_pos, plan, T, E, k);
     else if (pl <= 8)
-        topk_permute_small_kernel<8><<<1, 1024, lds, s>>>(logits, ids, tw, counts, offsets,
+        (void)timed_launch("topk_permute", topk_permute_small_kernel<8>, dim3(1), dim3(1024), lds, s, logits, ids, tw, counts, offsets,
                                                           sorted_rows, row_pos, plan, T, E, k);
     else
-        topk_permute_small_kernel<16><<<1, 1024, lds, s>>>(logits, ids, tw, counts, offsets,
+        (void)timed_launch("topk_permute", topk_permute_small_kernel<16>, dim3(1), dim3(1024), lds, s, logits, ids, tw, counts, offsets,
                                                            sorted_rows, row_pos, plan, T, E, k);
     return hipGetLastError();
 }

@@ -120,13 +120,13 @@ hipError_t launch_logits_tile(const uint16_t *x, const uint16_t *wr, const float
     dim3 grid((E + TE - 1) / TE, (T + TT - 1) / TT);
     const int P = d / 64;
     if (P % 8 == 0)
-        router_logits_kernel<TT, TE, 8><<<grid, 64, 0, s>>>(x, wr, bias, logits, T, d, E);
+        (void)timed_launch("router_logits", router_logits_kernel<TT, TE, 8>, dim3(grid), dim3(64), 0, s, x, wr, bias, logits, T, d, E);
     else if (P % 4 == 0)
-        router_logits_kernel<TT, TE, 4><<<grid, 64, 0, s>>>(x, wr, bias, logits, T, d, E);
+        (void)timed_launch("router_logits", router_logits_kernel<TT, TE, 4>, dim3(grid), dim3(64), 0, s, x, wr, bias, logits, T, d, E);
     else if (P % 2 == 0)
-        router_logits_kernel<TT, TE, 2><<<grid, 64, 0, s>>>(x, wr, bias, logits, T, d, E);
+        (void)timed_launch("router_logits", router_logits_kernel<TT, TE, 2>, dim3(grid), dim3(64), 0, s, x, wr, bias, logits, T, d, E);
     else
-        router_logits_kernel<TT, TE, 1><<<grid, 64, 0, s>>>(x, wr, bias, logits, T, d, E);
+        (void)timed_launch("router_logits", router_logits_kernel<TT, TE, 1>, dim3(grid), dim3(64), 0, s, x, wr, bias, logits, T, d, E);
     return hipGetLastError();
 }
 
@@ -235,7 +235,7 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const flo
     constexpr int kRpb = kRouterRowsPerBlock;
     const size_t lds = (size_t)kRpb * 64 * ((P / 8) + 1) * 16 + 16;   // + spare slot
     if (T == 1 && P % 8 == 0 && d <= 8192 && lds <= 65536) {
-        router_small_kernel<kRpb><<<(E + kRpb - 1) / kRpb, 64 * kRpb, lds, s>>>(x, wr, bias, logits,
+        (void)timed_launch("router_logits", router_small_kernel<kRpb>, dim3((E + kRpb - 1) / kRpb), dim3(64 * kRpb), lds, s, x, wr, bias, logits,
                                                                                T, d, E);
         return hipGetLastError();
     }
@@ -249,11 +249,11 @@ hipError_t launch_topk_softmax(const float *logits, int32_t *ids, float *w, int 
     dim3 grid((T + 3) / 4);
     const int pl = (E + 63) / 64;
     if (pl <= 4)
-        topk_softmax_kernel<4><<<grid, 256, 0, s>>>(logits, ids, w, T, E, k);
+        (void)timed_launch("topk_softmax", topk_softmax_kernel<4>, dim3(grid), dim3(256), 0, s, logits, ids, w, T, E, k);
     else if (pl <= 8)
-        topk_softmax_kernel<8><<<grid, 256, 0, s>>>(logits, ids, w, T, E, k);
+        (void)timed_launch("topk_softmax", topk_softmax_kernel<8>, dim3(grid), dim3(256), 0, s, logits, ids, w, T, E, k);
     else
-        topk_softmax_kernel<16><<<grid, 256, 0, s>>>(logits, ids, w, T, E, k);
+        (void)timed_launch("topk_softmax", topk_softmax_kernel<16>, dim3(grid), dim3(256), 0, s, logits, ids, w, T, E, k);
     return hipGetLastError();
 }
 

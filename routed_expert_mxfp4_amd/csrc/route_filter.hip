@@ -400,9 +400,8 @@ hipError_t launch_route_filtered(const uint16_t *x, const uint16_t *wr, const fl
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
-        DiagScope ds("router_filter_gemm", s);
         dim3 grid((E + kFE - 1) / kFE, (T + kFT - 1) / kFT);
-        filter_gemm_kernel<<<grid, 256, kFLds, s>>>(x, wr, zt, T, d, E);
+        (void)timed_launch("router_filter_gemm", filter_gemm_kernel, dim3(grid), dim3(256), kFLds, s, x, wr, zt, T, d, E);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const double c = 2.0 * (double)(d + 64) / 8388608.0;
@@ -410,19 +409,18 @@ hipError_t launch_route_filtered(const uint16_t *x, const uint16_t *wr, const fl
     const size_t lds = (size_t)4 * E * sizeof(float);
     const int pl = (E + 63) / 64;
     {
-        DiagScope ds("router_refine", s);
         const unsigned grid = (unsigned)((T + 3) / 4);
         const int P = d / 64;
         // the register-resident chunk covers d = 512 * NQ; other d take the
         // loop that reads both chunks from memory
         if (pl <= 16 && P == 112)
-            select_refine_kernel<16, 14><<<grid, 256, lds, s>>>(zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+            (void)timed_launch("router_refine", select_refine_kernel<16, 14>, dim3(grid), dim3(256), lds, s, zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
         else if (pl <= 4)
-            select_refine_kernel<4, 0><<<grid, 256, lds, s>>>(zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+            (void)timed_launch("router_refine", select_refine_kernel<4, 0>, dim3(grid), dim3(256), lds, s, zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
         else if (pl <= 8)
-            select_refine_kernel<8, 0><<<grid, 256, lds, s>>>(zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+            (void)timed_launch("router_refine", select_refine_kernel<8, 0>, dim3(grid), dim3(256), lds, s, zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
         else
-            select_refine_kernel<16, 0><<<grid, 256, lds, s>>>(zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+            (void)timed_launch("router_refine", select_refine_kernel<16, 0>, dim3(grid), dim3(256), lds, s, zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
     }
     return hipGetLastError();
 }
