@@ -42,7 +42,7 @@
  *   - T == 0 is valid: the call returns MOE_OK and launches nothing.
  *   - Results are deterministic: identical inputs give identical bits.
  *   - Limits: d % 64 == 0, f % 32 == 0, 1 <= k <= min(E, 32), E <= 1024,
- *     T * k < 2^31, d <= 65536, f <= 16384.  Pointers to x, router_w, the
+ *     T * k < 2^31, d <= 32768, f <= 16384.  Pointers to x, router_w, the
  *     expert tensors, rows_out, y and the workspace must be 16-byte aligned.
  *   - `ws` is scratch device memory of at least moe_workspace_bytes(dims,
  *     entry) bytes (may be NULL when that is 0).  It must not be shared by
