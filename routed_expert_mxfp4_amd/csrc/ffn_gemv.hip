@@ -14,6 +14,7 @@
 // Down: o[p][m] = h[p] . Wd[m] -> bf16 rows_out (expert-major), or fused
 // with the weighted combine per token for small T.
 #include "moe_internal.hpp"
+#include "select_dev.hpp"
 
 namespace moe {
 namespace {
@@ -238,6 +239,8 @@ __global__ __launch_bounds__(64) void down_combine_kernel(
 // a row issued before any of it is used, DPP lane reductions.
 // ---------------------------------------------------------------------------
 constexpr int kRxPairs = 32;         // gate/up pairs per block (8 per wave)
+constexpr int kTokPairs = 48;        // the same for the one-token kernel: 512 blocks
+                                     // at f = 1536, k = 16 (one round of two per CU)
 constexpr int kStageX = 4;           // x staging: d <= 4 * 256 * 8 = 8192
 
 // Gate/up for decode-sized groups, software-pipelined: lane l owns the MX
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
 #pragma unroll
             for (int j = 0; j < kStageX; ++j)
                 tmp[j] = xrow[min((int)threadIdx.x + 256 * j, nvec - 1)];
-            loads_done(tmp);                        // all loads before any store      // all loads before any store
+            loads_done(tmp);                        // all loads before any store
 #pragma unroll
             for (int j = 0; j < kStageX; ++j) {     // spare slot: no branch per store
                 const int i = (int)threadIdx.x + 256 * j;
@@ -349,6 +352,98 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
             if (lane == 0) hrow[n_base + 4 * (q + 1)] = vb;
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+}
+
+// One token (T = 1): the top-k and the grouping happen inside the gate/up
+// pass.  Every block selects the token's experts itself from the logits row
+// (E floats, read by one wave) while x is staged; the k selected experts are
+// distinct, so in ascending expert order the a-th of them is the one whose h
+// row is a, routed from top-k slot sorted_rows[a] -- exactly the grouping of
+// the permute step.  Block (0, 0) writes that grouping (ids, weights,
+// counts, offsets, sorted_rows, row_pos, plan) for the later kernels.
+template <int NBL>
+__global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
+    const float *__restrict__ logits, const uint16_t *__restrict__ x, ExpertArgs W,
+    int32_t *__restrict__ ids, float *__restrict__ tw, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
+    int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, float *__restrict__ h, int d,
+    int E, int k, int f) {
+    extern __shared__ uint4 xs[];                 // the token row, d/8 x 16 B, + 1 spare
+    __shared__ __align__(16) uint32_t tsc[kTopkScratch];
+    __shared__ int sel[32];                       // selected experts, ascending
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int nvec = d >> 3;
+    const bool first = blockIdx.x == 0 && blockIdx.y == 0;
+    {
+        const uint4 *xrow = reinterpret_cast<const uint4 *>(x);
+        uint4 tmp[kStageX];
+#pragma unroll
+        for (int j = 0; j < kStageX; ++j)
+            tmp[j] = xrow[min((int)threadIdx.x + 256 * j, nvec - 1)];
+        loads_done(tmp);                            // all loads before any store
+#pragma unroll
+        for (int j = 0; j < kStageX; ++j) {         // spare slot: no branch per store
+            const int i = (int)threadIdx.x + 256 * j;
+            xs[i < nvec ? i : nvec] = tmp[j];
+        }
+    }
+    if (wid == 0) {
+        int e;
+        float wt;
+        wave_topk_softmax<16>(logits, E, k, tsc, &e, &wt);
+        int rank = 0;                               // place among the selected
+        for (int i = 0; i < k; ++i) rank += __shfl(e, i) < e ? 1 : 0;
+        if (lane < k) {
+            sel[rank] = e;
+            if (first) {
+                ids[lane] = e;
+                tw[lane] = wt;
+                sorted_rows[rank] = lane;
+                row_pos[lane] = rank;
+                plan[1 + rank] = e;
+            }
+        }
+        if (first && lane == 0) plan[0] = k;
+    }
+    __syncthreads();
+    if (first) {
+        for (int c = threadIdx.x; c <= E; c += 256) {
+            int below = 0, hit = 0;
+            for (int i = 0; i < k; ++i) {
+                below += sel[i] < c ? 1 : 0;
+                hit += sel[i] == c ? 1 : 0;
+            }
+            offsets[c] = below;
+            if (c < E) counts[c] = hit;
+        }
+    }
+    const int a = blockIdx.y;
+    const int e = sel[a];
+    if ((unsigned)e >= (unsigned)E) return;
+    const int nblk = d >> 5;
+    const uint32_t code_row = (uint32_t)d >> 1;
+    const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
+    const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
+    constexpr int kPerWave = kTokPairs / 4;        // pairs n_base + wid + 4 q
+    const int n_base = blockIdx.x * kTokPairs + wid;
+    float *hrow = h + (size_t)a * f;
+    PairBuf<NBL> A, B;
+    load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);
+#pragma unroll 1
+    for (int q = 0; q < kPerWave; q += 2) {
+        load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
+        __builtin_amdgcn_sched_barrier(0);
+        const float va = pair_h<NBL>(A, xs, lane, nblk);
+        if (lane == 0) hrow[n_base + 4 * q] = va;
+        __builtin_amdgcn_sched_barrier(0);
+        if (q + 2 < kPerWave)
+            load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
+        __builtin_amdgcn_sched_barrier(0);
+        const float vb = pair_h<NBL>(B, xs, lane, nblk);
+        if (lane == 0) hrow[n_base + 4 * (q + 1)] = vb;
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -588,6 +683,31 @@ hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets
     (void)timed_launch("gemv_down", gemv_down_kernel, dim3(grid), dim3(256), (size_t)rpp * f * 4, s, h, w, offsets, plan, rows_out, T, d,
                                                             E, k, f, rpp);
     return hipGetLastError();
+}
+
+bool gate_up_token_fusable(int T, int d, int E, int k, int f) {
+    const int nbl = (d / 32 + 63) / 64;
+    return T == 1 && k <= 32 && k <= E && E <= 1024 && f % kTokPairs == 0 && nbl <= 4 && d <= 8192;
+}
+
+hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertArgs w,
+                                int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
+                                int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, float *h,
+                                int d, int E, int k, int f, hipStream_t s) {
+    const int nbl = (d / 32 + 63) / 64;
+    const dim3 grid(f / kTokPairs, k);
+    const size_t lds = (size_t)d * 2 + 16;
+    if (nbl == 1)
+        return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<1>, grid, dim3(256), lds, s,
+                            logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, h,
+                            d, E, k, f);
+    if (nbl == 2)
+        return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<2>, grid, dim3(256), lds, s,
+                            logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, h,
+                            d, E, k, f);
+    return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<4>, grid, dim3(256), lds, s,
+                        logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, h, d,
+                        E, k, f);
 }
 
 template <int NBLD>

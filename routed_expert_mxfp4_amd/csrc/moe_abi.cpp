@@ -344,6 +344,9 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
 
         hipError_t e;
         const bool filtered = moe::route_filter_ok(D.T, D.d, D.E);
+        // one token: top-k and grouping run inside the gate/up pass
+        const bool token_fused =
+            !filtered && moe::gate_up_token_fusable(D.T, D.d, D.E, D.k, D.f);
         if (filtered) {
             e = moe::launch_route_filtered(x, router_w, router_bias, logits,
                                            reinterpret_cast<float *>(base + L.route + RW.nx),
@@ -358,6 +361,7 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
                 e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
                                         D.E, D.k, perm_ws, s);
             }
+        } else if (token_fused) {
         } else if (moe::topk_permute_fusable(D.T, D.E, D.k)) {
             if (e == hipSuccess) {
                 e = moe::launch_topk_permute_small(logits, ids, tw, counts, offsets, sorted_rows,
@@ -385,8 +389,11 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
             return device_status(e);
         }
         if (e == hipSuccess) {
-            e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
-                                         D.f, s);
+            e = token_fused ? moe::launch_gate_up_token(logits, x, W, ids, tw, counts, offsets,
+                                                        sorted_rows, row_pos, plan, h, D.d, D.E,
+                                                        D.k, D.f, s)
+                            : moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T,
+                                                       D.d, D.E, D.k, D.f, s);
         }
         if (D.T <= kFuseMaxT) {
             if (e == hipSuccess) {

@@ -205,6 +205,14 @@ struct ExpertArgs {
 hipError_t launch_gemv_gate_up(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                                const int32_t *sorted_rows, const int32_t *plan, float *h,
                                int T, int d, int E, int k, int f, hipStream_t s);
+// One token: top-k, softmax and grouping inside the gate/up GEMV (writes
+// ids, tw, counts, offsets, sorted_rows, row_pos and plan as the permute
+// step would).  Needs gate_up_token_fusable.
+bool gate_up_token_fusable(int T, int d, int E, int k, int f);
+hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertArgs w,
+                                int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
+                                int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, float *h,
+                                int d, int E, int k, int f, hipStream_t s);
 hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets,
                             const int32_t *plan, uint16_t *rows_out, int T, int d, int E,
                             int k, int f, hipStream_t s);

@@ -63,20 +63,58 @@ __device__ __forceinline__ float key_logit(uint32_t key) {
 }
 
 // LDS scratch of one wave for wave_topk_softmax (uint32 words, 16-byte
-// aligned).
-constexpr int kTopkScratch = 192;
+// aligned): candidate keys at 64.., their experts at 128.., spare write
+// targets at 192 and 193.
+constexpr int kTopkScratch = 196;
+
+// Sum of a double over lanes 0..31 (lanes past them are ignored): rotations
+// within rows of 16 lanes, then rows 0 and 1 through scalar registers.
+__device__ __forceinline__ double sum_lanes32_f64(double v) {
+#pragma unroll
+    for (int r = 8; r >= 1; r >>= 1) {
+        const unsigned long long u = __double_as_longlong(v);
+        int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+        if (r == 8) {
+            lo = __builtin_amdgcn_update_dpp(lo, lo, 0x128, 0xF, 0xF, false);
+            hi = __builtin_amdgcn_update_dpp(hi, hi, 0x128, 0xF, 0xF, false);
+        } else if (r == 4) {
+            lo = __builtin_amdgcn_update_dpp(lo, lo, 0x124, 0xF, 0xF, false);
+            hi = __builtin_amdgcn_update_dpp(hi, hi, 0x124, 0xF, 0xF, false);
+        } else if (r == 2) {
+            lo = __builtin_amdgcn_update_dpp(lo, lo, 0x122, 0xF, 0xF, false);
+            hi = __builtin_amdgcn_update_dpp(hi, hi, 0x122, 0xF, 0xF, false);
+        } else {
+            lo = __builtin_amdgcn_update_dpp(lo, lo, 0x121, 0xF, 0xF, false);
+            hi = __builtin_amdgcn_update_dpp(hi, hi, 0x121, 0xF, 0xF, false);
+        }
+        v += __longlong_as_double((long long)(((unsigned long long)(uint32_t)hi << 32) |
+                                               (uint32_t)lo));
+    }
+    const unsigned long long u = __double_as_longlong(v);
+    const uint32_t lo0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 0);
+    const uint32_t hi0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 0);
+    const uint32_t lo1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 16);
+    const uint32_t hi1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 16);
+    return __longlong_as_double((long long)(((unsigned long long)hi0 << 32) | lo0)) +
+           __longlong_as_double((long long)(((unsigned long long)hi1 << 32) | lo1));
+}
 
 // Selects the top-k (k <= 32) of one token's logits row.  On return lane
 // j < k holds the j-th selected expert in *sel_e and its weight in *sel_w.
 // sc: this wave's kTopkScratch words of LDS.
 //
-// tau, the k-th largest of the 64 lane maxima (found by bisection on the
-// key), is at most the k-th largest key: those k lane maxima are k distinct
-// keys >= tau.  So every selected expert has key >= tau.  The keys >= tau
-// (about k + a few on real logits) are gathered and each one's rank in (key
-// descending, expert ascending) order is counted against the others.  If
-// more than 64 keys lie at or above tau (massive ties), k rounds of
-// wave-wide max/min select instead.
+// tau is a lower bound of the k-th largest of the 64 lane maxima: the
+// largest t with #{lanes : lmax >= t} >= k among the keys whose low 16 bits
+// are zero (bisection on the top 16 bits, one ballot per bit).  The k-th
+// largest lane maximum is at most the k-th largest key (those k lane maxima
+// are k distinct keys), so every selected expert has key >= tau.  The keys
+// >= tau (k and a few more on real logits) are gathered -- each lane's
+// count, a prefix sum over the wave from one ballot per count bit, then
+// branch-free LDS writes -- and each one's rank in (key descending, expert
+// ascending) order is counted against the others, whose keys come by
+// readlane.  The lane of rank r hands its candidate to lane r with one
+// ds_permute.  If more than 64 keys lie at or above tau (massive ties), k
+// rounds of wave-wide max/min select instead.
 template <int PL>
 __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row, int E, int k,
                                                   uint32_t *sc, int *sel_e, float *sel_w) {
@@ -92,56 +130,53 @@ __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row,
     uint32_t lmax = 0u;
 #pragma unroll
     for (int i = 0; i < PL; ++i) lmax = max(lmax, key[i]);
-    // tau = the largest t with #{lanes : lmax >= t} >= k, by bisection on
-    // the key (each step one compare whose result is the ballot)
     uint32_t tau = 0u;
 #pragma unroll 1
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 31; bit >= 16; --bit) {
         const uint32_t t = tau | (1u << bit);
         if ((int)__popcll(__ballot(lmax >= t)) >= k) tau = t;
     }
-    int C = 0;
     const unsigned long long below = (1ull << lane) - 1ull;
+    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-        const bool c = key[i] != 0u && key[i] >= tau;
-        const unsigned long long m = __ballot(c);
-        const int pos = C + (int)__popcll(m & below);
-        if (c && pos < 64) {
-            sc[64 + pos] = key[i];
-            sc[128 + pos] = (uint32_t)(lane + 64 * i);
-        }
-        C += (int)__popcll(m);
+    for (int i = 0; i < PL; ++i) cnt += (key[i] != 0u && key[i] >= tau) ? 1 : 0;
+    int base = 0, C = 0;                            // exclusive prefix of cnt, total
+#pragma unroll
+    for (int b = 0; (1 << b) <= PL; ++b) {
+        const unsigned long long m = __ballot((cnt >> b) & 1);
+        base += (int)__popcll(m & below) << b;
+        C += (int)__popcll(m) << b;
     }
     if (C <= 64) {
-        int rank = 64;
-        uint32_t ka = 0u, ea = 0u;
-        const uint4 *sc4 = reinterpret_cast<const uint4 *>(sc);
-        if (lane < C) {
-            ka = sc[64 + lane];
-            ea = sc[128 + lane];
-            rank = 0;
+        int p = base;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const bool c = key[i] != 0u && key[i] >= tau;
+            sc[c ? 64 + p : 192] = key[i];
+            sc[c ? 128 + p : 193] = (uint32_t)(lane + 64 * i);
+            p += c ? 1 : 0;
         }
-        // candidates past C are ignored (keys there may be stale)
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the writes have landed
+        __builtin_amdgcn_wave_barrier();
+        const uint32_t ka = lane < C ? sc[64 + lane] : 0u;
+        const uint32_t ea = lane < C ? sc[128 + lane] : 0xFFFFFFFFu;
+        int rank = 0;
+        for (int j0 = 0; j0 < C; j0 += 4) {           // four independent compares a pass
 #pragma unroll
-        for (int j4 = 0; j4 < 16; ++j4) {
-            if (4 * j4 < C) {
-                const uint4 kb4 = sc4[16 + j4], eb4 = sc4[32 + j4];
-                const uint32_t kb[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
-                const uint32_t eb[4] = {eb4.x, eb4.y, eb4.z, eb4.w};
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    rank += (4 * j4 + q < C && (kb[q] > ka || (kb[q] == ka && eb[q] < ea))) ? 1 : 0;
+            for (int q = 0; q < 4; ++q) {
+                const int j = min(j0 + q, C - 1);
+                const uint32_t kb = (uint32_t)__builtin_amdgcn_readlane((int)ka, j);
+                const uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)ea, j);
+                rank += (j0 + q < C && (kb > ka || (kb == ka && eb < ea))) ? 1 : 0;
             }
         }
-        if (lane >= C) rank = 64;
-        if (rank < k) {
-            sc[rank] = ea;
-            sc[32 + rank] = ka;
-        }
+        // a permutation: candidates go to their rank (< C), the others stay
+        const int tgt = lane < C ? rank : lane;
+        const uint32_t se = (uint32_t)__builtin_amdgcn_ds_permute(tgt << 2, (int)ea);
+        const uint32_t sk = (uint32_t)__builtin_amdgcn_ds_permute(tgt << 2, (int)ka);
         if (lane < k) {
-            my_e = (int)sc[lane];
-            my_v = key_logit(sc[32 + lane]);
+            my_e = (int)se;
+            my_v = key_logit(sk);
         }
     } else {
         for (int j = 0; j < k; ++j) {
@@ -170,9 +205,7 @@ __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row,
     }
     const double vmax = (double)__shfl(my_v, 0, 64);
     const double ex = lane < k ? exp((double)my_v - vmax) : 0.0;
-    double sum = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    const double sum = sum_lanes32_f64(ex);
     *sel_e = my_e;
     *sel_w = (float)(ex / sum);
 }

@@ -151,6 +151,52 @@ def test_router_bias_and_ties(dev):
     np.testing.assert_array_equal(ids_g.cpu().numpy(), ids_f)
 
 
+ONE_TOKEN_CASES = [
+    # (T, d, E, k, f, seed): one token, so top-k and grouping run inside the
+    # gate/up pass (f a multiple of that kernel's 48 pairs per block);
+    # router rows duplicated so that selected experts tie
+    (1, 512, 1000, 32, 96, 31),      # k = 32, E near the limit
+    (1, 192, 40, 5, 96, 32),         # chunk length 3, E not a multiple of 64
+    (1, 256, 16, 16, 96, 33),        # k = E: every expert selected
+]
+
+
+@pytest.mark.parametrize("case", ONE_TOKEN_CASES, ids=[str(c) for c in ONE_TOKEN_CASES])
+def test_one_token_layer_with_ties(dev, case):
+    moe = _moe()
+    T, d, E, k, f, seed = case
+    print("case", case, flush=True)
+    cfg = _small_cfg(T, d, E, k, f, seed)
+    L = synth.gen_layer(cfg)
+    x16 = synth.as_u16(L["x"])
+    wr = L["router_w"].clone()
+    lg0 = oracle.router_logits(x16, synth.as_u16(wr))
+    top = np.argsort(-lg0[0], kind="stable")[:3]
+    for j, e in enumerate(top):
+        wr[(int(e) + 7 + j) % E] = wr[int(e)]
+    bias = torch.linspace(-0.25, 0.25, E, dtype=torch.float32)
+    for j, e in enumerate(top):
+        bias[(int(e) + 7 + j) % E] = bias[int(e)]
+    lg = oracle.router_logits(x16, synth.as_u16(wr), bias.numpy())
+    ids_o, w_o = oracle.topk_softmax(lg, k)
+    if k < E:
+        sel = lg[0][ids_o[0]]
+        assert len(set(sel.tolist())) < k, "no tie among the selected experts"
+    W = _np_experts(L)
+    y_o = np.einsum("tj,tjd->td", w_o, _oracle_o_rows(x16, ids_o, W, d, f))
+    # no separate top-k launch: the fused kernel did the selection
+    moe.diag_time_kernel("topk_permute", capacity=4)
+    y, ids, w = moe.moe_layer_forward(L["x"].to(dev), wr.to(dev), _dev_experts(L, dev), k,
+                                      router_bias=bias.to(dev), return_routing=True)
+    torch.cuda.synchronize()
+    _, launches = moe.diag_kernel_time()
+    moe.diag_time_kernel(None, 0)
+    assert launches == 0
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    assert np.abs(w.cpu().numpy() - w_o).max() <= W_TOL
+    _close(_bf16_to_f64(y), y_o, "layer_forward y")
+
+
 def test_permute_synthetic_ids_full_size(dev):
     # grouping of the long-prefill shape, from seeded ids with a skewed
     # expert distribution (independent of the router)
