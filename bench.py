@@ -33,9 +33,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-WORKLOADS = {"tiny": 0, "decode": 1, "batched-decode": 2, "zipf-prefill": 3, "long-prefill": 4}
+WORKLOADS = {"tiny": 0, "decode": 1, "batched-decode": 2, "zipf-prefill": 3, "long-prefill": 4,
+             "mimo-decode": 5, "mimo-prefill": 6}
 DEFAULT_STEPS = {"tiny": 1000, "decode": 1000, "batched-decode": 200, "zipf-prefill": 20,
-                 "long-prefill": 5}
+                 "long-prefill": 5, "mimo-decode": 1000, "mimo-prefill": 20}
 KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm",
            "router_refine", "permute", "topk_permute", "gemv_gate_up",
            "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "down_mfma",
@@ -49,7 +50,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: decode 1000, batched-decode 200, "
-                         "zipf-prefill 20, long-prefill 5, tiny 1000)")
+                         "zipf-prefill 20, long-prefill 5, tiny 1000, mimo-decode 1000, "
+                         "mimo-prefill 20)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default: 20 decode-sized, 2 prefill)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")

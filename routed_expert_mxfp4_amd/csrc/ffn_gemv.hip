@@ -239,8 +239,8 @@ __global__ __launch_bounds__(64) void down_combine_kernel(
 // a row issued before any of it is used, DPP lane reductions.
 // ---------------------------------------------------------------------------
 constexpr int kRxPairs = 32;         // gate/up pairs per block (8 per wave)
-constexpr int kTokPairs = 48;        // the same for the one-token kernel: 512 blocks
-                                     // at f = 1536, k = 16 (one round of two per CU)
+// the one-token kernel: 48 pairs (512 blocks at f = 1536, k = 16: one round
+// of two per CU) when f allows, else 32
 constexpr int kStageX = 4;           // x staging: d <= 4 * 256 * 8 = 8192
 
 // Gate/up for decode-sized groups, software-pipelined: lane l owns the MX
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
 // row is a, routed from top-k slot sorted_rows[a] -- exactly the grouping of
 // the permute step.  Block (0, 0) writes that grouping (ids, weights,
 // counts, offsets, sorted_rows, row_pos, plan) for the later kernels.
-template <int NBL>
+template <int NBL, int PAIRS>
 __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
     const float *__restrict__ logits, const uint16_t *__restrict__ x, ExpertArgs W,
     int32_t *__restrict__ ids, float *__restrict__ tw, int32_t *__restrict__ counts,
@@ -426,8 +426,8 @@ __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
     const uint32_t code_row = (uint32_t)d >> 1;
     const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
     const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
-    constexpr int kPerWave = kTokPairs / 4;        // pairs n_base + wid + 4 q
-    const int n_base = blockIdx.x * kTokPairs + wid;
+    constexpr int kPerWave = PAIRS / 4;           // pairs n_base + wid + 4 q
+    const int n_base = blockIdx.x * PAIRS + wid;
     float *hrow = h + (size_t)a * f;
     PairBuf<NBL> A, B;
     load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);
@@ -687,27 +687,40 @@ hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets
 
 bool gate_up_token_fusable(int T, int d, int E, int k, int f) {
     const int nbl = (d / 32 + 63) / 64;
-    return T == 1 && k <= 32 && k <= E && E <= 1024 && f % kTokPairs == 0 && nbl <= 4 && d <= 8192;
+    return T == 1 && k <= 32 && k <= E && E <= 1024 && (f % 48 == 0 || f % 32 == 0) &&
+           nbl <= 4 && d <= 8192;
+}
+
+template <int PAIRS>
+hipError_t launch_gate_up_token_p(const float *logits, const uint16_t *x, ExpertArgs w,
+                                  int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
+                                  int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, float *h,
+                                  int d, int E, int k, int f, hipStream_t s) {
+    const int nbl = (d / 32 + 63) / 64;
+    const dim3 grid(f / PAIRS, k);
+    const size_t lds = (size_t)d * 2 + 16;
+    if (nbl == 1)
+        return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<1, PAIRS>, grid, dim3(256),
+                            lds, s, logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
+                            plan, h, d, E, k, f);
+    if (nbl == 2)
+        return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<2, PAIRS>, grid, dim3(256),
+                            lds, s, logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
+                            plan, h, d, E, k, f);
+    return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<4, PAIRS>, grid, dim3(256), lds,
+                        s, logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, h,
+                        d, E, k, f);
 }
 
 hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertArgs w,
                                 int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
                                 int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, float *h,
                                 int d, int E, int k, int f, hipStream_t s) {
-    const int nbl = (d / 32 + 63) / 64;
-    const dim3 grid(f / kTokPairs, k);
-    const size_t lds = (size_t)d * 2 + 16;
-    if (nbl == 1)
-        return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<1>, grid, dim3(256), lds, s,
-                            logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, h,
-                            d, E, k, f);
-    if (nbl == 2)
-        return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<2>, grid, dim3(256), lds, s,
-                            logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, h,
-                            d, E, k, f);
-    return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<4>, grid, dim3(256), lds, s,
-                        logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, h, d,
-                        E, k, f);
+    if (f % 48 == 0)
+        return launch_gate_up_token_p<48>(logits, x, w, ids, tw, counts, offsets, sorted_rows,
+                                          row_pos, plan, h, d, E, k, f, s);
+    return launch_gate_up_token_p<32>(logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
+                                      plan, h, d, E, k, f, s);
 }
 
 template <int NBLD>

@@ -67,8 +67,9 @@ class Config:
         return 2 * f * (d // 2) + 2 * f * (d // 32) + d * (f // 2) + d * (f // 32)
 
 
-# The five workloads: tiny parity layer, one-token decode (1000 tokens),
-# 64-token batched decode, 4096-token skewed prefill, 32768-token prefill.
+# The workloads: tiny parity layer, one-token decode (1000 tokens), 64-token
+# batched decode, 4096-token skewed prefill, 32768-token prefill; and the
+# same layer at a second routing shape, one-token decode and prefill.
 CONFIGS = {
     0: Config(0, "tiny T=8 d=256 E=16 k=2 f=128", 8, 256, 16, 2, 128, seed=0),
     1: Config(1, "decode T=1 d=7168 E=896 k=16 f=1536 x1000 tokens", 1, 7168,
@@ -79,6 +80,12 @@ CONFIGS = {
               896, 16, 1536, seed=3, zipf_beta=0.34),
     4: Config(4, "long prefill T=32768 d=7168 E=896 k=16 f=1536", 32768, 7168,
               896, 16, 1536, seed=4),
+    # a second routing shape: 256 experts, top-8 (MiMo V2.6 Flash); d and f
+    # are synthetic (d * f ~ 310e9 / (48 layers * 256 experts * 3))
+    5: Config(5, "mimo decode T=1 d=4096 E=256 k=8 f=2048 x1000 tokens", 1, 4096,
+              256, 8, 2048, seed=5, batches=1000),
+    6: Config(6, "mimo prefill T=4096 d=4096 E=256 k=8 f=2048", 4096, 4096, 256, 8,
+              2048, seed=6),
 }
 
 

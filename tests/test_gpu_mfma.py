@@ -156,3 +156,10 @@ def test_long_prefill_full_size(dev, full_experts):
     cfg = synth.CONFIGS[4]
     full_experts(4)
     _decode_parity(dev, cfg, 0, [0, 12345, 32767])
+
+
+def test_second_shape_prefill_full_size(dev, full_experts):
+    # 256 experts, top-8, d = 4096, f = 2048, 4096 tokens
+    cfg = synth.CONFIGS[6]
+    full_experts(6)
+    _decode_parity(dev, cfg, 0, [0, 2048, 4095])

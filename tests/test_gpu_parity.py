@@ -153,11 +153,12 @@ def test_router_bias_and_ties(dev):
 
 ONE_TOKEN_CASES = [
     # (T, d, E, k, f, seed): one token, so top-k and grouping run inside the
-    # gate/up pass (f a multiple of that kernel's 48 pairs per block);
+    # gate/up pass (48 or 32 pairs per block);
     # router rows duplicated so that selected experts tie
     (1, 512, 1000, 32, 96, 31),      # k = 32, E near the limit
     (1, 192, 40, 5, 96, 32),         # chunk length 3, E not a multiple of 64
     (1, 256, 16, 16, 96, 33),        # k = E: every expert selected
+    (1, 256, 64, 8, 64, 34),         # f not a multiple of 48: 32 pairs per block
 ]
 
 
@@ -338,6 +339,15 @@ def test_decode_full_size(dev, full_experts):
     cfg = synth.CONFIGS[1]
     full_experts(1)
     for batch in (0, 1, 999):
+        print("decode token", batch, flush=True)
+        _decode_parity(dev, cfg, batch, [0])
+
+
+def test_second_shape_decode_full_size(dev, full_experts):
+    # 256 experts, top-8, d = 4096, f = 2048
+    cfg = synth.CONFIGS[5]
+    full_experts(5)
+    for batch in (0, 500, 999):
         print("decode token", batch, flush=True)
         _decode_parity(dev, cfg, batch, [0])
 
