@@ -73,6 +73,12 @@ def lib():
         L.orc_combine_token.argtypes = [i, i, P, P, P, P]
         L.orc_layer_forward.restype = ctypes.c_int
         L.orc_layer_forward.argtypes = [i, i, i, i, i] + [P] * 12 + [i]
+        L.orc_layer_forward_act.restype = ctypes.c_int
+        L.orc_layer_forward_act.argtypes = [i, i, i, i, i, i] + [P] * 12 + [i]
+        L.orc_expert_row_act.restype = None
+        L.orc_expert_row_act.argtypes = [i, i, i, P, P, P, P, P, P, P]
+        L.orc_mx_round.restype = None
+        L.orc_mx_round.argtypes = [i, i, P]
         L.orc_elem_value.restype = ctypes.c_double
         L.orc_elem_value.argtypes = [i, ctypes.c_uint]
         L.orc_mx_quantize_block.restype = None
@@ -174,15 +180,29 @@ def permute(topk_ids, E):
 
 
 # ---- expert FFN / combine -----------------------------------------------------
-def expert_row(x_row, gu_codes, gu_scales, dn_codes, dn_scales, d, f):
+def expert_row(x_row, gu_codes, gu_scales, dn_codes, dn_scales, d, f, act=0):
     """One expert on one token row.  Weight arrays are that expert's own
-    [2f][d/2], [2f][d/32], [d][f/2], [d][f/32] slices.  Returns (h, o)."""
+    [2f][d/2], [2f][d/32], [d][f/2], [d][f/32] slices.  Returns (h, o).
+    act = 1: the activation-MX mode (x and h rounded to one MX E2M3 term per
+    32 elements before their products; h is returned rounded)."""
     x_row = _c(x_row, np.uint16)
     args = [_c(a, np.uint8) for a in (gu_codes, gu_scales, dn_codes, dn_scales)]
     h = np.empty(f, dtype=np.float64)
     o = np.empty(d, dtype=np.float64)
-    lib().orc_expert_row(d, f, _p(x_row), *[_p(a) for a in args], _p(h), _p(o))
+    if act:
+        lib().orc_expert_row_act(d, f, int(act), _p(x_row), *[_p(a) for a in args], _p(h),
+                                 _p(o))
+    else:
+        lib().orc_expert_row(d, f, _p(x_row), *[_p(a) for a in args], _p(h), _p(o))
     return h, o
+
+
+def mx_round(fmt, v):
+    """Each 32-element block of the fp64 vector v rounded to one MX term."""
+    v = np.array(v, dtype=np.float64, copy=True)
+    assert v.ndim == 1 and v.size % 32 == 0
+    lib().orc_mx_round(int(fmt), int(v.size), _p(v))
+    return v
 
 
 def combine_token(w, o):
@@ -196,8 +216,9 @@ def combine_token(w, o):
 
 
 def layer_forward(x, router_w, bias, gu_codes, gu_scales, dn_codes, dn_scales,
-                  k, n_threads=0):
-    """Whole layer on full weight arrays [E][...].  Returns a dict."""
+                  k, n_threads=0, act=0):
+    """Whole layer on full weight arrays [E][...].  Returns a dict.  act = 1:
+    expert rows in the activation-MX mode (the router sees x as given)."""
     x = _c(x, np.uint16)
     router_w = _c(router_w, np.uint16)
     T, d = x.shape
@@ -210,9 +231,14 @@ def layer_forward(x, router_w, bias, gu_codes, gu_scales, dn_codes, dn_scales,
     w = np.empty((T, k), dtype=np.float64)
     y64 = np.empty((T, d), dtype=np.float64)
     yb = np.empty((T, d), dtype=np.uint16)
-    rc = lib().orc_layer_forward(T, d, E, k, f, _p(x), _p(router_w), _p(b),
-                                 *[_p(a) for a in ws], _p(logits), _p(ids),
-                                 _p(w), _p(y64), _p(yb), int(n_threads))
+    if act:
+        rc = lib().orc_layer_forward_act(T, d, E, k, f, int(act), _p(x), _p(router_w), _p(b),
+                                         *[_p(a) for a in ws], _p(logits), _p(ids),
+                                         _p(w), _p(y64), _p(yb), int(n_threads))
+    else:
+        rc = lib().orc_layer_forward(T, d, E, k, f, _p(x), _p(router_w), _p(b),
+                                     *[_p(a) for a in ws], _p(logits), _p(ids),
+                                     _p(w), _p(y64), _p(yb), int(n_threads))
     if rc != 0:
         raise MemoryError("oracle layer_forward: allocation failed")
     return {"logits": logits, "topk_ids": ids, "topk_w": w, "y64": y64,

@@ -233,29 +233,69 @@ void orc_permute(int T, int E, int k, const int32_t *topk_ids,
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* Each consecutive 32-element block of v[0..n) replaced, in place, by its
+ * single-term MX value in element format fmt: the block quantised with
+ * orc_mx_quantize_block and decoded exactly.  n is a multiple of 32. */
+void orc_mx_round(int fmt, int n, double *v)
+{
+    for (int b = 0; b < n; b += 32) {
+        uint8_t sc, codes[32];
+        orc_mx_quantize_block(fmt, v + b, &sc, codes);
+        double s = orc_e8m0_value(sc);
+        for (int i = 0; i < 32; ++i)
+            v[b + i] = orc_elem_value(fmt, codes[i]) * s;
+    }
+}
+
 /* h[n] = silu(g_n) * u_n with g_n = sum_k x_k W_gu[n][k] and
  * u_n = sum_k x_k W_gu[f+n][k]; then o[m] = sum_n h_n W_dn[m][n].
- * All in fp64 with exact dequantised weights and exact bf16 inputs. */
-void orc_expert_row(int d, int f, const uint16_t *x_row,
-                    const uint8_t *gu_codes, const uint8_t *gu_scales,
-                    const uint8_t *dn_codes, const uint8_t *dn_scales,
-                    double *h, double *o)
+ * All in fp64 with exact dequantised weights and exact bf16 inputs.
+ * act = 1 (the activation-MX mode): x is rounded to one MX E2M3 term per
+ * 32 elements before the gate/up products and h likewise before the down
+ * products; h then returns the rounded values. */
+static void expert_row_impl(int d, int f, int act, const uint16_t *x_row,
+                            const uint8_t *gu_codes, const uint8_t *gu_scales,
+                            const uint8_t *dn_codes, const uint8_t *dn_scales,
+                            double *h, double *o)
 {
+    double *xv = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int kk = 0; kk < d; ++kk)
+        xv[kk] = orc_bf16_value(x_row[kk]);
+    if (act)
+        orc_mx_round(ORC_FMT_E2M3, d, xv);
     for (int n = 0; n < f; ++n) {
         double g = 0.0, u = 0.0;
         for (int kk = 0; kk < d; ++kk) {
-            double xv = orc_bf16_value(x_row[kk]);
-            g = g + xv * orc_mxfp4_weight(gu_codes, gu_scales, d, n, kk);
-            u = u + xv * orc_mxfp4_weight(gu_codes, gu_scales, d, f + n, kk);
+            g = g + xv[kk] * orc_mxfp4_weight(gu_codes, gu_scales, d, n, kk);
+            u = u + xv[kk] * orc_mxfp4_weight(gu_codes, gu_scales, d, f + n, kk);
         }
         h[n] = silu(g) * u;
     }
+    free(xv);
+    if (act)
+        orc_mx_round(ORC_FMT_E2M3, f, h);
     for (int m = 0; m < d; ++m) {
         double s = 0.0;
         for (int n = 0; n < f; ++n)
             s = s + h[n] * orc_mxfp4_weight(dn_codes, dn_scales, f, m, n);
         o[m] = s;
     }
+}
+
+void orc_expert_row(int d, int f, const uint16_t *x_row,
+                    const uint8_t *gu_codes, const uint8_t *gu_scales,
+                    const uint8_t *dn_codes, const uint8_t *dn_scales,
+                    double *h, double *o)
+{
+    expert_row_impl(d, f, 0, x_row, gu_codes, gu_scales, dn_codes, dn_scales, h, o);
+}
+
+void orc_expert_row_act(int d, int f, int act, const uint16_t *x_row,
+                        const uint8_t *gu_codes, const uint8_t *gu_scales,
+                        const uint8_t *dn_codes, const uint8_t *dn_scales,
+                        double *h, double *o)
+{
+    expert_row_impl(d, f, act, x_row, gu_codes, gu_scales, dn_codes, dn_scales, h, o);
 }
 
 /* ======================================================================= */
@@ -284,13 +324,15 @@ void orc_combine_token(int d, int k, const double *w, const double *o,
 
 /* router -> top-k -> per-row expert FFN -> combine, token by token.
  * Returns 0, or -1 when the scratch allocation fails.  Rows are independent,
- * so they are spread over n_threads OpenMP threads (<= 0: runtime default). */
-int orc_layer_forward(int T, int d, int E, int k, int f, const uint16_t *x,
-                      const uint16_t *router_w, const float *bias,
-                      const uint8_t *gu_codes, const uint8_t *gu_scales,
-                      const uint8_t *dn_codes, const uint8_t *dn_scales,
-                      float *logits, int32_t *topk_ids, double *topk_w,
-                      double *y64, uint16_t *y_bf16, int n_threads)
+ * so they are spread over n_threads OpenMP threads (<= 0: runtime default).
+ * act selects the expert rows' activation mode (see expert_row_impl); the
+ * router always sees x as given. */
+static int layer_forward_impl(int T, int d, int E, int k, int f, int act, const uint16_t *x,
+                              const uint16_t *router_w, const float *bias,
+                              const uint8_t *gu_codes, const uint8_t *gu_scales,
+                              const uint8_t *dn_codes, const uint8_t *dn_scales,
+                              float *logits, int32_t *topk_ids, double *topk_w,
+                              double *y64, uint16_t *y_bf16, int n_threads)
 {
     size_t gu_code_b = (size_t)2 * f * (d / 2), gu_sc_b = (size_t)2 * f * (d / 32);
     size_t dn_code_b = (size_t)d * (f / 2), dn_sc_b = (size_t)d * (f / 32);
@@ -306,9 +348,9 @@ int orc_layer_forward(int T, int d, int E, int k, int f, const uint16_t *x,
         double *h = (double *)malloc(sizeof(double) * (size_t)f);
         int t = r / k;
         size_t e = (size_t)topk_ids[r];
-        orc_expert_row(d, f, x + (size_t)t * d, gu_codes + e * gu_code_b,
-                       gu_scales + e * gu_sc_b, dn_codes + e * dn_code_b,
-                       dn_scales + e * dn_sc_b, h, o + (size_t)r * d);
+        expert_row_impl(d, f, act, x + (size_t)t * d, gu_codes + e * gu_code_b,
+                        gu_scales + e * gu_sc_b, dn_codes + e * dn_code_b,
+                        dn_scales + e * dn_sc_b, h, o + (size_t)r * d);
         free(h);
     }
     for (int t = 0; t < T; ++t)
@@ -317,6 +359,30 @@ int orc_layer_forward(int T, int d, int E, int k, int f, const uint16_t *x,
                           y_bf16 ? y_bf16 + (size_t)t * d : NULL);
     free(o);
     return 0;
+}
+
+int orc_layer_forward(int T, int d, int E, int k, int f, const uint16_t *x,
+                      const uint16_t *router_w, const float *bias,
+                      const uint8_t *gu_codes, const uint8_t *gu_scales,
+                      const uint8_t *dn_codes, const uint8_t *dn_scales,
+                      float *logits, int32_t *topk_ids, double *topk_w,
+                      double *y64, uint16_t *y_bf16, int n_threads)
+{
+    return layer_forward_impl(T, d, E, k, f, 0, x, router_w, bias, gu_codes, gu_scales,
+                              dn_codes, dn_scales, logits, topk_ids, topk_w, y64, y_bf16,
+                              n_threads);
+}
+
+int orc_layer_forward_act(int T, int d, int E, int k, int f, int act, const uint16_t *x,
+                          const uint16_t *router_w, const float *bias,
+                          const uint8_t *gu_codes, const uint8_t *gu_scales,
+                          const uint8_t *dn_codes, const uint8_t *dn_scales,
+                          float *logits, int32_t *topk_ids, double *topk_w,
+                          double *y64, uint16_t *y_bf16, int n_threads)
+{
+    return layer_forward_impl(T, d, E, k, f, act, x, router_w, bias, gu_codes, gu_scales,
+                              dn_codes, dn_scales, logits, topk_ids, topk_w, y64, y_bf16,
+                              n_threads);
 }
 
 /* ======================================================================= */

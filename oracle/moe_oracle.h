@@ -52,6 +52,14 @@ void orc_expert_row(int d, int f, const uint16_t *x_row,
                     const uint8_t *dn_codes, const uint8_t *dn_scales,
                     double *h, double *o);
 
+/* act = 1, the activation-MX mode: x and h each rounded to one MX E2M3 term
+ * per 32 elements (orc_mx_round) before their products; h returns the
+ * rounded values.  act = 0 is orc_expert_row. */
+void orc_expert_row_act(int d, int f, int act, const uint16_t *x_row,
+                        const uint8_t *gu_codes, const uint8_t *gu_scales,
+                        const uint8_t *dn_codes, const uint8_t *dn_scales,
+                        double *h, double *o);
+
 /* ---- weighted combine of one token's k expert outputs ------------------ */
 void orc_combine_token(int d, int k, const double *w, const double *o,
                        double *y64, uint16_t *y_bf16);
@@ -64,11 +72,22 @@ int orc_layer_forward(int T, int d, int E, int k, int f, const uint16_t *x,
                       float *logits, int32_t *topk_ids, double *topk_w,
                       double *y64, uint16_t *y_bf16, int n_threads);
 
+/* The same layer with the expert rows in activation mode act (above). */
+int orc_layer_forward_act(int T, int d, int E, int k, int f, int act, const uint16_t *x,
+                          const uint16_t *router_w, const float *bias,
+                          const uint8_t *gu_codes, const uint8_t *gu_scales,
+                          const uint8_t *dn_codes, const uint8_t *dn_scales,
+                          float *logits, int32_t *topk_ids, double *topk_w,
+                          double *y64, uint16_t *y_bf16, int n_threads);
+
 /* ---- OCP MX conversion model (element formats below) ------------------- */
 enum { ORC_FMT_E4M3 = 0, ORC_FMT_E2M3 = 1, ORC_FMT_E2M1 = 2 };
 double orc_elem_value(int fmt, unsigned code);
 void   orc_mx_quantize_block(int fmt, const double *v, uint8_t *scale_code,
                              uint8_t *codes);
+/* v[0..n) (n a multiple of 32) rounded in place, block by block, to one MX
+ * term of element format fmt. */
+void   orc_mx_round(int fmt, int n, double *v);
 void   orc_mx_split_block(int fmt, const float *v, uint8_t *hi_scale,
                           uint8_t *hi_codes, uint8_t *lo_scale,
                           uint8_t *lo_codes);

@@ -171,3 +171,45 @@ def test_tiny_layer_matches_independent_numpy_pipeline():
     np.testing.assert_allclose(res["y64"], y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
     yb = np.array([[oracle.round_to_bf16(v) for v in row] for row in res["y64"]], np.uint16)
     np.testing.assert_array_equal(res["y"], yb)
+
+
+def test_activation_mx_mode_hand_example():
+    """The activation-MX mode on a layer small enough to do by hand (one
+    expert, d = f = 32, weights 0 or 1.0, E8M0 scale 2^0).
+    x = (1.1015625, 0.30078125, 0, ...) (bf16 of 1.1 and 0.3).  Its block
+    amax gives X = floor(log2 1.10) - 2 = -2, so x / 2^X = (4.40625,
+    1.203125) rounds on the E2M3 grid to (4.5, 1.25): x' = (1.125, 0.3125).
+    Gate rows 0, 1 pick x'0, x'1 and up rows 0, 1 pick x'1, x'0, so
+    h0 = silu(1.125) * 0.3125 = 0.265400 and h1 = silu(0.3125) * 1.125 =
+    0.203026.  Their block gives X = -2 - 2 = -4: h / 2^X = (4.2464,
+    3.2484) round to (4.0, 3.25), h' = (0.25, 0.203125).  The down row 0
+    sums h'0 + h'1 = 0.453125, and k = 1 makes y0 = o0 exactly (every other
+    output is 0).  Without the rounding of x the result is 0.4375, without
+    that of h 0.468426; the plain mode gives silu(1.1015625) * 0.30078125 +
+    silu(0.30078125) * 1.1015625."""
+    d = f = 32
+    x = np.zeros((1, d), dtype=np.uint16)
+    x[0, 0], x[0, 1] = 0x3F8D, 0x3E9A               # bf16 1.1015625, 0.30078125
+    gu_codes = np.zeros((1, 2 * f, d // 2), dtype=np.uint8)
+    gu_codes[0, 0, 0] = 0x02                         # gate row 0: element 0 = 1.0
+    gu_codes[0, 1, 0] = 0x20                         # gate row 1: element 1 = 1.0
+    gu_codes[0, f + 0, 0] = 0x20                     # up row 0: element 1
+    gu_codes[0, f + 1, 0] = 0x02                     # up row 1: element 0
+    gu_scales = np.full((1, 2 * f, d // 32), 127, dtype=np.uint8)
+    dn_codes = np.zeros((1, d, f // 2), dtype=np.uint8)
+    dn_codes[0, 0, 0] = 0x22                         # down row 0: elements 0, 1
+    dn_scales = np.full((1, d, f // 32), 127, dtype=np.uint8)
+    wr = np.zeros((1, d), dtype=np.uint16)
+    args = (x, wr, None, gu_codes, gu_scales, dn_codes, dn_scales)
+    amx = oracle.layer_forward(*args, k=1, act=1)
+    assert amx["y64"][0, 0] == 0.453125
+    assert (amx["y64"][0, 1:] == 0.0).all()
+    plain = oracle.layer_forward(*args, k=1)
+    sl = lambda z: z / (1.0 + math.exp(-z))
+    x0, x1 = 1.1015625, 0.30078125
+    assert abs(plain["y64"][0, 0] - (sl(x0) * x1 + sl(x1) * x0)) <= 1e-15
+    # the rounding helper on its own: the x block above
+    v = np.zeros(32)
+    v[0], v[1] = x0, x1
+    r = oracle.mx_round(oracle.FMT_E2M3, v)
+    assert r[0] == 1.125 and r[1] == 0.3125 and (r[2:] == 0).all()

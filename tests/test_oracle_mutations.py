@@ -26,8 +26,8 @@ MUTATIONS = [
     ("scale block index",
      "(size_t)(col / 32)]", "(size_t)(col / 16) % (size_t)(K / 32)]"),
     ("gate and up swapped",
-     "g = g + xv * orc_mxfp4_weight(gu_codes, gu_scales, d, n, kk);",
-     "g = g + xv * orc_mxfp4_weight(gu_codes, gu_scales, d, f + n, kk);"),
+     "g = g + xv[kk] * orc_mxfp4_weight(gu_codes, gu_scales, d, n, kk);",
+     "g = g + xv[kk] * orc_mxfp4_weight(gu_codes, gu_scales, d, f + n, kk);"),
     ("silu sign",
      "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     ("router operand transposed",
@@ -62,6 +62,10 @@ MUTATIONS = [
      "{"),
     ("MX ties away from zero",
      "v = nearbyint(a / q) * q;", "v = round(a / q) * q;"),
+    ("activation-MX mode: x not rounded",
+     "    if (act)\n        orc_mx_round(ORC_FMT_E2M3, d, xv);", ""),
+    ("activation-MX mode: h not rounded",
+     "    if (act)\n        orc_mx_round(ORC_FMT_E2M3, f, h);", ""),
 ]
 
 
