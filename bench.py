@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default: 20 decode-sized, 2 prefill)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--act", choices=("bf16", "mx"), default="bf16",
+                    help="expert activations: bf16 (the W4A16 result; default) or mx (the "
+                         "activation-MX mode: x and h rounded to one MX E2M3 term per 32)")
     ap.add_argument("--cpu-sample", type=int, default=2,
                     help="tokens of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-breakdown", action="store_true",
@@ -194,13 +197,14 @@ def main():
     bias = None if bias is None else bias.to(dev)
     n_batches = min(cfg.batches, max(1, args.steps + args.warmup))
     xs = [synth.gen_x(cfg, b).to(dev) for b in range(n_batches)]
-    layer = moe.Layer(experts, wr, cfg.k, bias, T=cfg.T)
+    act = moe.ACT_MX_E2M3 if args.act == "mx" else moe.ACT_BF16
+    layer = moe.Layer(experts, wr, cfg.k, bias, T=cfg.T, act=act)
     y = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
-    dims = moe.dims_of(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f)
+    dims = moe.dims_of(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, act)
     ex = moe.experts_of(experts)
     ws = layer._ws
     argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(wr.data_ptr()),
@@ -271,7 +275,7 @@ def main():
                     "frac": achieved / MXFP4_PEAK_TFLOPS,
                     "traffic": traffic_from_profiles(dominant, args.workload, sha),
                     "algorithmic_flops_per_launch": flops_per_launch,
-                    "mfma_passes_per_product": 2,
+                    "mfma_passes_per_product": 1 if act else 2,
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
     else:
         bytes_per_launch = mean_touched * per_expert_gu
@@ -295,12 +299,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp6xfp4" if act and mfma else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "f": cfg.f, "distinct_batches": n_batches,
                    "weights": "MXFP4 (E2M1 codes + E8M0 scale per 32), resident in HBM",
-                   "activations": "bf16", "accumulate": "fp32",
+                   "activations": ("MX E2M3, one term per 32 (activation-MX mode)" if act
+                                   else "bf16"), "accumulate": "fp32",
                    "expert_path": "scaled MFMA" if mfma else "GEMV"},
         "expert_weight_GBps": layer_bytes * args.steps / elapsed / 1e9,
         "expert_weight_hbm_frac": layer_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBPS,

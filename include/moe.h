@@ -58,12 +58,31 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
+
+/* Activation modes of the expert GEMMs (moe_dims.act):
+ *   MOE_ACT_BF16     x and h as computed (bf16 x, fp32 h): the layer's
+ *                    W4A16 result; the prefill path gets there through a
+ *                    two-term MX split (two matrix passes).
+ *   MOE_ACT_MX_E2M3  the activation-MX mode: x and h are each rounded to
+ *                    one OCP MX E2M3 term per 32 elements along K (shared
+ *                    exponent floor(log2 amax) - 2, nearest-even elements
+ *                    saturating at 7.5) before their GEMM, so the prefill
+ *                    path makes one FP6 x FP4 matrix pass.  A different,
+ *                    approximate result (a few % of max|y| away from W4A16
+ *                    on the synthetic workloads).  The router always sees x
+ *                    as given.  Like the pages' engine quantising the
+ *                    routed-up activations ("Run layer-major prefill",
+ *                    Moonshine README). */
+#define MOE_ACT_BF16 0
+#define MOE_ACT_MX_E2M3 1
 
 /* Problem shape: T tokens, hidden size d, E experts, top-k, expert
- * intermediate size f. */
+ * intermediate size f; act: activation mode of moe_expert_ffn and
+ * moe_layer_forward (MOE_ACT_*; the other entry points ignore it). */
 typedef struct moe_dims {
     int32_t T, d, E, k, f;
+    int32_t act;
 } moe_dims;
 
 /* The routed experts in their canonical MXFP4 store (device memory):

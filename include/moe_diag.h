@@ -8,8 +8,9 @@
  * (the two fused, small T), "router_norms", "router_filter_gemm",
  * "router_refine" (routing of many tokens), "plan", "gemv_gate_up", "gemv_down",
  * "down_combine", "combine", "mfma_ffn" (the whole scaled-MFMA expert
- * FFN of large T), and its parts "mx_split_x", "gate_up_mfma",
- * "mx_split_h", "down_mfma".
+ * FFN of large T), its parts "mx_split_x", "gate_up_mfma" (which also
+ * splits h) and "down_mfma", and "mx_round" (the activation-MX mode's
+ * rounding of x and h on the GEMV paths).
  */
 #ifndef ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 #define ROUTED_EXPERT_MXFP4_MOE_DIAG_H

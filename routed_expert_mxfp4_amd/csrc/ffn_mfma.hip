@@ -171,6 +171,43 @@ __global__ __launch_bounds__(256) void mx_split_e2m3_kernel(const In *__restrict
     if ((b & 3) == 0) *reinterpret_cast<u32x2_t *>(step + 200) = u32x2_t{0u, 0u};
 }
 
+template <typename T>
+__device__ __forceinline__ void store_block32(T *p, const f32x32_t &v);
+template <>
+__device__ __forceinline__ void store_block32<uint16_t>(uint16_t *p, const f32x32_t &v) {
+    // one-term MX values carry at most 4 significant bits: exact in bf16
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        u32x4_t w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = (__float_as_uint(v[8 * c + 2 * q]) >> 16) |
+                   (__float_as_uint(v[8 * c + 2 * q + 1]) & 0xFFFF0000u);
+        *reinterpret_cast<u32x4_t *>(p + 8 * c) = w;
+    }
+}
+template <>
+__device__ __forceinline__ void store_block32<float>(float *p, const f32x32_t &v) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<f32x4_t *>(p + 4 * c) = f32x4_t{v[4 * c], v[4 * c + 1], v[4 * c + 2],
+                                                          v[4 * c + 3]};
+}
+
+// The activation-MX rounding: each 32-element block of a flat array (rows x
+// K with K % 32 == 0, so blocks never cross rows) replaced by its one-term
+// MX E2M3 value, decoded exactly -- the hi term of split_block32.  One lane
+// per block; out may be in.
+template <typename T>
+__global__ __launch_bounds__(256) void mx_round_kernel(const T *in, uint32_t items, T *out) {
+    const uint32_t item = blockIdx.x * 256u + threadIdx.x;
+    if (item >= items) return;
+    float v[32];
+    load_block32<T>(in + (size_t)item * 32, v);
+    const float sc = e8m0_operand(mx_exponent(amax32(v)));
+    store_block32<T>(out + (size_t)item * 32, e2m3_unpack32(e2m3_pack32(v, sc), sc));
+}
+
 // ---------------------------------------------------------------------------
 // Tile plan: per active expert, the number of 128-row tiles and their
 // exclusive prefix.  tiles[0] = total, tiles[1 + a] = prefix of expert a.
@@ -432,7 +469,8 @@ __device__ __forceinline__ void issue_a(uint32_t lds_addr, const uint8_t *aq,
 }
 
 // The scale operand reads byte 0 of the register (bits above are ignored).
-template <int PS, int SUB>
+// kSingle: the activation-MX mode, the hi term alone.
+template <int PS, int SUB, bool kSingle>
 __device__ __forceinline__ void mfma_mt(f32x4_t (&acc)[8], const AFrag &a, const BRing &br,
                                         const uint32_t (&bsc)[8]) {
 #pragma unroll
@@ -441,15 +479,16 @@ __device__ __forceinline__ void mfma_mt(f32x4_t (&acc)[8], const AFrag &a, const
         const i32x8_t b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
         acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.hi, b, acc[nt], 2, 4, 0,
                                                                    (int)a.sc, 0, (int)bsc[nt]);
-        acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.lo, b, acc[nt], 2, 4, 1,
-                                                                   (int)a.sc, 0, (int)bsc[nt]);
+        if constexpr (!kSingle)
+            acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.lo, b, acc[nt], 2, 4, 1,
+                                                                       (int)a.sc, 0, (int)bsc[nt]);
     }
 }
 
 // One K step at ring position R = kk % 4: wait for stage kk, queue step
 // kk + 3's activations (and, by R, a code pair or a scale group), then 128
 // MFMAs (A fragments read one m-tile ahead).
-template <int R>
+template <int R, bool kSingle>
 __device__ __forceinline__ void gemm_step(f32x4_t (&acc)[8][8], BRing &br, const GemmArgs &ga,
                                           const uint8_t *aq, const uint32_t (&src)[kDmaPerWave],
                                           uint32_t lds_addr, uint32_t a_lane, uint32_t s_lane,
@@ -475,27 +514,27 @@ __device__ __forceinline__ void gemm_step(f32x4_t (&acc)[8][8], BRing &br, const
     read_afrag<0>(f0, a, s);
     read_afrag<1>(f1, a, s);
     afrag_ready<5>(f0);
-    mfma_mt<PS, SUB>(acc[0], f0, br, bsc);
+    mfma_mt<PS, SUB, kSingle>(acc[0], f0, br, bsc);
     read_afrag<2>(f0, a, s);
     afrag_ready<5>(f1);
-    mfma_mt<PS, SUB>(acc[1], f1, br, bsc);
+    mfma_mt<PS, SUB, kSingle>(acc[1], f1, br, bsc);
     read_afrag<3>(f1, a, s);
     afrag_ready<5>(f0);
-    mfma_mt<PS, SUB>(acc[2], f0, br, bsc);
+    mfma_mt<PS, SUB, kSingle>(acc[2], f0, br, bsc);
     read_afrag<4>(f0, a, s);
     afrag_ready<5>(f1);
-    mfma_mt<PS, SUB>(acc[3], f1, br, bsc);
+    mfma_mt<PS, SUB, kSingle>(acc[3], f1, br, bsc);
     read_afrag<5>(f1, a, s);
     afrag_ready<5>(f0);
-    mfma_mt<PS, SUB>(acc[4], f0, br, bsc);
+    mfma_mt<PS, SUB, kSingle>(acc[4], f0, br, bsc);
     read_afrag<6>(f0, a, s);
     afrag_ready<5>(f1);
-    mfma_mt<PS, SUB>(acc[5], f1, br, bsc);
+    mfma_mt<PS, SUB, kSingle>(acc[5], f1, br, bsc);
     read_afrag<7>(f1, a, s);
     afrag_ready<5>(f0);
-    mfma_mt<PS, SUB>(acc[6], f0, br, bsc);
+    mfma_mt<PS, SUB, kSingle>(acc[6], f0, br, bsc);
     afrag_ready<0>(f1);
-    mfma_mt<PS, SUB>(acc[7], f1, br, bsc);
+    mfma_mt<PS, SUB, kSingle>(acc[7], f1, br, bsc);
 }
 
 // The block's tile: which expert, which 128 rows of it, which 512 weight
@@ -532,7 +571,7 @@ __device__ __forceinline__ bool select_tile(const int32_t *tiles, const int32_t 
 // kGateUp: A = split x (token rows), out = hq, the split of h = silu(gate) *
 //          up [rows][f] (expert-major rows), the down pass's A;
 // else:    A = hq, out = rows_out bf16 [rows][d].
-template <bool kGateUp>
+template <bool kGateUp, bool kSingle>
 __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     const uint8_t *__restrict__ aq, ExpertArgs W, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
@@ -615,12 +654,12 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     // load, wait or barrier (a step past the end only skips its MFMAs), so
     // the wait counts the compiler derives at the loop header are exact
     for (int kk = 0; kk < ga.nsteps; kk += 4) {
-        gemm_step<0>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk, wid, true);
-        gemm_step<1>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 1, wid,
+        gemm_step<0, kSingle>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk, wid, true);
+        gemm_step<1, kSingle>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 1, wid,
                      kk + 1 < ga.nsteps);
-        gemm_step<2>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 2, wid,
+        gemm_step<2, kSingle>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 2, wid,
                      kk + 2 < ga.nsteps);
-        gemm_step<3>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 3, wid,
+        gemm_step<3, kSingle>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 3, wid,
                      kk + 3 < ga.nsteps);
     }
     // drain the trailing (re-)loads before their registers or the block's
@@ -705,11 +744,13 @@ bool g_attr_done = false;
 
 hipError_t set_lds_attrs() {
     if (g_attr_done) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void *)ffn_mfma_kernel<true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void *)ffn_mfma_kernel<false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    const void *k[4] = {(const void *)ffn_mfma_kernel<true, false>,
+                        (const void *)ffn_mfma_kernel<true, true>,
+                        (const void *)ffn_mfma_kernel<false, false>,
+                        (const void *)ffn_mfma_kernel<false, true>};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 4 && e == hipSuccess; ++i)
+        e = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e == hipSuccess) g_attr_done = true;
     return e;
 }
@@ -745,9 +786,25 @@ hipError_t launch_mx_split_f32(const float *in, int rows, int K, uint8_t *q, hip
     return hipGetLastError();
 }
 
+hipError_t launch_mx_round_bf16(const uint16_t *in, int rows, int K, uint16_t *out,
+                                hipStream_t st) {
+    const uint32_t items = (uint32_t)rows * (uint32_t)(K / 32);
+    if (items == 0) return hipSuccess;
+    return timed_launch("mx_round", mx_round_kernel<uint16_t>, dim3((items + 255) / 256),
+                        dim3(256), 0, st, in, items, out);
+}
+
+hipError_t launch_mx_round_f32(const float *in, int rows, int K, float *out, hipStream_t st) {
+    const uint32_t items = (uint32_t)rows * (uint32_t)(K / 32);
+    if (items == 0) return hipSuccess;
+    return timed_launch("mx_round", mx_round_kernel<float>, dim3((items + 255) / 256), dim3(256),
+                        0, st, in, items, out);
+}
+
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                            const int32_t *sorted_rows, const int32_t *plan, uint16_t *rows_out,
-                           void *ws, int T, int d, int E, int k, int f, hipStream_t s) {
+                           void *ws, int T, int d, int E, int k, int f, bool single,
+                           hipStream_t s) {
     hipError_t e = set_lds_attrs();
     if (e != hipSuccess) return e;
     const size_t rows = (size_t)T * k;
@@ -768,12 +825,18 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
     const long long mt_max = min(E, (int)rows) + (long long)((rows + kBM - 1) / kBM);
     {
         const long long blocks = 8 * ((mt_max * (f / 256) + 7) / 8);
-        (void)timed_launch("gate_up_mfma", ffn_mfma_kernel<true>, dim3((unsigned)blocks), dim3(256), kLdsBytes, s, xq, w, offsets, sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f);
+        (void)timed_launch("gate_up_mfma",
+                           single ? ffn_mfma_kernel<true, true> : ffn_mfma_kernel<true, false>,
+                           dim3((unsigned)blocks), dim3(256), kLdsBytes, s, xq, w, offsets,
+                           sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
         const long long blocks = 8 * ((mt_max * (d / 512) + 7) / 8);
-        (void)timed_launch("down_mfma", ffn_mfma_kernel<false>, dim3((unsigned)blocks), dim3(256), kLdsBytes, s, hq, w, offsets, sorted_rows, plan, tiles, nullptr, rows_out, T, d, E, k, f);
+        (void)timed_launch("down_mfma",
+                           single ? ffn_mfma_kernel<false, true> : ffn_mfma_kernel<false, false>,
+                           dim3((unsigned)blocks), dim3(256), kLdsBytes, s, hq, w, offsets,
+                           sorted_rows, plan, tiles, nullptr, rows_out, T, d, E, k, f);
     }
     return hipGetLastError();
 }

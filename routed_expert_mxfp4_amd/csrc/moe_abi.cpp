@@ -37,6 +37,7 @@ moe_status check_dims(const moe_dims *dm) {
     if (D.E > moe::kMaxExperts) return MOE_ERR_SHAPE;
     if (D.k > D.E || D.k > moe::kMaxTopK) return MOE_ERR_SHAPE;
     if ((int64_t)D.T * D.k >= kRowsLimit) return MOE_ERR_SHAPE;
+    if (D.act != MOE_ACT_BF16 && D.act != MOE_ACT_MX_E2M3) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -68,18 +69,22 @@ RouteWs route_ws(const moe_dims &D) {
 }
 
 struct FfnWs {
-    size_t plan, h, mfma, total;
+    size_t plan, h, mfma, xr, total;
 };
 FfnWs ffn_ws(const moe_dims &D) {
     FfnWs w;
     w.plan = 0;
     w.h = al256((size_t)(D.E + 1) * 4);
     w.mfma = w.h;
-    // the fp32 h of the GEMV path; the MFMA path keeps h split in its own ws
-    if (moe::mfma_path_ok(D.T, D.d, D.k, D.f))
+    w.xr = w.h;
+    // the fp32 h of the GEMV path (and, in the activation-MX mode, the
+    // rounded copy of x); the MFMA path keeps h split in its own ws
+    if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
         w.total = w.mfma + al256(moe::mfma_ws_bytes(D.T, D.d, D.E, D.k, D.f));
-    else
-        w.total = w.h + al256((size_t)D.T * D.k * D.f * 4);
+    } else {
+        w.xr = w.h + al256((size_t)D.T * D.k * D.f * 4);
+        w.total = w.xr + (D.act ? al256((size_t)D.T * D.d * 2) : 0);
+    }
     return w;
 }
 
@@ -279,14 +284,24 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x,
             if (e == hipSuccess) {
                 DiagScope t("mfma_ffn", s);
                 e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
-                                         base + L.mfma, D.T, D.d, D.E, D.k, D.f, s);
+                                         base + L.mfma, D.T, D.d, D.E, D.k, D.f,
+                                         D.act == MOE_ACT_MX_E2M3, s);
             }
             return device_status(e);
         }
-        if (e == hipSuccess) {
-            e = moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
-                                         D.f, s);
+        // activation-MX mode on the GEMV path: x rounded into a copy, h in place
+        const uint16_t *xa = x;
+        if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess) {
+            uint16_t *xr = reinterpret_cast<uint16_t *>(base + L.xr);
+            e = moe::launch_mx_round_bf16(x, D.T, D.d, xr, s);
+            xa = xr;
         }
+        if (e == hipSuccess) {
+            e = moe::launch_gemv_gate_up(xa, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E,
+                                         D.k, D.f, s);
+        }
+        if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess)
+            e = moe::launch_mx_round_f32(h, D.T * D.k, D.f, h, s);
         if (e == hipSuccess) {
             e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f, s);
         }
@@ -381,20 +396,31 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
             if (e == hipSuccess) {
                 DiagScope t("mfma_ffn", s);
                 e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
-                                         base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f, s);
+                                         base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f,
+                                         D.act == MOE_ACT_MX_E2M3, s);
             }
             if (e == hipSuccess) {
                 e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
             }
             return device_status(e);
         }
+        // activation-MX mode on the GEMV path: x rounded into a copy (the
+        // router above saw it as given), h in place
+        const uint16_t *xa = x;
+        if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess) {
+            uint16_t *xr = reinterpret_cast<uint16_t *>(base + L.ffn + F.xr);
+            e = moe::launch_mx_round_bf16(x, D.T, D.d, xr, s);
+            xa = xr;
+        }
         if (e == hipSuccess) {
-            e = token_fused ? moe::launch_gate_up_token(logits, x, W, ids, tw, counts, offsets,
+            e = token_fused ? moe::launch_gate_up_token(logits, xa, W, ids, tw, counts, offsets,
                                                         sorted_rows, row_pos, plan, h, D.d, D.E,
                                                         D.k, D.f, s)
-                            : moe::launch_gemv_gate_up(x, W, offsets, sorted_rows, plan, h, D.T,
+                            : moe::launch_gemv_gate_up(xa, W, offsets, sorted_rows, plan, h, D.T,
                                                        D.d, D.E, D.k, D.f, s);
         }
+        if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess)
+            e = moe::launch_mx_round_f32(h, D.T * D.k, D.f, h, s);
         if (D.T <= kFuseMaxT) {
             if (e == hipSuccess) {
                 e = moe::launch_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E, D.k, D.f, s);

@@ -221,9 +221,16 @@ hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
 // f % 256 == 0; ws of mfma_ws_bytes.
 bool mfma_path_ok(int T, int d, int k, int f);
 size_t mfma_ws_bytes(int T, int d, int E, int k, int f);
+// single: the activation-MX mode (one matrix pass with the hi terms).
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                            const int32_t *sorted_rows, const int32_t *plan, uint16_t *rows_out,
-                           void *ws, int T, int d, int E, int k, int f, hipStream_t s);
+                           void *ws, int T, int d, int E, int k, int f, bool single,
+                           hipStream_t s);
+// The activation-MX rounding of rows x K (K % 32 == 0): every 32-element
+// block to its one-term MX E2M3 value (out may be in).
+hipError_t launch_mx_round_bf16(const uint16_t *in, int rows, int K, uint16_t *out,
+                                hipStream_t st);
+hipError_t launch_mx_round_f32(const float *in, int rows, int K, float *out, hipStream_t st);
 // rows x K (K % 128 == 0) -> two-term MX E2M3 split rows, 208 bytes per row
 // and 128-element step (codes of both terms, then their E8M0 scales).
 size_t mx_split_bytes(int rows, int K);

@@ -28,7 +28,10 @@ class MoeError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
-                ("k", ctypes.c_int32), ("f", ctypes.c_int32)]
+                ("k", ctypes.c_int32), ("f", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
+ACT_BF16, ACT_MX_E2M3 = 0, 1          # MOE_ACT_* (include/moe.h)
 
 
 class Experts(ctypes.Structure):
@@ -134,8 +137,8 @@ def _check(status: int, where: str):
         raise MoeError(status, where)
 
 
-def dims_of(T, d, E, k, f) -> Dims:
-    return Dims(int(T), int(d), int(E), int(k), int(f))
+def dims_of(T, d, E, k, f, act=ACT_BF16) -> Dims:
+    return Dims(int(T), int(d), int(E), int(k), int(f), int(act))
 
 
 def experts_of(w: dict) -> Experts:
@@ -201,12 +204,14 @@ def moe_permute(topk_ids, E, ws=None, stream=None):
     return counts, offsets, sorted_rows, row_pos
 
 
-def moe_expert_ffn(x, experts: dict, offsets, sorted_rows, k, ws=None, stream=None):
-    """Expert FFN over grouped rows.  Returns rows_out bf16 [T*k][d]."""
+def moe_expert_ffn(x, experts: dict, offsets, sorted_rows, k, ws=None, stream=None,
+                   act=ACT_BF16):
+    """Expert FFN over grouped rows.  Returns rows_out bf16 [T*k][d].
+    act: ACT_BF16, or ACT_MX_E2M3 for the activation-MX mode."""
     x = _bits16(x)
     T, d = x.shape
     E, two_f = experts["gu_codes"].shape[:2]
-    dims = dims_of(T, d, E, k, two_f // 2)
+    dims = dims_of(T, d, E, k, two_f // 2, act)
     rows_out = torch.empty((T * k, d), dtype=torch.bfloat16, device=x.device)
     if ws is None:
         ws = workspace(dims, ENTRY_EXPERT_FFN, x.device)
@@ -235,7 +240,8 @@ class Layer:
     """Holds device pointers, dims and a reusable workspace for repeated
     ``moe_layer_forward`` calls (the benchmark's hot loop)."""
 
-    def __init__(self, experts: dict, router_w, k, router_bias=None, T=1):
+    def __init__(self, experts: dict, router_w, k, router_bias=None, T=1, act=ACT_BF16):
+        self.act = int(act)
         self.experts = experts
         self.router_w = _bits16(router_w)
         self.bias = None if router_bias is None else router_bias.contiguous().float()
@@ -249,7 +255,7 @@ class Layer:
 
     def reserve(self, T):
         if T > self._ws_T:
-            dims = dims_of(T, self.d, self.E, self.k, self.f)
+            dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
             self._ws = workspace(dims, ENTRY_LAYER_FORWARD, self.router_w.device)
             self._ws_T = T
 
@@ -258,7 +264,7 @@ class Layer:
         self.reserve(T)
         if y is None:
             y = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
-        dims = dims_of(T, self.d, self.E, self.k, self.f)
+        dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
         st = lib().moe_layer_forward(ctypes.byref(dims), _ptr(x), _ptr(self.router_w),
                                      _ptr(self.bias), ctypes.byref(self._ex), _ptr(y),
                                      _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
@@ -268,11 +274,12 @@ class Layer:
 
 
 def moe_layer_forward(x, router_w, experts: dict, k, router_bias=None, return_routing=False,
-                      stream=None):
-    """The whole layer.  Returns y bf16 [T][d] (and topk_ids, topk_w)."""
+                      stream=None, act=ACT_BF16):
+    """The whole layer.  Returns y bf16 [T][d] (and topk_ids, topk_w).
+    act: ACT_BF16, or ACT_MX_E2M3 for the activation-MX mode."""
     x = _bits16(x)
     T = x.shape[0]
-    layer = Layer(experts, router_w, k, router_bias, T=T)
+    layer = Layer(experts, router_w, k, router_bias, T=T, act=act)
     ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
     w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
     y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(L):
     assert set(declared) == set(moe.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_status_strings(L):
@@ -45,8 +45,8 @@ def test_status_strings(L):
     assert "unknown" in moe.status_str(99)
 
 
-def _dims(T=8, d=256, E=16, k=2, f=128):
-    return moe.dims_of(T, d, E, k, f)
+def _dims(T=8, d=256, E=16, k=2, f=128, act=0):
+    return moe.dims_of(T, d, E, k, f, act)
 
 
 def test_workspace_sizes(L):
@@ -59,11 +59,16 @@ def test_workspace_sizes(L):
     assert L.moe_workspace_bytes(ctypes.byref(_dims()), 17) == moe.SIZE_MAX
     with pytest.raises(moe.MoeError):
         moe.moe_workspace_bytes(_dims(d=100), 0)
+    # the activation-MX mode's GEMV path adds a rounded copy of x
+    plain = moe.moe_workspace_bytes(_dims(), moe.ENTRY_EXPERT_FFN)
+    amx = moe.moe_workspace_bytes(_dims(act=moe.ACT_MX_E2M3), moe.ENTRY_EXPERT_FFN)
+    assert amx >= plain + 8 * 256 * 2
 
 
 @pytest.mark.parametrize("bad", [dict(d=100), dict(d=0), dict(f=48), dict(E=0), dict(E=2000),
                                  dict(k=0), dict(k=17, E=16), dict(k=33, E=64), dict(T=-1),
-                                 dict(T=1 << 27, k=16), dict(d=65536)])
+                                 dict(T=1 << 27, k=16), dict(d=65536), dict(act=2),
+                                 dict(act=-1)])
 def test_bad_shapes_refused(L, bad):
     dims = _dims(**bad)
     P = ctypes.c_void_p(0x1000)

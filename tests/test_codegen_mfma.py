@@ -111,11 +111,16 @@ def gemm_asm():
         return open(out).read()
 
 
-def test_both_gemm_kernels_present(gemm_asm):
-    assert len(_kernels(gemm_asm)) == 2
+# <gate/up?, one term (activation-MX mode)?>
+KERNELS = ["ILb1ELb0E", "ILb1ELb1E", "ILb0ELb0E", "ILb0ELb1E"]
+KERNEL_IDS = ["gate_up", "gate_up_single", "down", "down_single"]
 
 
-@pytest.mark.parametrize("which", ["ILb1E", "ILb0E"], ids=["gate_up", "down"])
+def test_all_gemm_kernels_present(gemm_asm):
+    assert len(_kernels(gemm_asm)) == 4
+
+
+@pytest.mark.parametrize("which", KERNELS, ids=KERNEL_IDS)
 def test_main_loop_has_no_register_copies(gemm_asm, which):
     (lines,) = [v for k, v in _kernels(gemm_asm).items() if which in k]
     body, copies, dests, _ = _analyse(lines)
@@ -124,7 +129,7 @@ def test_main_loop_has_no_register_copies(gemm_asm, which):
     assert copies == [], copies[:5]
 
 
-@pytest.mark.parametrize("which", ["ILb1E", "ILb0E"], ids=["gate_up", "down"])
+@pytest.mark.parametrize("which", KERNELS, ids=KERNEL_IDS)
 def test_in_flight_registers_untouched_until_drained(gemm_asm, which):
     (lines,) = [v for k, v in _kernels(gemm_asm).items() if which in k]
     _, _, _, clobbers = _analyse(lines)
