@@ -85,6 +85,12 @@ def lib():
         L.orc_mx_quantize_block.argtypes = [i, P, P, P]
         L.orc_mx_split_block.restype = None
         L.orc_mx_split_block.argtypes = [i, P, P, P, P, P]
+        L.orc_rmsnorm.restype = None
+        L.orc_rmsnorm.argtypes = [i, i, P, P, ctypes.c_float, P]
+        L.orc_shared_expert_row.restype = None
+        L.orc_shared_expert_row.argtypes = [i, i, P, P, P, P, P]
+        L.orc_block_forward.restype = ctypes.c_int
+        L.orc_block_forward.argtypes = ([i] * 6 + [P, P, ctypes.c_float] + [P] * 14 + [i])
         _lib = L
     return _lib
 
@@ -243,6 +249,63 @@ def layer_forward(x, router_w, bias, gu_codes, gu_scales, dn_codes, dn_scales,
         raise MemoryError("oracle layer_forward: allocation failed")
     return {"logits": logits, "topk_ids": ids, "topk_w": w, "y64": y64,
             "y": yb}
+
+
+# ---- MoE tail ---------------------------------------------------------------------
+def rmsnorm(x, gamma, eps):
+    """xn (bf16 bits [T][d]) = RMSNorm(x) * gamma, canonical fp64 (see the C source)."""
+    x = _c(x, np.uint16)
+    gamma = _c(gamma, np.uint16)
+    T, d = x.shape
+    xn = np.empty((T, d), dtype=np.uint16)
+    lib().orc_rmsnorm(T, d, _p(x), _p(gamma), float(eps), _p(xn))
+    return xn
+
+
+def shared_expert_row(xn_row, sgu, sdn):
+    """The shared expert on one normalised row: returns (h, o) in fp64."""
+    xn_row = _c(xn_row, np.uint16)
+    sgu = _c(sgu, np.uint16)
+    sdn = _c(sdn, np.uint16)
+    d = xn_row.size
+    fs = sgu.shape[0] // 2
+    h = np.empty(fs, dtype=np.float64)
+    o = np.empty(d, dtype=np.float64)
+    lib().orc_shared_expert_row(d, fs, _p(xn_row), _p(sgu), _p(sdn), _p(h), _p(o))
+    return h, o
+
+
+def block_forward(x, gamma, eps, router_w, bias, gu_codes, gu_scales, dn_codes, dn_scales,
+                  sgu, sdn, k, n_threads=0):
+    """out = x + routed(xn) + shared(xn), xn = RMSNorm(x) * gamma (sgu None: no
+    shared expert).  Returns a dict with xn, logits, topk_ids, topk_w, out64, out."""
+    x = _c(x, np.uint16)
+    gamma = _c(gamma, np.uint16)
+    router_w = _c(router_w, np.uint16)
+    T, d = x.shape
+    E = router_w.shape[0]
+    f = gu_codes.shape[1] // 2
+    b = None if bias is None else _c(bias, np.float32)
+    ws = [_c(a, np.uint8) for a in (gu_codes, gu_scales, dn_codes, dn_scales)]
+    if sgu is None:
+        fs, sgu_a, sdn_a = 0, None, None
+    else:
+        sgu_a, sdn_a = _c(sgu, np.uint16), _c(sdn, np.uint16)
+        fs = sgu_a.shape[0] // 2
+    xn = np.empty((T, d), dtype=np.uint16)
+    logits = np.empty((T, E), dtype=np.float32)
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    out64 = np.empty((T, d), dtype=np.float64)
+    out = np.empty((T, d), dtype=np.uint16)
+    rc = lib().orc_block_forward(T, d, E, k, f, fs, _p(x), _p(gamma), float(eps),
+                                 _p(router_w), _p(b), *[_p(a) for a in ws], _p(sgu_a),
+                                 _p(sdn_a), _p(xn), _p(logits), _p(ids), _p(w), _p(out64),
+                                 _p(out), int(n_threads))
+    if rc != 0:
+        raise MemoryError("oracle block_forward: allocation failed")
+    return {"xn": xn, "logits": logits, "topk_ids": ids, "topk_w": w, "out64": out64,
+            "out": out}
 
 
 # ---- MX conversion model --------------------------------------------------------

@@ -505,3 +505,127 @@ void orc_mx_split_block(int fmt, const float *v, uint8_t *hi_scale,
         r[i] = a[i] - orc_elem_value(fmt, hi_codes[i]) * s;
     orc_mx_quantize_block(fmt, r, lo_scale, lo_codes);
 }
+
+/* ======================================================================= */
+/* MoE tail: RMSNorm before the router, the shared expert, residual add     */
+/* ======================================================================= */
+
+/* The pages' profile of the model-shape MoE tail names its steps: the
+ * weighted reduction, RMSNorm, the routed-up activation quantisation and
+ * the residual adds (Moonshine README, "Run layer-major prefill"); shared
+ * experts and norms sit in the Q8/BF16 static tier next to the routers,
+ * apart from the MXFP4 routed experts (Moonshine README, "How the engine
+ * works", tier diagram).  Readings where the pages are silent:
+ *   - pre-norm block: xn = RMSNorm(x) * gamma feeds both the router and the
+ *     experts, out = x + routed(xn) + shared(xn);
+ *   - RMSNorm: ss = sum of x_i^2 in the router's canonical order (64 equal
+ *     chunks summed in ascending order, chunk sums combined by the fixed
+ *     pairwise tree), ms = ss / d, den = sqrt(ms + eps), then
+ *     xn_i = bf16((x_i / den) * gamma_i), every step one IEEE fp64 operation
+ *     and the last rounding straight from fp64 to bf16 (RNE).  A fixed order
+ *     makes xn, and hence the routing, reproducible bit for bit;
+ *   - shared expert: one SwiGLU MLP of width fs with bf16 weights, gate =
+ *     rows [0, fs) and up = rows [fs, 2fs) of sgu [2fs][d], down sdn [d][fs];
+ *     always applied with weight 1, no biases;
+ *   - out = x + y + s summed in fp64 (y the routed weighted sum, s the shared
+ *     expert's output), rounded once to bf16. */
+void orc_rmsnorm(int T, int d, const uint16_t *x, const uint16_t *gamma, float eps,
+                 uint16_t *xn)
+{
+    const int P = d / 64;
+    for (int t = 0; t < T; ++t) {
+        const uint16_t *xr = x + (size_t)t * d;
+        double part[64];
+        for (int c = 0; c < 64; ++c) {
+            double s = 0.0;
+            for (int i = 0; i < P; ++i) {
+                double v = orc_bf16_value(xr[(size_t)c * P + (size_t)i]);
+                s = s + v * v;
+            }
+            part[c] = s;
+        }
+        for (int width = 1; width < 64; width *= 2)
+            for (int c = 0; c < 64; c += 2 * width)
+                part[c] = part[c] + part[c + width];
+        double ms = part[0] / (double)d;
+        double den = sqrt(ms + (double)eps);
+        for (int i = 0; i < d; ++i) {
+            double v = (orc_bf16_value(xr[i]) / den) * orc_bf16_value(gamma[i]);
+            xn[(size_t)t * d + i] = orc_round_to_bf16(v);
+        }
+    }
+}
+
+/* The shared expert on one normalised row: h_n = silu(g_n) * u_n with
+ * g_n = sum_k xn_k sgu[n][k], u_n = sum_k xn_k sgu[fs+n][k], then
+ * o[m] = sum_n h_n sdn[m][n]; fp64 with exact bf16 weights. */
+void orc_shared_expert_row(int d, int fs, const uint16_t *xn_row, const uint16_t *sgu,
+                           const uint16_t *sdn, double *h, double *o)
+{
+    for (int n = 0; n < fs; ++n) {
+        double g = 0.0, u = 0.0;
+        for (int kk = 0; kk < d; ++kk) {
+            double xv = orc_bf16_value(xn_row[kk]);
+            g = g + xv * orc_bf16_value(sgu[(size_t)n * d + kk]);
+            u = u + xv * orc_bf16_value(sgu[(size_t)(fs + n) * d + kk]);
+        }
+        h[n] = silu(g) * u;
+    }
+    for (int m = 0; m < d; ++m) {
+        double s = 0.0;
+        for (int n = 0; n < fs; ++n)
+            s = s + h[n] * orc_bf16_value(sdn[(size_t)m * fs + n]);
+        o[m] = s;
+    }
+}
+
+/* The block: xn = RMSNorm(x) * gamma; the routed layer on xn (router, top-k,
+ * experts, weighted combine, all as orc_layer_forward); the shared expert on
+ * xn (skipped when sgu is NULL, i.e. s = 0); out = x + y + s in fp64, then
+ * bf16.  xn_out, logits, topk_ids, topk_w and out64 are outputs as well.
+ * Returns 0, or -1 when a scratch allocation fails. */
+int orc_block_forward(int T, int d, int E, int k, int f, int fs, const uint16_t *x,
+                      const uint16_t *gamma, float eps, const uint16_t *router_w,
+                      const float *bias, const uint8_t *gu_codes, const uint8_t *gu_scales,
+                      const uint8_t *dn_codes, const uint8_t *dn_scales, const uint16_t *sgu,
+                      const uint16_t *sdn, uint16_t *xn_out, float *logits,
+                      int32_t *topk_ids, double *topk_w, double *out64, uint16_t *out_bf16,
+                      int n_threads)
+{
+    double *y = (double *)malloc(sizeof(double) * (size_t)T * d);
+    if (!y)
+        return -1;
+    orc_rmsnorm(T, d, x, gamma, eps, xn_out);
+    if (layer_forward_impl(T, d, E, k, f, 0, xn_out, router_w, bias, gu_codes, gu_scales,
+                           dn_codes, dn_scales, logits, topk_ids, topk_w, y, NULL,
+                           n_threads) != 0) {
+        free(y);
+        return -1;
+    }
+    int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int t = 0; t < T; ++t) {
+        double *s = (double *)calloc((size_t)d, sizeof(double));
+        double *h = (double *)malloc(sizeof(double) * (size_t)(fs > 0 ? fs : 1));
+        if (!s || !h) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            if (sgu)
+                orc_shared_expert_row(d, fs, xn_out + (size_t)t * d, sgu, sdn, h, s);
+            for (int m = 0; m < d; ++m) {
+                size_t i = (size_t)t * d + m;
+                double v = orc_bf16_value(x[i]) + y[i] + s[m];
+                if (out64)
+                    out64[i] = v;
+                if (out_bf16)
+                    out_bf16[i] = orc_round_to_bf16(v);
+            }
+        }
+        free(s);
+        free(h);
+    }
+    free(y);
+    return failed ? -1 : 0;
+}

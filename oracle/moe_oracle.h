@@ -80,6 +80,23 @@ int orc_layer_forward_act(int T, int d, int E, int k, int f, int act, const uint
                           float *logits, int32_t *topk_ids, double *topk_w,
                           double *y64, uint16_t *y_bf16, int n_threads);
 
+/* ---- MoE tail (pre-norm block around the routed layer) ---------------- */
+/* xn = bf16((x / sqrt(ss/d + eps)) * gamma) with ss the canonical chunked
+ * fp64 sum of squares (the router's order). */
+void orc_rmsnorm(int T, int d, const uint16_t *x, const uint16_t *gamma, float eps,
+                 uint16_t *xn);
+/* SwiGLU shared expert of width fs, bf16 weights sgu [2fs][d], sdn [d][fs]. */
+void orc_shared_expert_row(int d, int fs, const uint16_t *xn_row, const uint16_t *sgu,
+                           const uint16_t *sdn, double *h, double *o);
+/* out = x + routed(xn) + shared(xn) (sgu NULL: no shared expert). */
+int orc_block_forward(int T, int d, int E, int k, int f, int fs, const uint16_t *x,
+                      const uint16_t *gamma, float eps, const uint16_t *router_w,
+                      const float *bias, const uint8_t *gu_codes, const uint8_t *gu_scales,
+                      const uint8_t *dn_codes, const uint8_t *dn_scales, const uint16_t *sgu,
+                      const uint16_t *sdn, uint16_t *xn_out, float *logits,
+                      int32_t *topk_ids, double *topk_w, double *out64, uint16_t *out_bf16,
+                      int n_threads);
+
 /* ---- OCP MX conversion model (element formats below) ------------------- */
 enum { ORC_FMT_E4M3 = 0, ORC_FMT_E2M3 = 1, ORC_FMT_E2M1 = 2 };
 double orc_elem_value(int fmt, unsigned code);

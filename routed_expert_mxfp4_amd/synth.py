@@ -18,7 +18,10 @@ Distributions (one per tensor):
   codes      uniform bytes, i.e. both E2M1 nibbles uniform over 16 codes;
   scales     E8M0 codes uniform over 123..127 (scales 2^-4 .. 2^0);
   bias       Zipf-style skew b_e = -beta * s * ln(e + 1) (s = 1.1) for the
-             skewed prefill workload, none elsewhere.
+             skewed prefill workload, none elsewhere;
+  MoE tail (pre-norm block): gamma bf16 = 1 + N(0, 0.1^2) (RMSNorm weight),
+             eps = 1e-6, one shared expert of width f with bf16 gate/up
+             [2f][d] and down [d][f] weights ~ N(0, 1).
 
 Integer draws are exact on every device.  The normal draws use fp64
 log/sqrt/cos, which may differ in the last ulp between CPU builds; they are
@@ -38,6 +41,8 @@ MIX2 = 0x94D049BB133111EB
 
 TENSOR_X, TENSOR_WR, TENSOR_GU_CODES, TENSOR_GU_SCALES = 1, 2, 3, 4
 TENSOR_DN_CODES, TENSOR_DN_SCALES = 5, 6
+TENSOR_GAMMA, TENSOR_SHARED_GU, TENSOR_SHARED_DN = 7, 8, 9
+TAIL_EPS = 1e-6
 
 SCALE_CODE_LO, SCALE_CODE_N = 123, 5      # E8M0 codes 123..127
 
@@ -243,6 +248,21 @@ def gen_layer(cfg: Config, batch: int = 0, device="cpu") -> dict:
         d["bias"] = b.to(device)
     d.update(gen_experts(cfg, device=device))
     return d
+
+
+def gen_tail(cfg: Config, fs: int = 0, device="cpu") -> dict:
+    """The MoE tail's weights: RMSNorm weight gamma [d] and one shared expert of
+    width fs (default f): gate/up [2fs][d] and down [d][fs], all bf16, drawn on
+    the CPU and copied to ``device``; eps is the norm's epsilon."""
+    fs = fs or cfg.f
+    d = cfg.d
+    g = normals_bf16(stream_key(cfg.seed, TENSOR_GAMMA), 0, d, 0.1)
+    gamma = (1.0 + g.to(torch.float32)).to(torch.bfloat16)
+    sgu = normals_bf16(stream_key(cfg.seed, TENSOR_SHARED_GU), 0, 2 * fs * d, 1.0)
+    sdn = normals_bf16(stream_key(cfg.seed, TENSOR_SHARED_DN), 0, d * fs, 1.0)
+    return {"gamma": gamma.to(device), "eps": TAIL_EPS,
+            "shared_gu": sgu.view(2 * fs, d).to(device),
+            "shared_dn": sdn.view(d, fs).to(device)}
 
 
 def as_u16(t: torch.Tensor):

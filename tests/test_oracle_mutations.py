@@ -66,6 +66,21 @@ MUTATIONS = [
      "    if (act)\n        orc_mx_round(ORC_FMT_E2M3, d, xv);", ""),
     ("activation-MX mode: h not rounded",
      "    if (act)\n        orc_mx_round(ORC_FMT_E2M3, f, h);", ""),
+    ("RMSNorm eps outside the square root",
+     "double den = sqrt(ms + (double)eps);", "double den = sqrt(ms) + (double)eps;"),
+    ("RMSNorm sum instead of mean",
+     "double ms = part[0] / (double)d;", "double ms = part[0];"),
+    ("RMSNorm gamma dropped",
+     "double v = (orc_bf16_value(xr[i]) / den) * orc_bf16_value(gamma[i]);",
+     "double v = (orc_bf16_value(xr[i]) / den);"),
+    ("shared expert gate and up swapped",
+     "g = g + xv * orc_bf16_value(sgu[(size_t)n * d + kk]);",
+     "g = g + xv * orc_bf16_value(sgu[(size_t)(fs + n) * d + kk]);"),
+    ("residual dropped",
+     "double v = orc_bf16_value(x[i]) + y[i] + s[m];", "double v = y[i] + s[m];"),
+    ("block routes the raw input",
+     "layer_forward_impl(T, d, E, k, f, 0, xn_out, router_w",
+     "layer_forward_impl(T, d, E, k, f, 0, x, router_w"),
 ]
 
 
@@ -83,7 +98,7 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
     env = dict(os.environ, MOE_ORACLE_LIB=str(so))
     pins = [os.path.join(ROOT, "tests", f) for f in
             ("test_oracle_formats.py", "test_oracle_router.py",
-             "test_oracle_ffn.py", "test_oracle_mx.py")]
+             "test_oracle_ffn.py", "test_oracle_mx.py", "test_oracle_tail.py")]
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + pins,
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "no pin caught: " + name + "\n" + r.stdout[-2000:]
