@@ -9,7 +9,9 @@ call on one batch (router, top-k, grouping, gate/up + SwiGLU, down,
 combine), cycling through the batches so that no token is timed twice in a
 row.  Inputs are synthetic and resident in HBM before timing starts.  The
 other workloads (batched-decode T=64, zipf-prefill T=4096, long-prefill
-T=32768) time the same call on their own shapes.
+T=32768) time the same call on their own shapes.  ``--tail`` times the
+pre-norm block instead (moe_block_forward: RMSNorm before the router, a bf16
+shared expert and the residual add around the same routed layer).
 
 Prints one JSON line: throughput (tokens/s), the roofline of the dominant
 kernel (HIP events on the library's own stream inside the timed region):
@@ -41,6 +43,9 @@ KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm"
            "router_refine", "permute", "topk_permute", "gemv_gate_up",
            "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "down_mfma",
            "combine")
+# the pre-norm block's own kernels (--tail)
+TAIL_KERNELS = ("rmsnorm", "shared_gate_up", "shared_down_add", "shared_gemm_gate_up",
+                "shared_swiglu", "shared_gemm_down")
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 / MXFP6, published
 MFMA_MIN_T = 128                # the library's scaled-MFMA path starts here
 
@@ -58,6 +63,10 @@ def parse():
     ap.add_argument("--act", choices=("bf16", "mx"), default="bf16",
                     help="expert activations: bf16 (the W4A16 result; default) or mx (the "
                          "activation-MX mode: x and h rounded to one MX E2M3 term per 32)")
+    ap.add_argument("--tail", action="store_true",
+                    help="time the pre-norm MoE block (moe_block_forward: RMSNorm, the routed "
+                         "layer, a bf16 shared expert of width f, the residual add) instead of "
+                         "the routed layer alone")
     ap.add_argument("--cpu-sample", type=int, default=2,
                     help="tokens of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-breakdown", action="store_true",
@@ -198,7 +207,12 @@ def main():
     n_batches = min(cfg.batches, max(1, args.steps + args.warmup))
     xs = [synth.gen_x(cfg, b).to(dev) for b in range(n_batches)]
     act = moe.ACT_MX_E2M3 if args.act == "mx" else moe.ACT_BF16
-    layer = moe.Layer(experts, wr, cfg.k, bias, T=cfg.T, act=act)
+    if args.tail:
+        tail = {n: (v.to(dev) if hasattr(v, "to") else v)
+                for n, v in synth.gen_tail(cfg).items()}
+        layer = moe.Block(experts, wr, cfg.k, tail, bias, T=cfg.T, act=act)
+    else:
+        layer = moe.Layer(experts, wr, cfg.k, bias, T=cfg.T, act=act)
     y = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
@@ -207,17 +221,25 @@ def main():
     dims = moe.dims_of(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, act)
     ex = moe.experts_of(experts)
     ws = layer._ws
-    argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(wr.data_ptr()),
-                None if bias is None else ctypes.c_void_p(bias.data_ptr()), ctypes.byref(ex),
-                ctypes.c_void_p(y.data_ptr()), None, None, ctypes.c_void_p(ws.data_ptr()),
-                ws.numel(), sptr) for x in xs]
-    fwd = L.moe_layer_forward
+    bptr = None if bias is None else ctypes.c_void_p(bias.data_ptr())
+    if args.tail:
+        argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()), ctypes.byref(layer._tw),
+                    ctypes.c_void_p(wr.data_ptr()), bptr, ctypes.byref(ex),
+                    ctypes.c_void_p(y.data_ptr()), None, None, ctypes.c_void_p(ws.data_ptr()),
+                    ws.numel(), sptr) for x in xs]
+        fwd, fname = L.moe_block_forward, "moe_block_forward"
+    else:
+        argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()),
+                    ctypes.c_void_p(wr.data_ptr()), bptr, ctypes.byref(ex),
+                    ctypes.c_void_p(y.data_ptr()), None, None, ctypes.c_void_p(ws.data_ptr()),
+                    ws.numel(), sptr) for x in xs]
+        fwd, fname = L.moe_layer_forward, "moe_layer_forward"
 
     def run(n0, count):
         for i in range(count):
             st = fwd(*argsets[(n0 + i) % n_batches])
             if st != 0:
-                raise moe.MoeError(st, "moe_layer_forward")
+                raise moe.MoeError(st, fname)
 
     run(0, args.warmup)
     torch.cuda.synchronize()
@@ -237,7 +259,7 @@ def main():
     # ---- per-kernel breakdown (separate passes, outside the timed region) -------
     breakdown = {}
     if not args.no_breakdown:
-        for kname in KERNELS:
+        for kname in KERNELS + (TAIL_KERNELS if args.tail else ()):
             moe.diag_time_kernel(kname, capacity=max(1, args.steps))
             run(args.warmup, args.steps)
             torch.cuda.synchronize()
@@ -255,7 +277,10 @@ def main():
     per_expert_gu = 2 * cfg.f * (cfg.d // 2) + 2 * cfg.f * (cfg.d // 32)
     touched = []
     for b in range(min(n_batches, 64)):
-        layer.forward(xs[b], y=y, topk_ids=ids_probe)
+        if args.tail:
+            layer.forward(xs[b], out=y, topk_ids=ids_probe)
+        else:
+            layer.forward(xs[b], y=y, topk_ids=ids_probe)
         touched.append(torch.unique(ids_probe).numel())
     torch.cuda.synchronize()
     mean_touched = sum(touched) / len(touched)
@@ -307,6 +332,12 @@ def main():
                    "activations": ("MX E2M3, one term per 32 (activation-MX mode)" if act
                                    else "bf16"), "accumulate": "fp32",
                    "expert_path": "scaled MFMA" if mfma else "GEMV"},
+        "block": (None if not args.tail else {
+            "entry": "moe_block_forward",
+            "steps": "RMSNorm (canonical fp64) -> routed layer on xn -> bf16 SwiGLU shared "
+                     "expert of width f -> residual add",
+            "shared_expert_bytes": 3 * cfg.d * cfg.f * 2,
+            "norm_bytes_per_token": 2 * 2 * cfg.d}),
         "expert_weight_GBps": layer_bytes * args.steps / elapsed / 1e9,
         "expert_weight_hbm_frac": layer_bytes * args.steps / elapsed / 1e9 / HBM_PEAK_GBPS,
         "tflops": layer_flops * args.steps / elapsed / 1e12,
@@ -317,6 +348,8 @@ def main():
     }
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+        if args.tail:
+            out["cpu_baseline"]["note"] = "the routed layer's oracle (the block's dominant work)"
     print(json.dumps(out))
 
 

@@ -2,8 +2,10 @@
 
     python -m routed_expert_mxfp4_amd.build
 
-Sources: ``csrc/*.hip`` (kernels) and ``csrc/moe_abi.cpp`` (the C ABI of
-``include/moe.h``).  Objects go to ``_build/`` at the repository root.
+Sources: ``csrc/*.hip`` (kernels), ``csrc/moe_abi.cpp`` (the C ABI of
+``include/moe.h`` and ``include/moe_tail.h``) and ``csrc/blas.cpp`` (the
+shared expert's library GEMMs; links rocBLAS).  Objects go to ``_build/`` at
+the repository root.
 """
 from __future__ import annotations
 
@@ -33,8 +35,8 @@ FLAGS = [
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [
-        os.path.join(CSRC, "moe_abi.cpp")]
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(
+        glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src: str) -> str:
@@ -59,7 +61,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib")
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + [
+        "-L" + rocm_lib, "-Wl,-rpath," + rocm_lib, "-lrocblas"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -5,6 +5,11 @@
 // Moonshine README, "Run layer-major prefill").  Each thread owns 8
 // consecutive outputs of one token, so every y element has exactly one
 // writer (no atomics) and all loads and stores are 16 bytes wide.
+//
+// In the pre-norm block the same pass also does the tail's adds: with resid
+// (bf16 [T][d], the block input) and extra (fp32 [T][d], the shared expert's
+// output; NULL: none) the accumulator starts at resid + extra, so
+// out = bf16(x + s + sum_j w_j rows_j) is written once.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -13,6 +18,8 @@ namespace {
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ rows_out,
                                                       const int32_t *__restrict__ row_pos,
                                                       const float *__restrict__ topk_w,
+                                                      const uint16_t *__restrict__ resid,
+                                                      const float *__restrict__ extra,
                                                       uint16_t *__restrict__ y, int T, int d,
                                                       int k) {
     const int t = blockIdx.y;
@@ -20,6 +27,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
     if (v >= (d >> 3)) return;
     const int nrows = T * k;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (resid) {
+        const uint4 r = reinterpret_cast<const uint4 *>(resid + (size_t)t * d)[v];
+        float4 e0 = {0.f, 0.f, 0.f, 0.f}, e1 = e0;
+        if (extra) {
+            const float4 *e = reinterpret_cast<const float4 *>(extra + (size_t)t * d) + 2 * v;
+            e0 = e[0];
+            e1 = e[1];
+        }
+        const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+        const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] = bf16_bits_to_f32(rw[i] & 0xFFFFu) + ev[2 * i];
+            acc[2 * i + 1] = bf16_bits_to_f32(rw[i] >> 16) + ev[2 * i + 1];
+        }
+    }
     // slots in groups of 8: all loads of a group are issued before use
     for (int j0 = 0; j0 < k; j0 += 8) {
         uint4 q[8];
@@ -57,10 +80,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 
 hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
                           const float *topk_w, uint16_t *y, int T, int d, int k,
-                          hipStream_t s) {
+                          hipStream_t s, const uint16_t *resid, const float *extra) {
     if (T <= 0) return hipSuccess;
     dim3 grid(((d >> 3) + 255) / 256, T);
-    (void)timed_launch("combine", combine_kernel, dim3(grid), dim3(256), 0, s, rows_out, row_pos, topk_w, y, T, d, k);
+    (void)timed_launch("combine", combine_kernel, dim3(grid), dim3(256), 0, s, rows_out, row_pos,
+                       topk_w, resid, extra, y, T, d, k);
     return hipGetLastError();
 }
 

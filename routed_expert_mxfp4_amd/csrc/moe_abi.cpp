@@ -6,10 +6,12 @@
 // synchronises the host with the device, and never lets a C++ exception out.
 #include "../../include/moe.h"
 #include "../../include/moe_diag.h"
+#include "../../include/moe_tail.h"
 
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -120,6 +122,43 @@ struct Diag {
 };
 Diag g_diag;
 
+// Pre-norm block: the routed layer's scratch, then xn; few tokens: the
+// routed output y and the shared expert's fp32 h; many tokens: the shared
+// expert's gate/up GEMM output (fp32), its bf16 h and its down output (fp32).
+struct BlockWs {
+    size_t layer, xn, yr, hs, gu, hb, sx, total;
+};
+BlockWs block_ws(const moe_dims &D, int fs) {
+    BlockWs w;
+    const size_t T = (size_t)D.T, d = (size_t)D.d;
+    size_t p = 0;
+    w.layer = p; p += layer_ws(D).total;
+    w.xn = p; p += al256(T * d * 2);
+    w.yr = w.hs = w.gu = w.hb = w.sx = p;
+    if (D.T <= moe::kSharedGemvMaxT) {
+        w.yr = p; p += al256(T * d * 2);
+        w.hs = p; p += al256(T * (size_t)fs * 4);
+    } else if (fs > 0) {
+        w.gu = p; p += al256(T * 2 * (size_t)fs * 4);
+        w.hb = p; p += al256(T * (size_t)fs * 2);
+        w.sx = p; p += al256(T * d * 4);
+    }
+    w.total = p;
+    return w;
+}
+
+moe_status check_tail(const moe_tail_weights *tw) {
+    if (!tw) return MOE_ERR_NULL;
+    if (!tw->norm_w) return MOE_ERR_NULL;
+    if (!std::isfinite(tw->eps) || tw->eps < 0.f) return MOE_ERR_SHAPE;
+    if (tw->fs < 0 || tw->fs > 16384 || tw->fs % 32 != 0) return MOE_ERR_SHAPE;
+    if (tw->fs > 0 && (!tw->shared_gu || !tw->shared_dn)) return MOE_ERR_NULL;
+    if (!aligned16(tw->norm_w)) return MOE_ERR_ALIGN;
+    if (tw->fs > 0 && (!aligned16(tw->shared_gu) || !aligned16(tw->shared_dn)))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
 template <typename Fn>
 moe_status guarded(Fn fn) {
     try {
@@ -158,6 +197,116 @@ void diag_launch_events(const char *kernel, hipEvent_t *start, hipEvent_t *stop)
 }  // namespace moe
 
 using moe::DiagScope;
+
+namespace {
+
+// The routed layer (steps 1-5 of moe.h) on validated arguments, its scratch
+// at base (layout layer_ws).  resid / extra (nullable, only with
+// D.T > kFuseMaxT): the pre-norm block's residual (bf16 [T][d]) and
+// shared-expert output (fp32 [T][d]) added in the combine pass.
+hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *router_w,
+                     const float *router_bias, const moe_mxfp4_experts &experts, uint16_t *y,
+                     int32_t *topk_ids_out, float *topk_w_out, char *base, hipStream_t s,
+                     const uint16_t *resid, const float *extra) {
+    const LayerWs L = layer_ws(D);
+    const RouteWs RW = route_ws(D);
+    float *logits = reinterpret_cast<float *>(base + L.route + RW.logits);
+    int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(base + L.ids);
+    float *tw = topk_w_out ? topk_w_out : reinterpret_cast<float *>(base + L.tw);
+    int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *sorted_rows = reinterpret_cast<int32_t *>(base + L.sorted_rows);
+    int32_t *row_pos = reinterpret_cast<int32_t *>(base + L.row_pos);
+    void *perm_ws = base + L.perm;
+    const FfnWs F = ffn_ws(D);
+    int32_t *plan = reinterpret_cast<int32_t *>(base + L.ffn + F.plan);
+    float *h = reinterpret_cast<float *>(base + L.ffn + F.h);
+    uint16_t *rows_out = reinterpret_cast<uint16_t *>(base + L.rows_out);
+    const ExpertArgs W{experts.gu_codes, experts.gu_scales, experts.dn_codes,
+                       experts.dn_scales};
+
+    hipError_t e;
+    const bool filtered = moe::route_filter_ok(D.T, D.d, D.E);
+    // one token: top-k and grouping run inside the gate/up pass
+    const bool token_fused =
+        !filtered && moe::gate_up_token_fusable(D.T, D.d, D.E, D.k, D.f);
+    if (filtered) {
+        e = moe::launch_route_filtered(x, router_w, router_bias, logits,
+                                       reinterpret_cast<float *>(base + L.route + RW.nx),
+                                       reinterpret_cast<float *>(base + L.route + RW.nw), ids,
+                                       tw, D.T, D.d, D.E, D.k, s);
+    } else {
+        e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
+    }
+    if (filtered) {
+        if (e == hipSuccess) {
+            DiagScope t("permute", s);
+            e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
+                                    D.E, D.k, perm_ws, s);
+        }
+    } else if (token_fused) {
+    } else if (moe::topk_permute_fusable(D.T, D.E, D.k)) {
+        if (e == hipSuccess) {
+            e = moe::launch_topk_permute_small(logits, ids, tw, counts, offsets, sorted_rows,
+                                               row_pos, plan, D.T, D.E, D.k, s);
+        }
+    } else {
+        if (e == hipSuccess) {
+            e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
+        }
+        if (e == hipSuccess) {
+            DiagScope t("permute", s);
+            e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
+                                    D.E, D.k, perm_ws, s);
+        }
+    }
+    if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
+        if (e == hipSuccess) {
+            DiagScope t("mfma_ffn", s);
+            e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
+                                     base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f,
+                                     D.act == MOE_ACT_MX_E2M3, s);
+        }
+        if (e == hipSuccess) {
+            e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s, resid, extra);
+        }
+        return e;
+    }
+    // activation-MX mode on the GEMV path: x rounded into a copy (the
+    // router above saw it as given), h in place
+    const uint16_t *xa = x;
+    if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess) {
+        uint16_t *xr = reinterpret_cast<uint16_t *>(base + L.ffn + F.xr);
+        e = moe::launch_mx_round_bf16(x, D.T, D.d, xr, s);
+        xa = xr;
+    }
+    if (e == hipSuccess) {
+        e = token_fused ? moe::launch_gate_up_token(logits, xa, W, ids, tw, counts, offsets,
+                                                    sorted_rows, row_pos, plan, h, D.d, D.E,
+                                                    D.k, D.f, s)
+                        : moe::launch_gemv_gate_up(xa, W, offsets, sorted_rows, plan, h, D.T,
+                                                   D.d, D.E, D.k, D.f, s);
+    }
+    if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess)
+        e = moe::launch_mx_round_f32(h, D.T * D.k, D.f, h, s);
+    if (D.T <= kFuseMaxT) {
+        if (e == hipSuccess) {
+            e = moe::launch_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E, D.k, D.f, s);
+        }
+    } else {
+        if (e == hipSuccess) {
+            e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f,
+                                      s);
+        }
+        if (e == hipSuccess) {
+            e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s, resid, extra);
+        }
+    }
+    return e;
+}
+
+}  // namespace
+
 
 extern "C" {
 
@@ -339,101 +488,89 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
         if (!ws) return MOE_ERR_NULL;
         if (!aligned16(ws)) return MOE_ERR_ALIGN;
         if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-        char *base = static_cast<char *>(ws);
-        const RouteWs RW = route_ws(D);
-        float *logits = reinterpret_cast<float *>(base + L.route + RW.logits);
-        int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(base + L.ids);
-        float *tw = topk_w_out ? topk_w_out : reinterpret_cast<float *>(base + L.tw);
-        int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
-        int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
-        int32_t *sorted_rows = reinterpret_cast<int32_t *>(base + L.sorted_rows);
-        int32_t *row_pos = reinterpret_cast<int32_t *>(base + L.row_pos);
-        void *perm_ws = base + L.perm;
-        const FfnWs F = ffn_ws(D);
-        int32_t *plan = reinterpret_cast<int32_t *>(base + L.ffn + F.plan);
-        float *h = reinterpret_cast<float *>(base + L.ffn + F.h);
-        uint16_t *rows_out = reinterpret_cast<uint16_t *>(base + L.rows_out);
-        const ExpertArgs W{experts->gu_codes, experts->gu_scales, experts->dn_codes,
-                           experts->dn_scales};
-        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        return device_status(run_layer(D, x, router_w, router_bias, *experts, y, topk_ids_out,
+                                       topk_w_out, static_cast<char *>(ws),
+                                       static_cast<hipStream_t>(hip_stream), nullptr, nullptr));
+    });
+}
 
-        hipError_t e;
-        const bool filtered = moe::route_filter_ok(D.T, D.d, D.E);
-        // one token: top-k and grouping run inside the gate/up pass
-        const bool token_fused =
-            !filtered && moe::gate_up_token_fusable(D.T, D.d, D.E, D.k, D.f);
-        if (filtered) {
-            e = moe::launch_route_filtered(x, router_w, router_bias, logits,
-                                           reinterpret_cast<float *>(base + L.route + RW.nx),
-                                           reinterpret_cast<float *>(base + L.route + RW.nw), ids,
-                                           tw, D.T, D.d, D.E, D.k, s);
-        } else {
-            e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
-        }
-        if (filtered) {
-            if (e == hipSuccess) {
-                DiagScope t("permute", s);
-                e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
-                                        D.E, D.k, perm_ws, s);
-            }
-        } else if (token_fused) {
-        } else if (moe::topk_permute_fusable(D.T, D.E, D.k)) {
-            if (e == hipSuccess) {
-                e = moe::launch_topk_permute_small(logits, ids, tw, counts, offsets, sorted_rows,
-                                                   row_pos, plan, D.T, D.E, D.k, s);
-            }
-        } else {
-            if (e == hipSuccess) {
-                e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
-            }
-            if (e == hipSuccess) {
-                DiagScope t("permute", s);
-                e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
-                                        D.E, D.k, perm_ws, s);
-            }
-        }
-        if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
-            if (e == hipSuccess) {
-                DiagScope t("mfma_ffn", s);
-                e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
-                                         base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f,
-                                         D.act == MOE_ACT_MX_E2M3, s);
-            }
-            if (e == hipSuccess) {
-                e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
-            }
+size_t moe_block_workspace_bytes(const moe_dims *dims, const moe_tail_weights *tail) {
+    if (check_dims(dims) != MOE_OK || check_tail(tail) != MOE_OK) return (size_t)-1;
+    return block_ws(*dims, tail->fs).total;
+}
+
+moe_status moe_rmsnorm(const moe_dims *dims, const uint16_t *x, const uint16_t *gamma,
+                       float eps, uint16_t *xn, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (!std::isfinite(eps) || eps < 0.f) return MOE_ERR_SHAPE;
+        if (D.T == 0) return MOE_OK;
+        if (!x || !gamma || !xn) return MOE_ERR_NULL;
+        if (!aligned16(x) || !aligned16(gamma) || !aligned16(xn)) return MOE_ERR_ALIGN;
+        return device_status(moe::launch_rmsnorm(x, gamma, eps, xn, D.T, D.d,
+                                                 static_cast<hipStream_t>(hip_stream)));
+    });
+}
+
+moe_status moe_block_forward(const moe_dims *dims, const uint16_t *x,
+                             const moe_tail_weights *tail, const uint16_t *router_w,
+                             const float *router_bias, const moe_mxfp4_experts *experts,
+                             uint16_t *out, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                             size_t ws_bytes, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        if ((st = check_tail(tail)) != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (D.T == 0) return MOE_OK;
+        if (!x || !router_w || !out) return MOE_ERR_NULL;
+        if ((st = check_experts(experts)) != MOE_OK) return st;
+        if (!aligned16(x) || !aligned16(router_w) || !aligned16(out)) return MOE_ERR_ALIGN;
+        if (x == out) return MOE_ERR_UNSUPPORTED;
+        const int fs = tail->fs;
+        const BlockWs B = block_ws(D, fs);
+        if (!ws) return MOE_ERR_NULL;
+        if (!aligned16(ws)) return MOE_ERR_ALIGN;
+        if (ws_bytes < B.total) return MOE_ERR_WORKSPACE;
+        char *base = static_cast<char *>(ws);
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        uint16_t *xn = reinterpret_cast<uint16_t *>(base + B.xn);
+        hipError_t e = moe::launch_rmsnorm(x, tail->norm_w, tail->eps, xn, D.T, D.d, s);
+        if (D.T <= moe::kSharedGemvMaxT) {
+            // few tokens: the routed output first, then the shared expert's
+            // GEMVs, whose down pass adds x and y
+            uint16_t *yr = reinterpret_cast<uint16_t *>(base + B.yr);
+            if (e == hipSuccess)
+                e = run_layer(D, xn, router_w, router_bias, *experts, yr, topk_ids_out,
+                              topk_w_out, base + B.layer, s, nullptr, nullptr);
+            if (e == hipSuccess)
+                e = moe::launch_shared_gemv(xn, tail->shared_gu, tail->shared_dn, x, yr,
+                                            reinterpret_cast<float *>(base + B.hs), out, D.T,
+                                            D.d, fs, s);
             return device_status(e);
         }
-        // activation-MX mode on the GEMV path: x rounded into a copy (the
-        // router above saw it as given), h in place
-        const uint16_t *xa = x;
-        if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess) {
-            uint16_t *xr = reinterpret_cast<uint16_t *>(base + L.ffn + F.xr);
-            e = moe::launch_mx_round_bf16(x, D.T, D.d, xr, s);
-            xa = xr;
-        }
-        if (e == hipSuccess) {
-            e = token_fused ? moe::launch_gate_up_token(logits, xa, W, ids, tw, counts, offsets,
-                                                        sorted_rows, row_pos, plan, h, D.d, D.E,
-                                                        D.k, D.f, s)
-                            : moe::launch_gemv_gate_up(xa, W, offsets, sorted_rows, plan, h, D.T,
-                                                       D.d, D.E, D.k, D.f, s);
-        }
-        if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess)
-            e = moe::launch_mx_round_f32(h, D.T * D.k, D.f, h, s);
-        if (D.T <= kFuseMaxT) {
+        // many tokens: the shared expert on the library GEMM, then the routed
+        // layer, whose combine pass adds x and the shared output
+        float *sx = nullptr;
+        if (fs > 0) {
+            float *gu = reinterpret_cast<float *>(base + B.gu);
+            uint16_t *hb = reinterpret_cast<uint16_t *>(base + B.hb);
+            sx = reinterpret_cast<float *>(base + B.sx);
             if (e == hipSuccess) {
-                e = moe::launch_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E, D.k, D.f, s);
+                DiagScope t("shared_gemm_gate_up", s);
+                e = moe::blas_gemm_bf16_nt(xn, tail->shared_gu, gu, D.T, 2 * fs, D.d, s);
             }
-        } else {
+            if (e == hipSuccess) e = moe::launch_shared_swiglu(gu, hb, D.T, fs, s);
             if (e == hipSuccess) {
-                e = moe::launch_gemv_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f,
-                                          s);
-            }
-            if (e == hipSuccess) {
-                e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
+                DiagScope t("shared_gemm_down", s);
+                e = moe::blas_gemm_bf16_nt(hb, tail->shared_dn, sx, D.T, D.d, fs, s);
             }
         }
+        if (e == hipSuccess)
+            e = run_layer(D, xn, router_w, router_bias, *experts, out, topk_ids_out, topk_w_out,
+                          base + B.layer, s, x, sx);
         return device_status(e);
     });
 }

@@ -237,8 +237,29 @@ size_t mx_split_bytes(int rows, int K);
 hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, hipStream_t st);
 hipError_t launch_mx_split_f32(const float *in, int rows, int K, uint8_t *q, hipStream_t st);
 
+// resid (bf16 [T][d]) and extra (fp32 [T][d], needs resid; either may be
+// NULL): the pre-norm block's residual and shared-expert terms, added in the
+// same pass.
 hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
                           const float *topk_w, uint16_t *y, int T, int d, int k,
-                          hipStream_t s);
+                          hipStream_t s, const uint16_t *resid = nullptr,
+                          const float *extra = nullptr);
+
+// ---- MoE tail (tail.hip, blas.cpp) --------------------------------------------
+// xn = bf16(RMSNorm(x) * gamma), canonical fp64 order, one wave per token.
+hipError_t launch_rmsnorm(const uint16_t *x, const uint16_t *gamma, float eps, uint16_t *xn,
+                          int T, int d, hipStream_t s);
+// Few tokens (1 <= T <= kSharedGemvMaxT): shared expert GEMVs, the down pass
+// writing out = bf16(xres + yr + shared(xn)); h: fp32 [T][fs] scratch.
+constexpr int kSharedGemvMaxT = 8;
+hipError_t launch_shared_gemv(const uint16_t *xn, const uint16_t *sgu, const uint16_t *sdn,
+                              const uint16_t *xres, const uint16_t *yr, float *h, uint16_t *out,
+                              int T, int d, int fs, hipStream_t s);
+// h = bf16(silu(gu[:, :fs]) * gu[:, fs:]) for gu fp32 [T][2fs].
+hipError_t launch_shared_swiglu(const float *gu, uint16_t *h, int T, int fs, hipStream_t s);
+// Row-major c[M][N] (fp32) = a[M][K] (bf16) * b[N][K]^T (bf16), fp32
+// accumulate, on the library GEMM (rocBLAS) of the current device.
+hipError_t blas_gemm_bf16_nt(const uint16_t *a, const uint16_t *b, float *c, int M, int N,
+                             int K, hipStream_t s);
 
 }  // namespace moe

@@ -1,4 +1,5 @@
-"""Thin Python binding of the C ABI in ``include/moe.h``.
+"""Thin Python binding of the C ABI in ``include/moe.h`` and
+``include/moe_tail.h``.
 
 Argument marshalling only: every step of the layer runs in the HIP kernels
 of ``libmoe_mxfp4.so``.  Torch supplies device memory (outputs and
@@ -39,9 +40,15 @@ class Experts(ctypes.Structure):
                 ("dn_codes", ctypes.c_void_p), ("dn_scales", ctypes.c_void_p)]
 
 
+class TailWeights(ctypes.Structure):
+    _fields_ = [("norm_w", ctypes.c_void_p), ("eps", ctypes.c_float), ("fs", ctypes.c_int32),
+                ("shared_gu", ctypes.c_void_p), ("shared_dn", ctypes.c_void_p)]
+
+
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_diag_time_kernel", "moe_diag_kernel_time", "moe_diag_mx_split_e2m3")
+           "moe_diag_time_kernel", "moe_diag_kernel_time", "moe_diag_mx_split_e2m3",
+           "moe_block_workspace_bytes", "moe_rmsnorm", "moe_block_forward")
 
 _lib = None
 
@@ -74,6 +81,13 @@ def lib():
         L.moe_combine.argtypes = [DP, P, P, P, P, P]
         L.moe_layer_forward.restype = I
         L.moe_layer_forward.argtypes = [DP, P, P, P, EP, P, P, P, P, S, P]
+        TP = ctypes.POINTER(TailWeights)
+        L.moe_block_workspace_bytes.restype = S
+        L.moe_block_workspace_bytes.argtypes = [DP, TP]
+        L.moe_rmsnorm.restype = I
+        L.moe_rmsnorm.argtypes = [DP, P, P, ctypes.c_float, P, P]
+        L.moe_block_forward.restype = I
+        L.moe_block_forward.argtypes = [DP, P, TP, P, P, EP, P, P, P, P, S, P]
         L.moe_diag_time_kernel.restype = I
         L.moe_diag_time_kernel.argtypes = [ctypes.c_char_p, I]
         L.moe_diag_mx_split_e2m3.restype = I
@@ -284,3 +298,83 @@ def moe_layer_forward(x, router_w, experts: dict, k, router_bias=None, return_ro
     w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
     y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)
     return (y, ids, w) if return_routing else y
+
+
+# ---- MoE tail (include/moe_tail.h) ------------------------------------------------
+def tail_of(tail: dict) -> TailWeights:
+    """tail: {"gamma": bf16 [d], "eps": float, "shared_gu": bf16 [2fs][d] or None,
+    "shared_dn": bf16 [d][fs] or None}."""
+    sgu, sdn = tail.get("shared_gu"), tail.get("shared_dn")
+    fs = 0 if sgu is None else sgu.shape[0] // 2
+    return TailWeights(tail["gamma"].data_ptr(), float(tail["eps"]), int(fs),
+                       None if sgu is None else sgu.data_ptr(),
+                       None if sdn is None else sdn.data_ptr())
+
+
+def moe_rmsnorm(x, gamma, eps, stream=None):
+    """xn bf16 [T][d] = RMSNorm(x) * gamma (canonical fp64 order, bit-exact)."""
+    x = _bits16(x)
+    T, d = x.shape
+    dims = dims_of(T, d, 1, 1, 32)
+    xn = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+    st = lib().moe_rmsnorm(ctypes.byref(dims), _ptr(x), _ptr(_bits16(gamma)), float(eps),
+                           _ptr(xn), _stream(stream))
+    _check(st, "moe_rmsnorm")
+    return xn
+
+
+class Block:
+    """Device pointers, dims and a reusable workspace for repeated
+    ``moe_block_forward`` calls: out = x + routed(xn) + shared(xn),
+    xn = RMSNorm(x) * gamma."""
+
+    def __init__(self, experts: dict, router_w, k, tail: dict, router_bias=None, T=1,
+                 act=ACT_BF16):
+        self.act = int(act)
+        self.experts = experts
+        self.tail = tail
+        self.router_w = _bits16(router_w)
+        self.bias = None if router_bias is None else router_bias.contiguous().float()
+        self.E, self.d = self.router_w.shape
+        self.f = experts["gu_codes"].shape[1] // 2
+        self.k = k
+        self._ex = experts_of(experts)
+        self._tw = tail_of(tail)
+        self._ws = None
+        self._ws_T = -1
+        self.reserve(T)
+
+    def reserve(self, T):
+        if T > self._ws_T:
+            dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
+            n = lib().moe_block_workspace_bytes(ctypes.byref(dims), ctypes.byref(self._tw))
+            if n == SIZE_MAX:
+                raise MoeError(MOE_ERR_SHAPE, "moe_block_workspace_bytes")
+            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.router_w.device)
+            self._ws_T = T
+
+    def forward(self, x, out=None, topk_ids=None, topk_w=None, stream=None):
+        x = _bits16(x)
+        T = x.shape[0]
+        self.reserve(T)
+        if out is None:
+            out = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
+        dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
+        st = lib().moe_block_forward(ctypes.byref(dims), _ptr(x), ctypes.byref(self._tw),
+                                     _ptr(self.router_w), _ptr(self.bias), ctypes.byref(self._ex),
+                                     _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
+                                     self._ws.numel(), _stream(stream))
+        _check(st, "moe_block_forward")
+        return out
+
+
+def moe_block_forward(x, router_w, experts: dict, k, tail: dict, router_bias=None,
+                      return_routing=False, stream=None, act=ACT_BF16):
+    """The pre-norm MoE block.  Returns out bf16 [T][d] (and topk_ids, topk_w)."""
+    x = _bits16(x)
+    T = x.shape[0]
+    blk = Block(experts, router_w, k, tail, router_bias, T=T, act=act)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
+    out = blk.forward(x, topk_ids=ids, topk_w=w, stream=stream)
+    return (out, ids, w) if return_routing else out

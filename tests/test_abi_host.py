@@ -134,3 +134,50 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         moe.lib()
+
+
+def test_tail_entries_refuse_bad_arguments(L):
+    dims = _dims()
+    A = ctypes.c_void_p(0x10000)
+    M = ctypes.c_void_p(0x10008)
+    B = ctypes.c_void_p(0x20000)          # an output that does not alias x
+    ex = moe.Experts(0x10000, 0x10000, 0x10000, 0x10000)
+    tw = moe.TailWeights(0x10000, 1e-6, 64, 0x10000, 0x10000)
+    big = 1 << 40
+    ws = L.moe_block_workspace_bytes
+    assert ws(ctypes.byref(dims), ctypes.byref(tw)) not in (0, moe.SIZE_MAX)
+    assert ws(ctypes.byref(dims), None) == moe.SIZE_MAX
+    for bad in (moe.TailWeights(0x10000, 1e-6, 48, 0x10000, 0x10000),      # fs % 32
+                moe.TailWeights(0x10000, -1.0, 64, 0x10000, 0x10000),      # eps < 0
+                moe.TailWeights(0x10000, float("nan"), 64, 0x10000, 0x10000),
+                moe.TailWeights(0x10000, 1e-6, 16384 + 32, 0x10000, 0x10000)):
+        assert ws(ctypes.byref(dims), ctypes.byref(bad)) == moe.SIZE_MAX
+    # no shared expert is valid and needs no shared pointers
+    none = moe.TailWeights(0x10000, 1e-6, 0, None, None)
+    assert ws(ctypes.byref(dims), ctypes.byref(none)) != moe.SIZE_MAX
+    f = L.moe_block_forward
+    need = ws(ctypes.byref(dims), ctypes.byref(tw))
+    call = lambda x, t, rw, e, out, w, n: f(ctypes.byref(dims), x, t, rw, None, e, out, None, None,
+                                            w, n, None)
+    assert call(None, ctypes.byref(tw), A, ctypes.byref(ex), B, A, big) == moe.MOE_ERR_NULL
+    assert call(A, None, A, ctypes.byref(ex), B, A, big) == moe.MOE_ERR_NULL
+    assert call(A, ctypes.byref(tw), A, ctypes.byref(ex), None, A, big) == moe.MOE_ERR_NULL
+    nog = moe.TailWeights(None, 1e-6, 64, 0x10000, 0x10000)
+    assert call(A, ctypes.byref(nog), A, ctypes.byref(ex), B, A, big) == moe.MOE_ERR_NULL
+    nos = moe.TailWeights(0x10000, 1e-6, 64, None, 0x10000)
+    assert call(A, ctypes.byref(nos), A, ctypes.byref(ex), B, A, big) == moe.MOE_ERR_NULL
+    mis = moe.TailWeights(0x10000, 1e-6, 64, 0x10008, 0x10000)
+    assert call(A, ctypes.byref(mis), A, ctypes.byref(ex), B, A, big) == moe.MOE_ERR_ALIGN
+    assert call(M, ctypes.byref(tw), A, ctypes.byref(ex), B, A, big) == moe.MOE_ERR_ALIGN
+    assert call(A, ctypes.byref(tw), A, ctypes.byref(ex), B, A, need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(A, ctypes.byref(tw), A, ctypes.byref(ex), B, None, big) == moe.MOE_ERR_NULL
+    # the output may not overwrite the residual input
+    assert call(A, ctypes.byref(tw), A, ctypes.byref(ex), A, A, big) == moe.MOE_ERR_UNSUPPORTED
+    r = L.moe_rmsnorm
+    assert r(ctypes.byref(dims), None, A, 1e-6, A, None) == moe.MOE_ERR_NULL
+    assert r(ctypes.byref(dims), A, M, 1e-6, A, None) == moe.MOE_ERR_ALIGN
+    assert r(ctypes.byref(dims), A, A, -1.0, A, None) == moe.MOE_ERR_SHAPE
+    zero = _dims(T=0)
+    assert r(ctypes.byref(zero), None, None, 1e-6, None, None) == moe.MOE_OK
+    assert f(ctypes.byref(zero), None, ctypes.byref(tw), None, None, ctypes.byref(ex), None,
+             None, None, None, 0, None) == moe.MOE_OK
