@@ -35,11 +35,14 @@ MUTATIONS = [
     ("router bias dropped",
      "(bias ? (double)bias[e] : 0.0)", "0.0"),
     ("router tree pairs wrong",
-     "part[c] = part[c] + part[c + width];",
-     "part[c] = part[c] + part[(c + 2 * width) % 64];"),
+     "part[c] = part[c] + part[c + width];\n            double l = part[0]",
+     "part[c] = part[c] + part[(c + 2 * width) % 64];\n            double l = part[0]"),
     ("router single running sum",
-     "for (int width = 1; width < 64; width *= 2)",
-     "for (int c = 1; c < 64; ++c) part[0] = part[0] + part[c];\n            for (int width = 64; width < 64; width *= 2)"),
+     "for (int width = 1; width < 64; width *= 2)\n                for",
+     "for (int c = 1; c < 64; ++c) part[0] = part[0] + part[c];\n            for (int width = 64; width < 64; width *= 2)\n                for"),
+    ("RMSNorm tree pairs wrong",
+     "part[c] = part[c] + part[c + width];\n        double ms",
+     "part[c] = part[c] + part[(c + 2 * width) % 64];\n        double ms"),
     ("top-k ties to higher index",
      "if (best < 0 || l[e] > l[best])", "if (best < 0 || l[e] >= l[best])"),
     ("softmax denominator misses a slot",
