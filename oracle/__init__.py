@@ -85,6 +85,12 @@ def lib():
         L.orc_mx_quantize_block.argtypes = [i, P, P, P]
         L.orc_mx_split_block.restype = None
         L.orc_mx_split_block.argtypes = [i, P, P, P, P, P]
+        L.orc_fp8_weight.restype = ctypes.c_double
+        L.orc_fp8_weight.argtypes = [P, P, i, i, i]
+        L.orc_expert_row_fp8.restype = None
+        L.orc_expert_row_fp8.argtypes = [i, i, P, P, P, P, P, P, P]
+        L.orc_layer_forward_fp8.restype = ctypes.c_int
+        L.orc_layer_forward_fp8.argtypes = [i, i, i, i, i] + [P] * 12 + [i]
         L.orc_rmsnorm.restype = None
         L.orc_rmsnorm.argtypes = [i, i, P, P, ctypes.c_float, P]
         L.orc_shared_expert_row.restype = None
@@ -249,6 +255,47 @@ def layer_forward(x, router_w, bias, gu_codes, gu_scales, dn_codes, dn_scales,
         raise MemoryError("oracle layer_forward: allocation failed")
     return {"logits": logits, "topk_ids": ids, "topk_w": w, "y64": y64,
             "y": yb}
+
+
+# ---- FP8 experts (E4M3FN, fp32 scale per 128 x 128 block) ---------------------
+def fp8_weight(codes, scales, K, row, col):
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    return lib().orc_fp8_weight(_p(codes), _p(scales), int(K), int(row), int(col))
+
+
+def expert_row_fp8(x_row, gu_codes, gu_scales, dn_codes, dn_scales, d, f):
+    """One FP8 expert on one token row: returns (h, o) in fp64."""
+    args = [_c(x_row, np.uint16), _c(gu_codes, np.uint8), _c(gu_scales, np.float32),
+            _c(dn_codes, np.uint8), _c(dn_scales, np.float32)]
+    h = np.empty(f, dtype=np.float64)
+    o = np.empty(d, dtype=np.float64)
+    lib().orc_expert_row_fp8(int(d), int(f), *[_p(a) for a in args], _p(h), _p(o))
+    return h, o
+
+
+def layer_forward_fp8(x, router_w, bias, gu_codes, gu_scales, dn_codes, dn_scales, k,
+                      n_threads=0):
+    """The layer with FP8 experts (full arrays [E][...])."""
+    x = _c(x, np.uint16)
+    router_w = _c(router_w, np.uint16)
+    T, d = x.shape
+    E = router_w.shape[0]
+    f = gu_codes.shape[1] // 2
+    b = None if bias is None else _c(bias, np.float32)
+    ws = [_c(gu_codes, np.uint8), _c(gu_scales, np.float32), _c(dn_codes, np.uint8),
+          _c(dn_scales, np.float32)]
+    logits = np.empty((T, E), dtype=np.float32)
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    y64 = np.empty((T, d), dtype=np.float64)
+    yb = np.empty((T, d), dtype=np.uint16)
+    rc = lib().orc_layer_forward_fp8(T, d, E, k, f, _p(x), _p(router_w), _p(b),
+                                     *[_p(a) for a in ws], _p(logits), _p(ids), _p(w), _p(y64),
+                                     _p(yb), int(n_threads))
+    if rc != 0:
+        raise MemoryError("oracle layer_forward_fp8: allocation failed")
+    return {"logits": logits, "topk_ids": ids, "topk_w": w, "y64": y64, "y": yb}
 
 
 # ---- MoE tail ---------------------------------------------------------------------

@@ -629,3 +629,90 @@ int orc_block_forward(int T, int d, int E, int k, int f, int fs, const uint16_t 
     free(y);
     return failed ? -1 : 0;
 }
+
+/* ======================================================================= */
+/* FP8 experts (E4M3FN codes, fp32 scale per 128 x 128 block)              */
+/* ======================================================================= */
+
+/* The pages' FP8 lane is an exhaustive OCP E4M3FN oracle, a fused GEMV and
+ * a bounded BF16-dequant prefill floor (Moonshine README, "GLM 5.3 Flash
+ * status").  They do not print the scale layout; the reading here is the
+ * block-scaled layout of official FP8 checkpoints: one fp32 scale per
+ * 128 x 128 block of each [rows][K] matrix, multiplying the decoded code.
+ * E4M3FN is the OCP 8-bit E4M3 format (bias 7, no infinities, S.1111.111 is
+ * NaN, largest finite 448): the E4M3 element type of orc_elem_value.
+ *
+ * Layout per expert (K contiguous):
+ *   gu codes [2f][d], gu scales [2f/128][d/128]; dn codes [d][f],
+ *   dn scales [d/128][f/128]; gate = rows [0, f), up = rows [f, 2f). */
+double orc_fp8_weight(const uint8_t *codes, const float *scales, int K, int row, int col)
+{
+    double v = orc_elem_value(ORC_FMT_E4M3, codes[(size_t)row * K + col]);
+    return v * (double)scales[(size_t)(row / 128) * (size_t)(K / 128) + (size_t)(col / 128)];
+}
+
+/* The SwiGLU expert of expert_row_impl with FP8 weights (fp64, exact
+ * dequantised weights, exact bf16 inputs). */
+void orc_expert_row_fp8(int d, int f, const uint16_t *x_row, const uint8_t *gu_codes,
+                        const float *gu_scales, const uint8_t *dn_codes,
+                        const float *dn_scales, double *h, double *o)
+{
+    for (int n = 0; n < f; ++n) {
+        double g = 0.0, u = 0.0;
+        for (int kk = 0; kk < d; ++kk) {
+            double xv = orc_bf16_value(x_row[kk]);
+            g = g + xv * orc_fp8_weight(gu_codes, gu_scales, d, n, kk);
+            u = u + xv * orc_fp8_weight(gu_codes, gu_scales, d, f + n, kk);
+        }
+        h[n] = silu(g) * u;
+    }
+    for (int m = 0; m < d; ++m) {
+        double s = 0.0;
+        for (int n = 0; n < f; ++n)
+            s = s + h[n] * orc_fp8_weight(dn_codes, dn_scales, f, m, n);
+        o[m] = s;
+    }
+}
+
+/* The layer of orc_layer_forward with FP8 experts: router, top-k, the FP8
+ * expert rows, weighted combine.  Returns 0, or -1 when scratch allocation
+ * fails. */
+int orc_layer_forward_fp8(int T, int d, int E, int k, int f, const uint16_t *x,
+                          const uint16_t *router_w, const float *bias, const uint8_t *gu_codes,
+                          const float *gu_scales, const uint8_t *dn_codes,
+                          const float *dn_scales, float *logits, int32_t *topk_ids,
+                          double *topk_w, double *y64, uint16_t *y_bf16, int n_threads)
+{
+    size_t gu_code_b = (size_t)2 * f * d, gu_sc_n = (size_t)(2 * f / 128) * (d / 128);
+    size_t dn_code_b = (size_t)d * f, dn_sc_n = (size_t)(d / 128) * (f / 128);
+    double *o = (double *)malloc(sizeof(double) * (size_t)T * k * d);
+    if (!o)
+        return -1;
+    orc_router_logits(T, d, E, x, router_w, bias, logits);
+    orc_topk_softmax(T, E, k, logits, topk_ids, topk_w);
+    int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+    int rows = T * k;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int r = 0; r < rows; ++r) {
+        double *h = (double *)malloc(sizeof(double) * (size_t)f);
+        if (!h) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        int t = r / k;
+        size_t e = (size_t)topk_ids[r];
+        orc_expert_row_fp8(d, f, x + (size_t)t * d, gu_codes + e * gu_code_b,
+                           gu_scales + e * gu_sc_n, dn_codes + e * dn_code_b,
+                           dn_scales + e * dn_sc_n, h, o + (size_t)r * d);
+        free(h);
+    }
+    if (!failed)
+        for (int t = 0; t < T; ++t)
+            orc_combine_token(d, k, topk_w + (size_t)t * k, o + (size_t)t * k * d,
+                              y64 ? y64 + (size_t)t * d : NULL,
+                              y_bf16 ? y_bf16 + (size_t)t * d : NULL);
+    free(o);
+    return failed ? -1 : 0;
+}

@@ -97,6 +97,19 @@ int orc_block_forward(int T, int d, int E, int k, int f, int fs, const uint16_t 
                       int32_t *topk_ids, double *topk_w, double *out64, uint16_t *out_bf16,
                       int n_threads);
 
+/* ---- FP8 experts: E4M3FN codes, fp32 scale per 128 x 128 block ---------
+ * gu codes [E][2f][d], gu scales [E][2f/128][d/128]; dn codes [E][d][f],
+ * dn scales [E][d/128][f/128] (d % 128 == 0, f % 128 == 0). */
+double orc_fp8_weight(const uint8_t *codes, const float *scales, int K, int row, int col);
+void orc_expert_row_fp8(int d, int f, const uint16_t *x_row, const uint8_t *gu_codes,
+                        const float *gu_scales, const uint8_t *dn_codes,
+                        const float *dn_scales, double *h, double *o);
+int orc_layer_forward_fp8(int T, int d, int E, int k, int f, const uint16_t *x,
+                          const uint16_t *router_w, const float *bias, const uint8_t *gu_codes,
+                          const float *gu_scales, const uint8_t *dn_codes,
+                          const float *dn_scales, float *logits, int32_t *topk_ids,
+                          double *topk_w, double *y64, uint16_t *y_bf16, int n_threads);
+
 /* ---- OCP MX conversion model (element formats below) ------------------- */
 enum { ORC_FMT_E4M3 = 0, ORC_FMT_E2M3 = 1, ORC_FMT_E2M1 = 2 };
 double orc_elem_value(int fmt, unsigned code);

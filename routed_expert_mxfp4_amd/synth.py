@@ -19,6 +19,10 @@ Distributions (one per tensor):
   scales     E8M0 codes uniform over 123..127 (scales 2^-4 .. 2^0);
   bias       Zipf-style skew b_e = -beta * s * ln(e + 1) (s = 1.1) for the
              skewed prefill workload, none elsewhere;
+  FP8 experts: E4M3FN codes uniform bytes with the two NaN codes (0x7F,
+             0xFF) moved to their neighbours +-448 (0x7E, 0xFE); one fp32
+             scale per 128 x 128 block, (1 + u) * 2^-8 with u uniform on a
+             24-bit grid in [0, 1);
   MoE tail (pre-norm block): gamma bf16 = 1 + N(0, 0.1^2) (RMSNorm weight),
              eps = 1e-6, one shared expert of width f with bf16 gate/up
              [2f][d] and down [d][f] weights ~ N(0, 1).
@@ -42,6 +46,7 @@ MIX2 = 0x94D049BB133111EB
 TENSOR_X, TENSOR_WR, TENSOR_GU_CODES, TENSOR_GU_SCALES = 1, 2, 3, 4
 TENSOR_DN_CODES, TENSOR_DN_SCALES = 5, 6
 TENSOR_GAMMA, TENSOR_SHARED_GU, TENSOR_SHARED_DN = 7, 8, 9
+TENSOR_FP8_GU_CODES, TENSOR_FP8_GU_SCALES, TENSOR_FP8_DN_CODES, TENSOR_FP8_DN_SCALES = 10, 11, 12, 13
 TAIL_EPS = 1e-6
 
 SCALE_CODE_LO, SCALE_CODE_N = 123, 5      # E8M0 codes 123..127
@@ -234,6 +239,46 @@ def gen_experts(cfg: Config, experts=None, device="cpu",
                 v = scale_codes(keys[name], e0 * per, cnt * per, device)
             flat[i:i + cnt] = v.view(cnt, per)
             i = j + 1
+    return out
+
+
+def fp8_expert_sizes(cfg: Config) -> dict:
+    d, f = cfg.d, cfg.f
+    return {"gu_codes": (2 * f, d), "gu_scales": (2 * f // 128, d // 128),
+            "dn_codes": (d, f), "dn_scales": (d // 128, f // 128)}
+
+
+def gen_experts_fp8(cfg: Config, experts=None, device="cpu") -> dict:
+    """FP8 expert tensors for the listed experts (default: all): gu_codes
+    uint8 [n][2f][d], gu_scales fp32 [n][2f/128][d/128], dn_codes uint8
+    [n][d][f], dn_scales fp32 [n][d/128][f/128].  Needs d, f % 128 == 0."""
+    assert cfg.d % 128 == 0 and cfg.f % 128 == 0
+    if experts is None:
+        experts = range(cfg.E)
+    experts = list(experts)
+    n = len(experts)
+    sizes = fp8_expert_sizes(cfg)
+    keys = {"gu_codes": stream_key(cfg.seed, TENSOR_FP8_GU_CODES),
+            "gu_scales": stream_key(cfg.seed, TENSOR_FP8_GU_SCALES),
+            "dn_codes": stream_key(cfg.seed, TENSOR_FP8_DN_CODES),
+            "dn_scales": stream_key(cfg.seed, TENSOR_FP8_DN_SCALES)}
+    out = {}
+    for name, shp in sizes.items():
+        per = shp[0] * shp[1]
+        if name.endswith("codes"):
+            t = torch.empty((n,) + shp, dtype=torch.uint8, device=device)
+            flat = t.view(n, per)
+            for i, e in enumerate(experts):
+                b = random_bytes(keys[name], e * per, per, device)
+                flat[i] = torch.where((b & 0x7F) == 0x7F, b - 1, b)     # no NaN codes
+        else:
+            t = torch.empty((n,) + shp, dtype=torch.float32, device=device)
+            flat = t.view(n, per)
+            for i, e in enumerate(experts):
+                z = splitmix64(_arange(e * per, per, device), keys[name])
+                u = _lsr(z, 40).to(torch.float64) * (1.0 / 16777216.0)     # 24-bit grid
+                flat[i] = ((1.0 + u) * 2.0 ** -8).to(torch.float32)        # exact in fp32
+        out[name] = t
     return out
 
 

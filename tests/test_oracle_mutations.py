@@ -69,6 +69,15 @@ MUTATIONS = [
      "    if (act)\n        orc_mx_round(ORC_FMT_E2M3, d, xv);", ""),
     ("activation-MX mode: h not rounded",
      "    if (act)\n        orc_mx_round(ORC_FMT_E2M3, f, h);", ""),
+    ("FP8 block scale column index",
+     "(size_t)(K / 128) + (size_t)(col / 128)]",
+     "(size_t)(K / 128) + (size_t)(col / 64) % (size_t)(K / 128)]"),
+    ("FP8 block scale row index",
+     "scales[(size_t)(row / 128) * (size_t)(K / 128)",
+     "scales[(size_t)((row / 64) % 2) * (size_t)(K / 128)"),
+    ("FP8 expert gate and up swapped",
+     "u = u + xv * orc_fp8_weight(gu_codes, gu_scales, d, f + n, kk);",
+     "u = u + xv * orc_fp8_weight(gu_codes, gu_scales, d, n, kk);"),
     ("RMSNorm eps outside the square root",
      "double den = sqrt(ms + (double)eps);", "double den = sqrt(ms) + (double)eps;"),
     ("RMSNorm sum instead of mean",
@@ -101,7 +110,7 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
     env = dict(os.environ, MOE_ORACLE_LIB=str(so))
     pins = [os.path.join(ROOT, "tests", f) for f in
             ("test_oracle_formats.py", "test_oracle_router.py",
-             "test_oracle_ffn.py", "test_oracle_mx.py", "test_oracle_tail.py")]
+             "test_oracle_ffn.py", "test_oracle_mx.py", "test_oracle_tail.py", "test_oracle_fp8.py")]
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + pins,
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "no pin caught: " + name + "\n" + r.stdout[-2000:]
