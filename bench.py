@@ -36,13 +36,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 WORKLOADS = {"tiny": 0, "decode": 1, "batched-decode": 2, "zipf-prefill": 3, "long-prefill": 4,
-             "mimo-decode": 5, "mimo-prefill": 6}
+             "mimo-decode": 5, "mimo-prefill": 6, "fp8-decode": 7, "fp8-prefill": 8}
 DEFAULT_STEPS = {"tiny": 1000, "decode": 1000, "batched-decode": 200, "zipf-prefill": 20,
-                 "long-prefill": 5, "mimo-decode": 1000, "mimo-prefill": 20}
+                 "long-prefill": 5, "mimo-decode": 1000, "mimo-prefill": 20, "fp8-decode": 1000,
+                 "fp8-prefill": 3}
+VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published (the FP8 prefill floor's bound)
 KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm",
            "router_refine", "permute", "topk_permute", "gemv_gate_up",
            "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "down_mfma",
-           "combine")
+           "combine", "fp8_gate_up", "fp8_down")
 # the pre-norm block's own kernels (--tail)
 TAIL_KERNELS = ("rmsnorm", "shared_gate_up", "shared_down_add", "shared_gemm_gate_up",
                 "shared_swiglu", "shared_gemm_down")
@@ -151,11 +153,14 @@ def cpu_baseline(cfg, n_tokens):
             ids, w = oracle.topk_softmax(lg, cfg.k)
             spent += time.perf_counter() - t0
             need = [int(e) for e in ids[0]]
-            W = {k: v.numpy() for k, v in synth.gen_experts(cfg, experts=need).items()}
+            fp8 = cfg.wfmt == "fp8"
+            gen = synth.gen_experts_fp8 if fp8 else synth.gen_experts
+            W = {k: v.numpy() for k, v in gen(cfg, experts=need).items()}
+            erow = oracle.expert_row_fp8 if fp8 else oracle.expert_row
 
             def row(j):
-                return oracle.expert_row(x16[0], W["gu_codes"][j], W["gu_scales"][j],
-                                         W["dn_codes"][j], W["dn_scales"][j], cfg.d, cfg.f)[1]
+                return erow(x16[0], W["gu_codes"][j], W["gu_scales"][j],
+                            W["dn_codes"][j], W["dn_scales"][j], cfg.d, cfg.f)[1]
             t0 = time.perf_counter()
             o = np.stack(list(pool.map(row, range(cfg.k))))
             oracle.combine_token(w[0], o)
@@ -195,19 +200,26 @@ def main():
     # the kernel that dominates the step: the expert-weight stream of the
     # gate/up GEMV (HBM-bound) for decode-sized T, the scaled-MFMA gate/up
     # GEMM (matrix-core-bound) for prefill-sized T
-    mfma = cfg.T >= MFMA_MIN_T and cfg.d % 512 == 0 and cfg.f % 256 == 0
-    dominant = "gate_up_mfma" if mfma else "gemv_gate_up"
+    fp8 = cfg.wfmt == "fp8"
+    if fp8 and (args.tail or args.act != "bf16"):
+        print("the FP8 expert variant runs the routed layer in bf16 activations only",
+              file=sys.stderr)
+        sys.exit(2)
+    mfma = (not fp8) and cfg.T >= MFMA_MIN_T and cfg.d % 512 == 0 and cfg.f % 256 == 0
+    dominant = "fp8_gate_up" if fp8 else ("gate_up_mfma" if mfma else "gemv_gate_up")
     L = moe.lib()
 
     # ---- inputs, resident in HBM before timing --------------------------------
-    experts = synth.gen_experts(cfg, device=dev)
+    experts = synth.gen_experts_fp8(cfg, device=dev) if fp8 else synth.gen_experts(cfg, device=dev)
     wr = synth.gen_router_w(cfg).to(dev)
     bias = synth.gen_bias(cfg)
     bias = None if bias is None else bias.to(dev)
     n_batches = min(cfg.batches, max(1, args.steps + args.warmup))
     xs = [synth.gen_x(cfg, b).to(dev) for b in range(n_batches)]
     act = moe.ACT_MX_E2M3 if args.act == "mx" else moe.ACT_BF16
-    if args.tail:
+    if fp8:
+        layer = moe.Fp8Layer(experts, wr, cfg.k, bias, T=cfg.T)
+    elif args.tail:
         tail = {n: (v.to(dev) if hasattr(v, "to") else v)
                 for n, v in synth.gen_tail(cfg).items()}
         layer = moe.Block(experts, wr, cfg.k, tail, bias, T=cfg.T, act=act)
@@ -219,7 +231,7 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
     dims = moe.dims_of(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, act)
-    ex = moe.experts_of(experts)
+    ex = moe.fp8_experts_of(experts) if fp8 else moe.experts_of(experts)
     ws = layer._ws
     bptr = None if bias is None else ctypes.c_void_p(bias.data_ptr())
     if args.tail:
@@ -228,6 +240,12 @@ def main():
                     ctypes.c_void_p(y.data_ptr()), None, None, ctypes.c_void_p(ws.data_ptr()),
                     ws.numel(), sptr) for x in xs]
         fwd, fname = L.moe_block_forward, "moe_block_forward"
+    elif fp8:
+        argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()),
+                    ctypes.c_void_p(wr.data_ptr()), bptr, ctypes.byref(ex),
+                    ctypes.c_void_p(y.data_ptr()), None, None, ctypes.c_void_p(ws.data_ptr()),
+                    ws.numel(), sptr) for x in xs]
+        fwd, fname = L.moe_layer_forward_fp8, "moe_layer_forward_fp8"
     else:
         argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()),
                     ctypes.c_void_p(wr.data_ptr()), bptr, ctypes.byref(ex),
@@ -274,7 +292,7 @@ def main():
 
     # ---- algorithmic work ------------------------------------------------------------
     ids_probe = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
-    per_expert_gu = 2 * cfg.f * (cfg.d // 2) + 2 * cfg.f * (cfg.d // 32)
+    per_expert_gu = cfg.gate_up_bytes
     touched = []
     for b in range(min(n_batches, 64)):
         if args.tail:
@@ -289,7 +307,19 @@ def main():
     value = tokens / elapsed
     layer_bytes = mean_touched * cfg.expert_bytes
     layer_flops = 2.0 * cfg.T * cfg.k * 3 * cfg.d * cfg.f
-    if mfma:
+    if fp8 and cfg.T >= MFMA_MIN_T:
+        # the FP8 prefill floor: the dequant-GEMV's dot products on the VALU
+        flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
+        achieved = flops_per_launch / avg_launch_s / 1e12
+        src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_fp8.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        roofline = {"bound": "alu", "kernel": dominant, "achieved": achieved,
+                    "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / VALU_FP32_PEAK_TFLOPS,
+                    "traffic": traffic_from_profiles(dominant, args.workload, sha),
+                    "algorithmic_flops_per_launch": flops_per_launch,
+                    "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
+    elif mfma:
         # gate/up: every routed row times the [2f x d] gate/up matrix
         flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
         achieved = flops_per_launch / avg_launch_s / 1e12
@@ -305,7 +335,8 @@ def main():
     else:
         bytes_per_launch = mean_touched * per_expert_gu
         achieved = bytes_per_launch / avg_launch_s / 1e9
-        src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_gemv.hip")
+        src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc",
+                           "ffn_fp8.hip" if fp8 else "ffn_gemv.hip")
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
@@ -328,10 +359,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "f": cfg.f, "distinct_batches": n_batches,
-                   "weights": "MXFP4 (E2M1 codes + E8M0 scale per 32), resident in HBM",
+                   "weights": ("FP8 (E4M3FN codes + fp32 scale per 128x128 block), resident in HBM"
+                               if fp8 else
+                               "MXFP4 (E2M1 codes + E8M0 scale per 32), resident in HBM"),
                    "activations": ("MX E2M3, one term per 32 (activation-MX mode)" if act
                                    else "bf16"), "accumulate": "fp32",
-                   "expert_path": "scaled MFMA" if mfma else "GEMV"},
+                   "expert_path": ("FP8 dequant-GEMV" + (" (prefill floor)" if cfg.T >= MFMA_MIN_T
+                                                          else "") if fp8 else
+                                   "scaled MFMA" if mfma else "GEMV")},
         "block": (None if not args.tail else {
             "entry": "moe_block_forward",
             "steps": "RMSNorm (canonical fp64) -> routed layer on xn -> bf16 SwiGLU shared "

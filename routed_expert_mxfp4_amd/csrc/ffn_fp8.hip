@@ -1,0 +1,236 @@
+// ffn_fp8.hip -- routed expert FFN with FP8 experts on gfx950: E4M3FN codes
+// (one byte per weight, K contiguous) with one fp32 scale per 128 x 128
+// block of each matrix.
+//
+// The pages' FP8 lane pairs an exhaustive OCP E4M3FN oracle with a fused
+// GEMV and a bounded BF16-dequant prefill floor (Moonshine README, "GLM 5.3
+// Flash status").  Here one grouped dequant-GEMV serves every T: each wave
+// streams whole weight rows with 16-byte loads (16 codes per lane), gfx950
+// converts code pairs exactly to bf16 (against bf16 x) or fp32 (against fp32
+// h) -- the bf16 copy of a weight lives only in registers, so the dequant is
+// bounded to the tile in flight -- and each 16-element partial sum is
+// multiplied by its block's fp32 scale.  Every decoded weight is reused for
+// all token rows of the expert staged in LDS (up to kRows8 per pass).  At
+// prefill sizes this is the floor: correct and bounded, not matrix-core fast.
+//
+// Gate/up: h[p][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]) (fp32), p over the
+// expert's rows (t = sorted_rows[p] / k); gate rows [0, f), up [f, 2f).
+// Down: rows_out[p][m] = h[p] . Wd[m] (bf16), expert-major.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kPairs8 = 16;      // gate/up output pairs per block
+constexpr int kRows8 = 4;        // token rows of one expert per LDS pass
+constexpr int kDnRows8 = 64;     // down output rows per block
+
+__device__ __forceinline__ float silu_mul8(float g, float u) {
+    return g / (1.0f + expf(-g)) * u;
+}
+
+// The expert group of blockIdx.y from device data, bounds-checked.
+__device__ __forceinline__ bool group8(const int32_t *plan, const int32_t *offsets, int a,
+                                       int E, int nrows, int &e, int &row0, int &ne) {
+    if (a >= plan[0]) return false;
+    e = plan[1 + a];
+    if ((unsigned)e >= (unsigned)E) return false;
+    row0 = offsets[e];
+    ne = offsets[e + 1] - row0;
+    return row0 >= 0 && ne > 0 && row0 + ne <= nrows;
+}
+
+// 16 E4M3FN codes (byte i = element i) dotted with 16 bf16 values (x0:
+// elements 0..7, x1: 8..15), fp32 accumulate.  The scaled convert (scale
+// 1.0) gives the codes' exact bf16 values, low byte first.
+__device__ __forceinline__ float dot16_fp8_bf16(uint4 c, uint4 x0, uint4 x1, float acc) {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[i], 1.0f, false);
+        const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[i], 1.0f, true);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(lo, __builtin_bit_cast(bf16x2_t, xw[2 * i]), acc,
+                                              false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(hi, __builtin_bit_cast(bf16x2_t, xw[2 * i + 1]),
+                                              acc, false);
+    }
+    return acc;
+}
+
+// 16 E4M3FN codes dotted with 16 fp32 values h[0..15].
+__device__ __forceinline__ float dot16_fp8_f32(uint4 c, const float4 (&hv)[4], float acc) {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[i], 1.0f, false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[i], 1.0f, true);
+        acc = fmaf(lo.x, hv[i].x, acc);
+        acc = fmaf(lo.y, hv[i].y, acc);
+        acc = fmaf(hi.x, hv[i].z, acc);
+        acc = fmaf(hi.y, hv[i].w, acc);
+    }
+    return acc;
+}
+
+// Block (kPairs8 output pairs, expert a = blockIdx.y); wave w takes pairs
+// w, w + 4, ..; lane l takes the 16-code chunks c = l + 64 i of a row, two
+// chunks per turn so that four 16-byte loads are in flight.
+__global__ __launch_bounds__(256) void fp8_gate_up_kernel(
+    const uint16_t *__restrict__ x, Fp8Args W, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
+    float *__restrict__ h, int T, int d, int E, int k, int f, int rpp) {
+    const int nrows = T * k;
+    int e, row0, ne;
+    if (!group8(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t *codes = W.gu_codes + (size_t)e * 2 * f * d;
+    const int sbk = d >> 7;                               // scale blocks along K
+    const float *scales = W.gu_scales + (size_t)e * (2 * f >> 7) * sbk;
+    extern __shared__ uint4 xs4[];                        // [rpp][d / 8]
+    const int nvec = d >> 3, nch = d >> 4;
+    const int n_base = blockIdx.x * kPairs8;
+
+    for (int r0 = 0; r0 < ne; r0 += rpp) {
+        const int R = min(rpp, ne - r0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < R * nvec; i += 256) {
+            const int r = i / nvec, v = i - r * nvec;
+            const int row = sorted_rows[row0 + r0 + r];
+            const int tok = (unsigned)row < (unsigned)nrows ? row / k : 0;
+            xs4[r * nvec + v] = reinterpret_cast<const uint4 *>(x + (size_t)tok * d)[v];
+        }
+        __syncthreads();
+        for (int p = wid; p < kPairs8; p += 4) {
+            const int n = n_base + p;
+            const uint4 *grow = reinterpret_cast<const uint4 *>(codes + (size_t)n * d);
+            const uint4 *urow = reinterpret_cast<const uint4 *>(codes + (size_t)(f + n) * d);
+            const float *gsc = scales + (size_t)(n >> 7) * sbk;
+            const float *usc = scales + (size_t)((f + n) >> 7) * sbk;
+            float g[kRows8], u[kRows8];
+#pragma unroll
+            for (int r = 0; r < kRows8; ++r) g[r] = u[r] = 0.f;
+            for (int c = lane; c < nch; c += 128) {
+                const bool two = c + 64 < nch;
+                const uint4 cg0 = grow[c], cu0 = urow[c];
+                const uint4 cg1 = two ? grow[c + 64] : uint4{0, 0, 0, 0};
+                const uint4 cu1 = two ? urow[c + 64] : uint4{0, 0, 0, 0};
+                const float sg0 = gsc[c >> 3], su0 = usc[c >> 3];
+                const float sg1 = two ? gsc[(c + 64) >> 3] : 0.f;
+                const float su1 = two ? usc[(c + 64) >> 3] : 0.f;
+#pragma unroll
+                for (int r = 0; r < kRows8; ++r) {
+                    if (r < R) {
+                        const uint4 *xv = xs4 + r * nvec;
+                        g[r] += sg0 * dot16_fp8_bf16(cg0, xv[2 * c], xv[2 * c + 1], 0.f);
+                        u[r] += su0 * dot16_fp8_bf16(cu0, xv[2 * c], xv[2 * c + 1], 0.f);
+                        if (two) {
+                            const int c1 = c + 64;
+                            g[r] += sg1 * dot16_fp8_bf16(cg1, xv[2 * c1], xv[2 * c1 + 1], 0.f);
+                            u[r] += su1 * dot16_fp8_bf16(cu1, xv[2 * c1], xv[2 * c1 + 1], 0.f);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kRows8; ++r) {
+                if (r < R) {
+                    const float gs = wave_sum_f32(g[r]), us = wave_sum_f32(u[r]);
+                    if (lane == 0) h[(size_t)(row0 + r0 + r) * f + n] = silu_mul8(gs, us);
+                }
+            }
+        }
+    }
+}
+
+// Block (kDnRows8 output rows, expert a); wave w owns rows 16 w .. 16 w + 15
+// as four groups of 16 lanes with 4 rows each; lane gl of a group takes the
+// 16-code chunks gl + 16 i of those rows.
+__global__ __launch_bounds__(256) void fp8_down_kernel(
+    const float *__restrict__ h, Fp8Args W, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ plan, uint16_t *__restrict__ rows_out, int T, int d, int E,
+    int k, int f, int rpp) {
+    const int nrows = T * k;
+    int e, row0, ne;
+    if (!group8(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane >> 4, gl = lane & 15;
+    const uint8_t *codes = W.dn_codes + (size_t)e * d * f;
+    const int sbk = f >> 7;
+    const float *scales = W.dn_scales + (size_t)e * (d >> 7) * sbk;
+    extern __shared__ float4 hs4[];                       // [rpp][f / 4]
+    const int nv = f >> 2, nch = f >> 4;
+    const int m_base = blockIdx.x * kDnRows8 + wid * 16 + grp * 4;
+
+    for (int r0 = 0; r0 < ne; r0 += rpp) {
+        const int R = min(rpp, ne - r0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < R * nv; i += 256) {
+            const int r = i / nv, v = i - r * nv;
+            hs4[r * nv + v] = reinterpret_cast<const float4 *>(h + (size_t)(row0 + r0 + r) * f)[v];
+        }
+        __syncthreads();
+        float acc[4][kRows8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < kRows8; ++r) acc[q][r] = 0.f;
+        for (int c = gl; c < nch; c += 16) {
+            uint4 cq[4];
+            float sq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = m_base + q;
+                cq[q] = reinterpret_cast<const uint4 *>(codes + (size_t)m * f)[c];
+                sq[q] = scales[(size_t)(m >> 7) * sbk + (c >> 3)];
+            }
+#pragma unroll
+            for (int r = 0; r < kRows8; ++r) {
+                if (r < R) {
+                    const float4 *hr = hs4 + r * nv + 4 * c;
+                    const float4 hv[4] = {hr[0], hr[1], hr[2], hr[3]};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q][r] += sq[q] * dot16_fp8_f32(cq[q], hv, 0.f);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < kRows8; ++r) {
+                if (r < R) {
+                    const float v = group16_sum_f32(acc[q][r]);
+                    if (gl == 0)
+                        rows_out[(size_t)(row0 + r0 + r) * d + m_base + q] = f32_to_bf16_rne(v);
+                }
+            }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_gate_up(const uint16_t *x, Fp8Args w, const int32_t *offsets,
+                              const int32_t *sorted_rows, const int32_t *plan, float *h, int T,
+                              int d, int E, int k, int f, hipStream_t s) {
+    const int amax = min(E, T * k);
+    if (amax <= 0) return hipSuccess;
+    const int rpp = max(1, min(kRows8, 32768 / d));      // <= 64 KB of LDS
+    return timed_launch("fp8_gate_up", fp8_gate_up_kernel, dim3(f / kPairs8, amax), dim3(256),
+                        (size_t)rpp * d * 2, s, x, w, offsets, sorted_rows, plan, h, T, d, E, k,
+                        f, rpp);
+}
+
+hipError_t launch_fp8_down(const float *h, Fp8Args w, const int32_t *offsets,
+                           const int32_t *plan, uint16_t *rows_out, int T, int d, int E, int k,
+                           int f, hipStream_t s) {
+    const int amax = min(E, T * k);
+    if (amax <= 0) return hipSuccess;
+    const int rpp = max(1, min(kRows8, 16384 / f));      // <= 64 KB of LDS
+    return timed_launch("fp8_down", fp8_down_kernel, dim3(d / kDnRows8, amax), dim3(256),
+                        (size_t)rpp * f * 4, s, h, w, offsets, plan, rows_out, T, d, E, k, f,
+                        rpp);
+}
+
+}  // namespace moe

@@ -6,6 +6,7 @@
 // synchronises the host with the device, and never lets a C++ exception out.
 #include "../../include/moe.h"
 #include "../../include/moe_diag.h"
+#include "../../include/moe_fp8.h"
 #include "../../include/moe_tail.h"
 
 #include <hip/hip_runtime.h>
@@ -121,6 +122,51 @@ struct Diag {
     int used = 0;
 };
 Diag g_diag;
+
+// FP8 experts: the grouped GEMV path for every T.  FFN: the plan, then h
+// [T*k][f] fp32.  Layer: the routed layer's routing and grouping scratch,
+// that, and rows_out [T*k][d] bf16.
+struct Fp8FfnWs {
+    size_t plan, h, total;
+};
+Fp8FfnWs fp8_ffn_ws(const moe_dims &D) {
+    Fp8FfnWs w;
+    w.plan = 0;
+    w.h = al256((size_t)(D.E + 1) * 4);
+    w.total = w.h + al256((size_t)D.T * D.k * D.f * 4);
+    return w;
+}
+struct Fp8LayerWs {
+    size_t route, ids, tw, counts, offsets, sorted_rows, row_pos, perm, ffn, rows_out, total;
+};
+Fp8LayerWs fp8_layer_ws(const moe_dims &D) {
+    const size_t rows = (size_t)D.T * D.k;
+    Fp8LayerWs w;
+    size_t p = 0;
+    w.route = p; p += route_ws(D).total;
+    w.ids = p; p += al256(rows * 4);
+    w.tw = p; p += al256(rows * 4);
+    w.counts = p; p += al256((size_t)D.E * 4);
+    w.offsets = p; p += al256((size_t)(D.E + 1) * 4);
+    w.sorted_rows = p; p += al256(rows * 4);
+    w.row_pos = p; p += al256(rows * 4);
+    w.perm = p; p += al256(moe::permute_ws_bytes(D.T, D.E));
+    w.ffn = p; p += fp8_ffn_ws(D).total;
+    w.rows_out = p; p += al256(rows * D.d * 2);
+    w.total = p;
+    return w;
+}
+
+moe_status check_fp8(const moe_dims &D, const moe_fp8_experts *w) {
+    if (D.d % 128 != 0 || D.f % 128 != 0) return MOE_ERR_SHAPE;
+    if (D.act != MOE_ACT_BF16) return MOE_ERR_UNSUPPORTED;
+    if (!w) return MOE_ERR_NULL;
+    if (!w->gu_codes || !w->gu_scales || !w->dn_codes || !w->dn_scales) return MOE_ERR_NULL;
+    if (!aligned16(w->gu_codes) || !aligned16(w->gu_scales) || !aligned16(w->dn_codes) ||
+        !aligned16(w->dn_scales))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
 
 // Pre-norm block: the routed layer's scratch, then xn; few tokens: the
 // routed output y and the shared expert's fp32 h; many tokens: the shared
@@ -491,6 +537,115 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
         return device_status(run_layer(D, x, router_w, router_bias, *experts, y, topk_ids_out,
                                        topk_w_out, static_cast<char *>(ws),
                                        static_cast<hipStream_t>(hip_stream), nullptr, nullptr));
+    });
+}
+
+size_t moe_fp8_workspace_bytes(const moe_dims *dims, int entry) {
+    if (check_dims(dims) != MOE_OK) return (size_t)-1;
+    if (dims->d % 128 != 0 || dims->f % 128 != 0) return (size_t)-1;
+    if (entry == MOE_ENTRY_EXPERT_FFN) return fp8_ffn_ws(*dims).total;
+    if (entry == MOE_ENTRY_LAYER_FORWARD) return fp8_layer_ws(*dims).total;
+    return (size_t)-1;
+}
+
+moe_status moe_expert_ffn_fp8(const moe_dims *dims, const uint16_t *x,
+                              const moe_fp8_experts *experts, const int32_t *offsets,
+                              const int32_t *sorted_rows, uint16_t *rows_out, void *ws,
+                              size_t ws_bytes, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if ((st = check_fp8(D, experts)) != MOE_OK) return st;
+        if (D.T == 0) return MOE_OK;
+        if (!x || !offsets || !sorted_rows || !rows_out) return MOE_ERR_NULL;
+        if (!aligned16(x) || !aligned16(rows_out)) return MOE_ERR_ALIGN;
+        const Fp8FfnWs F = fp8_ffn_ws(D);
+        if (!ws) return MOE_ERR_NULL;
+        if (!aligned16(ws)) return MOE_ERR_ALIGN;
+        if (ws_bytes < F.total) return MOE_ERR_WORKSPACE;
+        char *base = static_cast<char *>(ws);
+        int32_t *plan = reinterpret_cast<int32_t *>(base + F.plan);
+        float *h = reinterpret_cast<float *>(base + F.h);
+        const moe::Fp8Args W{experts->gu_codes, experts->gu_scales, experts->dn_codes,
+                             experts->dn_scales};
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        hipError_t e = moe::launch_plan(offsets, plan, D.E, s);
+        if (e == hipSuccess)
+            e = moe::launch_fp8_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
+                                        D.f, s);
+        if (e == hipSuccess)
+            e = moe::launch_fp8_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f, s);
+        return device_status(e);
+    });
+}
+
+moe_status moe_layer_forward_fp8(const moe_dims *dims, const uint16_t *x,
+                                 const uint16_t *router_w, const float *router_bias,
+                                 const moe_fp8_experts *experts, uint16_t *y,
+                                 int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                                 size_t ws_bytes, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if ((st = check_fp8(D, experts)) != MOE_OK) return st;
+        if (D.T == 0) return MOE_OK;
+        if (!x || !router_w || !y) return MOE_ERR_NULL;
+        if (!aligned16(x) || !aligned16(router_w) || !aligned16(y)) return MOE_ERR_ALIGN;
+        const Fp8LayerWs L = fp8_layer_ws(D);
+        if (!ws) return MOE_ERR_NULL;
+        if (!aligned16(ws)) return MOE_ERR_ALIGN;
+        if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+        char *base = static_cast<char *>(ws);
+        const RouteWs RW = route_ws(D);
+        float *logits = reinterpret_cast<float *>(base + L.route + RW.logits);
+        int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(base + L.ids);
+        float *tw = topk_w_out ? topk_w_out : reinterpret_cast<float *>(base + L.tw);
+        int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
+        int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+        int32_t *sorted_rows = reinterpret_cast<int32_t *>(base + L.sorted_rows);
+        int32_t *row_pos = reinterpret_cast<int32_t *>(base + L.row_pos);
+        const Fp8FfnWs F = fp8_ffn_ws(D);
+        int32_t *plan = reinterpret_cast<int32_t *>(base + L.ffn + F.plan);
+        float *h = reinterpret_cast<float *>(base + L.ffn + F.h);
+        uint16_t *rows_out = reinterpret_cast<uint16_t *>(base + L.rows_out);
+        const moe::Fp8Args W{experts->gu_codes, experts->gu_scales, experts->dn_codes,
+                             experts->dn_scales};
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        hipError_t e;
+        // routing and grouping as in the MXFP4 layer (the plan is written too)
+        if (moe::route_filter_ok(D.T, D.d, D.E)) {
+            e = moe::launch_route_filtered(x, router_w, router_bias, logits,
+                                           reinterpret_cast<float *>(base + L.route + RW.nx),
+                                           reinterpret_cast<float *>(base + L.route + RW.nw), ids,
+                                           tw, D.T, D.d, D.E, D.k, s);
+            if (e == hipSuccess)
+                e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
+                                        D.E, D.k, base + L.perm, s);
+        } else {
+            e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
+            if (e == hipSuccess) {
+                if (moe::topk_permute_fusable(D.T, D.E, D.k)) {
+                    e = moe::launch_topk_permute_small(logits, ids, tw, counts, offsets,
+                                                       sorted_rows, row_pos, plan, D.T, D.E, D.k,
+                                                       s);
+                } else {
+                    e = moe::launch_topk_softmax(logits, ids, tw, D.T, D.E, D.k, s);
+                    if (e == hipSuccess)
+                        e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan,
+                                                D.T, D.E, D.k, base + L.perm, s);
+                }
+            }
+        }
+        if (e == hipSuccess)
+            e = moe::launch_fp8_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
+                                        D.f, s);
+        if (e == hipSuccess)
+            e = moe::launch_fp8_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f, s);
+        if (e == hipSuccess)
+            e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
+        return device_status(e);
     });
 }
 

@@ -245,6 +245,23 @@ hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
                           hipStream_t s, const uint16_t *resid = nullptr,
                           const float *extra = nullptr);
 
+// ---- FP8 experts (ffn_fp8.hip) ---------------------------------------------------
+// E4M3FN codes [E][rows][K], fp32 scales [E][rows/128][K/128].
+struct Fp8Args {
+    const uint8_t *gu_codes;
+    const float *gu_scales;
+    const uint8_t *dn_codes;
+    const float *dn_scales;
+};
+// Grouped dequant-GEMVs for any T: h fp32 [T*k][f] (expert-major rows),
+// rows_out bf16 [T*k][d].  Need d % 128 == 0, f % 128 == 0.
+hipError_t launch_fp8_gate_up(const uint16_t *x, Fp8Args w, const int32_t *offsets,
+                              const int32_t *sorted_rows, const int32_t *plan, float *h, int T,
+                              int d, int E, int k, int f, hipStream_t s);
+hipError_t launch_fp8_down(const float *h, Fp8Args w, const int32_t *offsets,
+                           const int32_t *plan, uint16_t *rows_out, int T, int d, int E, int k,
+                           int f, hipStream_t s);
+
 // ---- MoE tail (tail.hip, blas.cpp) --------------------------------------------
 // xn = bf16(RMSNorm(x) * gamma), canonical fp64 order, one wave per token.
 hipError_t launch_rmsnorm(const uint16_t *x, const uint16_t *gamma, float eps, uint16_t *xn,

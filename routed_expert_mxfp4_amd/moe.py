@@ -1,5 +1,5 @@
-"""Thin Python binding of the C ABI in ``include/moe.h`` and
-``include/moe_tail.h``.
+"""Thin Python binding of the C ABI in ``include/moe.h``,
+``include/moe_tail.h`` and ``include/moe_fp8.h``.
 
 Argument marshalling only: every step of the layer runs in the HIP kernels
 of ``libmoe_mxfp4.so``.  Torch supplies device memory (outputs and
@@ -40,6 +40,11 @@ class Experts(ctypes.Structure):
                 ("dn_codes", ctypes.c_void_p), ("dn_scales", ctypes.c_void_p)]
 
 
+class Fp8Experts(ctypes.Structure):
+    _fields_ = [("gu_codes", ctypes.c_void_p), ("gu_scales", ctypes.c_void_p),
+                ("dn_codes", ctypes.c_void_p), ("dn_scales", ctypes.c_void_p)]
+
+
 class TailWeights(ctypes.Structure):
     _fields_ = [("norm_w", ctypes.c_void_p), ("eps", ctypes.c_float), ("fs", ctypes.c_int32),
                 ("shared_gu", ctypes.c_void_p), ("shared_dn", ctypes.c_void_p)]
@@ -48,7 +53,8 @@ class TailWeights(ctypes.Structure):
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_diag_time_kernel", "moe_diag_kernel_time", "moe_diag_mx_split_e2m3",
-           "moe_block_workspace_bytes", "moe_rmsnorm", "moe_block_forward")
+           "moe_block_workspace_bytes", "moe_rmsnorm", "moe_block_forward",
+           "moe_fp8_workspace_bytes", "moe_expert_ffn_fp8", "moe_layer_forward_fp8")
 
 _lib = None
 
@@ -81,6 +87,13 @@ def lib():
         L.moe_combine.argtypes = [DP, P, P, P, P, P]
         L.moe_layer_forward.restype = I
         L.moe_layer_forward.argtypes = [DP, P, P, P, EP, P, P, P, P, S, P]
+        FP = ctypes.POINTER(Fp8Experts)
+        L.moe_fp8_workspace_bytes.restype = S
+        L.moe_fp8_workspace_bytes.argtypes = [DP, I]
+        L.moe_expert_ffn_fp8.restype = I
+        L.moe_expert_ffn_fp8.argtypes = [DP, P, FP, P, P, P, P, S, P]
+        L.moe_layer_forward_fp8.restype = I
+        L.moe_layer_forward_fp8.argtypes = [DP, P, P, P, FP, P, P, P, P, S, P]
         TP = ctypes.POINTER(TailWeights)
         L.moe_block_workspace_bytes.restype = S
         L.moe_block_workspace_bytes.argtypes = [DP, TP]
@@ -378,3 +391,82 @@ def moe_block_forward(x, router_w, experts: dict, k, tail: dict, router_bias=Non
     w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
     out = blk.forward(x, topk_ids=ids, topk_w=w, stream=stream)
     return (out, ids, w) if return_routing else out
+
+
+# ---- FP8 experts (include/moe_fp8.h) ----------------------------------------------
+def fp8_experts_of(w: dict) -> Fp8Experts:
+    return Fp8Experts(w["gu_codes"].data_ptr(), w["gu_scales"].data_ptr(),
+                      w["dn_codes"].data_ptr(), w["dn_scales"].data_ptr())
+
+
+def fp8_workspace(dims: Dims, entry: int, device) -> torch.Tensor:
+    n = lib().moe_fp8_workspace_bytes(ctypes.byref(dims), int(entry))
+    if n == SIZE_MAX:
+        raise MoeError(MOE_ERR_SHAPE, "moe_fp8_workspace_bytes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_expert_ffn_fp8(x, experts: dict, offsets, sorted_rows, k, ws=None, stream=None):
+    """Expert FFN over grouped rows with FP8 experts.  Returns rows_out bf16
+    [T*k][d]."""
+    x = _bits16(x)
+    T, d = x.shape
+    E, two_f = experts["gu_codes"].shape[:2]
+    dims = dims_of(T, d, E, k, two_f // 2)
+    rows_out = torch.empty((T * k, d), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = fp8_workspace(dims, ENTRY_EXPERT_FFN, x.device)
+    ex = fp8_experts_of(experts)
+    st = lib().moe_expert_ffn_fp8(ctypes.byref(dims), _ptr(x), ctypes.byref(ex), _ptr(offsets),
+                                  _ptr(sorted_rows), _ptr(rows_out), _ptr(ws), ws.numel(),
+                                  _stream(stream))
+    _check(st, "moe_expert_ffn_fp8")
+    return rows_out
+
+
+class Fp8Layer:
+    """Reusable workspace and pointers for repeated moe_layer_forward_fp8 calls."""
+
+    def __init__(self, experts: dict, router_w, k, router_bias=None, T=1):
+        self.experts = experts
+        self.router_w = _bits16(router_w)
+        self.bias = None if router_bias is None else router_bias.contiguous().float()
+        self.E, self.d = self.router_w.shape
+        self.f = experts["gu_codes"].shape[1] // 2
+        self.k = k
+        self._ex = fp8_experts_of(experts)
+        self._ws = None
+        self._ws_T = -1
+        self.reserve(T)
+
+    def reserve(self, T):
+        if T > self._ws_T:
+            dims = dims_of(T, self.d, self.E, self.k, self.f)
+            self._ws = fp8_workspace(dims, ENTRY_LAYER_FORWARD, self.router_w.device)
+            self._ws_T = T
+
+    def forward(self, x, y=None, topk_ids=None, topk_w=None, stream=None):
+        x = _bits16(x)
+        T = x.shape[0]
+        self.reserve(T)
+        if y is None:
+            y = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
+        dims = dims_of(T, self.d, self.E, self.k, self.f)
+        st = lib().moe_layer_forward_fp8(ctypes.byref(dims), _ptr(x), _ptr(self.router_w),
+                                         _ptr(self.bias), ctypes.byref(self._ex), _ptr(y),
+                                         _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
+                                         self._ws.numel(), _stream(stream))
+        _check(st, "moe_layer_forward_fp8")
+        return y
+
+
+def moe_layer_forward_fp8(x, router_w, experts: dict, k, router_bias=None,
+                          return_routing=False, stream=None):
+    """The layer with FP8 experts.  Returns y bf16 [T][d] (and topk_ids, topk_w)."""
+    x = _bits16(x)
+    T = x.shape[0]
+    layer = Fp8Layer(experts, router_w, k, router_bias, T=T)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
+    y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)
+    return (y, ids, w) if return_routing else y

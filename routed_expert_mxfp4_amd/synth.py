@@ -65,6 +65,7 @@ class Config:
     batches: int = 1          # distinct seeded batches (decode: tokens)
     zipf_beta: float = 0.0    # 0 -> no router bias
     zipf_s: float = 1.1
+    wfmt: str = "mxfp4"       # expert store: "mxfp4" or "fp8" (E4M3FN + 128x128 fp32 scales)
     notes: str = field(default="", compare=False)
 
     @property
@@ -74,7 +75,16 @@ class Config:
     @property
     def expert_bytes(self) -> int:
         d, f = self.d, self.f
+        if self.wfmt == "fp8":
+            return 3 * d * f + 4 * (2 * f // 128) * (d // 128) + 4 * (d // 128) * (f // 128)
         return 2 * f * (d // 2) + 2 * f * (d // 32) + d * (f // 2) + d * (f // 32)
+
+    @property
+    def gate_up_bytes(self) -> int:
+        d, f = self.d, self.f
+        if self.wfmt == "fp8":
+            return 2 * f * d + 4 * (2 * f // 128) * (d // 128)
+        return 2 * f * (d // 2) + 2 * f * (d // 32)
 
 
 # The workloads: tiny parity layer, one-token decode (1000 tokens), 64-token
@@ -96,6 +106,11 @@ CONFIGS = {
               256, 8, 2048, seed=5, batches=1000),
     6: Config(6, "mimo prefill T=4096 d=4096 E=256 k=8 f=2048", 4096, 4096, 256, 8,
               2048, seed=6),
+    # the K3 shape with FP8 experts (E4M3FN, fp32 scale per 128 x 128 block)
+    7: Config(7, "fp8 decode T=1 d=7168 E=896 k=16 f=1536 x1000 tokens", 1, 7168, 896, 16,
+              1536, seed=7, batches=1000, wfmt="fp8"),
+    8: Config(8, "fp8 zipf prefill T=4096 d=7168 E=896 k=16 f=1536", 4096, 7168, 896, 16,
+              1536, seed=8, zipf_beta=0.34, wfmt="fp8"),
 }
 
 

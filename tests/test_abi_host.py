@@ -181,3 +181,35 @@ def test_tail_entries_refuse_bad_arguments(L):
     assert r(ctypes.byref(zero), None, None, 1e-6, None, None) == moe.MOE_OK
     assert f(ctypes.byref(zero), None, ctypes.byref(tw), None, None, ctypes.byref(ex), None,
              None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_fp8_entries_refuse_bad_arguments(L):
+    A = ctypes.c_void_p(0x10000)
+    M = ctypes.c_void_p(0x10008)
+    big = 1 << 40
+    dims = _dims(d=256, f=128)
+    ex = moe.Fp8Experts(0x10000, 0x10000, 0x10000, 0x10000)
+    exm = moe.Fp8Experts(0x10000, 0x10004, 0x10000, 0x10000)
+    exn = moe.Fp8Experts(0x10000, 0x10000, None, 0x10000)
+    w = L.moe_fp8_workspace_bytes
+    assert w(ctypes.byref(dims), moe.ENTRY_LAYER_FORWARD) not in (0, moe.SIZE_MAX)
+    assert w(ctypes.byref(dims), moe.ENTRY_EXPERT_FFN) not in (0, moe.SIZE_MAX)
+    assert w(ctypes.byref(dims), moe.ENTRY_ROUTE) == moe.SIZE_MAX
+    bad = _dims(d=192, f=128)                     # d % 128 != 0
+    assert w(ctypes.byref(bad), moe.ENTRY_LAYER_FORWARD) == moe.SIZE_MAX
+    f = L.moe_layer_forward_fp8
+    assert f(ctypes.byref(bad), A, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_SHAPE
+    amx = _dims(d=256, f=128, act=1)
+    assert f(ctypes.byref(amx), A, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(ctypes.byref(dims), A, A, None, None, A, None, None, A, big, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(exn), A, None, None, A, big, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(exm), A, None, None, A, big, None) == moe.MOE_ERR_ALIGN
+    assert f(ctypes.byref(dims), M, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_ALIGN
+    need = w(ctypes.byref(dims), moe.ENTRY_LAYER_FORWARD)
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(ex), A, None, None, A, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    e = L.moe_expert_ffn_fp8
+    assert e(ctypes.byref(dims), A, ctypes.byref(ex), A, A, None, A, big, None) == moe.MOE_ERR_NULL
+    need = w(ctypes.byref(dims), moe.ENTRY_EXPERT_FFN)
+    assert e(ctypes.byref(dims), A, ctypes.byref(ex), A, A, A, A, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    zero = _dims(T=0, d=256, f=128)
+    assert f(ctypes.byref(zero), None, None, None, ctypes.byref(ex), None, None, None, None, 0, None) == moe.MOE_OK
