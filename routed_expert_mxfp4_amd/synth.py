@@ -263,10 +263,11 @@ def fp8_expert_sizes(cfg: Config) -> dict:
             "dn_codes": (d, f), "dn_scales": (d // 128, f // 128)}
 
 
-def gen_experts_fp8(cfg: Config, experts=None, device="cpu") -> dict:
+def gen_experts_fp8(cfg: Config, experts=None, device="cpu", chunk_experts: int = 32) -> dict:
     """FP8 expert tensors for the listed experts (default: all): gu_codes
     uint8 [n][2f][d], gu_scales fp32 [n][2f/128][d/128], dn_codes uint8
-    [n][d][f], dn_scales fp32 [n][d/128][f/128].  Needs d, f % 128 == 0."""
+    [n][d][f], dn_scales fp32 [n][d/128][f/128].  Needs d, f % 128 == 0.
+    Contiguous runs of expert ids are drawn in one go."""
     assert cfg.d % 128 == 0 and cfg.f % 128 == 0
     if experts is None:
         experts = range(cfg.E)
@@ -280,19 +281,24 @@ def gen_experts_fp8(cfg: Config, experts=None, device="cpu") -> dict:
     out = {}
     for name, shp in sizes.items():
         per = shp[0] * shp[1]
-        if name.endswith("codes"):
-            t = torch.empty((n,) + shp, dtype=torch.uint8, device=device)
-            flat = t.view(n, per)
-            for i, e in enumerate(experts):
-                b = random_bytes(keys[name], e * per, per, device)
-                flat[i] = torch.where((b & 0x7F) == 0x7F, b - 1, b)     # no NaN codes
-        else:
-            t = torch.empty((n,) + shp, dtype=torch.float32, device=device)
-            flat = t.view(n, per)
-            for i, e in enumerate(experts):
-                z = splitmix64(_arange(e * per, per, device), keys[name])
+        codes = name.endswith("codes")
+        t = torch.empty((n,) + shp, dtype=torch.uint8 if codes else torch.float32, device=device)
+        flat = t.view(n, per)
+        i = 0
+        while i < n:
+            j = i
+            while (j + 1 < n and experts[j + 1] == experts[j] + 1
+                   and j + 1 - i < chunk_experts):
+                j += 1
+            e0, cnt = experts[i], j - i + 1
+            if codes:
+                b = random_bytes(keys[name], e0 * per, cnt * per, device)
+                flat[i:i + cnt] = torch.where((b & 0x7F) == 0x7F, b - 1, b).view(cnt, per)
+            else:
+                z = splitmix64(_arange(e0 * per, cnt * per, device), keys[name])
                 u = _lsr(z, 40).to(torch.float64) * (1.0 / 16777216.0)     # 24-bit grid
-                flat[i] = ((1.0 + u) * 2.0 ** -8).to(torch.float32)        # exact in fp32
+                flat[i:i + cnt] = ((1.0 + u) * 2.0 ** -8).to(torch.float32).view(cnt, per)
+            i = j + 1
         out[name] = t
     return out
 
