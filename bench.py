@@ -69,6 +69,10 @@ def parse():
                     help="time the pre-norm MoE block (moe_block_forward: RMSNorm, the routed "
                          "layer, a bf16 shared expert of width f, the residual add) instead of "
                          "the routed layer alone")
+    ap.add_argument("--packed", action="store_true",
+                    help="prefill workloads: the experts re-laid once (before timing) in the "
+                         "scaled-MFMA GEMM's operand order (moe_prepack_experts), timed through "
+                         "moe_layer_forward_packed; the same bytes and the same results")
     ap.add_argument("--cpu-sample", type=int, default=2,
                     help="tokens of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-breakdown", action="store_true",
@@ -206,6 +210,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     mfma = (not fp8) and cfg.T >= MFMA_MIN_T and cfg.d % 512 == 0 and cfg.f % 256 == 0
+    if args.packed and not (mfma and cfg.f % 512 == 0 and not args.tail):
+        print("--packed needs a prefill workload on the scaled-MFMA path (d, f % 512 == 0), "
+              "without --tail", file=sys.stderr)
+        sys.exit(2)
     dominant = "fp8_gate_up" if fp8 else ("gate_up_mfma" if mfma else "gemv_gate_up")
     L = moe.lib()
 
@@ -217,7 +225,11 @@ def main():
     n_batches = min(cfg.batches, max(1, args.steps + args.warmup))
     xs = [synth.gen_x(cfg, b).to(dev) for b in range(n_batches)]
     act = moe.ACT_MX_E2M3 if args.act == "mx" else moe.ACT_BF16
-    if fp8:
+    if args.packed:
+        experts = moe.moe_prepack_experts(experts, cfg.d, cfg.f)   # outside the timed region
+        torch.cuda.synchronize()
+        layer = moe.PackedLayer(experts, wr, cfg.k, bias, T=cfg.T, act=act)
+    elif fp8:
         layer = moe.Fp8Layer(experts, wr, cfg.k, bias, T=cfg.T)
     elif args.tail:
         tail = {n: (v.to(dev) if hasattr(v, "to") else v)
@@ -246,6 +258,12 @@ def main():
                     ctypes.c_void_p(y.data_ptr()), None, None, ctypes.c_void_p(ws.data_ptr()),
                     ws.numel(), sptr) for x in xs]
         fwd, fname = L.moe_layer_forward_fp8, "moe_layer_forward_fp8"
+    elif args.packed:
+        argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()),
+                    ctypes.c_void_p(wr.data_ptr()), bptr, ctypes.byref(ex),
+                    ctypes.c_void_p(y.data_ptr()), None, None, ctypes.c_void_p(ws.data_ptr()),
+                    ws.numel(), sptr) for x in xs]
+        fwd, fname = L.moe_layer_forward_packed, "moe_layer_forward_packed"
     else:
         argsets = [(ctypes.byref(dims), ctypes.c_void_p(x.data_ptr()),
                     ctypes.c_void_p(wr.data_ptr()), bptr, ctypes.byref(ex),
@@ -328,7 +346,8 @@ def main():
         roofline = {"bound": "mfma", "kernel": dominant, "achieved": achieved,
                     "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / MXFP4_PEAK_TFLOPS,
-                    "traffic": traffic_from_profiles(dominant, args.workload, sha),
+                    "traffic": traffic_from_profiles(
+                        dominant, args.workload + ("-packed" if args.packed else ""), sha),
                     "algorithmic_flops_per_launch": flops_per_launch,
                     "mfma_passes_per_product": 1 if act else 2,
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
@@ -361,7 +380,9 @@ def main():
                    "f": cfg.f, "distinct_batches": n_batches,
                    "weights": ("FP8 (E4M3FN codes + fp32 scale per 128x128 block), resident in HBM"
                                if fp8 else
-                               "MXFP4 (E2M1 codes + E8M0 scale per 32), resident in HBM"),
+                               "MXFP4 (E2M1 codes + E8M0 scale per 32), resident in HBM" +
+                               (", in the GEMM's operand order (re-laid once before timing; "
+                                "same bytes)" if args.packed else "")),
                    "activations": ("MX E2M3, one term per 32 (activation-MX mode)" if act
                                    else "bf16"), "accumulate": "fp32",
                    "expert_path": ("FP8 dequant-GEMV" + (" (prefill floor)" if cfg.T >= MFMA_MIN_T

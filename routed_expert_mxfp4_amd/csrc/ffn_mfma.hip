@@ -367,6 +367,7 @@ struct GemmArgs {
     uint32_t boff, soff;        // this lane's offsets in its first B tile (codes, scales)
     uint32_t tq[8], ts[8];      // wave-uniform offsets of the 8 B tiles (codes, scales)
     uint32_t psel01;            // v_perm selector: byte g of two dwords
+    uint32_t cstep, sgrp;       // bytes from one K step's codes to the next, one scale group's
     int nsteps;
 };
 
@@ -418,15 +419,15 @@ template <int PS>
 __device__ __forceinline__ void issue_codes(BRing &br, const GemmArgs &ga, int j) {
     const uint32_t j0 = (uint32_t)min(j, ga.nsteps - 1), j1 = (uint32_t)min(j + 1, ga.nsteps - 1);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.q[PS][0][nt], ga.bq, ga.boff, ga.tq[nt] + j0 * 64u);
+    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.q[PS][0][nt], ga.bq, ga.boff, ga.tq[nt] + j0 * ga.cstep);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.q[PS][1][nt], ga.bq, ga.boff, ga.tq[nt] + j1 * 64u);
+    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.q[PS][1][nt], ga.bq, ga.boff, ga.tq[nt] + j1 * ga.cstep);
 }
 
 __device__ __forceinline__ void issue_scales(BRing &br, const GemmArgs &ga, int G) {
     const uint32_t gg = (uint32_t)min(G, (ga.nsteps - 1) >> 2);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.sraw[nt], ga.bs, ga.soff, ga.ts[nt] + gg * 16u);
+    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.sraw[nt], ga.bs, ga.soff, ga.ts[nt] + gg * ga.sgrp);
 }
 
 // After the last step some weight loads (the clamped re-loads past the end)
@@ -571,12 +572,16 @@ __device__ __forceinline__ bool select_tile(const int32_t *tiles, const int32_t 
 // kGateUp: A = split x (token rows), out = hq, the split of h = silu(gate) *
 //          up [rows][f] (expert-major rows), the down pass's A;
 // else:    A = hq, out = rows_out bf16 [rows][d].
+// packed: the weights are in the operand-order layout of prepack_kernel
+// (K % 512 == 0): each code load of a 16-row tile and K step reads 1 KB
+// contiguous, each scale load 256 B, instead of 16 rows x 64 B (16 B); the
+// registers receive the same bytes either way.
 template <bool kGateUp, bool kSingle>
 __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     const uint8_t *__restrict__ aq, ExpertArgs W, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
     const int32_t *__restrict__ tiles, uint8_t *__restrict__ hq, uint16_t *__restrict__ rows_out,
-    int T, int d, int E, int k, int f) {
+    int T, int d, int E, int k, int f, int packed) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ int a_rowidx[kBM];
     const int nrows = T * k;
@@ -612,11 +617,15 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
         const int wr = kGateUp ? (nt < 4 ? ts.nb * 256 + 64 * wid + 16 * nt
                                          : f + ts.nb * 256 + 64 * wid + 16 * (nt - 4))
                                : ts.nb * 512 + 128 * wid + 16 * nt;
-        ga.tq[nt] = (uint32_t)wr * code_row;
-        ga.ts[nt] = (uint32_t)wr * nblk;
+        // tile wr / 16 of the expert: (K / 128) code blocks of 1 KB and
+        // (K / 512) scale groups of 256 B when packed
+        ga.tq[nt] = packed ? (uint32_t)(wr >> 4) * (uint32_t)(K >> 7) * 1024u : (uint32_t)wr * code_row;
+        ga.ts[nt] = packed ? (uint32_t)(wr >> 4) * (uint32_t)(K >> 9) * 256u : (uint32_t)wr * nblk;
     }
-    ga.boff = (uint32_t)r16 * code_row + 16u * g;
-    ga.soff = (uint32_t)r16 * nblk;                 // nblk % 4 == 0: dword aligned
+    ga.boff = packed ? 16u * (uint32_t)lane : (uint32_t)r16 * code_row + 16u * g;
+    ga.soff = packed ? 16u * (uint32_t)r16 : (uint32_t)r16 * nblk;   // dword aligned
+    ga.cstep = packed ? 1024u : 64u;
+    ga.sgrp = packed ? 256u : 16u;
     ga.psel01 = (uint32_t)g | ((4u + (uint32_t)g) << 8);
     uint32_t src[kDmaPerWave];                      // byte offsets into aq (< 4 GiB)
 #pragma unroll
@@ -738,6 +747,46 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     }
 }
 
+// The operand-order ("packed") layout of one MXFP4 matrix [rows][K] per
+// expert, rows % 16 == 0, K % 512 == 0, the same bytes as the canonical one:
+//   codes: 1 KB block per (16-row tile t, K step s of 128), at
+//     (t * (K / 128) + s) * 1024; in it lane l = r + 16 g (r < 16, g < 4)
+//     holds, at 16 l, the 16 code bytes of row 16 t + r, K elements
+//     128 s + 32 g .. + 31 -- the B operand of one lane of the scaled MFMA;
+//   scales: 256 B block per (tile t, group G of 4 K steps), at
+//     (t * (K / 512) + G) * 256; row r's 16 scale bytes (blocks 16 G ..
+//     16 G + 15) at 16 r.
+// One thread per 16-byte piece; grid.y = 0 codes, 1 scales.
+__global__ __launch_bounds__(256) void prepack_kernel(const uint8_t *__restrict__ codes,
+                                                      const uint8_t *__restrict__ scales,
+                                                      uint8_t *__restrict__ pcodes,
+                                                      uint8_t *__restrict__ pscales, int E,
+                                                      int rows, int K) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t tiles = (size_t)(rows >> 4);
+    if (blockIdx.y == 0) {
+        const size_t S = (size_t)(K >> 7);
+        const size_t n = (size_t)E * tiles * S * 64;
+        if (i >= n) return;
+        const size_t l = i & 63, blk = i >> 6;          // blk = (e * tiles + t) * S + s
+        const size_t s = blk % S, et = blk / S;
+        const size_t e = et / tiles, t = et - e * tiles;
+        const size_t row = t * 16 + (l & 15), g = l >> 4;
+        const size_t src = (e * (size_t)rows + row) * (size_t)(K >> 1) + 64 * s + 16 * g;
+        reinterpret_cast<uint4 *>(pcodes)[i] = *reinterpret_cast<const uint4 *>(codes + src);
+    } else {
+        const size_t G = (size_t)(K >> 9);
+        const size_t n = (size_t)E * tiles * G * 16;
+        if (i >= n) return;
+        const size_t r = i & 15, blk = i >> 4;          // blk = (e * tiles + t) * G + q
+        const size_t q = blk % G, et = blk / G;
+        const size_t e = et / tiles, t = et - e * tiles;
+        const size_t row = t * 16 + r;
+        const size_t src = (e * (size_t)rows + row) * (size_t)(K >> 5) + 16 * q;
+        reinterpret_cast<uint4 *>(pscales)[i] = *reinterpret_cast<const uint4 *>(scales + src);
+    }
+}
+
 size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool g_attr_done = false;
@@ -804,7 +853,7 @@ hipError_t launch_mx_round_f32(const float *in, int rows, int K, float *out, hip
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                            const int32_t *sorted_rows, const int32_t *plan, uint16_t *rows_out,
                            void *ws, int T, int d, int E, int k, int f, bool single,
-                           hipStream_t s) {
+                           hipStream_t s, bool packed) {
     hipError_t e = set_lds_attrs();
     if (e != hipSuccess) return e;
     const size_t rows = (size_t)T * k;
@@ -828,7 +877,7 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
         (void)timed_launch("gate_up_mfma",
                            single ? ffn_mfma_kernel<true, true> : ffn_mfma_kernel<true, false>,
                            dim3((unsigned)blocks), dim3(256), kLdsBytes, s, xq, w, offsets,
-                           sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f);
+                           sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f, (int)packed);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     {
@@ -836,9 +885,29 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
         (void)timed_launch("down_mfma",
                            single ? ffn_mfma_kernel<false, true> : ffn_mfma_kernel<false, false>,
                            dim3((unsigned)blocks), dim3(256), kLdsBytes, s, hq, w, offsets,
-                           sorted_rows, plan, tiles, nullptr, rows_out, T, d, E, k, f);
+                           sorted_rows, plan, tiles, nullptr, rows_out, T, d, E, k, f, (int)packed);
     }
     return hipGetLastError();
+}
+
+bool prepack_ok(int d, int f) { return d % 512 == 0 && f % 512 == 0; }
+
+hipError_t launch_prepack(ExpertArgs src, ExpertArgs dst, int E, int d, int f, hipStream_t s) {
+    // gate/up: rows 2f, K = d; down: rows d, K = f
+    const int mats[2][2] = {{2 * f, d}, {d, f}};
+    for (int m = 0; m < 2; ++m) {
+        const int rows = mats[m][0], K = mats[m][1];
+        const size_t n_codes = (size_t)E * rows * (K / 32);     // 16-byte pieces
+        const size_t blocks = (n_codes + 255) / 256;             // >= the scale pieces' blocks
+        if (blocks == 0) continue;
+        prepack_kernel<<<dim3((unsigned)blocks, 2), 256, 0, s>>>(
+            m == 0 ? src.gu_codes : src.dn_codes, m == 0 ? src.gu_scales : src.dn_scales,
+            const_cast<uint8_t *>(m == 0 ? dst.gu_codes : dst.dn_codes),
+            const_cast<uint8_t *>(m == 0 ? dst.gu_scales : dst.dn_scales), E, rows, K);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace moe

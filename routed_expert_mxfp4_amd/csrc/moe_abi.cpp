@@ -7,6 +7,7 @@
 #include "../../include/moe.h"
 #include "../../include/moe_diag.h"
 #include "../../include/moe_fp8.h"
+#include "../../include/moe_packed.h"
 #include "../../include/moe_tail.h"
 
 #include <hip/hip_runtime.h>
@@ -253,7 +254,7 @@ namespace {
 hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *router_w,
                      const float *router_bias, const moe_mxfp4_experts &experts, uint16_t *y,
                      int32_t *topk_ids_out, float *topk_w_out, char *base, hipStream_t s,
-                     const uint16_t *resid, const float *extra) {
+                     const uint16_t *resid, const float *extra, bool packed = false) {
     const LayerWs L = layer_ws(D);
     const RouteWs RW = route_ws(D);
     float *logits = reinterpret_cast<float *>(base + L.route + RW.logits);
@@ -311,7 +312,7 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
             DiagScope t("mfma_ffn", s);
             e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
                                      base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f,
-                                     D.act == MOE_ACT_MX_E2M3, s);
+                                     D.act == MOE_ACT_MX_E2M3, s, packed);
         }
         if (e == hipSuccess) {
             e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s, resid, extra);
@@ -537,6 +538,60 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
         return device_status(run_layer(D, x, router_w, router_bias, *experts, y, topk_ids_out,
                                        topk_w_out, static_cast<char *>(ws),
                                        static_cast<hipStream_t>(hip_stream), nullptr, nullptr));
+    });
+}
+
+moe_status moe_prepack_experts(const moe_dims *dims, const moe_mxfp4_experts *src,
+                               const moe_mxfp4_experts *dst, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if ((st = check_experts(src)) != MOE_OK) return st;
+        if ((st = check_experts(dst)) != MOE_OK) return st;
+        if (!moe::prepack_ok(D.d, D.f)) return MOE_ERR_UNSUPPORTED;
+        // no overlap between any source array and any destination array
+        const size_t E = (size_t)D.E, d = (size_t)D.d, f = (size_t)D.f;
+        const void *sp[4] = {src->gu_codes, src->gu_scales, src->dn_codes, src->dn_scales};
+        const void *dp[4] = {dst->gu_codes, dst->gu_scales, dst->dn_codes, dst->dn_scales};
+        const size_t nb[4] = {E * 2 * f * (d / 2), E * 2 * f * (d / 32), E * d * (f / 2),
+                              E * d * (f / 32)};
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j) {
+                const uintptr_t a0 = (uintptr_t)sp[i], a1 = a0 + nb[i];
+                const uintptr_t b0 = (uintptr_t)dp[j], b1 = b0 + nb[j];
+                if (a0 < b1 && b0 < a1) return MOE_ERR_UNSUPPORTED;
+            }
+        const ExpertArgs S{src->gu_codes, src->gu_scales, src->dn_codes, src->dn_scales};
+        const ExpertArgs Dd{dst->gu_codes, dst->gu_scales, dst->dn_codes, dst->dn_scales};
+        return device_status(moe::launch_prepack(S, Dd, D.E, D.d, D.f,
+                                                 static_cast<hipStream_t>(hip_stream)));
+    });
+}
+
+moe_status moe_layer_forward_packed(const moe_dims *dims, const uint16_t *x,
+                                    const uint16_t *router_w, const float *router_bias,
+                                    const moe_mxfp4_experts *packed, uint16_t *y,
+                                    int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                                    size_t ws_bytes, void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (D.T == 0) return MOE_OK;
+        if (!moe::prepack_ok(D.d, D.f) || !moe::mfma_path_ok(D.T, D.d, D.k, D.f))
+            return MOE_ERR_UNSUPPORTED;
+        if (!x || !router_w || !y) return MOE_ERR_NULL;
+        if ((st = check_experts(packed)) != MOE_OK) return st;
+        if (!aligned16(x) || !aligned16(router_w) || !aligned16(y)) return MOE_ERR_ALIGN;
+        const LayerWs L = layer_ws(D);
+        if (!ws) return MOE_ERR_NULL;
+        if (!aligned16(ws)) return MOE_ERR_ALIGN;
+        if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+        return device_status(run_layer(D, x, router_w, router_bias, *packed, y, topk_ids_out,
+                                       topk_w_out, static_cast<char *>(ws),
+                                       static_cast<hipStream_t>(hip_stream), nullptr, nullptr,
+                                       true));
     });
 }
 

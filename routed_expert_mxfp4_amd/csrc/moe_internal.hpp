@@ -225,7 +225,12 @@ size_t mfma_ws_bytes(int T, int d, int E, int k, int f);
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                            const int32_t *sorted_rows, const int32_t *plan, uint16_t *rows_out,
                            void *ws, int T, int d, int E, int k, int f, bool single,
-                           hipStream_t s);
+                           hipStream_t s, bool packed = false);
+// The operand-order layout of the MXFP4 store for the scaled-MFMA GEMM (same
+// bytes; needs d % 512 == 0 and f % 512 == 0): dst = prepack(src), dst must
+// not overlap src.
+bool prepack_ok(int d, int f);
+hipError_t launch_prepack(ExpertArgs src, ExpertArgs dst, int E, int d, int f, hipStream_t s);
 // The activation-MX rounding of rows x K (K % 32 == 0): every 32-element
 // block to its one-term MX E2M3 value (out may be in).
 hipError_t launch_mx_round_bf16(const uint16_t *in, int rows, int K, uint16_t *out,

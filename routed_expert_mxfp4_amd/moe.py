@@ -1,5 +1,5 @@
 """Thin Python binding of the C ABI in ``include/moe.h``,
-``include/moe_tail.h`` and ``include/moe_fp8.h``.
+``include/moe_tail.h``, ``include/moe_fp8.h`` and ``include/moe_packed.h``.
 
 Argument marshalling only: every step of the layer runs in the HIP kernels
 of ``libmoe_mxfp4.so``.  Torch supplies device memory (outputs and
@@ -54,7 +54,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_diag_time_kernel", "moe_diag_kernel_time", "moe_diag_mx_split_e2m3",
            "moe_block_workspace_bytes", "moe_rmsnorm", "moe_block_forward",
-           "moe_fp8_workspace_bytes", "moe_expert_ffn_fp8", "moe_layer_forward_fp8")
+           "moe_fp8_workspace_bytes", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
+           "moe_prepack_experts", "moe_layer_forward_packed")
 
 _lib = None
 
@@ -94,6 +95,10 @@ def lib():
         L.moe_expert_ffn_fp8.argtypes = [DP, P, FP, P, P, P, P, S, P]
         L.moe_layer_forward_fp8.restype = I
         L.moe_layer_forward_fp8.argtypes = [DP, P, P, P, FP, P, P, P, P, S, P]
+        L.moe_prepack_experts.restype = I
+        L.moe_prepack_experts.argtypes = [DP, EP, EP, P]
+        L.moe_layer_forward_packed.restype = I
+        L.moe_layer_forward_packed.argtypes = [DP, P, P, P, EP, P, P, P, P, S, P]
         TP = ctypes.POINTER(TailWeights)
         L.moe_block_workspace_bytes.restype = S
         L.moe_block_workspace_bytes.argtypes = [DP, TP]
@@ -466,6 +471,50 @@ def moe_layer_forward_fp8(x, router_w, experts: dict, k, router_bias=None,
     x = _bits16(x)
     T = x.shape[0]
     layer = Fp8Layer(experts, router_w, k, router_bias, T=T)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
+    y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)
+    return (y, ids, w) if return_routing else y
+
+
+# ---- operand-order (packed) expert store (include/moe_packed.h) ---------------------
+def moe_prepack_experts(experts: dict, d: int, f: int, stream=None) -> dict:
+    """The packed layout of an MXFP4 store (new tensors of the same shapes)."""
+    E = experts["gu_codes"].shape[0]
+    dims = dims_of(1, d, E, 1, f)
+    out = {n: torch.empty_like(v) for n, v in experts.items()
+           if n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")}
+    src, dst = experts_of(experts), experts_of(out)
+    st = lib().moe_prepack_experts(ctypes.byref(dims), ctypes.byref(src), ctypes.byref(dst),
+                                   _stream(stream))
+    _check(st, "moe_prepack_experts")
+    return out
+
+
+class PackedLayer(Layer):
+    """moe_layer_forward_packed with a reusable workspace (prefill-sized T)."""
+
+    def forward(self, x, y=None, topk_ids=None, topk_w=None, stream=None):
+        x = _bits16(x)
+        T = x.shape[0]
+        self.reserve(T)
+        if y is None:
+            y = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
+        dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
+        st = lib().moe_layer_forward_packed(ctypes.byref(dims), _ptr(x), _ptr(self.router_w),
+                                            _ptr(self.bias), ctypes.byref(self._ex), _ptr(y),
+                                            _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
+                                            self._ws.numel(), _stream(stream))
+        _check(st, "moe_layer_forward_packed")
+        return y
+
+
+def moe_layer_forward_packed(x, router_w, packed: dict, k, router_bias=None,
+                             return_routing=False, stream=None, act=ACT_BF16):
+    """The layer on a packed store (T >= 128).  Returns y (and topk_ids, topk_w)."""
+    x = _bits16(x)
+    T = x.shape[0]
+    layer = PackedLayer(packed, router_w, k, router_bias, T=T, act=act)
     ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
     w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
     y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)

@@ -213,3 +213,26 @@ def test_fp8_entries_refuse_bad_arguments(L):
     assert e(ctypes.byref(dims), A, ctypes.byref(ex), A, A, A, A, need - 1, None) == moe.MOE_ERR_WORKSPACE
     zero = _dims(T=0, d=256, f=128)
     assert f(ctypes.byref(zero), None, None, None, ctypes.byref(ex), None, None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_packed_entries_refuse_bad_arguments(L):
+    A = ctypes.c_void_p(0x10000)
+    big = 1 << 40
+    ex = moe.Experts(0x10000, 0x10000, 0x10000, 0x10000)
+    exo = moe.Experts(0x100000000, 0x200000000, 0x300000000, 0x400000000)
+    dims = _dims(T=256, d=512, E=16, k=2, f=512)
+    p = L.moe_prepack_experts
+    assert p(ctypes.byref(_dims(d=256, f=128)), ctypes.byref(ex), ctypes.byref(exo), None) == moe.MOE_ERR_UNSUPPORTED
+    assert p(ctypes.byref(dims), ctypes.byref(ex), None, None) == moe.MOE_ERR_NULL
+    # destination overlapping the source
+    assert p(ctypes.byref(dims), ctypes.byref(ex), ctypes.byref(ex), None) == moe.MOE_ERR_UNSUPPORTED
+    f = L.moe_layer_forward_packed
+    small = _dims(T=64, d=512, E=16, k=2, f=512)          # below the prefill path
+    assert f(ctypes.byref(small), A, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_UNSUPPORTED
+    odd = _dims(T=256, d=512, E=16, k=2, f=256)           # f % 512 != 0
+    assert f(ctypes.byref(odd), A, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_UNSUPPORTED
+    assert f(ctypes.byref(dims), None, A, None, ctypes.byref(ex), A, None, None, A, big, None) == moe.MOE_ERR_NULL
+    need = moe.moe_workspace_bytes(dims, moe.ENTRY_LAYER_FORWARD)
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(ex), A, None, None, A, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    zero = _dims(T=0, d=512, f=512)
+    assert f(ctypes.byref(zero), None, None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
