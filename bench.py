@@ -337,8 +337,9 @@ def main():
                     "traffic": traffic_from_profiles(dominant, args.workload, sha),
                     "algorithmic_flops_per_launch": flops_per_launch,
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
-    elif mfma:
-        # gate/up: every routed row times the [2f x d] gate/up matrix
+    elif mfma and layer_flops / layer_bytes >= MXFP4_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3:
+        # past the ridge (10.1 PFLOP/s / 8 TB/s = 1262 flop/B): the matrix
+        # cores bound the gate/up GEMM (every routed row times [2f x d])
         flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
         achieved = flops_per_launch / avg_launch_s / 1e12
         src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_mfma.hip")
@@ -349,6 +350,25 @@ def main():
                     "traffic": traffic_from_profiles(
                         dominant, args.workload + ("-packed" if args.packed else ""), sha),
                     "algorithmic_flops_per_launch": flops_per_launch,
+                    "mfma_passes_per_product": 1 if act else 2,
+                    "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
+    elif mfma:
+        # below the ridge: HBM bounds the layer (every touched expert's
+        # weights read once); the gate/up GEMM's bytes are its experts'
+        # gate/up matrices, its flops are reported beside them
+        bytes_per_launch = mean_touched * per_expert_gu
+        flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
+        achieved = bytes_per_launch / avg_launch_s / 1e9
+        src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_mfma.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                    "traffic": traffic_from_profiles(
+                        dominant, args.workload + ("-packed" if args.packed else ""), sha),
+                    "algorithmic_bytes_per_launch": bytes_per_launch,
+                    "layer_flop_per_byte": layer_flops / layer_bytes,
+                    "mxfp4_tflops": flops_per_launch / avg_launch_s / 1e12,
+                    "mxfp4_frac": flops_per_launch / avg_launch_s / 1e12 / MXFP4_PEAK_TFLOPS,
                     "mfma_passes_per_product": 1 if act else 2,
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
     else:
