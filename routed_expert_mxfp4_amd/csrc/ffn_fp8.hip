@@ -209,6 +209,111 @@ __global__ __launch_bounds__(256) void fp8_down_kernel(
     }
 }
 
+// Decode-sized T (<= 8 rows per expert): the gate and up rows of a wave's
+// pairs are streamed one row at a time, double-buffered -- the next row's
+// loads (d bytes of codes and its block scales) are in flight while the
+// current row is reduced -- against the token row staged once in LDS.  Lane
+// l owns the 16-code chunks l + 64 i (i < NCL) of every row.
+constexpr int kRxPairs8 = 32;       // pairs per block (8 per wave)
+constexpr int kStageX8 = 4;         // x staging: d <= 4 * 256 * 8 = 8192
+
+template <int NCL>
+struct Row8 {
+    uint4 c[NCL];
+    float s[NCL];
+};
+
+template <int NCL>
+__device__ __forceinline__ void load_row8(const uint8_t *codes, const float *scales, int row,
+                                          int d, int sbk, int nch, int lane, Row8<NCL> &rb) {
+    const uint4 *r = reinterpret_cast<const uint4 *>(codes + (size_t)row * d);
+    const float *sr = scales + (size_t)(row >> 7) * sbk;
+#pragma unroll
+    for (int i = 0; i < NCL; ++i) {
+        const int c = min(lane + 64 * i, nch - 1);
+        rb.c[i] = r[c];
+        rb.s[i] = sr[c >> 3];
+    }
+}
+
+template <int NCL>
+__device__ __forceinline__ float row_dot8(const Row8<NCL> &rb, const uint4 *__restrict__ xs,
+                                          int lane, int nch) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCL; ++i) {
+        const int c = lane + 64 * i;
+        const int cc = min(c, nch - 1);
+        const float p = dot16_fp8_bf16(rb.c[i], xs[2 * cc], xs[2 * cc + 1], 0.f);
+        acc += c < nch ? p * rb.s[i] : 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return wave_sum_f32(acc);
+}
+
+template <int NCL>
+__global__ __launch_bounds__(256) void fp8_gate_up_rx_kernel(
+    const uint16_t *__restrict__ x, Fp8Args W, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
+    float *__restrict__ h, int T, int d, int E, int k, int f) {
+    const int nrows = T * k;
+    int e, row0, ne;
+    if (!group8(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
+    extern __shared__ uint4 xs[];                         // d / 8 x 16 B, + 1 spare
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nch = d >> 4, nvec = d >> 3, sbk = d >> 7;
+    const uint8_t *codes = W.gu_codes + (size_t)e * 2 * f * d;
+    const float *scales = W.gu_scales + (size_t)e * (2 * f >> 7) * sbk;
+    constexpr int kPerWave = kRxPairs8 / 4;               // pairs n_base + 4 q
+    const int n_base = blockIdx.x * kRxPairs8 + wid;
+    for (int r = 0; r < ne; ++r) {
+        const int row = sorted_rows[row0 + r];
+        const int tok = (unsigned)row < (unsigned)nrows ? row / k : 0;
+        Row8<NCL> A, B;
+        load_row8<NCL>(codes, scales, n_base, d, sbk, nch, lane, A);   // before the x sync
+        __syncthreads();
+        {
+            const uint4 *xrow = reinterpret_cast<const uint4 *>(x + (size_t)tok * d);
+            uint4 tmp[kStageX8];
+#pragma unroll
+            for (int j = 0; j < kStageX8; ++j)
+                tmp[j] = xrow[min((int)threadIdx.x + 256 * j, nvec - 1)];
+            loads_done(tmp);
+#pragma unroll
+            for (int j = 0; j < kStageX8; ++j) {
+                const int i = (int)threadIdx.x + 256 * j;
+                xs[i < nvec ? i : nvec] = tmp[j];
+            }
+        }
+        __syncthreads();
+        float *hrow = h + (size_t)(row0 + r) * f;
+#pragma unroll 1
+        for (int q = 0; q < kPerWave; ++q) {
+            const int n = n_base + 4 * q;
+            load_row8<NCL>(codes, scales, f + n, d, sbk, nch, lane, B);          // up row
+            __builtin_amdgcn_sched_barrier(0);
+            const float g = row_dot8<NCL>(A, xs, lane, nch);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q + 1 < kPerWave)
+                load_row8<NCL>(codes, scales, n + 4, d, sbk, nch, lane, A);     // next gate row
+            __builtin_amdgcn_sched_barrier(0);
+            const float u = row_dot8<NCL>(B, xs, lane, nch);
+            if (lane == 0) hrow[n] = silu_mul8(g, u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <int NCL>
+hipError_t launch_fp8_rx(const uint16_t *x, Fp8Args w, const int32_t *offsets,
+                         const int32_t *sorted_rows, const int32_t *plan, float *h, int T, int d,
+                         int E, int k, int f, int amax, hipStream_t s) {
+    return timed_launch("fp8_gate_up", fp8_gate_up_rx_kernel<NCL>, dim3(f / kRxPairs8, amax),
+                        dim3(256), (size_t)d * 2 + 16, s, x, w, offsets, sorted_rows, plan, h, T,
+                        d, E, k, f);
+}
+
 }  // namespace
 
 hipError_t launch_fp8_gate_up(const uint16_t *x, Fp8Args w, const int32_t *offsets,
@@ -216,6 +321,18 @@ hipError_t launch_fp8_gate_up(const uint16_t *x, Fp8Args w, const int32_t *offse
                               int d, int E, int k, int f, hipStream_t s) {
     const int amax = min(E, T * k);
     if (amax <= 0) return hipSuccess;
+    if (T <= 8 && d <= 8192 && f % kRxPairs8 == 0) {
+        switch ((d + 1023) / 1024) {                      // 16-code chunks per lane
+        case 1: return launch_fp8_rx<1>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        case 2: return launch_fp8_rx<2>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        case 3: return launch_fp8_rx<3>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        case 4: return launch_fp8_rx<4>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        case 5: return launch_fp8_rx<5>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        case 6: return launch_fp8_rx<6>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        case 7: return launch_fp8_rx<7>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        default: return launch_fp8_rx<8>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        }
+    }
     const int rpp = max(1, min(kRows8, 32768 / d));      // <= 64 KB of LDS
     return timed_launch("fp8_gate_up", fp8_gate_up_kernel, dim3(f / kPairs8, amax), dim3(256),
                         (size_t)rpp * d * 2, s, x, w, offsets, sorted_rows, plan, h, T, d, E, k,
