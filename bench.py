@@ -287,7 +287,8 @@ def main():
     run(args.warmup, args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    dom_ms, dom_n = moe.diag_kernel_time()
+    per_launch = moe.diag_kernel_times(max(1, args.steps))
+    dom_ms, dom_n = sum(per_launch), len(per_launch)
     moe.diag_time_kernel(None, 0)
     elapsed = t1 - t0
 
@@ -321,6 +322,11 @@ def main():
     torch.cuda.synchronize()
     mean_touched = sum(touched) / len(touched)
     avg_launch_s = (dom_ms / dom_n) * 1e-3 if dom_n else float("nan")
+    pl = sorted(per_launch)
+
+    def pct(q):
+        return 1e3 * pl[min(len(pl) - 1, int(q * (len(pl) - 1) + 0.5))] if pl else None
+    launch_pct = {"p10_us": pct(0.10), "p50_us": pct(0.50), "p90_us": pct(0.90)}
     tokens = args.steps * cfg.T
     value = tokens / elapsed
     layer_bytes = mean_touched * cfg.expert_bytes
@@ -383,6 +389,7 @@ def main():
                     "algorithmic_bytes_per_launch": bytes_per_launch,
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
 
+    roofline["launch_us_percentiles"] = launch_pct
     out = {
         "metric": "MoE-layer tokens/s + expert-weight GB/s (decode) / MXFP4 TFLOP/s (prefill), 1 GPU",
         "value": value,

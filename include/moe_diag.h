@@ -10,7 +10,10 @@
  * "down_combine", "combine", "mfma_ffn" (the whole scaled-MFMA expert
  * FFN of large T), its parts "mx_split_x", "gate_up_mfma" (which also
  * splits h) and "down_mfma", and "mx_round" (the activation-MX mode's
- * rounding of x and h on the GEMV paths).
+ * rounding of x and h on the GEMV paths); for FP8 experts "fp8_gate_up" and
+ * "fp8_down"; for the pre-norm block "rmsnorm", "shared_gate_up",
+ * "shared_down_add", "shared_gemm_gate_up", "shared_swiglu" and
+ * "shared_gemm_down".
  */
 #ifndef ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 #define ROUTED_EXPERT_MXFP4_MOE_DIAG_H
@@ -54,6 +57,13 @@ int moe_diag_time_kernel(const char *kernel, int capacity);
  * Call only after the device has been synchronised.  Clears
  * the records (timing stays on).  Returns 0, or -1 on a HIP error. */
 int moe_diag_kernel_time(double *total_ms, long long *launches);
+
+/* The elapsed time (ms) of each recorded launch, in launch order: up to
+ * `cap` of them into ms_out (host memory), their number into *launches.
+ * Call only after the device has been synchronised.  Clears the records
+ * like moe_diag_kernel_time.  Returns 0, or -1 on a HIP error or bad
+ * arguments. */
+int moe_diag_kernel_times(double *ms_out, int cap, long long *launches);
 
 #ifdef __cplusplus
 }

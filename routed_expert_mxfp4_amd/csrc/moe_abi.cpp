@@ -843,4 +843,23 @@ int moe_diag_kernel_time(double *total_ms, long long *launches) {
     }
 }
 
+int moe_diag_kernel_times(double *ms_out, int cap, long long *launches) {
+    try {
+        if (cap < 0 || (cap > 0 && !ms_out)) return -1;
+        std::lock_guard<std::mutex> lk(g_diag.mu);
+        int rc = 0;
+        for (int i = 0; i < g_diag.used && i < cap; ++i) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, g_diag.ev[2 * i], g_diag.ev[2 * i + 1]) != hipSuccess)
+                rc = -1;
+            ms_out[i] = ms;
+        }
+        if (launches) *launches = g_diag.used;
+        g_diag.used = 0;
+        return rc;
+    } catch (...) {
+        return -1;
+    }
+}
+
 }  // extern "C"

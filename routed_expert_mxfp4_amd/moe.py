@@ -55,7 +55,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_diag_time_kernel", "moe_diag_kernel_time", "moe_diag_mx_split_e2m3",
            "moe_block_workspace_bytes", "moe_rmsnorm", "moe_block_forward",
            "moe_fp8_workspace_bytes", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
-           "moe_prepack_experts", "moe_layer_forward_packed")
+           "moe_prepack_experts", "moe_layer_forward_packed", "moe_diag_kernel_times")
 
 _lib = None
 
@@ -110,6 +110,9 @@ def lib():
         L.moe_diag_time_kernel.argtypes = [ctypes.c_char_p, I]
         L.moe_diag_mx_split_e2m3.restype = I
         L.moe_diag_mx_split_e2m3.argtypes = [P, I, I, I, P, P]
+        L.moe_diag_kernel_times.restype = I
+        L.moe_diag_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_double), I,
+                                            ctypes.POINTER(ctypes.c_longlong)]
         L.moe_diag_kernel_time.restype = I
         L.moe_diag_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_longlong)]
@@ -131,6 +134,16 @@ def diag_kernel_time():
     if lib().moe_diag_kernel_time(ctypes.byref(ms), ctypes.byref(n)) != 0:
         raise RuntimeError("moe_diag_kernel_time failed")
     return ms.value, n.value
+
+
+def diag_kernel_times(cap: int):
+    """Per-launch times (ms, launch order) recorded since the last call;
+    synchronise first."""
+    buf = (ctypes.c_double * max(cap, 1))()
+    n = ctypes.c_longlong(0)
+    if lib().moe_diag_kernel_times(buf, int(cap), ctypes.byref(n)) != 0:
+        raise RuntimeError("moe_diag_kernel_times failed")
+    return [buf[i] for i in range(min(cap, n.value))]
 
 
 def diag_mx_split_e2m3(rows_tensor, stream=None):
