@@ -90,8 +90,9 @@ typedef struct moe_dims {
  *   gu_scales [E][2f][d/32]  E8M0 scale codes
  *   dn_codes  [E][d][f/2]    E2M1 codes of the down matrix (K = f)
  *   dn_scales [E][d][f/32]
- * 3*d*f*17/32 bytes per expert; kernels read these bytes as they are (no
- * dequantised or repacked copy). */
+ * 3*d*f*17/32 bytes per expert; the entry points here read these bytes as
+ * they are (no dequantised or repacked copy).  moe_packed.h adds a one-time
+ * re-layout of the same bytes for the prefill GEMM. */
 typedef struct moe_mxfp4_experts {
     const uint8_t *gu_codes;
     const uint8_t *gu_scales;
@@ -105,7 +106,7 @@ typedef enum moe_status {
     MOE_ERR_SHAPE = 2,       /* dims outside the limits above              */
     MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned           */
     MOE_ERR_WORKSPACE = 4,   /* ws_bytes < moe_workspace_bytes(...)        */
-    MOE_ERR_UNSUPPORTED = 5, /* valid request this build does not serve    */
+    MOE_ERR_UNSUPPORTED = 5, /* valid request the library does not serve   */
     MOE_ERR_DEVICE = 6       /* HIP reported an error while launching      */
 } moe_status;
 

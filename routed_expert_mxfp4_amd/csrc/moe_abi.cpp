@@ -366,7 +366,7 @@ const char *moe_status_str(int status) {
     case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: dims outside the supported limits";
     case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a pointer is not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes()";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: request not served by this build";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid request this library does not serve";
     case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: HIP reported an error while launching";
     default: return "unknown moe_status";
     }

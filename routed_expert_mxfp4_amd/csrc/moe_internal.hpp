@@ -14,7 +14,7 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Fixed limits of this build (checked on the host before any launch).
+// Fixed limits of the library (checked on the host before any launch).
 // ---------------------------------------------------------------------------
 constexpr int kMaxExperts = 1024;   // top-k keeps <= 16 logits per lane
 constexpr int kMaxTopK = 32;
