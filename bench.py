@@ -42,7 +42,7 @@ DEFAULT_STEPS = {"tiny": 1000, "decode": 1000, "batched-decode": 200, "zipf-pref
                  "fp8-prefill": 3}
 VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published (the FP8 prefill floor's bound)
 KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm",
-           "router_refine", "permute", "topk_permute", "gemv_gate_up",
+           "router_select", "router_refine", "permute", "topk_permute", "gemv_gate_up",
            "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "down_mfma",
            "combine", "fp8_gate_up", "fp8_down")
 # the pre-norm block's own kernels (--tail)

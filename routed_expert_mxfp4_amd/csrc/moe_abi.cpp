@@ -58,9 +58,9 @@ moe_status device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E
 
 // ---- workspace layouts ------------------------------------------------------
 // Route: logits (the canonical ones, or the filter's approximations) and
-// the row norms of the filtered path.
+// the row norms and candidate lists of the filtered path.
 struct RouteWs {
-    size_t logits, nx, nw, total;
+    size_t logits, nx, nw, cand, ncand, total;
 };
 RouteWs route_ws(const moe_dims &D) {
     RouteWs w;
@@ -68,6 +68,8 @@ RouteWs route_ws(const moe_dims &D) {
     w.logits = p; p += al256((size_t)D.T * D.E * 4);
     w.nx = p; p += al256((size_t)D.T * 4);
     w.nw = p; p += al256((size_t)D.E * 4);
+    w.cand = p; p += al256((size_t)D.T * moe::kRouteCandMax * 4);
+    w.ncand = p; p += al256((size_t)D.T * 4);
     w.total = p;
     return w;
 }
@@ -280,8 +282,10 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
     if (filtered) {
         e = moe::launch_route_filtered(x, router_w, router_bias, logits,
                                        reinterpret_cast<float *>(base + L.route + RW.nx),
-                                       reinterpret_cast<float *>(base + L.route + RW.nw), ids,
-                                       tw, D.T, D.d, D.E, D.k, s);
+                                       reinterpret_cast<float *>(base + L.route + RW.nw),
+                                       reinterpret_cast<int32_t *>(base + L.route + RW.cand),
+                                       reinterpret_cast<int32_t *>(base + L.route + RW.ncand),
+                                       ids, tw, D.T, D.d, D.E, D.k, s);
     } else {
         e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
     }
@@ -406,7 +410,9 @@ moe_status moe_route(const moe_dims *dims, const uint16_t *x, const uint16_t *ro
             e = moe::launch_route_filtered(x, router_w, router_bias,
                                            reinterpret_cast<float *>(base + R.logits),
                                            reinterpret_cast<float *>(base + R.nx),
-                                           reinterpret_cast<float *>(base + R.nw), topk_ids,
+                                           reinterpret_cast<float *>(base + R.nw),
+                                           reinterpret_cast<int32_t *>(base + R.cand),
+                                           reinterpret_cast<int32_t *>(base + R.ncand), topk_ids,
                                            topk_w, D.T, D.d, D.E, D.k, s);
             return device_status(e);
         }
@@ -673,8 +679,10 @@ moe_status moe_layer_forward_fp8(const moe_dims *dims, const uint16_t *x,
         if (moe::route_filter_ok(D.T, D.d, D.E)) {
             e = moe::launch_route_filtered(x, router_w, router_bias, logits,
                                            reinterpret_cast<float *>(base + L.route + RW.nx),
-                                           reinterpret_cast<float *>(base + L.route + RW.nw), ids,
-                                           tw, D.T, D.d, D.E, D.k, s);
+                                           reinterpret_cast<float *>(base + L.route + RW.nw),
+                                           reinterpret_cast<int32_t *>(base + L.route + RW.cand),
+                                           reinterpret_cast<int32_t *>(base + L.route + RW.ncand),
+                                           ids, tw, D.T, D.d, D.E, D.k, s);
             if (e == hipSuccess)
                 e = moe::launch_permute(ids, counts, offsets, sorted_rows, row_pos, plan, D.T,
                                         D.E, D.k, base + L.perm, s);

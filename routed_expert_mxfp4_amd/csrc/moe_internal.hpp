@@ -175,11 +175,14 @@ hipError_t launch_topk_softmax(const float *logits, int32_t *ids, float *w, int 
                                int k, hipStream_t s);
 // Many tokens: top-k + softmax of the canonical logits without computing all
 // of them (bf16 MFMA filter, certified bounds, canonical refinement).
-// zt: fp32 [T][E] scratch, nx: fp32 [T], nw: fp32 [E] scratch.
+// zt: fp32 [T][E] scratch, nx: fp32 [T], nw: fp32 [E] scratch; cand: int32
+// [T][kRouteCandMax] and ncand: int32 [T] scratch (each token's candidates).
+constexpr int kRouteCandMax = 64;
 bool route_filter_ok(int T, int d, int E);
 hipError_t launch_route_filtered(const uint16_t *x, const uint16_t *wr, const float *bias,
-                                 float *zt, float *nx, float *nw, int32_t *ids, float *tw,
-                                 int T, int d, int E, int k, hipStream_t s);
+                                 float *zt, float *nx, float *nw, int32_t *cand, int32_t *ncand,
+                                 int32_t *ids, float *tw, int T, int d, int E, int k,
+                                 hipStream_t s);
 
 size_t permute_ws_bytes(int T, int E);
 // plan (nullable): int32 [1 + E] = number of active experts, then their ids.

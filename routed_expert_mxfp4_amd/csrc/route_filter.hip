@@ -12,16 +12,20 @@
 //        |z_te - (zt_te + b_e)| <= B_te
 //        B_te = gamma |x_t| |w_e| (1 + 2^-20) + 2^-23 (|zt_te + b_e| + gamma |x_t| |w_e|)
 //               + 1e-30
-//      with gamma = 2 (d + 64) 2^-23 / (1 - 2 (d + 64) 2^-23): twice the
-//      classic bound (d u / (1 - d u)) sum |x_i w_i| of any fp32 summation
-//      order (u = 2^-23 also covers truncating adders), Cauchy-Schwarz for
-//      sum |x_i w_i| <= |x_t| |w_e|, and 2^-23 |z| for the final rounding of
-//      the canonical value.  Rows holding a subnormal, infinite or NaN bf16
-//      get an infinite norm (no finite interval), which forces the exact
-//      path below.
+//      with gamma = 2 (d/64 + 128) 2^-23 / (1 - 2 (d/64 + 128) 2^-23).  The
+//      GEMM sums each 64-wide K stage on its own (two chained MFMAs, the
+//      first from zero: 64 products in any internal order, at most 63
+//      roundings) and adds the d/64 stage sums in fp32, so the error is at
+//      most (63 + d/64) u sum |x_i w_i| to first order, whatever order and
+//      rounding the MFMA uses inside (u = 2^-23 also covers truncating
+//      adders); gamma doubles that with room to spare, Cauchy-Schwarz gives
+//      sum |x_i w_i| <= |x_t| |w_e|, and 2^-23 |z| covers the final rounding
+//      of the canonical value.  Rows holding a subnormal, infinite or NaN
+//      bf16 get an infinite norm (no finite interval), which forces the
+//      exact path below.
 //   3. tau = the k-th largest lower end.  An expert whose upper end is
 //      below tau is below k others for certain, so it is not selected; the
-//      canonical logits of the others (the candidates, usually ~20) are
+//      canonical logits of the others (the candidates, usually ~17) are
 //      computed exactly, and top-k + softmax run over them with the
 //      non-candidates at -inf.  A token with any non-finite interval, or
 //      more than kCandMax candidates (e.g. massively tied logits), takes
@@ -37,7 +41,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kCandMax = 64;
+constexpr int kCandMax = kRouteCandMax;
 
 // ---------------------------------------------------------------------------
 // Row norms in fp64, rounded up to fp32; +inf if the row holds a subnormal,
@@ -136,6 +140,10 @@ __global__ __launch_bounds__(256) void filter_gemm_kernel(const uint16_t *__rest
             ra[i] = *reinterpret_cast<const uint4 *>(pa[i] + koff);
             rb[i] = *reinterpret_cast<const uint4 *>(pb[i] + koff);
         }
+        // this stage's products summed on their own (the first MFMA starts
+        // from zero), then added to the running sum in fp32: the summation
+        // chains stay short, which keeps the certified bound tight
+        f32x4_t part[4][4];
 #pragma unroll
         for (int ks = 0; ks < kFK / 32; ++ks) {
             bf16x8_t af[4], bfr[4];
@@ -151,9 +159,16 @@ __global__ __launch_bounds__(256) void filter_gemm_kernel(const uint16_t *__rest
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
-                    acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bfr[nt],
-                                                                          acc[mt][nt], 0, 0, 0);
+                    part[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        af[mt], bfr[nt], ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : part[mt][nt],
+                        0, 0, 0);
         }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][nt][i] += part[mt][nt][i];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             *reinterpret_cast<uint4 *>(nxt + so[i]) = ra[i];
@@ -177,8 +192,8 @@ __global__ __launch_bounds__(256) void filter_gemm_kernel(const uint16_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// Certified selection + canonical refinement + top-k/softmax: one wave per
-// token.
+// Certified selection (one wave per token), canonical refinement (one
+// block per token); top-k/softmax then runs over the masked rows.
 // ---------------------------------------------------------------------------
 // fp32 bounds that contain a finite double: round toward -inf / +inf (one
 // step of the fp32 grid when the nearest rounding went the wrong way).
@@ -248,19 +263,19 @@ __device__ __forceinline__ float canonical_from_regs(const uint4 (&xq)[NQ], cons
     return (float)(acc + bias);
 }
 
-template <int PL, int NQ>
-__global__ __launch_bounds__(256) void select_refine_kernel(
-    const float *__restrict__ zt, const float *__restrict__ nx, const float *__restrict__ nw,
-    const float *__restrict__ bias, const uint16_t *__restrict__ x,
-    const uint16_t *__restrict__ wr, int32_t *__restrict__ ids, float *__restrict__ tw, int T,
-    int d, int E, int k, double gamma) {
-    extern __shared__ float srow[];                        // [4][E] masked canonical logits
-    __shared__ int cand[4][kCandMax];
-    __shared__ __align__(16) uint32_t tsc[4][kTopkScratch];
+// Per token (one wave): the certified intervals, tau and the candidate
+// list, written to cand[t][..] with their number in ncand_out[t] (-1: the
+// token takes all E canonical logits); the token's zt row is overwritten
+// with -inf, to be filled in at the candidates by refine_kernel.
+template <int PL>
+__global__ __launch_bounds__(256) void select_cand_kernel(
+    float *__restrict__ zt, const float *__restrict__ nx, const float *__restrict__ nw,
+    const float *__restrict__ bias, int32_t *__restrict__ cand, int32_t *__restrict__ ncand_out,
+    int T, int E, int k, double gamma) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wid;
     if (t >= T) return;                                    // no block-level sync below
-    float *row = srow + (size_t)wid * E;
+    int32_t *mycand = cand + (size_t)t * kCandMax;
     const double gx = gamma * (double)nx[t];
     uint32_t lok[PL], upk[PL];
     bool bad = !(gx < INFINITY);
@@ -296,14 +311,14 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
             for (int i = 0; i < PL; ++i) bk = max(bk, kk[i]);
             const uint32_t gk = wave_max_u32(bk);
             const unsigned long long m = __ballot(bk == gk);
-            if (lane == (int)__builtin_ctzll(m)) {
-                bool done = false;
+            // the lowest lane holding the maximum drops one copy of it;
+            // selects, not branches, keep the kk[] in place
+            bool take = lane == (int)__builtin_ctzll(m);
 #pragma unroll
-                for (int i = 0; i < PL; ++i)
-                    if (!done && kk[i] == gk) {
-                        kk[i] = 0u;
-                        done = true;
-                    }
+            for (int i = 0; i < PL; ++i) {
+                const bool hit = take && kk[i] == gk;
+                kk[i] = hit ? 0u : kk[i];
+                take = take && !hit;
             }
             tau = gk;
         }
@@ -313,64 +328,69 @@ __global__ __launch_bounds__(256) void select_refine_kernel(
             const bool c = lane + 64 * i < E && upk[i] >= tau;
             const unsigned long long m = __ballot(c);
             const int pos = base + (int)__popcll(m & ((1ull << lane) - 1ull));
-            if (c && pos < kCandMax) cand[wid][pos] = lane + 64 * i;
+            if (c && pos < kCandMax) mycand[pos] = lane + 64 * i;
             base += (int)__popcll(m);
         }
         ncand = base;
         bad = ncand > kCandMax;
     }
-    if (bad) ncand = E;
+    // the token's row of zt (already in registers) becomes its masked row
+    // of canonical logits: -inf until the refine kernel fills the candidates
 #pragma unroll
     for (int i = 0; i < PL; ++i)
-        if (lane + 64 * i < E) row[lane + 64 * i] = -INFINITY;
+        if (lane + 64 * i < E) zt[(size_t)t * E + lane + 64 * i] = -INFINITY;
+    if (lane == 0) ncand_out[t] = bad ? -1 : ncand;       // -1: all E experts
+}
+
+// The canonical logits of the candidates: block = one token, its four waves
+// take candidates wid, wid + 4, ..  With P = 8 NQ the lane's chunk of x
+// stays in registers and each candidate's chunk of its router row is loaded
+// in one go (every load before any use); else the chunks stream from
+// memory.  Few registers, so many tokens are in flight at once.
+template <int NQ>
+__global__ __launch_bounds__(256) void refine_kernel(
+    float *__restrict__ zt, const float *__restrict__ bias, const uint16_t *__restrict__ x,
+    const uint16_t *__restrict__ wr, const int32_t *__restrict__ cand,
+    const int32_t *__restrict__ ncand_in, int T, int d, int E) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int t = blockIdx.x;
+    if (t >= T) return;
+    const int nc = ncand_in[t];
+    const bool all = nc < 0;
+    const int n = all ? E : min(nc, kCandMax);
     const int P = d >> 6;
     const uint16_t *xr = x + (size_t)t * d;
+    const int32_t *mycand = cand + (size_t)t * kCandMax;
     if constexpr (NQ > 0) {
-        // P = 8 NQ: the lane's chunk of x stays in registers; the next
-        // candidate's chunk of its router row is loaded while the current
-        // one is summed (every load of a chunk issued before any use)
-        uint4 xq[NQ], wq[2][NQ];
+        uint4 xq[NQ];
         const uint4 *xc = reinterpret_cast<const uint4 *>(xr + (size_t)lane * P);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) xq[q] = xc[q];
-        auto wchunk = [&](int c) {
-            const int e = bad ? c : cand[wid][min(c, kCandMax - 1)];
-            return reinterpret_cast<const uint4 *>(wr + (size_t)min(e, E - 1) * d + (size_t)lane * P);
-        };
-        {
-            const uint4 *wc = wchunk(0);
+        for (int c = wid; c < n; c += 4) {
+            const int e = all ? c : mycand[c];
+            if ((unsigned)e >= (unsigned)E) continue;
+            const uint4 *wc = reinterpret_cast<const uint4 *>(wr + (size_t)e * d + (size_t)lane * P);
+            uint4 wq[NQ];
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) wq[0][q] = wc[q];
-        }
-        for (int c = 0; c < ncand; c += 2) {
+            for (int q = 0; q < NQ; ++q) wq[q] = wc[q];
+            // an empty asm that "changes" the x chunk each pass keeps the
+            // compiler from hoisting its 8 NQ fp64 conversions out of the
+            // loop (2 VGPRs each), which would cap the kernel at one wave
+            // per SIMD
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int cc = c + h;
-                if (cc < ncand) {
-                    const uint4 *wn = wchunk(min(cc + 1, ncand - 1));
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) wq[h ^ 1][q] = wn[q];
-                    const int e = bad ? cc : cand[wid][cc];
-                    const float z = canonical_from_regs<NQ>(xq, wq[h], lane,
-                                                            bias ? (double)bias[e] : 0.0);
-                    if (lane == 0) row[e] = z;
-                }
-            }
+            for (int q = 0; q < NQ; ++q)
+                asm volatile("" : "+v"(xq[q].x), "+v"(xq[q].y), "+v"(xq[q].z), "+v"(xq[q].w));
+            const float z = canonical_from_regs<NQ>(xq, wq, lane, bias ? (double)bias[e] : 0.0);
+            if (lane == 0) zt[(size_t)t * E + e] = z;
         }
     } else {
-        for (int c = 0; c < ncand; ++c) {
-            const int e = bad ? c : cand[wid][c];
+        for (int c = wid; c < n; c += 4) {
+            const int e = all ? c : mycand[c];
+            if ((unsigned)e >= (unsigned)E) continue;
             const float z = canonical_logit(xr, wr + (size_t)e * d, P, lane,
                                             bias ? (double)bias[e] : 0.0);
-            if (lane == 0) row[e] = z;
+            if (lane == 0) zt[(size_t)t * E + e] = z;
         }
-    }
-    int se;
-    float sw;
-    wave_topk_softmax<PL>(row, E, k, tsc[wid], &se, &sw);
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = se;
-        tw[(size_t)t * k + lane] = sw;
     }
 }
 
@@ -383,8 +403,9 @@ bool route_filter_ok(int T, int d, int E) {
 }
 
 hipError_t launch_route_filtered(const uint16_t *x, const uint16_t *wr, const float *bias,
-                                 float *zt, float *nx, float *nw, int32_t *ids, float *tw,
-                                 int T, int d, int E, int k, hipStream_t s) {
+                                 float *zt, float *nx, float *nw, int32_t *cand, int32_t *ncand,
+                                 int32_t *ids, float *tw, int T, int d, int E, int k,
+                                 hipStream_t s) {
     if (T <= 0) return hipSuccess;
     hipError_t e;
     if (!g_filter_attr) {
@@ -404,24 +425,35 @@ hipError_t launch_route_filtered(const uint16_t *x, const uint16_t *wr, const fl
         (void)timed_launch("router_filter_gemm", filter_gemm_kernel, dim3(grid), dim3(256), kFLds, s, x, wr, zt, T, d, E);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const double c = 2.0 * (double)(d + 64) / 8388608.0;
+    const double c = 2.0 * (double)(d / 64 + 128) / 8388608.0;
     const double gamma = c / (1.0 - c);
-    const size_t lds = (size_t)4 * E * sizeof(float);
     const int pl = (E + 63) / 64;
     {
         const unsigned grid = (unsigned)((T + 3) / 4);
-        const int P = d / 64;
+        if (pl <= 4)
+            (void)timed_launch("router_select", select_cand_kernel<4>, dim3(grid), dim3(256), 0, s, zt, nx, nw, bias, cand, ncand, T, E, k, gamma);
+        else if (pl <= 8)
+            (void)timed_launch("router_select", select_cand_kernel<8>, dim3(grid), dim3(256), 0, s, zt, nx, nw, bias, cand, ncand, T, E, k, gamma);
+        else
+            (void)timed_launch("router_select", select_cand_kernel<16>, dim3(grid), dim3(256), 0, s, zt, nx, nw, bias, cand, ncand, T, E, k, gamma);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
         // the register-resident chunk covers d = 512 * NQ; other d take the
         // loop that reads both chunks from memory
-        if (pl <= 16 && P == 112)
-            (void)timed_launch("router_refine", select_refine_kernel<16, 14>, dim3(grid), dim3(256), lds, s, zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
-        else if (pl <= 4)
-            (void)timed_launch("router_refine", select_refine_kernel<4, 0>, dim3(grid), dim3(256), lds, s, zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
-        else if (pl <= 8)
-            (void)timed_launch("router_refine", select_refine_kernel<8, 0>, dim3(grid), dim3(256), lds, s, zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+        const int P = d / 64;
+        if (P == 112)
+            (void)timed_launch("router_refine", refine_kernel<14>, dim3(T), dim3(256), 0, s, zt, bias, x, wr, cand, ncand, T, d, E);
+        else if (P == 64)
+            (void)timed_launch("router_refine", refine_kernel<8>, dim3(T), dim3(256), 0, s, zt, bias, x, wr, cand, ncand, T, d, E);
         else
-            (void)timed_launch("router_refine", select_refine_kernel<16, 0>, dim3(grid), dim3(256), lds, s, zt, nx, nw, bias, x, wr, ids, tw, T, d, E, k, gamma);
+            (void)timed_launch("router_refine", refine_kernel<0>, dim3(T), dim3(256), 0, s, zt, bias, x, wr, cand, ncand, T, d, E);
     }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // top-k + softmax over the masked canonical rows (the same wave
+    // selection the small-T path uses)
+    e = launch_topk_softmax(zt, ids, tw, T, E, k, s);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 
