@@ -6,8 +6,8 @@
  *
  * Kernel names: "router_logits", "topk_softmax", "permute", "topk_permute"
  * (the two fused, small T), "router_norms", "router_filter_gemm",
- * "router_select", "router_refine" (routing of many tokens, which then ends
- * in "topk_softmax"), "plan", "gemv_gate_up", "gemv_down",
+ * "router_select", "router_refine" (routing of many tokens; the refine
+ * kernel also takes the top-k), "plan", "gemv_gate_up", "gemv_down",
  * "down_combine", "combine", "mfma_ffn" (the whole scaled-MFMA expert
  * FFN of large T), its parts "mx_split_x", "gate_up_mfma" (which also
  * splits h) and "down_mfma", and "mx_round" (the activation-MX mode's

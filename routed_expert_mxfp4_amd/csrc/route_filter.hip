@@ -26,8 +26,7 @@
 //   3. tau = the k-th largest lower end.  An expert whose upper end is
 //      below tau is below k others for certain, so it is not selected; the
 //      canonical logits of the others (the candidates, usually ~17) are
-//      computed exactly, and top-k + softmax run over them with the
-//      non-candidates at -inf.  A token with any non-finite interval, or
+//      computed exactly, and top-k + softmax run over them alone.  A token with any non-finite interval, or
 //      more than kCandMax candidates (e.g. massively tied logits), takes
 //      the canonical logits of all E experts instead.
 // The selected experts and weights are therefore exactly those of the
@@ -192,8 +191,8 @@ __global__ __launch_bounds__(256) void filter_gemm_kernel(const uint16_t *__rest
 }
 
 // ---------------------------------------------------------------------------
-// Certified selection (one wave per token), canonical refinement (one
-// block per token); top-k/softmax then runs over the masked rows.
+// Certified selection (one wave per token), then canonical refinement and
+// top-k/softmax (one block per token).
 // ---------------------------------------------------------------------------
 // fp32 bounds that contain a finite double: round toward -inf / +inf (one
 // step of the fp32 grid when the nearest rounding went the wrong way).
@@ -264,12 +263,11 @@ __device__ __forceinline__ float canonical_from_regs(const uint4 (&xq)[NQ], cons
 }
 
 // Per token (one wave): the certified intervals, tau and the candidate
-// list, written to cand[t][..] with their number in ncand_out[t] (-1: the
-// token takes all E canonical logits); the token's zt row is overwritten
-// with -inf, to be filled in at the candidates by refine_kernel.
+// list, written to cand[t][..] in ascending expert order with their number
+// in ncand_out[t] (-1: the token takes all E canonical logits).
 template <int PL>
 __global__ __launch_bounds__(256) void select_cand_kernel(
-    float *__restrict__ zt, const float *__restrict__ nx, const float *__restrict__ nw,
+    const float *__restrict__ zt, const float *__restrict__ nx, const float *__restrict__ nw,
     const float *__restrict__ bias, int32_t *__restrict__ cand, int32_t *__restrict__ ncand_out,
     int T, int E, int k, double gamma) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -334,27 +332,30 @@ __global__ __launch_bounds__(256) void select_cand_kernel(
         ncand = base;
         bad = ncand > kCandMax;
     }
-    // the token's row of zt (already in registers) becomes its masked row
-    // of canonical logits: -inf until the refine kernel fills the candidates
-#pragma unroll
-    for (int i = 0; i < PL; ++i)
-        if (lane + 64 * i < E) zt[(size_t)t * E + lane + 64 * i] = -INFINITY;
     if (lane == 0) ncand_out[t] = bad ? -1 : ncand;       // -1: all E experts
 }
 
-// The canonical logits of the candidates: block = one token, its four waves
-// take candidates wid, wid + 4, ..  With P = 8 NQ the lane's chunk of x
-// stays in registers and each candidate's chunk of its router row is loaded
-// in one go (every load before any use); else the chunks stream from
-// memory.  Few registers, so many tokens are in flight at once.
+// The canonical logits of the candidates, then the token's top-k + softmax:
+// block = one token.  Its four waves take candidates wid, wid + 4, .. and
+// park the logits in LDS.  With P = 8 NQ the lane's chunk of x stays in
+// registers and each candidate's chunk of its router row is loaded in one go
+// (every load before any use); else both chunks stream from memory.  Wave 0
+// then ranks the candidates (at most 64, one per lane), or, for a token that
+// takes all E experts, runs the full-row selection over them.  Either way
+// the k selected and their order are those of the full row of canonical
+// logits, since the candidates hold its top k, and the weights come from the
+// same softmax tail as the unfiltered path.
 template <int NQ>
-__global__ __launch_bounds__(256) void refine_kernel(
-    float *__restrict__ zt, const float *__restrict__ bias, const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void refine_topk_kernel(
+    const float *__restrict__ bias, const uint16_t *__restrict__ x,
     const uint16_t *__restrict__ wr, const int32_t *__restrict__ cand,
-    const int32_t *__restrict__ ncand_in, int T, int d, int E) {
+    const int32_t *__restrict__ ncand_in, int32_t *__restrict__ ids, float *__restrict__ tw,
+    int T, int d, int E, int k) {
+    __shared__ __align__(16) float zc[kMaxExperts];
+    __shared__ __align__(16) uint32_t tsc[kTopkScratch];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int t = blockIdx.x;
-    if (t >= T) return;
+    if (t >= T) return;                                    // whole block: before any barrier
     const int nc = ncand_in[t];
     const bool all = nc < 0;
     const int n = all ? E : min(nc, kCandMax);
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(256) void refine_kernel(
             for (int q = 0; q < NQ; ++q)
                 asm volatile("" : "+v"(xq[q].x), "+v"(xq[q].y), "+v"(xq[q].z), "+v"(xq[q].w));
             const float z = canonical_from_regs<NQ>(xq, wq, lane, bias ? (double)bias[e] : 0.0);
-            if (lane == 0) zt[(size_t)t * E + e] = z;
+            if (lane == 0) zc[c] = z;
         }
     } else {
         for (int c = wid; c < n; c += 4) {
@@ -389,8 +390,32 @@ __global__ __launch_bounds__(256) void refine_kernel(
             if ((unsigned)e >= (unsigned)E) continue;
             const float z = canonical_logit(xr, wr + (size_t)e * d, P, lane,
                                             bias ? (double)bias[e] : 0.0);
-            if (lane == 0) zt[(size_t)t * E + e] = z;
+            if (lane == 0) zc[c] = z;
         }
+    }
+    __syncthreads();
+    if (wid != 0) return;
+    // a fresh copy of the lane index: the 64-bit offsets built from it are
+    // then formed here, not kept in registers across the loop above
+    int li = lane;
+    asm volatile("" : "+v"(li));
+    int se = 0;
+    float sw = 0.f;
+    if (all) {
+        wave_topk_softmax<kMaxExperts / 64>(zc, E, k, tsc, &se, &sw);
+    } else {
+        const int e = li < n ? mycand[li] : -1;
+        const bool ok = (unsigned)e < (unsigned)E;
+        const uint32_t ka = ok ? logit_key(zc[li]) : 0u;
+        const uint32_t ea = ok ? (uint32_t)e : 0xFFFFFFFFu;
+        int my_e = 0;
+        float my_v = 0.f;
+        wave_rank_select(ka, ea, n, k, &my_e, &my_v);
+        wave_softmax_tail(my_e, my_v, k, &se, &sw);
+    }
+    if (li < k) {
+        ids[(size_t)t * k + li] = se;
+        tw[(size_t)t * k + li] = sw;
     }
 }
 
@@ -443,17 +468,12 @@ hipError_t launch_route_filtered(const uint16_t *x, const uint16_t *wr, const fl
         // loop that reads both chunks from memory
         const int P = d / 64;
         if (P == 112)
-            (void)timed_launch("router_refine", refine_kernel<14>, dim3(T), dim3(256), 0, s, zt, bias, x, wr, cand, ncand, T, d, E);
+            (void)timed_launch("router_refine", refine_topk_kernel<14>, dim3(T), dim3(256), 0, s, bias, x, wr, cand, ncand, ids, tw, T, d, E, k);
         else if (P == 64)
-            (void)timed_launch("router_refine", refine_kernel<8>, dim3(T), dim3(256), 0, s, zt, bias, x, wr, cand, ncand, T, d, E);
+            (void)timed_launch("router_refine", refine_topk_kernel<8>, dim3(T), dim3(256), 0, s, bias, x, wr, cand, ncand, ids, tw, T, d, E, k);
         else
-            (void)timed_launch("router_refine", refine_kernel<0>, dim3(T), dim3(256), 0, s, zt, bias, x, wr, cand, ncand, T, d, E);
+            (void)timed_launch("router_refine", refine_topk_kernel<0>, dim3(T), dim3(256), 0, s, bias, x, wr, cand, ncand, ids, tw, T, d, E, k);
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // top-k + softmax over the masked canonical rows (the same wave
-    // selection the small-T path uses)
-    e = launch_topk_softmax(zt, ids, tw, T, E, k, s);
-    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -99,6 +99,47 @@ __device__ __forceinline__ double sum_lanes32_f64(double v) {
            __longlong_as_double((long long)(((unsigned long long)hi1 << 32) | lo1));
 }
 
+// C <= 64 candidates, one per lane (lane < C: key ka, expert ea; other
+// lanes key 0, expert ~0): each one's rank in (key descending, expert
+// ascending) order is counted against the others, whose keys come by
+// readlane, and the lane of rank r < k receives its expert and logit with
+// one ds_permute.
+__device__ __forceinline__ void wave_rank_select(uint32_t ka, uint32_t ea, int C, int k,
+                                                 int *my_e, float *my_v) {
+    const int lane = threadIdx.x & 63;
+    int rank = 0;
+    for (int j0 = 0; j0 < C; j0 += 4) {               // four independent compares a pass
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = min(j0 + q, C - 1);
+            const uint32_t kb = (uint32_t)__builtin_amdgcn_readlane((int)ka, j);
+            const uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)ea, j);
+            rank += (j0 + q < C && (kb > ka || (kb == ka && eb < ea))) ? 1 : 0;
+        }
+    }
+    // a permutation: candidates go to their rank (< C), the others stay
+    const int tgt = lane < C ? rank : lane;
+    const uint32_t se = (uint32_t)__builtin_amdgcn_ds_permute(tgt << 2, (int)ea);
+    const uint32_t sk = (uint32_t)__builtin_amdgcn_ds_permute(tgt << 2, (int)ka);
+    if (lane < k) {
+        *my_e = (int)se;
+        *my_v = key_logit(sk);
+    }
+}
+
+// Softmax over the k selected logits (lane j < k holds the j-th, descending):
+// exp(v - v_0) in fp64, summed over lanes 0..31 in a fixed order, one
+// division and one rounding per weight.
+__device__ __forceinline__ void wave_softmax_tail(int my_e, float my_v, int k, int *sel_e,
+                                                  float *sel_w) {
+    const int lane = threadIdx.x & 63;
+    const double vmax = (double)__shfl(my_v, 0, 64);
+    const double ex = lane < k ? exp((double)my_v - vmax) : 0.0;
+    const double sum = sum_lanes32_f64(ex);
+    *sel_e = my_e;
+    *sel_w = (float)(ex / sum);
+}
+
 // Selects the top-k (k <= 32) of one token's logits row.  On return lane
 // j < k holds the j-th selected expert in *sel_e and its weight in *sel_w.
 // sc: this wave's kTopkScratch words of LDS.
@@ -160,24 +201,7 @@ __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row,
         __builtin_amdgcn_wave_barrier();
         const uint32_t ka = lane < C ? sc[64 + lane] : 0u;
         const uint32_t ea = lane < C ? sc[128 + lane] : 0xFFFFFFFFu;
-        int rank = 0;
-        for (int j0 = 0; j0 < C; j0 += 4) {           // four independent compares a pass
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = min(j0 + q, C - 1);
-                const uint32_t kb = (uint32_t)__builtin_amdgcn_readlane((int)ka, j);
-                const uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)ea, j);
-                rank += (j0 + q < C && (kb > ka || (kb == ka && eb < ea))) ? 1 : 0;
-            }
-        }
-        // a permutation: candidates go to their rank (< C), the others stay
-        const int tgt = lane < C ? rank : lane;
-        const uint32_t se = (uint32_t)__builtin_amdgcn_ds_permute(tgt << 2, (int)ea);
-        const uint32_t sk = (uint32_t)__builtin_amdgcn_ds_permute(tgt << 2, (int)ka);
-        if (lane < k) {
-            my_e = (int)se;
-            my_v = key_logit(sk);
-        }
+        wave_rank_select(ka, ea, C, k, &my_e, &my_v);
     } else {
         for (int j = 0; j < k; ++j) {
             uint32_t bk = 0u;
@@ -203,11 +227,7 @@ __device__ __forceinline__ void wave_topk_softmax(const float *__restrict__ row,
             }
         }
     }
-    const double vmax = (double)__shfl(my_v, 0, 64);
-    const double ex = lane < k ? exp((double)my_v - vmax) : 0.0;
-    const double sum = sum_lanes32_f64(ex);
-    *sel_e = my_e;
-    *sel_w = (float)(ex / sum);
+    wave_softmax_tail(my_e, my_v, k, sel_e, sel_w);
 }
 
 }  // namespace moe
