@@ -15,6 +15,7 @@
 namespace moe {
 namespace {
 
+template <int G>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ rows_out,
                                                       const int32_t *__restrict__ row_pos,
                                                       const float *__restrict__ topk_w,
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
                                                       uint16_t *__restrict__ y, int T, int d,
                                                       int k) {
     const int t = blockIdx.y;
-    const int v = blockIdx.x * 256 + threadIdx.x;       // 8-element vector index
+    const int v = blockIdx.x * blockDim.x + threadIdx.x;   // 8-element vector index
     if (v >= (d >> 3)) return;
     const int nrows = T * k;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -43,12 +44,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
             acc[2 * i + 1] = bf16_bits_to_f32(rw[i] >> 16) + ev[2 * i + 1];
         }
     }
-    // slots in groups of 8: all loads of a group are issued before use
-    for (int j0 = 0; j0 < k; j0 += 8) {
-        uint4 q[8];
-        float wj[8];
+    // slots in groups of G: all loads of a group are issued before use
+    for (int j0 = 0; j0 < k; j0 += G) {
+        uint4 q[G];
+        float wj[G];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        for (int jj = 0; jj < G; ++jj) {
             const int j = min(j0 + jj, k - 1);
             int p = row_pos[(size_t)t * k + j];
             const bool ok = j0 + jj < k && (unsigned)p < (unsigned)nrows;
@@ -57,7 +58,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
             q[jj] = reinterpret_cast<const uint4 *>(rows_out + (size_t)p * d)[v];
         }
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
+        for (int jj = 0; jj < G; ++jj) {
             if (j0 + jj < k) {
                 const uint32_t wds[4] = {q[jj].x, q[jj].y, q[jj].z, q[jj].w};
 #pragma unroll
@@ -82,9 +83,17 @@ hipError_t launch_combine(const uint16_t *rows_out, const int32_t *row_pos,
                           const float *topk_w, uint16_t *y, int T, int d, int k,
                           hipStream_t s, const uint16_t *resid, const float *extra) {
     if (T <= 0) return hipSuccess;
-    dim3 grid(((d >> 3) + 255) / 256, T);
-    (void)timed_launch("combine", combine_kernel, dim3(grid), dim3(256), 0, s, rows_out, row_pos,
-                       topk_w, resid, extra, y, T, d, k);
+    // 128-thread blocks when they tile the row exactly (d = 7168: 7 blocks,
+    // no idle lanes); every slot's load in flight at once for k <= 16
+    const int nv = d >> 3;
+    const int bs = nv % 128 == 0 ? 128 : 256;
+    dim3 grid((nv + bs - 1) / bs, T);
+    if (k > 8)
+        (void)timed_launch("combine", combine_kernel<16>, dim3(grid), dim3(bs), 0, s, rows_out,
+                           row_pos, topk_w, resid, extra, y, T, d, k);
+    else
+        (void)timed_launch("combine", combine_kernel<8>, dim3(grid), dim3(bs), 0, s, rows_out,
+                           row_pos, topk_w, resid, extra, y, T, d, k);
     return hipGetLastError();
 }
 
