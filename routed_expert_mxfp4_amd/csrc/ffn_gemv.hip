@@ -522,15 +522,17 @@ __device__ __forceinline__ void dot_batch(const RowBuf<NBLD, B> &rb, const float
 
 // Fused down + combine for small T: block (ROWS output rows, token t); wave
 // j computes slot j's expert output for the block's rows (j = wid, wid + 16,
-// ...) in batches of B rows (the next batch's loads in flight during the
-// current batch's math) and parks it in LDS; then y = sum_j w_j o_j in fp32,
-// slot order, one writer per output.  ROWS is a multiple of B.
-template <int NBLD, int ROWS, int B>
+// ...) in batches of B rows held in a ring of R batch buffers, so R - 1
+// batches' loads are in flight during each batch's math, and parks it in
+// LDS; then y = sum_j w_j o_j in fp32, slot order, one writer per output.
+// ROWS is a multiple of B.
+template <int NBLD, int ROWS, int B, int R>
 __global__ __launch_bounds__(1024) void down_combine_split_kernel(
     const float *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ ids,
     const float *__restrict__ topk_w, const int32_t *__restrict__ row_pos,
     uint16_t *__restrict__ y, int T, int d, int E, int k, int f) {
     static_assert(ROWS % B == 0, "whole batches");
+    static_assert(R >= 2, "a ring");
     __shared__ float part[kMaxTopK][ROWS];
     const int t = blockIdx.y;
     const int m0 = blockIdx.x * ROWS;
@@ -549,28 +551,22 @@ __global__ __launch_bounds__(1024) void down_combine_split_kernel(
             const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
             float4 hv[NBLD][8];
             load_h_slice<NBLD>(hbuf, (uint32_t)p * f * 4u, lane, nblk, hv);
-            RowBuf<NBLD, B> A, Bb;
             constexpr int NB = ROWS / B;
-            load_batch<NBLD, B>(codes, scales, m0, lane, nblk, code_row, A);
+            RowBuf<NBLD, B> ring[R];
 #pragma unroll
-            for (int bi = 0; bi < NB; bi += 2) {
-                if (bi + 1 < NB) load_batch<NBLD, B>(codes, scales, m0 + (bi + 1) * B, lane, nblk, code_row, Bb);
+            for (int i = 0; i < R - 1 && i < NB; ++i)
+                load_batch<NBLD, B>(codes, scales, m0 + i * B, lane, nblk, code_row, ring[i]);
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi) {
+                if (bi + R - 1 < NB)
+                    load_batch<NBLD, B>(codes, scales, m0 + (bi + R - 1) * B, lane, nblk, code_row,
+                                        ring[(bi + R - 1) % R]);
                 __builtin_amdgcn_sched_barrier(0);
                 float out[B];
-                dot_batch<NBLD, B>(A, hv, lane, nblk, out);
+                dot_batch<NBLD, B>(ring[bi % R], hv, lane, nblk, out);
                 if (lane == 0) {
 #pragma unroll
                     for (int rr = 0; rr < B; ++rr) part[j][bi * B + rr] = out[rr];
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (bi + 2 < NB) load_batch<NBLD, B>(codes, scales, m0 + (bi + 2) * B, lane, nblk, code_row, A);
-                __builtin_amdgcn_sched_barrier(0);
-                if (bi + 1 < NB) {
-                    dot_batch<NBLD, B>(Bb, hv, lane, nblk, out);
-                    if (lane == 0) {
-#pragma unroll
-                        for (int rr = 0; rr < B; ++rr) part[j][(bi + 1) * B + rr] = out[rr];
-                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -723,6 +719,9 @@ hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertAr
                                       plan, h, d, E, k, f, s);
 }
 
+// rows per batch and batch buffers of the fused down + combine
+constexpr int kDcB = 4, kDcR = 2;
+
 template <int NBLD>
 hipError_t launch_dc_split(const float *h, ExpertArgs w, const int32_t *ids,
                            const float *topk_w, const int32_t *row_pos, uint16_t *y, int T,
@@ -730,11 +729,11 @@ hipError_t launch_dc_split(const float *h, ExpertArgs w, const int32_t *ids,
     // 28 output rows per block: 7168 / 28 = 256 blocks, one per CU
     if (d % 28 == 0) {
         dim3 grid(d / 28, T);
-        (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, 28, 4>, dim3(grid), dim3(1024), 0, s, h, w, ids, topk_w, row_pos, y,
+        (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, 28, kDcB, kDcR>, dim3(grid), dim3(1024), 0, s, h, w, ids, topk_w, row_pos, y,
                                                                       T, d, E, k, f);
     } else {
         dim3 grid(d / 32, T);
-        (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, 32, 4>, dim3(grid), dim3(1024), 0, s, h, w, ids, topk_w, row_pos, y,
+        (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, 32, kDcB, kDcR>, dim3(grid), dim3(1024), 0, s, h, w, ids, topk_w, row_pos, y,
                                                                       T, d, E, k, f);
     }
     return hipGetLastError();
