@@ -159,12 +159,20 @@ __global__ __launch_bounds__(64 * RPB) void router_small_kernel(
     const int e0 = blockIdx.x * RPB;
     const int pieces = 64 * q_per_chunk;            // 16-byte pieces per row
     const int total = RPB * pieces;                 // <= kThreads * kPer
+    // n / pieces and n / q_per_chunk by multiply-high with ceil(2^32 / D):
+    // exact for n, D < 2^16 (n D < 2^32), which holds here (n < 4096,
+    // D <= 1024); the wave-uniform magic numbers cost one scalar division
+    // each instead of a vector division per piece
+    const uint64_t mg_p = ((1ull << 32) + (uint64_t)pieces - 1) / (uint64_t)pieces;
+    const uint64_t mg_q = ((1ull << 32) + (uint64_t)q_per_chunk - 1) / (uint64_t)q_per_chunk;
+    auto div_p = [mg_p](int n) { return (int)(((uint64_t)(uint32_t)n * mg_p) >> 32); };
+    auto div_q = [mg_q](int n) { return (int)(((uint64_t)(uint32_t)n * mg_q) >> 32); };
     // every load first, then every LDS store: one memory round trip
     uint4 buf[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int i = min((int)threadIdx.x + kThreads * j, total - 1);
-        const int r = i / pieces, q = i - r * pieces;
+        const int r = div_p(i), q = i - r * pieces;
         buf[j] = reinterpret_cast<const uint4 *>(wr + (size_t)min(e0 + r, E - 1) * d)[q];
     }
     // every load completes here, then unconditional stores (pieces past the
@@ -174,8 +182,8 @@ __global__ __launch_bounds__(64 * RPB) void router_small_kernel(
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int i = (int)threadIdx.x + kThreads * j;
-        const int r = i / pieces, q = i - r * pieces;
-        const int c = q / q_per_chunk, w = q - c * q_per_chunk;
+        const int r = div_p(i), q = i - r * pieces;
+        const int c = div_q(q), w = q - c * q_per_chunk;
         wrs[i < total ? (r * 64 + c) * cstride + w : spare] = buf[j];
     }
     __syncthreads();
