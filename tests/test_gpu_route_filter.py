@@ -6,7 +6,9 @@ then computed exactly.  Its top-k ids and softmax weights must therefore be
 bit-identical to those of the canonical path (moe_route asked for its
 logits computes all of them) and match the oracle's routing.  Covered:
 random rows at several shapes, exact ties from duplicated router rows (lower
-index first), all-equal logits (more candidates than the filter keeps: every
+index first), a block of identical router rows that puts 41 or 71 tied
+experts into the candidate lists (ranking at up to 64 candidates, then the
+fallback), all-equal logits (more candidates than the filter keeps: every
 expert is refined), rows holding subnormal or huge values (no finite
 interval: every expert is refined), and the Zipf router bias.
 """
@@ -58,6 +60,7 @@ ROUTE_CASES = [
     (300, 1024, 256, 16, 82),        # ragged 128-token GEMM tiles
     (257, 192, 40, 5, 83),           # chunk length 3, E not a multiple of 64
     (320, 7168, 896, 16, 84),        # the layer's router shape (register-resident chunks)
+    (272, 4096, 256, 8, 89),         # the second routing shape (64-element chunks in registers)
     (260, 64, 1000, 32, 85),         # k = 32, E near the limit, chunk length 1
 ]
 
@@ -112,3 +115,22 @@ def test_filtered_routing_zipf_bias(dev):
     wr = synth.gen_router_w(cfg)
     bias = synth.gen_bias(cfg)
     _check(dev, x, wr, cfg.k, bias)
+
+
+@pytest.mark.parametrize("copies", [40, 70])
+def test_filtered_routing_many_tied_candidates(dev, copies):
+    # expert 5's router row copied into `copies` others: for every token
+    # where it ranks high, all copies tie with it, so a token's candidate
+    # list holds them all (40: ranked within the 64-entry list; 70: more
+    # than it holds, so every expert is refined for that token)
+    cfg = _small_cfg(256, 512, 128, 16, 64, 90 + copies)
+    x = synth.gen_x(cfg)
+    wr = synth.gen_router_w(cfg).clone()
+    for j in range(copies):
+        wr[(5 + 1 + 3 * j) % cfg.E] = wr[5]
+    ids = _check(dev, x, wr, cfg.k)
+    lg = oracle.router_logits(synth.as_u16(x), synth.as_u16(wr))
+    tied = (lg[:, 5:6] == lg).sum(axis=1)
+    # the copies really tie, and some token takes several of them
+    assert tied.min() >= copies + 1
+    assert (np.isin(ids, [5] + [(5 + 1 + 3 * j) % cfg.E for j in range(copies)]).sum(axis=1) >= 2).any()
