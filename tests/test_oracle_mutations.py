@@ -108,9 +108,18 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
     subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-std=c11",
                            "-shared", "-fPIC", "-o", str(so), str(mutated), "-lm"])
     env = dict(os.environ, MOE_ORACLE_LIB=str(so))
-    pins = [os.path.join(ROOT, "tests", f) for f in
-            ("test_oracle_formats.py", "test_oracle_router.py",
-             "test_oracle_ffn.py", "test_oracle_mx.py", "test_oracle_tail.py", "test_oracle_fp8.py")]
+    files = ["test_oracle_formats.py", "test_oracle_router.py", "test_oracle_ffn.py",
+             "test_oracle_mx.py", "test_oracle_tail.py", "test_oracle_fp8.py"]
+    # every pin file runs; the one aimed at the mutated function goes first,
+    # so that -x stops early (a speed-up only: any failing pin counts)
+    for key, f in (("FP8", "test_oracle_fp8.py"), ("RMSNorm", "test_oracle_tail.py"),
+                   ("residual", "test_oracle_tail.py"), ("shared", "test_oracle_tail.py"),
+                   ("block", "test_oracle_tail.py"), ("MX", "test_oracle_mx.py")):
+        if key in name:
+            files.remove(f)
+            files.insert(0, f)
+            break
+    pins = [os.path.join(ROOT, "tests", f) for f in files]
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + pins,
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "no pin caught: " + name + "\n" + r.stdout[-2000:]
