@@ -177,6 +177,23 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """The stream a call runs on (the current one if None).  Wrappers make
+    their temporaries (workspace, outputs, dtype or layout copies) inside
+    ``torch.cuda.stream(_on(stream))``, so the caching allocator ties those
+    blocks to the stream whose kernels use them: a block freed when the
+    wrapper returns is not handed to another stream's work while the
+    queued kernels still read or write it."""
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _keep(t, stream):
+    """A long-lived buffer (a Layer's workspace) used on ``stream``: mark it
+    in use there, so that freeing it later waits for that stream's work."""
+    if t is not None and stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+
+
 def _check(status: int, where: str):
     if status != MOE_OK:
         raise MoeError(status, where)
@@ -211,20 +228,22 @@ def _bits16(t: torch.Tensor) -> torch.Tensor:
 def moe_route(x, router_w, k, router_bias=None, want_logits=False, ws=None, stream=None):
     """Router + top-k + softmax.  Returns (topk_ids int32 [T][k],
     topk_w fp32 [T][k]) and, if ``want_logits``, the fp32 [T][E] logits."""
-    x, router_w = _bits16(x), _bits16(router_w)
-    T, d = x.shape
-    E = router_w.shape[0]
-    dims = dims_of(T, d, E, k, 32)
-    dev = x.device
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
-    if ws is None and not want_logits:
-        ws = workspace(dims, ENTRY_ROUTE, dev)
-    bias = None if router_bias is None else router_bias.contiguous().float()
-    st = lib().moe_route(ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(logits),
-                         _ptr(ids), _ptr(w), _ptr(ws), 0 if ws is None else ws.numel(),
-                         _stream(stream))
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x, router_w = _bits16(x), _bits16(router_w)
+        T, d = x.shape
+        E = router_w.shape[0]
+        dims = dims_of(T, d, E, k, 32)
+        dev = x.device
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+        if ws is None and not want_logits:
+            ws = workspace(dims, ENTRY_ROUTE, dev)
+        bias = None if router_bias is None else router_bias.contiguous().float()
+        st = lib().moe_route(ctypes.byref(dims), _ptr(x), _ptr(router_w), _ptr(bias),
+                             _ptr(logits), _ptr(ids), _ptr(w), _ptr(ws),
+                             0 if ws is None else ws.numel(), _stream(s))
     _check(st, "moe_route")
     return (ids, w, logits) if want_logits else (ids, w)
 
@@ -232,19 +251,21 @@ def moe_route(x, router_w, k, router_bias=None, want_logits=False, ws=None, stre
 def moe_permute(topk_ids, E, ws=None, stream=None):
     """Group rows by expert.  Returns (counts [E], offsets [E+1],
     sorted_rows [T*k], row_pos [T*k]), all int32."""
-    topk_ids = topk_ids.contiguous()
-    T, k = topk_ids.shape
-    dims = dims_of(T, 64, E, k, 32)
-    dev = topk_ids.device
-    counts = torch.empty(E, dtype=torch.int32, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    sorted_rows = torch.empty(T * k, dtype=torch.int32, device=dev)
-    row_pos = torch.empty(T * k, dtype=torch.int32, device=dev)
-    if ws is None:
-        ws = workspace(dims, ENTRY_PERMUTE, dev)
-    st = lib().moe_permute(ctypes.byref(dims), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
-                           _ptr(sorted_rows), _ptr(row_pos), _ptr(ws), ws.numel(),
-                           _stream(stream))
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        topk_ids = topk_ids.contiguous()
+        T, k = topk_ids.shape
+        dims = dims_of(T, 64, E, k, 32)
+        dev = topk_ids.device
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        sorted_rows = torch.empty(T * k, dtype=torch.int32, device=dev)
+        row_pos = torch.empty(T * k, dtype=torch.int32, device=dev)
+        if ws is None:
+            ws = workspace(dims, ENTRY_PERMUTE, dev)
+        st = lib().moe_permute(ctypes.byref(dims), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                               _ptr(sorted_rows), _ptr(row_pos), _ptr(ws), ws.numel(),
+                               _stream(s))
     _check(st, "moe_permute")
     return counts, offsets, sorted_rows, row_pos
 
@@ -253,37 +274,61 @@ def moe_expert_ffn(x, experts: dict, offsets, sorted_rows, k, ws=None, stream=No
                    act=ACT_BF16):
     """Expert FFN over grouped rows.  Returns rows_out bf16 [T*k][d].
     act: ACT_BF16, or ACT_MX_E2M3 for the activation-MX mode."""
-    x = _bits16(x)
-    T, d = x.shape
-    E, two_f = experts["gu_codes"].shape[:2]
-    dims = dims_of(T, d, E, k, two_f // 2, act)
-    rows_out = torch.empty((T * k, d), dtype=torch.bfloat16, device=x.device)
-    if ws is None:
-        ws = workspace(dims, ENTRY_EXPERT_FFN, x.device)
-    ex = experts_of(experts)
-    st = lib().moe_expert_ffn(ctypes.byref(dims), _ptr(x), ctypes.byref(ex), _ptr(offsets),
-                              _ptr(sorted_rows), _ptr(rows_out), _ptr(ws), ws.numel(),
-                              _stream(stream))
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x = _bits16(x)
+        T, d = x.shape
+        E, two_f = experts["gu_codes"].shape[:2]
+        dims = dims_of(T, d, E, k, two_f // 2, act)
+        rows_out = torch.empty((T * k, d), dtype=torch.bfloat16, device=x.device)
+        if ws is None:
+            ws = workspace(dims, ENTRY_EXPERT_FFN, x.device)
+        offsets, sorted_rows = offsets.contiguous(), sorted_rows.contiguous()
+        ex = experts_of(experts)
+        st = lib().moe_expert_ffn(ctypes.byref(dims), _ptr(x), ctypes.byref(ex), _ptr(offsets),
+                                  _ptr(sorted_rows), _ptr(rows_out), _ptr(ws), ws.numel(),
+                                  _stream(s))
     _check(st, "moe_expert_ffn")
     return rows_out
 
 
 def moe_combine(rows_out, row_pos, topk_w, stream=None):
     """Weighted combine.  Returns y bf16 [T][d]."""
-    rows_out = _bits16(rows_out)
-    T, k = topk_w.shape
-    d = rows_out.shape[1]
-    dims = dims_of(T, d, max(k, 1), k, 32)
-    y = torch.empty((T, d), dtype=torch.bfloat16, device=rows_out.device)
-    st = lib().moe_combine(ctypes.byref(dims), _ptr(rows_out), _ptr(row_pos.contiguous()),
-                           _ptr(topk_w.contiguous()), _ptr(y), _stream(stream))
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        rows_out = _bits16(rows_out)
+        T, k = topk_w.shape
+        d = rows_out.shape[1]
+        dims = dims_of(T, d, max(k, 1), k, 32)
+        y = torch.empty((T, d), dtype=torch.bfloat16, device=rows_out.device)
+        row_pos, topk_w = row_pos.contiguous(), topk_w.contiguous()
+        st = lib().moe_combine(ctypes.byref(dims), _ptr(rows_out), _ptr(row_pos),
+                               _ptr(topk_w), _ptr(y), _stream(s))
     _check(st, "moe_combine")
     return y
 
 
-class Layer:
+class _Reusable:
+    """A workspace kept across calls, grown when a call needs more bytes
+    (the byte count is not monotonic in T: the expert path changes with
+    it)."""
+
+    _ws = None
+
+    def _ensure_ws(self, nbytes: int, device):
+        if nbytes == SIZE_MAX:
+            raise MoeError(MOE_ERR_SHAPE, type(self).__name__ + " workspace")
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = None
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self._ws
+
+
+class Layer(_Reusable):
     """Holds device pointers, dims and a reusable workspace for repeated
     ``moe_layer_forward`` calls (the benchmark's hot loop)."""
+
+    _entry = "moe_layer_forward"
 
     def __init__(self, experts: dict, router_w, k, router_bias=None, T=1, act=ACT_BF16):
         self.act = int(act)
@@ -294,40 +339,54 @@ class Layer:
         self.f = experts["gu_codes"].shape[1] // 2
         self.k = k
         self._ex = experts_of(experts)
-        self._ws = None
-        self._ws_T = -1
         self.reserve(T)
+
+    def _dims(self, T):
+        return dims_of(T, self.d, self.E, self.k, self.f, self.act)
+
+    def _ws_bytes(self, dims):
+        return lib().moe_workspace_bytes(ctypes.byref(dims), ENTRY_LAYER_FORWARD)
 
     def reserve(self, T):
-        if T > self._ws_T:
-            dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
-            self._ws = workspace(dims, ENTRY_LAYER_FORWARD, self.router_w.device)
-            self._ws_T = T
+        """Make the workspace large enough for a call with T tokens."""
+        return self._ensure_ws(self._ws_bytes(self._dims(T)), self.router_w.device)
 
     def forward(self, x, y=None, topk_ids=None, topk_w=None, stream=None):
-        T = x.shape[0]
-        self.reserve(T)
-        if y is None:
-            y = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
-        dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
-        st = lib().moe_layer_forward(ctypes.byref(dims), _ptr(x), _ptr(self.router_w),
-                                     _ptr(self.bias), ctypes.byref(self._ex), _ptr(y),
-                                     _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
-                                     self._ws.numel(), _stream(stream))
-        _check(st, "moe_layer_forward")
+        s = _on(stream)
+        with torch.cuda.stream(s):
+            x = _bits16(x)
+            T = x.shape[0]
+            dims = self._dims(T)
+            ws = self.reserve(T)
+            _keep(ws, s)
+            if y is None:
+                y = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
+            st = getattr(lib(), self._entry)(
+                ctypes.byref(dims), _ptr(x), _ptr(self.router_w), _ptr(self.bias),
+                ctypes.byref(self._ex), _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(ws),
+                ws.numel(), _stream(s))
+        _check(st, self._entry)
         return y
+
+
+def _routing_outputs(T, k, device, want):
+    if not want:
+        return None, None
+    return (torch.empty((T, k), dtype=torch.int32, device=device),
+            torch.empty((T, k), dtype=torch.float32, device=device))
 
 
 def moe_layer_forward(x, router_w, experts: dict, k, router_bias=None, return_routing=False,
                       stream=None, act=ACT_BF16):
     """The whole layer.  Returns y bf16 [T][d] (and topk_ids, topk_w).
     act: ACT_BF16, or ACT_MX_E2M3 for the activation-MX mode."""
-    x = _bits16(x)
-    T = x.shape[0]
-    layer = Layer(experts, router_w, k, router_bias, T=T, act=act)
-    ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
-    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
-    y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x = _bits16(x)
+        T = x.shape[0]
+        layer = Layer(experts, router_w, k, router_bias, T=T, act=act)
+        ids, w = _routing_outputs(T, k, x.device, return_routing)
+        y = layer.forward(x, topk_ids=ids, topk_w=w, stream=s)
     return (y, ids, w) if return_routing else y
 
 
@@ -344,17 +403,19 @@ def tail_of(tail: dict) -> TailWeights:
 
 def moe_rmsnorm(x, gamma, eps, stream=None):
     """xn bf16 [T][d] = RMSNorm(x) * gamma (canonical fp64 order, bit-exact)."""
-    x = _bits16(x)
-    T, d = x.shape
-    dims = dims_of(T, d, 1, 1, 32)
-    xn = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
-    st = lib().moe_rmsnorm(ctypes.byref(dims), _ptr(x), _ptr(_bits16(gamma)), float(eps),
-                           _ptr(xn), _stream(stream))
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x, gamma = _bits16(x), _bits16(gamma)
+        T, d = x.shape
+        dims = dims_of(T, d, 1, 1, 32)
+        xn = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+        st = lib().moe_rmsnorm(ctypes.byref(dims), _ptr(x), _ptr(gamma), float(eps),
+                               _ptr(xn), _stream(s))
     _check(st, "moe_rmsnorm")
     return xn
 
 
-class Block:
+class Block(_Reusable):
     """Device pointers, dims and a reusable workspace for repeated
     ``moe_block_forward`` calls: out = x + routed(xn) + shared(xn),
     xn = RMSNorm(x) * gamma."""
@@ -371,30 +432,28 @@ class Block:
         self.k = k
         self._ex = experts_of(experts)
         self._tw = tail_of(tail)
-        self._ws = None
-        self._ws_T = -1
         self.reserve(T)
 
     def reserve(self, T):
-        if T > self._ws_T:
-            dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
-            n = lib().moe_block_workspace_bytes(ctypes.byref(dims), ctypes.byref(self._tw))
-            if n == SIZE_MAX:
-                raise MoeError(MOE_ERR_SHAPE, "moe_block_workspace_bytes")
-            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.router_w.device)
-            self._ws_T = T
+        """Make the workspace large enough for a call with T tokens."""
+        dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
+        n = lib().moe_block_workspace_bytes(ctypes.byref(dims), ctypes.byref(self._tw))
+        return self._ensure_ws(n, self.router_w.device)
 
     def forward(self, x, out=None, topk_ids=None, topk_w=None, stream=None):
-        x = _bits16(x)
-        T = x.shape[0]
-        self.reserve(T)
-        if out is None:
-            out = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
-        dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
-        st = lib().moe_block_forward(ctypes.byref(dims), _ptr(x), ctypes.byref(self._tw),
-                                     _ptr(self.router_w), _ptr(self.bias), ctypes.byref(self._ex),
-                                     _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
-                                     self._ws.numel(), _stream(stream))
+        s = _on(stream)
+        with torch.cuda.stream(s):
+            x = _bits16(x)
+            T = x.shape[0]
+            ws = self.reserve(T)
+            _keep(ws, s)
+            if out is None:
+                out = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
+            dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
+            st = lib().moe_block_forward(ctypes.byref(dims), _ptr(x), ctypes.byref(self._tw),
+                                         _ptr(self.router_w), _ptr(self.bias),
+                                         ctypes.byref(self._ex), _ptr(out), _ptr(topk_ids),
+                                         _ptr(topk_w), _ptr(ws), ws.numel(), _stream(s))
         _check(st, "moe_block_forward")
         return out
 
@@ -402,12 +461,13 @@ class Block:
 def moe_block_forward(x, router_w, experts: dict, k, tail: dict, router_bias=None,
                       return_routing=False, stream=None, act=ACT_BF16):
     """The pre-norm MoE block.  Returns out bf16 [T][d] (and topk_ids, topk_w)."""
-    x = _bits16(x)
-    T = x.shape[0]
-    blk = Block(experts, router_w, k, tail, router_bias, T=T, act=act)
-    ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
-    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
-    out = blk.forward(x, topk_ids=ids, topk_w=w, stream=stream)
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x = _bits16(x)
+        T = x.shape[0]
+        blk = Block(experts, router_w, k, tail, router_bias, T=T, act=act)
+        ids, w = _routing_outputs(T, k, x.device, return_routing)
+        out = blk.forward(x, topk_ids=ids, topk_w=w, stream=s)
     return (out, ids, w) if return_routing else out
 
 
@@ -427,79 +487,62 @@ def fp8_workspace(dims: Dims, entry: int, device) -> torch.Tensor:
 def moe_expert_ffn_fp8(x, experts: dict, offsets, sorted_rows, k, ws=None, stream=None):
     """Expert FFN over grouped rows with FP8 experts.  Returns rows_out bf16
     [T*k][d]."""
-    x = _bits16(x)
-    T, d = x.shape
-    E, two_f = experts["gu_codes"].shape[:2]
-    dims = dims_of(T, d, E, k, two_f // 2)
-    rows_out = torch.empty((T * k, d), dtype=torch.bfloat16, device=x.device)
-    if ws is None:
-        ws = fp8_workspace(dims, ENTRY_EXPERT_FFN, x.device)
-    ex = fp8_experts_of(experts)
-    st = lib().moe_expert_ffn_fp8(ctypes.byref(dims), _ptr(x), ctypes.byref(ex), _ptr(offsets),
-                                  _ptr(sorted_rows), _ptr(rows_out), _ptr(ws), ws.numel(),
-                                  _stream(stream))
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x = _bits16(x)
+        T, d = x.shape
+        E, two_f = experts["gu_codes"].shape[:2]
+        dims = dims_of(T, d, E, k, two_f // 2)
+        rows_out = torch.empty((T * k, d), dtype=torch.bfloat16, device=x.device)
+        if ws is None:
+            ws = fp8_workspace(dims, ENTRY_EXPERT_FFN, x.device)
+        offsets, sorted_rows = offsets.contiguous(), sorted_rows.contiguous()
+        ex = fp8_experts_of(experts)
+        st = lib().moe_expert_ffn_fp8(ctypes.byref(dims), _ptr(x), ctypes.byref(ex),
+                                      _ptr(offsets), _ptr(sorted_rows), _ptr(rows_out),
+                                      _ptr(ws), ws.numel(), _stream(s))
     _check(st, "moe_expert_ffn_fp8")
     return rows_out
 
 
-class Fp8Layer:
+class Fp8Layer(Layer):
     """Reusable workspace and pointers for repeated moe_layer_forward_fp8 calls."""
 
+    _entry = "moe_layer_forward_fp8"
+
     def __init__(self, experts: dict, router_w, k, router_bias=None, T=1):
-        self.experts = experts
-        self.router_w = _bits16(router_w)
-        self.bias = None if router_bias is None else router_bias.contiguous().float()
-        self.E, self.d = self.router_w.shape
-        self.f = experts["gu_codes"].shape[1] // 2
-        self.k = k
+        super().__init__(experts, router_w, k, router_bias, T=T)
         self._ex = fp8_experts_of(experts)
-        self._ws = None
-        self._ws_T = -1
-        self.reserve(T)
 
-    def reserve(self, T):
-        if T > self._ws_T:
-            dims = dims_of(T, self.d, self.E, self.k, self.f)
-            self._ws = fp8_workspace(dims, ENTRY_LAYER_FORWARD, self.router_w.device)
-            self._ws_T = T
-
-    def forward(self, x, y=None, topk_ids=None, topk_w=None, stream=None):
-        x = _bits16(x)
-        T = x.shape[0]
-        self.reserve(T)
-        if y is None:
-            y = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
-        dims = dims_of(T, self.d, self.E, self.k, self.f)
-        st = lib().moe_layer_forward_fp8(ctypes.byref(dims), _ptr(x), _ptr(self.router_w),
-                                         _ptr(self.bias), ctypes.byref(self._ex), _ptr(y),
-                                         _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
-                                         self._ws.numel(), _stream(stream))
-        _check(st, "moe_layer_forward_fp8")
-        return y
+    def _ws_bytes(self, dims):
+        return lib().moe_fp8_workspace_bytes(ctypes.byref(dims), ENTRY_LAYER_FORWARD)
 
 
 def moe_layer_forward_fp8(x, router_w, experts: dict, k, router_bias=None,
                           return_routing=False, stream=None):
     """The layer with FP8 experts.  Returns y bf16 [T][d] (and topk_ids, topk_w)."""
-    x = _bits16(x)
-    T = x.shape[0]
-    layer = Fp8Layer(experts, router_w, k, router_bias, T=T)
-    ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
-    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
-    y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x = _bits16(x)
+        T = x.shape[0]
+        layer = Fp8Layer(experts, router_w, k, router_bias, T=T)
+        ids, w = _routing_outputs(T, k, x.device, return_routing)
+        y = layer.forward(x, topk_ids=ids, topk_w=w, stream=s)
     return (y, ids, w) if return_routing else y
 
 
 # ---- operand-order (packed) expert store (include/moe_packed.h) ---------------------
 def moe_prepack_experts(experts: dict, d: int, f: int, stream=None) -> dict:
     """The packed layout of an MXFP4 store (new tensors of the same shapes)."""
-    E = experts["gu_codes"].shape[0]
-    dims = dims_of(1, d, E, 1, f)
-    out = {n: torch.empty_like(v) for n, v in experts.items()
-           if n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")}
-    src, dst = experts_of(experts), experts_of(out)
-    st = lib().moe_prepack_experts(ctypes.byref(dims), ctypes.byref(src), ctypes.byref(dst),
-                                   _stream(stream))
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        E = experts["gu_codes"].shape[0]
+        dims = dims_of(1, d, E, 1, f)
+        out = {n: torch.empty_like(v) for n, v in experts.items()
+               if n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")}
+        src, dst = experts_of(experts), experts_of(out)
+        st = lib().moe_prepack_experts(ctypes.byref(dims), ctypes.byref(src), ctypes.byref(dst),
+                                       _stream(s))
     _check(st, "moe_prepack_experts")
     return out
 
@@ -507,28 +550,17 @@ def moe_prepack_experts(experts: dict, d: int, f: int, stream=None) -> dict:
 class PackedLayer(Layer):
     """moe_layer_forward_packed with a reusable workspace (prefill-sized T)."""
 
-    def forward(self, x, y=None, topk_ids=None, topk_w=None, stream=None):
-        x = _bits16(x)
-        T = x.shape[0]
-        self.reserve(T)
-        if y is None:
-            y = torch.empty((T, self.d), dtype=torch.bfloat16, device=x.device)
-        dims = dims_of(T, self.d, self.E, self.k, self.f, self.act)
-        st = lib().moe_layer_forward_packed(ctypes.byref(dims), _ptr(x), _ptr(self.router_w),
-                                            _ptr(self.bias), ctypes.byref(self._ex), _ptr(y),
-                                            _ptr(topk_ids), _ptr(topk_w), _ptr(self._ws),
-                                            self._ws.numel(), _stream(stream))
-        _check(st, "moe_layer_forward_packed")
-        return y
+    _entry = "moe_layer_forward_packed"
 
 
 def moe_layer_forward_packed(x, router_w, packed: dict, k, router_bias=None,
                              return_routing=False, stream=None, act=ACT_BF16):
     """The layer on a packed store (T >= 128).  Returns y (and topk_ids, topk_w)."""
-    x = _bits16(x)
-    T = x.shape[0]
-    layer = PackedLayer(packed, router_w, k, router_bias, T=T, act=act)
-    ids = torch.empty((T, k), dtype=torch.int32, device=x.device) if return_routing else None
-    w = torch.empty((T, k), dtype=torch.float32, device=x.device) if return_routing else None
-    y = layer.forward(x, topk_ids=ids, topk_w=w, stream=stream)
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x = _bits16(x)
+        T = x.shape[0]
+        layer = PackedLayer(packed, router_w, k, router_bias, T=T, act=act)
+        ids, w = _routing_outputs(T, k, x.device, return_routing)
+        y = layer.forward(x, topk_ids=ids, topk_w=w, stream=s)
     return (y, ids, w) if return_routing else y
