@@ -96,8 +96,11 @@ CONFIGS = {
               896, 16, 1536, seed=1, batches=1000),
     2: Config(2, "batched decode T=64 d=7168 E=896 k=16 f=1536", 64, 7168, 896,
               16, 1536, seed=2, batches=50),
+    # beta bisected so that the hottest expert gets 9.5-10.5x the mean load
+    # under the canonical routing (9.98x: 730 rows against 73.1; the
+    # coldest gets 20) -- tests/golden/zipf_beta.py, zipf_beta.json
     3: Config(3, "zipf prefill T=4096 d=7168 E=896 k=16 f=1536", 4096, 7168,
-              896, 16, 1536, seed=3, zipf_beta=0.34),
+              896, 16, 1536, seed=3, zipf_beta=0.3375),
     4: Config(4, "long prefill T=32768 d=7168 E=896 k=16 f=1536", 32768, 7168,
               896, 16, 1536, seed=4),
     # a second routing shape: 256 experts, top-8 (MiMo V2.6 Flash); d and f
