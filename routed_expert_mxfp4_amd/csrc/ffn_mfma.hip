@@ -102,6 +102,11 @@ struct SplitBlock {
 
 __device__ __forceinline__ SplitBlock split_block32(const float (&v)[32]) {
     SplitBlock b;
+    // a NaN element has no E2M3 code: the block's scales become the E8M0
+    // NaN code 255, which the scaled MFMA carries into every product
+    bool nan = false;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) nan |= v[i] != v[i];
     const int xh = mx_exponent(amax32(v));
     b.hi = e2m3_pack32(v, e8m0_operand(xh));
     const f32x32_t hd = e2m3_unpack32(b.hi, e8m0_operand(xh));
@@ -110,7 +115,7 @@ __device__ __forceinline__ SplitBlock split_block32(const float (&v)[32]) {
     for (int i = 0; i < 32; ++i) r[i] = v[i] - hd[i];
     const int xl = mx_exponent(amax32(r));
     b.lo = e2m3_pack32(r, e8m0_operand(xl));
-    b.scales = (uint32_t)(xh + 127) | ((uint32_t)(xl + 127) << 8);
+    b.scales = nan ? 0xFFFFu : (uint32_t)(xh + 127) | ((uint32_t)(xl + 127) << 8);
     return b;
 }
 
