@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Activation modes of the expert GEMMs (moe_dims.act):
  *   MOE_ACT_BF16     x and h as computed (bf16 x, fp32 h): the layer's
@@ -107,7 +107,9 @@ typedef enum moe_status {
     MOE_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned           */
     MOE_ERR_WORKSPACE = 4,   /* ws_bytes < moe_workspace_bytes(...)        */
     MOE_ERR_UNSUPPORTED = 5, /* valid request the library does not serve   */
-    MOE_ERR_DEVICE = 6       /* HIP reported an error while launching      */
+    MOE_ERR_DEVICE = 6,      /* HIP reported an error while launching      */
+    MOE_ERR_SCRATCH = 7      /* moe_layer_forward_noalloc: the call needs
+                                more than MOE_NOALLOC_SCRATCH_BYTES        */
 } moe_status;
 
 typedef enum moe_entry {
@@ -189,6 +191,35 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x,
                              const moe_mxfp4_experts *experts, uint16_t *y,
                              int32_t *topk_ids_out, float *topk_w_out,
                              void *ws, size_t ws_bytes, void *hip_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * exactly as moe_layer_forward computes it (same kernels, same bits), with
+ * no workspace argument and no allocation of any kind.  Its scratch is one
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES, which the library holds
+ * on every GPU it runs on until the process ends.
+ *   - A call whose moe_workspace_bytes(dims, MOE_ENTRY_LAYER_FORWARD)
+ *     exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH and
+ *     launches nothing.  (The Kimi-K3 shape, d = 7168, 896 experts, top-16,
+ *     f = 1536, fits up to 235 tokens.)
+ *   - Every call on one GPU uses that GPU's one array: calls that can
+ *     overlap on one GPU (other streams, other host threads) race on it and
+ *     must be serialised by the caller.  The array keeps the last call's
+ *     contents; no kernel reads a byte of it that the same call has not
+ *     written first, so nothing needs clearing between calls.
+ *   - hip_stream must belong to the calling thread's current device
+ *     (MOE_ERR_UNSUPPORTED otherwise).  The first call on a device looks up
+ *     that device's address of the array (hipGetSymbolAddress, which
+ *     allocates nothing).
+ * Arguments, outputs, validation and the other conventions are those of
+ * moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(const moe_dims *dims, const uint16_t *x,
+                                     const uint16_t *router_w,
+                                     const float *router_bias,
+                                     const moe_mxfp4_experts *experts, uint16_t *y,
+                                     int32_t *topk_ids_out, float *topk_w_out,
+                                     void *hip_stream);
 
 #ifdef __cplusplus
 }

@@ -358,6 +358,42 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
 
 }  // namespace
 
+// ---- static scratch of moe_layer_forward_noalloc ------------------------------
+// One array per device, in the code object's data (not an allocation).  Host
+// code never passes `scratch` itself to a kernel or a copy: on the host the
+// name is only a stand-in for the symbol.  Its address on a device comes
+// from hipGetSymbolAddress with that device current, once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on first use).
+moe_status scratch_for_current_device(hipStream_t s, void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_DEVICE;
+    if (dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    if (s) {
+        hipDevice_t sd = -1;
+        if (hipStreamGetDevice(s, &sd) != hipSuccess) return MOE_ERR_DEVICE;
+        if ((int)sd != dev) return MOE_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOE_ERR_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
 
 extern "C" {
 
@@ -372,6 +408,8 @@ const char *moe_status_str(int status) {
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes()";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid request this library does not serve";
     case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE: HIP reported an error while launching";
+    case MOE_ERR_SCRATCH:
+        return "MOE_ERR_SCRATCH: the call needs more scratch than MOE_NOALLOC_SCRATCH_BYTES";
     default: return "unknown moe_status";
     }
 }
@@ -544,6 +582,29 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x, const uint
         return device_status(run_layer(D, x, router_w, router_bias, *experts, y, topk_ids_out,
                                        topk_w_out, static_cast<char *>(ws),
                                        static_cast<hipStream_t>(hip_stream), nullptr, nullptr));
+    });
+}
+
+moe_status moe_layer_forward_noalloc(const moe_dims *dims, const uint16_t *x,
+                                     const uint16_t *router_w, const float *router_bias,
+                                     const moe_mxfp4_experts *experts, uint16_t *y,
+                                     int32_t *topk_ids_out, float *topk_w_out,
+                                     void *hip_stream) {
+    return guarded([&]() -> moe_status {
+        moe_status st = check_dims(dims);
+        if (st != MOE_OK) return st;
+        const moe_dims &D = *dims;
+        if (D.T == 0) return MOE_OK;
+        if (!x || !router_w || !y) return MOE_ERR_NULL;
+        if ((st = check_experts(experts)) != MOE_OK) return st;
+        if (!aligned16(x) || !aligned16(router_w) || !aligned16(y)) return MOE_ERR_ALIGN;
+        if (layer_ws(D).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+        hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        void *ws = nullptr;
+        if ((st = scratch_for_current_device(s, &ws)) != MOE_OK) return st;
+        return device_status(run_layer(D, x, router_w, router_bias, *experts, y, topk_ids_out,
+                                       topk_w_out, static_cast<char *>(ws), s, nullptr,
+                                       nullptr));
     });
 }
 

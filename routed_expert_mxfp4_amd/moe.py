@@ -16,7 +16,8 @@ import torch
 from .build import LIB_PATH
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN = 0, 1, 2, 3
-MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE = 4, 5, 6
+MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED, MOE_ERR_DEVICE, MOE_ERR_SCRATCH = 4, 5, 6, 7
+NOALLOC_SCRATCH_BYTES = 64 << 20      # MOE_NOALLOC_SCRATCH_BYTES (include/moe.h)
 ENTRY_ROUTE, ENTRY_PERMUTE, ENTRY_EXPERT_FFN, ENTRY_COMBINE, ENTRY_LAYER_FORWARD = range(5)
 SIZE_MAX = (1 << 64) - 1
 
@@ -55,7 +56,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_diag_time_kernel", "moe_diag_kernel_time", "moe_diag_mx_split_e2m3",
            "moe_block_workspace_bytes", "moe_rmsnorm", "moe_block_forward",
            "moe_fp8_workspace_bytes", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
-           "moe_prepack_experts", "moe_layer_forward_packed", "moe_diag_kernel_times")
+           "moe_prepack_experts", "moe_layer_forward_packed", "moe_diag_kernel_times",
+           "moe_layer_forward_noalloc")
 
 _lib = None
 
@@ -88,6 +90,8 @@ def lib():
         L.moe_combine.argtypes = [DP, P, P, P, P, P]
         L.moe_layer_forward.restype = I
         L.moe_layer_forward.argtypes = [DP, P, P, P, EP, P, P, P, P, S, P]
+        L.moe_layer_forward_noalloc.restype = I
+        L.moe_layer_forward_noalloc.argtypes = [DP, P, P, P, EP, P, P, P, P]
         FP = ctypes.POINTER(Fp8Experts)
         L.moe_fp8_workspace_bytes.restype = S
         L.moe_fp8_workspace_bytes.argtypes = [DP, I]
@@ -388,6 +392,29 @@ def moe_layer_forward(x, router_w, experts: dict, k, router_bias=None, return_ro
         ids, w = _routing_outputs(T, k, x.device, return_routing)
         y = layer.forward(x, topk_ids=ids, topk_w=w, stream=s)
     return (y, ids, w) if return_routing else y
+
+
+def moe_layer_forward_noalloc(x, router_w, experts: dict, k, router_bias=None, y=None,
+                              topk_ids=None, topk_w=None, stream=None):
+    """The layer on the library's static scratch (no workspace, no device
+    allocation inside the call).  Outputs are the caller's: pass y (bf16
+    [T][d]) and, if wanted, topk_ids / topk_w to allocate nothing at all."""
+    s = _on(stream)
+    with torch.cuda.stream(s):
+        x, router_w = _bits16(x), _bits16(router_w)
+        T, d = x.shape
+        E = router_w.shape[0]
+        f = experts["gu_codes"].shape[1] // 2
+        if y is None:
+            y = torch.empty((T, d), dtype=torch.bfloat16, device=x.device)
+        bias = None if router_bias is None else router_bias.contiguous().float()
+        dims = dims_of(T, d, E, k, f)
+        ex = experts_of(experts)
+        st = lib().moe_layer_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(router_w),
+                                             _ptr(bias), ctypes.byref(ex), _ptr(y),
+                                             _ptr(topk_ids), _ptr(topk_w), _stream(s))
+    _check(st, "moe_layer_forward_noalloc")
+    return y
 
 
 # ---- MoE tail (include/moe_tail.h) ------------------------------------------------

@@ -35,11 +35,11 @@ def test_exports_every_declared_symbol(L):
     assert set(declared) == set(moe.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_status_strings(L):
-    for s in range(7):
+    for s in range(8):
         txt = moe.status_str(s)
         assert txt and "unknown" not in txt
     assert "unknown" in moe.status_str(99)
@@ -127,6 +127,29 @@ def test_zero_tokens_is_a_no_op(L):
                                None, None, None, 0, None) == moe.MOE_OK
     assert L.moe_permute(ctypes.byref(dims), None, None, None, None, None, None, 0, None) == moe.MOE_OK
     assert L.moe_combine(ctypes.byref(dims), None, None, None, None, None) == moe.MOE_OK
+
+
+def test_noalloc_refuses_before_any_launch(L):
+    A = ctypes.c_void_p(0x10000)
+    M = ctypes.c_void_p(0x10008)
+    ex = moe.Experts(0x10000, 0x10000, 0x10000, 0x10000)
+    f = L.moe_layer_forward_noalloc
+    # the K3 shape fits the static scratch up to 235 tokens, not at 236
+    fit, over = _dims(T=235, d=7168, E=896, k=16, f=1536), _dims(T=236, d=7168, E=896, k=16, f=1536)
+    assert moe.moe_workspace_bytes(fit, moe.ENTRY_LAYER_FORWARD) <= moe.NOALLOC_SCRATCH_BYTES
+    assert moe.moe_workspace_bytes(over, moe.ENTRY_LAYER_FORWARD) > moe.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(over), A, A, None, ctypes.byref(ex), A, None, None, None) == moe.MOE_ERR_SCRATCH
+    big = _dims(T=32768, d=7168, E=896, k=16, f=1536)
+    assert f(ctypes.byref(big), A, A, None, ctypes.byref(ex), A, None, None, None) == moe.MOE_ERR_SCRATCH
+    dims = _dims()
+    assert f(None, A, A, None, ctypes.byref(ex), A, None, None, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), None, A, None, ctypes.byref(ex), A, None, None, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), A, A, None, None, A, None, None, None) == moe.MOE_ERR_NULL
+    assert f(ctypes.byref(dims), A, A, None, ctypes.byref(ex), M, None, None, None) == moe.MOE_ERR_ALIGN
+    assert f(ctypes.byref(_dims(d=100)), A, A, None, ctypes.byref(ex), A, None, None, None) == moe.MOE_ERR_SHAPE
+    assert f(ctypes.byref(_dims(T=0)), None, None, None, ctypes.byref(ex), None, None, None,
+             None) == moe.MOE_OK
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in moe.status_str(moe.MOE_ERR_SCRATCH)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
