@@ -47,7 +47,7 @@ KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm"
            "combine", "fp8_gate_up", "fp8_down")
 # the pre-norm block's own kernels (--tail)
 TAIL_KERNELS = ("rmsnorm", "shared_gate_up", "shared_down_add", "shared_gemm_gate_up",
-                "shared_swiglu", "shared_gemm_down")
+                "shared_gemm_down")
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 / MXFP6, published
 MFMA_MIN_T = 128                # the library's scaled-MFMA path starts here
 

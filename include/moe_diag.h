@@ -13,8 +13,8 @@
  * splits h) and "down_mfma", and "mx_round" (the activation-MX mode's
  * rounding of x and h on the GEMV paths); for FP8 experts "fp8_gate_up" and
  * "fp8_down"; for the pre-norm block "rmsnorm", "shared_gate_up",
- * "shared_down_add", "shared_gemm_gate_up", "shared_swiglu" and
- * "shared_gemm_down".
+ * "shared_down_add", "shared_gemm_gate_up" (which also applies the SwiGLU)
+ * and "shared_gemm_down".
  */
 #ifndef ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 #define ROUTED_EXPERT_MXFP4_MOE_DIAG_H

@@ -36,8 +36,9 @@
  * launches nothing and touches no output), T == 0 a no-op, no exception
  * crosses the boundary, identical inputs give identical bits.  The MoE
  * block also needs fs % 32 == 0, fs <= 16384, and 16-byte aligned gamma and
- * shared weights.  For T > 8 the shared expert's GEMMs run on rocBLAS
- * (one handle per device, created on the first such call).
+ * shared weights.  Like every entry point, the block allocates nothing: for
+ * T <= 8 the shared expert runs as GEMVs, for T > 8 as two bf16
+ * matrix-core GEMMs (SwiGLU fused into the first), all in this library.
  */
 #ifndef ROUTED_EXPERT_MXFP4_MOE_TAIL_H
 #define ROUTED_EXPERT_MXFP4_MOE_TAIL_H

@@ -2,10 +2,9 @@
 
     python -m routed_expert_mxfp4_amd.build
 
-Sources: ``csrc/*.hip`` (kernels), ``csrc/moe_abi.cpp`` (the C ABI of
-``include/moe.h`` and ``include/moe_tail.h``) and ``csrc/blas.cpp`` (the
-shared expert's library GEMMs; links rocBLAS).  Objects go to ``_build/`` at
-the repository root.
+Sources: ``csrc/*.hip`` (kernels) and ``csrc/moe_abi.cpp`` (the C ABI of the
+``include/*.h`` headers).  The library links the HIP runtime only.  Objects
+go to ``_build/`` at the repository root.
 """
 from __future__ import annotations
 
@@ -63,7 +62,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib")
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + [
-        "-L" + rocm_lib, "-Wl,-rpath," + rocm_lib, "-lrocblas"]
+        "-L" + rocm_lib, "-Wl,-rpath," + rocm_lib]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -173,9 +173,9 @@ moe_status check_fp8(const moe_dims &D, const moe_fp8_experts *w) {
 
 // Pre-norm block: the routed layer's scratch, then xn; few tokens: the
 // routed output y and the shared expert's fp32 h; many tokens: the shared
-// expert's gate/up GEMM output (fp32), its bf16 h and its down output (fp32).
+// expert's bf16 h and its down output (fp32).
 struct BlockWs {
-    size_t layer, xn, yr, hs, gu, hb, sx, total;
+    size_t layer, xn, yr, hs, hb, sx, total;
 };
 BlockWs block_ws(const moe_dims &D, int fs) {
     BlockWs w;
@@ -183,12 +183,11 @@ BlockWs block_ws(const moe_dims &D, int fs) {
     size_t p = 0;
     w.layer = p; p += layer_ws(D).total;
     w.xn = p; p += al256(T * d * 2);
-    w.yr = w.hs = w.gu = w.hb = w.sx = p;
+    w.yr = w.hs = w.hb = w.sx = p;
     if (D.T <= moe::kSharedGemvMaxT) {
         w.yr = p; p += al256(T * d * 2);
         w.hs = p; p += al256(T * (size_t)fs * 4);
     } else if (fs > 0) {
-        w.gu = p; p += al256(T * 2 * (size_t)fs * 4);
         w.hb = p; p += al256(T * (size_t)fs * 2);
         w.sx = p; p += al256(T * d * 4);
     }
@@ -830,22 +829,17 @@ moe_status moe_block_forward(const moe_dims *dims, const uint16_t *x,
                                             D.d, fs, s);
             return device_status(e);
         }
-        // many tokens: the shared expert on the library GEMM, then the routed
-        // layer, whose combine pass adds x and the shared output
+        // many tokens: the shared expert's two GEMMs (SwiGLU fused into the
+        // first), then the routed layer, whose combine pass adds x and the
+        // shared output
         float *sx = nullptr;
         if (fs > 0) {
-            float *gu = reinterpret_cast<float *>(base + B.gu);
             uint16_t *hb = reinterpret_cast<uint16_t *>(base + B.hb);
             sx = reinterpret_cast<float *>(base + B.sx);
-            if (e == hipSuccess) {
-                DiagScope t("shared_gemm_gate_up", s);
-                e = moe::blas_gemm_bf16_nt(xn, tail->shared_gu, gu, D.T, 2 * fs, D.d, s);
-            }
-            if (e == hipSuccess) e = moe::launch_shared_swiglu(gu, hb, D.T, fs, s);
-            if (e == hipSuccess) {
-                DiagScope t("shared_gemm_down", s);
-                e = moe::blas_gemm_bf16_nt(hb, tail->shared_dn, sx, D.T, D.d, fs, s);
-            }
+            if (e == hipSuccess)
+                e = moe::launch_shared_gate_up_gemm(xn, tail->shared_gu, hb, D.T, D.d, fs, s);
+            if (e == hipSuccess)
+                e = moe::launch_shared_down_gemm(hb, tail->shared_dn, sx, D.T, D.d, fs, s);
         }
         if (e == hipSuccess)
             e = run_layer(D, xn, router_w, router_bias, *experts, out, topk_ids_out, topk_w_out,

@@ -270,7 +270,7 @@ hipError_t launch_fp8_down(const float *h, Fp8Args w, const int32_t *offsets,
                            const int32_t *plan, uint16_t *rows_out, int T, int d, int E, int k,
                            int f, hipStream_t s);
 
-// ---- MoE tail (tail.hip, blas.cpp) --------------------------------------------
+// ---- MoE tail (tail.hip, shared_gemm.hip) --------------------------------------
 // xn = bf16(RMSNorm(x) * gamma), canonical fp64 order, one wave per token.
 hipError_t launch_rmsnorm(const uint16_t *x, const uint16_t *gamma, float eps, uint16_t *xn,
                           int T, int d, hipStream_t s);
@@ -280,11 +280,12 @@ constexpr int kSharedGemvMaxT = 8;
 hipError_t launch_shared_gemv(const uint16_t *xn, const uint16_t *sgu, const uint16_t *sdn,
                               const uint16_t *xres, const uint16_t *yr, float *h, uint16_t *out,
                               int T, int d, int fs, hipStream_t s);
-// h = bf16(silu(gu[:, :fs]) * gu[:, fs:]) for gu fp32 [T][2fs].
-hipError_t launch_shared_swiglu(const float *gu, uint16_t *h, int T, int fs, hipStream_t s);
-// Row-major c[M][N] (fp32) = a[M][K] (bf16) * b[N][K]^T (bf16), fp32
-// accumulate, on the library GEMM (rocBLAS) of the current device.
-hipError_t blas_gemm_bf16_nt(const uint16_t *a, const uint16_t *b, float *c, int M, int N,
-                             int K, hipStream_t s);
+// Many tokens, on the bf16 matrix cores (shared_gemm.hip):
+// h bf16 [T][fs] = bf16(silu(xn Wgu[:fs]^T) * (xn Wgu[fs:]^T)), and
+// sx fp32 [T][d] = h Wdn^T.  Need d % 64 == 0, fs % 32 == 0.
+hipError_t launch_shared_gate_up_gemm(const uint16_t *xn, const uint16_t *sgu, uint16_t *h, int T,
+                                      int d, int fs, hipStream_t s);
+hipError_t launch_shared_down_gemm(const uint16_t *h, const uint16_t *sdn, float *sx, int T,
+                                   int d, int fs, hipStream_t s);
 
 }  // namespace moe

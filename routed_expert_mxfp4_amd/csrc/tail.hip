@@ -1,6 +1,6 @@
 // tail.hip -- the MoE tail around the routed layer on gfx950: the RMSNorm
-// that feeds the router and the experts, the shared expert for few tokens,
-// and the SwiGLU between the shared expert's two library GEMMs for many.
+// that feeds the router and the experts, and the shared expert for few
+// tokens (for many tokens its GEMMs are in shared_gemm.hip).
 //
 // The pages' model-shape MoE tail is the weighted reduction, RMSNorm, the
 // routed-up activation quantisation and the residual adds (Moonshine README,
@@ -228,29 +228,6 @@ __global__ __launch_bounds__(256) void shared_down_add_kernel(
     }
 }
 
-// Many tokens: gu = xn W_gu^T came from the library GEMM as fp32 [T][2fs];
-// h = bf16(silu(gate) * up), the down GEMM's bf16 operand.  8 columns per
-// thread.
-__global__ __launch_bounds__(256) void shared_swiglu_kernel(const float *__restrict__ gu,
-                                                            uint16_t *__restrict__ h, int T,
-                                                            int fs) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;      // 8-column group
-    const size_t per = (size_t)(fs >> 3);
-    if (i >= (size_t)T * per) return;
-    const size_t t = i / per, c = (i - t * per) * 8;
-    const float4 *g = reinterpret_cast<const float4 *>(gu + t * 2 * fs + c);
-    const float4 *u = reinterpret_cast<const float4 *>(gu + t * 2 * fs + fs + c);
-    const float4 g0 = g[0], g1 = g[1], u0 = u[0], u1 = u[1];
-    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        o[j] = (uint32_t)f32_to_bf16_rne(silu_mul(gv[2 * j], uv[2 * j])) |
-               ((uint32_t)f32_to_bf16_rne(silu_mul(gv[2 * j + 1], uv[2 * j + 1])) << 16);
-    *reinterpret_cast<uint4 *>(h + t * fs + c) = uint4{o[0], o[1], o[2], o[3]};
-}
-
 template <int NT>
 hipError_t shared_gemv_nt(const uint16_t *xn, const uint16_t *sgu, const uint16_t *sdn,
                           const uint16_t *xres, const uint16_t *yr, float *h, uint16_t *out,
@@ -292,13 +269,6 @@ hipError_t launch_shared_gemv(const uint16_t *xn, const uint16_t *sgu, const uin
     case 8: return shared_gemv_nt<8>(xn, sgu, sdn, xres, yr, h, out, d, fs, s);
     default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_shared_swiglu(const float *gu, uint16_t *h, int T, int fs, hipStream_t s) {
-    const size_t items = (size_t)T * (size_t)(fs >> 3);
-    if (items == 0) return hipSuccess;
-    return timed_launch("shared_swiglu", shared_swiglu_kernel, dim3((unsigned)((items + 255) / 256)),
-                        dim3(256), 0, s, gu, h, T, fs);
 }
 
 }  // namespace moe

@@ -49,6 +49,7 @@ def _close(gpu, ref, what):
     err = float(np.max(np.abs(gpu - ref)))
     scale = float(np.max(np.abs(ref)))
     assert err <= TOL * scale, "%s: max err %.4g > %.0e * %.4g" % (what, err, TOL, scale)
+    return err, scale
 
 
 def _bits_to_bf16(a):
@@ -134,10 +135,13 @@ BLOCK_CASES = [
     (8, 256, 16, 2, 128, 128, 1),     # the tiny workload's shape
     (5, 192, 40, 5, 64, 96, 2),       # odd chunk length, unfused routed down
     (3, 256, 16, 2, 128, 0, 3),       # no shared expert, few tokens
-    (20, 256, 24, 3, 128, 64, 4),     # many tokens: library GEMMs, combine adds
+    (20, 256, 24, 3, 128, 64, 4),     # many tokens: shared GEMMs, combine adds
     (40, 256, 24, 3, 128, 0, 5),      # no shared expert, many tokens
     (200, 512, 16, 2, 256, 256, 6),   # scaled-MFMA routed experts (T >= 128)
     (300, 512, 24, 4, 256, 160, 7),   # filtered routing (T >= 256), ragged fs
+    (20, 256, 24, 3, 128, 96, 8),     # shared down GEMM's K = 96: a half K step
+    (12, 192, 40, 5, 64, 96, 9),      # d = 192: a half N tile in the down GEMM
+    (520, 1024, 32, 4, 256, 320, 10), # five row tiles (the last ragged), five gate tiles
 ]
 
 
@@ -151,6 +155,18 @@ def test_block_small(dev, case):
     np.testing.assert_array_equal(ids.cpu().numpy(), ref["topk_ids"])
     assert np.abs(w.cpu().numpy() - ref["topk_w"]).max() <= W_TOL
     _close(_bf16_to_f64(out), ref["out64"], "block out")
+
+
+@pytest.mark.parametrize("T", [9, 333])
+def test_block_shared_expert_at_the_model_shape(dev, T):
+    """Routed experts all zero, so out = x + shared(xn): the shared expert's
+    two matrix-core GEMMs at d = 7168, fs = 1536 (ragged row tiles) against
+    the oracle's fp64 shared expert."""
+    cfg, L, tail = _small(T, 7168, 8, 2, 256, 1536, 60 + T, zero_experts=True)
+    out, _, _ = _gpu_block(dev, cfg, L, tail)
+    ref = _oracle_block(cfg, L, tail)
+    err, scale = _close(_bf16_to_f64(out), ref["out64"], "block out")
+    print("T=%d: max err %.3g of max|out| %.3g" % (T, err, scale))
 
 
 @pytest.mark.parametrize("T", [2, 6, 20, 150])
