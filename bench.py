@@ -77,6 +77,14 @@ def parse():
                     help="tokens of the workload the CPU oracle runs (0: skip)")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel timing passes after the timed region")
+    ap.add_argument("--gemv-max-rows", type=int, default=None, metavar="N",
+                    help="diagnostic: override the per-expert crossover (experts with at most "
+                         "N rows take the GEMVs in a scaled-MFMA call; 0..16)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="only measure the per-expert crossover of the expert paths: "
+                         "moe_expert_ffn at the K3 shape with every expert given n rows, all "
+                         "experts on the grouped GEMVs against all on scaled-MFMA tiles, for "
+                         "n = 1..16; prints one JSON line and exits")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain fp32 device copy (torch.neg) of MIB MiB five "
                          "times, the reference for scaling HBM traffic counters, and exit")
@@ -96,6 +104,58 @@ def calibrate_copy(mib: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
                       "launches": 5}))
+
+
+def crossover(reps: int = 10) -> None:
+    """Time moe_expert_ffn on the K3 shape (d=7168, E=896, top-16, f=1536)
+    with exactly n rows per expert (T = n*E/k tokens, token t's slot j on
+    expert (t*k + j) mod E), once with every expert on the grouped GEMVs
+    (crossover override 16) and once with every expert on 128-row
+    scaled-MFMA tiles (override 0).  The crossover is the largest n up to
+    which the GEMVs are faster at every n."""
+    import torch
+    from routed_expert_mxfp4_amd import moe, synth
+    cfg = synth.CONFIGS[4]
+    dev = torch.device("cuda:0")
+    E, k, d, f = cfg.E, cfg.k, cfg.d, cfg.f
+    experts = synth.gen_experts(cfg, device=dev)
+    ns = (1, 2, 3, 4, 5, 6, 8, 10, 12, 16)
+    xs = synth.gen_x(cfg, tokens=range(max(ns) * E // k)).to(dev)
+    table = []
+    for n in ns:
+        T = n * E // k
+        t = torch.arange(T, dtype=torch.int64)[:, None] * k + torch.arange(k)[None, :]
+        ids = (t % E).to(torch.int32).to(dev)
+        _, offsets, sr, _ = moe.moe_permute(ids, E)
+        x = xs[:T].contiguous()
+        row = {"rows_per_expert": n, "tokens": T}
+        for path, R in (("gemv", 16), ("mfma", 0)):
+            moe.diag_set_gemv_max_rows(R)
+            ws = moe.workspace(moe.dims_of(T, d, E, k, f), moe.ENTRY_EXPERT_FFN, dev)
+            for _ in range(3):
+                moe.moe_expert_ffn(x, experts, offsets, sr, k, ws=ws)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+            for i in range(reps):
+                ev[2 * i].record()
+                moe.moe_expert_ffn(x, experts, offsets, sr, k, ws=ws)
+                ev[2 * i + 1].record()
+            torch.cuda.synchronize()
+            ms = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps))
+            row[path + "_ms"] = ms[reps // 2]
+            row[path + "_us_per_expert"] = 1e3 * ms[reps // 2] / E
+        moe.diag_set_gemv_max_rows(None)
+        table.append(row)
+        print("rows/expert %2d: gemv %.3f ms, mfma %.3f ms" % (n, row["gemv_ms"], row["mfma_ms"]),
+              file=sys.stderr, flush=True)
+    cross = 0
+    for row in table:
+        if row["gemv_ms"] < row["mfma_ms"]:
+            cross = row["rows_per_expert"]
+        else:
+            break
+    print(json.dumps({"crossover_rows": cross, "built_in": moe.diag_gemv_max_rows(),
+                      "shape": {"d": d, "E": E, "k": k, "f": f}, "median_of": reps,
+                      "table": table}))
 
 
 def cpu_model():
@@ -195,6 +255,11 @@ def main():
     if args.calibrate_copy > 0:
         calibrate_copy(args.calibrate_copy)
         return
+    if args.crossover:
+        crossover()
+        return
+    if args.gemv_max_rows is not None:
+        moe.diag_set_gemv_max_rows(args.gemv_max_rows)
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[WORKLOADS[args.workload]]
     if args.steps is None:

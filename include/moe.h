@@ -201,7 +201,7 @@ moe_status moe_layer_forward(const moe_dims *dims, const uint16_t *x,
  *   - A call whose moe_workspace_bytes(dims, MOE_ENTRY_LAYER_FORWARD)
  *     exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH and
  *     launches nothing.  (The Kimi-K3 shape, d = 7168, 896 experts, top-16,
- *     f = 1536, fits up to 235 tokens.)
+ *     f = 1536, fits up to 216 tokens.)
  *   - Every call on one GPU uses that GPU's one array: calls that can
  *     overlap on one GPU (other streams, other host threads) race on it and
  *     must be serialised by the caller.  The array keeps the last call's

@@ -9,8 +9,8 @@
  * "router_select", "router_refine" (routing of many tokens; the refine
  * kernel also takes the top-k), "plan", "gemv_gate_up", "gemv_down",
  * "down_combine", "combine", "mfma_ffn" (the whole scaled-MFMA expert
- * FFN of large T), its parts "mx_split_x", "gate_up_mfma" (which also
- * splits h) and "down_mfma", and "mx_round" (the activation-MX mode's
+ * FFN, with its small experts' GEMVs), its parts "mx_split_x",
+ * "gate_up_mfma" (which also splits h) and "down_mfma", and "mx_round" (the activation-MX mode's
  * rounding of x and h on the GEMV paths); for FP8 experts "fp8_gate_up" and
  * "fp8_down"; for the pre-norm block "rmsnorm", "shared_gate_up",
  * "shared_down_add", "shared_gemm_gate_up" (which also applies the SwiGLU)
@@ -65,6 +65,18 @@ int moe_diag_kernel_time(double *total_ms, long long *launches);
  * like moe_diag_kernel_time.  Returns 0, or -1 on a HIP error or bad
  * arguments. */
 int moe_diag_kernel_times(double *ms_out, int cap, long long *launches);
+
+/* The per-expert path choice of the bf16 layer: in a call on the
+ * scaled-MFMA expert path, experts with at most this many rows take the
+ * grouped dequant-GEMVs instead of 128-row MFMA tiles.  Set 0..16 to
+ * override the built-in crossover for the calls that follow (0: every
+ * expert on MFMA tiles), -1 to restore it; a benchmark sweeps it to measure
+ * the crossover.  Process-wide; moe_workspace_bytes follows the setting, so
+ * size workspaces after setting it.  Returns 0, or -1 outside -1..16. */
+int moe_diag_set_gemv_max_rows(int rows);
+
+/* The crossover in effect (the override if one is set). */
+int moe_diag_gemv_max_rows(void);
 
 #ifdef __cplusplus
 }

@@ -296,14 +296,19 @@ __device__ __forceinline__ float pair_h(const PairBuf<NBL> &pb, const uint4 *__r
     return silu_mul(g, u);
 }
 
+// Experts a = blockIdx.y, blockIdx.y + gridDim.y, ... of the plan.  h row of
+// (expert a, its r-th row): row0 + r, or a * hstride + r when hstride > 0
+// (the compact rows of the mixed path's small experts).
 template <int NBL>
 __global__ __launch_bounds__(256) void gate_up_regx_kernel(
     const uint16_t *__restrict__ x, ExpertArgs W, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
-    float *__restrict__ h, int T, int d, int E, int k, int f) {
+    float *__restrict__ h, int T, int d, int E, int k, int f, int hstride) {
     const int nrows = T * k;
+    for (int a = blockIdx.y; a < plan[0]; a += gridDim.y) {
     int e, row0, ne;
-    if (!expert_group(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
+    if (!expert_group(plan, offsets, a, E, nrows, e, row0, ne)) continue;
+    if (hstride > 0 && ne > hstride) continue;
     extern __shared__ uint4 xs[];                 // one token row, d/8 x 16 B, + 1 spare
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
             }
         }
         __syncthreads();
-        float* hrow = h + (size_t)(row0 + r) * f;
+        float* hrow = h + (size_t)(hstride > 0 ? a * hstride + r : row0 + r) * f;
         // sched_barrier keeps each stage in place: a later pair's loads may
         // not be hoisted above an earlier pair's math (that would only grow
         // the register footprint, not the bytes in flight)
@@ -352,6 +357,7 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
             if (lane == 0) hrow[n_base + 4 * (q + 1)] = vb;
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
     }
 }
 
@@ -589,10 +595,12 @@ template <int NBLD>
 __global__ __launch_bounds__(256) void down_rows_kernel(
     const float *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ plan, uint16_t *__restrict__ rows_out, int T, int d, int E,
-    int k, int f) {
+    int k, int f, int hstride) {
     const int nrows = T * k;
+    for (int a = blockIdx.y; a < plan[0]; a += gridDim.y) {
     int e, row0, ne;
-    if (!expert_group(plan, offsets, blockIdx.y, E, nrows, e, row0, ne)) return;
+    if (!expert_group(plan, offsets, a, E, nrows, e, row0, ne)) continue;
+    if (hstride > 0 && ne > hstride) continue;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nblk = f >> 5;
@@ -600,7 +608,8 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
     const int m = blockIdx.x * 64 + wid * 16;
     const rsrc_t codes = make_rsrc(W.dn_codes + (size_t)e * d * code_row, (uint32_t)d * code_row);
     const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
-    const rsrc_t hbuf = make_rsrc(h + (size_t)row0 * f, (uint32_t)ne * f * 4u);
+    const rsrc_t hbuf = make_rsrc(h + (size_t)(hstride > 0 ? a * hstride : row0) * f,
+                                  (uint32_t)ne * f * 4u);
     for (int r = 0; r < ne; ++r) {
         float4 hv[NBLD][8];
         load_h_slice<NBLD>(hbuf, (uint32_t)r * f * 4u, lane, nblk, hv);
@@ -623,6 +632,7 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    }
 }
 
 }  // namespace
@@ -630,10 +640,10 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
 template <int NBL>
 hipError_t launch_regx(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                        const int32_t *sorted_rows, const int32_t *plan, float *h, int T, int d,
-                       int E, int k, int f, int amax, hipStream_t s) {
+                       int E, int k, int f, int amax, hipStream_t s, int hstride = 0) {
     dim3 grid(f / kRxPairs, amax);
     (void)timed_launch("gemv_gate_up", gate_up_regx_kernel<NBL>, dim3(grid), dim3(256), (size_t)d * 2 + 16, s, x, w, offsets, sorted_rows, plan, h,
-                                                              T, d, E, k, f);
+                                                              T, d, E, k, f, hstride);
     return hipGetLastError();
 }
 
@@ -658,9 +668,9 @@ hipError_t launch_gemv_gate_up(const uint16_t *x, ExpertArgs w, const int32_t *o
 template <int NBLD>
 hipError_t launch_down_rows(const float *h, ExpertArgs w, const int32_t *offsets,
                             const int32_t *plan, uint16_t *rows_out, int T, int d, int E,
-                            int k, int f, int amax, hipStream_t s) {
+                            int k, int f, int amax, hipStream_t s, int hstride = 0) {
     dim3 grid(d / 64, amax);
-    (void)timed_launch("gemv_down", down_rows_kernel<NBLD>, dim3(grid), dim3(256), 0, s, h, w, offsets, plan, rows_out, T, d, E, k, f);
+    (void)timed_launch("gemv_down", down_rows_kernel<NBLD>, dim3(grid), dim3(256), 0, s, h, w, offsets, plan, rows_out, T, d, E, k, f, hstride);
     return hipGetLastError();
 }
 
@@ -679,6 +689,39 @@ hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets
     (void)timed_launch("gemv_down", gemv_down_kernel, dim3(grid), dim3(256), (size_t)rpp * f * 4, s, h, w, offsets, plan, rows_out, T, d,
                                                             E, k, f, rpp);
     return hipGetLastError();
+}
+
+bool gemv_small_ok(int d, int f) {
+    return f % kRxPairs == 0 && d <= 8192 && (f / 32 + 63) / 64 <= 2;
+}
+
+hipError_t launch_gemv_gate_up_small(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
+                                     const int32_t *sorted_rows, const int32_t *small,
+                                     float *h_small, int T, int d, int E, int k, int f,
+                                     int gemv_max, hipStream_t s) {
+    const int amax = min(E, T * k);
+    if (amax <= 0) return hipSuccess;
+    const int nbl = (d / 32 + 63) / 64;
+    if (nbl == 1)
+        return launch_regx<1>(x, w, offsets, sorted_rows, small, h_small, T, d, E, k, f, amax, s,
+                              gemv_max);
+    if (nbl == 2)
+        return launch_regx<2>(x, w, offsets, sorted_rows, small, h_small, T, d, E, k, f, amax, s,
+                              gemv_max);
+    return launch_regx<4>(x, w, offsets, sorted_rows, small, h_small, T, d, E, k, f, amax, s,
+                          gemv_max);
+}
+
+hipError_t launch_gemv_down_small(const float *h_small, ExpertArgs w, const int32_t *offsets,
+                                  const int32_t *small, uint16_t *rows_out, int T, int d, int E,
+                                  int k, int f, int gemv_max, hipStream_t s) {
+    const int amax = min(E, T * k);
+    if (amax <= 0) return hipSuccess;
+    if ((f / 32 + 63) / 64 == 1)
+        return launch_down_rows<1>(h_small, w, offsets, small, rows_out, T, d, E, k, f, amax, s,
+                                   gemv_max);
+    return launch_down_rows<2>(h_small, w, offsets, small, rows_out, T, d, E, k, f, amax, s,
+                               gemv_max);
 }
 
 bool gate_up_token_fusable(int T, int d, int E, int k, int f) {

@@ -22,6 +22,8 @@
 // MFMA operand layout (16x16x128): lane l holds row (l % 16) of a 16-row
 // tile and K block (l / 16) of the step; the output tile holds
 // C[4 * (l / 16) + i][l % 16] in lane l, register i.
+#include <algorithm>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -216,33 +218,51 @@ __global__ __launch_bounds__(256) void mx_round_kernel(const T *in, uint32_t ite
 // ---------------------------------------------------------------------------
 // Tile plan: per active expert, the number of 128-row tiles and their
 // exclusive prefix.  tiles[0] = total, tiles[1 + a] = prefix of expert a.
+// Experts with at most gemv_max rows get no tiles: they are listed in
+// small[] (small[0] = count, then their ids, ascending) for the GEMV path.
 // ---------------------------------------------------------------------------
 constexpr int kBM = 128;
 
 __global__ __launch_bounds__(1024) void mfma_plan_kernel(const int32_t *__restrict__ offsets,
                                                          const int32_t *__restrict__ plan,
-                                                         int32_t *__restrict__ tiles, int E) {
-    __shared__ int wsum[16];
+                                                         int32_t *__restrict__ tiles,
+                                                         int32_t *__restrict__ small, int E,
+                                                         int gemv_max) {
+    __shared__ int wsum[16], ssum[16];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int nact = plan[0];
-    int c = 0;
+    int c = 0, sm = 0, e = -1;
     if (tid < nact) {
-        const int e = plan[1 + tid];
+        e = plan[1 + tid];
         const int n = ((unsigned)e < (unsigned)E) ? offsets[e + 1] - offsets[e] : 0;
-        c = (n + kBM - 1) / kBM;
+        if (n > gemv_max) c = (n + kBM - 1) / kBM;
+        else if (n > 0) sm = 1;
     }
-    int inc = c;
+    int inc = c, sinc = sm;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += u;
+        const int u = __shfl_up(inc, o, 64), v = __shfl_up(sinc, o, 64);
+        if (lane >= o) {
+            inc += u;
+            sinc += v;
+        }
     }
-    if (lane == 63) wsum[wid] = inc;
+    if (lane == 63) {
+        wsum[wid] = inc;
+        ssum[wid] = sinc;
+    }
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wid; ++w) base += wsum[w];
+    int base = 0, sbase = 0;
+    for (int w = 0; w < wid; ++w) {
+        base += wsum[w];
+        sbase += ssum[w];
+    }
     if (tid < nact) tiles[1 + tid] = base + inc - c;
-    if (tid == 1023) tiles[0] = base + inc;
+    if (small && sm) small[1 + sbase + sinc - 1] = e;
+    if (tid == 1023) {
+        tiles[0] = base + inc;
+        if (small) small[0] = sbase + sinc;
+    }
 }
 
 // Which active expert a global m-tile index belongs to: binary search over
@@ -812,8 +832,8 @@ hipError_t set_lds_attrs() {
 }  // namespace
 
 // The split rows are addressed with 32-bit byte offsets.
-bool mfma_path_ok(int T, int d, int k, int f) {
-    return d % 512 == 0 && f % 256 == 0 && T >= kMfmaMinT &&
+bool mfma_shape_ok(int T, int d, int k, int f) {
+    return d % 512 == 0 && f % 256 == 0 &&
            (double)T * (d / 128) * kStepBytes < 4294967296.0 &&
            (double)T * k * (f / 128) * kStepBytes < 4294967296.0;
 }
@@ -824,6 +844,14 @@ size_t mfma_ws_bytes(int T, int d, int E, int k, int f) {
     const size_t rows = (size_t)T * k;
     return al256(mx_split_bytes(T, d)) + al256(mx_split_bytes((int)rows, f)) +
            al256((size_t)(E + 1) * 4);
+}
+
+size_t mixed_ws_bytes(int T, int d, int E, int k, int f, int gemv_max) {
+    // the scaled-MFMA scratch, the small experts' list and their fp32 h rows
+    const size_t rows = (size_t)T * k;
+    const size_t small_rows = gemv_max > 0 ? std::min(rows, (size_t)E * gemv_max) : 0;
+    return al256(mfma_ws_bytes(T, d, E, k, f)) + al256((size_t)(E + 1) * 4) +
+           al256(small_rows * f * 4);
 }
 
 hipError_t launch_mx_split_bf16(const uint16_t *in, int rows, int K, uint8_t *q, hipStream_t st) {
@@ -858,7 +886,7 @@ hipError_t launch_mx_round_f32(const float *in, int rows, int K, float *out, hip
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                            const int32_t *sorted_rows, const int32_t *plan, uint16_t *rows_out,
                            void *ws, int T, int d, int E, int k, int f, bool single,
-                           hipStream_t s, bool packed) {
+                           hipStream_t s, bool packed, int gemv_max) {
     hipError_t e = set_lds_attrs();
     if (e != hipSuccess) return e;
     const size_t rows = (size_t)T * k;
@@ -868,13 +896,27 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
     uint8_t *hq = reinterpret_cast<uint8_t *>(p);
     p += al256(mx_split_bytes((int)rows, f));
     int32_t *tiles = reinterpret_cast<int32_t *>(p);
+    p += al256((size_t)(E + 1) * 4);
+    // the mixed path's part of the scratch (mixed_ws_bytes)
+    int32_t *small = reinterpret_cast<int32_t *>(p);
+    p += al256((size_t)(E + 1) * 4);
+    float *h_small = reinterpret_cast<float *>(p);
+    const bool mixed = gemv_max > 0;
 
     {
         e = launch_mx_split_bf16(x, T, d, xq, s);
     }
     if (e != hipSuccess) return e;
-    mfma_plan_kernel<<<1, 1024, 0, s>>>(offsets, plan, tiles, E);
+    mfma_plan_kernel<<<1, 1024, 0, s>>>(offsets, plan, tiles, mixed ? small : nullptr, E,
+                                        mixed ? gemv_max : 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // experts with few rows: the grouped GEMVs (weights streamed once per
+    // row), their h rows at small-expert index * gemv_max
+    if (mixed) {
+        e = launch_gemv_gate_up_small(x, w, offsets, sorted_rows, small, h_small, T, d, E, k, f,
+                                      gemv_max, s);
+        if (e != hipSuccess) return e;
+    }
     // upper bound on the m-tiles: one partial tile per expert plus full tiles
     const long long mt_max = min(E, (int)rows) + (long long)((rows + kBM - 1) / kBM);
     {
@@ -885,6 +927,11 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
                            sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f, (int)packed);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (mixed) {
+        e = launch_gemv_down_small(h_small, w, offsets, small, rows_out, T, d, E, k, f,
+                                   gemv_max, s);
+        if (e != hipSuccess) return e;
+    }
     {
         const long long blocks = 8 * ((mt_max * (d / 512) + 7) / 8);
         (void)timed_launch("down_mfma",

@@ -12,6 +12,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -74,19 +75,48 @@ RouteWs route_ws(const moe_dims &D) {
     return w;
 }
 
+// ---- expert path ---------------------------------------------------------------
+// The diagnostic override of the per-expert crossover (-1: the built-in one).
+std::atomic<int> g_gemv_max_override{-1};
+
+// Rows at or below which an expert of a scaled-MFMA call takes the grouped
+// GEMVs (0: every expert on MFMA tiles).  -1 where there is no per-expert
+// choice: the activation-MX mode (whose GEMVs would need a rounded copy of
+// x), the packed store (the GEMVs read the canonical one) and shapes the
+// small-expert GEMVs do not serve.
+int ffn_gemv_max(const moe_dims &D, bool packed) {
+    if (packed || D.act != MOE_ACT_BF16 || !moe::gemv_small_ok(D.d, D.f)) return -1;
+    const int o = g_gemv_max_override.load(std::memory_order_relaxed);
+    return o >= 0 ? o : moe::kGemvMaxRows;
+}
+
+// Whether a call takes the scaled-MFMA expert path (with its small experts
+// on the GEMVs), else the GEMV path for every expert.  The choice is per
+// expert, by its rows: with the crossover R the call goes to the mixed path
+// as soon as some expert could have more than R rows (T > R).  Without a
+// per-expert choice, from kMfmaMinT tokens on.  A few tokens keep the fused
+// down + combine.
+bool use_mfma(const moe_dims &D, bool packed) {
+    if (!moe::mfma_shape_ok(D.T, D.d, D.k, D.f) || D.T <= kFuseMaxT) return false;
+    const int R = ffn_gemv_max(D, packed);
+    return R < 0 ? D.T >= moe::kMfmaMinT : D.T > R;
+}
+
 struct FfnWs {
     size_t plan, h, mfma, xr, total;
 };
-FfnWs ffn_ws(const moe_dims &D) {
+FfnWs ffn_ws(const moe_dims &D, bool packed = false) {
     FfnWs w;
     w.plan = 0;
     w.h = al256((size_t)(D.E + 1) * 4);
     w.mfma = w.h;
     w.xr = w.h;
     // the fp32 h of the GEMV path (and, in the activation-MX mode, the
-    // rounded copy of x); the MFMA path keeps h split in its own ws
-    if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
-        w.total = w.mfma + al256(moe::mfma_ws_bytes(D.T, D.d, D.E, D.k, D.f));
+    // rounded copy of x); the MFMA path keeps h split in its own ws, and the
+    // mixed path its small experts' compact fp32 h
+    if (use_mfma(D, packed)) {
+        w.total = w.mfma + al256(moe::mixed_ws_bytes(D.T, D.d, D.E, D.k, D.f,
+                                                     std::max(0, ffn_gemv_max(D, packed))));
     } else {
         w.xr = w.h + al256((size_t)D.T * D.k * D.f * 4);
         w.total = w.xr + (D.act ? al256((size_t)D.T * D.d * 2) : 0);
@@ -97,7 +127,7 @@ FfnWs ffn_ws(const moe_dims &D) {
 struct LayerWs {
     size_t route, ids, tw, counts, offsets, sorted_rows, row_pos, perm, ffn, rows_out, total;
 };
-LayerWs layer_ws(const moe_dims &D) {
+LayerWs layer_ws(const moe_dims &D, bool packed = false) {
     const size_t rows = (size_t)D.T * D.k;
     LayerWs w;
     size_t p = 0;
@@ -109,7 +139,7 @@ LayerWs layer_ws(const moe_dims &D) {
     w.sorted_rows = p; p += al256(rows * 4);
     w.row_pos = p; p += al256(rows * 4);
     w.perm = p; p += al256(moe::permute_ws_bytes(D.T, D.E));
-    w.ffn = p; p += al256(ffn_ws(D).total);
+    w.ffn = p; p += al256(ffn_ws(D, packed).total);
     w.rows_out = p;
     if (D.T > kFuseMaxT) p += al256(rows * D.d * 2);
     w.total = p;
@@ -256,7 +286,7 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
                      const float *router_bias, const moe_mxfp4_experts &experts, uint16_t *y,
                      int32_t *topk_ids_out, float *topk_w_out, char *base, hipStream_t s,
                      const uint16_t *resid, const float *extra, bool packed = false) {
-    const LayerWs L = layer_ws(D);
+    const LayerWs L = layer_ws(D, packed);
     const RouteWs RW = route_ws(D);
     float *logits = reinterpret_cast<float *>(base + L.route + RW.logits);
     int32_t *ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t *>(base + L.ids);
@@ -266,7 +296,7 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
     int32_t *sorted_rows = reinterpret_cast<int32_t *>(base + L.sorted_rows);
     int32_t *row_pos = reinterpret_cast<int32_t *>(base + L.row_pos);
     void *perm_ws = base + L.perm;
-    const FfnWs F = ffn_ws(D);
+    const FfnWs F = ffn_ws(D, packed);
     int32_t *plan = reinterpret_cast<int32_t *>(base + L.ffn + F.plan);
     float *h = reinterpret_cast<float *>(base + L.ffn + F.h);
     uint16_t *rows_out = reinterpret_cast<uint16_t *>(base + L.rows_out);
@@ -310,12 +340,13 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
                                     D.E, D.k, perm_ws, s);
         }
     }
-    if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
+    if (use_mfma(D, packed)) {
         if (e == hipSuccess) {
             DiagScope t("mfma_ffn", s);
             e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
                                      base + L.ffn + F.mfma, D.T, D.d, D.E, D.k, D.f,
-                                     D.act == MOE_ACT_MX_E2M3, s, packed);
+                                     D.act == MOE_ACT_MX_E2M3, s, packed,
+                                     std::max(0, ffn_gemv_max(D, packed)));
         }
         if (e == hipSuccess) {
             e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s, resid, extra);
@@ -519,12 +550,13 @@ moe_status moe_expert_ffn(const moe_dims *dims, const uint16_t *x,
             DiagScope t("plan", s);
             e = moe::launch_plan(offsets, plan, D.E, s);
         }
-        if (moe::mfma_path_ok(D.T, D.d, D.k, D.f)) {
+        if (use_mfma(D, false)) {
             if (e == hipSuccess) {
                 DiagScope t("mfma_ffn", s);
                 e = moe::launch_mfma_ffn(x, W, offsets, sorted_rows, plan, rows_out,
                                          base + L.mfma, D.T, D.d, D.E, D.k, D.f,
-                                         D.act == MOE_ACT_MX_E2M3, s);
+                                         D.act == MOE_ACT_MX_E2M3, s, false,
+                                         std::max(0, ffn_gemv_max(D, false)));
             }
             return device_status(e);
         }
@@ -645,15 +677,16 @@ moe_status moe_layer_forward_packed(const moe_dims *dims, const uint16_t *x,
         if (st != MOE_OK) return st;
         const moe_dims &D = *dims;
         if (D.T == 0) return MOE_OK;
-        if (!moe::prepack_ok(D.d, D.f) || !moe::mfma_path_ok(D.T, D.d, D.k, D.f))
-            return MOE_ERR_UNSUPPORTED;
+        if (!moe::prepack_ok(D.d, D.f) || !use_mfma(D, true)) return MOE_ERR_UNSUPPORTED;
         if (!x || !router_w || !y) return MOE_ERR_NULL;
         if ((st = check_experts(packed)) != MOE_OK) return st;
         if (!aligned16(x) || !aligned16(router_w) || !aligned16(y)) return MOE_ERR_ALIGN;
-        const LayerWs L = layer_ws(D);
+        // the documented size (moe_workspace_bytes for the canonical store),
+        // which covers the packed call's own layout
         if (!ws) return MOE_ERR_NULL;
         if (!aligned16(ws)) return MOE_ERR_ALIGN;
-        if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+        if (ws_bytes < layer_ws(D).total || ws_bytes < layer_ws(D, true).total)
+            return MOE_ERR_WORKSPACE;
         return device_status(run_layer(D, x, router_w, router_bias, *packed, y, topk_ids_out,
                                        topk_w_out, static_cast<char *>(ws),
                                        static_cast<hipStream_t>(hip_stream), nullptr, nullptr,
@@ -862,6 +895,17 @@ int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint
     } catch (...) {
         return -1;
     }
+}
+
+int moe_diag_set_gemv_max_rows(int rows) {
+    if (rows < -1 || rows > moe::kGemvMaxRowsCap) return -1;
+    g_gemv_max_override.store(rows, std::memory_order_relaxed);
+    return 0;
+}
+
+int moe_diag_gemv_max_rows(void) {
+    const int o = g_gemv_max_override.load(std::memory_order_relaxed);
+    return o >= 0 ? o : moe::kGemvMaxRows;
 }
 
 int moe_diag_time_kernel(const char *kernel, int capacity) {

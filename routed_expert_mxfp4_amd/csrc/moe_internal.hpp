@@ -18,7 +18,14 @@ namespace moe {
 // ---------------------------------------------------------------------------
 constexpr int kMaxExperts = 1024;   // top-k keeps <= 16 logits per lane
 constexpr int kMaxTopK = 32;
-constexpr int kMfmaMinT = 128;      // tokens from which the scaled-MFMA expert path runs
+constexpr int kMfmaMinT = 128;      // tokens from which the activation-MX mode and the
+                                    // packed store take the scaled-MFMA expert path
+// Per-expert path choice of the bf16 (W4A16) layer: in a call on the
+// scaled-MFMA path, experts with at most kGemvMaxRows rows take the grouped
+// GEMVs and the rest the MFMA tiles (the crossover measured on MI355X by
+// bench.py --crossover); a diagnostic override may set 0..kGemvMaxRowsCap.
+constexpr int kGemvMaxRows = 1;
+constexpr int kGemvMaxRowsCap = 16;
 constexpr int kRouteFilterMinT = 256; // tokens from which routing filters on bf16 MFMA logits
 
 // ---------------------------------------------------------------------------
@@ -219,16 +226,30 @@ hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets
 hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
                                const float *topk_w, const int32_t *row_pos, uint16_t *y,
                                int T, int d, int E, int k, int f, hipStream_t s);
-// Prefill expert FFN on scaled MFMA (x and h as two-term MX E2M3, weights
-// as stored; the gate/up pass writes h already split).  Needs d % 512 == 0,
-// f % 256 == 0; ws of mfma_ws_bytes.
-bool mfma_path_ok(int T, int d, int k, int f);
+// The mixed path's small experts (at most gemv_max rows each, listed in
+// small[]: count, then ids): the grouped GEMVs with their fp32 h rows at
+// small-expert index * gemv_max of h_small.  Need gemv_small_ok(d, f).
+bool gemv_small_ok(int d, int f);
+hipError_t launch_gemv_gate_up_small(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
+                                     const int32_t *sorted_rows, const int32_t *small,
+                                     float *h_small, int T, int d, int E, int k, int f,
+                                     int gemv_max, hipStream_t s);
+hipError_t launch_gemv_down_small(const float *h_small, ExpertArgs w, const int32_t *offsets,
+                                  const int32_t *small, uint16_t *rows_out, int T, int d, int E,
+                                  int k, int f, int gemv_max, hipStream_t s);
+// Expert FFN on scaled MFMA (x and h as two-term MX E2M3, weights as
+// stored; the gate/up pass writes h already split).  Needs d % 512 == 0,
+// f % 256 == 0; ws of mfma_ws_bytes, or of mixed_ws_bytes with
+// gemv_max > 0: then the experts with at most gemv_max rows take the
+// grouped GEMVs instead (the per-expert path choice; needs gemv_small_ok).
+bool mfma_shape_ok(int T, int d, int k, int f);
 size_t mfma_ws_bytes(int T, int d, int E, int k, int f);
+size_t mixed_ws_bytes(int T, int d, int E, int k, int f, int gemv_max);
 // single: the activation-MX mode (one matrix pass with the hi terms).
 hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                            const int32_t *sorted_rows, const int32_t *plan, uint16_t *rows_out,
                            void *ws, int T, int d, int E, int k, int f, bool single,
-                           hipStream_t s, bool packed = false);
+                           hipStream_t s, bool packed = false, int gemv_max = 0);
 // The operand-order layout of the MXFP4 store for the scaled-MFMA GEMM (same
 // bytes; needs d % 512 == 0 and f % 512 == 0): dst = prepack(src), dst must
 // not overlap src.

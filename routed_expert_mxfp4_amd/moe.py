@@ -57,7 +57,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_block_workspace_bytes", "moe_rmsnorm", "moe_block_forward",
            "moe_fp8_workspace_bytes", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
            "moe_prepack_experts", "moe_layer_forward_packed", "moe_diag_kernel_times",
-           "moe_layer_forward_noalloc")
+           "moe_layer_forward_noalloc", "moe_diag_set_gemv_max_rows",
+           "moe_diag_gemv_max_rows")
 
 _lib = None
 
@@ -117,6 +118,10 @@ def lib():
         L.moe_diag_kernel_times.restype = I
         L.moe_diag_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_double), I,
                                             ctypes.POINTER(ctypes.c_longlong)]
+        L.moe_diag_set_gemv_max_rows.restype = I
+        L.moe_diag_set_gemv_max_rows.argtypes = [I]
+        L.moe_diag_gemv_max_rows.restype = I
+        L.moe_diag_gemv_max_rows.argtypes = []
         L.moe_diag_kernel_time.restype = I
         L.moe_diag_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_longlong)]
@@ -148,6 +153,17 @@ def diag_kernel_times(cap: int):
     if lib().moe_diag_kernel_times(buf, int(cap), ctypes.byref(n)) != 0:
         raise RuntimeError("moe_diag_kernel_times failed")
     return [buf[i] for i in range(min(cap, n.value))]
+
+
+def diag_set_gemv_max_rows(rows):
+    """Override the per-expert crossover (experts with at most ``rows`` rows
+    take the GEMVs in a scaled-MFMA call); None restores the built-in one."""
+    if lib().moe_diag_set_gemv_max_rows(-1 if rows is None else int(rows)) != 0:
+        raise ValueError("gemv_max_rows must be 0..16 or None")
+
+
+def diag_gemv_max_rows() -> int:
+    return int(lib().moe_diag_gemv_max_rows())
 
 
 def diag_mx_split_e2m3(rows_tensor, stream=None):

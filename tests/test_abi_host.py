@@ -134,10 +134,12 @@ def test_noalloc_refuses_before_any_launch(L):
     M = ctypes.c_void_p(0x10008)
     ex = moe.Experts(0x10000, 0x10000, 0x10000, 0x10000)
     f = L.moe_layer_forward_noalloc
-    # the K3 shape fits the static scratch up to 235 tokens, not at 236
-    fit, over = _dims(T=235, d=7168, E=896, k=16, f=1536), _dims(T=236, d=7168, E=896, k=16, f=1536)
-    assert moe.moe_workspace_bytes(fit, moe.ENTRY_LAYER_FORWARD) <= moe.NOALLOC_SCRATCH_BYTES
-    assert moe.moe_workspace_bytes(over, moe.ENTRY_LAYER_FORWARD) > moe.NOALLOC_SCRATCH_BYTES
+    # the K3 shape: the largest token count whose layer scratch fits, and the next
+    need = [moe.moe_workspace_bytes(_dims(T=t, d=7168, E=896, k=16, f=1536),
+                                    moe.ENTRY_LAYER_FORWARD) for t in range(1, 400)]
+    limit = max(t for t, n in zip(range(1, 400), need) if n <= moe.NOALLOC_SCRATCH_BYTES)
+    assert limit >= 128 and all(n <= moe.NOALLOC_SCRATCH_BYTES for n in need[:limit])
+    over = _dims(T=limit + 1, d=7168, E=896, k=16, f=1536)
     assert f(ctypes.byref(over), A, A, None, ctypes.byref(ex), A, None, None, None) == moe.MOE_ERR_SCRATCH
     big = _dims(T=32768, d=7168, E=896, k=16, f=1536)
     assert f(ctypes.byref(big), A, A, None, ctypes.byref(ex), A, None, None, None) == moe.MOE_ERR_SCRATCH

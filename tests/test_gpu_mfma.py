@@ -179,6 +179,76 @@ def test_mfma_path_small(dev, case):
     _close(_bf16_to_f64(y2), y_o, "layer_forward y")
 
 
+def _skewed_case(T, d, E, k, f, seed):
+    """A layer whose router bias makes a few experts hot and many cold, so
+    that one call holds experts on both sides of the GEMV / MFMA crossover."""
+    cfg = _small_cfg(T, d, E, k, f, seed)
+    L = synth.gen_layer(cfg)
+    bias = torch.zeros(E, dtype=torch.float32)
+    bias[:4] = 0.3                       # hot experts
+    bias[E // 2:] = -0.6                 # cold experts: a few rows or none
+    return cfg, L, bias
+
+
+def test_mixed_path_in_one_call(dev):
+    """Experts with at most the crossover's rows take the GEMVs, the others
+    the MFMA tiles, in the same call; both match the oracle."""
+    moe = _moe()
+    T, d, E, k, f = 160, 512, 32, 4, 256
+    cfg, L, bias = _skewed_case(T, d, E, k, f, 91)
+    x16, wr16 = synth.as_u16(L["x"]), synth.as_u16(L["router_w"])
+    W = _np_experts(L)
+    lg = oracle.router_logits(x16, wr16, bias.numpy())
+    ids_o, w_o = oracle.topk_softmax(lg, k)
+    counts = np.bincount(ids_o.ravel(), minlength=E)
+    R = moe.diag_gemv_max_rows()
+    assert R >= 1
+    assert ((counts >= 1) & (counts <= R)).any() and (counts > R).any(), counts
+    o_rows = _oracle_o_rows(x16, ids_o, W, d, f)
+    y_o = np.einsum("tj,tjd->td", w_o, o_rows)
+    x, wr, bd = L["x"].to(dev), L["router_w"].to(dev), bias.to(dev)
+    ex = _dev_experts(L, dev)
+    launched = {}
+    for kname in ("gemv_gate_up", "gate_up_mfma", "gemv_down", "down_mfma"):
+        moe.diag_time_kernel(kname, capacity=4)
+        y, ids, w = moe.moe_layer_forward(x, wr, ex, k, router_bias=bd, return_routing=True)
+        torch.cuda.synchronize()
+        launched[kname] = moe.diag_kernel_time()[1]
+    moe.diag_time_kernel(None, 0)
+    assert all(n == 1 for n in launched.values()), launched
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_o)
+    _close(_bf16_to_f64(y), y_o, "mixed layer y")
+    ids2, w2 = moe.moe_route(x, wr, k, router_bias=bd)
+    counts_d, offsets, sr, rp = moe.moe_permute(ids2, E)
+    rows_out = moe.moe_expert_ffn(x, ex, offsets, sr, k)
+    torch.cuda.synchronize()
+    _, _, sr_o, _ = oracle.permute(ids_o, E)
+    _close(_bf16_to_f64(rows_out), o_rows.reshape(T * k, d)[sr_o], "mixed rows_out")
+
+
+@pytest.mark.parametrize("override", [0, 1, 16, None])
+def test_crossover_override(dev, override):
+    """Every crossover setting (all MFMA tiles, GEMVs for one-row experts,
+    GEMVs up to 16 rows, the built-in one) gives the oracle's result; T = 48
+    takes the MFMA tiles only through the per-expert choice."""
+    moe = _moe()
+    T, d, E, k, f = 48, 512, 32, 4, 256
+    cfg, L, bias = _skewed_case(T, d, E, k, f, 92)
+    x16, wr16 = synth.as_u16(L["x"]), synth.as_u16(L["router_w"])
+    W = _np_experts(L)
+    lg = oracle.router_logits(x16, wr16, bias.numpy())
+    ids_o, w_o = oracle.topk_softmax(lg, k)
+    y_o = np.einsum("tj,tjd->td", w_o, _oracle_o_rows(x16, ids_o, W, d, f))
+    moe.diag_set_gemv_max_rows(override)
+    try:
+        y = moe.moe_layer_forward(L["x"].to(dev), L["router_w"].to(dev), _dev_experts(L, dev), k,
+                                  router_bias=bias.to(dev))
+        torch.cuda.synchronize()
+    finally:
+        moe.diag_set_gemv_max_rows(None)
+    _close(_bf16_to_f64(y), y_o, "override %s" % override)
+
+
 def test_mfma_path_deterministic(dev):
     moe = _moe()
     cfg = _small_cfg(256, 512, 12, 3, 256, 75)
