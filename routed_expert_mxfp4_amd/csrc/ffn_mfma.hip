@@ -295,10 +295,16 @@ __device__ __forceinline__ int find_expert(const int32_t *tiles, int nact, int m
 // the last step), so the wait counts are constants.
 // ---------------------------------------------------------------------------
 constexpr int kNst = 4;                              // LDS stages
-constexpr int kDmaPerWave = 7;                       // 128 x 13 pieces = 26 wave loads, 28 issued
-constexpr int kStageBytes = 4 * kDmaPerWave * 1024;  // 28672 (26624 used + overflow of the pad loads)
-constexpr int kLdsBytes = kNst * kStageBytes;        // 114688
-static_assert(kBM * kSlotsRow <= 4 * kDmaPerWave * 64, "direct loads must cover the stage");
+// Tile heights: MT m-tiles of 16 rows (MT = 1, 2, 4 or 8).  The A stage of
+// MT * 16 rows x 13 pieces takes DMA(MT) direct loads per wave (4 waves).
+template <int MT>
+struct Tile {
+    static constexpr int kDma = (MT * 16 * kSlotsRow + 255) / 256;   // 1, 2, 4, 7
+    static constexpr int kStageBytes = 4 * kDma * 1024;              // pad loads overflow here
+    static_assert(MT * 16 * kSlotsRow <= 4 * kDma * 64, "direct loads must cover the stage");
+};
+constexpr int kLdsBytes = kNst * Tile<8>::kStageBytes;  // 114688: the 128-row ring, and the
+                                                        // gate/up epilogue's staging
 
 // Global -> LDS direct load of 16 bytes per lane (lane l fills LDS bytes
 // m0 + 16 l).  Written as inline asm so that the compiler's wait-count
@@ -430,15 +436,16 @@ constexpr int kCodeLoads = 16, kScaleLoads = 8;
 //   R = 2: last needed = codes s0 of step kk-2; after: s1 (8), A(kk+2), 8 scales
 //   R = 3: last needed = codes s1 of step kk-3; after: A(kk+1), 8 scales,
 //          A(kk+2), 16 codes
-constexpr int step_top_vmcnt(int R) {
-    return R == 0 ? 8 + kDmaPerWave
-         : R == 1 ? kDmaPerWave + kDmaPerWave + kCodeLoads
-         : R == 2 ? 8 + kDmaPerWave + kScaleLoads
-         : kDmaPerWave + kScaleLoads + kDmaPerWave + kCodeLoads;
+constexpr int step_top_vmcnt(int R, int dma) {
+    return R == 0 ? 8 + dma
+         : R == 1 ? dma + dma + kCodeLoads
+         : R == 2 ? 8 + dma + kScaleLoads
+         : dma + kScaleLoads + dma + kCodeLoads;
 }
-static_assert(step_top_vmcnt(0) == 15 && step_top_vmcnt(1) == 30 && step_top_vmcnt(2) == 23 &&
-                  step_top_vmcnt(3) == 38,
-              "wait counts");
+static_assert(step_top_vmcnt(0, 7) == 15 && step_top_vmcnt(1, 7) == 30 &&
+                  step_top_vmcnt(2, 7) == 23 && step_top_vmcnt(3, 7) == 38 &&
+                  step_top_vmcnt(3, 1) == 26,
+              "wait counts (the largest, 38, fits the 6-bit vmcnt)");
 
 template <int PS>
 __device__ __forceinline__ void issue_codes(BRing &br, const GemmArgs &ga, int j) {
@@ -483,13 +490,14 @@ __device__ __forceinline__ void pack_scales(BRing &br, const GemmArgs &ga) {
     }
 }
 
+template <int MT>
 __device__ __forceinline__ void issue_a(uint32_t lds_addr, const uint8_t *aq,
-                                        const uint32_t (&src)[kDmaPerWave], int nsteps, int j,
+                                        const uint32_t (&src)[Tile<MT>::kDma], int nsteps, int j,
                                         int wid) {
     const uint32_t jj = (uint32_t)min(j, nsteps - 1);
-    const uint32_t stage = lds_addr + (uint32_t)((j & (kNst - 1)) * kStageBytes);
+    const uint32_t stage = lds_addr + (uint32_t)((j & (kNst - 1)) * Tile<MT>::kStageBytes);
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i)
+    for (int i = 0; i < Tile<MT>::kDma; ++i)
         direct16(src[i] + jj * (uint32_t)kStepBytes, aq,
                  (uint32_t)__builtin_amdgcn_readfirstlane((int)(stage + 1024u * (4 * i + wid))));
 }
@@ -511,56 +519,50 @@ __device__ __forceinline__ void mfma_mt(f32x4_t (&acc)[8], const AFrag &a, const
     }
 }
 
+// The MT m-tiles of one K step: m-tile I's fragment is waited for (the
+// next one's five reads may still be in flight), its 8 x (1 or 2) MFMAs
+// issued, and m-tile I + 2's reads queued into the freed fragment.
+template <int I, int MT, int PS, int SUB, bool kSingle>
+__device__ __forceinline__ void mt_chain(f32x4_t (&acc)[MT][8], AFrag (&f)[2], const BRing &br,
+                                         const uint32_t (&bsc)[8], uint32_t a, uint32_t s) {
+    if constexpr (I < MT) {
+        afrag_ready<(I + 1 < MT) ? 5 : 0>(f[I & 1]);
+        mfma_mt<PS, SUB, kSingle>(acc[I], f[I & 1], br, bsc);
+        if constexpr (I + 2 < MT) read_afrag<I + 2>(f[I & 1], a, s);
+        mt_chain<I + 1, MT, PS, SUB, kSingle>(acc, f, br, bsc, a, s);
+    }
+}
+
 // One K step at ring position R = kk % 4: wait for stage kk, queue step
-// kk + 3's activations (and, by R, a code pair or a scale group), then 128
-// MFMAs (A fragments read one m-tile ahead).
-template <int R, bool kSingle>
-__device__ __forceinline__ void gemm_step(f32x4_t (&acc)[8][8], BRing &br, const GemmArgs &ga,
-                                          const uint8_t *aq, const uint32_t (&src)[kDmaPerWave],
+// kk + 3's activations (and, by R, a code pair or a scale group), then
+// MT * 16 (or MT * 8) MFMAs (A fragments read one m-tile ahead).
+template <int R, bool kSingle, int MT>
+__device__ __forceinline__ void gemm_step(f32x4_t (&acc)[MT][8], BRing &br, const GemmArgs &ga,
+                                          const uint8_t *aq,
+                                          const uint32_t (&src)[Tile<MT>::kDma],
                                           uint32_t lds_addr, uint32_t a_lane, uint32_t s_lane,
                                           int kk, int wid, bool live) {
     constexpr int PS = (R >> 1) & 1;        // pair slot of steps kk (and kk ^ 1)
     constexpr int SUB = R & 1;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(step_top_vmcnt(R)));   // see step_top_vmcnt
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(step_top_vmcnt(R, Tile<MT>::kDma)));
     __builtin_amdgcn_s_barrier();                        // everyone's part; stage kk-1 free
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(lds_addr, aq, src, ga.nsteps, kk + 3, wid);
+    issue_a<MT>(lds_addr, aq, src, ga.nsteps, kk + 3, wid);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr ((R & 1) == 0) issue_codes<PS ^ 1>(br, ga, kk + 2);
     if constexpr (R == 1) issue_scales(br, ga, (kk + 3) >> 2);
     if constexpr (R == 0) pack_scales(br, ga);
     __builtin_amdgcn_sched_barrier(0);
     if (!live) return;
-    const uint32_t st = lds_addr + (uint32_t)((kk & (kNst - 1)) * kStageBytes);
+    const uint32_t st = lds_addr + (uint32_t)((kk & (kNst - 1)) * Tile<MT>::kStageBytes);
     const uint32_t a = st + a_lane, s = st + s_lane;
     uint32_t bsc[8];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) bsc[nt] = br.spk[nt] >> (8 * R);
-    AFrag f0, f1;
-    read_afrag<0>(f0, a, s);
-    read_afrag<1>(f1, a, s);
-    afrag_ready<5>(f0);
-    mfma_mt<PS, SUB, kSingle>(acc[0], f0, br, bsc);
-    read_afrag<2>(f0, a, s);
-    afrag_ready<5>(f1);
-    mfma_mt<PS, SUB, kSingle>(acc[1], f1, br, bsc);
-    read_afrag<3>(f1, a, s);
-    afrag_ready<5>(f0);
-    mfma_mt<PS, SUB, kSingle>(acc[2], f0, br, bsc);
-    read_afrag<4>(f0, a, s);
-    afrag_ready<5>(f1);
-    mfma_mt<PS, SUB, kSingle>(acc[3], f1, br, bsc);
-    read_afrag<5>(f1, a, s);
-    afrag_ready<5>(f0);
-    mfma_mt<PS, SUB, kSingle>(acc[4], f0, br, bsc);
-    read_afrag<6>(f0, a, s);
-    afrag_ready<5>(f1);
-    mfma_mt<PS, SUB, kSingle>(acc[5], f1, br, bsc);
-    read_afrag<7>(f1, a, s);
-    afrag_ready<5>(f0);
-    mfma_mt<PS, SUB, kSingle>(acc[6], f0, br, bsc);
-    afrag_ready<0>(f1);
-    mfma_mt<PS, SUB, kSingle>(acc[7], f1, br, bsc);
+    AFrag f[2];
+    read_afrag<0>(f[0], a, s);
+    if constexpr (MT > 1) read_afrag<1>(f[1], a, s);
+    mt_chain<0, MT, PS, SUB, kSingle>(acc, f, br, bsc, a, s);
 }
 
 // The block's tile: which expert, which 128 rows of it, which 512 weight
@@ -601,31 +603,18 @@ __device__ __forceinline__ bool select_tile(const int32_t *tiles, const int32_t 
 // (K % 512 == 0): each code load of a 16-row tile and K step reads 1 KB
 // contiguous, each scale load 256 B, instead of 16 rows x 64 B (16 B); the
 // registers receive the same bytes either way.
-template <bool kGateUp, bool kSingle>
-__global__ __launch_bounds__(256) void ffn_mfma_kernel(
-    const uint8_t *__restrict__ aq, ExpertArgs W, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
-    const int32_t *__restrict__ tiles, uint8_t *__restrict__ hq, uint16_t *__restrict__ rows_out,
-    int T, int d, int E, int k, int f, int packed) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    __shared__ int a_rowidx[kBM];
-    const int nrows = T * k;
-    const int NB = kGateUp ? f / 256 : d / 512;
-    TileSel ts;
-    if (!select_tile(tiles, plan, offsets, E, nrows, NB, ts)) return;
+// MT: the tile's height in 16-row m-tiles, the smallest of 1, 2, 4, 8 that
+// holds its rows, so that an expert with few rows pays matrix work for
+// those rows (rounded up to 16, 32 or 64) rather than for 128.
+template <bool kGateUp, bool kSingle, int MT>
+__device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, const ExpertArgs &W,
+                                          uint8_t *__restrict__ hq,
+                                          uint16_t *__restrict__ rows_out, int d, int f,
+                                          int packed, const TileSel &ts,
+                                          const int *a_rowidx, uint8_t *lds) {
+    constexpr int kDma = Tile<MT>::kDma;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (tid < kBM) {
-        const int r = ts.row0 + min(ts.m0 + tid, ts.ne - 1);
-        if (kGateUp) {
-            const int row = sorted_rows[r];
-            a_rowidx[tid] = (unsigned)row < (unsigned)nrows ? row / k : 0;
-        } else {
-            a_rowidx[tid] = r;                      // h rows are expert-major
-        }
-    }
-    __syncthreads();
-
     const int K = kGateUp ? d : f;
     GemmArgs ga;
     ga.nsteps = K >> 7;
@@ -652,21 +641,22 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     ga.cstep = packed ? 1024u : 64u;
     ga.sgrp = packed ? 256u : 16u;
     ga.psel01 = (uint32_t)g | ((4u + (uint32_t)g) << 8);
-    uint32_t src[kDmaPerWave];                      // byte offsets into aq (< 4 GiB)
+    uint32_t src[kDma];                             // byte offsets into aq (< 4 GiB)
+    constexpr int kRows = MT * 16;
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
+    for (int i = 0; i < kDma; ++i) {
         const int sl = 64 * (4 * i + wid) + lane;
-        const int r = sl < kBM * kSlotsRow ? sl / kSlotsRow : kBM - 1;
-        const int pc = sl < kBM * kSlotsRow ? sl - r * kSlotsRow : kSlotsRow - 1;
+        const int r = sl < kRows * kSlotsRow ? sl / kSlotsRow : kRows - 1;
+        const int pc = sl < kRows * kSlotsRow ? sl - r * kSlotsRow : kSlotsRow - 1;
         src[i] = (uint32_t)a_rowidx[r] * a_row_bytes + 16u * pc;
     }
     const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
     const uint32_t a_lane = (uint32_t)(r16 * kStepBytes + 48 * g);
     const uint32_t s_lane = (uint32_t)(r16 * kStepBytes + 192 + 2 * g);
 
-    f32x4_t acc[8][8];
+    f32x4_t acc[MT][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -674,27 +664,27 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     // (ring positions 1, 2, 3): A(0) + scale group 0, A(1) + codes of steps
     // 0 and 1, A(2)
     BRing br = {};
-    issue_a(lds_addr, aq, src, ga.nsteps, 0, wid);
+    issue_a<MT>(lds_addr, aq, src, ga.nsteps, 0, wid);
     __builtin_amdgcn_sched_barrier(0);
     issue_scales(br, ga, 0);
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(lds_addr, aq, src, ga.nsteps, 1, wid);
+    issue_a<MT>(lds_addr, aq, src, ga.nsteps, 1, wid);
     __builtin_amdgcn_sched_barrier(0);
     issue_codes<0>(br, ga, 0);
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(lds_addr, aq, src, ga.nsteps, 2, wid);
+    issue_a<MT>(lds_addr, aq, src, ga.nsteps, 2, wid);
     __builtin_amdgcn_sched_barrier(0);
     // four steps per turn of the register ring and no branch around any
     // load, wait or barrier (a step past the end only skips its MFMAs), so
     // the wait counts the compiler derives at the loop header are exact
     for (int kk = 0; kk < ga.nsteps; kk += 4) {
-        gemm_step<0, kSingle>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk, wid, true);
-        gemm_step<1, kSingle>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 1, wid,
-                     kk + 1 < ga.nsteps);
-        gemm_step<2, kSingle>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 2, wid,
-                     kk + 2 < ga.nsteps);
-        gemm_step<3, kSingle>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 3, wid,
-                     kk + 3 < ga.nsteps);
+        gemm_step<0, kSingle, MT>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk, wid, true);
+        gemm_step<1, kSingle, MT>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 1, wid,
+                                  kk + 1 < ga.nsteps);
+        gemm_step<2, kSingle, MT>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 2, wid,
+                                  kk + 2 < ga.nsteps);
+        gemm_step<3, kSingle, MT>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 3, wid,
+                                  kk + 3 < ga.nsteps);
     }
     // drain the trailing (re-)loads before their registers or the block's
     // LDS can be reused
@@ -704,10 +694,11 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
     // epilogue: lane holds rows 4 (l / 16) + i, column l % 16 of each tile
     if (kGateUp) {
         // h = silu(gate) * up goes through LDS (the A ring is idle now) in
-        // two halves of 64 rows, then is split one 32-element block per
+        // passes of up to 64 rows, then is split one 32-element block per
         // lane: the wave's 64 h columns hc0 .. hc0 + 63 are MX blocks gb0,
         // gb0 + 1 of down step hc0 / 128
         constexpr int kHs = 68;                          // floats per staged row
+        constexpr int kPassMt = MT < 4 ? MT : 4;         // m-tiles per pass
         float *hs = reinterpret_cast<float *>(lds) + wid * 64 * kHs;
         const int hc0 = ts.nb * 256 + 64 * wid;
         const uint32_t hq_row = (uint32_t)(f >> 7) * kStepBytes;
@@ -715,27 +706,28 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
         const int gb0 = (hc0 & 127) >> 5;
         __syncthreads();                                 // every wave is done with the ring
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
+        for (int pass = 0; pass < MT / kPassMt; ++pass) {
             const int left = ts.ne - ts.m0 - 64 * pass;   // rows of the tile from this pass on
             if (left <= 0) break;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < kPassMt; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int nt = 0; nt < 4; ++nt) {
-                        const float gv = acc[4 * pass + m][nt][i], uv = acc[4 * pass + m][nt + 4][i];
+                        const float gv = acc[kPassMt * pass + m][nt][i];
+                        const float uv = acc[kPassMt * pass + m][nt + 4][i];
                         hs[(16 * m + 4 * g + i) * kHs + 16 * nt + r16] = gv / (1.0f + expf(-gv)) * uv;
                     }
             __syncthreads();
             // buffer stores drop offsets past the pass's live rows
-            const uint32_t live_bytes = (uint32_t)min(left, 64) * hq_row;
+            const uint32_t live_bytes = (uint32_t)min(left, 16 * kPassMt) * hq_row;
             const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
                 hq_step + (size_t)(ts.row0 + ts.m0 + 64 * pass) * hq_row, 0, (int)live_bytes,
                 0x00020000);
 #pragma unroll
             for (int it = 0; it < 2; ++it) {
-                if (it == 1 && left <= 32) break;
+                if (it == 1 && (kPassMt < 4 || left <= 32)) break;
                 const int item = 64 * it + lane, rl = item >> 1, blk = gb0 + (item & 1);
                 float v[32];
                 const float *src = hs + rl * kHs + 32 * (item & 1);
@@ -759,7 +751,7 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
         }
     } else {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = ts.m0 + mt * 16 + 4 * g + i;
@@ -770,6 +762,43 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
                 }
             }
     }
+}
+
+// One block per (m-tile, n-block) unit of the tile plan; the tile's height
+// is chosen from its rows (block-uniform, so the branch below and every
+// barrier inside gemm_tile are taken by the whole block).
+template <bool kGateUp, bool kSingle>
+__global__ __launch_bounds__(256) void ffn_mfma_kernel(
+    const uint8_t *__restrict__ aq, ExpertArgs W, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
+    const int32_t *__restrict__ tiles, uint8_t *__restrict__ hq, uint16_t *__restrict__ rows_out,
+    int T, int d, int E, int k, int f, int packed) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ int a_rowidx[kBM];
+    const int nrows = T * k;
+    const int NB = kGateUp ? f / 256 : d / 512;
+    TileSel ts;
+    if (!select_tile(tiles, plan, offsets, E, nrows, NB, ts)) return;
+    const int tid = threadIdx.x;
+    if (tid < kBM) {
+        const int r = ts.row0 + min(ts.m0 + tid, ts.ne - 1);
+        if (kGateUp) {
+            const int row = sorted_rows[r];
+            a_rowidx[tid] = (unsigned)row < (unsigned)nrows ? row / k : 0;
+        } else {
+            a_rowidx[tid] = r;                      // h rows are expert-major
+        }
+    }
+    __syncthreads();
+    const int rows = __builtin_amdgcn_readfirstlane(min(kBM, ts.ne - ts.m0));
+    if (rows <= 16)
+        gemm_tile<kGateUp, kSingle, 1>(aq, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
+    else if (rows <= 32)
+        gemm_tile<kGateUp, kSingle, 2>(aq, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
+    else if (rows <= 64)
+        gemm_tile<kGateUp, kSingle, 4>(aq, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
+    else
+        gemm_tile<kGateUp, kSingle, 8>(aq, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
 }
 
 // The operand-order ("packed") layout of one MXFP4 matrix [rows][K] per

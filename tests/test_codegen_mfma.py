@@ -46,7 +46,9 @@ def _kernels(asm):
     return out
 
 
-def _analyse(lines):
+def _loops(lines):
+    """Every loop holding MFMAs, as (blocks, all blocks) -- one per tile
+    height the kernel dispatches to."""
     blocks, cur = [], None
     for line in lines:
         m = re.match(r"^(\.LBB\d+_\d+):(.*)$", line)
@@ -62,8 +64,16 @@ def _analyse(lines):
         lp = [b for b in blocks if b is hb or ("Header=" + h) in b[1]]
         if any(x.startswith("v_mfma") for b in lp for x in b[2]):
             loops.append(lp)
-    assert len(loops) == 1, "expected one MFMA loop, found %d" % len(loops)
-    loop = loops[0]
+    return loops, blocks
+
+
+def _analyse_all(lines):
+    loops, blocks = _loops(lines)
+    assert len(loops) == 4, "expected one MFMA loop per tile height, found %d" % len(loops)
+    return [_analyse_loop(lp, blocks) for lp in loops]
+
+
+def _analyse_loop(loop, blocks):
     names = {b[0] for b in loop}
     body = [x for b in loop for x in b[2]]
     copies = [x for x in body if re.match(r"(v_mov_b32|v_accvgpr_\w+|scratch_\w+)\b", x)]
@@ -121,19 +131,19 @@ def test_all_gemm_kernels_present(gemm_asm):
 
 
 @pytest.mark.parametrize("which", KERNELS, ids=KERNEL_IDS)
-def test_main_loop_has_no_register_copies(gemm_asm, which):
+def test_main_loops_have_no_register_copies(gemm_asm, which):
     (lines,) = [v for k, v in _kernels(gemm_asm).items() if which in k]
-    body, copies, dests, _ = _analyse(lines)
-    assert sum(x.startswith("v_mfma") for x in body) > 0
-    assert len(dests) >= 128, "weight ring registers not found"
-    assert copies == [], copies[:5]
+    for body, copies, dests, _ in _analyse_all(lines):
+        assert sum(x.startswith("v_mfma") for x in body) > 0
+        assert len(dests) >= 128, "weight ring registers not found"
+        assert copies == [], copies[:5]
 
 
 @pytest.mark.parametrize("which", KERNELS, ids=KERNEL_IDS)
 def test_in_flight_registers_untouched_until_drained(gemm_asm, which):
     (lines,) = [v for k, v in _kernels(gemm_asm).items() if which in k]
-    _, _, _, clobbers = _analyse(lines)
-    assert clobbers == [], clobbers[:5]
+    for _, _, _, clobbers in _analyse_all(lines):
+        assert clobbers == [], clobbers[:5]
 
 
 def test_fp6_conversions_do_not_overlap_their_sources(gemm_asm):

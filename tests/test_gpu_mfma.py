@@ -249,6 +249,41 @@ def test_crossover_override(dev, override):
     _close(_bf16_to_f64(y), y_o, "override %s" % override)
 
 
+def test_tile_heights_at_their_edges(dev):
+    """Experts with 16, 17, 32, 33, 64, 65, 128 and 129 rows: tiles of 1, 2,
+    2, 4, 4, 8, 8 and 8 + 1 m-tiles of 16 rows (the smallest height that
+    holds a tile's rows), against the oracle row by row."""
+    moe = _moe()
+    n_e = [16, 17, 32, 33, 64, 65, 128, 129]
+    E, k, d, f = len(n_e), 1, 512, 256
+    T = sum(n_e)
+    cfg = _small_cfg(T, d, E, k, f, 93)
+    L = synth.gen_layer(cfg)
+    # token t goes to the expert whose row range holds t (one slot per token)
+    ids_np = np.repeat(np.arange(E, dtype=np.int32), n_e).reshape(T, 1)
+    ids_np = ids_np[np.random.default_rng(93).permutation(T)]
+    _, off_o, sr_o, _ = oracle.permute(ids_np, E)
+    x16 = synth.as_u16(L["x"])
+    W = _np_experts(L)
+    o = np.zeros((T, d))
+    for p, r in enumerate(sr_o):
+        e = ids_np[r, 0]
+        o[p] = oracle.expert_row(x16[r], W["gu_codes"][e], W["gu_scales"][e], W["dn_codes"][e],
+                                 W["dn_scales"][e], d, f)[1]
+    moe.diag_set_gemv_max_rows(0)                  # every expert on MFMA tiles
+    try:
+        counts, offsets, sr, rp = moe.moe_permute(torch.from_numpy(ids_np).to(dev), E)
+        rows = moe.moe_expert_ffn(L["x"].to(dev), _dev_experts(L, dev), offsets, sr, k)
+        torch.cuda.synchronize()
+    finally:
+        moe.diag_set_gemv_max_rows(None)
+    np.testing.assert_array_equal(counts.cpu().numpy(), n_e)
+    got = _bf16_to_f64(rows)
+    for e in range(E):
+        lo, hi = off_o[e], off_o[e + 1]
+        _close(got[lo:hi], o[lo:hi], "expert with %d rows" % n_e[e])
+
+
 def test_mfma_path_deterministic(dev):
     moe = _moe()
     cfg = _small_cfg(256, 512, 12, 3, 256, 75)
