@@ -278,51 +278,70 @@ __device__ __forceinline__ int find_expert(const int32_t *tiles, int nact, int m
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM block: 128 rows of one expert x 512 weight rows (gate/up:
-// 256 gate + the matching 256 up rows; down: 512 output columns), K in steps
-// of 128.  Four waves, one per SIMD, each owning all 128 rows x 128 weight
-// rows: 8 x 8 MFMA tiles, 256 fp32 accumulators, two MFMAs (hi, lo) per
-// tile and step.
+// Grouped GEMM block: one tile of an expert's rows -- MT m-tiles of 16 rows,
+// MT = 1, 2, 4 or 8, the smallest that holds them -- times 512 weight rows
+// (gate/up: 256 gate rows and the matching 256 up rows; down: 512 output
+// columns), K in steps of 128.  Eight waves, two per SIMD, so that while
+// one wave waits for a barrier or for its loads to issue, the other keeps
+// the matrix core busy.  A tile of 128 rows puts the waves on 2 x 4 parts
+// of 64 rows x 128 weight rows (4 x 8 MFMA tiles, 128 accumulators); a
+// shorter tile on 1 x 8 parts of all its rows x 64 weight rows.  Two MFMAs
+// (hi, lo terms) per tile and step, one in the activation-MX mode.
 //
-// Data movement per step:
-//   A (split activations, shared by the four waves): global -> LDS direct
-//     loads into a ring of kNst stages, issued kNst - 1 steps ahead; each
-//     wave waits for its own loads (vmcnt) and a barrier publishes them.
-//     Fragment reads are explicit ds_read instructions so that the next
-//     stages' loads stay in flight while a stage is read.
-//   B (weights, private to a wave): global -> registers (see BRing).
-// Every step issues the same number of loads (steps past the end re-load
-// the last step), so the wait counts are constants.
+// Data movement: every operand goes global -> LDS with buffer loads that
+// write LDS directly (lane l's 16 bytes to m0 + 16 l; bytes past a
+// buffer's end read as zero), shared by the eight waves:
+//   A  (split activations) MT x 16 rows x 208 B per step;
+//   B  (weight codes) 32 operand tiles of 1 KB per step: tile t's lane l
+//      holds row 16 t' + l % 16, K block l / 16 of the step, the MFMA's B
+//      operand layout, so a fragment read is 16 contiguous bytes per lane;
+//   scales of 4 steps at once, 256 B per operand tile (row r's 16 bytes at
+//      16 r).
+// Two LDS stages (and two scale groups) alternate: at the top of step kk
+// each wave waits for its own loads (vmcnt(0): only step kk's are
+// outstanding), a barrier publishes every wave's, then step kk + 1's loads
+// are issued into the other stage -- free, since every wave is past step
+// kk - 1 -- and step kk's fragments are read and multiplied.
 // ---------------------------------------------------------------------------
-constexpr int kNst = 4;                              // LDS stages
-// Tile heights: MT m-tiles of 16 rows (MT = 1, 2, 4 or 8).  The A stage of
-// MT * 16 rows x 13 pieces takes DMA(MT) direct loads per wave (4 waves).
+constexpr int kWaves = 8;
+constexpr int kAStageBytes = kBM * kStepBytes;              // 26624: a 128-row tile's step
+constexpr int kBStageBytes = 32 * 1024;                     // 32 operand tiles of 1 KB
+constexpr int kStageBytes = kAStageBytes + kBStageBytes;    // 59392
+constexpr int kSGroupBytes = 32 * 256;                      // scales of 4 steps, 32 tiles
+constexpr int kLdsBytes = 2 * kStageBytes + 2 * kSGroupBytes;   // 135168 of 160 KB
+
 template <int MT>
 struct Tile {
-    static constexpr int kDma = (MT * 16 * kSlotsRow + 255) / 256;   // 1, 2, 4, 7
-    static constexpr int kStageBytes = 4 * kDma * 1024;              // pad loads overflow here
-    static_assert(MT * 16 * kSlotsRow <= 4 * kDma * 64, "direct loads must cover the stage");
+    static constexpr int kMtw = MT == 8 ? 4 : MT;           // m-tiles per wave
+    static constexpr int kNtw = MT == 8 ? 8 : 4;            // operand tiles (16 cols) per wave
+    static constexpr int kALoads = (MT * 16 * kSlotsRow + 63) / 64;   // 26, 13, 7, 4 wave loads
+    static_assert(kALoads <= 4 * kWaves, "four A loads per wave at most");
+    static_assert(kALoads * 1024 <= kAStageBytes, "A loads stay in the A stage");
 };
-constexpr int kLdsBytes = kNst * Tile<8>::kStageBytes;  // 114688: the 128-row ring, and the
-                                                        // gate/up epilogue's staging
 
-// Global -> LDS direct load of 16 bytes per lane (lane l fills LDS bytes
-// m0 + 16 l).  Written as inline asm so that the compiler's wait-count
-// bookkeeping sees only the weight loads (all of one kind, hence exact
-// waits); the direct loads are waited for explicitly with vmcnt.  m0 holds
-// nothing else in these kernels (no other direct loads, GWS or messages).
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void direct16(uint32_t voff, const uint8_t *sbase, uint32_t lds_addr) {
+// Buffer load of 16 bytes per lane straight into LDS (lane l's bytes at
+// lds_addr + 16 l); lds_addr is wave-uniform.  Inline asm: the compiler does
+// not see these loads, and waits for them only where this file says
+// (vmcnt(0) at the top of a step, or before the epilogue reuses the LDS).
+// m0 holds nothing else in these kernels.
+__device__ __forceinline__ void lds_load16(brsrc_t r, uint32_t voff, uint32_t lds_addr) {
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
+        "buffer_load_dwordx4 %0, %1, 0 offen lds"
         :
-        : "v"(voff), "s"(sbase), "s"(lds_addr)
+        : "v"(voff), "s"(r), "s"(lds_addr)
         : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+__device__ __forceinline__ brsrc_t rsrc_of(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
 
 // s_waitcnt immediate: vmcnt(n), expcnt and lgkmcnt left free.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -374,195 +393,34 @@ __device__ __forceinline__ void afrag_ready(AFrag &f) {
     asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(f.hi), "+v"(f.lo), "+v"(f.sc) : "n"(N));
 }
 
-// Weight loads.  Codes: the 64 bytes a step needs from a row are half of a
-// 128-byte line, so steps are loaded in pairs (2p, 2p+1), first all tiles'
-// step 2p then all tiles' step 2p+1 (the second touch of each line hits the
-// L1), into a ring of two pair slots; pair p is issued at step 2p - 2.
-// Scales: one 16-byte load per row covers four steps (4 blocks each); group
-// G (steps 4G..4G+3) is issued at step 4G - 3 and each lane keeps its four
-// bytes (block g of each step) packed in one register.
-//
-// Like the direct loads, these are inline asm, waited for by the one
-// explicit vmcnt at the top of each step.  The destinations are tied
-// ("+v"): a ring slot keeps one register for its whole life, so no copy of
-// a register whose load is still in flight can exist (a codegen test checks
-// that the main loop holds no vector register copies).
-struct BRing {
-    u32x4_t q[2][2][8];         // [pair slot][step in pair][tile]
-    u32x4_t sraw[8];            // scale group in flight
-    uint32_t spk[8];            // current group, this lane's byte per step
+// B fragment of operand tile t in a stage: 16 bytes per lane, then the
+// lane's E8M0 byte of the step from the scale group.
+__device__ __forceinline__ u32x4_t ds_read128_at(uint32_t a) {
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+__device__ __forceinline__ uint32_t ds_read_u8_at(uint32_t a) {
+    uint32_t v;
+    asm volatile("ds_read_u8 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+}
+
+template <int N>
+struct BFrags {
+    u32x4_t q[N];
+    uint32_t sc[N];
 };
 
-struct GemmArgs {
-    i32x4_t bq, bs;             // buffer resources: this expert's codes / scales
-    uint32_t boff, soff;        // this lane's offsets in its first B tile (codes, scales)
-    uint32_t tq[8], ts[8];      // wave-uniform offsets of the 8 B tiles (codes, scales)
-    uint32_t psel01;            // v_perm selector: byte g of two dwords
-    uint32_t cstep, sgrp;       // bytes from one K step's codes to the next, one scale group's
-    int nsteps;
-};
-
-// A raw buffer resource (base, byte size) in scalar registers.
-__device__ __forceinline__ i32x4_t buffer_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    i32x4_t r;
-    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
-    r.z = __builtin_amdgcn_readfirstlane((int)bytes);
-    r.w = 0x00020000;
-    return r;
-}
-
-__device__ __forceinline__ void buf_load16_async(u32x4_t &dst, const i32x4_t &rsrc, uint32_t voff,
-                                                 uint32_t soff) {
-    asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
-                 : "+v"(dst)
-                 : "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory");
-}
-
-// Vector memory instructions issued at a step with ring position R (= the
-// step index mod 4), in this order: 7 direct loads; at even R 16 code loads
-// (8 of the pair's first step, then 8 of its second); at R == 1 8 scale
-// loads.
-constexpr int kCodeLoads = 16, kScaleLoads = 8;
-// The one wait at the top of step kk (ring position R): what must have
-// landed is this wave's part of stage kk (issued at step kk - 3), the codes
-// of step kk (issued at step kk - 2 for even R, kk - 3 for odd R) and, at
-// R == 0, the scale group (issued at step kk - 3).  The count is the number
-// of loads issued after the last of those.
-//   R = 0: last needed = codes s0 of step kk-2; after it: s1 (8), A(kk+2)
-//   R = 1: last needed = codes s1 of step kk-3; after: A(kk+1), A(kk+2), 16 codes
-//   R = 2: last needed = codes s0 of step kk-2; after: s1 (8), A(kk+2), 8 scales
-//   R = 3: last needed = codes s1 of step kk-3; after: A(kk+1), 8 scales,
-//          A(kk+2), 16 codes
-constexpr int step_top_vmcnt(int R, int dma) {
-    return R == 0 ? 8 + dma
-         : R == 1 ? dma + dma + kCodeLoads
-         : R == 2 ? 8 + dma + kScaleLoads
-         : dma + kScaleLoads + dma + kCodeLoads;
-}
-static_assert(step_top_vmcnt(0, 7) == 15 && step_top_vmcnt(1, 7) == 30 &&
-                  step_top_vmcnt(2, 7) == 23 && step_top_vmcnt(3, 7) == 38 &&
-                  step_top_vmcnt(3, 1) == 26,
-              "wait counts (the largest, 38, fits the 6-bit vmcnt)");
-
-template <int PS>
-__device__ __forceinline__ void issue_codes(BRing &br, const GemmArgs &ga, int j) {
-    const uint32_t j0 = (uint32_t)min(j, ga.nsteps - 1), j1 = (uint32_t)min(j + 1, ga.nsteps - 1);
+// Waits until at most PEND LDS reads of the wave are outstanding (those
+// issued after the B fragments'); each fragment register is then tied to
+// that point (the empty asm statements stay after the wait), so no use is
+// scheduled before it.
+template <int N, int PEND>
+__device__ __forceinline__ void bfrags_ready(BFrags<N> &b) {
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(PEND) : "memory");
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.q[PS][0][nt], ga.bq, ga.boff, ga.tq[nt] + j0 * ga.cstep);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.q[PS][1][nt], ga.bq, ga.boff, ga.tq[nt] + j1 * ga.cstep);
-}
-
-__device__ __forceinline__ void issue_scales(BRing &br, const GemmArgs &ga, int G) {
-    const uint32_t gg = (uint32_t)min(G, (ga.nsteps - 1) >> 2);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) buf_load16_async(br.sraw[nt], ga.bs, ga.soff, ga.ts[nt] + gg * ga.sgrp);
-}
-
-// After the last step some weight loads (the clamped re-loads past the end)
-// may still be in flight into ring registers the compiler no longer needs.
-// Waiting for them, then naming every ring register in an asm statement,
-// keeps those registers from being reused before the data has landed.
-__device__ __forceinline__ void drain_weight_loads(BRing &br) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-            asm volatile("" ::"v"(br.q[ps][sub][0]), "v"(br.q[ps][sub][1]), "v"(br.q[ps][sub][2]),
-                         "v"(br.q[ps][sub][3]), "v"(br.q[ps][sub][4]), "v"(br.q[ps][sub][5]),
-                         "v"(br.q[ps][sub][6]), "v"(br.q[ps][sub][7]));
-    asm volatile("" ::"v"(br.sraw[0]), "v"(br.sraw[1]), "v"(br.sraw[2]), "v"(br.sraw[3]),
-                 "v"(br.sraw[4]), "v"(br.sraw[5]), "v"(br.sraw[6]), "v"(br.sraw[7]));
-}
-
-// spk byte i = byte g of dword i of the group's 16 bytes.
-__device__ __forceinline__ void pack_scales(BRing &br, const GemmArgs &ga) {
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        const u32x4_t r = br.sraw[nt];
-        const uint32_t t01 = __builtin_amdgcn_perm(r.y, r.x, ga.psel01);
-        const uint32_t t23 = __builtin_amdgcn_perm(r.w, r.z, ga.psel01);
-        br.spk[nt] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
-    }
-}
-
-template <int MT>
-__device__ __forceinline__ void issue_a(uint32_t lds_addr, const uint8_t *aq,
-                                        const uint32_t (&src)[Tile<MT>::kDma], int nsteps, int j,
-                                        int wid) {
-    const uint32_t jj = (uint32_t)min(j, nsteps - 1);
-    const uint32_t stage = lds_addr + (uint32_t)((j & (kNst - 1)) * Tile<MT>::kStageBytes);
-#pragma unroll
-    for (int i = 0; i < Tile<MT>::kDma; ++i)
-        direct16(src[i] + jj * (uint32_t)kStepBytes, aq,
-                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(stage + 1024u * (4 * i + wid))));
-}
-
-// The scale operand reads byte 0 of the register (bits above are ignored).
-// kSingle: the activation-MX mode, the hi term alone.
-template <int PS, int SUB, bool kSingle>
-__device__ __forceinline__ void mfma_mt(f32x4_t (&acc)[8], const AFrag &a, const BRing &br,
-                                        const uint32_t (&bsc)[8]) {
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        const u32x4_t q = br.q[PS][SUB][nt];
-        const i32x8_t b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
-        acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.hi, b, acc[nt], 2, 4, 0,
-                                                                   (int)a.sc, 0, (int)bsc[nt]);
-        if constexpr (!kSingle)
-            acc[nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.lo, b, acc[nt], 2, 4, 1,
-                                                                       (int)a.sc, 0, (int)bsc[nt]);
-    }
-}
-
-// The MT m-tiles of one K step: m-tile I's fragment is waited for (the
-// next one's five reads may still be in flight), its 8 x (1 or 2) MFMAs
-// issued, and m-tile I + 2's reads queued into the freed fragment.
-template <int I, int MT, int PS, int SUB, bool kSingle>
-__device__ __forceinline__ void mt_chain(f32x4_t (&acc)[MT][8], AFrag (&f)[2], const BRing &br,
-                                         const uint32_t (&bsc)[8], uint32_t a, uint32_t s) {
-    if constexpr (I < MT) {
-        afrag_ready<(I + 1 < MT) ? 5 : 0>(f[I & 1]);
-        mfma_mt<PS, SUB, kSingle>(acc[I], f[I & 1], br, bsc);
-        if constexpr (I + 2 < MT) read_afrag<I + 2>(f[I & 1], a, s);
-        mt_chain<I + 1, MT, PS, SUB, kSingle>(acc, f, br, bsc, a, s);
-    }
-}
-
-// One K step at ring position R = kk % 4: wait for stage kk, queue step
-// kk + 3's activations (and, by R, a code pair or a scale group), then
-// MT * 16 (or MT * 8) MFMAs (A fragments read one m-tile ahead).
-template <int R, bool kSingle, int MT>
-__device__ __forceinline__ void gemm_step(f32x4_t (&acc)[MT][8], BRing &br, const GemmArgs &ga,
-                                          const uint8_t *aq,
-                                          const uint32_t (&src)[Tile<MT>::kDma],
-                                          uint32_t lds_addr, uint32_t a_lane, uint32_t s_lane,
-                                          int kk, int wid, bool live) {
-    constexpr int PS = (R >> 1) & 1;        // pair slot of steps kk (and kk ^ 1)
-    constexpr int SUB = R & 1;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(step_top_vmcnt(R, Tile<MT>::kDma)));
-    __builtin_amdgcn_s_barrier();                        // everyone's part; stage kk-1 free
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a<MT>(lds_addr, aq, src, ga.nsteps, kk + 3, wid);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr ((R & 1) == 0) issue_codes<PS ^ 1>(br, ga, kk + 2);
-    if constexpr (R == 1) issue_scales(br, ga, (kk + 3) >> 2);
-    if constexpr (R == 0) pack_scales(br, ga);
-    __builtin_amdgcn_sched_barrier(0);
-    if (!live) return;
-    const uint32_t st = lds_addr + (uint32_t)((kk & (kNst - 1)) * Tile<MT>::kStageBytes);
-    const uint32_t a = st + a_lane, s = st + s_lane;
-    uint32_t bsc[8];
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) bsc[nt] = br.spk[nt] >> (8 * R);
-    AFrag f[2];
-    read_afrag<0>(f[0], a, s);
-    if constexpr (MT > 1) read_afrag<1>(f[1], a, s);
-    mt_chain<0, MT, PS, SUB, kSingle>(acc, f, br, bsc, a, s);
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(b.q[i]), "+v"(b.sc[i]));
 }
 
 // The block's tile: which expert, which 128 rows of it, which 512 weight
@@ -596,169 +454,246 @@ __device__ __forceinline__ bool select_tile(const int32_t *tiles, const int32_t 
     return true;
 }
 
+// The per-block constants of a tile: where this lane's A pieces, B tiles
+// and scale rows come from, and the buffer resources.
+struct Plan8 {
+    brsrc_t ra, rb, rs;              // split activations, weight codes, weight scales
+    uint32_t a_src[4];               // this lane's A piece offsets (step 0)
+    uint32_t b_src[4];               // this lane's offsets in its 4 B loads (step 0)
+    uint32_t s_src;                  // this lane's scale row offset (group 0)
+    uint32_t cstep, sgrp;            // bytes from one step's codes to the next, one group's scales
+    int nsteps, n_a;                 // K steps; A loads of this wave
+};
+
+// First weight row of operand tile t (16 rows) of the block's 512.
+// Gate/up: the tiles a wave multiplies are half gate, half up, the up tile
+// j + n/2 matching gate tile j, so that the SwiGLU is local to the wave.
+template <bool kGateUp, int MT>
+__device__ __forceinline__ int tile_row(int t, int nb, int f) {
+    if (!kGateUp) return nb * 512 + 16 * t;
+    constexpr int kNtw = Tile<MT>::kNtw, kPer = kNtw / 2;
+    const int owner = t / kNtw, j = t - owner * kNtw;
+    const int col = nb * 256 + owner * 16 * kPer + 16 * (j < kPer ? j : j - kPer);
+    return j < kPer ? col : f + col;
+}
+
+template <bool kGateUp, int MT>
+__device__ __forceinline__ void plan8(Plan8 &P, const uint8_t *aq, uint32_t a_bytes,
+                                      const ExpertArgs &W, int d, int f, int packed,
+                                      const TileSel &ts, const int *a_rowidx, int wid,
+                                      int lane) {
+    const int K = kGateUp ? d : f;
+    P.nsteps = K >> 7;
+    const uint32_t code_row = (uint32_t)K >> 1, nblk = (uint32_t)K >> 5;
+    const uint32_t wrows = kGateUp ? 2u * (uint32_t)f : (uint32_t)d;
+    P.ra = rsrc_of(aq, a_bytes);
+    P.rb = rsrc_of((kGateUp ? W.gu_codes : W.dn_codes) + (size_t)ts.e * wrows * code_row,
+                   wrows * code_row);
+    P.rs = rsrc_of((kGateUp ? W.gu_scales : W.dn_scales) + (size_t)ts.e * wrows * nblk,
+                   wrows * nblk);
+    const uint32_t a_row_bytes = (uint32_t)P.nsteps * kStepBytes;
+    constexpr int kRows = MT * 16;
+    P.n_a = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = wid + kWaves * j;                       // this wave's j-th A load
+        if (i < Tile<MT>::kALoads) P.n_a = j + 1;
+        const int p = 64 * min(i, Tile<MT>::kALoads - 1) + lane;
+        const int r = p < kRows * kSlotsRow ? p / kSlotsRow : kRows - 1;
+        const int pc = p < kRows * kSlotsRow ? p - r * kSlotsRow : kSlotsRow - 1;
+        P.a_src[j] = (uint32_t)a_rowidx[r] * a_row_bytes + 16u * (uint32_t)pc;
+    }
+    const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = wid + kWaves * j;
+        const uint32_t row = (uint32_t)tile_row<kGateUp, MT>(t, ts.nb, f);
+        P.b_src[j] = packed ? (row >> 4) * (uint32_t)(K >> 7) * 1024u + 16u * (uint32_t)lane
+                            : (row + (uint32_t)r16) * code_row + 16u * (uint32_t)g;
+    }
+    {
+        const int t = 4 * wid + g;                            // this lane's scale row
+        const uint32_t row = (uint32_t)tile_row<kGateUp, MT>(t, ts.nb, f);
+        P.s_src = packed ? (row >> 4) * (uint32_t)(K >> 9) * 256u + 16u * (uint32_t)r16
+                         : (row + (uint32_t)r16) * nblk;
+    }
+    P.cstep = packed ? 1024u : 64u;
+    P.sgrp = packed ? 256u : 16u;
+}
+
+// Step kk's A and B loads into stage kk & 1, and at kk % 4 == 0 scale group
+// kk / 4 into its buffer.  Wave-uniform branches only.
+template <int MT>
+__device__ __forceinline__ void issue8(const Plan8 &P, uint32_t lds, int kk, int wid) {
+    const uint32_t st = lds + (uint32_t)((kk & 1) * kStageBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < P.n_a)
+            lds_load16(P.ra, P.a_src[j] + (uint32_t)kk * kStepBytes,
+                       (uint32_t)__builtin_amdgcn_readfirstlane(
+                           (int)(st + 1024u * (uint32_t)(wid + kWaves * j))));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        lds_load16(P.rb, P.b_src[j] + (uint32_t)kk * P.cstep,
+                   (uint32_t)__builtin_amdgcn_readfirstlane(
+                       (int)(st + kAStageBytes + 1024u * (uint32_t)(wid + kWaves * j))));
+    if ((kk & 3) == 0) {
+        const uint32_t sg = lds + 2u * kStageBytes + (uint32_t)(((kk >> 2) & 1) * kSGroupBytes);
+        lds_load16(P.rs, P.s_src + (uint32_t)(kk >> 2) * P.sgrp,
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(sg + 1024u * (uint32_t)wid)));
+    }
+}
+
+// The A fragments of m-tiles I..kMtw-1, two in flight: m-tile I's is waited
+// for, its MFMAs issued against every B fragment, m-tile I + 2's queued.
+template <int I, int MTW, int NTW, bool kSingle>
+__device__ __forceinline__ void chain8(f32x4_t (&acc)[MTW][NTW], AFrag (&fa)[2],
+                                       const BFrags<NTW> &fb, uint32_t a, uint32_t s) {
+    if constexpr (I < MTW) {
+        afrag_ready<(I + 1 < MTW) ? 5 : 0>(fa[I & 1]);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const u32x4_t q = fb.q[nt];
+            const i32x8_t b = {(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+            acc[I][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                fa[I & 1].hi, b, acc[I][nt], 2, 4, 0, (int)fa[I & 1].sc, 0, (int)fb.sc[nt]);
+            if constexpr (!kSingle)
+                acc[I][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fa[I & 1].lo, b, acc[I][nt], 2, 4, 1, (int)fa[I & 1].sc, 0, (int)fb.sc[nt]);
+        }
+        if constexpr (I + 2 < MTW) read_afrag<I + 2>(fa[I & 1], a, s);
+        chain8<I + 1, MTW, NTW, kSingle>(acc, fa, fb, a, s);
+    }
+}
+
 // kGateUp: A = split x (token rows), out = hq, the split of h = silu(gate) *
 //          up [rows][f] (expert-major rows), the down pass's A;
 // else:    A = hq, out = rows_out bf16 [rows][d].
 // packed: the weights are in the operand-order layout of prepack_kernel
-// (K % 512 == 0): each code load of a 16-row tile and K step reads 1 KB
-// contiguous, each scale load 256 B, instead of 16 rows x 64 B (16 B); the
-// registers receive the same bytes either way.
-// MT: the tile's height in 16-row m-tiles, the smallest of 1, 2, 4, 8 that
-// holds its rows, so that an expert with few rows pays matrix work for
-// those rows (rounded up to 16, 32 or 64) rather than for 128.
+// (K % 512 == 0): each 1 KB operand tile of a step is contiguous there (16
+// rows x 64 B gathered otherwise), each scale group 256 B.
 template <bool kGateUp, bool kSingle, int MT>
-__device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, const ExpertArgs &W,
-                                          uint8_t *__restrict__ hq,
+__device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32_t a_bytes,
+                                          const ExpertArgs &W, uint8_t *__restrict__ hq,
                                           uint16_t *__restrict__ rows_out, int d, int f,
-                                          int packed, const TileSel &ts,
-                                          const int *a_rowidx, uint8_t *lds) {
-    constexpr int kDma = Tile<MT>::kDma;
+                                          int packed, const TileSel &ts, const int *a_rowidx,
+                                          uint8_t *lds) {
+    constexpr int kMtw = Tile<MT>::kMtw, kNtw = Tile<MT>::kNtw;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int K = kGateUp ? d : f;
-    GemmArgs ga;
-    ga.nsteps = K >> 7;
-    const uint32_t a_row_bytes = (uint32_t)ga.nsteps * kStepBytes;
-    const uint32_t code_row = (uint32_t)K >> 1, nblk = (uint32_t)K >> 5;
-    const uint32_t wrows = kGateUp ? 2u * (uint32_t)f : (uint32_t)d;
-    const uint8_t *bq = (kGateUp ? W.gu_codes : W.dn_codes) + (size_t)ts.e * wrows * code_row;
-    const uint8_t *bsb = (kGateUp ? W.gu_scales : W.dn_scales) + (size_t)ts.e * wrows * nblk;
-    ga.bq = buffer_rsrc(bq, wrows * code_row);
-    ga.bs = buffer_rsrc(bsb, wrows * nblk);
     const int r16 = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        const int wr = kGateUp ? (nt < 4 ? ts.nb * 256 + 64 * wid + 16 * nt
-                                         : f + ts.nb * 256 + 64 * wid + 16 * (nt - 4))
-                               : ts.nb * 512 + 128 * wid + 16 * nt;
-        // tile wr / 16 of the expert: (K / 128) code blocks of 1 KB and
-        // (K / 512) scale groups of 256 B when packed
-        ga.tq[nt] = packed ? (uint32_t)(wr >> 4) * (uint32_t)(K >> 7) * 1024u : (uint32_t)wr * code_row;
-        ga.ts[nt] = packed ? (uint32_t)(wr >> 4) * (uint32_t)(K >> 9) * 256u : (uint32_t)wr * nblk;
-    }
-    ga.boff = packed ? 16u * (uint32_t)lane : (uint32_t)r16 * code_row + 16u * g;
-    ga.soff = packed ? 16u * (uint32_t)r16 : (uint32_t)r16 * nblk;   // dword aligned
-    ga.cstep = packed ? 1024u : 64u;
-    ga.sgrp = packed ? 256u : 16u;
-    ga.psel01 = (uint32_t)g | ((4u + (uint32_t)g) << 8);
-    uint32_t src[kDma];                             // byte offsets into aq (< 4 GiB)
-    constexpr int kRows = MT * 16;
-#pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-        const int sl = 64 * (4 * i + wid) + lane;
-        const int r = sl < kRows * kSlotsRow ? sl / kSlotsRow : kRows - 1;
-        const int pc = sl < kRows * kSlotsRow ? sl - r * kSlotsRow : kSlotsRow - 1;
-        src[i] = (uint32_t)a_rowidx[r] * a_row_bytes + 16u * pc;
-    }
+    // this wave's part: m-tiles mbase.., operand tiles nbase..
+    const int mbase = MT == 8 ? 4 * (wid & 1) : 0;
+    const int nbase = MT == 8 ? 8 * (wid >> 1) : 4 * wid;
+    Plan8 P;
+    plan8<kGateUp, MT>(P, aq, a_bytes, W, d, f, packed, ts, a_rowidx, wid, lane);
     const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-    const uint32_t a_lane = (uint32_t)(r16 * kStepBytes + 48 * g);
-    const uint32_t s_lane = (uint32_t)(r16 * kStepBytes + 192 + 2 * g);
+    const uint32_t a_lane = (uint32_t)((16 * mbase + r16) * kStepBytes + 48 * g);
+    const uint32_t s_lane = (uint32_t)((16 * mbase + r16) * kStepBytes + 192 + 2 * g);
 
-    f32x4_t acc[MT][8];
+    f32x4_t acc[kMtw][kNtw];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < kMtw; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kNtw; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: the loads of steps -3, -2, -1 in the steady state's roles
-    // (ring positions 1, 2, 3): A(0) + scale group 0, A(1) + codes of steps
-    // 0 and 1, A(2)
-    BRing br = {};
-    issue_a<MT>(lds_addr, aq, src, ga.nsteps, 0, wid);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_scales(br, ga, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a<MT>(lds_addr, aq, src, ga.nsteps, 1, wid);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_codes<0>(br, ga, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a<MT>(lds_addr, aq, src, ga.nsteps, 2, wid);
-    __builtin_amdgcn_sched_barrier(0);
-    // four steps per turn of the register ring and no branch around any
-    // load, wait or barrier (a step past the end only skips its MFMAs), so
-    // the wait counts the compiler derives at the loop header are exact
-    for (int kk = 0; kk < ga.nsteps; kk += 4) {
-        gemm_step<0, kSingle, MT>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk, wid, true);
-        gemm_step<1, kSingle, MT>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 1, wid,
-                                  kk + 1 < ga.nsteps);
-        gemm_step<2, kSingle, MT>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 2, wid,
-                                  kk + 2 < ga.nsteps);
-        gemm_step<3, kSingle, MT>(acc, br, ga, aq, src, lds_addr, a_lane, s_lane, kk + 3, wid,
-                                  kk + 3 < ga.nsteps);
+    issue8<MT>(P, lds_addr, 0, wid);
+    for (int kk = 0; kk < P.nsteps; ++kk) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));           // this wave's step-kk loads
+        __builtin_amdgcn_s_barrier();                       // everyone's; stage kk+1 is free
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < P.nsteps) issue8<MT>(P, lds_addr, kk + 1, wid);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t st = lds_addr + (uint32_t)((kk & 1) * kStageBytes);
+        const uint32_t sg = lds_addr + 2u * kStageBytes +
+                            (uint32_t)(((kk >> 2) & 1) * kSGroupBytes) +
+                            16u * (uint32_t)r16 + 4u * (uint32_t)(kk & 3) + (uint32_t)g;
+        BFrags<kNtw> fb;
+#pragma unroll
+        for (int nt = 0; nt < kNtw; ++nt) {
+            fb.q[nt] = ds_read128_at(st + kAStageBytes + 1024u * (uint32_t)(nbase + nt) +
+                                     16u * (uint32_t)lane);
+            fb.sc[nt] = ds_read_u8_at(sg + 256u * (uint32_t)(nbase + nt));
+        }
+        AFrag fa[2];
+        const uint32_t a = st + a_lane, s = st + s_lane;
+        read_afrag<0>(fa[0], a, s);
+        if constexpr (kMtw > 1) read_afrag<1>(fa[1], a, s);
+        // the B fragments and m-tile 0's A fragment; m-tile 1's may still fly
+        bfrags_ready<kNtw, (kMtw > 1 ? 5 : 0)>(fb);
+        chain8<0, kMtw, kNtw, kSingle>(acc, fa, fb, a, s);
     }
-    // drain the trailing (re-)loads before their registers or the block's
-    // LDS can be reused
-    drain_weight_loads(br);
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();                                        // the stages are free for the epilogue
 
     // epilogue: lane holds rows 4 (l / 16) + i, column l % 16 of each tile
     if (kGateUp) {
-        // h = silu(gate) * up goes through LDS (the A ring is idle now) in
-        // passes of up to 64 rows, then is split one 32-element block per
-        // lane: the wave's 64 h columns hc0 .. hc0 + 63 are MX blocks gb0,
-        // gb0 + 1 of down step hc0 / 128
-        constexpr int kHs = 68;                          // floats per staged row
-        constexpr int kPassMt = MT < 4 ? MT : 4;         // m-tiles per pass
-        float *hs = reinterpret_cast<float *>(lds) + wid * 64 * kHs;
-        const int hc0 = ts.nb * 256 + 64 * wid;
+        // h = silu(gate) * up, kNtw / 2 * 16 columns of the wave's rows, goes
+        // through LDS two m-tiles (32 rows) at a time, then is split one
+        // 32-element MX block per lane
+        constexpr int kPer = kNtw / 2;                       // gate tiles of the wave
+        constexpr int kCols = 16 * kPer;                     // 64 or 32 h columns
+        constexpr int kHs = kCols + 4;                       // floats per staged row
+        constexpr int kPassMt = kMtw < 2 ? kMtw : 2;
+        float *hs = reinterpret_cast<float *>(lds) + wid * 32 * kHs;
+        const int hc0 = ts.nb * 256 + (MT == 8 ? (wid >> 1) : wid) * kCols;
         const uint32_t hq_row = (uint32_t)(f >> 7) * kStepBytes;
         uint8_t *hq_step = hq + (size_t)(hc0 >> 7) * kStepBytes;
         const int gb0 = (hc0 & 127) >> 5;
-        __syncthreads();                                 // every wave is done with the ring
 #pragma unroll
-        for (int pass = 0; pass < MT / kPassMt; ++pass) {
-            const int left = ts.ne - ts.m0 - 64 * pass;   // rows of the tile from this pass on
-            if (left <= 0) break;
+        for (int pass = 0; pass < kMtw / kPassMt; ++pass) {
+            const int r_first = ts.m0 + 16 * (mbase + kPassMt * pass);
+            const int left = ts.ne - r_first;               // rows from this pass on
 #pragma unroll
             for (int m = 0; m < kPassMt; ++m)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int nt = 0; nt < 4; ++nt) {
+                    for (int nt = 0; nt < kPer; ++nt) {
                         const float gv = acc[kPassMt * pass + m][nt][i];
-                        const float uv = acc[kPassMt * pass + m][nt + 4][i];
+                        const float uv = acc[kPassMt * pass + m][nt + kPer][i];
                         hs[(16 * m + 4 * g + i) * kHs + 16 * nt + r16] = gv / (1.0f + expf(-gv)) * uv;
                     }
             __syncthreads();
-            // buffer stores drop offsets past the pass's live rows
-            const uint32_t live_bytes = (uint32_t)min(left, 16 * kPassMt) * hq_row;
-            const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(
-                hq_step + (size_t)(ts.row0 + ts.m0 + 64 * pass) * hq_row, 0, (int)live_bytes,
-                0x00020000);
+            if (left > 0) {
+                // buffer stores drop offsets past the pass's live rows
+                const uint32_t live = (uint32_t)min(left, 16 * kPassMt) * hq_row;
+                const brsrc_t out = rsrc_of(hq_step + (size_t)(ts.row0 + r_first) * hq_row, live);
+                const int item = lane, rl = item / (kCols / 32), blk = item % (kCols / 32);
+                if (rl < 16 * kPassMt) {
+                    float v[32];
+                    const float *src = hs + rl * kHs + 32 * blk;
 #pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                if (it == 1 && (kPassMt < 4 || left <= 32)) break;
-                const int item = 64 * it + lane, rl = item >> 1, blk = gb0 + (item & 1);
-                float v[32];
-                const float *src = hs + rl * kHs + 32 * (item & 1);
+                    for (int c = 0; c < 8; ++c) {
+                        const f32x4_t w = *reinterpret_cast<const f32x4_t *>(src + 4 * c);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    const f32x4_t w = *reinterpret_cast<const f32x4_t *>(src + 4 * c);
+                        for (int q = 0; q < 4; ++q) v[4 * c + q] = w[q];
+                    }
+                    const SplitBlock sb = split_block32(v);
+                    u32x4_t w[3];
+                    split_words(sb, w);
+                    const uint32_t o = (uint32_t)rl * hq_row, b = (uint32_t)(gb0 + blk);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) v[4 * c + q] = w[q];
+                    for (int c = 0; c < 3; ++c)
+                        __builtin_amdgcn_raw_buffer_store_b128(w[c], out, o + 48u * b + 16u * c, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sb.scales, out, o + 192u + 2u * b,
+                                                          0, 0);
                 }
-                const SplitBlock sb = split_block32(v);
-                u32x4_t w[3];
-                split_words(sb, w);
-                const uint32_t o = (uint32_t)rl * hq_row;
-#pragma unroll
-                for (int c = 0; c < 3; ++c)
-                    __builtin_amdgcn_raw_buffer_store_b128(w[c], out, o + 48u * blk + 16u * c, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)sb.scales, out, o + 192u + 2u * blk,
-                                                      0, 0);
             }
             __syncthreads();
         }
     } else {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < kMtw; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = ts.m0 + mt * 16 + 4 * g + i;
+                const int r = ts.m0 + 16 * (mbase + mt) + 4 * g + i;
                 if (r < ts.ne) {
-                    uint16_t *orow = rows_out + (size_t)(ts.row0 + r) * d + ts.nb * 512 + 128 * wid;
+                    uint16_t *orow = rows_out + (size_t)(ts.row0 + r) * d + ts.nb * 512 + 16 * nbase;
 #pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) orow[16 * nt + r16] = f32_to_bf16_rne(acc[mt][nt][i]);
+                    for (int nt = 0; nt < kNtw; ++nt)
+                        orow[16 * nt + r16] = f32_to_bf16_rne(acc[mt][nt][i]);
                 }
             }
     }
@@ -768,7 +703,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, const 
 // is chosen from its rows (block-uniform, so the branch below and every
 // barrier inside gemm_tile are taken by the whole block).
 template <bool kGateUp, bool kSingle>
-__global__ __launch_bounds__(256) void ffn_mfma_kernel(
+__global__ __launch_bounds__(512, 1) void ffn_mfma_kernel(
     const uint8_t *__restrict__ aq, ExpertArgs W, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
     const int32_t *__restrict__ tiles, uint8_t *__restrict__ hq, uint16_t *__restrict__ rows_out,
@@ -790,15 +725,18 @@ __global__ __launch_bounds__(256) void ffn_mfma_kernel(
         }
     }
     __syncthreads();
+    // the A operand's buffer: T (gate/up) or T * k (down) split rows
+    const uint32_t a_bytes = (uint32_t)((kGateUp ? (size_t)T : (size_t)nrows) *
+                                        (size_t)((kGateUp ? d : f) >> 7) * kStepBytes);
     const int rows = __builtin_amdgcn_readfirstlane(min(kBM, ts.ne - ts.m0));
     if (rows <= 16)
-        gemm_tile<kGateUp, kSingle, 1>(aq, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
+        gemm_tile<kGateUp, kSingle, 1>(aq, a_bytes, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
     else if (rows <= 32)
-        gemm_tile<kGateUp, kSingle, 2>(aq, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
+        gemm_tile<kGateUp, kSingle, 2>(aq, a_bytes, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
     else if (rows <= 64)
-        gemm_tile<kGateUp, kSingle, 4>(aq, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
+        gemm_tile<kGateUp, kSingle, 4>(aq, a_bytes, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
     else
-        gemm_tile<kGateUp, kSingle, 8>(aq, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
+        gemm_tile<kGateUp, kSingle, 8>(aq, a_bytes, W, hq, rows_out, d, f, packed, ts, a_rowidx, lds);
 }
 
 // The operand-order ("packed") layout of one MXFP4 matrix [rows][K] per
@@ -952,7 +890,7 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
         const long long blocks = 8 * ((mt_max * (f / 256) + 7) / 8);
         (void)timed_launch("gate_up_mfma",
                            single ? ffn_mfma_kernel<true, true> : ffn_mfma_kernel<true, false>,
-                           dim3((unsigned)blocks), dim3(256), kLdsBytes, s, xq, w, offsets,
+                           dim3((unsigned)blocks), dim3(512), kLdsBytes, s, xq, w, offsets,
                            sorted_rows, plan, tiles, hq, nullptr, T, d, E, k, f, (int)packed);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -965,7 +903,7 @@ hipError_t launch_mfma_ffn(const uint16_t *x, ExpertArgs w, const int32_t *offse
         const long long blocks = 8 * ((mt_max * (d / 512) + 7) / 8);
         (void)timed_launch("down_mfma",
                            single ? ffn_mfma_kernel<false, true> : ffn_mfma_kernel<false, false>,
-                           dim3((unsigned)blocks), dim3(256), kLdsBytes, s, hq, w, offsets,
+                           dim3((unsigned)blocks), dim3(512), kLdsBytes, s, hq, w, offsets,
                            sorted_rows, plan, tiles, nullptr, rows_out, T, d, E, k, f, (int)packed);
     }
     return hipGetLastError();

@@ -1,13 +1,13 @@
 """Code-generation invariants of the scaled-MFMA expert GEMM (CPU only).
 
-The GEMM's weight and activation loads are inline asm, waited for by one
-explicit vmcnt per K step, so the compiler does not know when their
-destination registers are written.  That is only correct if (1) the main
-loop never copies a vector register (a copy could read a register whose load
-is still in flight) and (2) after the loop no instruction writes a register
-that an in-flight load targets before the final vmcnt(0).  This test builds
-the kernel source to gfx950 assembly with hipcc and checks both on the
-kernels' main loop (the loop that holds the MFMAs).
+The GEMM moves every operand global -> LDS with inline-asm buffer loads that
+write LDS directly, waited for by an explicit vmcnt(0) and a barrier at the
+top of each K step; the compiler sees none of them.  That is only correct if
+the kernels' MFMA loops hold no vector-memory load into registers (whose
+wait the compiler would place on its own), and the design relies on two
+waves per SIMD (no scratch, at most 256 registers).  This test builds the
+kernel source to gfx950 assembly with hipcc and checks the MFMA loops (one
+per tile height) and the resource use.
 """
 import os
 import re
@@ -61,50 +61,10 @@ def _loops(lines):
     loops = []
     for hb in [b for b in blocks if "Loop Header" in b[1]]:
         h = hb[0].replace(".LBB", "BB")
-        lp = [b for b in blocks if b is hb or ("Header=" + h) in b[1]]
+        lp = [b for b in blocks if b is hb or re.search(r"Header=%s\b" % h, b[1])]
         if any(x.startswith("v_mfma") for b in lp for x in b[2]):
             loops.append(lp)
     return loops, blocks
-
-
-def _analyse_all(lines):
-    loops, blocks = _loops(lines)
-    assert len(loops) == 4, "expected one MFMA loop per tile height, found %d" % len(loops)
-    return [_analyse_loop(lp, blocks) for lp in loops]
-
-
-def _analyse_loop(loop, blocks):
-    names = {b[0] for b in loop}
-    body = [x for b in loop for x in b[2]]
-    copies = [x for x in body if re.match(r"(v_mov_b32|v_accvgpr_\w+|scratch_\w+)\b", x)]
-    dests = set()
-    for x in body:
-        if x.startswith("buffer_load"):
-            dests |= _regs(x.split()[1].rstrip(","))
-    exits = set()
-    for b in loop:
-        for x in b[2]:
-            m = re.match(r"s_cbranch_\w+\s+(\.LBB\d+_\d+)|s_branch\s+(\.LBB\d+_\d+)", x)
-            if m:
-                t = m.group(1) or m.group(2)
-                if t not in names:
-                    exits.add(t)
-    order = [b[0] for b in blocks]
-    clobbers = []
-    for t in exits:
-        done = False
-        for b in blocks[order.index(t):]:
-            for x in b[2]:
-                if "s_waitcnt vmcnt(0)" in x:
-                    done = True
-                    break
-                m = re.match(r"(v_\w+)\s+(v\[\d+:\d+\]|v\d+)", x)
-                if m and _regs(m.group(2)) & dests:
-                    clobbers.append(x)
-            if done:
-                break
-        assert done, "no vmcnt(0) on the loop exit path"
-    return body, copies, dests, clobbers
 
 
 @pytest.fixture(scope="module")
@@ -121,6 +81,37 @@ def gemm_asm():
         return open(out).read()
 
 
+@pytest.fixture(scope="module")
+def gemm_resources():
+    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    hipcc = HIPCC if os.path.exists(HIPCC) else shutil.which("hipcc")
+    with tempfile.TemporaryDirectory() as td:
+        cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+               "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+               "--cuda-device-only", "-c", "-o", os.path.join(td, "x.o"), SRC,
+               "-Rpass-analysis=kernel-resource-usage"]
+        err = subprocess.run(cmd, check=True, capture_output=True, text=True).stderr
+    out, cur = {}, None
+    for line in err.splitlines():
+        m = re.search(r"Function Name: (\S*ffn_mfma_kernel\S*)", line)
+        if m:
+            cur = m.group(1)
+            out[cur] = {}
+            continue
+        if cur is None:
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m:
+            out[cur]["scratch"] = int(m.group(1))
+        m = re.search(r"Occupancy \[waves/SIMD\]: (\d+)", line)
+        if m:
+            out[cur]["occupancy"] = int(m.group(1))
+            cur = None
+    assert len(out) == 4, out
+    return out
+
+
 # <gate/up?, one term (activation-MX mode)?>
 KERNELS = ["ILb1ELb0E", "ILb1ELb1E", "ILb0ELb0E", "ILb0ELb1E"]
 KERNEL_IDS = ["gate_up", "gate_up_single", "down", "down_single"]
@@ -131,19 +122,25 @@ def test_all_gemm_kernels_present(gemm_asm):
 
 
 @pytest.mark.parametrize("which", KERNELS, ids=KERNEL_IDS)
-def test_main_loops_have_no_register_copies(gemm_asm, which):
+def test_mfma_loops_load_only_into_lds(gemm_asm, which):
     (lines,) = [v for k, v in _kernels(gemm_asm).items() if which in k]
-    for body, copies, dests, _ in _analyse_all(lines):
-        assert sum(x.startswith("v_mfma") for x in body) > 0
-        assert len(dests) >= 128, "weight ring registers not found"
-        assert copies == [], copies[:5]
+    loops, _ = _loops(lines)
+    assert len(loops) == 4, "expected one MFMA loop per tile height, found %d" % len(loops)
+    for lp in loops:
+        body = [x for b in lp for x in b[2]]
+        assert sum(x.startswith("v_mfma_scale") for x in body) > 0
+        loads = [x for x in body if re.match(r"(buffer|global|flat)_load", x)]
+        assert loads and all(x.rstrip().endswith(" lds") for x in loads), loads[:5]
+        assert not [x for x in body if x.startswith("scratch_")]
+        # the step's wait: every load of the wave, then the barrier
+        i = next(i for i, x in enumerate(body) if x.startswith("s_barrier"))
+        assert any("vmcnt(0)" in x for x in body[:i]), body[:i]
 
 
-@pytest.mark.parametrize("which", KERNELS, ids=KERNEL_IDS)
-def test_in_flight_registers_untouched_until_drained(gemm_asm, which):
-    (lines,) = [v for k, v in _kernels(gemm_asm).items() if which in k]
-    for _, _, _, clobbers in _analyse_all(lines):
-        assert clobbers == [], clobbers[:5]
+def test_two_waves_per_simd(gemm_resources):
+    for name, res in gemm_resources.items():
+        assert res["scratch"] == 0, name
+        assert res["occupancy"] >= 2, (name, res)
 
 
 def test_fp6_conversions_do_not_overlap_their_sources(gemm_asm):
