@@ -297,18 +297,22 @@ __device__ __forceinline__ int find_expert(const int32_t *tiles, int nact, int m
 //      operand layout, so a fragment read is 16 contiguous bytes per lane;
 //   scales of 4 steps at once, 256 B per operand tile (row r's 16 bytes at
 //      16 r).
-// Two LDS stages (and two scale groups) alternate: at the top of step kk
-// each wave waits for its own loads (vmcnt(0): only step kk's are
-// outstanding), a barrier publishes every wave's, then step kk + 1's loads
-// are issued into the other stage -- free, since every wave is past step
-// kk - 1 -- and step kk's fragments are read and multiplied.
+// The weight codes (first touch often from HBM) are loaded two steps ahead
+// into three LDS stages, the activations (mostly L2 hits) one step ahead
+// into two, and the weight scales once per 4 steps into one buffer that each
+// lane copies into registers at the group's first step.  At the top of step
+// kk each wave waits until only its loads of step kk + 1's codes remain, a
+// barrier publishes every wave's, then the next loads are issued into
+// buffers every wave has finished reading, and step kk is multiplied.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 8;
 constexpr int kAStageBytes = kBM * kStepBytes;              // 26624: a 128-row tile's step
 constexpr int kBStageBytes = 32 * 1024;                     // 32 operand tiles of 1 KB
-constexpr int kStageBytes = kAStageBytes + kBStageBytes;    // 59392
 constexpr int kSGroupBytes = 32 * 256;                      // scales of 4 steps, 32 tiles
-constexpr int kLdsBytes = 2 * kStageBytes + 2 * kSGroupBytes;   // 135168 of 160 KB
+constexpr int kBBase = 2 * kAStageBytes;                    // 2 A stages, 3 B stages, 1 group
+constexpr int kSBase = kBBase + 3 * kBStageBytes;
+constexpr int kLdsBytes = kSBase + kSGroupBytes;            // 159744 of 160 KB
+constexpr int kBLoads = 4;                                  // code loads per wave and step
 
 template <int MT>
 struct Tile {
@@ -424,10 +428,11 @@ __device__ __forceinline__ void bfrags_ready(BFrags<N> &b) {
 }
 
 // The block's tile: which expert, which 128 rows of it, which 512 weight
-// rows.  Blocks are spread over the 8 XCDs (consecutive block ids go to
-// consecutive XCDs) so that each XCD walks a contiguous range of the
-// (m-tile, n-block) order: the n-blocks of one m-tile, and the m-tiles of
-// one expert, meet in the same L2.
+// rows.  Units (tile, n-block) are numbered expert by expert, and inside an
+// expert n-block by n-block, its row tiles next to each other: the blocks
+// that read the same weight slice run at the same time.  Blocks are spread
+// over the 8 XCDs (consecutive block ids go to consecutive XCDs) so that
+// each XCD walks a contiguous range of units: those blocks meet in its L2.
 struct TileSel {
     int e, row0, ne, m0, nb;
 };
@@ -441,16 +446,21 @@ __device__ __forceinline__ bool select_tile(const int32_t *tiles, const int32_t 
     if (loc >= per) return false;
     const int u = (int)(blockIdx.x & 7) * per + loc;
     if (u >= total_u) return false;
-    const int mt = u / NB;
-    ts.nb = u - mt * NB;
+    // expert a owns units [tiles[1 + a] * NB, (its tile end) * NB)
     const int nact = plan[0];
-    const int a = find_expert(tiles, nact, mt);
+    const int a = find_expert(tiles, nact, u / NB);
+    const int t0 = tiles[1 + a];
+    const int nt = (a + 1 < nact ? tiles[2 + a] : tiles[0]) - t0;
+    if (nt <= 0) return false;
+    const int v = u - t0 * NB;
+    ts.nb = v / nt;
     ts.e = plan[1 + a];
-    if ((unsigned)ts.e >= (unsigned)E) return false;
+    if ((unsigned)ts.e >= (unsigned)E || ts.nb >= NB) return false;
     ts.row0 = offsets[ts.e];
     ts.ne = offsets[ts.e + 1] - ts.row0;
     if (ts.row0 < 0 || ts.ne <= 0 || ts.row0 + ts.ne > nrows) return false;
-    ts.m0 = (mt - tiles[1 + a]) * kBM;
+    ts.m0 = (v - ts.nb * nt) * kBM;
+    if (ts.m0 >= ts.ne) return false;
     return true;
 }
 
@@ -521,11 +531,11 @@ __device__ __forceinline__ void plan8(Plan8 &P, const uint8_t *aq, uint32_t a_by
     P.sgrp = packed ? 256u : 16u;
 }
 
-// Step kk's A and B loads into stage kk & 1, and at kk % 4 == 0 scale group
-// kk / 4 into its buffer.  Wave-uniform branches only.
+// Step kk's activation loads into A stage kk & 1, and at kk % 4 == 0 the
+// scale group kk / 4.  Wave-uniform branches only.
 template <int MT>
-__device__ __forceinline__ void issue8(const Plan8 &P, uint32_t lds, int kk, int wid) {
-    const uint32_t st = lds + (uint32_t)((kk & 1) * kStageBytes);
+__device__ __forceinline__ void issue_a8(const Plan8 &P, uint32_t lds, int kk, int wid) {
+    const uint32_t st = lds + (uint32_t)((kk & 1) * kAStageBytes);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         if (j < P.n_a)
@@ -533,15 +543,35 @@ __device__ __forceinline__ void issue8(const Plan8 &P, uint32_t lds, int kk, int
                        (uint32_t)__builtin_amdgcn_readfirstlane(
                            (int)(st + 1024u * (uint32_t)(wid + kWaves * j))));
     }
+    if ((kk & 3) == 0)
+        lds_load16(P.rs, P.s_src + (uint32_t)(kk >> 2) * P.sgrp,
+                   (uint32_t)__builtin_amdgcn_readfirstlane(
+                       (int)(lds + kSBase + 1024u * (uint32_t)wid)));
+}
+
+// Step kk's weight-code loads (kBLoads per wave) into B stage sb = kk % 3.
+__device__ __forceinline__ void issue_b8(const Plan8 &P, uint32_t lds, int kk, int sb, int wid) {
+    const uint32_t st = lds + kBBase + (uint32_t)(sb * kBStageBytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kBLoads; ++j)
         lds_load16(P.rb, P.b_src[j] + (uint32_t)kk * P.cstep,
                    (uint32_t)__builtin_amdgcn_readfirstlane(
-                       (int)(st + kAStageBytes + 1024u * (uint32_t)(wid + kWaves * j))));
-    if ((kk & 3) == 0) {
-        const uint32_t sg = lds + 2u * kStageBytes + (uint32_t)(((kk >> 2) & 1) * kSGroupBytes);
-        lds_load16(P.rs, P.s_src + (uint32_t)(kk >> 2) * P.sgrp,
-                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(sg + 1024u * (uint32_t)wid)));
+                       (int)(st + 1024u * (uint32_t)(wid + kWaves * j))));
+}
+
+// The lane's E8M0 codes of one scale group for its operand tiles: byte s of
+// sc[nt] is the code of K block 4 s + g of row r16 (step s of the group),
+// picked from the row's 16 bytes.
+template <int N>
+__device__ __forceinline__ void read_group_scales(uint32_t (&sc)[N], uint32_t addr,
+                                                  uint32_t psel01) {
+#pragma unroll
+    for (int nt = 0; nt < N; ++nt) {
+        u32x4_t r = ds_read128_at(addr + 256u * (uint32_t)nt);
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r));
+        const uint32_t t01 = __builtin_amdgcn_perm(r.y, r.x, psel01);
+        const uint32_t t23 = __builtin_amdgcn_perm(r.w, r.z, psel01);
+        sc[nt] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
     }
 }
 
@@ -598,23 +628,35 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
 #pragma unroll
         for (int j = 0; j < kNtw; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    issue8<MT>(P, lds_addr, 0, wid);
+    // prologue: step 0's activations and scale group, steps 0 and 1's codes
+    issue_a8<MT>(P, lds_addr, 0, wid);
+    issue_b8(P, lds_addr, 0, 0, wid);
+    if (P.nsteps > 1) issue_b8(P, lds_addr, 1, 1, wid);
+    const uint32_t psel01 = (uint32_t)g | ((4u + (uint32_t)g) << 8);
+    const uint32_t sgrp_lane = lds_addr + kSBase + 256u * (uint32_t)nbase + 16u * (uint32_t)r16;
+    uint32_t spk[kNtw];
+    int sb = 0;                                             // kk % 3
     for (int kk = 0; kk < P.nsteps; ++kk) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));           // this wave's step-kk loads
-        __builtin_amdgcn_s_barrier();                       // everyone's; stage kk+1 is free
+        // step kk's operands: all but step kk + 1's codes, the last loads
+        // issued (when there are any)
+        if (kk + 1 < P.nsteps)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBLoads));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_s_barrier();                       // everyone's; step kk-1's buffers free
         __builtin_amdgcn_sched_barrier(0);
-        if (kk + 1 < P.nsteps) issue8<MT>(P, lds_addr, kk + 1, wid);
+        if ((kk & 3) == 0) read_group_scales<kNtw>(spk, sgrp_lane, psel01);
         __builtin_amdgcn_sched_barrier(0);
-        const uint32_t st = lds_addr + (uint32_t)((kk & 1) * kStageBytes);
-        const uint32_t sg = lds_addr + 2u * kStageBytes +
-                            (uint32_t)(((kk >> 2) & 1) * kSGroupBytes) +
-                            16u * (uint32_t)r16 + 4u * (uint32_t)(kk & 3) + (uint32_t)g;
+        if (kk + 1 < P.nsteps) issue_a8<MT>(P, lds_addr, kk + 1, wid);
+        if (kk + 2 < P.nsteps) issue_b8(P, lds_addr, kk + 2, sb == 0 ? 2 : sb - 1, wid);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t st = lds_addr + (uint32_t)((kk & 1) * kAStageBytes);
+        const uint32_t sbq = lds_addr + kBBase + (uint32_t)(sb * kBStageBytes);
         BFrags<kNtw> fb;
 #pragma unroll
         for (int nt = 0; nt < kNtw; ++nt) {
-            fb.q[nt] = ds_read128_at(st + kAStageBytes + 1024u * (uint32_t)(nbase + nt) +
-                                     16u * (uint32_t)lane);
-            fb.sc[nt] = ds_read_u8_at(sg + 256u * (uint32_t)(nbase + nt));
+            fb.q[nt] = ds_read128_at(sbq + 1024u * (uint32_t)(nbase + nt) + 16u * (uint32_t)lane);
+            fb.sc[nt] = spk[nt] >> (8 * (kk & 3));
         }
         AFrag fa[2];
         const uint32_t a = st + a_lane, s = st + s_lane;
@@ -623,6 +665,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
         // the B fragments and m-tile 0's A fragment; m-tile 1's may still fly
         bfrags_ready<kNtw, (kMtw > 1 ? 5 : 0)>(fb);
         chain8<0, kMtw, kNtw, kSingle>(acc, fa, fb, a, s);
+        sb = sb == 2 ? 0 : sb + 1;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();                                        // the stages are free for the epilogue
