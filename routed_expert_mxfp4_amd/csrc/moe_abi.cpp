@@ -361,6 +361,17 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
         e = moe::launch_mx_round_bf16(x, D.T, D.d, xr, s);
         xa = xr;
     }
+    // one token in bf16: gate/up writes h' = w h split in two MX terms, and
+    // the down pass with the combine runs on the matrix cores
+    if (token_fused && D.act == MOE_ACT_BF16 && moe::decode_mfma_ok(D.d, D.E, D.k, D.f)) {
+        uint8_t *hq = reinterpret_cast<uint8_t *>(h);
+        if (e == hipSuccess)
+            e = moe::launch_gate_up_token_split(logits, x, W, ids, tw, counts, offsets,
+                                                sorted_rows, row_pos, plan, hq, D.d, D.E, D.k,
+                                                D.f, s);
+        if (e == hipSuccess) e = moe::launch_down_token_mfma(hq, W, plan, y, D.d, D.E, D.k, D.f, s);
+        return e;
+    }
     if (e == hipSuccess) {
         e = token_fused ? moe::launch_gate_up_token(logits, xa, W, ids, tw, counts, offsets,
                                                     sorted_rows, row_pos, plan, h, D.d, D.E,
@@ -892,6 +903,29 @@ int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint
                            ? moe::launch_mx_split_bf16(static_cast<const uint16_t *>(in), rows, K, out, st)
                            : moe::launch_mx_split_f32(static_cast<const float *>(in), rows, K, out, st);
         return e == hipSuccess ? 0 : -1;
+    } catch (...) {
+        return -1;
+    }
+}
+
+int moe_diag_stream_read(const void *src, size_t bytes, uint32_t *out, int blocks,
+                         void *hip_stream) {
+    try {
+        return moe::launch_stream_read(src, bytes, out, blocks,
+                                       static_cast<hipStream_t>(hip_stream)) == hipSuccess
+                   ? 0
+                   : -1;
+    } catch (...) {
+        return -1;
+    }
+}
+
+int moe_diag_mfma_rate(int kind, int blocks, int iters, float *out, void *hip_stream) {
+    try {
+        return moe::launch_mfma_rate(kind, blocks, iters, out,
+                                     static_cast<hipStream_t>(hip_stream)) == hipSuccess
+                   ? 0
+                   : -1;
     } catch (...) {
         return -1;
     }
