@@ -49,7 +49,10 @@ KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm"
 TAIL_KERNELS = ("rmsnorm", "shared_gate_up", "shared_down_add", "shared_gemm_gate_up",
                 "shared_gemm_down")
 MXFP4_PEAK_TFLOPS = 10100.0     # MI355X dense MXFP4 / MXFP6, published
-MFMA_MIN_T = 128                # the library's scaled-MFMA path starts here
+FP8_PEAK_TFLOPS = 5000.0        # MI355X dense FP8, published
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16, published
+MFMA_MIN_T = 128                # the library's scaled-MFMA path starts here (no per-expert choice)
+FUSE_MAX_T = 4                  # up to here the library keeps the fused GEMV token path
 
 
 def parse():
@@ -73,8 +76,12 @@ def parse():
                     help="prefill workloads: the experts re-laid once (before timing) in the "
                          "scaled-MFMA GEMM's operand order (moe_prepack_experts), timed through "
                          "moe_layer_forward_packed; the same bytes and the same results")
-    ap.add_argument("--cpu-sample", type=int, default=2,
-                    help="tokens of the workload the CPU oracle runs (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=24,
+                    help="tokens of the workload the CPU oracle runs on the host's threads "
+                         "(0: skip the CPU baseline)")
+    ap.add_argument("--cpu-one-core-sample", type=int, default=2,
+                    help="tokens of the workload the CPU oracle runs on one thread, the "
+                         "per-core reference (0: skip)")
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip the per-kernel timing passes after the timed region")
     ap.add_argument("--gemv-max-rows", type=int, default=None, metavar="N",
@@ -85,6 +92,10 @@ def parse():
                          "moe_expert_ffn at the K3 shape with every expert given n rows, all "
                          "experts on the grouped GEMVs against all on scaled-MFMA tiles, for "
                          "n = 1..16; prints one JSON line and exits")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure this GPU's ceilings: one-launch streaming reads of "
+                         "several sizes and the matrix instructions' issue rate per operand "
+                         "format; prints one JSON line and exits")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain fp32 device copy (torch.neg) of MIB MiB five "
                          "times, the reference for scaling HBM traffic counters, and exit")
@@ -104,6 +115,78 @@ def calibrate_copy(mib: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes_read": n * 4, "calibrate_copy_bytes_written": n * 4,
                       "launches": 5}))
+
+
+def stream_read_gbps(nbytes: int, reps: int = 5, _buf={}):
+    """The best bandwidth (GB/s) of one launch reading nbytes (rounded down to
+    16 B) with the library's plain streaming-read kernel, over reps launches
+    at each of a few grid sizes: what a kernel reading the same bytes in one
+    launch can reach here, ramp-up and tail included."""
+    import torch
+    from routed_expert_mxfp4_amd import moe
+    nbytes -= nbytes % 16
+    if _buf.get("n", 0) < nbytes:
+        _buf.clear()
+        torch.cuda.synchronize()
+        _buf["t"] = torch.randint(-2 ** 31, 2 ** 31 - 1, ((nbytes + 3) // 4,), dtype=torch.int32,
+                                  device="cuda:0")
+        _buf["out"] = torch.empty(1 << 16, dtype=torch.int32, device="cuda:0")
+        _buf["n"] = nbytes
+    buf, out = _buf["t"], _buf["out"]
+    best = (float("inf"), 0)
+    for blocks in (1024, 2048, 4096, 8192):
+        moe.diag_stream_read(buf, nbytes, out, blocks)          # warm
+        moe.diag_time_kernel("stream_read", capacity=reps)
+        for i in range(reps):
+            moe.diag_stream_read(buf, nbytes, out, blocks)
+        torch.cuda.synchronize()
+        best = min([best] + [(ms * 1e-3, blocks) for ms in moe.diag_kernel_times(reps)])
+    moe.diag_time_kernel(None, 0)
+    return nbytes / best[0] / 1e9, best[1]
+
+
+def mfma_rate_tflops(kind: str, reps: int = 3):
+    """The best rate (TFLOP/s) of the matrix instruction of this kind issued
+    from registers by two and by four waves per SIMD."""
+    import torch
+    from routed_expert_mxfp4_amd import moe
+    out = torch.empty(4 * 1024, dtype=torch.float32, device="cuda:0")
+    best = 0.0
+    for blocks, iters in ((512, 2048), (1024, 1024)):
+        flops = moe.diag_mfma_rate(kind, blocks, iters, out)   # warm
+        moe.diag_time_kernel("mfma_rate", capacity=reps)
+        for i in range(reps):
+            moe.diag_mfma_rate(kind, blocks, iters, out)
+        torch.cuda.synchronize()
+        best = max([best] + [flops / (ms * 1e-3) / 1e12 for ms in moe.diag_kernel_times(reps)])
+    moe.diag_time_kernel(None, 0)
+    return best
+
+
+def peaks() -> None:
+    """Measured ceilings next to the published ones."""
+    from routed_expert_mxfp4_amd import synth
+    cfg = synth.CONFIGS[1]
+    gu, dn = cfg.k * cfg.gate_up_bytes, cfg.k * (cfg.expert_bytes - cfg.gate_up_bytes)
+    reads = []
+    for label, n in (("16 MiB", 16 << 20), ("decode down, 16 experts", dn),
+                     ("decode gate/up, 16 experts", gu), ("decode layer, 16 experts", gu + dn),
+                     ("1 GiB", 1 << 30), ("4 GiB", 4 << 30)):
+        gbps, blocks = stream_read_gbps(n)
+        reads.append({"what": label, "bytes": n - n % 16, "GBps": gbps, "blocks": blocks,
+                      "frac_of_published": gbps / HBM_PEAK_GBPS})
+    rates = {}
+    for kind, pub in (("fp6xfp4", MXFP4_PEAK_TFLOPS), ("fp4xfp4", MXFP4_PEAK_TFLOPS),
+                      ("fp6xfp4_32x32x64", MXFP4_PEAK_TFLOPS),
+                      ("fp4xfp4_32x32x64", MXFP4_PEAK_TFLOPS),
+                      ("fp8xfp4", None), ("fp8xfp8", FP8_PEAK_TFLOPS), ("bf16", BF16_PEAK_TFLOPS)):
+        r = mfma_rate_tflops(kind)
+        rates[kind] = {"TFLOPs": r, "published_TFLOPs": pub,
+                       "frac_of_published": None if pub is None else r / pub}
+    print(json.dumps({"stream_read": reads, "mfma_rate": rates,
+                      "published": {"hbm_GBps": HBM_PEAK_GBPS, "mxfp4_TFLOPs": MXFP4_PEAK_TFLOPS,
+                                    "fp8_TFLOPs": FP8_PEAK_TFLOPS,
+                                    "bf16_TFLOPs": BF16_PEAK_TFLOPS}}))
 
 
 def crossover(reps: int = 10) -> None:
@@ -169,11 +252,16 @@ def cpu_model():
 
 
 def usable_cores():
+    """Threads the CPU baseline runs: the cores this process may use, at most
+    16 (the host share of one GPU)."""
+    return max(1, min(affinity_cores(), 16))
+
+
+def affinity_cores():
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
 
 
 def traffic_from_profiles(kernel: str, workload: str, src_sha: str):
@@ -195,10 +283,12 @@ def traffic_from_profiles(kernel: str, workload: str, src_sha: str):
         return None
 
 
-def cpu_baseline(cfg, n_tokens):
-    """The oracle, as it stands, on the first n_tokens tokens of the workload:
-    router + top-k over all experts, the k expert rows (in parallel threads,
-    the C code releases the GIL), combine.  Weight generation is excluded."""
+def cpu_baseline(cfg, n_tokens, n_one_core):
+    """The oracle, as it stands, on the first tokens of the workload: router +
+    top-k over all experts, the k expert rows, combine.  n_tokens tokens run
+    with the k rows of a token in parallel threads (the C code releases the
+    GIL), then n_one_core further tokens on a single thread, the per-core
+    reference.  Weight generation is excluded from the timing."""
     import numpy as np
     import oracle
     from routed_expert_mxfp4_amd import synth
@@ -206,35 +296,43 @@ def cpu_baseline(cfg, n_tokens):
     bias = synth.gen_bias(cfg)
     bias_np = None if bias is None else bias.numpy()
     threads = usable_cores()
+    fp8 = cfg.wfmt == "fp8"
+    gen = synth.gen_experts_fp8 if fp8 else synth.gen_experts
+    erow = oracle.expert_row_fp8 if fp8 else oracle.expert_row
+
+    def token(n, pool):
+        batch, t = (n, 0) if cfg.T == 1 else (0, n)
+        x16 = synth.as_u16(synth.gen_x(cfg, batch, tokens=[t]))
+        t0 = time.perf_counter()
+        lg = oracle.router_logits(x16, wr16, bias_np)
+        ids, w = oracle.topk_softmax(lg, cfg.k)
+        spent = time.perf_counter() - t0
+        W = {k: v.numpy() for k, v in gen(cfg, experts=[int(e) for e in ids[0]]).items()}
+
+        def row(j):
+            return erow(x16[0], W["gu_codes"][j], W["gu_scales"][j],
+                        W["dn_codes"][j], W["dn_scales"][j], cfg.d, cfg.f)[1]
+        t0 = time.perf_counter()
+        rows = pool.map(row, range(cfg.k)) if pool is not None else map(row, range(cfg.k))
+        oracle.combine_token(w[0], np.stack(list(rows)))
+        return spent + time.perf_counter() - t0
+
     spent = 0.0
-    tokens = 0
     with cf.ThreadPoolExecutor(max_workers=threads) as pool:
         for n in range(n_tokens):
-            batch, t = (n, 0) if cfg.T == 1 else (0, n)
-            x16 = synth.as_u16(synth.gen_x(cfg, batch, tokens=[t]))
-            t0 = time.perf_counter()
-            lg = oracle.router_logits(x16, wr16, bias_np)
-            ids, w = oracle.topk_softmax(lg, cfg.k)
-            spent += time.perf_counter() - t0
-            need = [int(e) for e in ids[0]]
-            fp8 = cfg.wfmt == "fp8"
-            gen = synth.gen_experts_fp8 if fp8 else synth.gen_experts
-            W = {k: v.numpy() for k, v in gen(cfg, experts=need).items()}
-            erow = oracle.expert_row_fp8 if fp8 else oracle.expert_row
-
-            def row(j):
-                return erow(x16[0], W["gu_codes"][j], W["gu_scales"][j],
-                            W["dn_codes"][j], W["dn_scales"][j], cfg.d, cfg.f)[1]
-            t0 = time.perf_counter()
-            o = np.stack(list(pool.map(row, range(cfg.k))))
-            oracle.combine_token(w[0], o)
-            spent += time.perf_counter() - t0
-            tokens += 1
-    return {"value": tokens / spent, "unit": "tokens/s", "cores": min(threads, cfg.k),
+            spent += token(n, pool)
+    one = None
+    if n_one_core > 0:
+        s1 = sum(token(n_tokens + n, None) for n in range(n_one_core))
+        one = {"value": n_one_core / s1, "unit": "tokens/s", "cores": 1, "seconds": s1,
+               "sample": "%d further token(s), every step on one thread" % n_one_core}
+    return {"value": n_tokens / spent, "unit": "tokens/s", "cores": min(threads, cfg.k),
             "kind": "oracle",
-            "sample": "%d token(s) of the %s workload, all %d expert rows each, oracle "
-                      "(plain C, fp64) on %s" % (tokens, cfg.name, cfg.k, cpu_model()),
-            "seconds": spent}
+            "sample": "%d token(s) of the %s workload, all %d expert rows each (one thread "
+                      "per row, up to %d at once), oracle (plain C, fp64) on %s"
+                      % (n_tokens, cfg.name, cfg.k, threads, cpu_model()),
+            "seconds": spent, "nproc": os.cpu_count(), "affinity_cores": affinity_cores(),
+            "one_core": one}
 
 
 def main():
@@ -258,8 +356,9 @@ def main():
     if args.crossover:
         crossover()
         return
-    if args.gemv_max_rows is not None:
-        moe.diag_set_gemv_max_rows(args.gemv_max_rows)
+    if args.peaks:
+        peaks()
+        return
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[WORKLOADS[args.workload]]
     if args.steps is None:
@@ -274,7 +373,18 @@ def main():
         print("the FP8 expert variant runs the routed layer in bf16 activations only",
               file=sys.stderr)
         sys.exit(2)
-    mfma = (not fp8) and cfg.T >= MFMA_MIN_T and cfg.d % 512 == 0 and cfg.f % 256 == 0
+    # the expert path the library takes (moe_abi.cpp's choice, mirrored): the
+    # scaled-MFMA GEMMs once some expert can hold more than the crossover's
+    # rows (bf16, canonical store), from MFMA_MIN_T tokens on otherwise; in
+    # such a call experts with at most gemv_max rows stay on the GEMVs
+    shape_ok = cfg.d % 512 == 0 and cfg.f % 256 == 0
+    per_expert = (args.act == "bf16" and not args.packed and cfg.f % 32 == 0 and cfg.d <= 8192
+                  and cfg.f <= 4096)
+    if args.gemv_max_rows is not None:
+        moe.diag_set_gemv_max_rows(args.gemv_max_rows)
+    gemv_max = moe.diag_gemv_max_rows() if per_expert else 0
+    mfma = (not fp8) and shape_ok and cfg.T > FUSE_MAX_T and (
+        cfg.T > gemv_max if per_expert else cfg.T >= MFMA_MIN_T)
     if args.packed and not (mfma and cfg.f % 512 == 0 and not args.tail):
         print("--packed needs a prefill workload on the scaled-MFMA path (d, f % 512 == 0), "
               "without --tail", file=sys.stderr)
@@ -346,7 +456,10 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, dominant kernel timed with HIP events ------------
-    moe.diag_time_kernel(dominant, capacity=max(1, args.steps))
+    # one launch in `every` carries the events (a 1000-step decode run: 125
+    # timed launches), so the events' own cost is not in most steps
+    every = 8 if args.steps >= 200 else 1
+    moe.diag_time_kernel(dominant, capacity=max(1, args.steps), every=every)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(args.warmup, args.steps)
@@ -377,15 +490,22 @@ def main():
     # ---- algorithmic work ------------------------------------------------------------
     ids_probe = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
     per_expert_gu = cfg.gate_up_bytes
-    touched = []
+    touched, on_mfma, rows_mfma = [], [], []
     for b in range(min(n_batches, 64)):
         if args.tail:
             layer.forward(xs[b], out=y, topk_ids=ids_probe)
         else:
             layer.forward(xs[b], y=y, topk_ids=ids_probe)
-        touched.append(torch.unique(ids_probe).numel())
+        counts = torch.bincount(ids_probe.flatten().long(), minlength=cfg.E)
+        touched.append(int((counts > 0).sum()))
+        big = counts > gemv_max
+        on_mfma.append(int(big.sum()))
+        rows_mfma.append(int(counts[big].sum()))
     torch.cuda.synchronize()
     mean_touched = sum(touched) / len(touched)
+    # the dominant GEMM's own share: the experts on the MFMA tiles and their rows
+    mean_on_mfma = sum(on_mfma) / len(on_mfma)
+    mean_rows_mfma = sum(rows_mfma) / len(rows_mfma)
     avg_launch_s = (dom_ms / dom_n) * 1e-3 if dom_n else float("nan")
     pl = sorted(per_launch)
 
@@ -410,8 +530,8 @@ def main():
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
     elif mfma and layer_flops / layer_bytes >= MXFP4_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3:
         # past the ridge (10.1 PFLOP/s / 8 TB/s = 1262 flop/B): the matrix
-        # cores bound the gate/up GEMM (every routed row times [2f x d])
-        flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
+        # cores bound the gate/up GEMM (its rows times [2f x d])
+        flops_per_launch = 2.0 * mean_rows_mfma * 2 * cfg.f * cfg.d
         achieved = flops_per_launch / avg_launch_s / 1e12
         src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_mfma.hip")
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -427,8 +547,8 @@ def main():
         # below the ridge: HBM bounds the layer (every touched expert's
         # weights read once); the gate/up GEMM's bytes are its experts'
         # gate/up matrices, its flops are reported beside them
-        bytes_per_launch = mean_touched * per_expert_gu
-        flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
+        bytes_per_launch = mean_on_mfma * per_expert_gu
+        flops_per_launch = 2.0 * mean_rows_mfma * 2 * cfg.f * cfg.d
         achieved = bytes_per_launch / avg_launch_s / 1e9
         src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_mfma.hip")
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
@@ -437,6 +557,8 @@ def main():
                     "traffic": traffic_from_profiles(
                         dominant, args.workload + ("-packed" if args.packed else ""), sha),
                     "algorithmic_bytes_per_launch": bytes_per_launch,
+                    "experts_on_mfma_per_launch": mean_on_mfma,
+                    "experts_on_gemv_per_launch": mean_touched - mean_on_mfma,
                     "layer_flop_per_byte": layer_flops / layer_bytes,
                     "mxfp4_tflops": flops_per_launch / avg_launch_s / 1e12,
                     "mxfp4_frac": flops_per_launch / avg_launch_s / 1e12 / MXFP4_PEAK_TFLOPS,
@@ -455,6 +577,21 @@ def main():
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
 
     roofline["launch_us_percentiles"] = launch_pct
+    roofline["timed_every"] = every
+    # the same launch against what this GPU measurably sustains for its bound
+    if roofline["bound"] == "hbm":
+        mp, blocks = stream_read_gbps(int(roofline["algorithmic_bytes_per_launch"]))
+        roofline["measured_peak"] = {
+            "value": mp, "unit": "GB/s", "frac": roofline["achieved"] / mp,
+            "what": "one launch of a plain streaming read of the same bytes (%d blocks; "
+                    "bench.py --peaks)" % blocks}
+    elif roofline["bound"] == "mfma":
+        kind = "fp6xfp4"
+        mp = mfma_rate_tflops(kind)
+        roofline["measured_peak"] = {
+            "value": mp, "unit": "TFLOP/s", "frac": roofline["achieved"] / mp,
+            "what": "%s scaled 16x16x128 matrix instructions issued from registers "
+                    "(bench.py --peaks)" % kind}
     out = {
         "metric": "MoE-layer tokens/s + expert-weight GB/s (decode) / MXFP4 TFLOP/s (prefill), 1 GPU",
         "value": value,
@@ -495,7 +632,7 @@ def main():
         "breakdown": breakdown,
     }
     if args.cpu_sample > 0:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample, args.cpu_one_core_sample)
         if args.tail:
             out["cpu_baseline"]["note"] = "the routed layer's oracle (the block's dominant work)"
     print(json.dumps(out))

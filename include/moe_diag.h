@@ -19,6 +19,7 @@
 #ifndef ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 #define ROUTED_EXPERT_MXFP4_MOE_DIAG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -54,6 +55,12 @@ int moe_diag_mx_split_e2m3(const void *in, int in_is_bf16, int rows, int K, uint
  * capacity < 0. */
 int moe_diag_time_kernel(const char *kernel, int capacity);
 
+/* As moe_diag_time_kernel, but only the 1st, (every+1)-th, (2 every+1)-th,
+ * ... launch of the kernel is timed (every >= 1), so that a long run of
+ * short launches carries the events' own cost on a sample of them only.
+ * Returns 0, or -1 as moe_diag_time_kernel or if every < 1. */
+int moe_diag_time_kernel_every(const char *kernel, int capacity, int every);
+
 /* Sum of the elapsed times (ms) of the recorded launches and their count.
  * Call only after the device has been synchronised.  Clears
  * the records (timing stays on).  Returns 0, or -1 on a HIP error. */
@@ -65,6 +72,33 @@ int moe_diag_kernel_time(double *total_ms, long long *launches);
  * like moe_diag_kernel_time.  Returns 0, or -1 on a HIP error or bad
  * arguments. */
 int moe_diag_kernel_times(double *ms_out, int cap, long long *launches);
+
+/* Measured ceilings, for reporting each kernel's fraction of what this GPU
+ * sustains next to the published peaks.
+ *
+ * moe_diag_stream_read: one launch that reads `bytes` bytes at `src`
+ * (device memory, 16-byte aligned, bytes a multiple of 16) with 16-byte
+ * loads, eight in flight per thread, over `blocks` blocks of 256 threads,
+ * and writes an XOR checksum per block to out[0 .. blocks-1] (device
+ * memory).  Time it with events on hip_stream: bytes / time is the
+ * streaming-read bandwidth a kernel reading the same bytes in one launch
+ * can reach.
+ *
+ * moe_diag_mfma_rate: one launch of `blocks` blocks of four waves; each
+ * wave issues iters x 4 independent matrix instructions from registers (no
+ * memory traffic) and writes one sum to out[4 blocks] (device memory).
+ * kind 0: scaled 16x16x128 with A FP6 E2M3, B FP4 E2M1 (the expert GEMMs'
+ * split activations x weights); 1: A FP8 E4M3, B FP4; 2: FP4 x FP4;
+ * 3: FP8 x FP8; 4: bf16 32x32x16 (the shared expert's GEMMs); 5: FP6 x
+ * FP4 and 6: FP4 x FP4 in the 32x32x64 scaled shape.  Flops per
+ * instruction: 2*16*16*128 for kinds 0-3, 2*32*32*16 for kind 4,
+ * 2*32*32*64 for kinds 5 and 6.
+ *
+ * Both are asynchronous on hip_stream; return 0, or -1 on bad arguments or
+ * a launch error. */
+int moe_diag_stream_read(const void *src, size_t bytes, uint32_t *out, int blocks,
+                         void *hip_stream);
+int moe_diag_mfma_rate(int kind, int blocks, int iters, float *out, void *hip_stream);
 
 /* The per-expert path choice of the bf16 layer: in a call on the
  * scaled-MFMA expert path, experts with at most this many rows take the

@@ -14,7 +14,6 @@
 // Down: o[p][m] = h[p] . Wd[m] -> bf16 rows_out (expert-major), or fused
 // with the weighted combine per token for small T.
 #include "moe_internal.hpp"
-#include "mx_split.hpp"
 #include "select_dev.hpp"
 
 namespace moe {
@@ -454,118 +453,6 @@ __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
     }
 }
 
-// The one-token gate/up kernel feeding the matrix-core down pass: 96 output
-// pairs per block, three whole MX blocks of h, eight waves (12 pairs each),
-// so 16 selected experts at f = 1536 make 256 blocks, one per CU.  Top-k,
-// softmax and grouping as in gate_up_regx_token_kernel.  The epilogue
-// multiplies the block's h by its expert's routing weight and splits each
-// 32-element block into two MX E2M3 terms: record (a * f/32 + block) of hq,
-// 64 bytes: hi codes [0, 24), lo codes [24, 48), hi E8M0 at 48, lo at 49.
-constexpr int kSplitPairs = 96;
-constexpr int kSplitRec = 64;
-
-template <int NBL>
-__global__ __launch_bounds__(512) void gate_up_token_split_kernel(
-    const float *__restrict__ logits, const uint16_t *__restrict__ x, ExpertArgs W,
-    int32_t *__restrict__ ids, float *__restrict__ tw, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
-    int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, uint8_t *__restrict__ hq, int d,
-    int E, int k, int f) {
-    extern __shared__ uint4 xs[];                 // the token row, d/8 x 16 B, + 1 spare
-    __shared__ __align__(16) uint32_t tsc[kTopkScratch];
-    __shared__ int sel[32];                       // selected experts, ascending
-    __shared__ float selw[32];                    // and their routing weights
-    __shared__ float hs[kSplitPairs];
-    const int lane = threadIdx.x & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int nvec = d >> 3;
-    const bool first = blockIdx.x == 0 && blockIdx.y == 0;
-    {
-        const uint4 *xrow = reinterpret_cast<const uint4 *>(x);
-        uint4 tmp[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            tmp[j] = xrow[min((int)threadIdx.x + 512 * j, nvec - 1)];
-        loads_done(tmp);                            // all loads before any store
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {               // spare slot: no branch per store
-            const int i = (int)threadIdx.x + 512 * j;
-            xs[i < nvec ? i : nvec] = tmp[j];
-        }
-    }
-    if (wid == 0) {
-        int e;
-        float wt;
-        wave_topk_softmax<16>(logits, E, k, tsc, &e, &wt);
-        int rank = 0;                               // place among the selected
-        for (int i = 0; i < k; ++i) rank += __shfl(e, i) < e ? 1 : 0;
-        if (lane < k) {
-            sel[rank] = e;
-            selw[rank] = wt;
-            if (first) {
-                ids[lane] = e;
-                tw[lane] = wt;
-                sorted_rows[rank] = lane;
-                row_pos[lane] = rank;
-                plan[1 + rank] = e;
-            }
-        }
-        if (first && lane == 0) plan[0] = k;
-    }
-    __syncthreads();
-    if (first) {
-        for (int c = threadIdx.x; c <= E; c += 512) {
-            int below = 0, hit = 0;
-            for (int i = 0; i < k; ++i) {
-                below += sel[i] < c ? 1 : 0;
-                hit += sel[i] == c ? 1 : 0;
-            }
-            offsets[c] = below;
-            if (c < E) counts[c] = hit;
-        }
-    }
-    const int a = blockIdx.y;
-    const int e = sel[a];
-    if ((unsigned)e >= (unsigned)E) return;
-    const int nblk = d >> 5;
-    const uint32_t code_row = (uint32_t)d >> 1;
-    const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
-    const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
-    constexpr int kPerWave = kSplitPairs / 8;     // pairs n_base + wid + 8 q
-    const int n_base = blockIdx.x * kSplitPairs + wid;
-    PairBuf<NBL> A, B;
-    load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);
-#pragma unroll 1
-    for (int q = 0; q < kPerWave; q += 2) {
-        load_pair<NBL>(codes, scales, n_base + 8 * (q + 1), f, lane, nblk, code_row, B);
-        __builtin_amdgcn_sched_barrier(0);
-        const float va = pair_h<NBL>(A, xs, lane, nblk);
-        if (lane == 0) hs[wid + 8 * q] = va;
-        __builtin_amdgcn_sched_barrier(0);
-        if (q + 2 < kPerWave)
-            load_pair<NBL>(codes, scales, n_base + 8 * (q + 2), f, lane, nblk, code_row, A);
-        __builtin_amdgcn_sched_barrier(0);
-        const float vb = pair_h<NBL>(B, xs, lane, nblk);
-        if (lane == 0) hs[wid + 8 * (q + 1)] = vb;
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-    // three MX blocks of h' = w h: one lane each
-    if (threadIdx.x < kSplitPairs / 32) {
-        const float wa = selw[a];
-        float v[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = wa * hs[32 * threadIdx.x + i];
-        const SplitBlock sb = split_block32(v);
-        const size_t rec = (size_t)a * (f >> 5) + (size_t)blockIdx.x * (kSplitPairs / 32) + threadIdx.x;
-        uint4 *dst = reinterpret_cast<uint4 *>(hq + rec * kSplitRec);
-        dst[0] = uint4{sb.hi[0], sb.hi[1], sb.hi[2], sb.hi[3]};
-        dst[1] = uint4{sb.hi[4], sb.hi[5], sb.lo[0], sb.lo[1]};
-        dst[2] = uint4{sb.lo[2], sb.lo[3], sb.lo[4], sb.lo[5]};
-        dst[3] = uint4{sb.scales, 0u, 0u, 0u};
-    }
-}
-
 // Down rows for one h row: lane l owns the MX blocks b = l + 64 i (i < NBLD)
 // of f, so its slice of h (32 floats per block) is loaded once into
 // registers and reused for every output row; rows go in batches of 8 whose
@@ -873,38 +760,6 @@ hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertAr
                                           row_pos, plan, h, d, E, k, f, s);
     return launch_gate_up_token_p<32>(logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
                                       plan, h, d, E, k, f, s);
-}
-
-// f a multiple of 96 (whole blocks of pairs) and of 512 (whole 16-byte
-// scale pieces per down row), f / 128 steps instantiated (12 or 24), h' of
-// all selected experts within 64 KB of LDS.
-bool decode_mfma_ok(int d, int E, int k, int f) {
-    const int nbl = (d / 32 + 63) / 64;
-    return k <= 32 && k <= E && E <= 1024 && f % kSplitPairs == 0 && f % 512 == 0 &&
-           (f / 128 == 12 || f / 128 == 24) && (size_t)k * (f / 32) * kSplitRec <= 65536 &&
-           nbl <= 4 && d <= 8192 && (d % 28 == 0 || d % 32 == 0) && d % 16 == 0;
-}
-
-size_t decode_mfma_ws_bytes(int k, int f) { return (size_t)k * (f / 32) * kSplitRec; }
-
-hipError_t launch_gate_up_token_split(const float *logits, const uint16_t *x, ExpertArgs w,
-                                      int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
-                                      int32_t *sorted_rows, int32_t *row_pos, int32_t *plan,
-                                      uint8_t *hq, int d, int E, int k, int f, hipStream_t s) {
-    const int nbl = (d / 32 + 63) / 64;
-    const dim3 grid(f / kSplitPairs, k);
-    const size_t lds = (size_t)d * 2 + 16;
-    if (nbl == 1)
-        return timed_launch("gemv_gate_up", gate_up_token_split_kernel<1>, grid, dim3(512), lds,
-                            s, logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan,
-                            hq, d, E, k, f);
-    if (nbl == 2)
-        return timed_launch("gemv_gate_up", gate_up_token_split_kernel<2>, grid, dim3(512), lds,
-                            s, logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan,
-                            hq, d, E, k, f);
-    return timed_launch("gemv_gate_up", gate_up_token_split_kernel<4>, grid, dim3(512), lds, s,
-                        logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, hq, d,
-                        E, k, f);
 }
 
 // rows per batch and batch buffers of the fused down + combine

@@ -153,6 +153,8 @@ struct Diag {
     std::string name;
     std::vector<hipEvent_t> ev;       // [2 * capacity]: start, stop pairs
     int used = 0;
+    int every = 1;                    // time one launch in `every`
+    long long seen = 0;               // launches of the named kernel so far
 };
 Diag g_diag;
 
@@ -254,7 +256,9 @@ namespace moe {
 DiagScope::DiagScope(const char *kernel, hipStream_t s) : s_(s) {
     if (!g_diag.active.load(std::memory_order_acquire)) return;
     std::lock_guard<std::mutex> lk(g_diag.mu);
-    if (g_diag.name != kernel || 2 * (g_diag.used + 1) > (int)g_diag.ev.size()) return;
+    if (g_diag.name != kernel) return;
+    if (g_diag.seen++ % g_diag.every != 0) return;
+    if (2 * (g_diag.used + 1) > (int)g_diag.ev.size()) return;
     hipEvent_t start = g_diag.ev[2 * g_diag.used];
     stop_ = g_diag.ev[2 * g_diag.used + 1];
     ++g_diag.used;
@@ -267,7 +271,9 @@ void diag_launch_events(const char *kernel, hipEvent_t *start, hipEvent_t *stop)
     *start = *stop = nullptr;
     if (!g_diag.active.load(std::memory_order_acquire)) return;
     std::lock_guard<std::mutex> lk(g_diag.mu);
-    if (g_diag.name != kernel || 2 * (g_diag.used + 1) > (int)g_diag.ev.size()) return;
+    if (g_diag.name != kernel) return;
+    if (g_diag.seen++ % g_diag.every != 0) return;
+    if (2 * (g_diag.used + 1) > (int)g_diag.ev.size()) return;
     *start = g_diag.ev[2 * g_diag.used];
     *stop = g_diag.ev[2 * g_diag.used + 1];
     ++g_diag.used;
@@ -360,17 +366,6 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
         uint16_t *xr = reinterpret_cast<uint16_t *>(base + L.ffn + F.xr);
         e = moe::launch_mx_round_bf16(x, D.T, D.d, xr, s);
         xa = xr;
-    }
-    // one token in bf16: gate/up writes h' = w h split in two MX terms, and
-    // the down pass with the combine runs on the matrix cores
-    if (token_fused && D.act == MOE_ACT_BF16 && moe::decode_mfma_ok(D.d, D.E, D.k, D.f)) {
-        uint8_t *hq = reinterpret_cast<uint8_t *>(h);
-        if (e == hipSuccess)
-            e = moe::launch_gate_up_token_split(logits, x, W, ids, tw, counts, offsets,
-                                                sorted_rows, row_pos, plan, hq, D.d, D.E, D.k,
-                                                D.f, s);
-        if (e == hipSuccess) e = moe::launch_down_token_mfma(hq, W, plan, y, D.d, D.E, D.k, D.f, s);
-        return e;
     }
     if (e == hipSuccess) {
         e = token_fused ? moe::launch_gate_up_token(logits, xa, W, ids, tw, counts, offsets,
@@ -943,11 +938,17 @@ int moe_diag_gemv_max_rows(void) {
 }
 
 int moe_diag_time_kernel(const char *kernel, int capacity) {
+    return moe_diag_time_kernel_every(kernel, capacity, 1);
+}
+
+int moe_diag_time_kernel_every(const char *kernel, int capacity, int every) {
     try {
-        if (capacity < 0) return -1;
+        if (capacity < 0 || every < 1) return -1;
         std::lock_guard<std::mutex> lk(g_diag.mu);
         g_diag.active.store(false, std::memory_order_release);
         g_diag.used = 0;
+        g_diag.every = every;
+        g_diag.seen = 0;
         g_diag.name = kernel ? kernel : "";
         while ((int)g_diag.ev.size() < 2 * capacity) {
             hipEvent_t ev;

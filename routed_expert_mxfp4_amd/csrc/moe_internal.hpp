@@ -226,27 +226,14 @@ hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertAr
 hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets,
                             const int32_t *plan, uint16_t *rows_out, int T, int d, int E,
                             int k, int f, hipStream_t s);
-// One token on the matrix cores (bf16 activations): gate/up + SwiGLU with
-// the top-k and grouping inside (as launch_gate_up_token), whose epilogue
-// writes h' = w_a * h_a split into two MX E2M3 terms per 32 elements
-// (hq: [k][f/32] records of 64 bytes: hi codes, lo codes, hi and lo E8M0);
-// then the down GEMV of every selected expert with the combine folded into
-// its accumulation, y bf16 [d].  Need decode_mfma_ok.
-bool decode_mfma_ok(int d, int E, int k, int f);
-size_t decode_mfma_ws_bytes(int k, int f);
-hipError_t launch_gate_up_token_split(const float *logits, const uint16_t *x, ExpertArgs w,
-                                      int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
-                                      int32_t *sorted_rows, int32_t *row_pos, int32_t *plan,
-                                      uint8_t *hq, int d, int E, int k, int f, hipStream_t s);
-hipError_t launch_down_token_mfma(const uint8_t *hq, ExpertArgs w, const int32_t *plan,
-                                  uint16_t *y, int d, int E, int k, int f, hipStream_t s);
 
 // Measured ceilings (peaks.hip): one streaming read of `bytes` (a multiple
 // of 16, src 16-byte aligned) over `blocks` blocks of 256 threads, a checksum
 // per block into out[blocks]; and `iters` x 4 independent matrix
 // instructions per wave on `blocks` blocks of four waves, one sum per wave
 // into out[4 blocks].  kind: 0 FP6 E2M3 x FP4, 1 FP8 E4M3 x FP4, 2 FP4 x FP4,
-// 3 FP8 x FP8 (scaled 16x16x128), 4 bf16 (32x32x16).
+// 3 FP8 x FP8 (scaled 16x16x128), 4 bf16 (32x32x16), 5 FP6 x FP4 and 6 FP4
+// x FP4 (scaled 32x32x64).
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *out, int blocks,
                               hipStream_t s);
 hipError_t launch_mfma_rate(int kind, int blocks, int iters, float *out, hipStream_t s);

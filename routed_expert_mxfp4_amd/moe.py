@@ -58,7 +58,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_rout
            "moe_fp8_workspace_bytes", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
            "moe_prepack_experts", "moe_layer_forward_packed", "moe_diag_kernel_times",
            "moe_layer_forward_noalloc", "moe_diag_set_gemv_max_rows",
-           "moe_diag_gemv_max_rows")
+           "moe_diag_gemv_max_rows", "moe_diag_stream_read", "moe_diag_mfma_rate",
+           "moe_diag_time_kernel_every")
 
 _lib = None
 
@@ -113,6 +114,8 @@ def lib():
         L.moe_block_forward.argtypes = [DP, P, TP, P, P, EP, P, P, P, P, S, P]
         L.moe_diag_time_kernel.restype = I
         L.moe_diag_time_kernel.argtypes = [ctypes.c_char_p, I]
+        L.moe_diag_time_kernel_every.restype = I
+        L.moe_diag_time_kernel_every.argtypes = [ctypes.c_char_p, I, I]
         L.moe_diag_mx_split_e2m3.restype = I
         L.moe_diag_mx_split_e2m3.argtypes = [P, I, I, I, P, P]
         L.moe_diag_kernel_times.restype = I
@@ -122,6 +125,10 @@ def lib():
         L.moe_diag_set_gemv_max_rows.argtypes = [I]
         L.moe_diag_gemv_max_rows.restype = I
         L.moe_diag_gemv_max_rows.argtypes = []
+        L.moe_diag_stream_read.restype = I
+        L.moe_diag_stream_read.argtypes = [P, S, P, I, P]
+        L.moe_diag_mfma_rate.restype = I
+        L.moe_diag_mfma_rate.argtypes = [I, I, I, P, P]
         L.moe_diag_kernel_time.restype = I
         L.moe_diag_kernel_time.argtypes = [ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_longlong)]
@@ -129,11 +136,12 @@ def lib():
     return _lib
 
 
-def diag_time_kernel(kernel, capacity: int = 4096):
-    """Time every launch of one named kernel with HIP events (None stops)."""
+def diag_time_kernel(kernel, capacity: int = 4096, every: int = 1):
+    """Time every launch (or one launch in ``every``) of one named kernel
+    with HIP events (None stops)."""
     name = None if kernel is None else kernel.encode()
-    if lib().moe_diag_time_kernel(name, int(capacity)) != 0:
-        raise RuntimeError("moe_diag_time_kernel failed")
+    if lib().moe_diag_time_kernel_every(name, int(capacity), int(every)) != 0:
+        raise RuntimeError("moe_diag_time_kernel_every failed")
 
 
 def diag_kernel_time():
@@ -164,6 +172,43 @@ def diag_set_gemv_max_rows(rows):
 
 def diag_gemv_max_rows() -> int:
     return int(lib().moe_diag_gemv_max_rows())
+
+
+MFMA_RATE_KINDS = {"fp6xfp4": 0, "fp8xfp4": 1, "fp4xfp4": 2, "fp8xfp8": 3, "bf16": 4,
+                   "fp6xfp4_32x32x64": 5, "fp4xfp4_32x32x64": 6}
+MFMA_RATE_FLOPS = {0: 2 * 16 * 16 * 128, 1: 2 * 16 * 16 * 128, 2: 2 * 16 * 16 * 128,
+                   3: 2 * 16 * 16 * 128, 4: 2 * 32 * 32 * 16, 5: 2 * 32 * 32 * 64,
+                   6: 2 * 32 * 32 * 64}
+
+
+def diag_stream_read(src, nbytes: int, out, blocks: int, stream=None):
+    """One streaming-read launch over the first ``nbytes`` bytes of the device
+    tensor ``src``; ``out`` (int32, >= blocks elements) takes a checksum per
+    block."""
+    import torch
+    if nbytes > src.numel() * src.element_size() or out.numel() < blocks:
+        raise ValueError("buffer too small")
+    with torch.cuda.stream(_on(stream)) as _:
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if lib().moe_diag_stream_read(ctypes.c_void_p(src.data_ptr()), int(nbytes),
+                                      ctypes.c_void_p(out.data_ptr()), int(blocks), s) != 0:
+            raise RuntimeError("moe_diag_stream_read failed")
+
+
+def diag_mfma_rate(kind: str, blocks: int, iters: int, out, stream=None):
+    """One launch issuing blocks * 4 waves * iters * 4 matrix instructions of
+    the given kind; ``out`` (float32, >= 4 blocks elements) takes one sum per
+    wave.  Returns the launch's flops."""
+    import torch
+    k = MFMA_RATE_KINDS[kind]
+    if out.numel() < 4 * blocks:
+        raise ValueError("out too small")
+    with torch.cuda.stream(_on(stream)) as _:
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if lib().moe_diag_mfma_rate(k, int(blocks), int(iters), ctypes.c_void_p(out.data_ptr()),
+                                    s) != 0:
+            raise RuntimeError("moe_diag_mfma_rate failed")
+    return float(blocks) * 4 * iters * 4 * MFMA_RATE_FLOPS[k]
 
 
 def diag_mx_split_e2m3(rows_tensor, stream=None):

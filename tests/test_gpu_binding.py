@@ -53,20 +53,24 @@ def test_layer_on_side_stream(dev):
 
 
 def test_layer_workspace_grows_by_bytes(dev):
+    # The activation-MX mode switches from the GEMVs (fp32 h of every row)
+    # to the scaled-MFMA path at 128 tokens, so 127 tokens need more
+    # workspace than 128: a Layer reserved for 128 must grow for 127.
     moe = _moe()
+    act = moe.ACT_MX_E2M3
     cfg = _small_cfg(128, 512, 16, 4, 256, 402)
     big_t, small_t = 128, 127
-    n_big = moe.moe_workspace_bytes(moe.dims_of(big_t, cfg.d, cfg.E, cfg.k, cfg.f),
+    n_big = moe.moe_workspace_bytes(moe.dims_of(big_t, cfg.d, cfg.E, cfg.k, cfg.f, act),
                                     moe.ENTRY_LAYER_FORWARD)
-    n_small = moe.moe_workspace_bytes(moe.dims_of(small_t, cfg.d, cfg.E, cfg.k, cfg.f),
+    n_small = moe.moe_workspace_bytes(moe.dims_of(small_t, cfg.d, cfg.E, cfg.k, cfg.f, act),
                                       moe.ENTRY_LAYER_FORWARD)
     assert n_small > n_big, "shape no longer exercises a smaller workspace at larger T"
     L = synth.gen_layer(cfg)
     x, wr = L["x"].to(dev), L["router_w"].to(dev)
     ex = {n: L[n].to(dev) for n in ("gu_codes", "gu_scales", "dn_codes", "dn_scales")}
-    layer = moe.Layer(ex, wr, cfg.k, None, T=big_t)
+    layer = moe.Layer(ex, wr, cfg.k, None, T=big_t, act=act)
     layer.forward(x)
     y = layer.forward(x[:small_t].contiguous())
-    y_ref = moe.moe_layer_forward(x[:small_t].contiguous(), wr, ex, cfg.k)
+    y_ref = moe.moe_layer_forward(x[:small_t].contiguous(), wr, ex, cfg.k, act=act)
     torch.cuda.synchronize()
     assert torch.equal(y, y_ref)

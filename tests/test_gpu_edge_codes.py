@@ -5,8 +5,8 @@ The workloads draw scale codes 123..127 only.  OCP MX E8M0 code c means
 255 is NaN.  These cases put such codes into small layers on each path the
 library takes:
 
-  one token (top-k and grouping inside the gate/up GEMV, fused down+combine,
-  on the vector ALU or, at f = 1536, on the matrix cores),
+  one token (top-k and grouping inside the gate/up GEMV, fused down+combine;
+  at f = 128 and at the K3 width f = 1536),
   few tokens (one-launch top-k + grouping, grouped GEMV, fused down+combine),
   more tokens (grouped GEMVs, separate combine),
   the scaled-MFMA GEMMs on the canonical store and on the packed store,
@@ -40,7 +40,7 @@ TOL = 1e-2
 PATHS = [
     # (name, T, d, E, k, f, seed, packed)
     ("one_token", 1, 256, 16, 4, 128, 301, False),
-    ("one_token_mfma_down", 1, 512, 16, 4, 1536, 306, False),
+    ("one_token_f1536", 1, 512, 16, 4, 1536, 306, False),
     ("few_tokens", 3, 256, 16, 4, 128, 302, False),
     ("grouped_gemv", 20, 256, 16, 4, 128, 303, False),
     ("mfma", 160, 512, 8, 2, 256, 304, False),

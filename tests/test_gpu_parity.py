@@ -159,7 +159,7 @@ ONE_TOKEN_CASES = [
     (1, 192, 40, 5, 96, 32),         # chunk length 3, E not a multiple of 64
     (1, 256, 16, 16, 96, 33),        # k = E: every expert selected
     (1, 256, 64, 8, 64, 34),         # f not a multiple of 48: 32 pairs per block
-    # f = 1536: the down pass and the combine on the matrix cores
+    # f = 1536, the K3 width: 48 MX blocks of h per down row
     (1, 512, 64, 8, 1536, 35),
     (1, 256, 40, 16, 1536, 36),      # k = 16, chunk length 4
     (1, 192, 20, 20, 1536, 37),      # k = E, odd chunk length
