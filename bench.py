@@ -40,11 +40,10 @@ WORKLOADS = {"tiny": 0, "decode": 1, "batched-decode": 2, "zipf-prefill": 3, "lo
 DEFAULT_STEPS = {"tiny": 1000, "decode": 1000, "batched-decode": 200, "zipf-prefill": 20,
                  "long-prefill": 5, "mimo-decode": 1000, "mimo-prefill": 20, "fp8-decode": 1000,
                  "fp8-prefill": 3}
-VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published (the FP8 prefill floor's bound)
 KERNELS = ("router_logits", "topk_softmax", "router_norms", "router_filter_gemm",
            "router_select", "router_refine", "permute", "topk_permute", "gemv_gate_up",
            "down_combine", "gemv_down", "mx_split_x", "gate_up_mfma", "down_mfma",
-           "combine", "fp8_gate_up", "fp8_down")
+           "combine", "fp8_plan", "fp8_gate_up", "fp8_down")
 # the pre-norm block's own kernels (--tail)
 TAIL_KERNELS = ("rmsnorm", "shared_gate_up", "shared_down_add", "shared_gemm_gate_up",
                 "shared_gemm_down")
@@ -517,17 +516,27 @@ def main():
     layer_bytes = mean_touched * cfg.expert_bytes
     layer_flops = 2.0 * cfg.T * cfg.k * 3 * cfg.d * cfg.f
     if fp8 and cfg.T >= MFMA_MIN_T:
-        # the FP8 prefill floor: the dequant-GEMV's dot products on the VALU
+        # FP8 experts on the bf16 matrix cores (codes converted exactly to
+        # bf16): the gate/up GEMM against the bf16 matrix peak past the bf16
+        # ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B), else against HBM
         flops_per_launch = 2.0 * cfg.T * cfg.k * 2 * cfg.f * cfg.d
-        achieved = flops_per_launch / avg_launch_s / 1e12
-        src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_fp8.hip")
+        bytes_per_launch = mean_touched * per_expert_gu
+        tflops = flops_per_launch / avg_launch_s / 1e12
+        src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_fp8_mfma.hip")
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        roofline = {"bound": "alu", "kernel": dominant, "achieved": achieved,
-                    "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / VALU_FP32_PEAK_TFLOPS,
-                    "traffic": traffic_from_profiles(dominant, args.workload, sha),
-                    "algorithmic_flops_per_launch": flops_per_launch,
-                    "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
+        common = {"kernel": dominant, "traffic": traffic_from_profiles(dominant, args.workload, sha),
+                  "algorithmic_flops_per_launch": flops_per_launch,
+                  "algorithmic_bytes_per_launch": bytes_per_launch,
+                  "layer_flop_per_byte": layer_flops / layer_bytes,
+                  "bf16_tflops": tflops, "bf16_frac": tflops / BF16_PEAK_TFLOPS,
+                  "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
+        if layer_flops / layer_bytes >= BF16_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3:
+            roofline = dict(common, bound="mfma", achieved=tflops, peak=BF16_PEAK_TFLOPS,
+                            unit="TFLOP/s", frac=tflops / BF16_PEAK_TFLOPS)
+        else:
+            achieved = bytes_per_launch / avg_launch_s / 1e9
+            roofline = dict(common, bound="hbm", achieved=achieved, peak=HBM_PEAK_GBPS,
+                            unit="GB/s", frac=achieved / HBM_PEAK_GBPS)
     elif mfma and layer_flops / layer_bytes >= MXFP4_PEAK_TFLOPS / HBM_PEAK_GBPS * 1e3:
         # past the ridge (10.1 PFLOP/s / 8 TB/s = 1262 flop/B): the matrix
         # cores bound the gate/up GEMM (its rows times [2f x d])
@@ -586,7 +595,7 @@ def main():
             "what": "one launch of a plain streaming read of the same bytes (%d blocks; "
                     "bench.py --peaks)" % blocks}
     elif roofline["bound"] == "mfma":
-        kind = "fp6xfp4"
+        kind = "bf16" if fp8 else "fp6xfp4"
         mp = mfma_rate_tflops(kind)
         roofline["measured_peak"] = {
             "value": mp, "unit": "TFLOP/s", "frac": roofline["achieved"] / mp,
@@ -614,8 +623,8 @@ def main():
                                 "same bytes)" if args.packed else "")),
                    "activations": ("MX E2M3, one term per 32 (activation-MX mode)" if act
                                    else "bf16"), "accumulate": "fp32",
-                   "expert_path": ("FP8 dequant-GEMV" + (" (prefill floor)" if cfg.T >= MFMA_MIN_T
-                                                          else "") if fp8 else
+                   "expert_path": (("FP8 codes -> bf16 matrix-core GEMMs" if cfg.T >= MFMA_MIN_T
+                                    else "FP8 dequant-GEMV") if fp8 else
                                    "scaled MFMA" if mfma else "GEMV")},
         "block": (None if not args.tail else {
             "entry": "moe_block_forward",

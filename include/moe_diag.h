@@ -12,7 +12,9 @@
  * FFN, with its small experts' GEMVs), its parts "mx_split_x",
  * "gate_up_mfma" (which also splits h) and "down_mfma", and "mx_round" (the activation-MX mode's
  * rounding of x and h on the GEMV paths); for FP8 experts "fp8_gate_up" and
- * "fp8_down"; for the pre-norm block "rmsnorm", "shared_gate_up",
+ * "fp8_down" (GEMVs for few tokens, matrix-core GEMMs from 128 on) and
+ * "fp8_plan" (the GEMMs' row tiles); "stream_read" and "mfma_rate" (the
+ * measured ceilings below); for the pre-norm block "rmsnorm", "shared_gate_up",
  * "shared_down_add", "shared_gemm_gate_up" (which also applies the SwiGLU)
  * and "shared_gemm_down".
  */

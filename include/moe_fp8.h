@@ -18,9 +18,13 @@
  * layout of block-scaled official FP8 checkpoints).  3*d*f bytes of codes
  * per expert, twice the MXFP4 store.
  *
- * Every T runs one grouped dequant-GEMV (bf16 weights exist only in
- * registers, per tile in flight); at prefill sizes that is the floor, not a
- * matrix-core path.  Conventions are those of moe.h (device pointers owned
+ * Below 128 tokens the experts run as grouped dequant-GEMVs (bf16 weights
+ * exist only in registers, per tile in flight).  From 128 tokens on they
+ * run as grouped GEMMs on the bf16 matrix cores: weight tiles are
+ * converted exactly to bf16 on their way into LDS (every E4M3FN value is a
+ * bf16 value), activations are used as given, and each 128 x 128 block
+ * scale multiplies its 128-element K chunk's fp32 partial sums; h is
+ * rounded to bf16 between the two GEMMs.  Conventions are those of moe.h (device pointers owned
  * by the caller, asynchronous on hip_stream, validation before any launch,
  * T == 0 a no-op, deterministic).  Also: d % 128 == 0, f % 128 == 0,
  * dims->act == MOE_ACT_BF16 (else MOE_ERR_UNSUPPORTED), codes and scales

@@ -4,14 +4,14 @@
 //
 // The pages' FP8 lane pairs an exhaustive OCP E4M3FN oracle with a fused
 // GEMV and a bounded BF16-dequant prefill floor (Moonshine README, "GLM 5.3
-// Flash status").  Here one grouped dequant-GEMV serves every T: each wave
+// Flash status").  Here a grouped dequant-GEMV serves fewer than 128
+// tokens (ffn_fp8_mfma.hip takes over from there): each wave
 // streams whole weight rows with 16-byte loads (16 codes per lane), gfx950
 // converts code pairs exactly to bf16 (against bf16 x) or fp32 (against fp32
-// h) -- the bf16 copy of a weight lives only in registers, so the dequant is
-// bounded to the tile in flight -- and each 16-element partial sum is
-// multiplied by its block's fp32 scale.  Every decoded weight is reused for
-// all token rows of the expert staged in LDS (up to kRows8 per pass).  At
-// prefill sizes this is the floor: correct and bounded, not matrix-core fast.
+// h) -- the bf16 copy of a weight lives only in registers -- and each
+// 16-element partial sum is multiplied by its block's fp32 scale.  Every
+// decoded weight is reused for all token rows of the expert staged in LDS
+// (up to kRows8 per pass).
 //
 // Gate/up: h[p][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]) (fp32), p over the
 // expert's rows (t = sorted_rows[p] / k); gate rows [0, f), up [f, 2f).

@@ -158,17 +158,22 @@ struct Diag {
 };
 Diag g_diag;
 
-// FP8 experts: the grouped GEMV path for every T.  FFN: the plan, then h
-// [T*k][f] fp32.  Layer: the routed layer's routing and grouping scratch,
-// that, and rows_out [T*k][d] bf16.
+// FP8 experts: the grouped GEMVs for few tokens, the bf16 matrix-core GEMMs
+// from kMfmaMinT tokens on.  FFN: the plan, then h [T*k][f] (fp32 on the
+// GEMV path, bf16 on the GEMM path), then the GEMMs' row-tile list.  Layer:
+// the routed layer's routing and grouping scratch, that, and rows_out
+// [T*k][d] bf16.
 struct Fp8FfnWs {
-    size_t plan, h, total;
+    size_t plan, h, tiles, total;
 };
 Fp8FfnWs fp8_ffn_ws(const moe_dims &D) {
     Fp8FfnWs w;
     w.plan = 0;
     w.h = al256((size_t)(D.E + 1) * 4);
-    w.total = w.h + al256((size_t)D.T * D.k * D.f * 4);
+    w.tiles = w.h + al256((size_t)D.T * D.k * D.f * 4);
+    w.total = w.tiles;
+    if (moe::fp8_mfma_ok(D.T, D.d, D.E, D.k, D.f))
+        w.total += al256(moe::fp8_mfma_tiles_bytes(D.T, D.E, D.k));
     return w;
 }
 struct Fp8LayerWs {
@@ -730,6 +735,10 @@ moe_status moe_expert_ffn_fp8(const moe_dims *dims, const uint16_t *x,
         const moe::Fp8Args W{experts->gu_codes, experts->gu_scales, experts->dn_codes,
                              experts->dn_scales};
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
+        if (moe::fp8_mfma_ok(D.T, D.d, D.E, D.k, D.f))
+            return device_status(moe::launch_fp8_mfma_ffn(
+                x, W, offsets, sorted_rows, reinterpret_cast<int32_t *>(base + F.tiles),
+                reinterpret_cast<uint16_t *>(h), rows_out, D.T, D.d, D.E, D.k, D.f, s));
         hipError_t e = moe::launch_plan(offsets, plan, D.E, s);
         if (e == hipSuccess)
             e = moe::launch_fp8_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
@@ -800,11 +809,20 @@ moe_status moe_layer_forward_fp8(const moe_dims *dims, const uint16_t *x,
                 }
             }
         }
-        if (e == hipSuccess)
-            e = moe::launch_fp8_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E, D.k,
-                                        D.f, s);
-        if (e == hipSuccess)
-            e = moe::launch_fp8_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f, s);
+        if (moe::fp8_mfma_ok(D.T, D.d, D.E, D.k, D.f)) {
+            if (e == hipSuccess)
+                e = moe::launch_fp8_mfma_ffn(x, W, offsets, sorted_rows,
+                                             reinterpret_cast<int32_t *>(base + L.ffn + F.tiles),
+                                             reinterpret_cast<uint16_t *>(h), rows_out, D.T, D.d,
+                                             D.E, D.k, D.f, s);
+        } else {
+            if (e == hipSuccess)
+                e = moe::launch_fp8_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E,
+                                            D.k, D.f, s);
+            if (e == hipSuccess)
+                e = moe::launch_fp8_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f,
+                                         s);
+        }
         if (e == hipSuccess)
             e = moe::launch_combine(rows_out, row_pos, tw, y, D.T, D.d, D.k, s);
         return device_status(e);

@@ -304,6 +304,17 @@ hipError_t launch_fp8_gate_up(const uint16_t *x, Fp8Args w, const int32_t *offse
 hipError_t launch_fp8_down(const float *h, Fp8Args w, const int32_t *offsets,
                            const int32_t *plan, uint16_t *rows_out, int T, int d, int E, int k,
                            int f, hipStream_t s);
+// Many tokens (fp8_mfma_ok): the bf16 matrix-core GEMMs of ffn_fp8_mfma.hip
+// (codes converted exactly to bf16 in LDS, block scales applied per 128-K
+// chunk in fp32): tiles int32 scratch of fp8_mfma_tiles_bytes, h bf16
+// [T*k][f], rows_out bf16 [T*k][d], both expert-major.
+bool fp8_mfma_ok(int T, int d, int E, int k, int f);
+int fp8_mfma_max_tiles(int T, int E, int k);
+size_t fp8_mfma_tiles_bytes(int T, int E, int k);
+hipError_t launch_fp8_mfma_ffn(const uint16_t *x, Fp8Args w, const int32_t *offsets,
+                               const int32_t *sorted_rows, int32_t *tiles, uint16_t *h,
+                               uint16_t *rows_out, int T, int d, int E, int k, int f,
+                               hipStream_t s);
 
 // ---- MoE tail (tail.hip, shared_gemm.hip) --------------------------------------
 // xn = bf16(RMSNorm(x) * gamma), canonical fp64 order, one wave per token.

@@ -2,7 +2,8 @@
 oracle.
 
 Bar: routing ids bit-exact, weights within 1e-5; rows_out and y within
-max|gpu - oracle| <= 1e-2 * max|oracle|.  Exact checks: doubling an
+max|gpu - oracle| <= 1e-2 * max|oracle|.  Exact checks, on the GEMVs (few
+tokens) and on the matrix-core GEMMs (from 128 tokens): doubling an
 expert's down scales doubles its rows bit for bit; all-zero codes give
 exactly zero; two runs are identical.  Full size (d = 7168, E = 896, top-16,
 f = 1536): decode and skewed prefill on sampled tokens.
@@ -65,7 +66,12 @@ CASES = [
     (8, 256, 16, 2, 128, 1),          # fused top-k + grouping (T <= 16)
     (5, 384, 40, 5, 256, 2),          # three scale blocks along d, two along f
     (20, 256, 24, 3, 128, 3),         # separate top-k and permute
-    (300, 256, 24, 4, 128, 4),        # filtered routing; many rows per expert (LDS passes)
+    (300, 256, 24, 4, 128, 4),        # filtered routing; matrix-core GEMMs (T >= 128)
+    # matrix-core GEMMs: a partial down column block (d = 384: 256 + 128),
+    # ragged row tiles, three gate/up column blocks, experts over 128 rows
+    (160, 384, 8, 2, 256, 10),
+    (400, 256, 4, 2, 384, 11),
+    (130, 512, 64, 3, 128, 12),       # many experts with a handful of rows, some with none
 ]
 
 
@@ -87,9 +93,10 @@ def test_fp8_layer_small(dev, case):
     _close(_bf16_to_f64(y), ref["y64"], "y")
 
 
-def test_fp8_expert_ffn_entry_and_exact_scaling(dev):
+@pytest.mark.parametrize("T", [12, 160], ids=["gemv", "mfma"])
+def test_fp8_expert_ffn_entry_and_exact_scaling(dev, T):
     moe = _moe()
-    T, d, E, k, f = 12, 256, 8, 3, 256
+    d, E, k, f = 256, 8, 3, 256
     cfg, x, wr, W = _case(T, d, E, k, f, 9)
     Wd = {n: v.to(dev) for n, v in W.items()}
     ids, _ = moe.moe_route(x.to(dev), wr.to(dev), k)
