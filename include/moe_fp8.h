@@ -19,11 +19,12 @@
  * per expert, twice the MXFP4 store.
  *
  * Below 128 tokens the experts run as grouped dequant-GEMVs (bf16 weights
- * exist only in registers, per tile in flight).  From 128 tokens on they
- * run as grouped GEMMs on the bf16 matrix cores: weight tiles are
- * converted exactly to bf16 on their way into LDS (every E4M3FN value is a
- * bf16 value), activations are used as given, and each 128 x 128 block
- * scale multiplies its 128-element K chunk's fp32 partial sums; h is
+ * exist only in registers, per tile in flight; each 16-element partial sum
+ * is multiplied by its block scale in fp32).  From 128 tokens on they run
+ * as grouped GEMMs on the bf16 matrix cores: each weight, converted exactly
+ * from E4M3FN and multiplied by its block scale in fp32, is rounded once to
+ * bf16 (relative error at most 2^-9) as the wave reads its fragment from
+ * LDS; activations are used as given, accumulation is fp32, and h is
  * rounded to bf16 between the two GEMMs.  Conventions are those of moe.h (device pointers owned
  * by the caller, asynchronous on hip_stream, validation before any launch,
  * T == 0 a no-op, deterministic).  Also: d % 128 == 0, f % 128 == 0,
