@@ -146,12 +146,12 @@ def stream_read_gbps(nbytes: int, reps: int = 5, _buf={}):
 
 def mfma_rate_tflops(kind: str, reps: int = 3):
     """The best rate (TFLOP/s) of the matrix instruction of this kind issued
-    from registers by two and by four waves per SIMD."""
+    from registers by two, four and eight waves per SIMD."""
     import torch
     from routed_expert_mxfp4_amd import moe
-    out = torch.empty(4 * 1024, dtype=torch.float32, device="cuda:0")
+    out = torch.empty(4 * 2048, dtype=torch.float32, device="cuda:0")
     best = 0.0
-    for blocks, iters in ((512, 2048), (1024, 1024)):
+    for blocks, iters in ((512, 2048), (1024, 1024), (2048, 512)):
         flops = moe.diag_mfma_rate(kind, blocks, iters, out)   # warm
         moe.diag_time_kernel("mfma_rate", capacity=reps)
         for i in range(reps):

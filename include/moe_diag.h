@@ -87,8 +87,10 @@ int moe_diag_kernel_times(double *ms_out, int cap, long long *launches);
  * can reach.
  *
  * moe_diag_mfma_rate: one launch of `blocks` blocks of four waves; each
- * wave issues iters x 4 independent matrix instructions from registers (no
- * memory traffic) and writes one sum to out[4 blocks] (device memory).
+ * wave issues iters x 4 matrix instructions (iters a multiple of 4) from
+ * registers, in sixteen (16x16 shapes) or four (32x32 shapes) independent
+ * accumulation chains, with no memory traffic, and writes one sum to
+ * out[4 blocks] (device memory).
  * kind 0: scaled 16x16x128 with A FP6 E2M3, B FP4 E2M1 (the expert GEMMs'
  * split activations x weights); 1: A FP8 E4M3, B FP4; 2: FP4 x FP4;
  * 3: FP8 x FP8; 4: bf16 32x32x16 (the shared expert's GEMMs); 5: FP6 x

@@ -47,22 +47,33 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
     if (threadIdx.x == 0) out[blockIdx.x] = red[0];
 }
 
-// Four independent accumulators per wave; operands differ per lane so that
-// nothing folds.  Scale code 127 (2^0) for both operands.
+// Sixteen independent accumulation chains per wave, each with its own
+// operand registers: the 16x16x128 shape's result latency is long against
+// its issue time, and only this much independent work (with up to eight
+// waves per SIMD) comes near its issue rate.  Operands differ per lane and
+// chain so that nothing folds.  Scale code 127 (2^0) for both operands.
 template <int FA, int FB>
 __global__ __launch_bounds__(256) void mfma_scaled_rate_kernel(int iters, float *__restrict__ out) {
+    constexpr int kCh = 16;
     const int lane = threadIdx.x & 63;
     const int v = 0x22222222 ^ (lane & 7);
-    const i32x8_t a = {v, v, v, v, v, v, v, v};
-    const i32x8_t b = {v ^ 1, v ^ 1, v ^ 1, v ^ 1, v ^ 1, v ^ 1, v ^ 1, v ^ 1};
-    f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;
-    for (int i = 0; i < iters; ++i) {
-        c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c0, FA, FB, 0, 127, 0, 127);
-        c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c1, FA, FB, 0, 127, 0, 127);
-        c2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c2, FA, FB, 0, 127, 0, 127);
-        c3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c3, FA, FB, 0, 127, 0, 127);
+    i32x8_t a[kCh], b[kCh];
+    f32x4_t c[kCh];
+#pragma unroll
+    for (int j = 0; j < kCh; ++j) {
+        const int vj = v ^ (j << 8);
+        a[j] = i32x8_t{vj, vj, vj, vj, vj, vj, vj, vj};
+        b[j] = i32x8_t{vj ^ 1, vj ^ 1, vj ^ 1, vj ^ 1, vj ^ 1, vj ^ 1, vj ^ 1, vj ^ 1};
+        c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const float s = (c0[0] + c1[1]) + (c2[2] + c3[3]);
+    for (int i = 0; i < iters; i += 4) {
+#pragma unroll
+        for (int j = 0; j < kCh; ++j)
+            c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[j], b[j], c[j], FA, FB, 0, 127, 0, 127);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kCh; ++j) s += c[j][j & 3];
     if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
 }
 
@@ -119,7 +130,7 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *out, int 
 }
 
 hipError_t launch_mfma_rate(int kind, int blocks, int iters, float *out, hipStream_t s) {
-    if (out == nullptr || blocks <= 0 || iters <= 0) return hipErrorInvalidValue;
+    if (out == nullptr || blocks <= 0 || iters <= 0 || iters % 4 != 0) return hipErrorInvalidValue;
     switch (kind) {
     case 0:   // FP6 E2M3 x FP4 E2M1
         return timed_launch("mfma_rate", mfma_scaled_rate_kernel<2, 4>, dim3(blocks), dim3(256), 0, s, iters, out);

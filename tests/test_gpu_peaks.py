@@ -35,10 +35,10 @@ def test_stream_read_refuses_unaligned(dev):
         moe.diag_stream_read(src, 24, out, 4)          # not a multiple of 16
 
 
-# E2M1 0x2 = 1.0, 0x3 = 1.5; E2M3 0x22 pattern: fields of 6 bits; E4M3 0x22 =
-# 2^-3 * 1.25.  The kernels' operands are v = 0x22222222 ^ (lane & 7) and v ^ 1
-# in every register, so every product is fixed; here only the FP4 x FP4 kinds
-# are checked in closed form, the others for finiteness and sign.
+# The kernels' operands are v = 0x22222222 ^ (lane & 7) (the 16x16 kinds: ^
+# (chain << 8)) for A and v ^ 1 for B, in every register, so every product is
+# fixed; the FP4 x FP4 kinds are checked in closed form (E2M1 magnitudes 0,
+# 0.5, 1, 1.5, 2, 3, 4, 6, bit 3 the sign), the others for finiteness.
 def _fp4(code):
     mag = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0][code & 7]
     return -mag if code & 8 else mag
@@ -50,40 +50,39 @@ def _fp4_row(v):
     return [_fp4((w >> (4 * i)) & 15) for w in words for i in range(8)]
 
 
+def _product(M, K, xor):
+    """C = A B^T of the operands every lane builds from v = 0x22222222 ^
+    (lane & 7) ^ xor (A) and v ^ 1 (B): lane l holds row l % M, K block
+    l // M."""
+    A = np.zeros((M, K))
+    B = np.zeros((M, K))
+    for lane in range(64):
+        v = 0x22222222 ^ (lane & 7) ^ xor
+        r, g = lane % M, lane // M
+        A[r, 32 * g:32 * g + 32] = _fp4_row(v)
+        B[r, 32 * g:32 * g + 32] = _fp4_row(v ^ 1)
+    return A @ B.T
+
+
 @pytest.mark.parametrize("kind", ["fp4xfp4", "fp4xfp4_32x32x64"])
 def test_mfma_rate_fp4_closed_form(dev, kind):
     from routed_expert_mxfp4_amd import moe
-    blocks, iters = 2, 3
+    blocks, iters = 2, 8
     out = torch.zeros(4 * blocks, dtype=torch.float32, device=dev)
     moe.diag_mfma_rate(kind, blocks, iters, out)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    # lane 0 of each wave writes its accumulator entries; every lane's A and
-    # B rows are the same within a K block group because lanes 0..7 differ
-    # only in the low 3 bits of each word, so compute C = A B^T explicitly
     if kind == "fp4xfp4":
-        M = N = 16
-        K = 128
-        groups = 4
+        # sixteen chains of iters / 4 products; chain j's operands are built
+        # from v ^ (j << 8) and the sum takes its entry j % 4, which lane 0
+        # holds as C[j % 4][0]
+        want = sum(iters // 4 * _product(16, 128, j << 8)[j % 4, 0] for j in range(16))
     else:
-        M = N = 32
-        K = 64
-        groups = 2
-    A = np.zeros((M, K))
-    B = np.zeros((N, K))
-    for lane in range(64):
-        v = 0x22222222 ^ (lane & 7)
-        r, g = lane % M, lane // M
-        A[r, 32 * g:32 * g + 32] = _fp4_row(v)
-        B[r, 32 * g:32 * g + 32] = _fp4_row(v ^ 1)
-    C = A @ B.T
-    if kind == "fp4xfp4":
-        # lane 0 holds C[0][0] .. C[3][0]; the sum takes c0[0] + c1[1] + c2[2] + c3[3]
-        want = iters * (C[0, 0] + C[1, 0] + C[2, 0] + C[3, 0])
-    else:
-        # 32x32: register r of lane 0 holds row 8 (r / 4) + r % 4, column 0
-        rows = [8 * (r // 4) + r % 4 for r in (0, 5, 10, 15)]
-        want = iters * sum(C[m, 0] for m in rows)
+        # four chains of iters products on the same operands; register r of
+        # lane 0 holds row 8 (r / 4) + r % 4, column 0, and the sum takes
+        # registers 0, 5, 10, 15 of chains 0..3
+        C = _product(32, 64, 0)
+        want = iters * sum(C[8 * (r // 4) + r % 4, 0] for r in (0, 5, 10, 15))
     np.testing.assert_allclose(got, want, rtol=1e-6)
 
 
@@ -91,6 +90,13 @@ def test_mfma_rate_fp4_closed_form(dev, kind):
 def test_mfma_rate_other_kinds_finite(dev, kind):
     from routed_expert_mxfp4_amd import moe
     out = torch.full((8,), float("nan"), dtype=torch.float32, device=dev)
-    flops = moe.diag_mfma_rate(kind, 2, 5, out)
+    flops = moe.diag_mfma_rate(kind, 2, 8, out)
     torch.cuda.synchronize()
     assert flops > 0 and torch.isfinite(out).all()
+
+
+def test_mfma_rate_refuses_iterations_not_multiple_of_four(dev):
+    from routed_expert_mxfp4_amd import moe
+    out = torch.zeros(8, dtype=torch.float32, device=dev)
+    with pytest.raises(RuntimeError):
+        moe.diag_mfma_rate("fp6xfp4", 2, 6, out)
