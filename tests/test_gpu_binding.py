@@ -4,10 +4,10 @@
   the stream it launches on.  The layer run on a side stream, with
   allocations churning on the default stream meanwhile, must give the same
   bits as the layer run on the default stream.
-* The layer workspace is not monotonic in T (the expert path changes at the
-  MFMA threshold).  A Layer first used at the larger T of the MFMA path and
-  then at one token fewer (the GEMV path, whose fp32 h is larger) must grow
-  its workspace instead of refusing the call.
+* The layer workspace is not monotonic in T: in the activation-MX mode the
+  expert path changes at 128 tokens.  A Layer first used at 128 tokens (the
+  MFMA path) and then at 127 (the GEMV path, whose fp32 h is larger) must
+  grow its workspace instead of refusing the call.
 """
 import pytest
 import torch
