@@ -221,6 +221,8 @@ __device__ __forceinline__ int find_expert(const int32_t *tiles, int nact, int m
 // kk each wave waits until only its loads of step kk + 1's codes remain, a
 // barrier publishes every wave's, then the next loads are issued into
 // buffers every wave has finished reading, and step kk is multiplied.
+// 16-row tiles take a deeper ring instead (four stages of each operand,
+// every load three steps ahead; see issue_step_deep).
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 8;
 constexpr int kAStageBytes = kBM * kStepBytes;              // 26624: a 128-row tile's step
@@ -471,6 +473,55 @@ __device__ __forceinline__ void issue_b8(const Plan8 &P, uint32_t lds, int kk, i
                        (int)(st + 1024u * (uint32_t)(wid + kWaves * j))));
 }
 
+// 16-row tiles (decode-sized experts): an A stage is 4 KB, so four A
+// stages, four weight stages and the scale group fit in LDS with every load
+// issued three K steps ahead.  Such a tile does little matrix work per step,
+// so its weight stream is set by the bytes in flight; twice as many as the
+// two-ahead ring keep it going.
+constexpr int kDeepAStage = 4096;
+constexpr int kDeepBBase = 4 * kDeepAStage;
+constexpr int kDeepSBase = kDeepBBase + 4 * kBStageBytes;
+static_assert(kDeepSBase + kSGroupBytes <= kLdsBytes, "the deep ring fits the block's LDS");
+
+// All of step kk's loads into stage kk % 4: activations (and, at kk % 4 ==
+// 0, the scale group), then the weight codes.
+__device__ __forceinline__ void issue_step_deep(const Plan8 &P, uint32_t lds, int kk, int wid) {
+    const uint32_t st = (uint32_t)(kk & 3);
+    const uint32_t a_st = lds + st * kDeepAStage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j < P.n_a)
+            lds_load16(P.ra, P.a_src[j] + (uint32_t)kk * kStepBytes,
+                       (uint32_t)__builtin_amdgcn_readfirstlane(
+                           (int)(a_st + 1024u * (uint32_t)(wid + kWaves * j))));
+    }
+    if ((kk & 3) == 0)
+        lds_load16(P.rs, P.s_src + (uint32_t)(kk >> 2) * P.sgrp,
+                   (uint32_t)__builtin_amdgcn_readfirstlane(
+                       (int)(lds + kDeepSBase + 1024u * (uint32_t)wid)));
+    const uint32_t b_st = lds + kDeepBBase + st * kBStageBytes;
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j)
+        lds_load16(P.rb, P.b_src[j] + (uint32_t)kk * P.cstep,
+                   (uint32_t)__builtin_amdgcn_readfirstlane(
+                       (int)(b_st + 1024u * (uint32_t)(wid + kWaves * j))));
+}
+
+// Waits until at most n of the wave's loads are outstanding; n is one of
+// the values the deep ring produces (0, or one or two later steps' loads).
+__device__ __forceinline__ void deep_wait(int n) {
+    switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(vmcnt_imm(9)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(vmcnt_imm(10)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(vmcnt_imm(11)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    }
+}
+
 // The lane's E8M0 codes of one scale group for its operand tiles: byte s of
 // sc[nt] is the code of K block 4 s + g of row r16 (step s of the group),
 // picked from the row's 16 bytes.
@@ -540,30 +591,10 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
 #pragma unroll
         for (int j = 0; j < kNtw; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // prologue: step 0's activations and scale group, steps 0 and 1's codes
-    issue_a8<MT>(P, lds_addr, 0, wid);
-    issue_b8(P, lds_addr, 0, 0, wid);
-    if (P.nsteps > 1) issue_b8(P, lds_addr, 1, 1, wid);
     const uint32_t psel01 = (uint32_t)g | ((4u + (uint32_t)g) << 8);
-    const uint32_t sgrp_lane = lds_addr + kSBase + 256u * (uint32_t)nbase + 16u * (uint32_t)r16;
     uint32_t spk[kNtw];
-    int sb = 0;                                             // kk % 3
-    for (int kk = 0; kk < P.nsteps; ++kk) {
-        // step kk's operands: all but step kk + 1's codes, the last loads
-        // issued (when there are any)
-        if (kk + 1 < P.nsteps)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBLoads));
-        else
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        __builtin_amdgcn_s_barrier();                       // everyone's; step kk-1's buffers free
-        __builtin_amdgcn_sched_barrier(0);
-        if ((kk & 3) == 0) read_group_scales<kNtw>(spk, sgrp_lane, psel01);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk + 1 < P.nsteps) issue_a8<MT>(P, lds_addr, kk + 1, wid);
-        if (kk + 2 < P.nsteps) issue_b8(P, lds_addr, kk + 2, sb == 0 ? 2 : sb - 1, wid);
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t st = lds_addr + (uint32_t)((kk & 1) * kAStageBytes);
-        const uint32_t sbq = lds_addr + kBBase + (uint32_t)(sb * kBStageBytes);
+    // one K step's products from A stage st and B stage sbq
+    auto multiply = [&](uint32_t st, uint32_t sbq, int kk) {
         BFrags<kNtw> fb;
 #pragma unroll
         for (int nt = 0; nt < kNtw; ++nt) {
@@ -577,7 +608,51 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
         // the B fragments and m-tile 0's A fragment; m-tile 1's may still fly
         bfrags_ready<kNtw, (kMtw > 1 ? 5 : 0)>(fb);
         chain8<0, kMtw, kNtw, kSingle>(acc, fa, fb, a, s);
-        sb = sb == 2 ? 0 : sb + 1;
+    };
+    if constexpr (MT == 1) {
+        // the deep ring: steps 0..2 first, then step kk + 3 at step kk
+        const uint32_t sgrp_lane = lds_addr + kDeepSBase + 256u * (uint32_t)nbase + 16u * (uint32_t)r16;
+        for (int s0 = 0; s0 < 3 && s0 < P.nsteps; ++s0) issue_step_deep(P, lds_addr, s0, wid);
+        for (int kk = 0; kk < P.nsteps; ++kk) {
+            // step kk's loads, with those of the (at most two) later steps
+            // issued so far still allowed in flight
+            const int pend = min(2, P.nsteps - 1 - kk);
+            const int scl = (pend >= 1 && ((kk + 1) & 3) == 0) + (pend >= 2 && ((kk + 2) & 3) == 0);
+            deep_wait(pend * (P.n_a + kBLoads) + scl);
+            __builtin_amdgcn_s_barrier();                   // everyone's; step kk-1's stages free
+            __builtin_amdgcn_sched_barrier(0);
+            if ((kk & 3) == 0) read_group_scales<kNtw>(spk, sgrp_lane, psel01);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk + 3 < P.nsteps) issue_step_deep(P, lds_addr, kk + 3, wid);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(lds_addr + (uint32_t)((kk & 3) * kDeepAStage),
+                     lds_addr + kDeepBBase + (uint32_t)((kk & 3) * kBStageBytes), kk);
+        }
+    } else {
+        // prologue: step 0's activations and scale group, steps 0 and 1's codes
+        issue_a8<MT>(P, lds_addr, 0, wid);
+        issue_b8(P, lds_addr, 0, 0, wid);
+        if (P.nsteps > 1) issue_b8(P, lds_addr, 1, 1, wid);
+        const uint32_t sgrp_lane = lds_addr + kSBase + 256u * (uint32_t)nbase + 16u * (uint32_t)r16;
+        int sb = 0;                                         // kk % 3
+        for (int kk = 0; kk < P.nsteps; ++kk) {
+            // step kk's operands: all but step kk + 1's codes, the last loads
+            // issued (when there are any)
+            if (kk + 1 < P.nsteps)
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(kBLoads));
+            else
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            __builtin_amdgcn_s_barrier();                   // everyone's; step kk-1's buffers free
+            __builtin_amdgcn_sched_barrier(0);
+            if ((kk & 3) == 0) read_group_scales<kNtw>(spk, sgrp_lane, psel01);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk + 1 < P.nsteps) issue_a8<MT>(P, lds_addr, kk + 1, wid);
+            if (kk + 2 < P.nsteps) issue_b8(P, lds_addr, kk + 2, sb == 0 ? 2 : sb - 1, wid);
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(lds_addr + (uint32_t)((kk & 1) * kAStageBytes),
+                     lds_addr + kBBase + (uint32_t)(sb * kBStageBytes), kk);
+            sb = sb == 2 ? 0 : sb + 1;
+        }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();                                        // the stages are free for the epilogue
