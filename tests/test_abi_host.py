@@ -38,6 +38,12 @@ def test_exports_every_declared_symbol(L):
     assert L.moe_abi_version() == 3
 
 
+def test_build_entry_checks_the_headers_abi_version(L):
+    # __graft_entry__.build() compares the built library with include/moe.h
+    import __graft_entry__
+    assert __graft_entry__.header_abi_version() == L.moe_abi_version()
+
+
 def test_status_strings(L):
     for s in range(8):
         txt = moe.status_str(s)
