@@ -695,11 +695,17 @@ bool gemv_small_ok(int d, int f) {
     return f % kRxPairs == 0 && d <= 8192 && (f / 32 + 63) / 64 <= 2;
 }
 
+// The small-expert passes run in a scaled-MFMA call whose small list may
+// be empty (every expert over the crossover): a bounded grid whose blocks
+// walk the list (a += gridDim.y) keeps that case to a few microseconds
+// instead of one block per possible expert.
+constexpr int kSmallGridY = 320;
+
 hipError_t launch_gemv_gate_up_small(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                                      const int32_t *sorted_rows, const int32_t *small,
                                      float *h_small, int T, int d, int E, int k, int f,
                                      int gemv_max, hipStream_t s) {
-    const int amax = min(E, T * k);
+    const int amax = min(min(E, T * k), kSmallGridY);
     if (amax <= 0) return hipSuccess;
     const int nbl = (d / 32 + 63) / 64;
     if (nbl == 1)
@@ -715,7 +721,7 @@ hipError_t launch_gemv_gate_up_small(const uint16_t *x, ExpertArgs w, const int3
 hipError_t launch_gemv_down_small(const float *h_small, ExpertArgs w, const int32_t *offsets,
                                   const int32_t *small, uint16_t *rows_out, int T, int d, int E,
                                   int k, int f, int gemv_max, hipStream_t s) {
-    const int amax = min(E, T * k);
+    const int amax = min(min(E, T * k), kSmallGridY);
     if (amax <= 0) return hipSuccess;
     if ((f / 32 + 63) / 64 == 1)
         return launch_down_rows<1>(h_small, w, offsets, small, rows_out, T, d, E, k, f, amax, s,
