@@ -526,14 +526,14 @@ __device__ __forceinline__ void dot_batch(const RowBuf<NBLD, B> &rb, const float
     }
 }
 
-// Fused down + combine for small T: block (ROWS output rows, token t); wave
-// j computes slot j's expert output for the block's rows (j = wid, wid + 16,
-// ...) in batches of B rows held in a ring of R batch buffers, so R - 1
-// batches' loads are in flight during each batch's math, and parks it in
-// LDS; then y = sum_j w_j o_j in fp32, slot order, one writer per output.
-// ROWS is a multiple of B.
-template <int NBLD, int ROWS, int B, int R>
-__global__ __launch_bounds__(1024) void down_combine_split_kernel(
+// Fused down + combine for small T: block (ROWS output rows, token t) of NW
+// waves; wave j computes slot j's expert output for the block's rows (j =
+// wid, wid + NW, ...) in batches of B rows held in a ring of R batch buffers,
+// so R - 1 batches' loads are in flight during each batch's math, and parks
+// it in LDS; then y = sum_j w_j o_j in fp32, slot order, one writer per
+// output.  ROWS is a multiple of B.
+template <int NBLD, int ROWS, int B, int R, int NW>
+__global__ __launch_bounds__(64 * NW) void down_combine_split_kernel(
     const float *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ ids,
     const float *__restrict__ topk_w, const int32_t *__restrict__ row_pos,
     uint16_t *__restrict__ y, int T, int d, int E, int k, int f) {
@@ -548,7 +548,7 @@ __global__ __launch_bounds__(1024) void down_combine_split_kernel(
     const uint32_t code_row = (uint32_t)f >> 1;
     const int nrows = T * k;
     const rsrc_t hbuf = make_rsrc(h, (uint32_t)min((size_t)nrows * f * 4, (size_t)0xFFFFFFF0u));
-    for (int j = wid; j < k; j += 16) {
+    for (int j = wid; j < k; j += NW) {
         const int e = __builtin_amdgcn_readfirstlane(ids[(size_t)t * k + j]);
         const int p = __builtin_amdgcn_readfirstlane(row_pos[(size_t)t * k + j]);
         const bool ok = (unsigned)e < (unsigned)E && (unsigned)p < (unsigned)nrows;
@@ -771,19 +771,31 @@ hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertAr
 // rows per batch and batch buffers of the fused down + combine
 constexpr int kDcB = 4, kDcR = 2;
 
+template <int NBLD, int ROWS, int NW>
+void launch_dc(const float *h, ExpertArgs w, const int32_t *ids, const float *topk_w,
+               const int32_t *row_pos, uint16_t *y, int T, int d, int E, int k, int f,
+               hipStream_t s) {
+    (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, ROWS, kDcB, kDcR, NW>,
+                       dim3(d / ROWS, T), dim3(64 * NW), 0, s, h, w, ids, topk_w, row_pos, y, T, d,
+                       E, k, f);
+}
+
 template <int NBLD>
 hipError_t launch_dc_split(const float *h, ExpertArgs w, const int32_t *ids,
                            const float *topk_w, const int32_t *row_pos, uint16_t *y, int T,
                            int d, int E, int k, int f, hipStream_t s) {
-    // 28 output rows per block: 7168 / 28 = 256 blocks, one per CU
-    if (d % 28 == 0) {
-        dim3 grid(d / 28, T);
-        (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, 28, kDcB, kDcR>, dim3(grid), dim3(1024), 0, s, h, w, ids, topk_w, row_pos, y,
-                                                                      T, d, E, k, f);
+    // about one block per CU: 28 output rows per block where d allows
+    // (7168 / 28 = 256), else 16 (4096 / 16 = 256) or 32; one wave per slot
+    // (16 waves, or 8 when k <= 8)
+    const int rows = d % 28 == 0 ? 28 : (d % 16 == 0 && d / 16 <= 512 ? 16 : 32);
+    if (k <= 8) {
+        if (rows == 28) launch_dc<NBLD, 28, 8>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+        else if (rows == 16) launch_dc<NBLD, 16, 8>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+        else launch_dc<NBLD, 32, 8>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
     } else {
-        dim3 grid(d / 32, T);
-        (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, 32, kDcB, kDcR>, dim3(grid), dim3(1024), 0, s, h, w, ids, topk_w, row_pos, y,
-                                                                      T, d, E, k, f);
+        if (rows == 28) launch_dc<NBLD, 28, 16>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+        else if (rows == 16) launch_dc<NBLD, 16, 16>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+        else launch_dc<NBLD, 32, 16>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
     }
     return hipGetLastError();
 }
