@@ -17,6 +17,7 @@
 // expert's rows (t = sorted_rows[p] / k); gate rows [0, f), up [f, 2f).
 // Down: rows_out[p][m] = h[p] . Wd[m] (bf16), expert-major.
 #include "moe_internal.hpp"
+#include "select_dev.hpp"
 
 namespace moe {
 namespace {
@@ -305,6 +306,176 @@ __global__ __launch_bounds__(256) void fp8_gate_up_rx_kernel(
     }
 }
 
+// One token (T = 1): the top-k and the grouping happen inside the gate/up
+// pass, as in the MXFP4 one-token kernel.  Every block selects the token's
+// experts from the logits row (one wave) after staging x; in ascending
+// expert order the a-th selected expert is the one whose h row is a
+// (blockIdx.y = a), routed from top-k slot sorted_rows[a].  Block (0, 0)
+// writes the grouping (ids, weights, counts, offsets, sorted_rows, row_pos,
+// plan) for the later kernels.  The gate/up rows are streamed as in
+// fp8_gate_up_rx_kernel.
+template <int NCL>
+__global__ __launch_bounds__(256) void fp8_gate_up_token_kernel(
+    const float *__restrict__ logits, const uint16_t *__restrict__ x, Fp8Args W,
+    int32_t *__restrict__ ids, float *__restrict__ tw, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
+    int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, float *__restrict__ h, int d,
+    int E, int k, int f) {
+    extern __shared__ uint4 xs[];                         // d / 8 x 16 B, + 1 spare
+    __shared__ __align__(16) uint32_t tsc[kTopkScratch];
+    __shared__ int sel[kMaxTopK];                         // selected experts, ascending
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nch = d >> 4, nvec = d >> 3, sbk = d >> 7;
+    const bool first = blockIdx.x == 0 && blockIdx.y == 0;
+    {
+        const uint4 *xrow = reinterpret_cast<const uint4 *>(x);
+        uint4 tmp[kStageX8];
+#pragma unroll
+        for (int j = 0; j < kStageX8; ++j)
+            tmp[j] = xrow[min((int)threadIdx.x + 256 * j, nvec - 1)];
+        loads_done(tmp);
+#pragma unroll
+        for (int j = 0; j < kStageX8; ++j) {
+            const int i = (int)threadIdx.x + 256 * j;
+            xs[i < nvec ? i : nvec] = tmp[j];
+        }
+    }
+    if (wid == 0) {
+        int e;
+        float wt;
+        wave_topk_softmax<16>(logits, E, k, tsc, &e, &wt);
+        int rank = 0;                                     // place among the selected
+        for (int i = 0; i < k; ++i) rank += __shfl(e, i) < e ? 1 : 0;
+        if (lane < k) {
+            sel[rank] = e;
+            if (first) {
+                ids[lane] = e;
+                tw[lane] = wt;
+                sorted_rows[rank] = lane;
+                row_pos[lane] = rank;
+                plan[1 + rank] = e;
+            }
+        }
+        if (first && lane == 0) plan[0] = k;
+    }
+    __syncthreads();
+    if (first) {
+        for (int c = threadIdx.x; c <= E; c += 256) {
+            int below = 0, hit = 0;
+            for (int i = 0; i < k; ++i) {
+                below += sel[i] < c ? 1 : 0;
+                hit += sel[i] == c ? 1 : 0;
+            }
+            offsets[c] = below;
+            if (c < E) counts[c] = hit;
+        }
+    }
+    const int a = blockIdx.y;
+    const int e = sel[a];
+    if ((unsigned)e >= (unsigned)E) return;
+    const uint8_t *codes = W.gu_codes + (size_t)e * 2 * f * d;
+    const float *scales = W.gu_scales + (size_t)e * (2 * f >> 7) * sbk;
+    constexpr int kPerWave = kRxPairs8 / 4;               // pairs n_base + 4 q
+    const int n_base = blockIdx.x * kRxPairs8 + wid;
+    float *hrow = h + (size_t)a * f;
+    Row8<NCL> A, B;
+    load_row8<NCL>(codes, scales, n_base, d, sbk, nch, lane, A);
+#pragma unroll 1
+    for (int q = 0; q < kPerWave; ++q) {
+        const int n = n_base + 4 * q;
+        load_row8<NCL>(codes, scales, f + n, d, sbk, nch, lane, B);              // up row
+        __builtin_amdgcn_sched_barrier(0);
+        const float g = row_dot8<NCL>(A, xs, lane, nch);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q + 1 < kPerWave)
+            load_row8<NCL>(codes, scales, n + 4, d, sbk, nch, lane, A);         // next gate row
+        __builtin_amdgcn_sched_barrier(0);
+        const float u = row_dot8<NCL>(B, xs, lane, nch);
+        if (lane == 0) hrow[n] = silu_mul8(g, u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Down + combine for small T: block (ROWS output rows, token t); wave j
+// computes slot j's expert output for the block's rows (j = wid, wid + 16,
+// ...) from h row row_pos[t k + j], lane l owning the 16-code chunks l + 64 i
+// (i < NCL) of f, whose h values it holds in registers; rows go in batches
+// of B in a ring of R batch buffers (R - 1 batches' loads in flight during
+// each batch's math).  Each row's partial sums are reduced across the wave
+// and parked in LDS; then y = sum_j w_j o_j in fp32, slot order, one writer
+// per output.
+template <int NCL, int ROWS, int B, int R>
+__global__ __launch_bounds__(1024) void fp8_down_combine_kernel(
+    const float *__restrict__ h, Fp8Args W, const int32_t *__restrict__ ids,
+    const float *__restrict__ topk_w, const int32_t *__restrict__ row_pos,
+    uint16_t *__restrict__ y, int T, int d, int E, int k, int f) {
+    static_assert(ROWS % B == 0, "whole batches");
+    static_assert(R >= 2, "a ring");
+    __shared__ float part[kMaxTopK][ROWS];
+    const int t = blockIdx.y;
+    const int m0 = blockIdx.x * ROWS;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nch = f >> 4, sbk = f >> 7;
+    const int nrows = T * k;
+    for (int j = wid; j < k; j += 16) {
+        const int e = __builtin_amdgcn_readfirstlane(ids[(size_t)t * k + j]);
+        const int p = __builtin_amdgcn_readfirstlane(row_pos[(size_t)t * k + j]);
+        if ((unsigned)e < (unsigned)E && (unsigned)p < (unsigned)nrows) {
+            const uint8_t *codes = W.dn_codes + (size_t)e * d * f;
+            const float *scales = W.dn_scales + (size_t)e * (d >> 7) * sbk;
+            const float4 *hrow = reinterpret_cast<const float4 *>(h + (size_t)p * f);
+            float4 hv[NCL][4];
+#pragma unroll
+            for (int i = 0; i < NCL; ++i) {
+                const int c = min(lane + 64 * i, nch - 1);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) hv[i][q] = hrow[4 * c + q];
+            }
+            constexpr int NB = ROWS / B;
+            Row8<NCL> ring[R][B];
+#pragma unroll
+            for (int b0 = 0; b0 < R - 1 && b0 < NB; ++b0)
+#pragma unroll
+                for (int rr = 0; rr < B; ++rr)
+                    load_row8<NCL>(codes, scales, m0 + b0 * B + rr, f, sbk, nch, lane, ring[b0][rr]);
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi) {
+                if (bi + R - 1 < NB) {
+#pragma unroll
+                    for (int rr = 0; rr < B; ++rr)
+                        load_row8<NCL>(codes, scales, m0 + (bi + R - 1) * B + rr, f, sbk, nch,
+                                       lane, ring[(bi + R - 1) % R][rr]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int rr = 0; rr < B; ++rr) {
+                    const Row8<NCL> &rb = ring[bi % R][rr];
+                    float acc = 0.f;
+#pragma unroll
+                    for (int i = 0; i < NCL; ++i) {
+                        const int c = lane + 64 * i;
+                        const float pi = dot16_fp8_f32(rb.c[i], hv[i], 0.f);
+                        acc += c < nch ? pi * rb.s[i] : 0.f;
+                    }
+                    const float o = wave_sum_f32(acc);
+                    if (lane == 0) part[j][bi * B + rr] = o;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if (lane < ROWS) {
+            part[j][lane] = 0.f;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < ROWS) {
+        float yv = 0.f;
+        for (int j = 0; j < k; ++j) yv += topk_w[(size_t)t * k + j] * part[j][threadIdx.x];
+        y[(size_t)t * d + m0 + threadIdx.x] = f32_to_bf16_rne(yv);
+    }
+}
+
 template <int NCL>
 hipError_t launch_fp8_rx(const uint16_t *x, Fp8Args w, const int32_t *offsets,
                          const int32_t *sorted_rows, const int32_t *plan, float *h, int T, int d,
@@ -348,6 +519,58 @@ hipError_t launch_fp8_down(const float *h, Fp8Args w, const int32_t *offsets,
     return timed_launch("fp8_down", fp8_down_kernel, dim3(d / kDnRows8, amax), dim3(256),
                         (size_t)rpp * f * 4, s, h, w, offsets, plan, rows_out, T, d, E, k, f,
                         rpp);
+}
+
+bool fp8_gate_up_token_fusable(int T, int d, int E, int k, int f) {
+    return T == 1 && k <= kMaxTopK && k <= E && E <= 1024 && d <= 8192 && d % 128 == 0 &&
+           f % kRxPairs8 == 0;
+}
+
+hipError_t launch_fp8_gate_up_token(const float *logits, const uint16_t *x, Fp8Args w,
+                                    int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
+                                    int32_t *sorted_rows, int32_t *row_pos, int32_t *plan,
+                                    float *h, int d, int E, int k, int f, hipStream_t s) {
+    const dim3 grid(f / kRxPairs8, k);
+    const size_t lds = (size_t)d * 2 + 16;
+#define MOE_FP8_TOK(N)                                                                       \
+    case N:                                                                                  \
+        return timed_launch("fp8_gate_up", fp8_gate_up_token_kernel<N>, grid, dim3(256), lds, s, \
+                            logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,    \
+                            plan, h, d, E, k, f);
+    switch ((d + 1023) / 1024) {                          // 16-code chunks per lane
+        MOE_FP8_TOK(1) MOE_FP8_TOK(2) MOE_FP8_TOK(3) MOE_FP8_TOK(4)
+        MOE_FP8_TOK(5) MOE_FP8_TOK(6) MOE_FP8_TOK(7) MOE_FP8_TOK(8)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef MOE_FP8_TOK
+}
+
+bool fp8_down_combine_ok(int T, int d, int k, int f) {
+    return T >= 1 && T <= 4 && k <= kMaxTopK && f <= 2048 && f % 128 == 0 && d % 32 == 0;
+}
+
+hipError_t launch_fp8_down_combine(const float *h, Fp8Args w, const int32_t *ids,
+                                   const float *topk_w, const int32_t *row_pos, uint16_t *y,
+                                   int T, int d, int E, int k, int f, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    if (!fp8_down_combine_ok(T, d, k, f)) return hipErrorInvalidValue;
+    // 28 output rows per block where d allows (7168 / 28 = 256 blocks), else 32
+    const int ncl = (f / 16 + 63) / 64;
+    if (d % 28 == 0) {
+        const dim3 grid(d / 28, T);
+        if (ncl == 1)
+            return timed_launch("fp8_down", fp8_down_combine_kernel<1, 28, 2, 2>, grid, dim3(1024), 0,
+                                s, h, w, ids, topk_w, row_pos, y, T, d, E, k, f);
+        return timed_launch("fp8_down", fp8_down_combine_kernel<2, 28, 2, 2>, grid, dim3(1024), 0, s,
+                            h, w, ids, topk_w, row_pos, y, T, d, E, k, f);
+    }
+    const dim3 grid(d / 32, T);
+    if (ncl == 1)
+        return timed_launch("fp8_down", fp8_down_combine_kernel<1, 32, 2, 2>, grid, dim3(1024), 0, s,
+                            h, w, ids, topk_w, row_pos, y, T, d, E, k, f);
+    return timed_launch("fp8_down", fp8_down_combine_kernel<2, 32, 2, 2>, grid, dim3(1024), 0, s, h,
+                        w, ids, topk_w, row_pos, y, T, d, E, k, f);
 }
 
 }  // namespace moe

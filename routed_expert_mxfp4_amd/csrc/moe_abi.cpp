@@ -783,8 +783,20 @@ moe_status moe_layer_forward_fp8(const moe_dims *dims, const uint16_t *x,
                              experts->dn_scales};
         hipStream_t s = static_cast<hipStream_t>(hip_stream);
         hipError_t e;
+        const bool mfma = moe::fp8_mfma_ok(D.T, D.d, D.E, D.k, D.f);
+        // one token: top-k and grouping inside the gate/up pass
+        const bool token_fused = !mfma && !moe::route_filter_ok(D.T, D.d, D.E) &&
+                                 moe::fp8_gate_up_token_fusable(D.T, D.d, D.E, D.k, D.f);
+        // few tokens: down and combine in one pass
+        const bool dc_fused = !mfma && moe::fp8_down_combine_ok(D.T, D.d, D.k, D.f);
         // routing and grouping as in the MXFP4 layer (the plan is written too)
-        if (moe::route_filter_ok(D.T, D.d, D.E)) {
+        if (token_fused) {
+            e = moe::launch_router_logits(x, router_w, router_bias, logits, D.T, D.d, D.E, s);
+            if (e == hipSuccess)
+                e = moe::launch_fp8_gate_up_token(logits, x, W, ids, tw, counts, offsets,
+                                                  sorted_rows, row_pos, plan, h, D.d, D.E, D.k,
+                                                  D.f, s);
+        } else if (moe::route_filter_ok(D.T, D.d, D.E)) {
             e = moe::launch_route_filtered(x, router_w, router_bias, logits,
                                            reinterpret_cast<float *>(base + L.route + RW.nx),
                                            reinterpret_cast<float *>(base + L.route + RW.nw),
@@ -809,16 +821,22 @@ moe_status moe_layer_forward_fp8(const moe_dims *dims, const uint16_t *x,
                 }
             }
         }
-        if (moe::fp8_mfma_ok(D.T, D.d, D.E, D.k, D.f)) {
+        if (mfma) {
             if (e == hipSuccess)
                 e = moe::launch_fp8_mfma_ffn(x, W, offsets, sorted_rows,
                                              reinterpret_cast<int32_t *>(base + L.ffn + F.tiles),
                                              reinterpret_cast<uint16_t *>(h), rows_out, D.T, D.d,
                                              D.E, D.k, D.f, s);
         } else {
-            if (e == hipSuccess)
+            if (e == hipSuccess && !token_fused)
                 e = moe::launch_fp8_gate_up(x, W, offsets, sorted_rows, plan, h, D.T, D.d, D.E,
                                             D.k, D.f, s);
+            if (dc_fused) {
+                if (e == hipSuccess)
+                    e = moe::launch_fp8_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E,
+                                                     D.k, D.f, s);
+                return device_status(e);
+            }
             if (e == hipSuccess)
                 e = moe::launch_fp8_down(h, W, offsets, plan, rows_out, D.T, D.d, D.E, D.k, D.f,
                                          s);

@@ -304,6 +304,20 @@ hipError_t launch_fp8_gate_up(const uint16_t *x, Fp8Args w, const int32_t *offse
 hipError_t launch_fp8_down(const float *h, Fp8Args w, const int32_t *offsets,
                            const int32_t *plan, uint16_t *rows_out, int T, int d, int E, int k,
                            int f, hipStream_t s);
+// One token: gate/up + SwiGLU with the top-k and grouping inside (as
+// launch_gate_up_token, writing ids, tw, counts, offsets, sorted_rows,
+// row_pos and plan), h fp32 [k][f].  Needs fp8_gate_up_token_fusable.
+bool fp8_gate_up_token_fusable(int T, int d, int E, int k, int f);
+hipError_t launch_fp8_gate_up_token(const float *logits, const uint16_t *x, Fp8Args w,
+                                    int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
+                                    int32_t *sorted_rows, int32_t *row_pos, int32_t *plan,
+                                    float *h, int d, int E, int k, int f, hipStream_t s);
+// Few tokens (fp8_down_combine_ok: T <= 4): down + weighted combine in one
+// pass, y bf16 [T][d] (fp32 expert outputs, summed in slot order).
+bool fp8_down_combine_ok(int T, int d, int k, int f);
+hipError_t launch_fp8_down_combine(const float *h, Fp8Args w, const int32_t *ids,
+                                   const float *topk_w, const int32_t *row_pos, uint16_t *y,
+                                   int T, int d, int E, int k, int f, hipStream_t s);
 // Many tokens (fp8_mfma_ok): the bf16 matrix-core GEMMs of ffn_fp8_mfma.hip
 // (codes converted exactly to bf16 in LDS, block scales applied per 128-K
 // chunk in fp32): tiles int32 scratch of fp8_mfma_tiles_bytes, h bf16

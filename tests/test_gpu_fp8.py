@@ -62,7 +62,10 @@ def _case(T, d, E, k, f, seed):
 
 CASES = [
     # (T, d, E, k, f, seed)
-    (1, 256, 16, 2, 128, 0),          # one token
+    (1, 256, 16, 2, 128, 0),          # one token: top-k inside gate/up, fused down + combine
+    (1, 512, 64, 8, 256, 6),          # one token, two scale blocks along f
+    (3, 384, 40, 5, 256, 5),          # fused down + combine for three tokens
+    (4, 256, 16, 16, 128, 7),         # four tokens, top-16 (the widest fused down + combine)
     (8, 256, 16, 2, 128, 1),          # fused top-k + grouping (T <= 16)
     (5, 384, 40, 5, 256, 2),          # three scale blocks along d, two along f
     (20, 256, 24, 3, 128, 3),         # separate top-k and permute
