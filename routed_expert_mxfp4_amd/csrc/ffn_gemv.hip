@@ -248,6 +248,11 @@ constexpr int kStageX = 4;           // x staging: d <= 4 * 256 * 8 = 8192
 // (shared by the block's four waves) and each wave streams its output pairs
 // with the next pair's code loads issued before the current pair's math, so
 // HBM reads and VALU work overlap instead of alternating.
+// h elements: fp32, or bf16 (the one-token and few-token paths of the bf16
+// mode, whose down pass then dots bf16 pairs, as the gate/up pass does).
+__device__ __forceinline__ void put_h(float *p, float v) { *p = v; }
+__device__ __forceinline__ void put_h(uint16_t *p, float v) { *p = f32_to_bf16_rne(v); }
+
 template <int NBL>
 struct PairBuf {
     uint4 c[2][NBL];       // gate, up
@@ -299,11 +304,11 @@ __device__ __forceinline__ float pair_h(const PairBuf<NBL> &pb, const uint4 *__r
 // Experts a = blockIdx.y, blockIdx.y + gridDim.y, ... of the plan.  h row of
 // (expert a, its r-th row): row0 + r, or a * hstride + r when hstride > 0
 // (the compact rows of the mixed path's small experts).
-template <int NBL>
+template <int NBL, typename HT>
 __global__ __launch_bounds__(256) void gate_up_regx_kernel(
     const uint16_t *__restrict__ x, ExpertArgs W, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
-    float *__restrict__ h, int T, int d, int E, int k, int f, int hstride) {
+    HT *__restrict__ h, int T, int d, int E, int k, int f, int hstride) {
     const int nrows = T * k;
     for (int a = blockIdx.y; a < plan[0]; a += gridDim.y) {
     int e, row0, ne;
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
             }
         }
         __syncthreads();
-        float* hrow = h + (size_t)(hstride > 0 ? a * hstride + r : row0 + r) * f;
+        HT *hrow = h + (size_t)(hstride > 0 ? a * hstride + r : row0 + r) * f;
         // sched_barrier keeps each stage in place: a later pair's loads may
         // not be hoisted above an earlier pair's math (that would only grow
         // the register footprint, not the bytes in flight)
@@ -348,13 +353,13 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
             load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
             __builtin_amdgcn_sched_barrier(0);
             const float va = pair_h<NBL>(A, xs, lane, nblk);
-            if (lane == 0) hrow[n_base + 4 * q] = va;
+            if (lane == 0) put_h(hrow + n_base + 4 * q, va);
             __builtin_amdgcn_sched_barrier(0);
             if (q + 2 < kPerWave)
                 load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
             __builtin_amdgcn_sched_barrier(0);
             const float vb = pair_h<NBL>(B, xs, lane, nblk);
-            if (lane == 0) hrow[n_base + 4 * (q + 1)] = vb;
+            if (lane == 0) put_h(hrow + n_base + 4 * (q + 1), vb);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -368,12 +373,12 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
 // row is a, routed from top-k slot sorted_rows[a] -- exactly the grouping of
 // the permute step.  Block (0, 0) writes that grouping (ids, weights,
 // counts, offsets, sorted_rows, row_pos, plan) for the later kernels.
-template <int NBL, int PAIRS>
+template <int NBL, int PAIRS, typename HT>
 __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
     const float *__restrict__ logits, const uint16_t *__restrict__ x, ExpertArgs W,
     int32_t *__restrict__ ids, float *__restrict__ tw, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
-    int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, float *__restrict__ h, int d,
+    int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, HT *__restrict__ h, int d,
     int E, int k, int f) {
     extern __shared__ uint4 xs[];                 // the token row, d/8 x 16 B, + 1 spare
     __shared__ __align__(16) uint32_t tsc[kTopkScratch];
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
     const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
     constexpr int kPerWave = PAIRS / 4;           // pairs n_base + wid + 4 q
     const int n_base = blockIdx.x * PAIRS + wid;
-    float *hrow = h + (size_t)a * f;
+    HT *hrow = h + (size_t)a * f;
     PairBuf<NBL> A, B;
     load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);
 #pragma unroll 1
@@ -442,22 +447,23 @@ __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
         load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
         __builtin_amdgcn_sched_barrier(0);
         const float va = pair_h<NBL>(A, xs, lane, nblk);
-        if (lane == 0) hrow[n_base + 4 * q] = va;
+        if (lane == 0) put_h(hrow + n_base + 4 * q, va);
         __builtin_amdgcn_sched_barrier(0);
         if (q + 2 < kPerWave)
             load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
         __builtin_amdgcn_sched_barrier(0);
         const float vb = pair_h<NBL>(B, xs, lane, nblk);
-        if (lane == 0) hrow[n_base + 4 * (q + 1)] = vb;
+        if (lane == 0) put_h(hrow + n_base + 4 * (q + 1), vb);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // Down rows for one h row: lane l owns the MX blocks b = l + 64 i (i < NBLD)
-// of f, so its slice of h (32 floats per block) is loaded once into
-// registers and reused for every output row; rows go in batches of 8 whose
-// code loads are all in flight together, and each row's partial sums are
-// reduced across the wave.  Lanes past the end of f hold zero h.
+// of f, so its slice of h (32 values per block: eight float4, or four uint4
+// of bf16 pairs) is loaded once into registers and reused for every output
+// row; rows go in batches whose code loads are all in flight together, and
+// each row's partial sums are reduced across the wave.  Lanes past the end
+// of f hold zero h.
 constexpr int kDnBatch = 4;
 
 template <int NBLD>
@@ -474,6 +480,44 @@ __device__ __forceinline__ void load_h_slice(rsrc_t hbuf, uint32_t hrow_off, int
         }
     }
 }
+
+template <int NBLD>
+__device__ __forceinline__ void load_h_slice(rsrc_t hbuf, uint32_t hrow_off, int lane, int nblk,
+                                             uint4 (&hv)[NBLD][4]) {
+#pragma unroll
+    for (int i = 0; i < NBLD; ++i) {
+        const uint32_t b = (uint32_t)min(lane + 64 * i, nblk - 1);
+        const bool ok = lane + 64 * i < nblk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 v = buf_load16(hbuf, 64u * b + 16u * q, hrow_off);
+            hv[i][q] = ok ? v : uint4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+// One MX block's 32 codes (16 bytes) dotted with the lane's h values of it.
+__device__ __forceinline__ float dot_block(uint4 c, const float4 (&hv)[8]) {
+    float s = 0.f;
+    s = dot8_fp4_f32(c.x, hv[0], hv[1], s);
+    s = dot8_fp4_f32(c.y, hv[2], hv[3], s);
+    s = dot8_fp4_f32(c.z, hv[4], hv[5], s);
+    s = dot8_fp4_f32(c.w, hv[6], hv[7], s);
+    return s;
+}
+__device__ __forceinline__ float dot_block(uint4 c, const uint4 (&hv)[4]) {
+    float s = 0.f;
+    s = dot8_fp4_bf16(c.x, hv[0], s);
+    s = dot8_fp4_bf16(c.y, hv[1], s);
+    s = dot8_fp4_bf16(c.z, hv[2], s);
+    s = dot8_fp4_bf16(c.w, hv[3], s);
+    return s;
+}
+
+// The lane's h slice of NBLD blocks: eight float4 per block for fp32 h,
+// four uint4 (bf16 pairs) for bf16 h.
+template <typename HT> struct HPart { typedef float4 type[8]; };
+template <> struct HPart<uint16_t> { typedef uint4 type[4]; };
 
 // Down rows in batches of kDnBatch: load_batch issues every code and scale
 // load of a batch, dot_batch does its math (out[rr] = h . Wd[m + rr], every
@@ -506,19 +550,15 @@ __device__ __forceinline__ void load_batch(rsrc_t codes, rsrc_t scales, int m, i
         }
 }
 
-template <int NBLD, int B = kDnBatch>
-__device__ __forceinline__ void dot_batch(const RowBuf<NBLD, B> &rb, const float4 (&hv)[NBLD][8],
+template <int NBLD, int B = kDnBatch, typename HV>
+__device__ __forceinline__ void dot_batch(const RowBuf<NBLD, B> &rb, const HV (&hv)[NBLD],
                                           int lane, int nblk, float (&out)[B]) {
 #pragma unroll
     for (int rr = 0; rr < B; ++rr) {
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < NBLD; ++i) {
-            float s = 0.f;
-            s = dot8_fp4_f32(rb.c[rr][i].x, hv[i][0], hv[i][1], s);
-            s = dot8_fp4_f32(rb.c[rr][i].y, hv[i][2], hv[i][3], s);
-            s = dot8_fp4_f32(rb.c[rr][i].z, hv[i][4], hv[i][5], s);
-            s = dot8_fp4_f32(rb.c[rr][i].w, hv[i][6], hv[i][7], s);
+            const float s = dot_block(rb.c[rr][i], hv[i]);
             acc += lane + 64 * i < nblk ? apply_e8m0(s, rb.s[rr][i]) : 0.f;
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -532,9 +572,9 @@ __device__ __forceinline__ void dot_batch(const RowBuf<NBLD, B> &rb, const float
 // so R - 1 batches' loads are in flight during each batch's math, and parks
 // it in LDS; then y = sum_j w_j o_j in fp32, slot order, one writer per
 // output.  ROWS is a multiple of B.
-template <int NBLD, int ROWS, int B, int R, int NW>
+template <int NBLD, int ROWS, int B, int R, int NW, typename HT>
 __global__ __launch_bounds__(64 * NW) void down_combine_split_kernel(
-    const float *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ ids,
+    const HT *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ ids,
     const float *__restrict__ topk_w, const int32_t *__restrict__ row_pos,
     uint16_t *__restrict__ y, int T, int d, int E, int k, int f) {
     static_assert(ROWS % B == 0, "whole batches");
@@ -547,7 +587,7 @@ __global__ __launch_bounds__(64 * NW) void down_combine_split_kernel(
     const int nblk = f >> 5;
     const uint32_t code_row = (uint32_t)f >> 1;
     const int nrows = T * k;
-    const rsrc_t hbuf = make_rsrc(h, (uint32_t)min((size_t)nrows * f * 4, (size_t)0xFFFFFFF0u));
+    const rsrc_t hbuf = make_rsrc(h, (uint32_t)min((size_t)nrows * f * sizeof(HT), (size_t)0xFFFFFFF0u));
     for (int j = wid; j < k; j += NW) {
         const int e = __builtin_amdgcn_readfirstlane(ids[(size_t)t * k + j]);
         const int p = __builtin_amdgcn_readfirstlane(row_pos[(size_t)t * k + j]);
@@ -555,8 +595,8 @@ __global__ __launch_bounds__(64 * NW) void down_combine_split_kernel(
         if (ok) {
             const rsrc_t codes = make_rsrc(W.dn_codes + (size_t)e * d * code_row, (uint32_t)d * code_row);
             const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
-            float4 hv[NBLD][8];
-            load_h_slice<NBLD>(hbuf, (uint32_t)p * f * 4u, lane, nblk, hv);
+            typename HPart<HT>::type hv[NBLD];
+            load_h_slice<NBLD>(hbuf, (uint32_t)p * f * (uint32_t)sizeof(HT), lane, nblk, hv);
             constexpr int NB = ROWS / B;
             RowBuf<NBLD, B> ring[R];
 #pragma unroll
@@ -640,23 +680,35 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
 template <int NBL>
 hipError_t launch_regx(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                        const int32_t *sorted_rows, const int32_t *plan, float *h, int T, int d,
-                       int E, int k, int f, int amax, hipStream_t s, int hstride = 0) {
+                       int E, int k, int f, int amax, hipStream_t s, int hstride = 0,
+                       bool hb = false) {
     dim3 grid(f / kRxPairs, amax);
-    (void)timed_launch("gemv_gate_up", gate_up_regx_kernel<NBL>, dim3(grid), dim3(256), (size_t)d * 2 + 16, s, x, w, offsets, sorted_rows, plan, h,
-                                                              T, d, E, k, f, hstride);
+    if (hb)
+        (void)timed_launch("gemv_gate_up", gate_up_regx_kernel<NBL, uint16_t>, dim3(grid),
+                           dim3(256), (size_t)d * 2 + 16, s, x, w, offsets, sorted_rows, plan,
+                           reinterpret_cast<uint16_t *>(h), T, d, E, k, f, hstride);
+    else
+        (void)timed_launch("gemv_gate_up", gate_up_regx_kernel<NBL, float>, dim3(grid), dim3(256),
+                           (size_t)d * 2 + 16, s, x, w, offsets, sorted_rows, plan, h, T, d, E, k,
+                           f, hstride);
     return hipGetLastError();
+}
+
+bool gemv_bf16_h_ok(int T, int d, int f) {
+    return T >= 1 && T <= 4 && d <= 8192 && f <= 4096 && f % kRxPairs == 0;
 }
 
 hipError_t launch_gemv_gate_up(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                                const int32_t *sorted_rows, const int32_t *plan, float *h,
-                               int T, int d, int E, int k, int f, hipStream_t s) {
+                               int T, int d, int E, int k, int f, hipStream_t s, bool hb) {
     const int amax = min(E, T * k);
     if (amax <= 0) return hipSuccess;
+    if (hb && !gemv_bf16_h_ok(T, d, f)) return hipErrorInvalidValue;
     const int nbl = (d / 32 + 63) / 64;               // MX blocks per lane along d
     if (f % kRxPairs == 0 && T <= 64 && nbl <= 4 && d <= 8192) {
-        if (nbl == 1) return launch_regx<1>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
-        if (nbl == 2) return launch_regx<2>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
-        return launch_regx<4>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s);
+        if (nbl == 1) return launch_regx<1>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s, 0, hb);
+        if (nbl == 2) return launch_regx<2>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s, 0, hb);
+        return launch_regx<4>(x, w, offsets, sorted_rows, plan, h, T, d, E, k, f, amax, s, 0, hb);
     }
     const int rpp = max(1, min(kRowsMax, 32768 / d));   // <= 64 KB of LDS
     dim3 grid(f / kGuPairs, amax);
@@ -736,31 +788,37 @@ bool gate_up_token_fusable(int T, int d, int E, int k, int f) {
            nbl <= 4 && d <= 8192;
 }
 
-template <int PAIRS>
-hipError_t launch_gate_up_token_p(const float *logits, const uint16_t *x, ExpertArgs w,
-                                  int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
-                                  int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, float *h,
-                                  int d, int E, int k, int f, hipStream_t s) {
-    const int nbl = (d / 32 + 63) / 64;
-    const dim3 grid(f / PAIRS, k);
-    const size_t lds = (size_t)d * 2 + 16;
-    if (nbl == 1)
-        return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<1, PAIRS>, grid, dim3(256),
-                            lds, s, logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
-                            plan, h, d, E, k, f);
-    if (nbl == 2)
-        return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<2, PAIRS>, grid, dim3(256),
-                            lds, s, logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
-                            plan, h, d, E, k, f);
-    return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<4, PAIRS>, grid, dim3(256), lds,
-                        s, logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos, plan, h,
-                        d, E, k, f);
+template <int NBL, int PAIRS, typename HT>
+hipError_t launch_token_n(const float *logits, const uint16_t *x, ExpertArgs w, int32_t *ids,
+                          float *tw, int32_t *counts, int32_t *offsets, int32_t *sorted_rows,
+                          int32_t *row_pos, int32_t *plan, HT *h, int d, int E, int k, int f,
+                          hipStream_t s) {
+    return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<NBL, PAIRS, HT>, dim3(f / PAIRS, k),
+                        dim3(256), (size_t)d * 2 + 16, s, logits, x, w, ids, tw, counts, offsets,
+                        sorted_rows, row_pos, plan, h, d, E, k, f);
 }
 
-hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertArgs w,
-                                int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
-                                int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, float *h,
-                                int d, int E, int k, int f, hipStream_t s) {
+template <int PAIRS, typename HT>
+hipError_t launch_gate_up_token_p(const float *logits, const uint16_t *x, ExpertArgs w,
+                                  int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
+                                  int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, HT *h,
+                                  int d, int E, int k, int f, hipStream_t s) {
+    const int nbl = (d / 32 + 63) / 64;
+    if (nbl == 1)
+        return launch_token_n<1, PAIRS>(logits, x, w, ids, tw, counts, offsets, sorted_rows,
+                                        row_pos, plan, h, d, E, k, f, s);
+    if (nbl == 2)
+        return launch_token_n<2, PAIRS>(logits, x, w, ids, tw, counts, offsets, sorted_rows,
+                                        row_pos, plan, h, d, E, k, f, s);
+    return launch_token_n<4, PAIRS>(logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
+                                    plan, h, d, E, k, f, s);
+}
+
+template <typename HT>
+hipError_t launch_gate_up_token_t(const float *logits, const uint16_t *x, ExpertArgs w,
+                                  int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
+                                  int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, HT *h,
+                                  int d, int E, int k, int f, hipStream_t s) {
     if (f % 48 == 0)
         return launch_gate_up_token_p<48>(logits, x, w, ids, tw, counts, offsets, sorted_rows,
                                           row_pos, plan, h, d, E, k, f, s);
@@ -768,43 +826,70 @@ hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertAr
                                       plan, h, d, E, k, f, s);
 }
 
+hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertArgs w,
+                                int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
+                                int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, float *h,
+                                int d, int E, int k, int f, hipStream_t s, bool hb) {
+    if (hb) {
+        if (!gemv_bf16_h_ok(1, d, f)) return hipErrorInvalidValue;
+        return launch_gate_up_token_t(logits, x, w, ids, tw, counts, offsets, sorted_rows,
+                                      row_pos, plan, reinterpret_cast<uint16_t *>(h), d, E, k, f,
+                                      s);
+    }
+    return launch_gate_up_token_t(logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
+                                  plan, h, d, E, k, f, s);
+}
+
 // rows per batch and batch buffers of the fused down + combine
 constexpr int kDcB = 4, kDcR = 2;
 
-template <int NBLD, int ROWS, int NW>
-void launch_dc(const float *h, ExpertArgs w, const int32_t *ids, const float *topk_w,
+template <int NBLD, int ROWS, int NW, typename HT>
+void launch_dc(const HT *h, ExpertArgs w, const int32_t *ids, const float *topk_w,
                const int32_t *row_pos, uint16_t *y, int T, int d, int E, int k, int f,
                hipStream_t s) {
-    (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, ROWS, kDcB, kDcR, NW>,
+    (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, ROWS, kDcB, kDcR, NW, HT>,
                        dim3(d / ROWS, T), dim3(64 * NW), 0, s, h, w, ids, topk_w, row_pos, y, T, d,
                        E, k, f);
 }
 
-template <int NBLD>
-hipError_t launch_dc_split(const float *h, ExpertArgs w, const int32_t *ids,
+template <int NBLD, int NW, typename HT>
+void launch_dc_rows(int rows, const HT *h, ExpertArgs w, const int32_t *ids,
+                    const float *topk_w, const int32_t *row_pos, uint16_t *y, int T, int d,
+                    int E, int k, int f, hipStream_t s) {
+    if (rows == 28) launch_dc<NBLD, 28, NW>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+    else if (rows == 16) launch_dc<NBLD, 16, NW>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+    else launch_dc<NBLD, 32, NW>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+}
+
+template <int NBLD, typename HT>
+hipError_t launch_dc_split(const HT *h, ExpertArgs w, const int32_t *ids,
                            const float *topk_w, const int32_t *row_pos, uint16_t *y, int T,
                            int d, int E, int k, int f, hipStream_t s) {
     // about one block per CU: 28 output rows per block where d allows
     // (7168 / 28 = 256), else 16 (4096 / 16 = 256) or 32; one wave per slot
-    // (16 waves, or 8 when k <= 8)
+    // (16 waves, or 8 when k <= 8), and 8 waves, two slots each, for two MX
+    // blocks per lane (whose registers do not fit 16 waves)
     const int rows = d % 28 == 0 ? 28 : (d % 16 == 0 && d / 16 <= 512 ? 16 : 32);
-    if (k <= 8) {
-        if (rows == 28) launch_dc<NBLD, 28, 8>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
-        else if (rows == 16) launch_dc<NBLD, 16, 8>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
-        else launch_dc<NBLD, 32, 8>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+    if constexpr (NBLD > 1) {
+        launch_dc_rows<NBLD, 8>(rows, h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
     } else {
-        if (rows == 28) launch_dc<NBLD, 28, 16>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
-        else if (rows == 16) launch_dc<NBLD, 16, 16>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
-        else launch_dc<NBLD, 32, 16>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+        if (k <= 8) launch_dc_rows<NBLD, 8>(rows, h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+        else launch_dc_rows<NBLD, 16>(rows, h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
                                const float *topk_w, const int32_t *row_pos, uint16_t *y,
-                               int T, int d, int E, int k, int f, hipStream_t s) {
+                               int T, int d, int E, int k, int f, hipStream_t s, bool hb) {
     if (T <= 0) return hipSuccess;
     const int nbld = (f / 32 + 63) / 64;
+    if (hb) {
+        if (!gemv_bf16_h_ok(T, d, f)) return hipErrorInvalidValue;
+        const uint16_t *hh = reinterpret_cast<const uint16_t *>(h);
+        if (nbld == 1) return launch_dc_split<1>(hh, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+        return launch_dc_split<2>(hh, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
+    }
     if (nbld <= 2) {
         if (nbld == 1) return launch_dc_split<1>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
         return launch_dc_split<2>(h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);

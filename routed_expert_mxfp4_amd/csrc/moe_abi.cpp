@@ -372,18 +372,24 @@ hipError_t run_layer(const moe_dims &D, const uint16_t *x, const uint16_t *route
         e = moe::launch_mx_round_bf16(x, D.T, D.d, xr, s);
         xa = xr;
     }
+    // bf16 mode, few tokens: h goes from gate/up to the fused down + combine
+    // as bf16 (the prefill path's two-term split of h carries the same
+    // precision); the activation-MX mode rounds an fp32 h in place
+    const bool hb = D.act == MOE_ACT_BF16 && D.T <= kFuseMaxT &&
+                    moe::gemv_bf16_h_ok(D.T, D.d, D.f);
     if (e == hipSuccess) {
         e = token_fused ? moe::launch_gate_up_token(logits, xa, W, ids, tw, counts, offsets,
                                                     sorted_rows, row_pos, plan, h, D.d, D.E,
-                                                    D.k, D.f, s)
+                                                    D.k, D.f, s, hb)
                         : moe::launch_gemv_gate_up(xa, W, offsets, sorted_rows, plan, h, D.T,
-                                                   D.d, D.E, D.k, D.f, s);
+                                                   D.d, D.E, D.k, D.f, s, hb);
     }
     if (D.act == MOE_ACT_MX_E2M3 && e == hipSuccess)
         e = moe::launch_mx_round_f32(h, D.T * D.k, D.f, h, s);
     if (D.T <= kFuseMaxT) {
         if (e == hipSuccess) {
-            e = moe::launch_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E, D.k, D.f, s);
+            e = moe::launch_down_combine(h, W, ids, tw, row_pos, y, D.T, D.d, D.E, D.k, D.f, s,
+                                         hb);
         }
     } else {
         if (e == hipSuccess) {

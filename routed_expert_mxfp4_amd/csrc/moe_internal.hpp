@@ -212,9 +212,13 @@ struct ExpertArgs {
 };
 
 // h: fp32 [T*k][f], expert-major rows (the row order of sorted_rows).
+// hb: h is stored as bf16 (h points at T*k*f bf16 values; needs
+// gemv_bf16_h_ok, else hipErrorInvalidValue), for a down + combine that
+// reads bf16 h; otherwise fp32.
+bool gemv_bf16_h_ok(int T, int d, int f);
 hipError_t launch_gemv_gate_up(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
                                const int32_t *sorted_rows, const int32_t *plan, float *h,
-                               int T, int d, int E, int k, int f, hipStream_t s);
+                               int T, int d, int E, int k, int f, hipStream_t s, bool hb = false);
 // One token: top-k, softmax and grouping inside the gate/up GEMV (writes
 // ids, tw, counts, offsets, sorted_rows, row_pos and plan as the permute
 // step would).  Needs gate_up_token_fusable.
@@ -222,7 +226,7 @@ bool gate_up_token_fusable(int T, int d, int E, int k, int f);
 hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertArgs w,
                                 int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
                                 int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, float *h,
-                                int d, int E, int k, int f, hipStream_t s);
+                                int d, int E, int k, int f, hipStream_t s, bool hb = false);
 hipError_t launch_gemv_down(const float *h, ExpertArgs w, const int32_t *offsets,
                             const int32_t *plan, uint16_t *rows_out, int T, int d, int E,
                             int k, int f, hipStream_t s);
@@ -239,7 +243,7 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *out, int 
 hipError_t launch_mfma_rate(int kind, int blocks, int iters, float *out, hipStream_t s);
 hipError_t launch_down_combine(const float *h, ExpertArgs w, const int32_t *ids,
                                const float *topk_w, const int32_t *row_pos, uint16_t *y,
-                               int T, int d, int E, int k, int f, hipStream_t s);
+                               int T, int d, int E, int k, int f, hipStream_t s, bool hb = false);
 // The mixed path's small experts (at most gemv_max rows each, listed in
 // small[]: count, then ids): the grouped GEMVs with their fp32 h rows at
 // small-expert index * gemv_max of h_small.  Need gemv_small_ok(d, f).

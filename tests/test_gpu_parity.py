@@ -77,6 +77,7 @@ SMALL_CASES = [
     (1, 256, 16, 2, 128, 11),
     (3, 192, 40, 5, 64, 12),        # odd chunk length (d/64 = 3), E not a multiple of 64
     (5, 128, 7, 7, 32, 13),         # k = E, a single MX block along f
+    (4, 256, 40, 12, 2560, 17),     # few tokens, bf16 h, two MX blocks of h per lane
     (17, 512, 70, 1, 96, 14),       # k = 1, ragged T
     (300, 128, 24, 3, 64, 15),      # T > 256: multi-block grouping
     (70, 64, 130, 4, 32, 16),       # E > 128
@@ -163,6 +164,10 @@ ONE_TOKEN_CASES = [
     (1, 512, 64, 8, 1536, 35),
     (1, 256, 40, 16, 1536, 36),      # k = 16, chunk length 4
     (1, 192, 20, 20, 1536, 37),      # k = E, odd chunk length
+    # f = 2560: two MX blocks of h per lane in the down pass (8-wave blocks,
+    # two slots a wave when k > 8)
+    (1, 512, 40, 16, 2560, 38),
+    (1, 448, 24, 6, 2560, 39),       # d a multiple of 28 (28-row blocks), k <= 8
 ]
 
 
