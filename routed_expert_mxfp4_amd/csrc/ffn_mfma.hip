@@ -507,6 +507,51 @@ __device__ __forceinline__ void issue_step_deep(const Plan8 &P, uint32_t lds, in
                        (int)(b_st + 1024u * (uint32_t)(wid + kWaves * j))));
 }
 
+// 16-row tiles on the canonical store, super-steps of two K steps: a weight
+// row's 128 bytes of two steps are one cache line, so each load takes 8 rows
+// x 128 bytes (whole lines) instead of 16 rows x 64 bytes (half lines, the
+// pattern the operand layout would need).  Lane l of load i (rows 8 i ..
+// 8 i + 7 of the block's 512) reads row 8 i + l % 8, bytes 16 (l / 8) of the
+// line, and lands at 16 l: piece p of row r sits at 1024 i + 128 p + 16 r,
+// so the fragment of step h (0, 1) and K group g of row r is piece 4 h + g.
+// Two super-stages of 64 KB (one loading while the other is multiplied),
+// four one-step A stages and the scale group.
+constexpr int kSupAStage = 4096;
+constexpr int kSupBBase = 4 * kSupAStage;
+constexpr int kSupBStage = 64 * 1024;
+constexpr int kSupSBase = kSupBBase + 2 * kSupBStage;
+static_assert(kSupSBase + kSGroupBytes <= kLdsBytes, "the super-step ring fits the block's LDS");
+
+// Super-step S's loads: the activations of steps 2S and 2S + 1 (and, at
+// 2S % 4 == 0, the scale group), then the weight lines of both steps into
+// super-stage S % 2.
+template <bool kGateUp>
+__device__ __forceinline__ void issue_super(const Plan8 &P, uint32_t lds, int S, int wid,
+                                            const uint32_t (&line_src)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kk = 2 * S + h;
+        const uint32_t a_st = lds + (uint32_t)(kk & 3) * kSupAStage;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < P.n_a)
+                lds_load16(P.ra, P.a_src[j] + (uint32_t)kk * kStepBytes,
+                           (uint32_t)__builtin_amdgcn_readfirstlane(
+                               (int)(a_st + 1024u * (uint32_t)(wid + kWaves * j))));
+        }
+        if ((kk & 3) == 0)
+            lds_load16(P.rs, P.s_src + (uint32_t)(kk >> 2) * P.sgrp,
+                       (uint32_t)__builtin_amdgcn_readfirstlane(
+                           (int)(lds + kSupSBase + 1024u * (uint32_t)wid)));
+    }
+    const uint32_t b_st = lds + kSupBBase + (uint32_t)(S & 1) * kSupBStage;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)        // loads 2 t and 2 t + 1 of operand tiles t = wid + 8 (j / 2)
+        lds_load16(P.rb, line_src[j] + 128u * (uint32_t)S,
+                   (uint32_t)__builtin_amdgcn_readfirstlane(
+                       (int)(b_st + 1024u * (uint32_t)(2 * (wid + kWaves * (j >> 1)) + (j & 1)))));
+}
+
 // Waits until at most n of the wave's loads are outstanding; n is one of
 // the values the deep ring produces (0, or one or two later steps' loads).
 __device__ __forceinline__ void deep_wait(int n) {
@@ -610,23 +655,69 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
         chain8<0, kMtw, kNtw, kSingle>(acc, fa, fb, a, s);
     };
     if constexpr (MT == 1) {
-        // the deep ring: steps 0..2 first, then step kk + 3 at step kk
-        const uint32_t sgrp_lane = lds_addr + kDeepSBase + 256u * (uint32_t)nbase + 16u * (uint32_t)r16;
-        for (int s0 = 0; s0 < 3 && s0 < P.nsteps; ++s0) issue_step_deep(P, lds_addr, s0, wid);
-        for (int kk = 0; kk < P.nsteps; ++kk) {
-            // step kk's loads, with those of the (at most two) later steps
-            // issued so far still allowed in flight
-            const int pend = min(2, P.nsteps - 1 - kk);
-            const int scl = (pend >= 1 && ((kk + 1) & 3) == 0) + (pend >= 2 && ((kk + 2) & 3) == 0);
-            deep_wait(pend * (P.n_a + kBLoads) + scl);
-            __builtin_amdgcn_s_barrier();                   // everyone's; step kk-1's stages free
-            __builtin_amdgcn_sched_barrier(0);
-            if ((kk & 3) == 0) read_group_scales<kNtw>(spk, sgrp_lane, psel01);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk + 3 < P.nsteps) issue_step_deep(P, lds_addr, kk + 3, wid);
-            __builtin_amdgcn_sched_barrier(0);
-            multiply(lds_addr + (uint32_t)((kk & 3) * kDeepAStage),
-                     lds_addr + kDeepBBase + (uint32_t)((kk & 3) * kBStageBytes), kk);
+        if (!packed && (P.nsteps & 1) == 0) {
+            // super-steps of two K steps, one ahead (see issue_super)
+            uint32_t line_src[8];
+            {
+                const uint32_t code_row = (uint32_t)(kGateUp ? d : f) >> 1;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = wid + kWaves * (j >> 1);
+                    const uint32_t row = (uint32_t)tile_row<kGateUp, MT>(t, ts.nb, f) + 8u * (uint32_t)(j & 1) +
+                                         (uint32_t)(lane & 7);
+                    line_src[j] = row * code_row + 16u * (uint32_t)(lane >> 3);
+                }
+            }
+            // this lane's fragment offset in a super-stage, step h = 0 (h = 1: + 512)
+            const uint32_t frag_lane = 1024u * (uint32_t)(r16 >> 3) + 128u * (uint32_t)g + 16u * (uint32_t)(r16 & 7);
+            const uint32_t sgrp_lane = lds_addr + kSupSBase + 256u * (uint32_t)nbase + 16u * (uint32_t)r16;
+            const int NS = P.nsteps >> 1;
+            issue_super<kGateUp>(P, lds_addr, 0, wid, line_src);
+            for (int S = 0; S < NS; ++S) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));       // super-step S's loads, the only ones out
+                __builtin_amdgcn_s_barrier();                   // everyone's; super-step S - 1's stages free
+                __builtin_amdgcn_sched_barrier(0);
+                if ((S & 1) == 0) read_group_scales<kNtw>(spk, sgrp_lane, psel01);
+                __builtin_amdgcn_sched_barrier(0);
+                if (S + 1 < NS) issue_super<kGateUp>(P, lds_addr, S + 1, wid, line_src);
+                __builtin_amdgcn_sched_barrier(0);
+                const uint32_t b_st = lds_addr + kSupBBase + (uint32_t)(S & 1) * kSupBStage;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int kk = 2 * S + h;
+                    BFrags<kNtw> fb;
+#pragma unroll
+                    for (int nt = 0; nt < kNtw; ++nt) {
+                        fb.q[nt] = ds_read128_at(b_st + 2048u * (uint32_t)(nbase + nt) + frag_lane + 512u * (uint32_t)h);
+                        fb.sc[nt] = spk[nt] >> (8 * (kk & 3));
+                    }
+                    AFrag fa[2];
+                    const uint32_t st = lds_addr + (uint32_t)(kk & 3) * kSupAStage;
+                    const uint32_t a = st + a_lane, sa = st + s_lane;
+                    read_afrag<0>(fa[0], a, sa);
+                    bfrags_ready<kNtw, 0>(fb);
+                    chain8<0, kMtw, kNtw, kSingle>(acc, fa, fb, a, sa);
+                }
+            }
+        } else {
+            // the deep ring: steps 0..2 first, then step kk + 3 at step kk
+            const uint32_t sgrp_lane = lds_addr + kDeepSBase + 256u * (uint32_t)nbase + 16u * (uint32_t)r16;
+            for (int s0 = 0; s0 < 3 && s0 < P.nsteps; ++s0) issue_step_deep(P, lds_addr, s0, wid);
+            for (int kk = 0; kk < P.nsteps; ++kk) {
+                // step kk's loads, with those of the (at most two) later steps
+                // issued so far still allowed in flight
+                const int pend = min(2, P.nsteps - 1 - kk);
+                const int scl = (pend >= 1 && ((kk + 1) & 3) == 0) + (pend >= 2 && ((kk + 2) & 3) == 0);
+                deep_wait(pend * (P.n_a + kBLoads) + scl);
+                __builtin_amdgcn_s_barrier();                   // everyone's; step kk-1's stages free
+                __builtin_amdgcn_sched_barrier(0);
+                if ((kk & 3) == 0) read_group_scales<kNtw>(spk, sgrp_lane, psel01);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk + 3 < P.nsteps) issue_step_deep(P, lds_addr, kk + 3, wid);
+                __builtin_amdgcn_sched_barrier(0);
+                multiply(lds_addr + (uint32_t)((kk & 3) * kDeepAStage),
+                         lds_addr + kDeepBBase + (uint32_t)((kk & 3) * kBStageBytes), kk);
+            }
         }
     } else {
         // prologue: step 0's activations and scale group, steps 0 and 1's codes
