@@ -14,6 +14,7 @@
 // Down: o[p][m] = h[p] . Wd[m] -> bf16 rows_out (expert-major), or fused
 // with the weighted combine per token for small T.
 #include "moe_internal.hpp"
+#include "mx_split.hpp"
 #include "select_dev.hpp"
 
 namespace moe {
@@ -366,40 +367,84 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// One token on the matrix cores, with the GEMV's load pattern.  A wave
+// streams one weight row at a time as the vector-ALU kernel does (lane l
+// holds the MX blocks l + 64 i of the row), and one scaled MFMA
+// (16x16x128, FP6 x FP4) per i takes those 64 blocks as its B operand -- B
+// row l % 16, K group l / 16 is lane l's block, with the block's own E8M0
+// scale -- against the same blocks of x as A (each lane's x block split in
+// two MX E2M3 terms, two MFMAs).  C[j][j] is then the dot over the four
+// blocks of lanes j + 16 g, so the trace of C is the row's dot product; the
+// off-diagonal products are not used.  The weights need no conversion on
+// the vector ALU; x is split once per block, by waves 1..3 while wave 0
+// selects the experts.
+// ---------------------------------------------------------------------------
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// One lane's A operand: its x block as two E2M3 terms and their scales
+// (byte 0 hi, byte 1 lo).  Lanes past the end of d hold zero codes.
+struct XSplit {
+    i32x8_t hi, lo;
+    uint32_t sc;
+};
+
+// The trace of a 16 x 16 product: lane l holds C[4 (l / 16) + r][l % 16] in
+// acc[r], so the diagonal sits in lanes 16 g + c with r = c - 4 g in 0..3.
+__device__ __forceinline__ float mfma_trace16(f32x4_t acc, int lane) {
+    const int r = (lane & 15) - 4 * (lane >> 4);
+    float v = 0.f;
+    v = r == 0 ? acc[0] : v;
+    v = r == 1 ? acc[1] : v;
+    v = r == 2 ? acc[2] : v;
+    v = r == 3 ? acc[3] : v;
+    return wave_sum_f32(v);
+}
+
+template <int NBL>
+__device__ __forceinline__ float pair_h_mfma(const PairBuf<NBL> &pb, const XSplit (&xa)[NBL],
+                                             int lane, int nblk) {
+    f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+        const bool ok = lane + 64 * i < nblk;
+        const uint4 wg = pb.c[0][i], wu = pb.c[1][i];
+        const i32x8_t bg = {(int)wg.x, (int)wg.y, (int)wg.z, (int)wg.w, 0, 0, 0, 0};
+        const i32x8_t bu = {(int)wu.x, (int)wu.y, (int)wu.z, (int)wu.w, 0, 0, 0, 0};
+        // lanes past the end carry a duplicate block: scale 2^0 against zero x
+        const int sg = ok ? (int)pb.s[0][i] : 127, su = ok ? (int)pb.s[1][i] : 127;
+        cg = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa[i].hi, bg, cg, 2, 4, 0, (int)xa[i].sc, 0, sg);
+        cu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa[i].hi, bu, cu, 2, 4, 0, (int)xa[i].sc, 0, su);
+        cg = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa[i].lo, bg, cg, 2, 4, 1, (int)xa[i].sc, 0, sg);
+        cu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xa[i].lo, bu, cu, 2, 4, 1, (int)xa[i].sc, 0, su);
+    }
+    return silu_mul(mfma_trace16(cg, lane), mfma_trace16(cu, lane));
+}
+
 // One token (T = 1): the top-k and the grouping happen inside the gate/up
 // pass.  Every block selects the token's experts itself from the logits row
-// (E floats, read by one wave) while x is staged; the k selected experts are
-// distinct, so in ascending expert order the a-th of them is the one whose h
-// row is a, routed from top-k slot sorted_rows[a] -- exactly the grouping of
-// the permute step.  Block (0, 0) writes that grouping (ids, weights,
-// counts, offsets, sorted_rows, row_pos, plan) for the later kernels.
+// (E floats, read by wave 0) while waves 1..3 split x; the k selected
+// experts are distinct, so in ascending expert order the a-th of them is
+// the one whose h row is a, routed from top-k slot sorted_rows[a] -- exactly
+// the grouping of the permute step.  Block (0, 0) writes that grouping (ids,
+// weights, counts, offsets, sorted_rows, row_pos, plan) for the later
+// kernels.  Each wave streams its output pairs as gate_up_regx_kernel does,
+// the next pair's loads issued before the current pair's products.
 template <int NBL, int PAIRS, typename HT>
-__global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
+__global__ __launch_bounds__(256) void gate_up_mfma_token_kernel(
     const float *__restrict__ logits, const uint16_t *__restrict__ x, ExpertArgs W,
     int32_t *__restrict__ ids, float *__restrict__ tw, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
     int32_t *__restrict__ row_pos, int32_t *__restrict__ plan, HT *__restrict__ h, int d,
     int E, int k, int f) {
-    extern __shared__ uint4 xs[];                 // the token row, d/8 x 16 B, + 1 spare
+    extern __shared__ uint4 xsr[];                // [d / 32] split records of 64 bytes
     __shared__ __align__(16) uint32_t tsc[kTopkScratch];
     __shared__ int sel[32];                       // selected experts, ascending
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int nvec = d >> 3;
+    const int nblk = d >> 5;
     const bool first = blockIdx.x == 0 && blockIdx.y == 0;
-    {
-        const uint4 *xrow = reinterpret_cast<const uint4 *>(x);
-        uint4 tmp[kStageX];
-#pragma unroll
-        for (int j = 0; j < kStageX; ++j)
-            tmp[j] = xrow[min((int)threadIdx.x + 256 * j, nvec - 1)];
-        loads_done(tmp);                            // all loads before any store
-#pragma unroll
-        for (int j = 0; j < kStageX; ++j) {         // spare slot: no branch per store
-            const int i = (int)threadIdx.x + 256 * j;
-            xs[i < nvec ? i : nvec] = tmp[j];
-        }
-    }
     if (wid == 0) {
         int e;
         float wt;
@@ -417,6 +462,28 @@ __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
             }
         }
         if (first && lane == 0) plan[0] = k;
+    } else {
+        // x split once: record b = hi codes [0, 24), lo codes [24, 48),
+        // scales at 48 (hi) and 49 (lo)
+        for (int b = (int)threadIdx.x - 64; b < nblk; b += 192) {
+            const uint4 *xb = reinterpret_cast<const uint4 *>(x) + 4 * b;
+            float v[32];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 w = xb[q];
+                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v[8 * q + 2 * t] = __uint_as_float(ww[t] << 16);
+                    v[8 * q + 2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
+                }
+            }
+            const SplitBlock sb = split_block32(v);
+            xsr[4 * b + 0] = uint4{sb.hi[0], sb.hi[1], sb.hi[2], sb.hi[3]};
+            xsr[4 * b + 1] = uint4{sb.hi[4], sb.hi[5], sb.lo[0], sb.lo[1]};
+            xsr[4 * b + 2] = uint4{sb.lo[2], sb.lo[3], sb.lo[4], sb.lo[5]};
+            xsr[4 * b + 3] = uint4{sb.scales, 0u, 0u, 0u};
+        }
     }
     __syncthreads();
     if (first) {
@@ -433,7 +500,21 @@ __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
     const int a = blockIdx.y;
     const int e = sel[a];
     if ((unsigned)e >= (unsigned)E) return;
-    const int nblk = d >> 5;
+    XSplit xa[NBL];
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+        const int b = lane + 64 * i;
+        if (b < nblk) {
+            const uint4 q0 = xsr[4 * b], q1 = xsr[4 * b + 1], q2 = xsr[4 * b + 2], q3 = xsr[4 * b + 3];
+            xa[i].hi = i32x8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, 0, 0};
+            xa[i].lo = i32x8_t{(int)q1.z, (int)q1.w, (int)q2.x, (int)q2.y, (int)q2.z, (int)q2.w, 0, 0};
+            xa[i].sc = q3.x;
+        } else {
+            xa[i].hi = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            xa[i].lo = xa[i].hi;
+            xa[i].sc = 0x7F7Fu;
+        }
+    }
     const uint32_t code_row = (uint32_t)d >> 1;
     const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
     const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
@@ -446,13 +527,13 @@ __global__ __launch_bounds__(256) void gate_up_regx_token_kernel(
     for (int q = 0; q < kPerWave; q += 2) {
         load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
         __builtin_amdgcn_sched_barrier(0);
-        const float va = pair_h<NBL>(A, xs, lane, nblk);
+        const float va = pair_h_mfma<NBL>(A, xa, lane, nblk);
         if (lane == 0) put_h(hrow + n_base + 4 * q, va);
         __builtin_amdgcn_sched_barrier(0);
         if (q + 2 < kPerWave)
             load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
         __builtin_amdgcn_sched_barrier(0);
-        const float vb = pair_h<NBL>(B, xs, lane, nblk);
+        const float vb = pair_h_mfma<NBL>(B, xa, lane, nblk);
         if (lane == 0) put_h(hrow + n_base + 4 * (q + 1), vb);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -566,6 +647,73 @@ __device__ __forceinline__ void dot_batch(const RowBuf<NBLD, B> &rb, const HV (&
     }
 }
 
+// The lane's h slice as the matrix cores' A operand: each MX block of it
+// split in two E2M3 terms (lanes past the end of f: zero codes).
+__device__ __forceinline__ void h_block_values(const float4 (&hv)[8], float (&v)[32]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        v[4 * q] = hv[q].x;
+        v[4 * q + 1] = hv[q].y;
+        v[4 * q + 2] = hv[q].z;
+        v[4 * q + 3] = hv[q].w;
+    }
+}
+__device__ __forceinline__ void h_block_values(const uint4 (&hv)[4], float (&v)[32]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t ww[4] = {hv[q].x, hv[q].y, hv[q].z, hv[q].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            v[8 * q + 2 * t] = __uint_as_float(ww[t] << 16);
+            v[8 * q + 2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
+        }
+    }
+}
+
+template <int NBLD, typename HV>
+__device__ __forceinline__ void split_h_slice(const HV (&hv)[NBLD], int lane, int nblk,
+                                              XSplit (&ha)[NBLD]) {
+#pragma unroll
+    for (int i = 0; i < NBLD; ++i) {
+        float v[32];
+        h_block_values(hv[i], v);
+        const SplitBlock sb = split_block32(v);
+        const bool ok = lane + 64 * i < nblk;
+        ha[i].hi = ok ? i32x8_t{(int)sb.hi[0], (int)sb.hi[1], (int)sb.hi[2], (int)sb.hi[3],
+                                (int)sb.hi[4], (int)sb.hi[5], 0, 0}
+                      : i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        ha[i].lo = ok ? i32x8_t{(int)sb.lo[0], (int)sb.lo[1], (int)sb.lo[2], (int)sb.lo[3],
+                                (int)sb.lo[4], (int)sb.lo[5], 0, 0}
+                      : i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        ha[i].sc = ok ? sb.scales : 0x7F7Fu;
+    }
+}
+
+// out[rr] = h . Wd[m + rr] for a batch: per row and MX block of the lanes,
+// two scaled MFMAs (the h terms against the row's blocks, as in
+// pair_h_mfma), the row's dot the trace of the product.
+template <int NBLD, int B>
+__device__ __forceinline__ void dot_batch_mfma(const RowBuf<NBLD, B> &rb, const XSplit (&ha)[NBLD],
+                                               int lane, int nblk, float (&out)[B]) {
+    f32x4_t c[B];
+#pragma unroll
+    for (int rr = 0; rr < B; ++rr) c[rr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NBLD; ++i) {
+        const bool ok = lane + 64 * i < nblk;
+#pragma unroll
+        for (int rr = 0; rr < B; ++rr) {
+            const uint4 w = rb.c[rr][i];
+            const i32x8_t bw = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+            const int sw = ok ? (int)rb.s[rr][i] : 127;
+            c[rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ha[i].hi, bw, c[rr], 2, 4, 0, (int)ha[i].sc, 0, sw);
+            c[rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ha[i].lo, bw, c[rr], 2, 4, 1, (int)ha[i].sc, 0, sw);
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < B; ++rr) out[rr] = mfma_trace16(c[rr], lane);
+}
+
 // Fused down + combine for small T: block (ROWS output rows, token t) of NW
 // waves; wave j computes slot j's expert output for the block's rows (j =
 // wid, wid + NW, ...) in batches of B rows held in a ring of R batch buffers,
@@ -595,8 +743,12 @@ __global__ __launch_bounds__(64 * NW) void down_combine_split_kernel(
         if (ok) {
             const rsrc_t codes = make_rsrc(W.dn_codes + (size_t)e * d * code_row, (uint32_t)d * code_row);
             const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
-            typename HPart<HT>::type hv[NBLD];
-            load_h_slice<NBLD>(hbuf, (uint32_t)p * f * (uint32_t)sizeof(HT), lane, nblk, hv);
+            XSplit ha[NBLD];
+            {
+                typename HPart<HT>::type hv[NBLD];
+                load_h_slice<NBLD>(hbuf, (uint32_t)p * f * (uint32_t)sizeof(HT), lane, nblk, hv);
+                split_h_slice<NBLD>(hv, lane, nblk, ha);
+            }
             constexpr int NB = ROWS / B;
             RowBuf<NBLD, B> ring[R];
 #pragma unroll
@@ -609,7 +761,7 @@ __global__ __launch_bounds__(64 * NW) void down_combine_split_kernel(
                                         ring[(bi + R - 1) % R]);
                 __builtin_amdgcn_sched_barrier(0);
                 float out[B];
-                dot_batch<NBLD, B>(ring[bi % R], hv, lane, nblk, out);
+                dot_batch_mfma<NBLD, B>(ring[bi % R], ha, lane, nblk, out);
                 if (lane == 0) {
 #pragma unroll
                     for (int rr = 0; rr < B; ++rr) part[j][bi * B + rr] = out[rr];
@@ -793,7 +945,7 @@ hipError_t launch_token_n(const float *logits, const uint16_t *x, ExpertArgs w, 
                           float *tw, int32_t *counts, int32_t *offsets, int32_t *sorted_rows,
                           int32_t *row_pos, int32_t *plan, HT *h, int d, int E, int k, int f,
                           hipStream_t s) {
-    return timed_launch("gemv_gate_up", gate_up_regx_token_kernel<NBL, PAIRS, HT>, dim3(f / PAIRS, k),
+    return timed_launch("gemv_gate_up", gate_up_mfma_token_kernel<NBL, PAIRS, HT>, dim3(f / PAIRS, k),
                         dim3(256), (size_t)d * 2 + 16, s, logits, x, w, ids, tw, counts, offsets,
                         sorted_rows, row_pos, plan, h, d, E, k, f);
 }
