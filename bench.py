@@ -588,7 +588,8 @@ def main():
     roofline["launch_us_percentiles"] = launch_pct
     roofline["timed_every"] = every
     # the same launch against what this GPU measurably sustains for its bound
-    if roofline["bound"] == "hbm":
+    if roofline["bound"] == "hbm" and roofline["algorithmic_bytes_per_launch"] >= 16:
+        # (a crossover override can leave the scaled-MFMA call no expert)
         mp, blocks = stream_read_gbps(int(roofline["algorithmic_bytes_per_launch"]))
         roofline["measured_peak"] = {
             "value": mp, "unit": "GB/s", "frac": roofline["achieved"] / mp,

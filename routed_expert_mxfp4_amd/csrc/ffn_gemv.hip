@@ -242,13 +242,13 @@ __global__ __launch_bounds__(64) void down_combine_kernel(
 constexpr int kRxPairs = 32;         // gate/up pairs per block (8 per wave)
 // the one-token kernel: 48 pairs (512 blocks at f = 1536, k = 16: one round
 // of two per CU) when f allows, else 32
-constexpr int kStageX = 4;           // x staging: d <= 4 * 256 * 8 = 8192
 
 // Gate/up for decode-sized groups, software-pipelined: lane l owns the MX
-// blocks b = l + 64 i (i < NBL) of d; the token row is staged once in LDS
+// blocks b = l + 64 i (i < NBL) of d; the token row is split once into LDS
 // (shared by the block's four waves) and each wave streams its output pairs
-// with the next pair's code loads issued before the current pair's math, so
-// HBM reads and VALU work overlap instead of alternating.
+// with the next pair's code loads issued before the current pair's dots (on
+// the matrix cores, below), so HBM reads and arithmetic overlap instead of
+// alternating.
 // h elements: fp32, or bf16 (the one-token and few-token paths of the bf16
 // mode, whose down pass then dots bf16 pairs, as the gate/up pass does).
 __device__ __forceinline__ void put_h(float *p, float v) { *p = v; }
@@ -275,100 +275,8 @@ __device__ __forceinline__ void load_pair(rsrc_t codes, rsrc_t scales, int n, in
     }
 }
 
-template <int NBL>
-__device__ __forceinline__ float pair_h(const PairBuf<NBL> &pb, const uint4 *__restrict__ xs,
-                                        int lane, int nblk) {
-    float g = 0.f, u = 0.f;
-#pragma unroll
-    for (int i = 0; i < NBL; ++i) {
-        const int b = min(lane + 64 * i, nblk - 1);
-        const bool ok = lane + 64 * i < nblk;
-        const uint4 x0 = xs[4 * b], x1 = xs[4 * b + 1], x2 = xs[4 * b + 2], x3 = xs[4 * b + 3];
-        float pg = 0.f, pu = 0.f;
-        pg = dot8_fp4_bf16(pb.c[0][i].x, x0, pg);
-        pu = dot8_fp4_bf16(pb.c[1][i].x, x0, pu);
-        pg = dot8_fp4_bf16(pb.c[0][i].y, x1, pg);
-        pu = dot8_fp4_bf16(pb.c[1][i].y, x1, pu);
-        pg = dot8_fp4_bf16(pb.c[0][i].z, x2, pg);
-        pu = dot8_fp4_bf16(pb.c[1][i].z, x2, pu);
-        pg = dot8_fp4_bf16(pb.c[0][i].w, x3, pg);
-        pu = dot8_fp4_bf16(pb.c[1][i].w, x3, pu);
-        g += ok ? apply_e8m0(pg, pb.s[0][i]) : 0.f;
-        u += ok ? apply_e8m0(pu, pb.s[1][i]) : 0.f;
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    g = wave_sum_f32(g);
-    u = wave_sum_f32(u);
-    return silu_mul(g, u);
-}
-
-// Experts a = blockIdx.y, blockIdx.y + gridDim.y, ... of the plan.  h row of
-// (expert a, its r-th row): row0 + r, or a * hstride + r when hstride > 0
-// (the compact rows of the mixed path's small experts).
-template <int NBL, typename HT>
-__global__ __launch_bounds__(256) void gate_up_regx_kernel(
-    const uint16_t *__restrict__ x, ExpertArgs W, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
-    HT *__restrict__ h, int T, int d, int E, int k, int f, int hstride) {
-    const int nrows = T * k;
-    for (int a = blockIdx.y; a < plan[0]; a += gridDim.y) {
-    int e, row0, ne;
-    if (!expert_group(plan, offsets, a, E, nrows, e, row0, ne)) continue;
-    if (hstride > 0 && ne > hstride) continue;
-    extern __shared__ uint4 xs[];                 // one token row, d/8 x 16 B, + 1 spare
-    const int lane = threadIdx.x & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int nblk = d >> 5;
-    const int nvec = d >> 3;
-    const uint32_t code_row = (uint32_t)d >> 1;
-    const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
-    const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
-    constexpr int kPerWave = kRxPairs / 4;        // pairs n_base + wid + 4 q
-    const int n_base = blockIdx.x * kRxPairs + wid;
-    for (int r = 0; r < ne; ++r) {
-        const int row = sorted_rows[row0 + r];
-        const int tok = (unsigned)row < (unsigned)nrows ? row / k : 0;
-        PairBuf<NBL> A, B;
-        load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);   // before the x sync
-        __syncthreads();
-        {
-            const uint4 *xrow = reinterpret_cast<const uint4 *>(x + (size_t)tok * d);
-            uint4 tmp[kStageX];
-#pragma unroll
-            for (int j = 0; j < kStageX; ++j)
-                tmp[j] = xrow[min((int)threadIdx.x + 256 * j, nvec - 1)];
-            loads_done(tmp);                        // all loads before any store
-#pragma unroll
-            for (int j = 0; j < kStageX; ++j) {     // spare slot: no branch per store
-                const int i = (int)threadIdx.x + 256 * j;
-                xs[i < nvec ? i : nvec] = tmp[j];
-            }
-        }
-        __syncthreads();
-        HT *hrow = h + (size_t)(hstride > 0 ? a * hstride + r : row0 + r) * f;
-        // sched_barrier keeps each stage in place: a later pair's loads may
-        // not be hoisted above an earlier pair's math (that would only grow
-        // the register footprint, not the bytes in flight)
-#pragma unroll 1
-        for (int q = 0; q < kPerWave; q += 2) {
-            load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
-            __builtin_amdgcn_sched_barrier(0);
-            const float va = pair_h<NBL>(A, xs, lane, nblk);
-            if (lane == 0) put_h(hrow + n_base + 4 * q, va);
-            __builtin_amdgcn_sched_barrier(0);
-            if (q + 2 < kPerWave)
-                load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
-            __builtin_amdgcn_sched_barrier(0);
-            const float vb = pair_h<NBL>(B, xs, lane, nblk);
-            if (lane == 0) put_h(hrow + n_base + 4 * (q + 1), vb);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// One token on the matrix cores, with the GEMV's load pattern.  A wave
+// Dots on the matrix cores, with the GEMV's load pattern.  A wave
 // streams one weight row at a time as the vector-ALU kernel does (lane l
 // holds the MX blocks l + 64 i of the row), and one scaled MFMA
 // (16x16x128, FP6 x FP4) per i takes those 64 blocks as its B operand -- B
@@ -377,8 +285,7 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
 // two MX E2M3 terms, two MFMAs).  C[j][j] is then the dot over the four
 // blocks of lanes j + 16 g, so the trace of C is the row's dot product; the
 // off-diagonal products are not used.  The weights need no conversion on
-// the vector ALU; x is split once per block, by waves 1..3 while wave 0
-// selects the experts.
+// the vector ALU; x is split once per token row into LDS.
 // ---------------------------------------------------------------------------
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -422,6 +329,106 @@ __device__ __forceinline__ float pair_h_mfma(const PairBuf<NBL> &pb, const XSpli
     return silu_mul(mfma_trace16(cg, lane), mfma_trace16(cu, lane));
 }
 
+// x row (bf16 [d]) split into records of 64 bytes per MX block in LDS: hi
+// codes [0, 24), lo codes [24, 48), scales at 48 (hi) and 49 (lo); threads
+// t0, t0 + stride, .. take a block each.
+__device__ __forceinline__ void split_x_to_lds(const uint16_t *__restrict__ xrow, int nblk, int t0,
+                                               int stride, uint4 *xsr) {
+    for (int b = t0; b < nblk; b += stride) {
+        const uint4 *xb = reinterpret_cast<const uint4 *>(xrow) + 4 * b;
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 w = xb[q];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v[8 * q + 2 * t] = __uint_as_float(ww[t] << 16);
+                v[8 * q + 2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
+            }
+        }
+        const SplitBlock sb = split_block32(v);
+        xsr[4 * b + 0] = uint4{sb.hi[0], sb.hi[1], sb.hi[2], sb.hi[3]};
+        xsr[4 * b + 1] = uint4{sb.hi[4], sb.hi[5], sb.lo[0], sb.lo[1]};
+        xsr[4 * b + 2] = uint4{sb.lo[2], sb.lo[3], sb.lo[4], sb.lo[5]};
+        xsr[4 * b + 3] = uint4{sb.scales, 0u, 0u, 0u};
+    }
+}
+
+// The lane's A operands (blocks lane + 64 i) from the split records.
+template <int NBL>
+__device__ __forceinline__ void load_xsplit(const uint4 *xsr, int lane, int nblk,
+                                            XSplit (&xa)[NBL]) {
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+        const int b = lane + 64 * i;
+        if (b < nblk) {
+            const uint4 q0 = xsr[4 * b], q1 = xsr[4 * b + 1], q2 = xsr[4 * b + 2], q3 = xsr[4 * b + 3];
+            xa[i].hi = i32x8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, 0, 0};
+            xa[i].lo = i32x8_t{(int)q1.z, (int)q1.w, (int)q2.x, (int)q2.y, (int)q2.z, (int)q2.w, 0, 0};
+            xa[i].sc = q3.x;
+        } else {
+            xa[i].hi = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            xa[i].lo = xa[i].hi;
+            xa[i].sc = 0x7F7Fu;
+        }
+    }
+}
+
+// Experts a = blockIdx.y, blockIdx.y + gridDim.y, ... of the plan.  h row of
+// (expert a, its r-th row): row0 + r, or a * hstride + r when hstride > 0
+// (the compact rows of the mixed path's small experts).
+template <int NBL, typename HT>
+__global__ __launch_bounds__(256) void gate_up_regx_kernel(
+    const uint16_t *__restrict__ x, ExpertArgs W, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ sorted_rows, const int32_t *__restrict__ plan,
+    HT *__restrict__ h, int T, int d, int E, int k, int f, int hstride) {
+    const int nrows = T * k;
+    for (int a = blockIdx.y; a < plan[0]; a += gridDim.y) {
+    int e, row0, ne;
+    if (!expert_group(plan, offsets, a, E, nrows, e, row0, ne)) continue;
+    if (hstride > 0 && ne > hstride) continue;
+    extern __shared__ uint4 xsr[];                // one token row split, d/32 records of 64 B
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int nblk = d >> 5;
+    const uint32_t code_row = (uint32_t)d >> 1;
+    const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
+    const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
+    constexpr int kPerWave = kRxPairs / 4;        // pairs n_base + wid + 4 q
+    const int n_base = blockIdx.x * kRxPairs + wid;
+    for (int r = 0; r < ne; ++r) {
+        const int row = sorted_rows[row0 + r];
+        const int tok = (unsigned)row < (unsigned)nrows ? row / k : 0;
+        PairBuf<NBL> A, B;
+        load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);   // before the x sync
+        __syncthreads();                            // the previous row's records are read
+        split_x_to_lds(x + (size_t)tok * d, nblk, (int)threadIdx.x, 256, xsr);
+        __syncthreads();
+        XSplit xa[NBL];
+        load_xsplit<NBL>(xsr, lane, nblk, xa);
+        HT *hrow = h + (size_t)(hstride > 0 ? a * hstride + r : row0 + r) * f;
+        // sched_barrier keeps each stage in place: a later pair's loads may
+        // not be hoisted above an earlier pair's math (that would only grow
+        // the register footprint, not the bytes in flight)
+#pragma unroll 1
+        for (int q = 0; q < kPerWave; q += 2) {
+            load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
+            __builtin_amdgcn_sched_barrier(0);
+            const float va = pair_h_mfma<NBL>(A, xa, lane, nblk);
+            if (lane == 0) put_h(hrow + n_base + 4 * q, va);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q + 2 < kPerWave)
+                load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
+            __builtin_amdgcn_sched_barrier(0);
+            const float vb = pair_h_mfma<NBL>(B, xa, lane, nblk);
+            if (lane == 0) put_h(hrow + n_base + 4 * (q + 1), vb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    }
+}
+
 // One token (T = 1): the top-k and the grouping happen inside the gate/up
 // pass.  Every block selects the token's experts itself from the logits row
 // (E floats, read by wave 0) while waves 1..3 split x; the k selected
@@ -463,27 +470,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_token_kernel(
         }
         if (first && lane == 0) plan[0] = k;
     } else {
-        // x split once: record b = hi codes [0, 24), lo codes [24, 48),
-        // scales at 48 (hi) and 49 (lo)
-        for (int b = (int)threadIdx.x - 64; b < nblk; b += 192) {
-            const uint4 *xb = reinterpret_cast<const uint4 *>(x) + 4 * b;
-            float v[32];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 w = xb[q];
-                const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    v[8 * q + 2 * t] = __uint_as_float(ww[t] << 16);
-                    v[8 * q + 2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
-                }
-            }
-            const SplitBlock sb = split_block32(v);
-            xsr[4 * b + 0] = uint4{sb.hi[0], sb.hi[1], sb.hi[2], sb.hi[3]};
-            xsr[4 * b + 1] = uint4{sb.hi[4], sb.hi[5], sb.lo[0], sb.lo[1]};
-            xsr[4 * b + 2] = uint4{sb.lo[2], sb.lo[3], sb.lo[4], sb.lo[5]};
-            xsr[4 * b + 3] = uint4{sb.scales, 0u, 0u, 0u};
-        }
+        split_x_to_lds(x, nblk, (int)threadIdx.x - 64, 192, xsr);   // waves 1..3
     }
     __syncthreads();
     if (first) {
@@ -501,20 +488,7 @@ __global__ __launch_bounds__(256) void gate_up_mfma_token_kernel(
     const int e = sel[a];
     if ((unsigned)e >= (unsigned)E) return;
     XSplit xa[NBL];
-#pragma unroll
-    for (int i = 0; i < NBL; ++i) {
-        const int b = lane + 64 * i;
-        if (b < nblk) {
-            const uint4 q0 = xsr[4 * b], q1 = xsr[4 * b + 1], q2 = xsr[4 * b + 2], q3 = xsr[4 * b + 3];
-            xa[i].hi = i32x8_t{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, 0, 0};
-            xa[i].lo = i32x8_t{(int)q1.z, (int)q1.w, (int)q2.x, (int)q2.y, (int)q2.z, (int)q2.w, 0, 0};
-            xa[i].sc = q3.x;
-        } else {
-            xa[i].hi = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-            xa[i].lo = xa[i].hi;
-            xa[i].sc = 0x7F7Fu;
-        }
-    }
+    load_xsplit<NBL>(xsr, lane, nblk, xa);
     const uint32_t code_row = (uint32_t)d >> 1;
     const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
     const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
@@ -577,31 +551,13 @@ __device__ __forceinline__ void load_h_slice(rsrc_t hbuf, uint32_t hrow_off, int
     }
 }
 
-// One MX block's 32 codes (16 bytes) dotted with the lane's h values of it.
-__device__ __forceinline__ float dot_block(uint4 c, const float4 (&hv)[8]) {
-    float s = 0.f;
-    s = dot8_fp4_f32(c.x, hv[0], hv[1], s);
-    s = dot8_fp4_f32(c.y, hv[2], hv[3], s);
-    s = dot8_fp4_f32(c.z, hv[4], hv[5], s);
-    s = dot8_fp4_f32(c.w, hv[6], hv[7], s);
-    return s;
-}
-__device__ __forceinline__ float dot_block(uint4 c, const uint4 (&hv)[4]) {
-    float s = 0.f;
-    s = dot8_fp4_bf16(c.x, hv[0], s);
-    s = dot8_fp4_bf16(c.y, hv[1], s);
-    s = dot8_fp4_bf16(c.z, hv[2], s);
-    s = dot8_fp4_bf16(c.w, hv[3], s);
-    return s;
-}
-
 // The lane's h slice of NBLD blocks: eight float4 per block for fp32 h,
 // four uint4 (bf16 pairs) for bf16 h.
 template <typename HT> struct HPart { typedef float4 type[8]; };
 template <> struct HPart<uint16_t> { typedef uint4 type[4]; };
 
 // Down rows in batches of kDnBatch: load_batch issues every code and scale
-// load of a batch, dot_batch does its math (out[rr] = h . Wd[m + rr], every
+// load of a batch, dot_batch_mfma does its math (out[rr] = h . Wd[m + rr], every
 // lane gets the sums).  Callers issue the next batch's loads before the
 // current batch's math.
 __device__ __forceinline__ void store_bf16x4(uint16_t *dst, const float (&v)[kDnBatch]) {
@@ -629,22 +585,6 @@ __device__ __forceinline__ void load_batch(rsrc_t codes, rsrc_t scales, int m, i
             rb.c[rr][i] = buf_load16(codes, 16u * b, row * code_row);
             rb.s[rr][i] = buf_load8(scales, b, row * (uint32_t)nblk);
         }
-}
-
-template <int NBLD, int B = kDnBatch, typename HV>
-__device__ __forceinline__ void dot_batch(const RowBuf<NBLD, B> &rb, const HV (&hv)[NBLD],
-                                          int lane, int nblk, float (&out)[B]) {
-#pragma unroll
-    for (int rr = 0; rr < B; ++rr) {
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < NBLD; ++i) {
-            const float s = dot_block(rb.c[rr][i], hv[i]);
-            acc += lane + 64 * i < nblk ? apply_e8m0(s, rb.s[rr][i]) : 0.f;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        out[rr] = wave_sum_f32(acc);
-    }
 }
 
 // The lane's h slice as the matrix cores' A operand: each MX block of it
@@ -803,8 +743,12 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
     const rsrc_t hbuf = make_rsrc(h + (size_t)(hstride > 0 ? a * hstride : row0) * f,
                                   (uint32_t)ne * f * 4u);
     for (int r = 0; r < ne; ++r) {
-        float4 hv[NBLD][8];
-        load_h_slice<NBLD>(hbuf, (uint32_t)r * f * 4u, lane, nblk, hv);
+        XSplit ha[NBLD];
+        {
+            float4 hv[NBLD][8];
+            load_h_slice<NBLD>(hbuf, (uint32_t)r * f * 4u, lane, nblk, hv);
+            split_h_slice<NBLD>(hv, lane, nblk, ha);
+        }
         uint16_t *orow = rows_out + (size_t)(row0 + r) * d + m;
         RowBuf<NBLD> A, B;
         load_batch<NBLD>(codes, scales, m, lane, nblk, code_row, A);
@@ -813,13 +757,13 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
             load_batch<NBLD>(codes, scales, m + b0 + kDnBatch, lane, nblk, code_row, B);
             __builtin_amdgcn_sched_barrier(0);
             float out[kDnBatch];
-            dot_batch<NBLD>(A, hv, lane, nblk, out);
+            dot_batch_mfma<NBLD, kDnBatch>(A, ha, lane, nblk, out);
             if (lane == 0) store_bf16x4(orow + b0, out);
             __builtin_amdgcn_sched_barrier(0);
             if (b0 + 2 * kDnBatch < 16)
                 load_batch<NBLD>(codes, scales, m + b0 + 2 * kDnBatch, lane, nblk, code_row, A);
             __builtin_amdgcn_sched_barrier(0);
-            dot_batch<NBLD>(B, hv, lane, nblk, out);
+            dot_batch_mfma<NBLD, kDnBatch>(B, ha, lane, nblk, out);
             if (lane == 0) store_bf16x4(orow + b0 + kDnBatch, out);
             __builtin_amdgcn_sched_barrier(0);
         }
