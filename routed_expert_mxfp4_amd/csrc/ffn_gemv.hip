@@ -240,6 +240,7 @@ __global__ __launch_bounds__(64) void down_combine_kernel(
 // a row issued before any of it is used, DPP lane reductions.
 // ---------------------------------------------------------------------------
 constexpr int kRxPairs = 32;         // gate/up pairs per block (8 per wave)
+constexpr int kRxRows = 4;           // token rows per weight pass (x split: 4 x d x 2 B of LDS)
 // the one-token kernel: 48 pairs (512 blocks at f = 1536, k = 16: one round
 // of two per CU) when f allows, else 32
 
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
     int e, row0, ne;
     if (!expert_group(plan, offsets, a, E, nrows, e, row0, ne)) continue;
     if (hstride > 0 && ne > hstride) continue;
-    extern __shared__ uint4 xsr[];                // one token row split, d/32 records of 64 B
+    extern __shared__ uint4 xsr[];                // kRxRows token rows split, d/32 records of 64 B each
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int nblk = d >> 5;
@@ -397,33 +398,68 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
     const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
     constexpr int kPerWave = kRxPairs / 4;        // pairs n_base + wid + 4 q
     const int n_base = blockIdx.x * kRxPairs + wid;
-    for (int r = 0; r < ne; ++r) {
-        const int row = sorted_rows[row0 + r];
-        const int tok = (unsigned)row < (unsigned)nrows ? row / k : 0;
+    // the expert's rows in chunks of up to kRxRows: each chunk's x rows are
+    // split into LDS once and every weight pair, loaded once, is dotted with
+    // all of them (weights are not re-streamed per row within a chunk)
+    for (int r0 = 0; r0 < ne; r0 += kRxRows) {
+        const int nr = min(kRxRows, ne - r0);   // block-uniform
         PairBuf<NBL> A, B;
         load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);   // before the x sync
-        __syncthreads();                            // the previous row's records are read
-        split_x_to_lds(x + (size_t)tok * d, nblk, (int)threadIdx.x, 256, xsr);
+        __syncthreads();                            // the previous chunk's records are read
+        for (int r = 0; r < nr; ++r) {
+            const int row = sorted_rows[row0 + r0 + r];
+            const int tok = (unsigned)row < (unsigned)nrows ? row / k : 0;
+            split_x_to_lds(x + (size_t)tok * d, nblk, (int)threadIdx.x, 256, xsr + 4 * nblk * r);
+        }
         __syncthreads();
-        XSplit xa[NBL];
-        load_xsplit<NBL>(xsr, lane, nblk, xa);
-        HT *hrow = h + (size_t)(hstride > 0 ? a * hstride + r : row0 + r) * f;
-        // sched_barrier keeps each stage in place: a later pair's loads may
-        // not be hoisted above an earlier pair's math (that would only grow
-        // the register footprint, not the bytes in flight)
+        HT *hrow = h + (size_t)(hstride > 0 ? a * hstride + r0 : row0 + r0) * f;
+        if (nr == 1) {
+            // one row: its split x stays in registers for the whole pass
+            XSplit xa[NBL];
+            load_xsplit<NBL>(xsr, lane, nblk, xa);
+            // sched_barrier keeps each stage in place: a later pair's loads
+            // may not be hoisted above an earlier pair's math (that would
+            // only grow the register footprint, not the bytes in flight)
 #pragma unroll 1
-        for (int q = 0; q < kPerWave; q += 2) {
-            load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
-            __builtin_amdgcn_sched_barrier(0);
-            const float va = pair_h_mfma<NBL>(A, xa, lane, nblk);
-            if (lane == 0) put_h(hrow + n_base + 4 * q, va);
-            __builtin_amdgcn_sched_barrier(0);
-            if (q + 2 < kPerWave)
-                load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
-            __builtin_amdgcn_sched_barrier(0);
-            const float vb = pair_h_mfma<NBL>(B, xa, lane, nblk);
-            if (lane == 0) put_h(hrow + n_base + 4 * (q + 1), vb);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int q = 0; q < kPerWave; q += 2) {
+                load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
+                __builtin_amdgcn_sched_barrier(0);
+                const float va = pair_h_mfma<NBL>(A, xa, lane, nblk);
+                if (lane == 0) put_h(hrow + n_base + 4 * q, va);
+                __builtin_amdgcn_sched_barrier(0);
+                if (q + 2 < kPerWave)
+                    load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
+                __builtin_amdgcn_sched_barrier(0);
+                const float vb = pair_h_mfma<NBL>(B, xa, lane, nblk);
+                if (lane == 0) put_h(hrow + n_base + 4 * (q + 1), vb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // several rows: each row's split x is read from LDS per pair
+#pragma unroll 1
+            for (int q = 0; q < kPerWave; q += 2) {
+                load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+                for (int r = 0; r < nr; ++r) {
+                    XSplit xa[NBL];
+                    load_xsplit<NBL>(xsr + 4 * nblk * r, lane, nblk, xa);
+                    const float va = pair_h_mfma<NBL>(A, xa, lane, nblk);
+                    if (lane == 0) put_h(hrow + (size_t)r * f + n_base + 4 * q, va);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (q + 2 < kPerWave)
+                    load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+                for (int r = 0; r < nr; ++r) {
+                    XSplit xa[NBL];
+                    load_xsplit<NBL>(xsr + 4 * nblk * r, lane, nblk, xa);
+                    const float vb = pair_h_mfma<NBL>(B, xa, lane, nblk);
+                    if (lane == 0) put_h(hrow + (size_t)r * f + n_base + 4 * (q + 1), vb);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     }
@@ -781,11 +817,11 @@ hipError_t launch_regx(const uint16_t *x, ExpertArgs w, const int32_t *offsets,
     dim3 grid(f / kRxPairs, amax);
     if (hb)
         (void)timed_launch("gemv_gate_up", gate_up_regx_kernel<NBL, uint16_t>, dim3(grid),
-                           dim3(256), (size_t)d * 2 + 16, s, x, w, offsets, sorted_rows, plan,
+                           dim3(256), (size_t)kRxRows * d * 2, s, x, w, offsets, sorted_rows, plan,
                            reinterpret_cast<uint16_t *>(h), T, d, E, k, f, hstride);
     else
         (void)timed_launch("gemv_gate_up", gate_up_regx_kernel<NBL, float>, dim3(grid), dim3(256),
-                           (size_t)d * 2 + 16, s, x, w, offsets, sorted_rows, plan, h, T, d, E, k,
+                           (size_t)kRxRows * d * 2, s, x, w, offsets, sorted_rows, plan, h, T, d, E, k,
                            f, hstride);
     return hipGetLastError();
 }
