@@ -389,6 +389,9 @@ def main():
               "without --tail", file=sys.stderr)
         sys.exit(2)
     dominant = "fp8_gate_up" if fp8 else ("gate_up_mfma" if mfma else "gemv_gate_up")
+    # the counter summary that belongs to this exact run variant
+    traffic_key = (args.workload + ("-packed" if args.packed else "") +
+                   ("-mx" if args.act == "mx" else "") + ("-block" if args.tail else ""))
     L = moe.lib()
 
     # ---- inputs, resident in HBM before timing --------------------------------
@@ -524,7 +527,7 @@ def main():
         tflops = flops_per_launch / avg_launch_s / 1e12
         src = os.path.join(ROOT, "routed_expert_mxfp4_amd", "csrc", "ffn_fp8_mfma.hip")
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        common = {"kernel": dominant, "traffic": traffic_from_profiles(dominant, args.workload, sha),
+        common = {"kernel": dominant, "traffic": traffic_from_profiles(dominant, traffic_key, sha),
                   "algorithmic_flops_per_launch": flops_per_launch,
                   "algorithmic_bytes_per_launch": bytes_per_launch,
                   "layer_flop_per_byte": layer_flops / layer_bytes,
@@ -547,8 +550,7 @@ def main():
         roofline = {"bound": "mfma", "kernel": dominant, "achieved": achieved,
                     "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": achieved / MXFP4_PEAK_TFLOPS,
-                    "traffic": traffic_from_profiles(
-                        dominant, args.workload + ("-packed" if args.packed else ""), sha),
+                    "traffic": traffic_from_profiles(dominant, traffic_key, sha),
                     "algorithmic_flops_per_launch": flops_per_launch,
                     "mfma_passes_per_product": 1 if act else 2,
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
@@ -563,8 +565,7 @@ def main():
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                    "traffic": traffic_from_profiles(
-                        dominant, args.workload + ("-packed" if args.packed else ""), sha),
+                    "traffic": traffic_from_profiles(dominant, traffic_key, sha),
                     "algorithmic_bytes_per_launch": bytes_per_launch,
                     "experts_on_mfma_per_launch": mean_on_mfma,
                     "experts_on_gemv_per_launch": mean_touched - mean_on_mfma,
@@ -581,7 +582,7 @@ def main():
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                    "traffic": traffic_from_profiles(dominant, args.workload, sha),
+                    "traffic": traffic_from_profiles(dominant, traffic_key, sha),
                     "algorithmic_bytes_per_launch": bytes_per_launch,
                     "avg_launch_us": avg_launch_s * 1e6, "launches_timed": dom_n}
 
