@@ -554,7 +554,8 @@ __global__ __launch_bounds__(256) void gate_up_mfma_token_kernel(
 // of bf16 pairs) is loaded once into registers and reused for every output
 // row; rows go in batches whose code loads are all in flight together, and
 // each row's partial sums are reduced across the wave.  Lanes past the end
-// of f hold zero h.
+// of f load a duplicate of the last block; split_h_slice turns it into zero
+// codes, so the loads need no select and can stay in flight.
 constexpr int kDnBatch = 4;
 
 template <int NBLD>
@@ -563,12 +564,9 @@ __device__ __forceinline__ void load_h_slice(rsrc_t hbuf, uint32_t hrow_off, int
 #pragma unroll
     for (int i = 0; i < NBLD; ++i) {
         const uint32_t b = (uint32_t)min(lane + 64 * i, nblk - 1);
-        const bool ok = lane + 64 * i < nblk;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float4 v = __builtin_bit_cast(float4, buf_load16(hbuf, 128u * b + 16u * q, hrow_off));
-            hv[i][q] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        for (int q = 0; q < 8; ++q)
+            hv[i][q] = __builtin_bit_cast(float4, buf_load16(hbuf, 128u * b + 16u * q, hrow_off));
     }
 }
 
@@ -578,12 +576,8 @@ __device__ __forceinline__ void load_h_slice(rsrc_t hbuf, uint32_t hrow_off, int
 #pragma unroll
     for (int i = 0; i < NBLD; ++i) {
         const uint32_t b = (uint32_t)min(lane + 64 * i, nblk - 1);
-        const bool ok = lane + 64 * i < nblk;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint4 v = buf_load16(hbuf, 64u * b + 16u * q, hrow_off);
-            hv[i][q] = ok ? v : uint4{0u, 0u, 0u, 0u};
-        }
+        for (int q = 0; q < 4; ++q) hv[i][q] = buf_load16(hbuf, 64u * b + 16u * q, hrow_off);
     }
 }
 
@@ -719,17 +713,17 @@ __global__ __launch_bounds__(64 * NW) void down_combine_split_kernel(
         if (ok) {
             const rsrc_t codes = make_rsrc(W.dn_codes + (size_t)e * d * code_row, (uint32_t)d * code_row);
             const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
-            XSplit ha[NBLD];
-            {
-                typename HPart<HT>::type hv[NBLD];
-                load_h_slice<NBLD>(hbuf, (uint32_t)p * f * (uint32_t)sizeof(HT), lane, nblk, hv);
-                split_h_slice<NBLD>(hv, lane, nblk, ha);
-            }
+            // h first, then the ring's first weight loads, then the split:
+            // the split waits for h alone while the weights are in flight
+            typename HPart<HT>::type hv[NBLD];
+            load_h_slice<NBLD>(hbuf, (uint32_t)p * f * (uint32_t)sizeof(HT), lane, nblk, hv);
             constexpr int NB = ROWS / B;
             RowBuf<NBLD, B> ring[R];
 #pragma unroll
             for (int i = 0; i < R - 1 && i < NB; ++i)
                 load_batch<NBLD, B>(codes, scales, m0 + i * B, lane, nblk, code_row, ring[i]);
+            XSplit ha[NBLD];
+            split_h_slice<NBLD>(hv, lane, nblk, ha);
 #pragma unroll
             for (int bi = 0; bi < NB; ++bi) {
                 if (bi + R - 1 < NB)
@@ -779,6 +773,8 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
     const rsrc_t hbuf = make_rsrc(h + (size_t)(hstride > 0 ? a * hstride : row0) * f,
                                   (uint32_t)ne * f * 4u);
     for (int r = 0; r < ne; ++r) {
+        // (issuing batch A's loads before the split costs this kernel a
+        // quarter of its waves: more registers live across the split)
         XSplit ha[NBLD];
         {
             float4 hv[NBLD][8];
