@@ -446,31 +446,40 @@ __device__ __forceinline__ void plan8(Plan8 &P, const uint8_t *aq, uint32_t a_by
 }
 
 // Step kk's activation loads into A stage kk & 1, and at kk % 4 == 0 the
-// scale group kk / 4.  Wave-uniform branches only.
+// scale group kk / 4.  P's offsets are those of step kk (scale group kk / 4)
+// and move on to the next step (group) in place, so the address of a load
+// takes no register beyond the one it lives in.  Wave-uniform branches only.
 template <int MT>
-__device__ __forceinline__ void issue_a8(const Plan8 &P, uint32_t lds, int kk, int wid) {
+__device__ __forceinline__ void issue_a8(Plan8 &P, uint32_t lds, int kk, int wid) {
     const uint32_t st = lds + (uint32_t)((kk & 1) * kAStageBytes);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if (j < P.n_a)
-            lds_load16(P.ra, P.a_src[j] + (uint32_t)kk * kStepBytes,
+        if (j < P.n_a) {
+            lds_load16(P.ra, P.a_src[j],
                        (uint32_t)__builtin_amdgcn_readfirstlane(
                            (int)(st + 1024u * (uint32_t)(wid + kWaves * j))));
+            P.a_src[j] += kStepBytes;
+        }
     }
-    if ((kk & 3) == 0)
-        lds_load16(P.rs, P.s_src + (uint32_t)(kk >> 2) * P.sgrp,
+    if ((kk & 3) == 0) {
+        lds_load16(P.rs, P.s_src,
                    (uint32_t)__builtin_amdgcn_readfirstlane(
                        (int)(lds + kSBase + 1024u * (uint32_t)wid)));
+        P.s_src += P.sgrp;
+    }
 }
 
-// Step kk's weight-code loads (kBLoads per wave) into B stage sb = kk % 3.
-__device__ __forceinline__ void issue_b8(const Plan8 &P, uint32_t lds, int kk, int sb, int wid) {
+// The next step's weight-code loads (kBLoads per wave) into B stage sb; P's
+// code offsets move on one step in place.
+__device__ __forceinline__ void issue_b8(Plan8 &P, uint32_t lds, int sb, int wid) {
     const uint32_t st = lds + kBBase + (uint32_t)(sb * kBStageBytes);
 #pragma unroll
-    for (int j = 0; j < kBLoads; ++j)
-        lds_load16(P.rb, P.b_src[j] + (uint32_t)kk * P.cstep,
+    for (int j = 0; j < kBLoads; ++j) {
+        lds_load16(P.rb, P.b_src[j],
                    (uint32_t)__builtin_amdgcn_readfirstlane(
                        (int)(st + 1024u * (uint32_t)(wid + kWaves * j))));
+        P.b_src[j] += P.cstep;
+    }
 }
 
 // 16-row tiles (decode-sized experts): an A stage is 4 KB, so four A
@@ -584,10 +593,15 @@ __device__ __forceinline__ void read_group_scales(uint32_t (&sc)[N], uint32_t ad
 }
 
 // The A fragments of m-tiles I..kMtw-1, two in flight: m-tile I's is waited
-// for, its MFMAs issued against every B fragment, m-tile I + 2's queued.
-template <int I, int MTW, int NTW, bool kSingle>
+// for, its MFMAs issued against every B fragment, m-tile I + 2's queued, then
+// hook(I) (the ring's next global loads, issued between MFMA groups).
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+template <int I, int MTW, int NTW, bool kSingle, typename H = NoHook>
 __device__ __forceinline__ void chain8(f32x4_t (&acc)[MTW][NTW], AFrag (&fa)[2],
-                                       const BFrags<NTW> &fb, uint32_t a, uint32_t s) {
+                                       const BFrags<NTW> &fb, uint32_t a, uint32_t s,
+                                       const H &hook = H()) {
     if constexpr (I < MTW) {
         afrag_ready<(I + 1 < MTW) ? 5 : 0>(fa[I & 1]);
 #pragma unroll
@@ -601,7 +615,8 @@ __device__ __forceinline__ void chain8(f32x4_t (&acc)[MTW][NTW], AFrag (&fa)[2],
                     fa[I & 1].lo, b, acc[I][nt], 2, 4, 1, (int)fa[I & 1].sc, 0, (int)fb.sc[nt]);
         }
         if constexpr (I + 2 < MTW) read_afrag<I + 2>(fa[I & 1], a, s);
-        chain8<I + 1, MTW, NTW, kSingle>(acc, fa, fb, a, s);
+        hook(I);
+        chain8<I + 1, MTW, NTW, kSingle>(acc, fa, fb, a, s, hook);
     }
 }
 
@@ -639,7 +654,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
     const uint32_t psel01 = (uint32_t)g | ((4u + (uint32_t)g) << 8);
     uint32_t spk[kNtw];
     // one K step's products from A stage st and B stage sbq
-    auto multiply = [&](uint32_t st, uint32_t sbq, int kk) {
+    auto multiply = [&](uint32_t st, uint32_t sbq, int kk, const auto &hook) {
         BFrags<kNtw> fb;
 #pragma unroll
         for (int nt = 0; nt < kNtw; ++nt) {
@@ -652,7 +667,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
         if constexpr (kMtw > 1) read_afrag<1>(fa[1], a, s);
         // the B fragments and m-tile 0's A fragment; m-tile 1's may still fly
         bfrags_ready<kNtw, (kMtw > 1 ? 5 : 0)>(fb);
-        chain8<0, kMtw, kNtw, kSingle>(acc, fa, fb, a, s);
+        chain8<0, kMtw, kNtw, kSingle>(acc, fa, fb, a, s, hook);
     };
     if constexpr (MT == 1) {
         if (!packed && (P.nsteps & 1) == 0) {
@@ -716,14 +731,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
                 if (kk + 3 < P.nsteps) issue_step_deep(P, lds_addr, kk + 3, wid);
                 __builtin_amdgcn_sched_barrier(0);
                 multiply(lds_addr + (uint32_t)((kk & 3) * kDeepAStage),
-                         lds_addr + kDeepBBase + (uint32_t)((kk & 3) * kBStageBytes), kk);
+                         lds_addr + kDeepBBase + (uint32_t)((kk & 3) * kBStageBytes), kk, NoHook());
             }
         }
     } else {
         // prologue: step 0's activations and scale group, steps 0 and 1's codes
         issue_a8<MT>(P, lds_addr, 0, wid);
-        issue_b8(P, lds_addr, 0, 0, wid);
-        if (P.nsteps > 1) issue_b8(P, lds_addr, 1, 1, wid);
+        issue_b8(P, lds_addr, 0, wid);
+        if (P.nsteps > 1) issue_b8(P, lds_addr, 1, wid);
         const uint32_t sgrp_lane = lds_addr + kSBase + 256u * (uint32_t)nbase + 16u * (uint32_t)r16;
         int sb = 0;                                         // kk % 3
         for (int kk = 0; kk < P.nsteps; ++kk) {
@@ -737,11 +752,21 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
             __builtin_amdgcn_sched_barrier(0);
             if ((kk & 3) == 0) read_group_scales<kNtw>(spk, sgrp_lane, psel01);
             __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < P.nsteps) issue_a8<MT>(P, lds_addr, kk + 1, wid);
-            if (kk + 2 < P.nsteps) issue_b8(P, lds_addr, kk + 2, sb == 0 ? 2 : sb - 1, wid);
-            __builtin_amdgcn_sched_barrier(0);
+            // the next loads go out between the MFMA groups (step kk + 1's
+            // activations after m-tile 0, step kk + 2's codes after the last
+            // m-tile), not all at once after the barrier: the eight waves'
+            // loads then queue at the texture unit while the matrix cores
+            // work
+            static_assert(Tile<MT>::kMtw >= 2, "both hooks run");
+            const int sbn = sb == 0 ? 2 : sb - 1;
+            auto hook = [&](int i) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (i == 0 && kk + 1 < P.nsteps) issue_a8<MT>(P, lds_addr, kk + 1, wid);
+                if (i == Tile<MT>::kMtw - 1 && kk + 2 < P.nsteps) issue_b8(P, lds_addr, sbn, wid);
+                __builtin_amdgcn_sched_barrier(0);
+            };
             multiply(lds_addr + (uint32_t)((kk & 1) * kAStageBytes),
-                     lds_addr + kBBase + (uint32_t)(sb * kBStageBytes), kk);
+                     lds_addr + kBBase + (uint32_t)(sb * kBStageBytes), kk, hook);
             sb = sb == 2 ? 0 : sb + 1;
         }
     }
