@@ -240,11 +240,17 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const flo
                                 float *logits, int T, int d, int E, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     const int P = d / 64;
-    constexpr int kRpb = kRouterRowsPerBlock;
-    const size_t lds = (size_t)kRpb * 64 * ((P / 8) + 1) * 16 + 16;   // + spare slot
-    if (T == 1 && P % 8 == 0 && d <= 8192 && lds <= 65536) {
-        (void)timed_launch("router_logits", router_small_kernel<kRpb>, dim3((E + kRpb - 1) / kRpb), dim3(64 * kRpb), lds, s, x, wr, bias, logits,
-                                                                               T, d, E);
+    if (T == 1 && P % 8 == 0 && d <= 8192) {
+        // 4 router rows per block, or 1 when that leaves CUs idle (E < 1024)
+        const int rpb = E >= 4 * 192 ? kRouterRowsPerBlock : 1;
+        const size_t lds = (size_t)rpb * 64 * ((P / 8) + 1) * 16 + 16;   // + spare slot
+        if (rpb == 1)
+            (void)timed_launch("router_logits", router_small_kernel<1>, dim3(E), dim3(64), lds, s,
+                               x, wr, bias, logits, T, d, E);
+        else
+            (void)timed_launch("router_logits", router_small_kernel<kRouterRowsPerBlock>,
+                               dim3((E + kRouterRowsPerBlock - 1) / kRouterRowsPerBlock),
+                               dim3(64 * kRouterRowsPerBlock), lds, s, x, wr, bias, logits, T, d, E);
         return hipGetLastError();
     }
     // larger token tiles re-read the router rows fewer times (8 x 8 at
