@@ -23,6 +23,7 @@
 // tile and K block (l / 16) of the step; the output tile holds
 // C[4 * (l / 16) + i][l % 16] in lane l, register i.
 #include <algorithm>
+#include <utility>
 
 #include "moe_internal.hpp"
 #include "mx_split.hpp"
@@ -316,12 +317,19 @@ __device__ __forceinline__ void afrag_ready(AFrag &f) {
     asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(f.hi), "+v"(f.lo), "+v"(f.sc) : "n"(N));
 }
 
-// B fragment of operand tile t in a stage: 16 bytes per lane, then the
-// lane's E8M0 byte of the step from the scale group.
-__device__ __forceinline__ u32x4_t ds_read128_at(uint32_t a) {
-    u32x4_t v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
-    return v;
+// N 16-byte reads at base + STRIDE i (i < N), the strides in the
+// instructions' offset field: one address register for all of them (the B
+// fragments of a wave's operand tiles, 16 bytes per lane each; the rows of
+// a scale group).
+template <int STRIDE, int... I>
+__device__ __forceinline__ void ds_read128_strided(u32x4_t *r, uint32_t base,
+                                                   std::integer_sequence<int, I...>) {
+    ((r[I] = ds_read128<STRIDE * I>(base)), ...);
+}
+template <int STRIDE, int N>
+__device__ __forceinline__ void ds_read128_rows(u32x4_t (&r)[N], uint32_t base) {
+    static_assert(STRIDE * (N - 1) < 65536, "offsets fit the instruction");
+    ds_read128_strided<STRIDE>(r, base, std::make_integer_sequence<int, N>());
 }
 
 template <int N>
@@ -579,15 +587,19 @@ __device__ __forceinline__ void deep_wait(int n) {
 // The lane's E8M0 codes of one scale group for its operand tiles: byte s of
 // sc[nt] is the code of K block 4 s + g of row r16 (step s of the group),
 // picked from the row's 16 bytes.
+// All N reads are issued before one wait (each row's bytes are then tied to
+// that wait, as in bfrags_ready).
 template <int N>
 __device__ __forceinline__ void read_group_scales(uint32_t (&sc)[N], uint32_t addr,
                                                   uint32_t psel01) {
+    u32x4_t r[N];
+    ds_read128_rows<256>(r, addr);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int nt = 0; nt < N; ++nt) {
-        u32x4_t r = ds_read128_at(addr + 256u * (uint32_t)nt);
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r));
-        const uint32_t t01 = __builtin_amdgcn_perm(r.y, r.x, psel01);
-        const uint32_t t23 = __builtin_amdgcn_perm(r.w, r.z, psel01);
+        asm volatile("" : "+v"(r[nt]));
+        const uint32_t t01 = __builtin_amdgcn_perm(r[nt].y, r[nt].x, psel01);
+        const uint32_t t23 = __builtin_amdgcn_perm(r[nt].w, r[nt].z, psel01);
         sc[nt] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
     }
 }
@@ -657,10 +669,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
     auto multiply = [&](uint32_t st, uint32_t sbq, int kk, const auto &hook) {
         BFrags<kNtw> fb;
 #pragma unroll
-        for (int nt = 0; nt < kNtw; ++nt) {
-            fb.q[nt] = ds_read128_at(sbq + 1024u * (uint32_t)(nbase + nt) + 16u * (uint32_t)lane);
-            fb.sc[nt] = spk[nt] >> (8 * (kk & 3));
-        }
+        for (int nt = 0; nt < kNtw; ++nt) fb.sc[nt] = spk[nt] >> (8 * (kk & 3));
+        ds_read128_rows<1024>(fb.q, sbq + 1024u * (uint32_t)nbase + 16u * (uint32_t)lane);
         AFrag fa[2];
         const uint32_t a = st + a_lane, s = st + s_lane;
         read_afrag<0>(fa[0], a, s);
@@ -702,10 +712,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t *__restrict__ aq, uint32
                     const int kk = 2 * S + h;
                     BFrags<kNtw> fb;
 #pragma unroll
-                    for (int nt = 0; nt < kNtw; ++nt) {
-                        fb.q[nt] = ds_read128_at(b_st + 2048u * (uint32_t)(nbase + nt) + frag_lane + 512u * (uint32_t)h);
-                        fb.sc[nt] = spk[nt] >> (8 * (kk & 3));
-                    }
+                    for (int nt = 0; nt < kNtw; ++nt) fb.sc[nt] = spk[nt] >> (8 * (kk & 3));
+                    ds_read128_rows<2048>(fb.q, b_st + 2048u * (uint32_t)nbase + frag_lane + 512u * (uint32_t)h);
                     AFrag fa[2];
                     const uint32_t st = lds_addr + (uint32_t)(kk & 3) * kSupAStage;
                     const uint32_t a = st + a_lane, sa = st + s_lane;
