@@ -330,24 +330,39 @@ __device__ __forceinline__ float pair_h_mfma(const PairBuf<NBL> &pb, const XSpli
     return silu_mul(mfma_trace16(cg, lane), mfma_trace16(cu, lane));
 }
 
-// x row (bf16 [d]) split into records of 64 bytes per MX block in LDS: hi
-// codes [0, 24), lo codes [24, 48), scales at 48 (hi) and 49 (lo); threads
-// t0, t0 + stride, .. take a block each.
-__device__ __forceinline__ void split_x_to_lds(const uint16_t *__restrict__ xrow, int nblk, int t0,
+// A row (bf16 x or fp32 h) split into records of 64 bytes per MX block in
+// LDS: hi codes [0, 24), lo codes [24, 48), scales at 48 (hi) and 49 (lo);
+// threads t0, t0 + stride, .. take a block each.
+__device__ __forceinline__ void block_values(const uint16_t *__restrict__ row, int b, float (&v)[32]) {
+    const uint4 *xb = reinterpret_cast<const uint4 *>(row) + 4 * b;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 w = xb[q];
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            v[8 * q + 2 * t] = __uint_as_float(ww[t] << 16);
+            v[8 * q + 2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
+        }
+    }
+}
+__device__ __forceinline__ void block_values(const float *__restrict__ row, int b, float (&v)[32]) {
+    const float4 *hb = reinterpret_cast<const float4 *>(row) + 8 * b;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float4 w = hb[q];
+        v[4 * q] = w.x;
+        v[4 * q + 1] = w.y;
+        v[4 * q + 2] = w.z;
+        v[4 * q + 3] = w.w;
+    }
+}
+template <typename RT>
+__device__ __forceinline__ void split_x_to_lds(const RT *__restrict__ xrow, int nblk, int t0,
                                                int stride, uint4 *xsr) {
     for (int b = t0; b < nblk; b += stride) {
-        const uint4 *xb = reinterpret_cast<const uint4 *>(xrow) + 4 * b;
         float v[32];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint4 w = xb[q];
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                v[8 * q + 2 * t] = __uint_as_float(ww[t] << 16);
-                v[8 * q + 2 * t + 1] = __uint_as_float(ww[t] & 0xFFFF0000u);
-            }
-        }
+        block_values(xrow, b, v);
         const SplitBlock sb = split_block32(v);
         xsr[4 * b + 0] = uint4{sb.hi[0], sb.hi[1], sb.hi[2], sb.hi[3]};
         xsr[4 * b + 1] = uint4{sb.hi[4], sb.hi[5], sb.lo[0], sb.lo[1]};
@@ -751,13 +766,19 @@ __global__ __launch_bounds__(64 * NW) void down_combine_split_kernel(
 }
 
 // Expert-major down for decode-sized groups: block (64 output rows, expert
-// a), 16 rows per wave; the expert's token rows are walked one by one
-// (weights re-read from L2 after the first).
-template <int NBLD>
+// a), 16 rows per wave.  An expert's token rows go one at a time, the
+// lane's split h slice in registers -- or, with kMulti and several rows,
+// kDnTokRows at a time through LDS, each weight batch loaded once for all
+// of them.  kMulti is off where every expert has one row (the small experts
+// of a scaled-MFMA call at a crossover of one row): that path keeps the
+// lighter code.
+constexpr int kDnTokRows = 4;
+template <int NBLD, bool kMulti>
 __global__ __launch_bounds__(256) void down_rows_kernel(
     const float *__restrict__ h, ExpertArgs W, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ plan, uint16_t *__restrict__ rows_out, int T, int d, int E,
     int k, int f, int hstride) {
+    extern __shared__ uint4 hsr[];                // kDnTokRows h rows split, f/32 records of 64 B each
     const int nrows = T * k;
     for (int a = blockIdx.y; a < plan[0]; a += gridDim.y) {
     int e, row0, ne;
@@ -772,9 +793,10 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
     const rsrc_t scales = make_rsrc(W.dn_scales + (size_t)e * d * nblk, (uint32_t)d * nblk);
     const rsrc_t hbuf = make_rsrc(h + (size_t)(hstride > 0 ? a * hstride : row0) * f,
                                   (uint32_t)ne * f * 4u);
-    for (int r = 0; r < ne; ++r) {
-        // (issuing batch A's loads before the split costs this kernel a
-        // quarter of its waves: more registers live across the split)
+    auto one_row = [&](int r) {
+        // the lane's split h slice stays in registers (issuing batch A's
+        // loads before the split costs this kernel a quarter of its waves:
+        // more registers live across the split)
         XSplit ha[NBLD];
         {
             float4 hv[NBLD][8];
@@ -797,6 +819,54 @@ __global__ __launch_bounds__(256) void down_rows_kernel(
             __builtin_amdgcn_sched_barrier(0);
             dot_batch_mfma<NBLD, kDnBatch>(B, ha, lane, nblk, out);
             if (lane == 0) store_bf16x4(orow + b0 + kDnBatch, out);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if constexpr (!kMulti) {
+        for (int r = 0; r < ne; ++r) one_row(r);
+        continue;
+    }
+    if (ne == 1) {
+        one_row(0);
+        continue;
+    }
+    // several rows: up to kDnTokRows of them split into LDS by the whole block,
+    // then every weight batch, loaded once, is dotted with each of them
+    const float *hrows = h + (size_t)(hstride > 0 ? a * hstride : row0) * f;
+    for (int r0 = 0; r0 < ne; r0 += kDnTokRows) {
+        const int nr = min(kDnTokRows, ne - r0);       // block-uniform
+        __syncthreads();                            // the previous chunk's records are read
+        for (int r = 0; r < nr; ++r)
+            split_x_to_lds(hrows + (size_t)(r0 + r) * f, nblk, (int)threadIdx.x, 256,
+                           hsr + 4 * nblk * r);
+        __syncthreads();
+        RowBuf<NBLD> A, B;
+        load_batch<NBLD>(codes, scales, m, lane, nblk, code_row, A);
+        uint16_t *orow = rows_out + (size_t)(row0 + r0) * d + m;
+#pragma unroll 1
+        for (int b0 = 0; b0 < 16; b0 += 2 * kDnBatch) {
+            load_batch<NBLD>(codes, scales, m + b0 + kDnBatch, lane, nblk, code_row, B);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+            for (int r = 0; r < nr; ++r) {
+                XSplit ha[NBLD];
+                load_xsplit<NBLD>(hsr + 4 * nblk * r, lane, nblk, ha);
+                float out[kDnBatch];
+                dot_batch_mfma<NBLD, kDnBatch>(A, ha, lane, nblk, out);
+                if (lane == 0) store_bf16x4(orow + (size_t)r * d + b0, out);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (b0 + 2 * kDnBatch < 16)
+                load_batch<NBLD>(codes, scales, m + b0 + 2 * kDnBatch, lane, nblk, code_row, A);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+            for (int r = 0; r < nr; ++r) {
+                XSplit ha[NBLD];
+                load_xsplit<NBLD>(hsr + 4 * nblk * r, lane, nblk, ha);
+                float out[kDnBatch];
+                dot_batch_mfma<NBLD, kDnBatch>(B, ha, lane, nblk, out);
+                if (lane == 0) store_bf16x4(orow + (size_t)r * d + b0 + kDnBatch, out);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -850,7 +920,14 @@ hipError_t launch_down_rows(const float *h, ExpertArgs w, const int32_t *offsets
                             const int32_t *plan, uint16_t *rows_out, int T, int d, int E,
                             int k, int f, int amax, hipStream_t s, int hstride = 0) {
     dim3 grid(d / 64, amax);
-    (void)timed_launch("gemv_down", down_rows_kernel<NBLD>, dim3(grid), dim3(256), 0, s, h, w, offsets, plan, rows_out, T, d, E, k, f, hstride);
+    // the several-row path only where an expert can have several rows
+    if (hstride == 1)
+        (void)timed_launch("gemv_down", down_rows_kernel<NBLD, false>, dim3(grid), dim3(256), 0,
+                           s, h, w, offsets, plan, rows_out, T, d, E, k, f, hstride);
+    else
+        (void)timed_launch("gemv_down", down_rows_kernel<NBLD, true>, dim3(grid), dim3(256),
+                           (size_t)kDnTokRows * f * 2, s, h, w, offsets, plan, rows_out, T, d, E,
+                           k, f, hstride);
     return hipGetLastError();
 }
 

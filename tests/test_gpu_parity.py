@@ -81,6 +81,8 @@ SMALL_CASES = [
     (17, 512, 70, 1, 96, 14),       # k = 1, ragged T
     (300, 128, 24, 3, 64, 15),      # T > 256: multi-block grouping
     (70, 64, 130, 4, 32, 16),       # E > 128
+    (3, 8192, 6, 4, 128, 18),       # d = 8192: four split x rows fill the GEMV's 64 KB of LDS
+    (40, 512, 6, 3, 64, 19),        # ~20 rows per expert on the GEMVs: chunks of four rows + a tail
 ]
 
 
