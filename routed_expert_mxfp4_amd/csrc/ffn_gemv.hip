@@ -241,8 +241,7 @@ __global__ __launch_bounds__(64) void down_combine_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kRxPairs = 32;         // gate/up pairs per block (8 per wave)
 constexpr int kRxRows = 4;           // token rows per weight pass (x split: 4 x d x 2 B of LDS)
-// the one-token kernel: 48 pairs (512 blocks at f = 1536, k = 16: one round
-// of two per CU) when f allows, else 32
+// the one-token kernel: 96, 48 or 32 pairs per block (launch_gate_up_token_t)
 
 // Gate/up for decode-sized groups, software-pipelined: lane l owns the MX
 // blocks b = l + 64 i (i < NBL) of d; the token row is split once into LDS
@@ -489,8 +488,8 @@ __global__ __launch_bounds__(256) void gate_up_regx_kernel(
 // weights, counts, offsets, sorted_rows, row_pos, plan) for the later
 // kernels.  Each wave streams its output pairs as gate_up_regx_kernel does,
 // the next pair's loads issued before the current pair's products.
-template <int NBL, int PAIRS, typename HT>
-__global__ __launch_bounds__(256) void gate_up_mfma_token_kernel(
+template <int NBL, int PAIRS, typename HT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void gate_up_mfma_token_kernel(
     const float *__restrict__ logits, const uint16_t *__restrict__ x, ExpertArgs W,
     int32_t *__restrict__ ids, float *__restrict__ tw, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_rows,
@@ -521,11 +520,11 @@ __global__ __launch_bounds__(256) void gate_up_mfma_token_kernel(
         }
         if (first && lane == 0) plan[0] = k;
     } else {
-        split_x_to_lds(x, nblk, (int)threadIdx.x - 64, 192, xsr);   // waves 1..3
+        split_x_to_lds(x, nblk, (int)threadIdx.x - 64, 64 * (NWV - 1), xsr);   // waves 1..
     }
     __syncthreads();
     if (first) {
-        for (int c = threadIdx.x; c <= E; c += 256) {
+        for (int c = threadIdx.x; c <= E; c += 64 * NWV) {
             int below = 0, hit = 0;
             for (int i = 0; i < k; ++i) {
                 below += sel[i] < c ? 1 : 0;
@@ -543,23 +542,24 @@ __global__ __launch_bounds__(256) void gate_up_mfma_token_kernel(
     const uint32_t code_row = (uint32_t)d >> 1;
     const rsrc_t codes = make_rsrc(W.gu_codes + (size_t)e * 2 * f * code_row, 2u * f * code_row);
     const rsrc_t scales = make_rsrc(W.gu_scales + (size_t)e * 2 * f * nblk, 2u * f * nblk);
-    constexpr int kPerWave = PAIRS / 4;           // pairs n_base + wid + 4 q
+    constexpr int kPerWave = PAIRS / NWV;         // pairs n_base + wid + NWV q
+    static_assert(kPerWave % 2 == 0, "pairs go two at a time");
     const int n_base = blockIdx.x * PAIRS + wid;
     HT *hrow = h + (size_t)a * f;
     PairBuf<NBL> A, B;
     load_pair<NBL>(codes, scales, n_base, f, lane, nblk, code_row, A);
 #pragma unroll 1
     for (int q = 0; q < kPerWave; q += 2) {
-        load_pair<NBL>(codes, scales, n_base + 4 * (q + 1), f, lane, nblk, code_row, B);
+        load_pair<NBL>(codes, scales, n_base + NWV * (q + 1), f, lane, nblk, code_row, B);
         __builtin_amdgcn_sched_barrier(0);
         const float va = pair_h_mfma<NBL>(A, xa, lane, nblk);
-        if (lane == 0) put_h(hrow + n_base + 4 * q, va);
+        if (lane == 0) put_h(hrow + n_base + NWV * q, va);
         __builtin_amdgcn_sched_barrier(0);
         if (q + 2 < kPerWave)
-            load_pair<NBL>(codes, scales, n_base + 4 * (q + 2), f, lane, nblk, code_row, A);
+            load_pair<NBL>(codes, scales, n_base + NWV * (q + 2), f, lane, nblk, code_row, A);
         __builtin_amdgcn_sched_barrier(0);
         const float vb = pair_h_mfma<NBL>(B, xa, lane, nblk);
-        if (lane == 0) put_h(hrow + n_base + 4 * (q + 1), vb);
+        if (lane == 0) put_h(hrow + n_base + NWV * (q + 1), vb);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -993,30 +993,30 @@ bool gate_up_token_fusable(int T, int d, int E, int k, int f) {
            nbl <= 4 && d <= 8192;
 }
 
-template <int NBL, int PAIRS, typename HT>
+template <int NBL, int PAIRS, typename HT, int NWV>
 hipError_t launch_token_n(const float *logits, const uint16_t *x, ExpertArgs w, int32_t *ids,
                           float *tw, int32_t *counts, int32_t *offsets, int32_t *sorted_rows,
                           int32_t *row_pos, int32_t *plan, HT *h, int d, int E, int k, int f,
                           hipStream_t s) {
-    return timed_launch("gemv_gate_up", gate_up_mfma_token_kernel<NBL, PAIRS, HT>, dim3(f / PAIRS, k),
-                        dim3(256), (size_t)d * 2 + 16, s, logits, x, w, ids, tw, counts, offsets,
+    return timed_launch("gemv_gate_up", gate_up_mfma_token_kernel<NBL, PAIRS, HT, NWV>,
+                        dim3(f / PAIRS, k), dim3(64 * NWV), (size_t)d * 2 + 16, s, logits, x, w, ids, tw, counts, offsets,
                         sorted_rows, row_pos, plan, h, d, E, k, f);
 }
 
-template <int PAIRS, typename HT>
+template <int PAIRS, int NWV, typename HT>
 hipError_t launch_gate_up_token_p(const float *logits, const uint16_t *x, ExpertArgs w,
                                   int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
                                   int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, HT *h,
                                   int d, int E, int k, int f, hipStream_t s) {
     const int nbl = (d / 32 + 63) / 64;
     if (nbl == 1)
-        return launch_token_n<1, PAIRS>(logits, x, w, ids, tw, counts, offsets, sorted_rows,
-                                        row_pos, plan, h, d, E, k, f, s);
+        return launch_token_n<1, PAIRS, HT, NWV>(logits, x, w, ids, tw, counts, offsets,
+                                                 sorted_rows, row_pos, plan, h, d, E, k, f, s);
     if (nbl == 2)
-        return launch_token_n<2, PAIRS>(logits, x, w, ids, tw, counts, offsets, sorted_rows,
-                                        row_pos, plan, h, d, E, k, f, s);
-    return launch_token_n<4, PAIRS>(logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
-                                    plan, h, d, E, k, f, s);
+        return launch_token_n<2, PAIRS, HT, NWV>(logits, x, w, ids, tw, counts, offsets,
+                                                 sorted_rows, row_pos, plan, h, d, E, k, f, s);
+    return launch_token_n<4, PAIRS, HT, NWV>(logits, x, w, ids, tw, counts, offsets, sorted_rows,
+                                             row_pos, plan, h, d, E, k, f, s);
 }
 
 template <typename HT>
@@ -1024,11 +1024,18 @@ hipError_t launch_gate_up_token_t(const float *logits, const uint16_t *x, Expert
                                   int32_t *ids, float *tw, int32_t *counts, int32_t *offsets,
                                   int32_t *sorted_rows, int32_t *row_pos, int32_t *plan, HT *h,
                                   int d, int E, int k, int f, hipStream_t s) {
-    if (f % 48 == 0)
-        return launch_gate_up_token_p<48>(logits, x, w, ids, tw, counts, offsets, sorted_rows,
-                                          row_pos, plan, h, d, E, k, f, s);
-    return launch_gate_up_token_p<32>(logits, x, w, ids, tw, counts, offsets, sorted_rows, row_pos,
-                                      plan, h, d, E, k, f, s);
+#define TOKEN_CFG(P, NW)                                                                   \
+    return launch_gate_up_token_p<P, NW>(logits, x, w, ids, tw, counts, offsets, sorted_rows, \
+                                         row_pos, plan, h, d, E, k, f, s)
+    // wide rows (d > 4096: two pairs in flight are 4 x 3.6 KB a wave at
+    // d = 7168): one block per CU streams best when the grid fills the chip
+    // (K3 shape: 96 pairs, 256 blocks, 37.4 us against 38.2 us for 48); the
+    // narrower rows of d = 4096 want two blocks per CU (64 pairs: 20.0 us
+    // against 17.4 us for 32)
+    if (d > 4096 && f % 96 == 0 && (f / 96) * k >= 256) TOKEN_CFG(96, 4);
+    if (f % 48 == 0) TOKEN_CFG(48, 4);
+    TOKEN_CFG(32, 4);
+#undef TOKEN_CFG
 }
 
 hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertArgs w,

@@ -156,7 +156,7 @@ def test_router_bias_and_ties(dev):
 
 ONE_TOKEN_CASES = [
     # (T, d, E, k, f, seed): one token, so top-k and grouping run inside the
-    # gate/up pass (48 or 32 pairs per block);
+    # gate/up pass (96, 48 or 32 pairs per block);
     # router rows duplicated so that selected experts tie
     (1, 512, 1000, 32, 96, 31),      # k = 32, E near the limit
     (1, 192, 40, 5, 96, 32),         # chunk length 3, E not a multiple of 64
@@ -170,6 +170,7 @@ ONE_TOKEN_CASES = [
     # two slots a wave when k > 8)
     (1, 512, 40, 16, 2560, 38),
     (1, 448, 24, 6, 2560, 39),       # d a multiple of 28 (28-row blocks), k <= 8
+    (1, 4608, 24, 16, 1536, 40),     # d > 4096 and 256 blocks of 96 pairs: one block per CU
 ]
 
 
