@@ -29,6 +29,7 @@ CASES = [
     ("mfma", 200, 130, 512, 16, 4, 256, 503),         # scaled-MFMA expert path both times
     ("mfma_then_gemv", 160, 40, 512, 16, 4, 256, 504),
     ("filtered_routing", 300, 257, 512, 64, 6, 256, 505),
+    ("wide_one_token", 4, 1, 4608, 24, 16, 1536, 506),   # one token on 96-pair gate/up blocks
 ]
 
 
