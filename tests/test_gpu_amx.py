@@ -27,6 +27,7 @@ AMX_CASES = [
     (1, 512, 64, 8, 96, 93),         # one token: top-k inside the gate/up kernel
     (3, 256, 40, 5, 64, 94),         # fused down + combine
     (20, 512, 70, 3, 128, 95),       # grouped GEMVs, rows_out + combine
+    (64, 512, 8, 4, 128, 96),        # ~32 rows per expert on the GEMVs: four-row passes
 ]
 
 
