@@ -11,6 +11,8 @@
 //
 // Top-k: descending logit, lower expert index first on equal logits; the
 // routing weights are a softmax over the k selected logits, no extra scale.
+#include <atomic>
+
 #include "moe_internal.hpp"
 #include "select_dev.hpp"
 
@@ -214,6 +216,120 @@ __global__ __launch_bounds__(64 * RPB) void router_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Few tokens (8 <= T < 256, d % 512 == 0): TE router rows staged through LDS
+// for TT tokens.  The block copies its router rows into LDS with coalesced
+// 16-byte loads, chunk by chunk with 16 bytes of padding (as above); wave w
+// then takes tokens t0 + (TT / 4) w .., lane c summing chunk c of every
+// token and row of the tile in ascending element order, the x chunk pieces
+// loaded straight from memory a few slices ahead.  The same arithmetic and
+// order as router_logits_kernel, so the logits are identical; the router
+// rows are read once per TT tokens with whole cache lines.
+constexpr int kLtTE = 8;                            // router rows per block
+constexpr int kLtTT = 16;                           // tokens per block (4 per wave)
+constexpr int kLtAhead = 2;                         // x slices in flight ahead
+
+__global__ __launch_bounds__(256) void router_lds_tile_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
+    const float *__restrict__ bias, float *__restrict__ logits, int T, int d, int E) {
+    constexpr int TPW = kLtTT / 4;                  // tokens per wave
+    extern __shared__ uint4 wrs[];                  // [kLtTE][64][cstride]
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int P = d >> 6;
+    const int q_per_chunk = P >> 3;                 // 16-byte pieces per chunk
+    const int cstride = q_per_chunk + 1;
+    const int e0 = blockIdx.x * kLtTE;
+    const int t0 = blockIdx.y * kLtTT + wid * TPW;
+    const int pieces = 64 * q_per_chunk;            // 16-byte pieces per row
+    const int total = kLtTE * pieces;
+    // staging, 16 pieces a thread per round: every load of a round first,
+    // then its LDS stores
+    for (int base = 0; base < total; base += 256 * 16) {
+        uint4 buf[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = min(base + (int)threadIdx.x + 256 * j, total - 1);
+            const int r = i / pieces, q = i - r * pieces;
+            buf[j] = reinterpret_cast<const uint4 *>(wr + (size_t)min(e0 + r, E - 1) * d)[q];
+        }
+        loads_done(buf);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = base + (int)threadIdx.x + 256 * j;
+            if (i < total) {
+                const int r = i / pieces, q = i - r * pieces;
+                const int c = q / q_per_chunk, w = q - c * q_per_chunk;
+                wrs[(r * 64 + c) * cstride + w] = buf[j];
+            }
+        }
+    }
+    __syncthreads();
+    const uint4 *xr[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+        xr[i] = reinterpret_cast<const uint4 *>(x + (size_t)min(t0 + i, T - 1) * d + (size_t)lane * P);
+    double acc[TPW][kLtTE];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int j = 0; j < kLtTE; ++j) acc[i][j] = 0.0;
+    uint4 xq[kLtAhead + 1][TPW];
+#pragma unroll
+    for (int a = 0; a < kLtAhead; ++a)
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) xq[a][i] = xr[i][min(a, q_per_chunk - 1)];
+    const uint4 *wc = wrs + lane * cstride;
+    for (int w = 0; w < q_per_chunk; ++w) {
+        // slice w + kLtAhead's x pieces, then slice w's products
+        const int wn = min(w + kLtAhead, q_per_chunk - 1);
+        uint4 xn[TPW];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) xn[i] = xr[i][wn];
+        uint32_t wv[kLtTE][4];
+#pragma unroll
+        for (int j = 0; j < kLtTE; ++j) {
+            const uint4 v = wc[j * 64 * cstride + w];
+            wv[j][0] = v.x; wv[j][1] = v.y; wv[j][2] = v.z; wv[j][3] = v.w;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {               // ascending element order
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const uint4 xv = xq[0][i];
+                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+                const double xe = (q & 1) ? bf16_hi(xw[q >> 1]) : bf16_lo(xw[q >> 1]);
+#pragma unroll
+                for (int j = 0; j < kLtTE; ++j) {
+                    const double we = (q & 1) ? bf16_hi(wv[j][q >> 1]) : bf16_lo(wv[j][q >> 1]);
+                    acc[i][j] = fma(xe, we, acc[i][j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < kLtAhead; ++a)
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) xq[a][i] = a + 1 < kLtAhead ? xq[a + 1][i] : xn[i];
+    }
+    // fixed pairwise tree over the 64 chunk sums
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1)
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int j = 0; j < kLtTE; ++j) acc[i][j] += __shfl_xor(acc[i][j], m, 64);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int j = 0; j < kLtTE; ++j) {
+            const int t = t0 + i, e = e0 + j;
+            if (lane == i * kLtTE + j && t < T && e < E) {
+                const double l = acc[i][j] + (bias ? (double)bias[e] : 0.0);
+                logits[(size_t)t * E + e] = (float)l;   // one RNE rounding
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // top-k + softmax: one wave per token.
 // ---------------------------------------------------------------------------
 template <int PL>
@@ -241,7 +357,7 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const flo
     if (T <= 0) return hipSuccess;
     const int P = d / 64;
     if (T == 1 && P % 8 == 0 && d <= 8192) {
-        // 4 router rows per block, or 1 when that leaves CUs idle (E < 1024)
+        // 4 router rows per block, or 1 when that leaves CUs idle (E < 768)
         const int rpb = E >= 4 * 192 ? kRouterRowsPerBlock : 1;
         const size_t lds = (size_t)rpb * 64 * ((P / 8) + 1) * 16 + 16;   // + spare slot
         if (rpb == 1)
@@ -257,6 +373,23 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const flo
     // T = 64: 67.6 us against 86.0 us for 4 x 8)
     if (T < 4) return launch_logits_tile<1, 4>(x, wr, bias, logits, T, d, E, s);
     if (T < 8) return launch_logits_tile<4, 8>(x, wr, bias, logits, T, d, E, s);
+    if (P % 8 == 0 && d <= 8192) {
+        // router rows staged through LDS, 16 tokens per block (up to 136 KB
+        // of LDS: the launch limit is raised once per process)
+        static std::atomic<bool> attr{false};
+        const size_t lds = (size_t)kLtTE * 64 * ((P / 8) + 1) * 16;
+        if (!attr.load(std::memory_order_acquire)) {
+            const hipError_t e = hipFuncSetAttribute((const void *)router_lds_tile_kernel,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)(8 * 64 * 17 * 16));
+            if (e != hipSuccess) return e;
+            attr.store(true, std::memory_order_release);
+        }
+        dim3 grid((E + kLtTE - 1) / kLtTE, (T + kLtTT - 1) / kLtTT);
+        (void)timed_launch("router_logits", router_lds_tile_kernel, dim3(grid), dim3(256), lds, s,
+                           x, wr, bias, logits, T, d, E);
+        return hipGetLastError();
+    }
     return launch_logits_tile<8, 8>(x, wr, bias, logits, T, d, E, s);
 }
 
