@@ -381,7 +381,7 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, const flo
         if (!attr.load(std::memory_order_acquire)) {
             const hipError_t e = hipFuncSetAttribute((const void *)router_lds_tile_kernel,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)(8 * 64 * 17 * 16));
+                                                     (int)(kLtTE * 64 * 17 * 16));
             if (e != hipSuccess) return e;
             attr.store(true, std::memory_order_release);
         }
