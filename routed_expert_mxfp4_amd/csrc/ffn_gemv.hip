@@ -1053,13 +1053,16 @@ hipError_t launch_gate_up_token(const float *logits, const uint16_t *x, ExpertAr
 }
 
 // rows per batch and batch buffers of the fused down + combine
-constexpr int kDcB = 4, kDcR = 2;
+// (batches of 4 rows; a ring of 3 batch buffers for one MX block of h per
+// lane, 2 for two, whose registers allow no more at 8 waves)
+constexpr int kDcB = 4;
 
 template <int NBLD, int ROWS, int NW, typename HT>
 void launch_dc(const HT *h, ExpertArgs w, const int32_t *ids, const float *topk_w,
                const int32_t *row_pos, uint16_t *y, int T, int d, int E, int k, int f,
                hipStream_t s) {
-    (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, ROWS, kDcB, kDcR, NW, HT>,
+    constexpr int R = NBLD == 1 ? 3 : 2;
+    (void)timed_launch("down_combine", down_combine_split_kernel<NBLD, ROWS, kDcB, R, NW, HT>,
                        dim3(d / ROWS, T), dim3(64 * NW), 0, s, h, w, ids, topk_w, row_pos, y, T, d,
                        E, k, f);
 }
@@ -1078,16 +1081,12 @@ hipError_t launch_dc_split(const HT *h, ExpertArgs w, const int32_t *ids,
                            const float *topk_w, const int32_t *row_pos, uint16_t *y, int T,
                            int d, int E, int k, int f, hipStream_t s) {
     // about one block per CU: 28 output rows per block where d allows
-    // (7168 / 28 = 256), else 16 (4096 / 16 = 256) or 32; one wave per slot
-    // (16 waves, or 8 when k <= 8), and 8 waves, two slots each, for two MX
-    // blocks per lane (whose registers do not fit 16 waves)
+    // (7168 / 28 = 256), else 16 (4096 / 16 = 256) or 32; 8 waves, a wave
+    // taking slots wid, wid + 8, .. (at k = 16 two slots a wave with three
+    // batches in flight: 18.6 us against 19.4 for 16 waves of one slot and
+    // two batches)
     const int rows = d % 28 == 0 ? 28 : (d % 16 == 0 && d / 16 <= 512 ? 16 : 32);
-    if constexpr (NBLD > 1) {
-        launch_dc_rows<NBLD, 8>(rows, h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
-    } else {
-        if (k <= 8) launch_dc_rows<NBLD, 8>(rows, h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
-        else launch_dc_rows<NBLD, 16>(rows, h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
-    }
+    launch_dc_rows<NBLD, 8>(rows, h, w, ids, topk_w, row_pos, y, T, d, E, k, f, s);
     return hipGetLastError();
 }
 

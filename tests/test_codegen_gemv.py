@@ -2,8 +2,9 @@
 
 The GEMV and fused down+combine kernels hide memory latency with the loads
 of several waves in flight, so their speed rests on how many waves fit on a
-SIMD; a 16-wave block of the fused down+combine does not fit at all above
-128 registers per lane.  This test builds ffn_gemv.hip for gfx950 with the
+SIMD; the fused down+combine keeps several batches of rows in flight per
+wave, which costs registers, and its 8-wave blocks must still fit two waves
+per SIMD.  This test builds ffn_gemv.hip for gfx950 with the
 compiler's resource-usage remarks and checks that no kernel spills to
 scratch and that the kernels keep the occupancy the launches are sized for.
 """
@@ -61,11 +62,14 @@ def test_no_kernel_spills(resources):
         assert r.get("scratch", 0) == 0, name
 
 
-def test_fused_down_combine_16_wave_blocks_fit(resources):
-    # the 16-wave variants (one wave per top-k slot, k <= 16) must fit 16
-    # waves on one CU: four per SIMD, at most 128 registers per lane
-    for name, r in _of(resources, r"down_combine_split_kernelILi1ELi\d+ELi4ELi2ELi16E").items():
-        assert r["occupancy"] >= 4, (name, r)
+def test_fused_down_combine_8_wave_blocks_fit(resources):
+    # 8-wave blocks (two waves per SIMD, at most 256 registers per lane);
+    # the one-MX-block-per-lane variants with their ring of three batches
+    # stay at three waves per SIMD
+    for name, r in _of(resources, r"down_combine_split_kernelILi\d+ELi\d+ELi4ELi\dELi8E").items():
+        assert r["occupancy"] >= 2, (name, r)
+    for name, r in _of(resources, r"down_combine_split_kernelILi1ELi\d+ELi4ELi3ELi8E").items():
+        assert r["occupancy"] >= 3, (name, r)
 
 
 def test_decode_gate_up_two_blocks_per_cu(resources):
