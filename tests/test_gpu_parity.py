@@ -171,6 +171,7 @@ ONE_TOKEN_CASES = [
     (1, 512, 40, 16, 2560, 38),
     (1, 448, 24, 6, 2560, 39),       # d a multiple of 28 (28-row blocks), k <= 8
     (1, 4608, 24, 16, 1536, 40),     # d > 4096 and 256 blocks of 96 pairs: one block per CU
+    (1, 8224, 12, 6, 1536, 41),      # d > 8192, not a multiple of 28: 32-row down blocks
 ]
 
 
