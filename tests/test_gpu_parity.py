@@ -83,6 +83,7 @@ SMALL_CASES = [
     (70, 64, 130, 4, 32, 16),       # E > 128
     (3, 8192, 6, 4, 128, 18),       # d = 8192: four split x rows fill the GEMV's 64 KB of LDS
     (40, 512, 6, 3, 64, 19),        # ~20 rows per expert on the GEMVs: chunks of four rows + a tail
+    (1, 8256, 12, 6, 1536, 41),     # d > 8192: fp32 h into the fused down+combine, 32-row blocks
 ]
 
 
@@ -171,7 +172,6 @@ ONE_TOKEN_CASES = [
     (1, 512, 40, 16, 2560, 38),
     (1, 448, 24, 6, 2560, 39),       # d a multiple of 28 (28-row blocks), k <= 8
     (1, 4608, 24, 16, 1536, 40),     # d > 4096 and 256 blocks of 96 pairs: one block per CU
-    (1, 8224, 12, 6, 1536, 41),      # d > 8192, not a multiple of 28: 32-row down blocks
 ]
 
 
